@@ -1,0 +1,181 @@
+"""Benchmark of one batched speculation cycle on one MI355X.
+
+A step is one full cycle (prefix cut, Markov-biased draft of every verified position, rejection
+verification, correction / bonus) over one batch of synthetic inputs already resident in HBM.
+Default workload: the 16-position long-block cycle, B=256, K=16, V=151936, rank 256, bf16.
+
+Prints one JSON line: throughput in verified draft tokens/s (sum of per-request verify lengths
+per second), the roofline of the dominant kernel (the per-step row sweep) from HIP events
+attached to its dispatches inside the timed region, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # MI355X HBM3E, bytes/s
+METRIC = "verified draft tokens/sec per MI355X + % HBM roofline (B=256,K=16,V=151936)"
+
+
+def hip_runtime():
+    hip = C.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+    hip.hipEventCreate.restype = C.c_int
+    hip.hipEventDestroy.argtypes = [C.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    hip.hipEventElapsedTime.restype = C.c_int
+    return hip
+
+
+def compulsory_bytes(cfg, L, a):
+    """Bytes the method must move at least once: draft rows of every verified position, target rows
+    of every decided position plus the correction/bonus row, W once, the gathered A rows, and the
+    small per-request inputs and outputs."""
+    e = 2 if cfg.dtype == 1 else 4
+    V, R, K = cfg.V, cfg.R, cfg.K
+    B = len(L)
+    sL = int(L.sum())
+    sa1 = int((a + 1).sum())
+    return (e * V * (sL + sa1) + e * R * V + e * R * sL + 4 * B * K + 12 * B + 4 * B * (K + 1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="longblock")
+    ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--noise", choices=["chunked", "flat"], default="chunked")
+    ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
+              "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from draft_sampling_lossless_spec_amd import CHUNKED, FLAT, spec_cycle, spec_cycle_kernel_count, spec_workspace_bytes
+    from draft_sampling_lossless_spec_amd import workloads as wl
+
+    noise = CHUNKED if args.noise == "chunked" else FLAT
+    t0 = time.time()
+    w = wl.generate(args.config, threshold=args.threshold)
+    cfg = w.cfg
+    print(f"[bench] generated {args.config} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base, target, A, W = t(w.base), t(w.target), t(w.A), t(w.W)
+    x0, conf, temp = t(w.x0), t(w.conf), t(w.temp)
+    B, K = cfg.B, cfg.K
+    ws = torch.empty(spec_workspace_bytes(B, K, cfg.V, cfg.R, cfg.dtype, noise), dtype=torch.uint8, device=dev)
+    out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
+    run = lambda **kw: spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise,
+                                  workspace=ws, out=out, **kw)
+    diag = spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise, workspace=ws,
+                      diag=True)
+    torch.cuda.synchronize()
+    L = diag["verify_len"].cpu().numpy()
+    a = diag["accepted_len"].cpu().numpy()
+    assert np.all(a >= 0), "synthetic workload produced invalid requests"
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    # events attached to every kernel dispatch of every timed step
+    hip = hip_runtime()
+    nk = spec_cycle_kernel_count(K)
+    ev = [(C.c_void_p * (2 * nk))() for _ in range(args.steps)]
+    for arr in ev:
+        for i in range(2 * nk):
+            h = C.c_void_p()
+            assert hip.hipEventCreate(C.byref(h)) == 0
+            arr[i] = h.value
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for i in range(args.steps):
+        run(_events=ev[i])
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    ms_per_step = (te - ts) * 1e3 / args.steps
+
+    def el(e0, e1):
+        f = C.c_float()
+        assert hip.hipEventElapsedTime(C.byref(f), C.c_void_p(e0), C.c_void_p(e1)) == 0
+        return f.value
+
+    sweep = np.zeros((args.steps, K + 1))
+    merge = np.zeros((args.steps, K + 1))
+    init = np.zeros(args.steps)
+    span = np.zeros(args.steps)
+    for i, arr in enumerate(ev):
+        init[i] = el(arr[0], arr[1])
+        for s in range(K + 1):
+            sweep[i, s] = el(arr[2 * (1 + 2 * s)], arr[2 * (1 + 2 * s) + 1])
+            merge[i, s] = el(arr[2 * (2 + 2 * s)], arr[2 * (2 + 2 * s) + 1])
+        span[i] = el(arr[0], arr[2 * nk - 1])
+    for arr in ev:
+        for i in range(2 * nk):
+            hip.hipEventDestroy(C.c_void_p(arr[i]))
+
+    sL = int(L.sum())
+    cbytes = compulsory_bytes(cfg, L, a)
+    t_cycle = ms_per_step * 1e-3
+    value = sL / t_cycle
+    sweep_ms = float(sweep.sum(axis=1).mean())
+    achieved = cbytes / (sweep_ms * 1e-3)
+    n_active = int(L.max()) + 1
+    print(f"[bench] sum L={sL} sum(a+1)={int((a + 1).sum())} max L={int(L.max())} compulsory={cbytes / 1e6:.1f} MB",
+          file=sys.stderr)
+    print(f"[bench] wall {ms_per_step * 1e3:.1f} us/cycle; event span {span.mean() * 1e3:.1f} us; init "
+          f"{init.mean() * 1e3:.1f} us; sweep total {sweep_ms * 1e3:.1f} us; merge total "
+          f"{merge.sum(axis=1).mean() * 1e3:.1f} us", file=sys.stderr)
+    print("[bench] per-step sweep us: " + " ".join(f"{x * 1e3:.1f}" for x in sweep.mean(axis=0)), file=sys.stderr)
+    print("[bench] per-step merge us: " + " ".join(f"{x * 1e3:.1f}" for x in merge.mean(axis=0)), file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(args.cpu_requests, B)
+        sub = slice(0, n)
+        tc = time.perf_counter()
+        r = oracle.spec_cycle_ref(w.base[sub], w.target[sub], w.A, w.W, w.x0[sub], w.conf[sub], w.temp[sub],
+                                  w.threshold, w.seed, noise=noise)
+        dt = time.perf_counter() - tc
+        cpu = {"value": float(r["verify_len"][r["verify_len"] > 0].sum() / dt), "unit": "verified draft tokens/s",
+               "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"first {n} of {B} requests of the same cycle ({dt:.1f} s wall, fp64 C + OpenMP)"}
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "verified draft tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == 1 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "K": K, "V": cfg.V, "R": cfg.R, "threshold": w.threshold,
+                   "noise": args.noise, "sum_verify_len": sL, "sum_emitted": int((a + 1).sum()),
+                   "steps_with_work": n_active},
+        "hbm_frac_cycle": cbytes / t_cycle / HBM_PEAK,
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK, "traffic": None, "kernel": "k_sweep",
+                     "sweep_us_per_cycle": sweep_ms * 1e3, "launches_per_cycle": K + 1},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

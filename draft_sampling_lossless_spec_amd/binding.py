@@ -1,0 +1,158 @@
+"""ctypes binding of libspeccycle.so.  Argument marshalling only: shapes and dtypes of torch
+device tensors are checked, pointers and the current HIP stream are passed to the C ABI
+(include/spec_cycle.h), and the C return code is turned into an exception."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+FP32, BF16 = 0, 1
+FLAT, CHUNKED = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libspeccycle.so")
+_lib = None
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+class _Dims(C.Structure):
+    _fields_ = [("B", C.c_int32), ("K", C.c_int32), ("V", C.c_int32), ("R", C.c_int32),
+                ("dtype", C.c_int32), ("noise", C.c_int32)]
+
+
+class _Diag(C.Structure):
+    _fields_ = [("verify_len", C.c_void_p), ("draft_tokens", C.c_void_p), ("logq", C.c_void_p),
+                ("logp", C.c_void_p)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch ships a HIP runtime with the same soname; loading it first keeps one runtime per process
+    import torch  # noqa: F401
+    if not os.path.exists(_LIB_PATH):
+        raise SpecError(f"{_LIB_PATH} is missing: build it with `python -m draft_sampling_lossless_spec_amd.build`")
+    lib = C.CDLL(_LIB_PATH)
+    lib.spec_workspace_bytes.restype = C.c_size_t
+    lib.spec_workspace_bytes.argtypes = [C.POINTER(_Dims)]
+    lib.spec_error_string.restype = C.c_char_p
+    lib.spec_error_string.argtypes = [C.c_int]
+    lib.spec_version.restype = C.c_int
+    lib.spec_version.argtypes = []
+    cycle_args = [C.POINTER(_Dims), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                  C.c_void_p, C.c_float, C.c_uint64, C.c_int64, C.c_void_p, C.c_void_p, C.POINTER(_Diag),
+                  C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.spec_cycle.restype = C.c_int
+    lib.spec_cycle.argtypes = cycle_args
+    lib.spec_cycle_timed.restype = C.c_int
+    lib.spec_cycle_timed.argtypes = cycle_args + [C.c_void_p, C.c_int]
+    lib.spec_cycle_kernel_count.restype = C.c_int
+    lib.spec_cycle_kernel_count.argtypes = [C.POINTER(_Dims)]
+    _lib = lib
+    return lib
+
+
+def spec_version() -> int:
+    return int(_load().spec_version())
+
+
+def spec_error_string(code: int) -> str:
+    return _load().spec_error_string(code).decode()
+
+
+def spec_workspace_bytes(B: int, K: int, V: int, R: int, dtype: int = BF16, noise: int = CHUNKED) -> int:
+    d = _Dims(B, K, V, R, dtype, noise)
+    return int(_load().spec_workspace_bytes(C.byref(d)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise SpecError(f"logits / factors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype=None):
+    if not t.is_cuda:
+        raise SpecError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise SpecError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise SpecError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise SpecError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def spec_cycle_kernel_count(K: int) -> int:
+    d = _Dims(1, K, 2, 16, BF16, CHUNKED)
+    return int(_load().spec_cycle_kernel_count(C.byref(d)))
+
+
+def spec_cycle_timed(*args, events, **kw) -> dict:
+    """spec_cycle with a start/stop event pair on every kernel; `events` is a ctypes array of
+    hipEvent_t handles (2 per kernel, see spec_cycle_kernel_count)."""
+    return spec_cycle(*args, _events=events, **kw)
+
+
+def spec_cycle(base_logits, target_logits, A, W, conf, temp, threshold: float, seed: int, x0=None,
+               request_offset: int = 0, noise: int = CHUNKED, diag: bool = False, workspace=None,
+               out=None, stream=None, _events=None) -> dict:
+    """Run one speculation cycle on the current HIP stream (or `stream`).  Returns a dict with
+    'accepted_len' [B] and 'tokens' [B, K+1] (int32 device tensors) and, with diag=True,
+    'verify_len', 'draft_tokens', 'logq', 'logp'.  Asynchronous like the C call."""
+    import torch
+    B, K, V = base_logits.shape
+    R = A.shape[1]
+    dt = _dtype_code(base_logits)
+    _check(base_logits, "base_logits", (B, K, V))
+    _check(target_logits, "target_logits", (B, K + 1, V), base_logits.dtype)
+    _check(A, "A", (V, R), base_logits.dtype)
+    _check(W, "W", (V, R), base_logits.dtype)
+    _check(conf, "conf", (B, K), torch.float32)
+    _check(temp, "temp", (B,), torch.float32)
+    if x0 is not None:
+        _check(x0, "x0", (B,), torch.int32)
+    dev = base_logits.device
+    lib = _load()
+    d = _Dims(B, K, V, R, dt, noise)
+    need = int(lib.spec_workspace_bytes(C.byref(d)))
+    if need == 0:
+        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
+    dg = None
+    if diag:
+        for k, shp, ty in (("verify_len", (B,), torch.int32), ("draft_tokens", (B, K), torch.int32),
+                           ("logq", (B, K), torch.float32), ("logp", (B, K), torch.float32)):
+            if k not in out:
+                out[k] = torch.empty(shp, dtype=ty, device=dev)
+        dg = _Diag(out["verify_len"].data_ptr(), out["draft_tokens"].data_ptr(), out["logq"].data_ptr(),
+                   out["logp"].data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    args = (C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(), W.data_ptr(),
+            x0.data_ptr() if x0 is not None else None, conf.data_ptr(), temp.data_ptr(),
+            C.c_float(threshold), C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), C.c_int64(request_offset),
+            out["accepted_len"].data_ptr(), out["tokens"].data_ptr(),
+            C.byref(dg) if dg is not None else None, workspace.data_ptr(), workspace.numel(),
+            C.c_void_p(stream.cuda_stream))
+    if _events is None:
+        rc = lib.spec_cycle(*args)
+    else:
+        rc = lib.spec_cycle_timed(*args, C.cast(_events, C.c_void_p), len(_events))
+    if rc != 0:
+        raise SpecError(f"spec_cycle failed: {spec_error_string(rc)} (code {rc})")
+    return out

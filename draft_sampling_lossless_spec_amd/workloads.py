@@ -29,7 +29,7 @@ structure of the workloads the pages discuss:
 
 Every request has its own numpy PCG64 stream (SeedSequence([gen_seed, config id, 0, b])), so a
 subset of requests can be regenerated bit-identically without drawing the whole batch; A and W
-have streams of their own.  bf16 arrays are returned as uint16 bit patterns (round to nearest
+have streams of their own (one per block of 4096 vocabulary rows).  bf16 arrays are returned as uint16 bit patterns (round to nearest
 even from the fp32 draw).  x0[b] (the last committed token) is uniform over the vocabulary.
 """
 from __future__ import annotations
@@ -145,13 +145,27 @@ def _request_rows(cfg: Config, gen_seed: int, b: int, V: int | None = None):
     return target, base, conf, x0, np.float32(temp)
 
 
-def markov_factors(cfg: Config, gen_seed: int):
-    """A [V,R], W [V,R] ~ N(0, aw_sigma^2) in the config dtype."""
+FACTOR_BLOCK = 4096   # rows of A / W drawn from one stream
+
+
+def markov_factors(cfg: Config, gen_seed: int, threads: int | None = None):
+    """A [V,R], W [V,R] ~ N(0, aw_sigma^2) in the config dtype; every block of 4096 rows has its
+    own stream (SeedSequence([gen_seed, config id, 1 for A / 2 for W, block]))."""
     out = []
+    nblk = -(-cfg.V // FACTOR_BLOCK)
     for kind in (1, 2):
-        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([gen_seed, cfg.cid, kind, 0])))
-        m = (rng.standard_normal((cfg.V, cfg.R), dtype=np.float32) * np.float32(cfg.aw_sigma))
-        out.append(to_bf16_bits(m) if cfg.dtype == BF16 else m)
+        m = np.empty((cfg.V, cfg.R), dtype=np.uint16 if cfg.dtype == BF16 else np.float32)
+
+        def one(blk, kind=kind, m=m):
+            lo, hi = blk * FACTOR_BLOCK, min(cfg.V, (blk + 1) * FACTOR_BLOCK)
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([gen_seed, cfg.cid, kind, blk])))
+            x = rng.standard_normal((hi - lo, cfg.R), dtype=np.float32) * np.float32(cfg.aw_sigma)
+            m[lo:hi] = to_bf16_bits(x) if cfg.dtype == BF16 else x
+
+        nthreads = threads or min(16, os.cpu_count() or 1)
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(one, range(nblk)))
+        out.append(m)
     return out[0], out[1]
 
 

@@ -1,0 +1,138 @@
+/*
+ * spec_cycle.h -- C ABI of libspeccycle.so: one fused, batched speculation cycle of
+ * confidence-scheduled speculative decoding on an MI355X (gfx950) GPU.
+ *
+ * The cycle (per request b, all requests in parallel):
+ *   1. prefix cut: L_b = number of leading draft positions whose running fp64 product of
+ *      confidences stays >= threshold, stopping at the first failure ("DSpark turns speculation
+ *      into a scheduler", section "Confidence is a serving primitive": prefix survival is the
+ *      product of the per-position confidences; "The Speed Claim Nobody's Really Questioning",
+ *      section "The Real Innovation: Confidence-Scheduled Verification": an early-stopping rule
+ *      keeps the schedule lossless);
+ *   2. semi-autoregressive draft: for j < L_b, x_j is sampled from
+ *      softmax((base_j + A[x_{j-1}] . W) / T_b), the low-rank Markov transition bias from the
+ *      previous sampled token ("DSpark turns speculation into a scheduler", section "DSpark's
+ *      semi-autoregressive compromise"; "The Speed Claim...", section "The Semi-Autoregressive
+ *      Trick": rank-256 Markov head);
+ *   3. lossless verification: x_j is accepted while u_j < p_j(x_j) / q_j(x_j); at the first
+ *      rejection one correction token is drawn from norm(max(0, p_j - q_j)); if all L_b drafts
+ *      survive one bonus token is drawn from p at position L_b ("DSpark turns speculation into a
+ *      scheduler", opening section and "Caveats"; "The Speed Claim...", section "Speculative
+ *      Decoding in Two Sentences").
+ * All randomness is a SplitMix64 counter hash of (seed, global request id, position, stream,
+ * index): the same noise on any device and under any batching.
+ *
+ * Conventions
+ *   - Every array pointer is a DEVICE pointer on the current HIP device; the caller owns every
+ *     buffer.  Row-major layouts, last index fastest.
+ *   - The call validates on the host, enqueues kernels on `stream` and returns; results are valid
+ *     once the caller synchronises the stream.  It allocates nothing and copies nothing between
+ *     host and device; scratch memory is the caller's `workspace`.
+ *   - Reentrant for distinct workspaces; two calls sharing one workspace must be ordered on one
+ *     stream.
+ *   - Errors are negative return codes (below); nothing is enqueued when the host checks fail.
+ *   - Per-request bad inputs (temperature not finite or <= 0, x0 outside [-1, V), a non-finite
+ *     log-normaliser in a row the request needs) mark that request: accepted_len = -1, tokens -1.
+ */
+#ifndef SPEC_CYCLE_H
+#define SPEC_CYCLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* spec_stream_t; /* a hipStream_t; NULL = the default stream */
+
+enum {
+  SPEC_OK = 0,
+  SPEC_E_INVAL = -1,     /* NULL required pointer or bad dimension                           */
+  SPEC_E_DTYPE = -2,     /* unsupported dtype / noise scheme / dimension combination          */
+  SPEC_E_WORKSPACE = -3, /* workspace NULL or smaller than spec_workspace_bytes()             */
+  SPEC_E_ARCH = -4,      /* current device is not gfx950                                      */
+  SPEC_E_HIP = -5        /* a HIP runtime call or kernel launch failed                        */
+};
+
+enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };          /* element type of logits, A and W           */
+enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
+
+typedef struct spec_dims {
+  int32_t B;      /* requests, >= 1                                                         */
+  int32_t K;      /* draft positions per request, 1..32                                     */
+  int32_t V;      /* vocabulary size, >= 2                                                  */
+  int32_t R;      /* Markov rank, 1..256; bf16 needs R % 16 == 0                            */
+  int32_t dtype;  /* SPEC_FP32 or SPEC_BF16                                                 */
+  int32_t noise;  /* SPEC_NOISE_FLAT: one Gumbel per vocabulary index;                      */
+                  /* SPEC_NOISE_CHUNKED: exact two-level Gumbel-max over 64-wide chunks     */
+} spec_dims;
+
+typedef struct spec_diag {   /* optional per-position diagnostics; any field may be NULL     */
+  int32_t* verify_len;       /* [B]   L_b (-1 for an invalid request)                        */
+  int32_t* draft_tokens;     /* [B,K] x_j for j < L_b, else -1                               */
+  float* logq;               /* [B,K] log q_j(x_j) for j < L_b, else NaN                     */
+  float* logp;               /* [B,K] log p_j(x_j) for decided positions (j <= a_b, j < L_b), else NaN */
+} spec_diag;
+
+/* Bytes of device workspace spec_cycle needs for these dimensions (0 if dims are invalid). */
+size_t spec_workspace_bytes(const spec_dims* d);
+
+/*
+ * One speculation cycle.
+ *   base_logits   [B, K, V]    draft backbone logits of each draft position
+ *   target_logits [B, K+1, V]  target logits; row j = target distribution at draft position j,
+ *                              row K holds the bonus row of a request with L_b = K
+ *   A             [V, R]       Markov factor gathered by the previous token
+ *   W             [V, R]       Markov output factor, vocabulary-major: row v holds column v of
+ *                              the R x V factor, so bias_v = sum_r A[prev, r] * W[v, r]
+ *   x0            [B] int32    last committed token per request (Markov bias at position 0);
+ *                              -1 = none; NULL = none for every request
+ *   conf          [B, K] fp32  confidence of each draft position
+ *   temp          [B] fp32     sampling temperature per request (scales both p and q)
+ *   threshold                  prefix-survival threshold of the cut
+ *   seed                       noise seed
+ *   request_offset             global id of local request 0 in the noise hash, so a batch split
+ *                              across calls (or GPUs) draws exactly the noise of one big call
+ *   accepted_len  [B] int32    out: accepted drafts a_b (emitted tokens = a_b + 1), -1 invalid
+ *   tokens        [B, K+1]     out: x_0..x_{a_b-1}, then the correction or bonus, then -1
+ *   diag                       host struct of optional device outputs, may be NULL
+ *   workspace                  device scratch of at least spec_workspace_bytes(d) bytes,
+ *                              256-byte aligned; contents need no initialisation
+ * Returns SPEC_OK or a negative SPEC_E_* code.
+ */
+int spec_cycle(const spec_dims* d, const void* base_logits, const void* target_logits,
+               const void* A, const void* W, const int32_t* x0, const float* conf,
+               const float* temp, float threshold, uint64_t seed, int64_t request_offset,
+               int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, void* workspace,
+               size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * Profiling variant of spec_cycle for benchmarks: identical work and results, and every kernel
+ * of the cycle is launched with a start/stop hipEvent_t pair attached to its own dispatch (no
+ * extra queue packets).  Kernel i is: 0 = set-up and prefix cut, 1 + 2s = row sweep of step s,
+ * 2 + 2s = per-request merge of step s, for s = 0..K.  `events` is a host array of
+ * n_events >= 2 * spec_cycle_kernel_count(d) events created by the caller (hipEventCreate);
+ * events[2i] / events[2i+1] bracket kernel i.  The caller reads hipEventElapsedTime after the
+ * stream is synchronised.  Returns SPEC_E_INVAL when the array is missing or too short.
+ */
+int spec_cycle_timed(const spec_dims* d, const void* base_logits, const void* target_logits,
+                     const void* A, const void* W, const int32_t* x0, const float* conf,
+                     const float* temp, float threshold, uint64_t seed, int64_t request_offset,
+                     int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, void* workspace,
+                     size_t workspace_bytes, spec_stream_t stream, void* const* events, int n_events);
+
+/* Number of kernels one spec_cycle call launches: 1 + 2 (K + 1); 0 for invalid dims. */
+int spec_cycle_kernel_count(const spec_dims* d);
+
+/* Static description of an error code (never NULL). */
+const char* spec_error_string(int code);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int spec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_CYCLE_H */

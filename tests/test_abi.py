@@ -1,0 +1,70 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the public header
+declares, sizes its workspace, and rejects bad arguments on the host before touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_cycle.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from draft_sampling_lossless_spec_amd import binding
+    if not os.path.exists(binding.lib_path()):
+        from draft_sampling_lossless_spec_amd import build
+        build.build()
+    return binding._load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"spec_cycle", "spec_workspace_bytes", "spec_error_string", "spec_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_sizing(lib):
+    from draft_sampling_lossless_spec_amd import spec_workspace_bytes, BF16, FP32, FLAT, CHUNKED
+    n = spec_workspace_bytes(256, 16, 151936, 256, BF16, CHUNKED)
+    assert n > 0 and n % 256 == 0
+    assert spec_workspace_bytes(512, 16, 151936, 256, BF16, CHUNKED) > n
+    assert spec_workspace_bytes(2, 4, 1024, 32, FP32, FLAT) > 0
+    for bad in [(0, 4, 100, 16), (2, 0, 100, 16), (2, 33, 100, 16), (2, 4, 1, 16), (2, 4, 100, 0),
+                (2, 4, 100, 300), (9000, 4, 100, 16)]:
+        assert spec_workspace_bytes(*bad, BF16, CHUNKED) == 0, bad
+    assert spec_workspace_bytes(2, 4, 100, 24, BF16, CHUNKED) == 0      # bf16 needs R % 16 == 0
+    assert spec_workspace_bytes(2, 4, 100, 24, FP32, CHUNKED) > 0
+    assert spec_workspace_bytes(2, 4, 100, 16, 7, CHUNKED) == 0
+    assert spec_workspace_bytes(2, 4, 100, 16, BF16, 5) == 0
+
+
+def test_host_checks_reject_before_any_gpu_call(lib):
+    from draft_sampling_lossless_spec_amd.binding import _Dims
+    d = _Dims(2, 4, 100, 16, 1, 1)
+    args = [None] * 7 + [C.c_float(0.5), C.c_uint64(1), C.c_int64(0), None, None, None, None, C.c_size_t(0), None]
+    assert lib.spec_cycle(C.byref(d), *args) == -1                      # NULL inputs
+    bad = _Dims(2, 4, 100, 24, 1, 1)
+    assert lib.spec_cycle(C.byref(bad), *args) == -2                    # bf16 with R % 16 != 0
+    assert lib.spec_cycle(None, *args) == -1
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    full = [fake, fake, fake, fake, None, fake, fake, C.c_float(0.5), C.c_uint64(1), C.c_int64(0), fake, fake,
+            None, None, C.c_size_t(0), None]
+    assert lib.spec_cycle(C.byref(d), *full) == -3                      # no workspace
+    mis = [fake, fake, C.c_void_p(4100), fake] + full[4:]
+    assert lib.spec_cycle(C.byref(d), *mis) == -1                       # misaligned A
+
+
+def test_error_strings(lib):
+    from draft_sampling_lossless_spec_amd import spec_error_string, spec_version
+    for code in (0, -1, -2, -3, -4, -5, 42):
+        assert isinstance(spec_error_string(code), str) and spec_error_string(code)
+    assert spec_version() >= 100

@@ -1,0 +1,130 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on the same seeded
+inputs.  Small cases are compared request by request on every output; full-size workloads are
+checked by invariants on every request and by the oracle on a sample of requests (each request's
+cycle is independent given its rows, so the oracle replays it alone with request_offset = its
+id)."""
+import numpy as np
+import pytest
+
+import oracle
+from draft_sampling_lossless_spec_amd import workloads as wl
+from gpu_util import run_gpu, to_device
+from parity import Report, check_structure, compare
+
+pytestmark = pytest.mark.gpu
+
+NOISES = [oracle.FLAT, oracle.CHUNKED]
+
+
+def ref(w, noise, request_offset=0, x0=True):
+    return oracle.spec_cycle_ref(w.base, w.target, w.A, w.W, w.x0 if x0 else None, w.conf, w.temp, w.threshold,
+                                 w.seed, noise=noise, request_offset=request_offset)
+
+
+def assert_parity(rep: Report):
+    print(rep.summary(), flush=True)
+    assert not rep.failures, "\n".join(rep.failures[:10])
+    assert rep.near_tie_rate < 1e-3
+
+
+def full_compare(w, noise, **kw):
+    g = run_gpu(w, noise, **kw)
+    o = ref(w, noise, **({"x0": kw["x0"]} if "x0" in kw else {}))
+    assert_parity(compare(o, g))
+    return g, o
+
+
+SMALL = {
+    "tiny_fp32": lambda: wl.generate("tiny"),
+    "ragged_v333_bf16": lambda: wl.generate(wl.small_config(B=12, K=6, V=333, R=32, threshold=0.15)),
+    "v20000_bf16_two_plain_items": lambda: wl.generate(wl.small_config(B=40, K=5, V=20000, R=64, threshold=0.1)),
+    "b300_two_row_blocks": lambda: wl.generate(wl.small_config(B=300, K=3, V=2048, R=16, threshold=0.05)),
+    "fp32_v1001": lambda: wl.generate(wl.small_config(B=5, K=4, V=1001, R=8, dtype=wl.FP32, threshold=0.1)),
+    "k1_b1": lambda: wl.generate(wl.small_config(B=1, K=1, V=4096, R=256, threshold=0.1)),
+    "temp06_k8": lambda: wl.generate(wl.small_config(B=16, K=8, V=5000, R=32, threshold=0.05, temp=0.6,
+                                                      sigma=(1.5,))),
+}
+
+
+@pytest.mark.parametrize("noise", NOISES)
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_cases_match_oracle(case, noise):
+    print(f"case {case} noise {noise}", flush=True)
+    full_compare(SMALL[case](), noise)
+
+
+@pytest.mark.parametrize("noise", NOISES)
+def test_no_previous_token_and_cut_extremes(noise):
+    w = wl.generate(wl.small_config(B=8, K=4, V=3000, R=32, threshold=0.2))
+    full_compare(w, noise, x0=False)
+    w.threshold = 2.0   # nothing survives the cut: one bonus token per request
+    g, _ = full_compare(w, noise)
+    assert np.all(g["verify_len"] == 0) and np.all(g["accepted_len"] == 0)
+    w.threshold = 0.0   # everything is verified
+    g, _ = full_compare(w, noise)
+    assert np.all(g["verify_len"] == 4)
+
+
+@pytest.mark.parametrize("noise", NOISES)
+def test_identical_draft_and_target_accept_all(noise):
+    w = wl.generate(wl.small_config(B=8, K=5, V=2000, R=16, threshold=0.05))
+    w.base[:] = w.target[:, :5]
+    w.A[:] = 0
+    w.W[:] = 0
+    g, _ = full_compare(w, noise)
+    assert np.array_equal(g["accepted_len"], g["verify_len"])
+
+
+@pytest.mark.parametrize("noise", NOISES)
+def test_invalid_requests(noise):
+    w = wl.generate(wl.small_config(B=6, K=3, V=600, R=16, dtype=wl.FP32, threshold=0.05))
+    w.temp[0] = 0.0
+    w.temp[1] = np.nan
+    w.x0[2] = w.cfg.V
+    w.target[3, 0, 5] = np.nan
+    w.conf[3] = 1.0
+    w.base[4, 1, :] = -np.inf
+    w.conf[4] = 1.0
+    g, o = full_compare(w, noise)
+    assert np.all(g["accepted_len"][:5] == -1) and g["accepted_len"][5] >= 0
+
+
+@pytest.mark.parametrize("noise", NOISES)
+def test_determinism_and_sharding(noise):
+    w = wl.generate(wl.small_config(B=20, K=5, V=4000, R=32, threshold=0.1))
+    g1 = run_gpu(w, noise)
+    g2 = run_gpu(w, noise)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g2[k])
+    h = 7
+    half = wl.Workload(w.cfg, w.base[h:], w.target[h:], w.A, w.W, w.x0[h:], w.conf[h:], w.temp[h:], w.threshold,
+                       w.seed, w.request_ids[h:])
+    g3 = run_gpu(half, noise, request_offset=h)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k][h:], g3[k])
+
+
+FULL = [("dspark5", None), ("longblock", None), ("mixed", None), ("highconc", 0.05), ("highconc", 0.2),
+        ("highconc", 0.5), ("highconc", 0.8)]
+
+
+@pytest.mark.parametrize("noise", NOISES)
+@pytest.mark.parametrize("name,thr", FULL)
+def test_full_size_workloads(name, thr, noise):
+    print(f"full {name} thr={thr} noise={noise}", flush=True)
+    w = wl.generate(name, threshold=thr)
+    g = run_gpu(w, noise)
+    errs = check_structure(w, g, oracle.cut)
+    assert not errs, "\n".join(errs[:10])
+    # oracle replay of a sample of requests (first, last and spread)
+    B = w.cfg.B
+    sample = sorted(set([0, 1, B - 1] + list(np.random.default_rng(B).choice(B, size=13, replace=False))))
+    rep = Report()
+    for b in sample:
+        sub = wl.Workload(w.cfg, w.base[b:b + 1], w.target[b:b + 1], w.A, w.W, w.x0[b:b + 1], w.conf[b:b + 1],
+                          w.temp[b:b + 1], w.threshold, w.seed, w.request_ids[b:b + 1])
+        o = ref(sub, noise, request_offset=b)
+        gb = {k: v[b:b + 1] for k, v in g.items()}
+        compare(o, gb, report=rep)
+    assert_parity(rep)
+    print(f"{name}: sum L={int(g['verify_len'].sum())} sum a={int(g['accepted_len'].sum())}", flush=True)
