@@ -45,19 +45,30 @@ __device__ __forceinline__ uint32_t bits_at(uint64_t key, uint32_t i) {
   return (i & 1u) ? (uint32_t)w : (uint32_t)(w >> 32);
 }
 
-// Gumbel noise from 32 random bits, fp32.  E = -log(1 - U) is taken from whichever side keeps
-// precision: log1p(-U) for U < 1/2, and log of the exact complement (2^32 - bits - 1/2) 2^-32
-// for U >= 1/2.
+// hardware transcendentals: v_exp_f32 / v_log_f32 (base 2).  Inputs of ex2 here are <= 0 or
+// small; lg2 arguments are positive normal numbers.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Gumbel noise from 32 random bits, fp32: G = -log(E), E = -log(1 - U).  E is taken from
+// whichever side keeps its relative precision: the series u + u^2/2 + ... + u^5/5 for u < 1/64
+// (truncation error below u^6/6), -log(1 - u) for 1/64 <= u < 1/2 (log2 magnitude >= 0.0227, so
+// its absolute error stays a small relative error), and 32 ln2 - log(complement) with the exact
+// complement (2^32 - bits - 1/2) 2^-32 for u >= 1/2.  Absolute error of G ~ 1e-6.
 __device__ __forceinline__ float gumbel_bits(uint32_t b) {
   float e;
   if (b < 0x80000000u) {
-    float u = ((float)b + 0.5f) * 0x1p-32f;
-    e = -log1pf(-u);
+    const float u = ((float)b + 0.5f) * 0x1p-32f;
+    if (u < 0.015625f) {
+      e = u * fmaf(u, fmaf(u, fmaf(u, fmaf(u, 0.2f, 0.25f), 0.33333334f), 0.5f), 1.0f);
+    } else {
+      e = -lg2(1.0f - u) * LN2;
+    }
   } else {
-    float c = (float)(~b) + 0.5f;
-    e = (32.0f - log2f(c)) * LN2;
+    const float c = (float)(~b) + 0.5f;
+    e = (32.0f - lg2(c)) * LN2;
   }
-  return -logf(e);
+  return -lg2(e) * LN2;
 }
 
 // rigorous upper bound of gumbel_bits(b): U >= 2^(31-clz) 2^-32 and -log1p(-U) >= U
@@ -73,7 +84,37 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 __device__ __forceinline__ float lse2(float a, float b) {
   float m = fmaxf(a, b);
   if (m == -INFINITY) return a + b;   // both empty: -inf; fmaxf drops a NaN, the sum keeps it
-  return m + log2f(exp2f((a - m) * LOG2E) + exp2f((b - m) * LOG2E)) * LN2;
+  return m + lg2(ex2((a - m) * LOG2E) + ex2((b - m) * LOG2E)) * LN2;
+}
+
+// lane permutes on the VALU (DPP), no LDS round trip.  Within each group of 8 lanes:
+// quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror (i <-> 7 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// max / sum over the 8 lanes of an aligned group; every lane gets the result
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  return fmaxf(x, dpp<0x141>(x));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  return x + dpp<0x141>(x);
+}
+
+// value of lane (l ^ 32) with one v_permlane32_swap
+__device__ __forceinline__ float xor32f(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (int)((threadIdx.x & 32) ? r[0] : r[1]));
+}
+__device__ __forceinline__ int xor32i(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (int)((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 // argmax merge: larger score wins, equal scores go to the smaller index

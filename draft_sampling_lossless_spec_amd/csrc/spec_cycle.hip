@@ -42,8 +42,8 @@ constexpr int SUB = 32;             // bias rows per MFMA sub-block
 constexpr int NSUB = 8;             // sub-blocks per kind-A item
 constexpr int RB = SUB * NSUB;      // bias rows per kind-A item
 constexpr int TILE_A = 256;         // vocabulary columns per kind-A item: 4 waves x 64
-constexpr int TILE_B = NT * CHUNK;  // vocabulary columns per kind-B item
-constexpr int MAX_B = 8192;
+constexpr int TILE_B = NT * 2 * CHUNK;  // vocabulary columns per kind-B item: two chunks per thread
+constexpr int MAX_B = 1024;
 constexpr int MAX_K = 32;
 constexpr int MAX_R = 256;
 constexpr int A_PAD = 8;            // bf16 elements of LDS row padding (kills bank conflicts)
@@ -184,9 +184,9 @@ __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* tmp, uint64_t* total) 
   return off + x - v;
 }
 
-struct RowMeta {       // one bias row of a sub-block, staged in LDS
-  int b, j, role, prev, slot;
-  float invT, lse_p, lse_q;
+struct RowMeta {       // one bias row of a kind-A item, staged in LDS
+  int b, j, role, prev;
+  float invT, lse_p, lse_q, pad;
   uint64_t key1, key2;
 };
 
@@ -194,40 +194,39 @@ struct Lists {
   int n_draft, n_correct, n_plain;
 };
 
-// Scan the role bytes of step s; fill `bias_req`/`bias_role` for bias slots [lo, lo+n) and
-// `plain_req` for one plain slot; workgroup 0 also publishes every request's slots.
-__device__ Lists build_lists(const Params& p, const uint8_t* roles, int bias_lo, int bias_n, int plain_slot,
-                             int* bias_req, int* bias_role, int* plain_req, uint64_t* tmp) {
+// Scan the role bytes of step s into the compact row lists of this step, in LDS:
+//   bias_list[i]  = (request << 1) | (1 if CORRECT)  for bias slot i (DRAFT rows first, then CORRECT)
+//   plain_list[i] = request                          for plain slot i (LSEP or BONUS)
+// Workgroup 0 also publishes every request's slots for the merge kernel.
+__device__ Lists build_lists(const Params& p, const uint8_t* roles, uint16_t* bias_list, uint16_t* plain_list,
+                             uint64_t* tmp, bool publish_slots = false) {
   const int per = (p.B + NT - 1) / NT;
   const int b0 = threadIdx.x * per;
   uint64_t cnt = 0;
   for (int i = 0; i < per; i++) {
-    int b = b0 + i;
+    const int b = b0 + i;
     if (b < p.B) {
-      int r = roles[b];
+      const int r = roles[b];
       cnt += (uint64_t)((r & RO_DRAFT) ? 1 : 0) | ((uint64_t)((r & RO_CORRECT) ? 1 : 0) << 16) |
              ((uint64_t)((r & (RO_LSEP | RO_BONUS)) ? 1 : 0) << 32);
     }
   }
   uint64_t tot;
-  uint64_t pre = block_excl_scan(cnt, tmp, &tot);
+  const uint64_t pre = block_excl_scan(cnt, tmp, &tot);
   Lists ls;
   ls.n_draft = (int)(tot & 0xFFFF);
   ls.n_correct = (int)((tot >> 16) & 0xFFFF);
   ls.n_plain = (int)((tot >> 32) & 0xFFFF);
   int d = (int)(pre & 0xFFFF), c = (int)((pre >> 16) & 0xFFFF), q = (int)((pre >> 32) & 0xFFFF);
-  const bool publish = (blockIdx.x == 0);
+  const bool publish = (blockIdx.x == 0) && publish_slots;
   for (int i = 0; i < per; i++) {
-    int b = b0 + i;
+    const int b = b0 + i;
     if (b >= p.B) break;
-    int r = roles[b];
+    const int r = roles[b];
     int sd = -1, sc = -1, sp = -1;
-    if (r & RO_DRAFT) sd = d++;
-    if (r & RO_CORRECT) sc = ls.n_draft + c++;
-    if (r & (RO_LSEP | RO_BONUS)) sp = q++;
-    if (sd >= bias_lo && sd < bias_lo + bias_n) { bias_req[sd - bias_lo] = b; bias_role[sd - bias_lo] = RO_DRAFT; }
-    if (sc >= bias_lo && sc < bias_lo + bias_n) { bias_req[sc - bias_lo] = b; bias_role[sc - bias_lo] = RO_CORRECT; }
-    if (sp >= 0 && sp == plain_slot) *plain_req = b;
+    if (r & RO_DRAFT) { sd = d++; bias_list[sd] = (uint16_t)(b << 1); }
+    if (r & RO_CORRECT) { sc = ls.n_draft + c++; bias_list[sc] = (uint16_t)((b << 1) | 1); }
+    if (r & (RO_LSEP | RO_BONUS)) { sp = q++; plain_list[sp] = (uint16_t)b; }
     if (publish) {
       p.slots[b] = sd;
       p.slots[p.B + b] = sc;
@@ -236,129 +235,6 @@ __device__ Lists build_lists(const Params& p, const uint8_t* roles, int bias_lo,
   }
   __syncthreads();
   return ls;
-}
-
-// ------------------------------------------------------------------------------------------
-// kind A: bias rows (DRAFT / CORRECT) over 256 columns
-// ------------------------------------------------------------------------------------------
-struct WaveOut {        // one wave's result for one row over its 64 columns
-  float4 a;             // {log-mass, best score, best index (bits), aux}
-  float4 b;             // CORRECT: target-row fallback {lse, best score, best index, 0}
-};
-
-// Element-wise work of one lane on its 32 columns (16 per fragment, 2 fragments) of one row.
-// z[i] = base + bias (unscaled), col(i) = v0 + 32*(i/16) + (i%16).  Returns the lane's
-// contribution; the two lanes of a row (h = 0, 1) are merged by the caller.
-template <int NOISE>
-__device__ __forceinline__ void lane_bias_row(const RowMeta& rm, const float (&z)[32], const float (&t)[32], int v0,
-                                              int V, int chunk, float4& oa, float4& ob) {
-  const float invT = rm.invT;
-  float s[32];
-#pragma unroll
-  for (int i = 0; i < 32; i++) {
-    int v = v0 + 32 * (i >> 4) + (i & 15);
-    s[i] = (v < V) ? z[i] * invT : -INFINITY;
-  }
-  if (rm.role == RO_DRAFT) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 32; i++) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float sum = 0.0f;
-    if (mx != -INFINITY) {
-      const float mo = mx * LOG2E;
-#pragma unroll
-      for (int i = 0; i < 32; i++) sum += exp2f(fmaf(s[i], LOG2E, -mo));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; i++) sum += s[i];   // every value -inf or NaN: keep a NaN visible
-    }
-    sum += __shfl_xor(sum, 32, 64);
-    const float lse = (mx == -INFINITY) ? sum : mx + log2f(sum) * LN2;
-    if (NOISE == SPEC_NOISE_CHUNKED) {
-      float score = -INFINITY;
-      if (lse != -INFINITY) score = lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk));
-      oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
-    } else {
-      float best = -INFINITY, bests = 0.0f;
-      int bestv = -1;
-#pragma unroll
-      for (int i = 0; i < 32; i += 2) {
-        int v = v0 + 32 * (i >> 4) + (i & 15);   // even column: one word serves v and v+1
-        if (v >= V) continue;
-        uint64_t w = pair_word(rm.key2, (uint32_t)v >> 1);
-        uint32_t bb[2] = {(uint32_t)(w >> 32), (uint32_t)w};
-#pragma unroll
-        for (int e = 0; e < 2; e++) {
-          float sv = s[i + e];
-          if (v + e >= V || sv == -INFINITY) continue;
-          if (sv + gumbel_bound(bb[e]) + 1e-3f < best) continue;
-          float zz = sv + gumbel_bits(bb[e]);
-          if (better(zz, v + e, best, bestv)) { best = zz; bestv = v + e; bests = sv; }
-        }
-      }
-      float ob_ = __shfl_xor(best, 32, 64);
-      int ov = __shfl_xor(bestv, 32, 64);
-      float os = __shfl_xor(bests, 32, 64);
-      if (ov >= 0 && (bestv < 0 || better(ob_, ov, best, bestv))) { best = ob_; bestv = ov; bests = os; }
-      oa = make_float4(lse, best, __int_as_float(bestv), bests);
-    }
-    ob = make_float4(0, 0, 0, 0);
-  } else {  // RO_CORRECT: residual norm(max(0, p - q)) and the target-row fallback
-    float tt[32];
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-      int v = v0 + 32 * (i >> 4) + (i & 15);
-      tt[i] = (v < V) ? t[i] * invT : -INFINITY;
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 32; i++) mt = fmaxf(mt, tt[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    float st = 0.0f, mass = 0.0f;
-    const float mo = mt * LOG2E;
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-      st += (mt != -INFINITY) ? exp2f(fmaf(tt[i], LOG2E, -mo)) : tt[i];
-      float lp = tt[i] - rm.lse_p, lq = s[i] - rm.lse_q;
-      if (lp > lq) mass += exp2f(lp * LOG2E) - exp2f(lq * LOG2E);
-    }
-    st += __shfl_xor(st, 32, 64);
-    mass += __shfl_xor(mass, 32, 64);
-    const float lse_t = (mt == -INFINITY) ? st : mt + log2f(st) * LN2;
-    const float lmass = (mass > 0.0f) ? log2f(mass) * LN2 : -INFINITY;
-    if (NOISE == SPEC_NOISE_CHUNKED) {
-      float g = gumbel_bits(bits_at(rm.key1, (uint32_t)chunk));
-      oa = make_float4(lmass, lmass == -INFINITY ? -INFINITY : lmass + g, __int_as_float(chunk), 0.0f);
-      ob = make_float4(lse_t, lse_t == -INFINITY ? -INFINITY : lse_t + g, __int_as_float(chunk), 0.0f);
-    } else {
-      float br = -INFINITY, bp = -INFINITY;
-      int vr = -1, vp = -1;
-#pragma unroll
-      for (int i = 0; i < 32; i++) {
-        int v = v0 + 32 * (i >> 4) + (i & 15);
-        if (v >= V) continue;
-        float g = gumbel_bits(bits_at(rm.key2, (uint32_t)v));
-        float lp = tt[i] - rm.lse_p, lq = s[i] - rm.lse_q;
-        if (lp > lq) {
-          float sc = lp + logf(-expm1f(lq - lp)) + g;
-          if (better(sc, v, br, vr)) { br = sc; vr = v; }
-        }
-        if (tt[i] != -INFINITY) {
-          float sc = tt[i] + g;
-          if (better(sc, v, bp, vp)) { bp = sc; vp = v; }
-        }
-      }
-      float o1 = __shfl_xor(br, 32, 64);
-      int i1 = __shfl_xor(vr, 32, 64);
-      if (i1 >= 0 && (vr < 0 || better(o1, i1, br, vr))) { br = o1; vr = i1; }
-      float o2 = __shfl_xor(bp, 32, 64);
-      int i2 = __shfl_xor(vp, 32, 64);
-      if (i2 >= 0 && (vp < 0 || better(o2, i2, bp, vp))) { bp = o2; vp = i2; }
-      oa = make_float4(lmass, br, __int_as_float(vr), 0.0f);
-      ob = make_float4(lse_t, bp, __int_as_float(vp), 0.0f);
-    }
-  }
 }
 
 // merge of two partial records {log-mass, best score, best index, aux}
@@ -373,256 +249,630 @@ __device__ __forceinline__ float4 merge_part(float4 x, float4 y) {
   return r;
 }
 
-template <int DT, int NOISE, bool VEC>
-__device__ void kind_a(const Params& p, int s, const Lists& ls, int rb, int range, const int* bias_req,
-                       const int* bias_role) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA16[SUB][MAX_R + A_PAD];
-  __shared__ float sA32[DT == SPEC_FP32 ? SUB : 1][DT == SPEC_FP32 ? (MAX_R + 4) : 1];
-  __shared__ RowMeta meta[SUB];
-  __shared__ WaveOut red[NT / 64][SUB];
+__device__ __forceinline__ float4 empty_part() { return make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f); }
 
+// log-sum-exp of n values held by a lane and its partner lane (lane ^ 32); NaN-preserving
+template <int N>
+__device__ __forceinline__ float pair_lse(const float* x) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; i++) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, xor32f(mx));
+  float sum = 0.0f;
+  if (mx != -INFINITY) {
+    const float mo = mx * LOG2E;
+#pragma unroll
+    for (int i = 0; i < N; i++) sum += ex2(fmaf(x[i], LOG2E, -mo));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i++) sum += x[i];   // every value -inf or NaN: keep a NaN visible
+  }
+  sum += xor32f(sum);
+  return (mx == -INFINITY) ? sum : mx + lg2(sum) * LN2;
+}
+
+// best (score, index, aux) of a lane and its partner lane
+__device__ __forceinline__ void pair_best(float& sc, int& ix, float& aux) {
+  const float s2 = xor32f(sc);
+  const int i2 = xor32i(ix);
+  const float a2 = xor32f(aux);
+  if (i2 >= 0 && (ix < 0 || better(s2, i2, sc, ix))) {
+    sc = s2;
+    ix = i2;
+    aux = a2;
+  }
+}
+
+// 16 consecutive bf16 / fp32 values of a row as raw words (bf16: 8 words, fp32: 16 words)
+template <int DT>
+struct Raw16 {
+  u32x4 w[DT == SPEC_BF16 ? 2 : 4];
+};
+
+// 16 columns of one row per lane; the lanes of one load instruction span 32 rows, so these are
+// ordinary (temporal) loads: the other pieces of each cache line arrive from neighbouring
+// instructions through the caches
+template <int DT>
+__device__ __forceinline__ void raw_load(const void* row, int v, Raw16<DT>& r) {
+  const u32x4* q = (const u32x4*)((const char*)row + (size_t)v * (DT == SPEC_BF16 ? 2 : 4));
+#pragma unroll
+  for (int k = 0; k < (DT == SPEC_BF16 ? 2 : 4); k++) r.w[k] = q[k];
+}
+
+// as raw_load, for rows whose 16-byte pieces are each wholly inside or wholly past column V
+// (aligned rows, V % 8 == 0 for bf16, V % 4 == 0 for fp32): the pieces past V read as -inf
+template <int DT>
+__device__ __forceinline__ void raw_load_pred(const void* row, int v, int V, Raw16<DT>& r) {
+  const u32x4* q = (const u32x4*)((const char*)row + (size_t)v * (DT == SPEC_BF16 ? 2 : 4));
+  const uint32_t ninf = (DT == SPEC_BF16) ? 0xFF80FF80u : 0xFF800000u;
+  constexpr int per = (DT == SPEC_BF16) ? 8 : 4;
+#pragma unroll
+  for (int k = 0; k < (DT == SPEC_BF16 ? 2 : 4); k++) {
+    if (v + per * k < V) r.w[k] = q[k];
+    else r.w[k] = (u32x4){ninf, ninf, ninf, ninf};
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float raw_at(const Raw16<DT>& r, int i) {
+  if (DT == SPEC_BF16) {
+    const uint32_t w = r.w[i >> 3][(i >> 1) & 3];
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  return __uint_as_float(r.w[i >> 2][i & 3]);
+}
+
+// ------------------------------------------------------------------------------------------
+// kind A: bias rows (DRAFT / CORRECT) over 256 columns, up to 256 rows
+// ------------------------------------------------------------------------------------------
+struct WaveOut {        // one wave's result for one row over its 64 columns
+  float4 a;             // {log-mass, best score, best index (bits), aux}
+  float4 b;             // CORRECT: target-row fallback {lse, best score, best index, 0}
+};
+
+struct KindALds {
+  uint16_t sA[2][SUB][MAX_R + A_PAD];   // gathered A rows, double-buffered by sub-block (bf16)
+  RowMeta meta[RB];
+  WaveOut red[2][NT / 64][SUB];         // per-wave results, double-buffered by sub-block
+};
+
+// FLAT draft: best (s_v + G(key2, v)) over the lane's 32 columns, s in place in x[]
+__device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint64_t key2, float& best, int& bestv,
+                                            float& bests) {
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    const int v = v0 + 32 * (i >> 4) + (i & 15);
+    if (v >= V) continue;
+    const uint64_t w = pair_word(key2, (uint32_t)v >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const float sv = x[i + e];
+      const uint32_t bb = e ? (uint32_t)w : (uint32_t)(w >> 32);
+      if (v + e >= V || !(sv > -INFINITY)) continue;
+      if (sv + gumbel_bound(bb) + 1e-3f < best) continue;
+      const float zz = sv + gumbel_bits(bb);
+      if (better(zz, v + e, best, bestv)) {
+        best = zz;
+        bestv = v + e;
+        bests = sv;
+      }
+    }
+  }
+}
+
+// fp32 factors: Markov bias of the lane's columns by VALU dot products (small vocabularies)
+__device__ __forceinline__ void fp32_bias16(const Params& p, const RowMeta& rm, int vstart, int V, bool active,
+                                            float* x) {
+  const int R = p.R;
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const int v = vstart + q;
+    float a = 0.0f;
+    if (active && rm.prev >= 0 && v < V) {
+      const float* wr = (const float*)p.W + (size_t)v * R;
+      const float* ar = (const float*)p.A + (size_t)rm.prev * R;
+      for (int k = 0; k < R; k++) a = fmaf(ar[k], wr[k], a);
+    }
+    x[q] = a;
+  }
+}
+
+// A rows of one sub-block: thread t carries segments t, t+256, t+512, t+768 (16 bytes each)
+struct APrefetch {
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ void a_fetch(const Params& p, const RowMeta* meta, int rows_base, APrefetch& ap) {
+  const int R = p.R, segs = R / 8;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = threadIdx.x + NT * i;
+    u32x4 val = {0, 0, 0, 0};
+    if (e < SUB * segs) {
+      const int prev = meta[rows_base + e / segs].prev;
+      if (prev >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)prev * R + 8 * (e % segs));
+    }
+    ap.v[i] = val;
+  }
+}
+
+__device__ __forceinline__ void a_store(const Params& p, const APrefetch& ap, uint16_t (*sA)[MAX_R + A_PAD]) {
+  const int segs = p.R / 8;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = threadIdx.x + NT * i;
+    if (e < SUB * segs) *(u32x4*)&sA[e / segs][8 * (e % segs)] = ap.v[i];
+  }
+}
+
+// write the partials of one sub-block (rows rs0 .. rs0 + 31 of the item) from red[buf]
+__device__ __forceinline__ void flush_partials(const Params& p, const KindALds& L, int buf, int row0, int rs0,
+                                               int nrows, int range) {
+  if (threadIdx.x < SUB) {
+    const int r = threadIdx.x, rs = rs0 + r;
+    if (rs < nrows) {
+      const bool corr = L.meta[rs].role == RO_CORRECT;
+      float4 pa = L.red[buf][0][r].a;
+#pragma unroll
+      for (int w = 1; w < NT / 64; w++) pa = merge_part(pa, L.red[buf][w][r].a);
+      const int slot = row0 + rs;
+      p.part_bias[(size_t)slot * p.nrA + range] = pa;
+      if (corr) {
+        float4 pb = L.red[buf][0][r].b;
+#pragma unroll
+        for (int w = 1; w < NT / 64; w++) pb = merge_part(pb, L.red[buf][w][r].b);
+        p.part_bias2[(size_t)slot * p.nrA + range] = pb;
+      }
+    }
+  }
+}
+
+template <int DT, int NOISE, bool VEC>
+__device__ void kind_a(const Params& p, int s, const Lists& ls, int rb, int range, const uint16_t* bias_list,
+                       KindALds& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, h = lane >> 5;
   const int V = p.V, R = p.R, K = p.K;
-  const int vt0 = range * TILE_A;
-  const int vw = vt0 + 64 * wave;          // this wave's 64 columns: one noise chunk
+  const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
   const int chunk = vw / CHUNK;
   const int n_bias = ls.n_draft + ls.n_correct;
   const int row0 = rb * RB;
   const int nrows = min(RB, n_bias - row0);
-  const int T16 = R / 16;                  // MFMA k-steps (bf16)
+  const int nsb = (nrows + SUB - 1) / SUB;
+  const int T16 = R / 16;                      // MFMA k-steps (bf16)
+  const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
+  const int v0 = vw + 16 * h;                  // lane's first column in fragment 0
+  const bool full = VEC;                        // predicated vector loads of the lane's columns
+  const int kb = h * (R / 2);
+  int n_draft_rows = ls.n_draft - row0;        // DRAFT rows come first in the item, CORRECT rows after
+  n_draft_rows = n_draft_rows < 0 ? 0 : (n_draft_rows < nrows ? n_draft_rows : nrows);
 
-  // W fragments of this wave, resident for the whole item: the MFMA A-operand row i of
-  // fragment f is column vw + 32f + perm(i), perm chosen so that accumulator q of lane l holds
-  // column vw + 32f + 16*(l/32) + q.
+  // row metadata of the whole item, one row per thread
+  __syncthreads();
+  {
+    const int r = threadIdx.x;
+    RowMeta rm;
+    if (r < nrows) {
+      const int e = bias_list[row0 + r];
+      const int b = e >> 1;
+      const int role = (e & 1) ? RO_CORRECT : RO_DRAFT;
+      const int j = (role == RO_DRAFT) ? s : p.acc[b];
+      const uint64_t g = (uint64_t)(p.req_off + b);
+      rm.b = b;
+      rm.j = j;
+      rm.role = role;
+      rm.prev = (j == 0) ? (p.x0 ? p.x0[b] : -1) : p.xs[(size_t)b * K + j - 1];
+      rm.invT = 1.0f / p.temp[b];
+      rm.pad = 0.0f;
+      if (role == RO_DRAFT) {
+        rm.key1 = row_key(p.seed, g, (uint64_t)j, ST_DRAFT_C);
+        rm.key2 = row_key(p.seed, g, (uint64_t)j, ST_DRAFT);
+        rm.lse_p = 0.0f;
+        rm.lse_q = 0.0f;
+      } else {
+        rm.key1 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL_C);
+        rm.key2 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL);
+        rm.lse_p = p.lse_p[(size_t)b * (K + 1) + j];
+        rm.lse_q = p.lse_q[(size_t)b * K + j];
+      }
+    } else {
+      rm.b = 0;
+      rm.j = 0;
+      rm.role = 0;
+      rm.prev = -1;
+      rm.invT = 1.0f;
+      rm.lse_p = rm.lse_q = rm.pad = 0.0f;
+      rm.key1 = rm.key2 = 0;
+    }
+    L.meta[r] = rm;
+  }
+
+  // W fragments of this wave, resident for the whole item: MFMA A-operand row i of fragment f is
+  // column vw + 32f + perm(i), perm chosen so that accumulator q of lane l holds column
+  // vw + 32f + 16*(l/32) + q; lane half l/32 covers k in [R/2 * (l/32), R/2 * (l/32 + 1)).
   bf16x8 wf[2][16];
   if (DT == SPEC_BF16) {
-    const int i = m;
-    const int col_in = 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
-    const int kb = h * (R / 2);
+    const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 #pragma unroll
     for (int f = 0; f < 2; f++) {
       const int v = vw + 32 * f + col_in;
 #pragma unroll
       for (int t = 0; t < 16; t++) {
         if (t < T16) {
-          if (v < V) {
-            wf[f][t] = *(const bf16x8*)((const uint16_t*)p.W + (size_t)v * R + kb + 8 * t);
-          } else {
-            wf[f][t] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
-          }
+          if (v < V) wf[f][t] = *(const bf16x8*)((const uint16_t*)p.W + (size_t)v * R + kb + 8 * t);
+          else wf[f][t] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
         }
       }
     }
   }
+  __syncthreads();   // meta visible
 
-  for (int sb = 0; sb * SUB < nrows; sb++) {
-    const int rows_here = min(SUB, nrows - sb * SUB);
-    __syncthreads();
-    // row metadata
-    if (threadIdx.x < SUB) {
-      RowMeta rm;
-      const int r = threadIdx.x;
-      if (r < rows_here) {
-        const int b = bias_req[sb * SUB + r];
-        const int role = bias_role[sb * SUB + r];
-        const int j = (role == RO_DRAFT) ? s : p.acc[b];
-        const int prev = (j == 0) ? (p.x0 ? p.x0[b] : -1) : p.xs[(size_t)b * K + j - 1];
-        const uint64_t g = (uint64_t)(p.req_off + b);
-        rm.b = b;
-        rm.j = j;
-        rm.role = role;
-        rm.prev = prev;
-        rm.slot = row0 + sb * SUB + r;
-        rm.invT = 1.0f / p.temp[b];
-        if (role == RO_DRAFT) {
-          rm.key1 = row_key(p.seed, g, (uint64_t)j, ST_DRAFT_C);
-          rm.key2 = row_key(p.seed, g, (uint64_t)j, ST_DRAFT);
-          rm.lse_p = 0.0f;
-          rm.lse_q = 0.0f;
-        } else {
-          rm.key1 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL_C);
-          rm.key2 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL);
-          rm.lse_p = p.lse_p[(size_t)b * (K + 1) + j];
-          rm.lse_q = p.lse_q[(size_t)b * K + j];
+  // (1) sub-blocks holding only DRAFT rows, software-pipelined: the A rows and the lane's draft
+  //     logits of sub-block sb+1 are in flight while sub-block sb runs
+  const int nsb_draft = n_draft_rows / SUB;     // whole DRAFT sub-blocks
+  APrefetch ap;
+  Raw16<DT> nb0, nb1;
+  if (nsb_draft > 0) {
+    if (DT == SPEC_BF16) a_fetch(p, L.meta, 0, ap);
+    const RowMeta& r0 = L.meta[m];
+    if (full) {
+      const void* br = (const char*)p.base + ((size_t)r0.b * K + r0.j) * (size_t)V * esz;
+      raw_load_pred<DT>(br, v0, V, nb0);
+      raw_load_pred<DT>(br, v0 + 32, V, nb1);
+    }
+  }
+  for (int sb = 0; sb < nsb_draft; sb++) {
+    const int buf = sb & 1;
+    if (DT == SPEC_BF16) a_store(p, ap, L.sA[buf]);
+    const Raw16<DT> cb0 = nb0, cb1 = nb1;
+    __syncthreads();   // A rows of sb in LDS; red[buf ^ 1] of sb - 1 complete
+    if (sb > 0) flush_partials(p, L, buf ^ 1, row0, (sb - 1) * SUB, nrows, range);
+    if (sb + 1 < nsb_draft) {
+      if (DT == SPEC_BF16) a_fetch(p, L.meta, (sb + 1) * SUB, ap);
+      const RowMeta& rn = L.meta[(sb + 1) * SUB + m];
+      if (full) {
+        const void* br = (const char*)p.base + ((size_t)rn.b * K + rn.j) * (size_t)V * esz;
+        raw_load_pred<DT>(br, v0, V, nb0);
+        raw_load_pred<DT>(br, v0 + 32, V, nb1);
+      }
+    }
+    const RowMeta& rm = L.meta[sb * SUB + m];
+    const void* base_row = (const char*)p.base + ((size_t)rm.b * K + rm.j) * (size_t)V * esz;
+    float x[32];
+    if (DT == SPEC_BF16) {
+      f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      f32x16 acc1 = acc0;
+#pragma unroll
+      for (int t = 0; t < 16; t++) {
+        if (t < T16) {
+          const bf16x8 bop = *(const bf16x8*)&L.sA[buf][m][kb + 8 * t];
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, acc1, 0, 0, 0);
         }
-      } else {
-        rm.b = -1;
-        rm.j = 0;
-        rm.role = 0;
-        rm.prev = -1;
-        rm.slot = -1;
-        rm.invT = 1.0f;
-        rm.key1 = rm.key2 = 0;
-        rm.lse_p = rm.lse_q = 0.0f;
       }
-      meta[r] = rm;
-    }
-    __syncthreads();
-    // stage the gathered A rows of the sub-block (zeros for "no previous token")
-    if (DT == SPEC_BF16) {
-      const int segs = R / 8;   // 16-byte segments per row
-      for (int e = threadIdx.x; e < SUB * segs; e += NT) {
-        const int r = e / segs, sg = e % segs;
-        const int prev = meta[r].prev;
-        u32x4 val = {0, 0, 0, 0};
-        if (prev >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)prev * R + 8 * sg);
-        *(u32x4*)&sA16[r][8 * sg] = val;
+#pragma unroll
+      for (int q = 0; q < 16; q++) {
+        x[q] = acc0[q];
+        x[16 + q] = acc1[q];
       }
     } else {
-      for (int e = threadIdx.x; e < SUB * R; e += NT) {
-        const int r = e / R, k = e % R;
-        const int prev = meta[r].prev;
-        sA32[r][k] = (prev >= 0) ? ((const float*)p.A)[(size_t)prev * R + k] : 0.0f;
+      fp32_bias16(p, rm, v0, V, true, x);
+      fp32_bias16(p, rm, v0 + 32, V, true, x + 16);
+    }
+    const float invT = rm.invT;
+    if (full) {
+#pragma unroll
+      for (int q = 0; q < 16; q++) {
+        x[q] = (raw_at<DT>(cb0, q) + x[q]) * invT;
+        x[16 + q] = (raw_at<DT>(cb1, q) + x[16 + q]) * invT;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        const int v = v0 + 32 * (i >> 4) + (i & 15);
+        x[i] = (v < V) ? (load1<DT>(base_row, (size_t)v) + x[i]) * invT : -INFINITY;
       }
     }
-    __syncthreads();
+    const float lse = pair_lse<32>(x);
+    float4 oa;
+    if (NOISE == SPEC_NOISE_CHUNKED) {
+      const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse;
+      oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
+    } else {
+      float best = -INFINITY, bests = 0.0f;
+      int bestv = -1;
+      flat_best32(x, v0, V, rm.key2, best, bestv, bests);
+      pair_best(best, bestv, bests);
+      oa = make_float4(lse, best, __int_as_float(bestv), bests);
+    }
+    if (h == 0) L.red[buf][wave][m].a = oa;
+  }
+  __syncthreads();
+  if (nsb_draft > 0) flush_partials(p, L, (nsb_draft - 1) & 1, row0, (nsb_draft - 1) * SUB, nrows, range);
 
-    const RowMeta rm = meta[m];
-    const bool active = rm.role != 0;
-    // element loads of this lane's row: 16 columns per fragment
-    float z[32], tv[32];
-    const size_t brow = (size_t)(active ? rm.b : 0) * K + rm.j;
-    const void* base_row = (const char*)p.base + brow * (size_t)V * (DT == SPEC_FP32 ? 4 : 2);
-    const size_t trow = (size_t)(active ? rm.b : 0) * (K + 1) + rm.j;
-    const void* targ_row = (const char*)p.target + trow * (size_t)V * (DT == SPEC_FP32 ? 4 : 2);
-    const int v0 = vw + 16 * h;
-#pragma unroll
+  // (2) remaining sub-blocks (CORRECT rows, or the DRAFT / CORRECT boundary): one fragment at a
+  //     time with online reductions, element loads straight from memory
+  for (int sb = nsb_draft; sb * SUB < nrows; sb++) {
+    const int buf = sb & 1;
+    __syncthreads();   // previous users of sA[buf] / red[buf] are done
+    if (DT == SPEC_BF16) {
+      APrefetch ac;
+      a_fetch(p, L.meta, sb * SUB, ac);
+      a_store(p, ac, L.sA[buf]);
+    }
+    __syncthreads();
+    const RowMeta rm = L.meta[sb * SUB + m];
+    const int role = rm.role;
+    const void* base_row = (const char*)p.base + ((size_t)rm.b * K + rm.j) * (size_t)V * esz;
+    const void* targ_row = (const char*)p.target + ((size_t)rm.b * (K + 1) + rm.j) * (size_t)V * esz;
+    const bool corr = role == RO_CORRECT;
+    float md = -INFINITY, sd = 0.0f;     // draft-row log-mass (DRAFT lanes)
+    float mt = -INFINITY, st = 0.0f;     // target-row log-mass (CORRECT lanes)
+    float mass = 0.0f;                   // residual mass
+    float br = -INFINITY, bp = -INFINITY, bd = -INFINITY, bds = 0.0f;
+    int vr = -1, vp = -1, vd = -1;
+#pragma unroll 1
     for (int f = 0; f < 2; f++) {
-      float x16[16];
-      if (active) load16<DT, VEC>(base_row, v0 + 32 * f, V, x16);
+      float x[16], t[16];
+      if (DT == SPEC_BF16) {
+        f32x16 acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int q = 0; q < 16; q++) z[16 * f + q] = active ? x16[q] : -INFINITY;
-    }
-    const bool corr = rm.role == RO_CORRECT;
-    if (corr) {
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
-        float x16[16];
-        load16<DT, VEC>(targ_row, v0 + 32 * f, V, x16);
-#pragma unroll
-        for (int q = 0; q < 16; q++) tv[16 * f + q] = x16[q];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 32; q++) tv[q] = 0.0f;
-    }
-
-    // Markov bias for the lane's 32 columns
-    if (DT == SPEC_BF16) {
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
-        f32x16 accv = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-        const int kb = h * (R / 2);
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-          if (t < T16) {
-            bf16x8 bop = *(const bf16x8*)&sA16[m][kb + 8 * t];
-            accv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[f][t], bop, accv, 0, 0, 0);
+        for (int tt = 0; tt < 16; tt++) {
+          if (tt < T16) {
+            const bf16x8 bop = *(const bf16x8*)&L.sA[buf][m][kb + 8 * tt];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f == 0 ? wf[0][tt] : wf[1][tt], bop, acc, 0, 0, 0);
           }
         }
 #pragma unroll
-        for (int q = 0; q < 16; q++) z[16 * f + q] += accv[q];
+        for (int q = 0; q < 16; q++) x[q] = acc[q];
+      } else {
+        fp32_bias16(p, rm, v0 + 32 * f, V, role != 0, x);
       }
-    } else {
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
+      const int vf = v0 + 32 * f;
+      if (VEC) {
+        Raw16<DT> rbs, rts;
+        if (role) raw_load_pred<DT>(base_row, vf, V, rbs);
+        if (corr) raw_load_pred<DT>(targ_row, vf, V, rts);
 #pragma unroll
         for (int q = 0; q < 16; q++) {
-          const int v = v0 + 32 * f + q;
-          float a = 0.0f;
-          if (v < V) {
-            const float* wr = (const float*)p.W + (size_t)v * R;
-            for (int k = 0; k < R; k++) a = fmaf(sA32[m][k], wr[k], a);
+          x[q] = role ? (raw_at<DT>(rbs, q) + x[q]) * rm.invT : -INFINITY;
+          t[q] = corr ? raw_at<DT>(rts, q) * rm.invT : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+          const int v = vf + q;
+          const bool ok = role && v < V;
+          x[q] = ok ? (load1<DT>(base_row, (size_t)v) + x[q]) * rm.invT : -INFINITY;
+          t[q] = (ok && corr) ? load1<DT>(targ_row, (size_t)v) * rm.invT : -INFINITY;
+        }
+      }
+      // online log-mass of the draft values (DRAFT lanes) and of the target values (CORRECT lanes)
+      const float* y = corr ? t : x;
+      float fm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 16; q++) fm = fmaxf(fm, y[q]);
+      float& mm = corr ? mt : md;
+      float& ss = corr ? st : sd;
+      const float nm = fmaxf(mm, fm);
+      if (nm > -INFINITY) {
+        float acc_s = (mm > -INFINITY) ? ss * ex2((mm - nm) * LOG2E) : (ss != ss ? ss : 0.0f);
+#pragma unroll
+        for (int q = 0; q < 16; q++) acc_s += ex2((y[q] - nm) * LOG2E);
+        ss = acc_s;
+        mm = nm;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; q++) ss += (y[q] != y[q]) ? y[q] : 0.0f;   // NaN stays visible
+      }
+      if (corr) {
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+          const float lp = t[q] - rm.lse_p, lq = x[q] - rm.lse_q;
+          if (lp > lq) mass += ex2(lp * LOG2E) - ex2(lq * LOG2E);
+        }
+      }
+      if (NOISE == SPEC_NOISE_FLAT && role) {
+#pragma unroll
+        for (int q = 0; q < 16; q++) {
+          const int v = vf + q;
+          if (v >= V) continue;
+          const float g = gumbel_bits(bits_at(rm.key2, (uint32_t)v));
+          if (corr) {
+            const float lp = t[q] - rm.lse_p, lq = x[q] - rm.lse_q;
+            if (lp > lq) {
+              const float sc = lp + logf(-expm1f(lq - lp)) + g;
+              if (better(sc, v, br, vr)) { br = sc; vr = v; }
+            }
+            if (t[q] > -INFINITY && better(t[q] + g, v, bp, vp)) { bp = t[q] + g; vp = v; }
+          } else if (x[q] > -INFINITY && better(x[q] + g, v, bd, vd)) {
+            bd = x[q] + g;
+            vd = v;
+            bds = x[q];
           }
-          z[16 * f + q] += a;
         }
       }
     }
-
-    float4 oa = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f), ob = oa;
-    if (active) lane_bias_row<NOISE>(rm, z, tv, v0, V, chunk, oa, ob);
+    // pair-combine the online states (lane ^ 32 holds the other 16 columns of each fragment)
+    const float mm = corr ? mt : md, ss = corr ? st : sd;
+    const float m2 = xor32f(mm), s2 = xor32f(ss);
+    const float nm = fmaxf(mm, m2);
+    float lse;
+    if (nm > -INFINITY) {
+      const float a = (mm > -INFINITY) ? ss * ex2((mm - nm) * LOG2E) : (ss != ss ? ss : 0.0f);
+      const float c = (m2 > -INFINITY) ? s2 * ex2((m2 - nm) * LOG2E) : (s2 != s2 ? s2 : 0.0f);
+      lse = nm + lg2(a + c) * LN2;
+    } else {
+      lse = (ss != ss || s2 != s2) ? NAN : -INFINITY;
+    }
+    mass += xor32f(mass);
+    float dummy = 0.0f;
+    pair_best(br, vr, dummy);
+    pair_best(bp, vp, dummy);
+    pair_best(bd, vd, bds);
+    float4 oa = empty_part(), ob = empty_part();
+    if (role == RO_DRAFT) {
+      if (NOISE == SPEC_NOISE_CHUNKED) {
+        const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse;
+        oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
+      } else {
+        oa = make_float4(lse, bd, __int_as_float(vd), bds);
+      }
+    } else if (corr) {
+      const float lmass = (mass > 0.0f) ? lg2(mass) * LN2 : -INFINITY;
+      if (NOISE == SPEC_NOISE_CHUNKED) {
+        const float g = gumbel_bits(bits_at(rm.key1, (uint32_t)chunk));
+        oa = make_float4(lmass, lmass > -INFINITY ? lmass + g : -INFINITY, __int_as_float(chunk), 0.0f);
+        ob = make_float4(lse, lse > -INFINITY ? lse + g : -INFINITY, __int_as_float(chunk), 0.0f);
+      } else {
+        oa = make_float4(lmass, br, __int_as_float(vr), 0.0f);
+        ob = make_float4(lse, bp, __int_as_float(vp), 0.0f);
+      }
+    }
     if (h == 0) {
-      red[wave][m].a = oa;
-      red[wave][m].b = ob;
+      L.red[buf][wave][m].a = oa;
+      L.red[buf][wave][m].b = ob;
     }
     __syncthreads();
-    if (threadIdx.x < SUB && threadIdx.x < rows_here) {
-      const int r = threadIdx.x;
-      float4 pa = red[0][r].a, pb = red[0][r].b;
-#pragma unroll
-      for (int w = 1; w < NT / 64; w++) {
-        pa = merge_part(pa, red[w][r].a);
-        pb = merge_part(pb, red[w][r].b);
-      }
-      const int slot = meta[r].slot;
-      p.part_bias[(size_t)slot * p.nrA + range] = pa;
-      if (meta[r].role == RO_CORRECT) p.part_bias2[(size_t)slot * p.nrA + range] = pb;
-    }
+    flush_partials(p, L, buf, row0, sb * SUB, nrows, range);
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// kind B: plain target rows (LSEP / BONUS), 64 consecutive columns (one chunk) per thread
+// kind B: plain target rows (LSEP / BONUS), 128 consecutive columns (two chunks) per thread,
+// every load of the item issued before any arithmetic
 // ------------------------------------------------------------------------------------------
+// kind B layout: load k (0..15) of a thread covers 8 columns at 2048 k + 8 t of the item, so every
+// load instruction of a wave reads 1 KiB of contiguous memory; the 64 columns of a noise chunk
+// are the 8 values of 8 neighbouring lanes.
+template <int DT>
+struct Raw8 {
+  u32x4 w[DT == SPEC_BF16 ? 1 : 2];
+};
+
+template <int DT>
+__device__ __forceinline__ float raw8_at(const Raw8<DT>& r, int i) {
+  if (DT == SPEC_BF16) {
+    const uint32_t w = r.w[0][i >> 1];
+    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  return __uint_as_float(r.w[i >> 2][i & 3]);
+}
+
+
+constexpr int KB_LOADS = 16;   // loads of 8 columns per thread per kind-B item
+
 template <int DT, int NOISE, bool VEC>
-__device__ void kind_b(const Params& p, int s, int b, int pslot, int range) {
-  __shared__ float4 redb[NT / 64];
+__device__ void kind_b(const Params& p, int s, int b, int pslot, int range, float4* redb) {
   const int K = p.K, V = p.V;
-  const int role = p.roles[(s & 1) * p.B + b] & (RO_LSEP | RO_BONUS);
+  const int role = p.roles[(size_t)(s & 1) * p.B + b] & (RO_LSEP | RO_BONUS);
   const int j = s;   // LSEP verifies position s; BONUS reads row L_b == s
   const float invT = 1.0f / p.temp[b];
-  const size_t trow = (size_t)b * (K + 1) + j;
-  const void* row = (const char*)p.target + trow * (size_t)V * (DT == SPEC_FP32 ? 4 : 2);
-  const int c = range * (TILE_B / CHUNK) + threadIdx.x;
-  const int v0 = c * CHUNK;
-  float x[64];
+  const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
+  const void* row = (const char*)p.target + ((size_t)b * (K + 1) + j) * (size_t)V * esz;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vbase = range * TILE_B;
+  const int vt = vbase + 8 * threadIdx.x;           // + 2048 k
+  Raw8<DT> r[KB_LOADS];
+  if (VEC) {
+    // rows are 16-byte aligned and V % 8 == 0 (bf16) / V % 4 == 0 (fp32), so each 16-byte load
+    // is wholly inside or wholly past the row end: predicate the loads, pad with -inf
+    const uint32_t ninf = (DT == SPEC_BF16) ? 0xFF80FF80u : 0xFF800000u;
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    float x16[16];
-    load16<DT, VEC>(row, v0 + 16 * q, V, x16);
+    for (int k = 0; k < KB_LOADS; k++) {
+      const u32x4* q = (const u32x4*)((const char*)row + (size_t)(vt + 2048 * k) * esz);
 #pragma unroll
-    for (int i = 0; i < 16; i++) x[16 * q + i] = x16[i] * invT;
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 64; i++) mx = fmaxf(mx, x[i]);
-  float lse = 0.0f;
-  if (mx != -INFINITY) {
-    float sum = 0.0f;
-    const float mo = mx * LOG2E;
-#pragma unroll
-    for (int i = 0; i < 64; i++) sum += exp2f(fmaf(x[i], LOG2E, -mo));
-    lse = mx + log2f(sum) * LN2;
+      for (int u = 0; u < (DT == SPEC_BF16 ? 1 : 2); u++) {
+        const int vv = vt + 2048 * k + 4 * u;
+        if (vv < V) r[k].w[u] = __builtin_nontemporal_load(q + u);
+        else r[k].w[u] = (u32x4){ninf, ninf, ninf, ninf};
+      }
+    }
   } else {
+    // unaligned rows: the same layout filled element by element, -inf past the row end
+#pragma unroll 1
+    for (int k = 0; k < KB_LOADS; k++) {
 #pragma unroll
-    for (int i = 0; i < 64; i++) lse += x[i];   // every value -inf or NaN: keep a NaN visible
+      for (int i = 0; i < 8; i++) {
+        const int v = vt + 2048 * k + i;
+        const float x = (v < V) ? load1<DT>(row, (size_t)v) : -INFINITY;
+        if (DT == SPEC_BF16) {
+          const uint32_t hb = __float_as_uint(x) >> 16;   // exact: the value came from a bf16
+          const uint32_t w = r[k].w[0][i >> 1];
+          r[k].w[0][i >> 1] = (i & 1) ? ((w & 0xFFFFu) | (hb << 16)) : ((w & 0xFFFF0000u) | hb);
+        } else {
+          r[k].w[i >> 2][i & 3] = __float_as_uint(x);
+        }
+      }
+    }
   }
-  float4 part = make_float4(lse, -INFINITY, __int_as_float(-1), 0.0f);
+  const uint64_t g = (uint64_t)(p.req_off + b);
+  const float sc2 = invT * LOG2E;
+  // log-mass of each 64-column chunk (8 lanes x 8 values); the rounds are independent and every
+  // lane keeps the two chunks it owns: rounds k = lane % 8 and lane % 8 + 8
+  float own0 = -INFINITY, own1 = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KB_LOADS; k++) {
+    float mx = raw8_at<DT>(r[k], 0);
+#pragma unroll
+    for (int i = 1; i < 8; i++) mx = fmaxf(mx, raw8_at<DT>(r[k], i));
+    mx = max8(mx);
+    float sum = 0.0f;
+    if (mx != -INFINITY) {
+      const float mo = mx * sc2;
+#pragma unroll
+      for (int i = 0; i < 8; i++) sum += ex2(fmaf(raw8_at<DT>(r[k], i), sc2, -mo));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) sum += raw8_at<DT>(r[k], i);   // every value -inf or NaN: keep a NaN visible
+    }
+    sum = sum8(sum);
+    const float lse = (mx == -INFINITY) ? sum : mx * invT + lg2(sum) * LN2;
+    if ((lane & 7) == (k & 7)) {
+      if (k < 8) own0 = lse;
+      else own1 = lse;
+    }
+  }
+  float4 part = make_float4(lse2(own0, own1), -INFINITY, __int_as_float(-1), 0.0f);
   if (role == RO_BONUS) {
-    const uint64_t g = (uint64_t)(p.req_off + b);
     if (NOISE == SPEC_NOISE_CHUNKED) {
-      if (lse != -INFINITY) {
-        const uint64_t k1 = row_key(p.seed, g, (uint64_t)j, ST_BONUS_C);
-        part.y = lse + gumbel_bits(bits_at(k1, (uint32_t)c));
-        part.z = __int_as_float(c);
+      const uint64_t k1 = row_key(p.seed, g, (uint64_t)j, ST_BONUS_C);
+#pragma unroll
+      for (int o = 0; o < 2; o++) {
+        const float lse = o ? own1 : own0;
+        const int k = (lane & 7) + 8 * o;
+        const int c = (vbase + 2048 * k) / CHUNK + (lane >> 3) + 8 * wave;
+        if (lse > -INFINITY) {
+          const float sc = lse + gumbel_bits(bits_at(k1, (uint32_t)c));
+          if (better(sc, c, part.y, __float_as_int(part.z))) {
+            part.y = sc;
+            part.z = __int_as_float(c);
+          }
+        }
       }
     } else {
       const uint64_t k2 = row_key(p.seed, g, (uint64_t)j, ST_BONUS);
       float best = -INFINITY;
       int bv = -1;
-      for (int i = 0; i < 64; i += 2) {
-        const int v = v0 + i;
-        if (v >= V) break;
-        const uint64_t w = pair_word(k2, (uint32_t)v >> 1);
-        const uint32_t bb[2] = {(uint32_t)(w >> 32), (uint32_t)w};
+#pragma unroll 1
+      for (int k = 0; k < KB_LOADS; k++) {
+        const int v0 = vt + 2048 * k;
 #pragma unroll
-        for (int e = 0; e < 2; e++) {
-          const float sv = x[i + e];
-          if (v + e >= V || sv == -INFINITY) continue;
-          if (sv + gumbel_bound(bb[e]) + 1e-3f < best) continue;
-          const float zz = sv + gumbel_bits(bb[e]);
-          if (better(zz, v + e, best, bv)) { best = zz; bv = v + e; }
+        for (int i = 0; i < 8; i += 2) {
+          const int v = v0 + i;
+          const uint64_t w = pair_word(k2, (uint32_t)v >> 1);
+#pragma unroll
+          for (int e = 0; e < 2; e++) {
+            const float sv = raw8_at<DT>(r[k], i + e) * invT;
+            const uint32_t bb = e ? (uint32_t)w : (uint32_t)(w >> 32);
+            if (v + e >= V || !(sv > -INFINITY)) continue;
+            if (sv + gumbel_bound(bb) + 1e-3f < best) continue;
+            const float zz = sv + gumbel_bits(bb);
+            if (better(zz, v + e, best, bv)) {
+              best = zz;
+              bv = v + e;
+            }
+          }
         }
       }
       part.y = best;
@@ -639,52 +889,57 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range) {
     y.w = __shfl_xor(part.w, o, 64);
     part = merge_part(part, y);
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
   if (lane == 0) redb[wave] = part;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float4 r = redb[0];
+    float4 rr = redb[0];
 #pragma unroll
-    for (int w = 1; w < NT / 64; w++) r = merge_part(r, redb[w]);
-    p.part_plain[(size_t)pslot * p.nrB + range] = r;
+    for (int w = 1; w < NT / 64; w++) rr = merge_part(rr, redb[w]);
+    p.part_plain[(size_t)pslot * p.nrB + range] = rr;
+  }
+}
+
+// Row sweeps of one step.  Every workgroup rebuilds the step's row lists from the role bytes,
+// then takes work items grid-stride.  k_bias takes the bias rows (MFMA, W fragments resident, two
+// workgroups per CU); k_plain streams the target rows of LSEP / BONUS roles at high occupancy.
+// For k_bias, items i and i + 8 run on one XCD, and consecutive items on an XCD are the
+// row-blocks of one column range, so its W tile is shared in that XCD's L2.
+template <int DT, int NOISE, bool VEC>
+__global__ __launch_bounds__(NT, 2) void k_bias(Params p, int s) {
+  extern __shared__ uint16_t dyn_lists[];      // bias list [2B], then plain list [B]
+  __shared__ uint64_t scan_tmp[NT / 64];
+  __shared__ KindALds lds_a;
+  uint16_t* bias_list = dyn_lists;
+  uint16_t* plain_list = dyn_lists + 2 * p.B;
+  const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
+  const Lists ls = build_lists(p, roles, bias_list, plain_list, scan_tmp, true);
+  const int n_bias = ls.n_draft + ls.n_correct;
+  const int nrb = (n_bias + RB - 1) / RB;
+  const int nA = 8 * p.nrA_xcd * nrb;
+  for (int it = blockIdx.x; it < nA; it += gridDim.x) {
+    const int xcd = it & 7, local = it >> 3;
+    const int rb = local % nrb;
+    const int range = (local / nrb) * 8 + xcd;
+    if (range < p.nrA) kind_a<DT, NOISE, VEC>(p, s, ls, rb, range, bias_list, lds_a);
   }
 }
 
 template <int DT, int NOISE, bool VEC>
-__global__ __launch_bounds__(NT, 2) void k_sweep(Params p, int s) {
-  __shared__ int bias_req[RB];
-  __shared__ int bias_role[RB];
-  __shared__ int plain_req;
+__global__ __launch_bounds__(NT, 3) void k_plain(Params p, int s) {
+  extern __shared__ uint16_t dyn_lists[];
   __shared__ uint64_t scan_tmp[NT / 64];
+  __shared__ float4 redb[NT / 64];
+  uint16_t* bias_list = dyn_lists;
+  uint16_t* plain_list = dyn_lists + 2 * p.B;
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
-
-  // which item is this workgroup?
-  int kind, rb = 0, range = 0, pslot = -1;
-  if ((int)blockIdx.x < p.gridA) {
-    kind = 0;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int ri = local / p.nrb;
-    rb = local % p.nrb;
-    range = ri * 8 + xcd;   // all row-blocks of one column range run on one XCD, back to back
-  } else {
-    kind = 1;
-    const int id = blockIdx.x - p.gridA;
-    pslot = id / p.nrB;
-    range = id % p.nrB;
-  }
-  if (threadIdx.x == 0) plain_req = -1;
-  const Lists ls = build_lists(p, roles, kind == 0 ? rb * RB : 0, kind == 0 ? RB : 0, pslot, bias_req, bias_role,
-                               &plain_req, scan_tmp);
-  if (kind == 0) {
-    if (range >= p.nrA || rb * RB >= ls.n_draft + ls.n_correct) return;
-    kind_a<DT, NOISE, VEC>(p, s, ls, rb, range, bias_req, bias_role);
-  } else {
-    if (pslot >= ls.n_plain) return;
-    const int b = plain_req;
-    kind_b<DT, NOISE, VEC>(p, s, b, pslot, range);
+  const Lists ls = build_lists(p, roles, bias_list, plain_list, scan_tmp);
+  const int n_items = ls.n_plain * p.nrB;
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int pslot = it / p.nrB, range = it % p.nrB;
+    kind_b<DT, NOISE, VEC>(p, s, plain_list[pslot], pslot, range, redb);
   }
 }
-
 
 // ------------------------------------------------------------------------------------------
 // merge: one workgroup per request
@@ -727,46 +982,67 @@ __device__ __forceinline__ void wave_argmax(float& sc, int& ix, float& aux) {
   }
 }
 
-// scaled draft logit of column v: (base + A[prev] . W[v]) / T, bias accumulated in fp32
+// Markov bias of column v, the share of thread quarter q = 0..3 of the rank (fp32 accumulate)
 template <int DT>
-__device__ float draft_logit(const Params& p, const void* base_row, int prev, int v, float invT) {
-  float bias = 0.0f;
-  if (prev >= 0) {
-    const int R = p.R;
-    for (int k = 0; k < R; k++)
-      bias = fmaf(load1<DT>(p.A, (size_t)prev * R + k), load1<DT>(p.W, (size_t)v * R + k), bias);
+__device__ float bias_quarter(const Params& p, int prev, int v, int q) {
+  float a = 0.0f;
+  const int R = p.R;
+  if (prev < 0) return a;
+  if (DT == SPEC_BF16) {
+    const uint16_t* ar = (const uint16_t*)p.A + (size_t)prev * R;
+    const uint16_t* wr = (const uint16_t*)p.W + (size_t)v * R;
+    for (int k = 8 * q; k < R; k += 32) {
+      const u32x4 aw = *(const u32x4*)(ar + k);
+      const u32x4 ww = *(const u32x4*)(wr + k);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        a = fmaf(bf16_lo(aw[i]), bf16_lo(ww[i]), a);
+        a = fmaf(bf16_hi(aw[i]), bf16_hi(ww[i]), a);
+      }
+    }
+  } else {
+    const float* ar = (const float*)p.A + (size_t)prev * R;
+    const float* wr = (const float*)p.W + (size_t)v * R;
+    for (int k = q; k < R; k += 4) a = fmaf(ar[k], wr[k], a);
   }
-  return (load1<DT>(base_row, (size_t)v) + bias) * invT;
+  return a;
 }
 
 enum { L2_DRAFT = 0, L2_TARGET = 1, L2_RESIDUAL = 2 };
 
-// Level two of the CHUNKED sampler, run by wave 0: argmax over the columns of chunk c of
-// (score_v + G(key2, v)).  Returns the column and (in aux) its scaled draft logit for DRAFT.
+// Level two of the CHUNKED sampler over chunk c, whole workgroup: argmax over the chunk's
+// columns of (score_v + G(key2, v)); thread t works on column 64c + t/4 with a quarter of the
+// rank.  Returns the column (-1 if none) and, for DRAFT, its scaled draft logit in *aux_out.
 template <int DT>
 __device__ int level_two(const Params& p, int kind, int c, uint64_t key2, const void* base_row,
-                         const void* targ_row, int prev, float invT, float lse_p, float lse_q, float* aux_out) {
-  const int lane = threadIdx.x & 63;
-  const int v = c * CHUNK + lane;
+                         const void* targ_row, int prev, float invT, float lse_p, float lse_q, float* aux_out,
+                         float4* lds) {
+  const int q = threadIdx.x & 3;
+  const int v = c * CHUNK + (threadIdx.x >> 2);
+  const bool in = c >= 0 && v < p.V;
+  float bias = 0.0f;
+  if (in && kind != L2_TARGET) bias = bias_quarter<DT>(p, prev, v, q);
+  bias += __shfl_xor(bias, 1, 64);
+  bias += __shfl_xor(bias, 2, 64);
   float sc = -INFINITY, aux = 0.0f;
   int ix = -1;
-  if (c >= 0 && v < p.V) {
+  if (in && q == 0) {
     const float g = gumbel_bits(bits_at(key2, (uint32_t)v));
     if (kind == L2_DRAFT) {
-      const float sv = draft_logit<DT>(p, base_row, prev, v, invT);
-      if (sv != -INFINITY) {
+      const float sv = (load1<DT>(base_row, (size_t)v) + bias) * invT;
+      if (sv > -INFINITY) {
         sc = sv + g;
         ix = v;
         aux = sv;
       }
     } else if (kind == L2_TARGET) {
       const float tv = load1<DT>(targ_row, (size_t)v) * invT;
-      if (tv != -INFINITY) {
+      if (tv > -INFINITY) {
         sc = tv + g;
         ix = v;
       }
     } else {
-      const float sv = draft_logit<DT>(p, base_row, prev, v, invT);
+      const float sv = (load1<DT>(base_row, (size_t)v) + bias) * invT;
       const float tv = load1<DT>(targ_row, (size_t)v) * invT;
       const float lp = tv - lse_p, lq = sv - lse_q;
       if (lp > lq) {
@@ -776,15 +1052,27 @@ __device__ int level_two(const Params& p, int kind, int c, uint64_t key2, const 
     }
   }
   wave_argmax(sc, ix, aux);
-  if (aux_out) *aux_out = aux;
-  return ix;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = make_float4(sc, aux, __int_as_float(ix), 0.0f);
+  __syncthreads();
+  float bs = lds[0].x, ba = lds[0].y;
+  int bi = __float_as_int(lds[0].z);
+#pragma unroll
+  for (int w = 1; w < NT / 64; w++) {
+    const int i2 = __float_as_int(lds[w].z);
+    if (i2 >= 0 && (bi < 0 || better(lds[w].x, i2, bs, bi))) {
+      bs = lds[w].x;
+      bi = i2;
+      ba = lds[w].y;
+    }
+  }
+  if (aux_out) *aux_out = ba;
+  return bi;
 }
 
 template <int DT, int NOISE>
 __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
   __shared__ float4 red[NT / 64];
-  __shared__ int sh_tok;
-  __shared__ float sh_aux;
   const int b = blockIdx.x;
   const int B = p.B, K = p.K, V = p.V;
   const int roles = p.roles[(size_t)(s & 1) * B + b];
@@ -817,18 +1105,8 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
         const int prev = (s == 0) ? x0 : p.xs[(size_t)b * K + s - 1];
         const void* base_row = (const char*)p.base + ((size_t)b * K + s) * V * esz;
         const uint64_t key2 = row_key(p.seed, g, (uint64_t)s, ST_DRAFT);
-        if (threadIdx.x < 64) {
-          float aux;
-          const int x = level_two<DT>(p, L2_DRAFT, __float_as_int(tot.z), key2, base_row, nullptr, prev, invT, 0.f,
-                                      0.f, &aux);
-          if (threadIdx.x == 0) {
-            sh_tok = x;
-            sh_aux = aux;
-          }
-        }
-        __syncthreads();
-        x_s = sh_tok;
-        sx = sh_aux;
+        x_s = level_two<DT>(p, L2_DRAFT, __float_as_int(tot.z), key2, base_row, nullptr, prev, invT, 0.f, 0.f, &sx,
+                            red);
       } else {
         x_s = __float_as_int(tot.z);
         sx = tot.w;
@@ -883,13 +1161,8 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
       if (NOISE == SPEC_NOISE_CHUNKED) {
         const void* targ_row = (const char*)p.target + ((size_t)b * (K + 1) + s) * V * esz;
         const uint64_t key2 = row_key(p.seed, g, (uint64_t)s, ST_BONUS);
-        if (threadIdx.x < 64) {
-          const int y = level_two<DT>(p, L2_TARGET, __float_as_int(tot.z), key2, nullptr, targ_row, -1, invT, 0.f,
-                                      0.f, nullptr);
-          if (threadIdx.x == 0) sh_tok = y;
-        }
-        __syncthreads();
-        final_tok = sh_tok;
+        final_tok = level_two<DT>(p, L2_TARGET, __float_as_int(tot.z), key2, nullptr, targ_row, -1, invT, 0.f, 0.f,
+                                  nullptr, red);
       } else {
         final_tok = __float_as_int(tot.z);
       }
@@ -910,15 +1183,10 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
       const uint64_t key2 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL);
       const float lse_p = p.lse_p[(size_t)b * (K + 1) + j];
       const float lse_q = p.lse_q[(size_t)b * K + j];
-      if (threadIdx.x < 64) {
-        const int y = residual ? level_two<DT>(p, L2_RESIDUAL, __float_as_int(prim.z), key2, base_row, targ_row, prev,
-                                               invT, lse_p, lse_q, nullptr)
-                               : level_two<DT>(p, L2_TARGET, __float_as_int(sec.z), key2, nullptr, targ_row, -1, invT,
-                                               0.f, 0.f, nullptr);
-        if (threadIdx.x == 0) sh_tok = y;
-      }
-      __syncthreads();
-      final_tok = sh_tok;
+      final_tok = residual ? level_two<DT>(p, L2_RESIDUAL, __float_as_int(prim.z), key2, base_row, targ_row, prev,
+                                           invT, lse_p, lse_q, nullptr, red)
+                           : level_two<DT>(p, L2_TARGET, __float_as_int(sec.z), key2, nullptr, targ_row, -1, invT,
+                                           0.f, 0.f, nullptr, red);
     } else {
       final_tok = __float_as_int(residual ? prim.z : sec.z);
     }
@@ -1005,6 +1273,24 @@ static Layout layout(const spec_dims* d) {
   return l;
 }
 
+static int cu_count() {
+  static int ncu[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int n = (dev >= 0 && dev < 64) ? ncu[dev] : 0;
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev >= 0 && dev < 64) ncu[dev] = n;
+  }
+  return n;
+}
+
+// resident grids: k_bias holds two 256-thread workgroups per CU, k_plain three
+static int grid_for(int max_items, int per_cu) {
+  const int resident = per_cu * cu_count();
+  return max_items < resident ? max_items : resident;
+}
+
 static int arch_ok() {
   static int cache[64] = {0};   // 0 unknown, 1 gfx950, -1 other
   int dev = 0;
@@ -1017,8 +1303,8 @@ static int arch_ok() {
   return ok > 0 ? SPEC_OK : SPEC_E_ARCH;
 }
 
-// Kernel i of a cycle (0 = init, 1 + 2s = sweep of step s, 2 + 2s = merge of step s) may carry
-// a start/stop event pair, attached to its own dispatch packet.
+// Kernel i of a cycle (0 = init; 1 + 3s, 2 + 3s, 3 + 3s = bias sweep, plain sweep, merge of step s)
+// may carry a start/stop event pair, attached to its own dispatch.
 struct Timing {
   hipEvent_t* ev;
   int n;
@@ -1028,11 +1314,15 @@ struct Timing {
 
 template <int DT, int NOISE, bool VEC>
 static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const Timing& tm) {
+  const size_t lists = (size_t)6 * p.B;
   for (int s = 0; s <= p.K; s++) {
-    const int ks = 1 + 2 * s, km = 2 + 2 * s;
-    hipExtLaunchKernelGGL((k_sweep<DT, NOISE, VEC>), dim3(l.gridA + l.gridB), dim3(NT), 0, st, tm.start(ks),
-                          tm.stop(ks), 0, p, s);
-    hipExtLaunchKernelGGL((k_merge<DT, NOISE>), dim3(p.B), dim3(NT), 0, st, tm.start(km), tm.stop(km), 0, p, s);
+    const int k0 = 1 + 3 * s;
+    hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(grid_for(l.gridA, 2)), dim3(NT), lists, st, tm.start(k0),
+                          tm.stop(k0), 0, p, s);
+    hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 3)), dim3(NT), lists, st,
+                          tm.start(k0 + 1), tm.stop(k0 + 1), 0, p, s);
+    hipExtLaunchKernelGGL((k_merge<DT, NOISE>), dim3(p.B), dim3(NT), 0, st, tm.start(k0 + 2), tm.stop(k0 + 2), 0, p,
+                          s);
   }
 }
 
@@ -1151,7 +1441,7 @@ extern "C" int spec_cycle(const spec_dims* d, const void* base_logits, const voi
 
 extern "C" int spec_cycle_kernel_count(const spec_dims* d) {
   if (!dims_ok(d)) return 0;
-  return 1 + 2 * (d->K + 1);
+  return 1 + 3 * (d->K + 1);
 }
 
 extern "C" int spec_cycle_timed(const spec_dims* d, const void* base_logits, const void* target_logits,

@@ -59,7 +59,7 @@ enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };          /* element type of logits, A and
 enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
 
 typedef struct spec_dims {
-  int32_t B;      /* requests, >= 1                                                         */
+  int32_t B;      /* requests, 1..1024                                                      */
   int32_t K;      /* draft positions per request, 1..32                                     */
   int32_t V;      /* vocabulary size, >= 2                                                  */
   int32_t R;      /* Markov rank, 1..256; bf16 needs R % 16 == 0                            */
@@ -110,8 +110,9 @@ int spec_cycle(const spec_dims* d, const void* base_logits, const void* target_l
 /*
  * Profiling variant of spec_cycle for benchmarks: identical work and results, and every kernel
  * of the cycle is launched with a start/stop hipEvent_t pair attached to its own dispatch (no
- * extra queue packets).  Kernel i is: 0 = set-up and prefix cut, 1 + 2s = row sweep of step s,
- * 2 + 2s = per-request merge of step s, for s = 0..K.  `events` is a host array of
+ * extra queue packets).  Kernel i is: 0 = set-up and prefix cut; 1 + 3s = sweep of the Markov-biased
+ * rows of step s, 2 + 3s = sweep of the plain target rows of step s, 3 + 3s = per-request merge of
+ * step s, for s = 0..K.  `events` is a host array of
  * n_events >= 2 * spec_cycle_kernel_count(d) events created by the caller (hipEventCreate);
  * events[2i] / events[2i+1] bracket kernel i.  The caller reads hipEventElapsedTime after the
  * stream is synchronised.  Returns SPEC_E_INVAL when the array is missing or too short.
@@ -122,7 +123,7 @@ int spec_cycle_timed(const spec_dims* d, const void* base_logits, const void* ta
                      int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, void* workspace,
                      size_t workspace_bytes, spec_stream_t stream, void* const* events, int n_events);
 
-/* Number of kernels one spec_cycle call launches: 1 + 2 (K + 1); 0 for invalid dims. */
+/* Number of kernels one spec_cycle call launches: 1 + 3 (K + 1); 0 for invalid dims. */
 int spec_cycle_kernel_count(const spec_dims* d);
 
 /* Static description of an error code (never NULL). */
