@@ -77,6 +77,7 @@ struct Params {
   uint8_t* roles;      // [2][B], step parity
   int32_t* slots;      // [3][B]: bias slot of DRAFT row, bias slot of CORRECT row, plain slot
   int32_t* xs;         // [B][K]
+  uint64_t* kreq;      // [B] noise-key prefix of each request: first(first(seed) ^ global id)
   float* lse_q;        // [B][K]
   float* logq;         // [B][K]
   float* lse_p;        // [B][K+1]
@@ -145,6 +146,7 @@ __global__ void k_init(Params p) {
     L = j + 1;
   }
   p.L[b] = L;
+  p.kreq[b] = sm_first(sm_first(p.seed) ^ (uint64_t)(p.req_off + b));
   p.acc[b] = 0;
   p.phase[b] = valid ? PH_ALIVE : PH_INVALID;
   p.roles[b] = valid ? (uint8_t)(L > 0 ? (RO_DRAFT | RO_LSEP) : RO_BONUS) : (uint8_t)0;
@@ -330,11 +332,6 @@ struct WaveOut {        // one wave's result for one row over its 64 columns
   float4 b;             // CORRECT: target-row fallback {lse, best score, best index, 0}
 };
 
-struct KindALds {
-  uint16_t sA[2][SUB][MAX_R + A_PAD];   // gathered A rows, double-buffered by sub-block (bf16)
-  RowMeta meta[RB];
-  WaveOut red[2][NT / 64][SUB];         // per-wave results, double-buffered by sub-block
-};
 
 // FLAT draft: best (s_v + G(key2, v)) over the lane's 32 columns, s in place in x[]
 __device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint64_t key2, float& best, int& bestv,
@@ -377,103 +374,47 @@ __device__ __forceinline__ void fp32_bias16(const Params& p, const RowMeta& rm, 
   }
 }
 
-// A rows of one sub-block: thread t carries segments t, t+256, t+512, t+768 (16 bytes each)
-struct APrefetch {
-  u32x4 v[4];
+// ------------------------------------------------------------------------------------------
+// bias-row sweep, unit by unit.  A unit is (column range of 256, sub-block of 32 bias rows); the
+// units of a step are split evenly over the resident workgroups in range-major order, so a
+// workgroup reloads its W fragments only when it crosses into the next column range.
+// ------------------------------------------------------------------------------------------
+struct BiasLds {
+  uint16_t sA[SUB][MAX_R + A_PAD];   // gathered A rows of the current unit (bf16)
+  uint16_t sX[SUB][TILE_A + 8];      // draft logits of the current unit, 32 rows x 256 columns (bf16)
+  WaveOut red[NT / 64][SUB];         // per-wave results of the current unit
 };
 
-__device__ __forceinline__ void a_fetch(const Params& p, const RowMeta* meta, int rows_base, APrefetch& ap) {
-  const int R = p.R, segs = R / 8;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = threadIdx.x + NT * i;
-    u32x4 val = {0, 0, 0, 0};
-    if (e < SUB * segs) {
-      const int prev = meta[rows_base + e / segs].prev;
-      if (prev >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)prev * R + 8 * (e % segs));
-    }
-    ap.v[i] = val;
-  }
+__device__ __forceinline__ uint64_t key_of(const Params& p, int b, int pos, uint64_t stream) {
+  return sm_first(sm_first(p.kreq[b] ^ (uint64_t)pos) ^ stream);
 }
 
-__device__ __forceinline__ void a_store(const Params& p, const APrefetch& ap, uint16_t (*sA)[MAX_R + A_PAD]) {
-  const int segs = p.R / 8;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = threadIdx.x + NT * i;
-    if (e < SUB * segs) *(u32x4*)&sA[e / segs][8 * (e % segs)] = ap.v[i];
-  }
-}
-
-// write the partials of one sub-block (rows rs0 .. rs0 + 31 of the item) from red[buf]
-__device__ __forceinline__ void flush_partials(const Params& p, const KindALds& L, int buf, int row0, int rs0,
-                                               int nrows, int range) {
-  if (threadIdx.x < SUB) {
-    const int r = threadIdx.x, rs = rs0 + r;
-    if (rs < nrows) {
-      const bool corr = L.meta[rs].role == RO_CORRECT;
-      float4 pa = L.red[buf][0][r].a;
-#pragma unroll
-      for (int w = 1; w < NT / 64; w++) pa = merge_part(pa, L.red[buf][w][r].a);
-      const int slot = row0 + rs;
-      p.part_bias[(size_t)slot * p.nrA + range] = pa;
-      if (corr) {
-        float4 pb = L.red[buf][0][r].b;
-#pragma unroll
-        for (int w = 1; w < NT / 64; w++) pb = merge_part(pb, L.red[buf][w][r].b);
-        p.part_bias2[(size_t)slot * p.nrA + range] = pb;
-      }
-    }
-  }
-}
-
-template <int DT, int NOISE, bool VEC>
-__device__ void kind_a(const Params& p, int s, const Lists& ls, int rb, int range, const uint16_t* bias_list,
-                       KindALds& L) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m = lane & 31, h = lane >> 5;
-  const int V = p.V, R = p.R, K = p.K;
-  const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
-  const int chunk = vw / CHUNK;
+// metadata of every bias row of the step (rows past n_bias up to a whole sub-block are inactive)
+__device__ void fill_all_meta(const Params& p, int s, const Lists& ls, const uint16_t* bias_list, RowMeta* meta) {
   const int n_bias = ls.n_draft + ls.n_correct;
-  const int row0 = rb * RB;
-  const int nrows = min(RB, n_bias - row0);
-  const int nsb = (nrows + SUB - 1) / SUB;
-  const int T16 = R / 16;                      // MFMA k-steps (bf16)
-  const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
-  const int v0 = vw + 16 * h;                  // lane's first column in fragment 0
-  const bool full = VEC;                        // predicated vector loads of the lane's columns
-  const int kb = h * (R / 2);
-  int n_draft_rows = ls.n_draft - row0;        // DRAFT rows come first in the item, CORRECT rows after
-  n_draft_rows = n_draft_rows < 0 ? 0 : (n_draft_rows < nrows ? n_draft_rows : nrows);
-
-  // row metadata of the whole item, one row per thread
-  __syncthreads();
-  {
-    const int r = threadIdx.x;
+  const int n_rows = (n_bias + SUB - 1) / SUB * SUB;
+  for (int slot = threadIdx.x; slot < n_rows; slot += NT) {
     RowMeta rm;
-    if (r < nrows) {
-      const int e = bias_list[row0 + r];
+    if (slot < n_bias) {
+      const int e = bias_list[slot];
       const int b = e >> 1;
       const int role = (e & 1) ? RO_CORRECT : RO_DRAFT;
       const int j = (role == RO_DRAFT) ? s : p.acc[b];
-      const uint64_t g = (uint64_t)(p.req_off + b);
       rm.b = b;
       rm.j = j;
       rm.role = role;
-      rm.prev = (j == 0) ? (p.x0 ? p.x0[b] : -1) : p.xs[(size_t)b * K + j - 1];
+      rm.prev = (j == 0) ? (p.x0 ? p.x0[b] : -1) : p.xs[(size_t)b * p.K + j - 1];
       rm.invT = 1.0f / p.temp[b];
       rm.pad = 0.0f;
       if (role == RO_DRAFT) {
-        rm.key1 = row_key(p.seed, g, (uint64_t)j, ST_DRAFT_C);
-        rm.key2 = row_key(p.seed, g, (uint64_t)j, ST_DRAFT);
-        rm.lse_p = 0.0f;
-        rm.lse_q = 0.0f;
+        rm.key1 = key_of(p, b, j, ST_DRAFT_C);
+        rm.key2 = key_of(p, b, j, ST_DRAFT);
+        rm.lse_p = rm.lse_q = 0.0f;
       } else {
-        rm.key1 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL_C);
-        rm.key2 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL);
-        rm.lse_p = p.lse_p[(size_t)b * (K + 1) + j];
-        rm.lse_q = p.lse_q[(size_t)b * K + j];
+        rm.key1 = key_of(p, b, j, ST_RESIDUAL_C);
+        rm.key2 = key_of(p, b, j, ST_RESIDUAL);
+        rm.lse_p = p.lse_p[(size_t)b * (p.K + 1) + j];
+        rm.lse_q = p.lse_q[(size_t)b * p.K + j];
       }
     } else {
       rm.b = 0;
@@ -484,60 +425,141 @@ __device__ void kind_a(const Params& p, int s, const Lists& ls, int rb, int rang
       rm.lse_p = rm.lse_q = rm.pad = 0.0f;
       rm.key1 = rm.key2 = 0;
     }
-    L.meta[r] = rm;
+    meta[slot] = rm;
   }
+}
 
-  // W fragments of this wave, resident for the whole item: MFMA A-operand row i of fragment f is
-  // column vw + 32f + perm(i), perm chosen so that accumulator q of lane l holds column
-  // vw + 32f + 16*(l/32) + q; lane half l/32 covers k in [R/2 * (l/32), R/2 * (l/32 + 1)).
+// register prefetch of one unit: A rows (bf16) and, for the tiled path, the 32 x 256 draft-logit
+// tile, read with coalesced 16-byte loads (each wave instruction covers two 512-byte row pieces)
+struct UnitPrefetch {
+  u32x4 a[4];
+  u32x4 x[4];
+};
+
+template <bool TILE>
+__device__ __forceinline__ void unit_fetch(const Params& p, const RowMeta* meta, int range, UnitPrefetch& up) {
+  const int R = p.R, segs = R / 8;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = threadIdx.x + NT * i;
+    u32x4 val = {0, 0, 0, 0};
+    if (e < SUB * segs) {
+      const int prev = meta[e / segs].prev;
+      if (prev >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)prev * R + 8 * (e % segs));
+    }
+    up.a[i] = val;
+  }
+  if (TILE) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = range * TILE_A + 8 * (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 8 * i + 2 * wave + (lane >> 5);
+      const RowMeta& rm = meta[r];
+      u32x4 val = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // -inf past the row / no row
+      if (rm.role != 0 && col < p.V)
+        val = *(const u32x4*)((const uint16_t*)p.base + ((size_t)rm.b * p.K + rm.j) * (size_t)p.V + col);
+      up.x[i] = val;
+    }
+  }
+}
+
+template <bool TILE>
+__device__ __forceinline__ void unit_store(const Params& p, const UnitPrefetch& up, BiasLds& L) {
+  const int segs = p.R / 8;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = threadIdx.x + NT * i;
+    if (e < SUB * segs) *(u32x4*)&L.sA[e / segs][8 * (e % segs)] = up.a[i];
+  }
+  if (TILE) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 8 * i + 2 * wave + (lane >> 5);
+      *(u32x4*)&L.sX[r][8 * (lane & 31)] = up.x[i];
+    }
+  }
+}
+
+// partials of one finished unit from red (threads 0..31)
+__device__ __forceinline__ void unit_flush(const Params& p, const Lists& ls, const BiasLds& L, int slot0, int range) {
+  if (threadIdx.x < SUB) {
+    const int r = threadIdx.x, slot = slot0 + r;
+    if (slot < ls.n_draft + ls.n_correct) {
+      float4 pa = L.red[0][r].a;
+#pragma unroll
+      for (int w = 1; w < NT / 64; w++) pa = merge_part(pa, L.red[w][r].a);
+      p.part_bias[(size_t)slot * p.nrA + range] = pa;
+      if (slot >= ls.n_draft) {
+        float4 pb = L.red[0][r].b;
+#pragma unroll
+        for (int w = 1; w < NT / 64; w++) pb = merge_part(pb, L.red[w][r].b);
+        p.part_bias2[(size_t)slot * p.nrA + range] = pb;
+      }
+    }
+  }
+}
+
+template <int DT, int NOISE, bool VEC>
+__device__ void bias_sweep(const Params& p, int s, const Lists& ls, const RowMeta* meta, BiasLds& L) {
+  constexpr bool TILE = (DT == SPEC_BF16) && VEC;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, h = lane >> 5;
+  const int V = p.V, R = p.R, K = p.K;
+  const int T16 = R / 16;
+  const int kb = h * (R / 2);
+  const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
+  const int n_bias = ls.n_draft + ls.n_correct;
+  const int nsb = (n_bias + SUB - 1) / SUB;
+  const long long units = (long long)p.nrA * nsb;
+  const int u0 = (int)(units * blockIdx.x / gridDim.x);
+  const int u1 = (int)(units * (blockIdx.x + 1) / gridDim.x);
+  if (u0 >= u1) return;
+
   bf16x8 wf[2][16];
-  if (DT == SPEC_BF16) {
-    const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  int w_range = -1;
+  UnitPrefetch up;
+  unit_fetch<TILE>(p, meta + (u0 % nsb) * SUB, u0 / nsb, up);
+
+  for (int u = u0; u < u1; u++) {
+    const int range = u / nsb, sb = u % nsb;
+    __syncthreads();   // waves are done with the previous unit's LDS tiles and red
+    if (DT == SPEC_BF16) unit_store<TILE>(p, up, L);
+    if (u > u0) unit_flush(p, ls, L, ((u - 1) % nsb) * SUB, (u - 1) / nsb);
+    __syncthreads();   // this unit's tiles are in LDS; red is free
+    if (range != w_range && DT == SPEC_BF16) {
+      // W fragments: MFMA A-operand row i of fragment f is column vw + 32f + perm(i), perm chosen
+      // so that accumulator q of lane l holds column vw + 32f + 16*(l/32) + q; lane half l/32
+      // covers k in [R/2 * (l/32), R/2 * (l/32 + 1))
+      const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+      const int vw = range * TILE_A + 64 * wave;
 #pragma unroll
-    for (int f = 0; f < 2; f++) {
-      const int v = vw + 32 * f + col_in;
+      for (int f = 0; f < 2; f++) {
+        const int v = vw + 32 * f + col_in;
 #pragma unroll
-      for (int t = 0; t < 16; t++) {
-        if (t < T16) {
-          if (v < V) wf[f][t] = *(const bf16x8*)((const uint16_t*)p.W + (size_t)v * R + kb + 8 * t);
-          else wf[f][t] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        for (int t = 0; t < 16; t++) {
+          if (t < T16) {
+            if (v < V) wf[f][t] = *(const bf16x8*)((const uint16_t*)p.W + (size_t)v * R + kb + 8 * t);
+            else wf[f][t] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
+          }
         }
       }
     }
-  }
-  __syncthreads();   // meta visible
+    w_range = range;
+    if (u + 1 < u1) unit_fetch<TILE>(p, meta + ((u + 1) % nsb) * SUB, (u + 1) / nsb, up);
 
-  // (1) sub-blocks holding only DRAFT rows, software-pipelined: the A rows and the lane's draft
-  //     logits of sub-block sb+1 are in flight while sub-block sb runs
-  const int nsb_draft = n_draft_rows / SUB;     // whole DRAFT sub-blocks
-  APrefetch ap;
-  Raw16<DT> nb0, nb1;
-  if (nsb_draft > 0) {
-    if (DT == SPEC_BF16) a_fetch(p, L.meta, 0, ap);
-    const RowMeta& r0 = L.meta[m];
-    if (full) {
-      const void* br = (const char*)p.base + ((size_t)r0.b * K + r0.j) * (size_t)V * esz;
-      raw_load_pred<DT>(br, v0, V, nb0);
-      raw_load_pred<DT>(br, v0 + 32, V, nb1);
-    }
-  }
-  for (int sb = 0; sb < nsb_draft; sb++) {
-    const int buf = sb & 1;
-    if (DT == SPEC_BF16) a_store(p, ap, L.sA[buf]);
-    const Raw16<DT> cb0 = nb0, cb1 = nb1;
-    __syncthreads();   // A rows of sb in LDS; red[buf ^ 1] of sb - 1 complete
-    if (sb > 0) flush_partials(p, L, buf ^ 1, row0, (sb - 1) * SUB, nrows, range);
-    if (sb + 1 < nsb_draft) {
-      if (DT == SPEC_BF16) a_fetch(p, L.meta, (sb + 1) * SUB, ap);
-      const RowMeta& rn = L.meta[(sb + 1) * SUB + m];
-      if (full) {
-        const void* br = (const char*)p.base + ((size_t)rn.b * K + rn.j) * (size_t)V * esz;
-        raw_load_pred<DT>(br, v0, V, nb0);
-        raw_load_pred<DT>(br, v0 + 32, V, nb1);
-      }
-    }
-    const RowMeta& rm = L.meta[sb * SUB + m];
+    const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
+    const int chunk = vw / CHUNK;
+    const int v0 = vw + 16 * h;                  // lane's first column in fragment 0
+    const int slot0 = sb * SUB;
+    const bool any_correct = slot0 + SUB > ls.n_draft && slot0 < n_bias;   // uniform
+    const RowMeta& rm = meta[slot0 + m];
+    const int role = rm.role;
+    const float invT = rm.invT;
     const void* base_row = (const char*)p.base + ((size_t)rm.b * K + rm.j) * (size_t)V * esz;
+
+    // Markov bias of the lane's 32 columns
     float x[32];
     if (DT == SPEC_BF16) {
       f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -545,7 +567,7 @@ __device__ void kind_a(const Params& p, int s, const Lists& ls, int rb, int rang
 #pragma unroll
       for (int t = 0; t < 16; t++) {
         if (t < T16) {
-          const bf16x8 bop = *(const bf16x8*)&L.sA[buf][m][kb + 8 * t];
+          const bf16x8 bop = *(const bf16x8*)&L.sA[m][kb + 8 * t];
           acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, acc0, 0, 0, 0);
           acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, acc1, 0, 0, 0);
         }
@@ -556,186 +578,163 @@ __device__ void kind_a(const Params& p, int s, const Lists& ls, int rb, int rang
         x[16 + q] = acc1[q];
       }
     } else {
-      fp32_bias16(p, rm, v0, V, true, x);
-      fp32_bias16(p, rm, v0 + 32, V, true, x + 16);
+      fp32_bias16(p, rm, v0, V, role != 0, x);
+      fp32_bias16(p, rm, v0 + 32, V, role != 0, x + 16);
     }
-    const float invT = rm.invT;
-    if (full) {
+    // draft logits s = (base + bias) / T
+    if (TILE) {
+      const uint16_t* xr = &L.sX[m][64 * wave + 16 * h];
+      const u32x4 a0 = *(const u32x4*)xr, a1 = *(const u32x4*)(xr + 8);
+      const u32x4 c0 = *(const u32x4*)(xr + 32), c1 = *(const u32x4*)(xr + 40);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        x[2 * i] = (bf16_lo(a0[i]) + x[2 * i]) * invT;
+        x[2 * i + 1] = (bf16_hi(a0[i]) + x[2 * i + 1]) * invT;
+        x[8 + 2 * i] = (bf16_lo(a1[i]) + x[8 + 2 * i]) * invT;
+        x[8 + 2 * i + 1] = (bf16_hi(a1[i]) + x[8 + 2 * i + 1]) * invT;
+        x[16 + 2 * i] = (bf16_lo(c0[i]) + x[16 + 2 * i]) * invT;
+        x[16 + 2 * i + 1] = (bf16_hi(c0[i]) + x[16 + 2 * i + 1]) * invT;
+        x[24 + 2 * i] = (bf16_lo(c1[i]) + x[24 + 2 * i]) * invT;
+        x[24 + 2 * i + 1] = (bf16_hi(c1[i]) + x[24 + 2 * i + 1]) * invT;
+      }
+    } else if (VEC) {
+      Raw16<DT> r0, r1;
+      if (role) {
+        raw_load_pred<DT>(base_row, v0, V, r0);
+        raw_load_pred<DT>(base_row, v0 + 32, V, r1);
+      }
 #pragma unroll
       for (int q = 0; q < 16; q++) {
-        x[q] = (raw_at<DT>(cb0, q) + x[q]) * invT;
-        x[16 + q] = (raw_at<DT>(cb1, q) + x[16 + q]) * invT;
+        x[q] = role ? (raw_at<DT>(r0, q) + x[q]) * invT : -INFINITY;
+        x[16 + q] = role ? (raw_at<DT>(r1, q) + x[16 + q]) * invT : -INFINITY;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 32; i++) {
         const int v = v0 + 32 * (i >> 4) + (i & 15);
-        x[i] = (v < V) ? (load1<DT>(base_row, (size_t)v) + x[i]) * invT : -INFINITY;
+        x[i] = (role && v < V) ? (load1<DT>(base_row, (size_t)v) + x[i]) * invT : -INFINITY;
       }
     }
-    const float lse = pair_lse<32>(x);
-    float4 oa;
-    if (NOISE == SPEC_NOISE_CHUNKED) {
-      const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse;
-      oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
-    } else {
-      float best = -INFINITY, bests = 0.0f;
-      int bestv = -1;
-      flat_best32(x, v0, V, rm.key2, best, bestv, bests);
-      pair_best(best, bestv, bests);
-      oa = make_float4(lse, best, __int_as_float(bestv), bests);
-    }
-    if (h == 0) L.red[buf][wave][m].a = oa;
-  }
-  __syncthreads();
-  if (nsb_draft > 0) flush_partials(p, L, (nsb_draft - 1) & 1, row0, (nsb_draft - 1) * SUB, nrows, range);
 
-  // (2) remaining sub-blocks (CORRECT rows, or the DRAFT / CORRECT boundary): one fragment at a
-  //     time with online reductions, element loads straight from memory
-  for (int sb = nsb_draft; sb * SUB < nrows; sb++) {
-    const int buf = sb & 1;
-    __syncthreads();   // previous users of sA[buf] / red[buf] are done
-    if (DT == SPEC_BF16) {
-      APrefetch ac;
-      a_fetch(p, L.meta, sb * SUB, ac);
-      a_store(p, ac, L.sA[buf]);
-    }
-    __syncthreads();
-    const RowMeta rm = L.meta[sb * SUB + m];
-    const int role = rm.role;
-    const void* base_row = (const char*)p.base + ((size_t)rm.b * K + rm.j) * (size_t)V * esz;
-    const void* targ_row = (const char*)p.target + ((size_t)rm.b * (K + 1) + rm.j) * (size_t)V * esz;
-    const bool corr = role == RO_CORRECT;
-    float md = -INFINITY, sd = 0.0f;     // draft-row log-mass (DRAFT lanes)
-    float mt = -INFINITY, st = 0.0f;     // target-row log-mass (CORRECT lanes)
-    float mass = 0.0f;                   // residual mass
-    float br = -INFINITY, bp = -INFINITY, bd = -INFINITY, bds = 0.0f;
-    int vr = -1, vp = -1, vd = -1;
-#pragma unroll 1
-    for (int f = 0; f < 2; f++) {
-      float x[16], t[16];
-      if (DT == SPEC_BF16) {
-        f32x16 acc = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int tt = 0; tt < 16; tt++) {
-          if (tt < T16) {
-            const bf16x8 bop = *(const bf16x8*)&L.sA[buf][m][kb + 8 * tt];
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f == 0 ? wf[0][tt] : wf[1][tt], bop, acc, 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 16; q++) x[q] = acc[q];
-      } else {
-        fp32_bias16(p, rm, v0 + 32 * f, V, role != 0, x);
-      }
-      const int vf = v0 + 32 * f;
-      if (VEC) {
-        Raw16<DT> rbs, rts;
-        if (role) raw_load_pred<DT>(base_row, vf, V, rbs);
-        if (corr) raw_load_pred<DT>(targ_row, vf, V, rts);
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          x[q] = role ? (raw_at<DT>(rbs, q) + x[q]) * rm.invT : -INFINITY;
-          t[q] = corr ? raw_at<DT>(rts, q) * rm.invT : -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          const int v = vf + q;
-          const bool ok = role && v < V;
-          x[q] = ok ? (load1<DT>(base_row, (size_t)v) + x[q]) * rm.invT : -INFINITY;
-          t[q] = (ok && corr) ? load1<DT>(targ_row, (size_t)v) * rm.invT : -INFINITY;
-        }
-      }
-      // online log-mass of the draft values (DRAFT lanes) and of the target values (CORRECT lanes)
-      const float* y = corr ? t : x;
-      float fm = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 16; q++) fm = fmaxf(fm, y[q]);
-      float& mm = corr ? mt : md;
-      float& ss = corr ? st : sd;
-      const float nm = fmaxf(mm, fm);
-      if (nm > -INFINITY) {
-        float acc_s = (mm > -INFINITY) ? ss * ex2((mm - nm) * LOG2E) : (ss != ss ? ss : 0.0f);
-#pragma unroll
-        for (int q = 0; q < 16; q++) acc_s += ex2((y[q] - nm) * LOG2E);
-        ss = acc_s;
-        mm = nm;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; q++) ss += (y[q] != y[q]) ? y[q] : 0.0f;   // NaN stays visible
-      }
-      if (corr) {
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          const float lp = t[q] - rm.lse_p, lq = x[q] - rm.lse_q;
-          if (lp > lq) mass += ex2(lp * LOG2E) - ex2(lq * LOG2E);
-        }
-      }
-      if (NOISE == SPEC_NOISE_FLAT && role) {
-#pragma unroll
-        for (int q = 0; q < 16; q++) {
-          const int v = vf + q;
-          if (v >= V) continue;
-          const float g = gumbel_bits(bits_at(rm.key2, (uint32_t)v));
-          if (corr) {
-            const float lp = t[q] - rm.lse_p, lq = x[q] - rm.lse_q;
-            if (lp > lq) {
-              const float sc = lp + logf(-expm1f(lq - lp)) + g;
-              if (better(sc, v, br, vr)) { br = sc; vr = v; }
-            }
-            if (t[q] > -INFINITY && better(t[q] + g, v, bp, vp)) { bp = t[q] + g; vp = v; }
-          } else if (x[q] > -INFINITY && better(x[q] + g, v, bd, vd)) {
-            bd = x[q] + g;
-            vd = v;
-            bds = x[q];
-          }
-        }
-      }
-    }
-    // pair-combine the online states (lane ^ 32 holds the other 16 columns of each fragment)
-    const float mm = corr ? mt : md, ss = corr ? st : sd;
-    const float m2 = xor32f(mm), s2 = xor32f(ss);
-    const float nm = fmaxf(mm, m2);
-    float lse;
-    if (nm > -INFINITY) {
-      const float a = (mm > -INFINITY) ? ss * ex2((mm - nm) * LOG2E) : (ss != ss ? ss : 0.0f);
-      const float c = (m2 > -INFINITY) ? s2 * ex2((m2 - nm) * LOG2E) : (s2 != s2 ? s2 : 0.0f);
-      lse = nm + lg2(a + c) * LN2;
-    } else {
-      lse = (ss != ss || s2 != s2) ? NAN : -INFINITY;
-    }
-    mass += xor32f(mass);
-    float dummy = 0.0f;
-    pair_best(br, vr, dummy);
-    pair_best(bp, vp, dummy);
-    pair_best(bd, vd, bds);
     float4 oa = empty_part(), ob = empty_part();
-    if (role == RO_DRAFT) {
-      if (NOISE == SPEC_NOISE_CHUNKED) {
-        const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse;
-        oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
-      } else {
-        oa = make_float4(lse, bd, __int_as_float(vd), bds);
+    if (!any_correct) {
+      // ---- DRAFT rows only
+      const float lse = pair_lse<32>(x);
+      if (role) {
+        if (NOISE == SPEC_NOISE_CHUNKED) {
+          const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse;
+          oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
+        } else {
+          float best = -INFINITY, bests = 0.0f;
+          int bestv = -1;
+          flat_best32(x, v0, V, rm.key2, best, bestv, bests);
+          pair_best(best, bestv, bests);
+          oa = make_float4(lse, best, __int_as_float(bestv), bests);
+        }
       }
-    } else if (corr) {
-      const float lmass = (mass > 0.0f) ? lg2(mass) * LN2 : -INFINITY;
-      if (NOISE == SPEC_NOISE_CHUNKED) {
-        const float g = gumbel_bits(bits_at(rm.key1, (uint32_t)chunk));
-        oa = make_float4(lmass, lmass > -INFINITY ? lmass + g : -INFINITY, __int_as_float(chunk), 0.0f);
-        ob = make_float4(lse, lse > -INFINITY ? lse + g : -INFINITY, __int_as_float(chunk), 0.0f);
+    } else {
+      // ---- unit holding CORRECT rows: residual norm(max(0, p - q)) and its target-row fallback,
+      //      the target row streamed one 16-column fragment at a time with online reductions
+      const bool corr = role == RO_CORRECT;
+      const float lse_x = pair_lse<32>(x);   // draft log-mass (used by DRAFT lanes)
+      const void* targ_row = (const char*)p.target + ((size_t)rm.b * (K + 1) + rm.j) * (size_t)V * esz;
+      float mt = -INFINITY, st = 0.0f, mass = 0.0f;
+      float br = -INFINITY, bp = -INFINITY, bd = -INFINITY, bds = 0.0f;
+      int vr = -1, vp = -1, vd = -1;
+      if (NOISE == SPEC_NOISE_FLAT && role == RO_DRAFT) flat_best32(x, v0, V, rm.key2, bd, vd, bds);
+#pragma unroll
+      for (int f = 0; f < 2; f++) {
+        float t[16];
+        if (VEC) {
+          Raw16<DT> r0;
+          if (corr) raw_load_pred<DT>(targ_row, v0 + 32 * f, V, r0);
+#pragma unroll
+          for (int q = 0; q < 16; q++) t[q] = corr ? raw_at<DT>(r0, q) * invT : -INFINITY;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16; q++) {
+            const int v = v0 + 32 * f + q;
+            t[q] = (corr && v < V) ? load1<DT>(targ_row, (size_t)v) * invT : -INFINITY;
+          }
+        }
+        if (corr) {
+          float fm = -INFINITY;
+#pragma unroll
+          for (int q = 0; q < 16; q++) fm = fmaxf(fm, t[q]);
+          const float nm = fmaxf(mt, fm);
+          if (nm > -INFINITY) {
+            float acc_s = (mt > -INFINITY) ? st * ex2((mt - nm) * LOG2E) : (st != st ? st : 0.0f);
+#pragma unroll
+            for (int q = 0; q < 16; q++) acc_s += ex2((t[q] - nm) * LOG2E);
+            st = acc_s;
+            mt = nm;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 16; q++) st += (t[q] != t[q]) ? t[q] : 0.0f;   // NaN stays visible
+          }
+#pragma unroll
+          for (int q = 0; q < 16; q++) {
+            const float lp = t[q] - rm.lse_p, lq = x[16 * f + q] - rm.lse_q;
+            if (lp > lq) mass += ex2(lp * LOG2E) - ex2(lq * LOG2E);
+          }
+          if (NOISE == SPEC_NOISE_FLAT) {
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+              const int v = v0 + 32 * f + q;
+              if (v >= V) continue;
+              const float g = gumbel_bits(bits_at(rm.key2, (uint32_t)v));
+              const float lp = t[q] - rm.lse_p, lq = x[16 * f + q] - rm.lse_q;
+              if (lp > lq) {
+                const float sc = lp + logf(-expm1f(lq - lp)) + g;
+                if (better(sc, v, br, vr)) { br = sc; vr = v; }
+              }
+              if (t[q] > -INFINITY && better(t[q] + g, v, bp, vp)) { bp = t[q] + g; vp = v; }
+            }
+          }
+        }
+      }
+      // pair-combine (lane ^ 32 holds the other 16 columns of each fragment of the same row)
+      const float m2 = xor32f(mt), s2 = xor32f(st);
+      const float nm = fmaxf(mt, m2);
+      float lse_t;
+      if (nm > -INFINITY) {
+        const float a = (mt > -INFINITY) ? st * ex2((mt - nm) * LOG2E) : (st != st ? st : 0.0f);
+        const float c = (m2 > -INFINITY) ? s2 * ex2((m2 - nm) * LOG2E) : (s2 != s2 ? s2 : 0.0f);
+        lse_t = nm + lg2(a + c) * LN2;
       } else {
-        oa = make_float4(lmass, br, __int_as_float(vr), 0.0f);
-        ob = make_float4(lse, bp, __int_as_float(vp), 0.0f);
+        lse_t = (st != st || s2 != s2) ? NAN : -INFINITY;
+      }
+      mass += xor32f(mass);
+      float dummy = 0.0f;
+      pair_best(br, vr, dummy);
+      pair_best(bp, vp, dummy);
+      pair_best(bd, vd, bds);
+      if (role == RO_DRAFT) {
+        if (NOISE == SPEC_NOISE_CHUNKED) {
+          const float score = (lse_x > -INFINITY) ? lse_x + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse_x;
+          oa = make_float4(lse_x, score, __int_as_float(chunk), 0.0f);
+        } else {
+          oa = make_float4(lse_x, bd, __int_as_float(vd), bds);
+        }
+      } else if (corr) {
+        const float lmass = (mass > 0.0f) ? lg2(mass) * LN2 : -INFINITY;
+        if (NOISE == SPEC_NOISE_CHUNKED) {
+          const float g = gumbel_bits(bits_at(rm.key1, (uint32_t)chunk));
+          oa = make_float4(lmass, lmass > -INFINITY ? lmass + g : -INFINITY, __int_as_float(chunk), 0.0f);
+          ob = make_float4(lse_t, lse_t > -INFINITY ? lse_t + g : -INFINITY, __int_as_float(chunk), 0.0f);
+        } else {
+          oa = make_float4(lmass, br, __int_as_float(vr), 0.0f);
+          ob = make_float4(lse_t, bp, __int_as_float(vp), 0.0f);
+        }
       }
     }
     if (h == 0) {
-      L.red[buf][wave][m].a = oa;
-      L.red[buf][wave][m].b = ob;
+      L.red[wave][m].a = oa;
+      L.red[wave][m].b = ob;
     }
-    __syncthreads();
-    flush_partials(p, L, buf, row0, sb * SUB, nrows, range);
   }
+  __syncthreads();
+  unit_flush(p, ls, L, ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -905,24 +904,24 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
 // workgroups per CU); k_plain streams the target rows of LSEP / BONUS roles at high occupancy.
 // For k_bias, items i and i + 8 run on one XCD, and consecutive items on an XCD are the
 // row-blocks of one column range, so its W tile is shared in that XCD's L2.
+// dynamic LDS of k_bias: row metadata of up to 2B bias rows (rounded to a sub-block), then the
+// bias list [2B] and plain list [B]
+__host__ __device__ constexpr size_t bias_meta_bytes(int B) { return (size_t)(2 * B + SUB) * sizeof(RowMeta); }
+
 template <int DT, int NOISE, bool VEC>
-__global__ __launch_bounds__(NT, 2) void k_bias(Params p, int s) {
-  extern __shared__ uint16_t dyn_lists[];      // bias list [2B], then plain list [B]
+__global__ __launch_bounds__(NT, 1) void k_bias(Params p, int s) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
   __shared__ uint64_t scan_tmp[NT / 64];
-  __shared__ KindALds lds_a;
-  uint16_t* bias_list = dyn_lists;
-  uint16_t* plain_list = dyn_lists + 2 * p.B;
+  __shared__ BiasLds lds_a;
+  RowMeta* meta = (RowMeta*)dyn_bias;
+  uint16_t* bias_list = (uint16_t*)(dyn_bias + bias_meta_bytes(p.B));
+  uint16_t* plain_list = bias_list + 2 * p.B;
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
   const Lists ls = build_lists(p, roles, bias_list, plain_list, scan_tmp, true);
-  const int n_bias = ls.n_draft + ls.n_correct;
-  const int nrb = (n_bias + RB - 1) / RB;
-  const int nA = 8 * p.nrA_xcd * nrb;
-  for (int it = blockIdx.x; it < nA; it += gridDim.x) {
-    const int xcd = it & 7, local = it >> 3;
-    const int rb = local % nrb;
-    const int range = (local / nrb) * 8 + xcd;
-    if (range < p.nrA) kind_a<DT, NOISE, VEC>(p, s, ls, rb, range, bias_list, lds_a);
-  }
+  if (ls.n_draft + ls.n_correct == 0) return;
+  fill_all_meta(p, s, ls, bias_list, meta);
+  __syncthreads();
+  bias_sweep<DT, NOISE, VEC>(p, s, ls, meta, lds_a);
 }
 
 template <int DT, int NOISE, bool VEC>
@@ -1226,7 +1225,7 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
 // host side
 // ------------------------------------------------------------------------------------------
 struct Layout {
-  size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_lse_q, off_logq, off_lse_p, off_logp,
+  size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
       off_pbias, off_pbias2, off_pplain, total;
   int nrA, nrB, nrA_xcd, nrb, gridA, gridB;
 };
@@ -1262,6 +1261,7 @@ static Layout layout(const spec_dims* d) {
   l.off_roles = o; o = align256(o + 2 * B);
   l.off_slots = o; o = align256(o + 12 * B);
   l.off_xs = o; o = align256(o + 4 * B * K);
+  l.off_kreq = o; o = align256(o + 8 * B);
   l.off_lse_q = o; o = align256(o + 4 * B * K);
   l.off_logq = o; o = align256(o + 4 * B * K);
   l.off_lse_p = o; o = align256(o + 4 * B * (K + 1));
@@ -1317,7 +1317,8 @@ static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const
   const size_t lists = (size_t)6 * p.B;
   for (int s = 0; s <= p.K; s++) {
     const int k0 = 1 + 3 * s;
-    hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(grid_for(l.gridA, 2)), dim3(NT), lists, st, tm.start(k0),
+    hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(cu_count()), dim3(NT), bias_meta_bytes(p.B) + lists, st,
+                          tm.start(k0),
                           tm.stop(k0), 0, p, s);
     hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 3)), dim3(NT), lists, st,
                           tm.start(k0 + 1), tm.stop(k0 + 1), 0, p, s);
@@ -1404,6 +1405,7 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
   p.roles = (uint8_t*)(ws + l.off_roles);
   p.slots = (int32_t*)(ws + l.off_slots);
   p.xs = (int32_t*)(ws + l.off_xs);
+  p.kreq = (uint64_t*)(ws + l.off_kreq);
   p.lse_q = (float*)(ws + l.off_lse_q);
   p.logq = (float*)(ws + l.off_logq);
   p.lse_p = (float*)(ws + l.off_lse_p);
