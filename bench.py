@@ -55,7 +55,8 @@ def main():
     ap.add_argument("--config", default="longblock")
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--noise", choices=["chunked", "flat"], default="chunked")
-    ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the oracle's timed sample")
+    ap.add_argument("--cpu-requests", type=int, default=0,
+                    help="requests in the oracle's timed sample (0 = the whole batch of one cycle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -168,7 +169,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        n = min(args.cpu_requests, B)
+        n = min(args.cpu_requests, B) if args.cpu_requests > 0 else B
         sub = slice(0, n)
         tc = time.perf_counter()
         r = oracle.spec_cycle_ref(w.base[sub], w.target[sub], w.A, w.W, w.x0[sub], w.conf[sub], w.temp[sub],
@@ -176,7 +177,8 @@ def main():
         dt = time.perf_counter() - tc
         cpu = {"value": float(r["verify_len"][r["verify_len"] > 0].sum() / dt), "unit": "verified draft tokens/s",
                "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"first {n} of {B} requests of the same cycle ({dt:.1f} s wall, fp64 C + OpenMP)"}
+               "sample": f"first {n} of {B} requests of one cycle of the same workload ({dt:.1f} s wall, "
+                         f"fp64 C + OpenMP)"}
 
     line = {
         "metric": METRIC, "value": value, "unit": "verified draft tokens/s", "n_gpus": 1, "steps": args.steps,
