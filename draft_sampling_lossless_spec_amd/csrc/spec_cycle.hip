@@ -38,11 +38,9 @@ enum : int { RO_DRAFT = 1, RO_CORRECT = 2, RO_LSEP = 4, RO_BONUS = 8 };
 enum : int { PH_ALIVE = 0, PH_REJECTED = 1, PH_DONE = 2, PH_INVALID = 3 };
 
 constexpr int NT = 256;             // threads per workgroup
-constexpr int SUB = 32;             // bias rows per MFMA sub-block
-constexpr int NSUB = 8;             // sub-blocks per kind-A item
-constexpr int RB = SUB * NSUB;      // bias rows per kind-A item
-constexpr int TILE_A = 256;         // vocabulary columns per kind-A item: 4 waves x 64
-constexpr int TILE_B = NT * 2 * CHUNK;  // vocabulary columns per kind-B item: two chunks per thread
+constexpr int SUB = 32;             // bias slots per MFMA sub-block
+constexpr int TILE_A = 256;         // vocabulary columns per bias-row unit: 4 waves x 64
+constexpr int TILE_B = NT * 2 * CHUNK;  // vocabulary columns per plain-row item: two chunks per thread
 constexpr int MAX_B = 1024;
 constexpr int MAX_K = 32;
 constexpr int MAX_R = 256;
@@ -82,10 +80,11 @@ struct Params {
   float* logq;         // [B][K]
   float* lse_p;        // [B][K+1]
   float* logp;         // [B][K]
-  float4* part_bias;   // [2B][nrA]
-  float4* part_bias2;  // [2B][nrA]  CORRECT rows: target-row fallback
+  float4* part_bias;   // [bias slots][nrA]
+  float4* part_bias2;  // [bias slots][nrA]  CORRECT rows: target-row fallback
   float4* part_plain;  // [B][nrB]
-  int nrA, nrB, nrA_xcd, nrb, gridA;
+  const u32x4* konst;  // [2]: 16 zero bytes, then 8 bf16 -inf (stand-in source of masked tile loads)
+  int nrA, nrB;
 };
 
 // ------------------------------------------------------------------------------------------
@@ -131,6 +130,10 @@ __device__ __forceinline__ void load16(const void* row, int v, int V, float (&x)
 // step-0 set-up: validation, prefix cut, state, output defaults
 // ------------------------------------------------------------------------------------------
 __global__ void k_init(Params p) {
+  if (blockIdx.x == 0 && threadIdx.x < 2) {
+    const uint32_t w = threadIdx.x ? 0xFF80FF80u : 0u;
+    ((u32x4*)p.konst)[threadIdx.x] = (u32x4){w, w, w, w};
+  }
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= p.B) return;
   const int K = p.K;
@@ -164,6 +167,7 @@ __global__ void k_init(Params p) {
 // ------------------------------------------------------------------------------------------
 // block-wide exclusive scan of packed counters (three 16-bit lanes in a uint64)
 // ------------------------------------------------------------------------------------------
+template <int NTH>
 __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* tmp, uint64_t* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint64_t x = v;
@@ -176,7 +180,7 @@ __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* tmp, uint64_t* total) 
   __syncthreads();
   uint64_t off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < NT / 64; i++) {
+  for (int i = 0; i < NTH / 64; i++) {
     uint64_t t = tmp[i];
     off += (i < w) ? t : 0;
     tot += t;
@@ -186,23 +190,52 @@ __device__ uint64_t block_excl_scan(uint64_t v, uint64_t* tmp, uint64_t* total) 
   return off + x - v;
 }
 
-struct RowMeta {       // one bias row of a kind-A item, staged in LDS
-  int b, j, role, prev;
-  float invT, lse_p, lse_q, pad;
-  uint64_t key1, key2;
-};
-
 struct Lists {
   int n_draft, n_correct, n_plain;
+  int c0;     // first CORRECT slot: n_draft rounded up to a whole sub-block, so no sub-block mixes roles
+  int n_sb;   // bias sub-blocks of SUB slots
 };
 
+constexpr uint16_t NO_ROW = 0xFFFF;   // bias slot without a row (alignment gap or tail)
+
+// bias-list capacity: 2B rows plus the two alignment gaps
+__host__ __device__ constexpr int bias_slots_max(int B) { return 2 * B + 2 * SUB; }
+
+// One request's bias-row inputs at step s, staged in LDS by every bias-sweep workgroup.  A DRAFT
+// row is position s; a CORRECT row is position s - 1 (the position rejected at step s - 1).  Every
+// field is a plain load indexed by (b, s), so all of them are issued at once.
+struct ReqMeta {
+  int prev_d;        // token before position s (x0 at s = 0); -1 = no Markov bias
+  int prev_c;        // token before position s - 1
+  float invT;
+  float lse_p_c;     // log-normalisers of the target and draft rows at position s - 1
+  float lse_q_c;
+  uint32_t key_d[2]; // sweep noise key of the DRAFT row (chunk stream for CHUNKED, index stream for
+                     // FLAT), low word first
+  uint32_t key_c[2]; // sweep noise key of the CORRECT row
+};
+
+__device__ __forceinline__ void put_key(uint32_t (&k)[2], uint64_t v) {
+  k[0] = (uint32_t)v;
+  k[1] = (uint32_t)(v >> 32);
+}
+__device__ __forceinline__ uint64_t get_key(const uint32_t (&k)[2]) { return (uint64_t)k[0] | ((uint64_t)k[1] << 32); }
+
+__device__ __forceinline__ uint64_t key_from(uint64_t kreq, int pos, uint64_t stream) {
+  return sm_first(sm_first(kreq ^ (uint64_t)pos) ^ stream);
+}
+
 // Scan the role bytes of step s into the compact row lists of this step, in LDS:
-//   bias_list[i]  = (request << 1) | (1 if CORRECT)  for bias slot i (DRAFT rows first, then CORRECT)
-//   plain_list[i] = request                          for plain slot i (LSEP or BONUS)
-// Workgroup 0 also publishes every request's slots for the merge kernel.
-__device__ Lists build_lists(const Params& p, const uint8_t* roles, uint16_t* bias_list, uint16_t* plain_list,
-                             uint64_t* tmp, bool publish_slots = false) {
-  const int per = (p.B + NT - 1) / NT;
+//   bias_list[i]  = (request << 1) | (1 if CORRECT): DRAFT rows in [0, n_draft), CORRECT rows in
+//                   [c0, c0 + n_correct), NO_ROW in the gap and the tail up to n_sb * SUB
+//   plain_list[i] = request, for plain slot i (LSEP or BONUS)
+// With `req`, every request's bias-row inputs are staged too; their loads go out with the role
+// loads, so the prologue costs one memory latency.  Workgroup 0 of a publishing kernel also writes
+// every request's slots for the merge kernel.
+template <int NOISE, int NTH>
+__device__ Lists build_lists(const Params& p, int s, const uint8_t* roles, uint16_t* bias_list, uint16_t* plain_list,
+                             uint64_t* tmp, ReqMeta* req, bool publish_slots) {
+  const int per = (p.B + NTH - 1) / NTH;
   const int b0 = threadIdx.x * per;
   uint64_t cnt = 0;
   for (int i = 0; i < per; i++) {
@@ -211,14 +244,32 @@ __device__ Lists build_lists(const Params& p, const uint8_t* roles, uint16_t* bi
       const int r = roles[b];
       cnt += (uint64_t)((r & RO_DRAFT) ? 1 : 0) | ((uint64_t)((r & RO_CORRECT) ? 1 : 0) << 16) |
              ((uint64_t)((r & (RO_LSEP | RO_BONUS)) ? 1 : 0) << 32);
+      if (req) {
+        // read whether or not the request has a bias row this step (the values are then unused)
+        const int x0 = p.x0 ? p.x0[b] : -1;
+        const int32_t* xr = p.xs + (size_t)b * p.K;
+        const int jc = s > 0 ? s - 1 : 0;
+        ReqMeta m;
+        m.prev_d = (s == 0) ? x0 : xr[s - 1];
+        m.prev_c = (s <= 1) ? x0 : xr[s - 2];
+        m.invT = 1.0f / p.temp[b];
+        m.lse_p_c = p.lse_p[(size_t)b * (p.K + 1) + jc];
+        m.lse_q_c = p.lse_q[(size_t)b * p.K + jc];
+        const uint64_t kr = p.kreq[b];
+        put_key(m.key_d, key_from(kr, s, NOISE == SPEC_NOISE_CHUNKED ? ST_DRAFT_C : ST_DRAFT));
+        put_key(m.key_c, key_from(kr, jc, NOISE == SPEC_NOISE_CHUNKED ? ST_RESIDUAL_C : ST_RESIDUAL));
+        req[b] = m;
+      }
     }
   }
   uint64_t tot;
-  const uint64_t pre = block_excl_scan(cnt, tmp, &tot);
+  const uint64_t pre = block_excl_scan<NTH>(cnt, tmp, &tot);
   Lists ls;
   ls.n_draft = (int)(tot & 0xFFFF);
   ls.n_correct = (int)((tot >> 16) & 0xFFFF);
   ls.n_plain = (int)((tot >> 32) & 0xFFFF);
+  ls.c0 = (ls.n_draft + SUB - 1) / SUB * SUB;
+  ls.n_sb = (ls.c0 + ls.n_correct + SUB - 1) / SUB;
   int d = (int)(pre & 0xFFFF), c = (int)((pre >> 16) & 0xFFFF), q = (int)((pre >> 32) & 0xFFFF);
   const bool publish = (blockIdx.x == 0) && publish_slots;
   for (int i = 0; i < per; i++) {
@@ -227,13 +278,19 @@ __device__ Lists build_lists(const Params& p, const uint8_t* roles, uint16_t* bi
     const int r = roles[b];
     int sd = -1, sc = -1, sp = -1;
     if (r & RO_DRAFT) { sd = d++; bias_list[sd] = (uint16_t)(b << 1); }
-    if (r & RO_CORRECT) { sc = ls.n_draft + c++; bias_list[sc] = (uint16_t)((b << 1) | 1); }
+    if (r & RO_CORRECT) { sc = ls.c0 + c++; bias_list[sc] = (uint16_t)((b << 1) | 1); }
     if (r & (RO_LSEP | RO_BONUS)) { sp = q++; plain_list[sp] = (uint16_t)b; }
     if (publish) {
       p.slots[b] = sd;
       p.slots[p.B + b] = sc;
       p.slots[2 * p.B + b] = sp;
     }
+  }
+  if (threadIdx.x < SUB) {
+    const int g = ls.n_draft + threadIdx.x;
+    if (g < ls.c0) bias_list[g] = NO_ROW;
+    const int t = ls.c0 + ls.n_correct + threadIdx.x;
+    if (t < ls.n_sb * SUB) bias_list[t] = NO_ROW;
   }
   __syncthreads();
   return ls;
@@ -325,22 +382,50 @@ __device__ __forceinline__ float raw_at(const Raw16<DT>& r, int i) {
 }
 
 // ------------------------------------------------------------------------------------------
-// kind A: bias rows (DRAFT / CORRECT) over 256 columns, up to 256 rows
+// bias rows (DRAFT / CORRECT): the Markov bias A[prev] . W of every column, never written out,
+// plus the element-wise work of the row.  A unit is (column range of 256, sub-block of 32 bias
+// slots); a sub-block holds one role only.  The units of a step are split evenly over one
+// workgroup per CU in range-major order, so a workgroup reloads its W fragments only when it
+// crosses into the next column range.
 // ------------------------------------------------------------------------------------------
-struct WaveOut {        // one wave's result for one row over its 64 columns
+struct WaveOut {        // one wave's result for one row over its 64 columns (one noise chunk)
   float4 a;             // {log-mass, best score, best index (bits), aux}
   float4 b;             // CORRECT: target-row fallback {lse, best score, best index, 0}
 };
 
+// the bias row of one slot, resolved from the lists and the per-request table
+struct RowMeta {
+  int b, j, prev;
+  bool active, corr;
+  float invT, lse_p, lse_q;
+  uint64_t key;
+};
 
-// FLAT draft: best (s_v + G(key2, v)) over the lane's 32 columns, s in place in x[]
-__device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint64_t key2, float& best, int& bestv,
+__device__ __forceinline__ RowMeta row_meta(const uint16_t* bias_list, const ReqMeta* req, int s, int slot) {
+  RowMeta rm;
+  const uint16_t e = bias_list[slot];
+  rm.active = e != NO_ROW;
+  rm.corr = rm.active && (e & 1);
+  rm.b = rm.active ? (e >> 1) : 0;
+  rm.j = rm.corr ? s - 1 : s;
+  const ReqMeta& m = req[rm.b];
+  rm.prev = !rm.active ? -1 : (rm.corr ? m.prev_c : m.prev_d);
+  rm.invT = rm.active ? m.invT : 1.0f;
+  rm.lse_p = rm.corr ? m.lse_p_c : 0.0f;
+  rm.lse_q = rm.corr ? m.lse_q_c : 0.0f;
+  rm.key = rm.corr ? get_key(m.key_c) : get_key(m.key_d);
+  return rm;
+}
+
+// FLAT draft: best (s_v + G(key, v)) over the lane's 32 columns (element i is column
+// v0 + 32 (i / 16) + i % 16), s in x[]
+__device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint64_t key, float& best, int& bestv,
                                             float& bests) {
 #pragma unroll
   for (int i = 0; i < 32; i += 2) {
     const int v = v0 + 32 * (i >> 4) + (i & 15);
     if (v >= V) continue;
-    const uint64_t w = pair_word(key2, (uint32_t)v >> 1);
+    const uint64_t w = pair_word(key, (uint32_t)v >> 1);
 #pragma unroll
     for (int e = 0; e < 2; e++) {
       const float sv = x[i + e];
@@ -357,384 +442,442 @@ __device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint6
   }
 }
 
-// fp32 factors: Markov bias of the lane's columns by VALU dot products (small vocabularies)
-__device__ __forceinline__ void fp32_bias16(const Params& p, const RowMeta& rm, int vstart, int V, bool active,
-                                            float* x) {
-  const int R = p.R;
-#pragma unroll
-  for (int q = 0; q < 16; q++) {
-    const int v = vstart + q;
-    float a = 0.0f;
-    if (active && rm.prev >= 0 && v < V) {
-      const float* wr = (const float*)p.W + (size_t)v * R;
-      const float* ar = (const float*)p.A + (size_t)rm.prev * R;
-      for (int k = 0; k < R; k++) a = fmaf(ar[k], wr[k], a);
+// DRAFT row over the 64 columns of a lane pair (lanes l and l ^ 32): x = draft logits / T of the
+// lane's 32 columns.  Every lane runs the cross-lane steps; inactive rows return an empty part.
+template <int NOISE>
+__device__ __forceinline__ float4 draft_part(const float (&x)[32], const RowMeta& rm, int chunk, int v0, int V) {
+  const float lse = pair_lse<32>(x);
+  float4 o = empty_part();
+  if (NOISE == SPEC_NOISE_CHUNKED) {
+    if (rm.active) {
+      const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key, (uint32_t)chunk)) : lse;
+      o = make_float4(lse, score, __int_as_float(chunk), 0.0f);
     }
-    x[q] = a;
+  } else {
+    float best = -INFINITY, bests = 0.0f;
+    int bestv = -1;
+    if (rm.active) flat_best32(x, v0, V, rm.key, best, bestv, bests);
+    pair_best(best, bestv, bests);
+    if (rm.active) o = make_float4(lse, best, __int_as_float(bestv), bests);
   }
+  return o;
 }
 
-// ------------------------------------------------------------------------------------------
-// bias-row sweep, unit by unit.  A unit is (column range of 256, sub-block of 32 bias rows); the
-// units of a step are split evenly over the resident workgroups in range-major order, so a
-// workgroup reloads its W fragments only when it crosses into the next column range.
-// ------------------------------------------------------------------------------------------
-struct BiasLds {
-  uint16_t sA[SUB][MAX_R + A_PAD];   // gathered A rows of the current unit (bf16)
-  uint16_t sX[SUB][TILE_A + 8];      // draft logits of the current unit, 32 rows x 256 columns (bf16)
-  WaveOut red[NT / 64][SUB];         // per-wave results of the current unit
-};
-
-__device__ __forceinline__ uint64_t key_of(const Params& p, int b, int pos, uint64_t stream) {
-  return sm_first(sm_first(p.kreq[b] ^ (uint64_t)pos) ^ stream);
-}
-
-// metadata of every bias row of the step (rows past n_bias up to a whole sub-block are inactive)
-__device__ void fill_all_meta(const Params& p, int s, const Lists& ls, const uint16_t* bias_list, RowMeta* meta) {
-  const int n_bias = ls.n_draft + ls.n_correct;
-  const int n_rows = (n_bias + SUB - 1) / SUB * SUB;
-  for (int slot = threadIdx.x; slot < n_rows; slot += NT) {
-    RowMeta rm;
-    if (slot < n_bias) {
-      const int e = bias_list[slot];
-      const int b = e >> 1;
-      const int role = (e & 1) ? RO_CORRECT : RO_DRAFT;
-      const int j = (role == RO_DRAFT) ? s : p.acc[b];
-      rm.b = b;
-      rm.j = j;
-      rm.role = role;
-      rm.prev = (j == 0) ? (p.x0 ? p.x0[b] : -1) : p.xs[(size_t)b * p.K + j - 1];
-      rm.invT = 1.0f / p.temp[b];
-      rm.pad = 0.0f;
-      if (role == RO_DRAFT) {
-        rm.key1 = key_of(p, b, j, ST_DRAFT_C);
-        rm.key2 = key_of(p, b, j, ST_DRAFT);
-        rm.lse_p = rm.lse_q = 0.0f;
-      } else {
-        rm.key1 = key_of(p, b, j, ST_RESIDUAL_C);
-        rm.key2 = key_of(p, b, j, ST_RESIDUAL);
-        rm.lse_p = p.lse_p[(size_t)b * (p.K + 1) + j];
-        rm.lse_q = p.lse_q[(size_t)b * p.K + j];
+// CORRECT row at the rejected position: residual norm(max(0, p - q)) and, for a residual with no
+// mass, the target row itself.  x = draft logits / T, t = target logits / T of the lane's 32 columns.
+template <int NOISE>
+__device__ __forceinline__ void correct_part(const float (&x)[32], const float (&t)[32], const RowMeta& rm, int chunk,
+                                             int v0, int V, float4& oa, float4& ob) {
+  const float lse_t = pair_lse<32>(t);
+  float mass = 0.0f;
+  float br = -INFINITY, bp = -INFINITY, dummy = 0.0f;
+  int vr = -1, vp = -1;
+#pragma unroll
+  for (int i = 0; i < 32; i++) {
+    const float lp = t[i] - rm.lse_p, lq = x[i] - rm.lse_q;
+    if (lp > lq) mass += ex2(lp * LOG2E) - ex2(lq * LOG2E);
+  }
+  if (NOISE == SPEC_NOISE_FLAT && rm.active) {
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      const int v = v0 + 32 * (i >> 4) + (i & 15);
+      if (v >= V) continue;
+      const float g = gumbel_bits(bits_at(rm.key, (uint32_t)v));
+      const float lp = t[i] - rm.lse_p, lq = x[i] - rm.lse_q;
+      if (lp > lq) {
+        const float sc = lp + logf(-expm1f(lq - lp)) + g;
+        if (better(sc, v, br, vr)) { br = sc; vr = v; }
       }
-    } else {
-      rm.b = 0;
-      rm.j = 0;
-      rm.role = 0;
-      rm.prev = -1;
-      rm.invT = 1.0f;
-      rm.lse_p = rm.lse_q = rm.pad = 0.0f;
-      rm.key1 = rm.key2 = 0;
-    }
-    meta[slot] = rm;
-  }
-}
-
-// register prefetch of one unit: A rows (bf16) and, for the tiled path, the 32 x 256 draft-logit
-// tile, read with coalesced 16-byte loads (each wave instruction covers two 512-byte row pieces)
-struct UnitPrefetch {
-  u32x4 a[4];
-  u32x4 x[4];
-};
-
-template <bool TILE>
-__device__ __forceinline__ void unit_fetch(const Params& p, const RowMeta* meta, int range, UnitPrefetch& up) {
-  const int R = p.R, segs = R / 8;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = threadIdx.x + NT * i;
-    u32x4 val = {0, 0, 0, 0};
-    if (e < SUB * segs) {
-      const int prev = meta[e / segs].prev;
-      if (prev >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)prev * R + 8 * (e % segs));
-    }
-    up.a[i] = val;
-  }
-  if (TILE) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = range * TILE_A + 8 * (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = 8 * i + 2 * wave + (lane >> 5);
-      const RowMeta& rm = meta[r];
-      u32x4 val = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};   // -inf past the row / no row
-      if (rm.role != 0 && col < p.V)
-        val = *(const u32x4*)((const uint16_t*)p.base + ((size_t)rm.b * p.K + rm.j) * (size_t)p.V + col);
-      up.x[i] = val;
+      if (t[i] > -INFINITY && better(t[i] + g, v, bp, vp)) { bp = t[i] + g; vp = v; }
     }
   }
-}
-
-template <bool TILE>
-__device__ __forceinline__ void unit_store(const Params& p, const UnitPrefetch& up, BiasLds& L) {
-  const int segs = p.R / 8;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = threadIdx.x + NT * i;
-    if (e < SUB * segs) *(u32x4*)&L.sA[e / segs][8 * (e % segs)] = up.a[i];
-  }
-  if (TILE) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = 8 * i + 2 * wave + (lane >> 5);
-      *(u32x4*)&L.sX[r][8 * (lane & 31)] = up.x[i];
-    }
+  mass += xor32f(mass);
+  pair_best(br, vr, dummy);
+  pair_best(bp, vp, dummy);
+  oa = empty_part();
+  ob = empty_part();
+  if (!rm.active) return;
+  const float lmass = (mass > 0.0f) ? lg2(mass) * LN2 : -INFINITY;
+  if (NOISE == SPEC_NOISE_CHUNKED) {
+    const float g = gumbel_bits(bits_at(rm.key, (uint32_t)chunk));
+    oa = make_float4(lmass, lmass > -INFINITY ? lmass + g : -INFINITY, __int_as_float(chunk), 0.0f);
+    ob = make_float4(lse_t, lse_t > -INFINITY ? lse_t + g : -INFINITY, __int_as_float(chunk), 0.0f);
+  } else {
+    oa = make_float4(lmass, br, __int_as_float(vr), 0.0f);
+    ob = make_float4(lse_t, bp, __int_as_float(vp), 0.0f);
   }
 }
 
 // partials of one finished unit from red (threads 0..31)
-__device__ __forceinline__ void unit_flush(const Params& p, const Lists& ls, const BiasLds& L, int slot0, int range) {
+__device__ __forceinline__ void unit_flush(const Params& p, const uint16_t* bias_list, const WaveOut (*red)[SUB],
+                                           int slot0, int range) {
   if (threadIdx.x < SUB) {
     const int r = threadIdx.x, slot = slot0 + r;
-    if (slot < ls.n_draft + ls.n_correct) {
-      float4 pa = L.red[0][r].a;
+    const uint16_t e = bias_list[slot];
+    if (e != NO_ROW) {
+      float4 pa = red[0][r].a;
 #pragma unroll
-      for (int w = 1; w < NT / 64; w++) pa = merge_part(pa, L.red[w][r].a);
+      for (int w = 1; w < NT / 64; w++) pa = merge_part(pa, red[w][r].a);
       p.part_bias[(size_t)slot * p.nrA + range] = pa;
-      if (slot >= ls.n_draft) {
-        float4 pb = L.red[0][r].b;
+      if (e & 1) {
+        float4 pb = red[0][r].b;
 #pragma unroll
-        for (int w = 1; w < NT / 64; w++) pb = merge_part(pb, L.red[w][r].b);
+        for (int w = 1; w < NT / 64; w++) pb = merge_part(pb, red[w][r].b);
         p.part_bias2[(size_t)slot * p.nrA + range] = pb;
       }
     }
   }
 }
 
+// W fragments of column range `range`: MFMA A-operand row i of fragment f is column
+// vw + 32 f + perm(i), perm chosen so that accumulator q of lane l holds column vw + 32 f +
+// 16 (l / 32) + q; lane half l / 32 covers k in [R/2 (l/32), R/2 (l/32 + 1))
+__device__ __forceinline__ void load_w(const Params& p, int range, bf16x8 (&wf)[2][16]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, h = lane >> 5;
+  const int R = p.R, T16 = R >> 4, kb = h * (R >> 1);
+  const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  const int vw = range * TILE_A + 64 * wave;
+  // Fragments past V or past the rank are zero.  They are read from the 16-byte zero constant
+  // rather than selected after the load, which would wait for it.
+#pragma unroll
+  for (int f = 0; f < 2; f++) {
+    const int v = vw + 32 * f + col_in;
+    const bool in = v < p.V;
+    const uint16_t* wr = (const uint16_t*)p.W + (size_t)v * R + kb;
+#pragma unroll
+    for (int t = 0; t < 16; t++)
+      wf[f][t] = *((in && t < T16) ? (const bf16x8*)(wr + 8 * t) : (const bf16x8*)p.konst);
+  }
+}
+
+// Markov bias of the lane's 32 columns (element i: column v0 + 32 (i / 16) + i % 16) for row
+// m = lane % 32 of the sub-block whose A rows sit in sA
+__device__ __forceinline__ void mfma_bias(const bf16x8 (&wf)[2][16], const uint16_t (*sA)[MAX_R + A_PAD], int R,
+                                          float (&x)[32]) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, h = lane >> 5;
+  const int T16 = R >> 4, kb = h * (R >> 1);
+  f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  f32x16 acc1 = acc0;
+#pragma unroll
+  for (int t = 0; t < 16; t++) {
+    // for t >= R/16 both operands are zero (zero W fragments; sA zero past the rank)
+    const bf16x8 bop = *(const bf16x8*)&sA[m][kb + 8 * (t < T16 ? t : 0)];
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, acc1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    x[q] = acc0[q];
+    x[16 + q] = acc1[q];
+  }
+}
+
+// ---- generic sweep: fp32 factors, or bf16 rows that are not 16-byte aligned / V % 8 != 0 ----
+
+// fp32 factors: Markov bias of 16 consecutive columns by VALU dot products (small vocabularies)
+__device__ __forceinline__ void fp32_bias16(const Params& p, int prev, int vstart, float* x) {
+  const int R = p.R;
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const int v = vstart + q;
+    float a = 0.0f;
+    if (prev >= 0 && v < p.V) {
+      const float* wr = (const float*)p.W + (size_t)v * R;
+      const float* ar = (const float*)p.A + (size_t)prev * R;
+      for (int k = 0; k < R; k++) a = fmaf(ar[k], wr[k], a);
+    }
+    x[q] = a;
+  }
+}
+
+struct GenericLds {
+  uint16_t sA[SUB][MAX_R + A_PAD];   // A rows of the current unit (bf16)
+  WaveOut red[NT / 64][SUB];
+};
+
 template <int DT, int NOISE, bool VEC>
-__device__ void bias_sweep(const Params& p, int s, const Lists& ls, const RowMeta* meta, BiasLds& L) {
-  constexpr bool TILE = (DT == SPEC_BF16) && VEC;
+__device__ void bias_sweep_generic(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
+                                   const ReqMeta* req, GenericLds& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, h = lane >> 5;
   const int V = p.V, R = p.R, K = p.K;
-  const int T16 = R / 16;
-  const int kb = h * (R / 2);
   const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
-  const int n_bias = ls.n_draft + ls.n_correct;
-  const int nsb = (n_bias + SUB - 1) / SUB;
+  const int nsb = ls.n_sb;
   const long long units = (long long)p.nrA * nsb;
   const int u0 = (int)(units * blockIdx.x / gridDim.x);
   const int u1 = (int)(units * (blockIdx.x + 1) / gridDim.x);
   if (u0 >= u1) return;
-
   bf16x8 wf[2][16];
   int w_range = -1;
-  UnitPrefetch up;
-  unit_fetch<TILE>(p, meta + (u0 % nsb) * SUB, u0 / nsb, up);
-
   for (int u = u0; u < u1; u++) {
-    const int range = u / nsb, sb = u % nsb;
-    __syncthreads();   // waves are done with the previous unit's LDS tiles and red
-    if (DT == SPEC_BF16) unit_store<TILE>(p, up, L);
-    if (u > u0) unit_flush(p, ls, L, ((u - 1) % nsb) * SUB, (u - 1) / nsb);
-    __syncthreads();   // this unit's tiles are in LDS; red is free
-    if (range != w_range && DT == SPEC_BF16) {
-      // W fragments: MFMA A-operand row i of fragment f is column vw + 32f + perm(i), perm chosen
-      // so that accumulator q of lane l holds column vw + 32f + 16*(l/32) + q; lane half l/32
-      // covers k in [R/2 * (l/32), R/2 * (l/32 + 1))
-      const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-      const int vw = range * TILE_A + 64 * wave;
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
-        const int v = vw + 32 * f + col_in;
-#pragma unroll
-        for (int t = 0; t < 16; t++) {
-          if (t < T16) {
-            if (v < V) wf[f][t] = *(const bf16x8*)((const uint16_t*)p.W + (size_t)v * R + kb + 8 * t);
-            else wf[f][t] = (bf16x8){0, 0, 0, 0, 0, 0, 0, 0};
-          }
-        }
+    const int range = u / nsb, slot0 = (u % nsb) * SUB;
+    const bool corr_unit = slot0 >= ls.c0;
+    __syncthreads();   // the previous unit is done with sA and red
+    if (u > u0) unit_flush(p, bias_list, L.red, ((u - 1) % nsb) * SUB, (u - 1) / nsb);
+    if (DT == SPEC_BF16) {
+      const int segs = R >> 3;
+      for (int e = threadIdx.x; e < SUB * segs; e += NT) {
+        const int row = e / segs, sg = e - row * segs;
+        const RowMeta rr = row_meta(bias_list, req, s, slot0 + row);
+        u32x4 val = {0, 0, 0, 0};
+        if (rr.prev >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)rr.prev * R + 8 * sg);
+        *(u32x4*)&L.sA[row][8 * sg] = val;
       }
     }
+    __syncthreads();   // sA holds this unit's A rows; red is free
+    if (DT == SPEC_BF16 && range != w_range) load_w(p, range, wf);
     w_range = range;
-    if (u + 1 < u1) unit_fetch<TILE>(p, meta + ((u + 1) % nsb) * SUB, (u + 1) / nsb, up);
 
     const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
     const int chunk = vw / CHUNK;
-    const int v0 = vw + 16 * h;                  // lane's first column in fragment 0
-    const int slot0 = sb * SUB;
-    const bool any_correct = slot0 + SUB > ls.n_draft && slot0 < n_bias;   // uniform
-    const RowMeta& rm = meta[slot0 + m];
-    const int role = rm.role;
-    const float invT = rm.invT;
-    const void* base_row = (const char*)p.base + ((size_t)rm.b * K + rm.j) * (size_t)V * esz;
-
-    // Markov bias of the lane's 32 columns
+    const int v0 = vw + 16 * h;
+    const RowMeta rm = row_meta(bias_list, req, s, slot0 + m);
     float x[32];
     if (DT == SPEC_BF16) {
-      f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      f32x16 acc1 = acc0;
-#pragma unroll
-      for (int t = 0; t < 16; t++) {
-        if (t < T16) {
-          const bf16x8 bop = *(const bf16x8*)&L.sA[m][kb + 8 * t];
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, acc1, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 16; q++) {
-        x[q] = acc0[q];
-        x[16 + q] = acc1[q];
-      }
+      mfma_bias(wf, L.sA, R, x);
     } else {
-      fp32_bias16(p, rm, v0, V, role != 0, x);
-      fp32_bias16(p, rm, v0 + 32, V, role != 0, x + 16);
+      fp32_bias16(p, rm.prev, v0, x);
+      fp32_bias16(p, rm.prev, v0 + 32, x + 16);
     }
-    // draft logits s = (base + bias) / T
-    if (TILE) {
-      const uint16_t* xr = &L.sX[m][64 * wave + 16 * h];
-      const u32x4 a0 = *(const u32x4*)xr, a1 = *(const u32x4*)(xr + 8);
-      const u32x4 c0 = *(const u32x4*)(xr + 32), c1 = *(const u32x4*)(xr + 40);
+    {
+      float bx[32];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        x[2 * i] = (bf16_lo(a0[i]) + x[2 * i]) * invT;
-        x[2 * i + 1] = (bf16_hi(a0[i]) + x[2 * i + 1]) * invT;
-        x[8 + 2 * i] = (bf16_lo(a1[i]) + x[8 + 2 * i]) * invT;
-        x[8 + 2 * i + 1] = (bf16_hi(a1[i]) + x[8 + 2 * i + 1]) * invT;
-        x[16 + 2 * i] = (bf16_lo(c0[i]) + x[16 + 2 * i]) * invT;
-        x[16 + 2 * i + 1] = (bf16_hi(c0[i]) + x[16 + 2 * i + 1]) * invT;
-        x[24 + 2 * i] = (bf16_lo(c1[i]) + x[24 + 2 * i]) * invT;
-        x[24 + 2 * i + 1] = (bf16_hi(c1[i]) + x[24 + 2 * i + 1]) * invT;
-      }
-    } else if (VEC) {
-      Raw16<DT> r0, r1;
-      if (role) {
-        raw_load_pred<DT>(base_row, v0, V, r0);
-        raw_load_pred<DT>(base_row, v0 + 32, V, r1);
+      for (int i = 0; i < 32; i++) bx[i] = -INFINITY;
+      const void* base_row = (const char*)p.base + ((size_t)rm.b * K + rm.j) * (size_t)V * esz;
+      if (rm.active) {
+        load16<DT, VEC>(base_row, v0, V, *(float(*)[16])bx);
+        load16<DT, VEC>(base_row, v0 + 32, V, *(float(*)[16])(bx + 16));
       }
 #pragma unroll
-      for (int q = 0; q < 16; q++) {
-        x[q] = role ? (raw_at<DT>(r0, q) + x[q]) * invT : -INFINITY;
-        x[16 + q] = role ? (raw_at<DT>(r1, q) + x[16 + q]) * invT : -INFINITY;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; i++) {
-        const int v = v0 + 32 * (i >> 4) + (i & 15);
-        x[i] = (role && v < V) ? (load1<DT>(base_row, (size_t)v) + x[i]) * invT : -INFINITY;
-      }
+      for (int i = 0; i < 32; i++) x[i] = rm.active ? (bx[i] + x[i]) * rm.invT : -INFINITY;
     }
-
-    float4 oa = empty_part(), ob = empty_part();
-    if (!any_correct) {
-      // ---- DRAFT rows only
-      const float lse = pair_lse<32>(x);
-      if (role) {
-        if (NOISE == SPEC_NOISE_CHUNKED) {
-          const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse;
-          oa = make_float4(lse, score, __int_as_float(chunk), 0.0f);
-        } else {
-          float best = -INFINITY, bests = 0.0f;
-          int bestv = -1;
-          flat_best32(x, v0, V, rm.key2, best, bestv, bests);
-          pair_best(best, bestv, bests);
-          oa = make_float4(lse, best, __int_as_float(bestv), bests);
-        }
-      }
+    WaveOut o;
+    if (!corr_unit) {
+      o.a = draft_part<NOISE>(x, rm, chunk, v0, V);
+      o.b = empty_part();
     } else {
-      // ---- unit holding CORRECT rows: residual norm(max(0, p - q)) and its target-row fallback,
-      //      the target row streamed one 16-column fragment at a time with online reductions
-      const bool corr = role == RO_CORRECT;
-      const float lse_x = pair_lse<32>(x);   // draft log-mass (used by DRAFT lanes)
+      float t[32];
+#pragma unroll
+      for (int i = 0; i < 32; i++) t[i] = -INFINITY;
       const void* targ_row = (const char*)p.target + ((size_t)rm.b * (K + 1) + rm.j) * (size_t)V * esz;
-      float mt = -INFINITY, st = 0.0f, mass = 0.0f;
-      float br = -INFINITY, bp = -INFINITY, bd = -INFINITY, bds = 0.0f;
-      int vr = -1, vp = -1, vd = -1;
-      if (NOISE == SPEC_NOISE_FLAT && role == RO_DRAFT) flat_best32(x, v0, V, rm.key2, bd, vd, bds);
-#pragma unroll
-      for (int f = 0; f < 2; f++) {
-        float t[16];
-        if (VEC) {
-          Raw16<DT> r0;
-          if (corr) raw_load_pred<DT>(targ_row, v0 + 32 * f, V, r0);
-#pragma unroll
-          for (int q = 0; q < 16; q++) t[q] = corr ? raw_at<DT>(r0, q) * invT : -INFINITY;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 16; q++) {
-            const int v = v0 + 32 * f + q;
-            t[q] = (corr && v < V) ? load1<DT>(targ_row, (size_t)v) * invT : -INFINITY;
-          }
-        }
-        if (corr) {
-          float fm = -INFINITY;
-#pragma unroll
-          for (int q = 0; q < 16; q++) fm = fmaxf(fm, t[q]);
-          const float nm = fmaxf(mt, fm);
-          if (nm > -INFINITY) {
-            float acc_s = (mt > -INFINITY) ? st * ex2((mt - nm) * LOG2E) : (st != st ? st : 0.0f);
-#pragma unroll
-            for (int q = 0; q < 16; q++) acc_s += ex2((t[q] - nm) * LOG2E);
-            st = acc_s;
-            mt = nm;
-          } else {
-#pragma unroll
-            for (int q = 0; q < 16; q++) st += (t[q] != t[q]) ? t[q] : 0.0f;   // NaN stays visible
-          }
-#pragma unroll
-          for (int q = 0; q < 16; q++) {
-            const float lp = t[q] - rm.lse_p, lq = x[16 * f + q] - rm.lse_q;
-            if (lp > lq) mass += ex2(lp * LOG2E) - ex2(lq * LOG2E);
-          }
-          if (NOISE == SPEC_NOISE_FLAT) {
-#pragma unroll
-            for (int q = 0; q < 16; q++) {
-              const int v = v0 + 32 * f + q;
-              if (v >= V) continue;
-              const float g = gumbel_bits(bits_at(rm.key2, (uint32_t)v));
-              const float lp = t[q] - rm.lse_p, lq = x[16 * f + q] - rm.lse_q;
-              if (lp > lq) {
-                const float sc = lp + logf(-expm1f(lq - lp)) + g;
-                if (better(sc, v, br, vr)) { br = sc; vr = v; }
-              }
-              if (t[q] > -INFINITY && better(t[q] + g, v, bp, vp)) { bp = t[q] + g; vp = v; }
-            }
-          }
-        }
+      if (rm.active) {
+        load16<DT, VEC>(targ_row, v0, V, *(float(*)[16])t);
+        load16<DT, VEC>(targ_row, v0 + 32, V, *(float(*)[16])(t + 16));
       }
-      // pair-combine (lane ^ 32 holds the other 16 columns of each fragment of the same row)
-      const float m2 = xor32f(mt), s2 = xor32f(st);
-      const float nm = fmaxf(mt, m2);
-      float lse_t;
-      if (nm > -INFINITY) {
-        const float a = (mt > -INFINITY) ? st * ex2((mt - nm) * LOG2E) : (st != st ? st : 0.0f);
-        const float c = (m2 > -INFINITY) ? s2 * ex2((m2 - nm) * LOG2E) : (s2 != s2 ? s2 : 0.0f);
-        lse_t = nm + lg2(a + c) * LN2;
-      } else {
-        lse_t = (st != st || s2 != s2) ? NAN : -INFINITY;
-      }
-      mass += xor32f(mass);
-      float dummy = 0.0f;
-      pair_best(br, vr, dummy);
-      pair_best(bp, vp, dummy);
-      pair_best(bd, vd, bds);
-      if (role == RO_DRAFT) {
-        if (NOISE == SPEC_NOISE_CHUNKED) {
-          const float score = (lse_x > -INFINITY) ? lse_x + gumbel_bits(bits_at(rm.key1, (uint32_t)chunk)) : lse_x;
-          oa = make_float4(lse_x, score, __int_as_float(chunk), 0.0f);
-        } else {
-          oa = make_float4(lse_x, bd, __int_as_float(vd), bds);
-        }
-      } else if (corr) {
-        const float lmass = (mass > 0.0f) ? lg2(mass) * LN2 : -INFINITY;
-        if (NOISE == SPEC_NOISE_CHUNKED) {
-          const float g = gumbel_bits(bits_at(rm.key1, (uint32_t)chunk));
-          oa = make_float4(lmass, lmass > -INFINITY ? lmass + g : -INFINITY, __int_as_float(chunk), 0.0f);
-          ob = make_float4(lse_t, lse_t > -INFINITY ? lse_t + g : -INFINITY, __int_as_float(chunk), 0.0f);
-        } else {
-          oa = make_float4(lmass, br, __int_as_float(vr), 0.0f);
-          ob = make_float4(lse_t, bp, __int_as_float(vp), 0.0f);
-        }
-      }
+#pragma unroll
+      for (int i = 0; i < 32; i++) t[i] = rm.active ? t[i] * rm.invT : -INFINITY;
+      correct_part<NOISE>(x, t, rm, chunk, v0, V, o.a, o.b);
     }
-    if (h == 0) {
-      L.red[wave][m].a = oa;
-      L.red[wave][m].b = ob;
-    }
+    if (h == 0) L.red[wave][m] = o;
   }
   __syncthreads();
-  unit_flush(p, ls, L, ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb);
+  unit_flush(p, bias_list, L.red, ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb);
+}
+
+// ---- fast sweep: bf16, 16-byte aligned rows, V % 8 == 0 ----
+// One workgroup of 4 waves per CU (one wave per SIMD, the full register file each).  Wave w owns
+// columns 64 w .. 64 w + 63 of the unit's 256: one noise chunk, held as two 32 x 32 MFMA tiles,
+// with its W fragments in registers (128 registers).  Per unit only the 32 gathered A rows go
+// through LDS (two stages); the draft and target logits are loaded straight into registers in the
+// accumulator layout (each lane reads 32 bytes of one row per fragment, which streams about as fast
+// as fully coalesced reads), two units ahead.  One barrier per unit.
+struct FastLds {
+  uint16_t sA[2][SUB][MAX_R + A_PAD];   // A rows of the unit's 32 slots, two stages
+  float4 red[2][2][NT / 64][SUB];       // [stage][record a / b][wave][row]
+};
+
+struct UnitRegs {
+  u32x4 a[4];   // A rows: thread t holds row t / 8, 16-byte pieces (t % 8) + 8 i
+  u32x4 x[4];   // draft logits of the lane's 32 columns (two pieces per fragment)
+  u32x4 t[4];   // target logits (CORRECT units)
+};
+
+__device__ __forceinline__ void fast_issue(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
+                                           const ReqMeta* req, int u, int nsb, UnitRegs& P) {
+  const int range = u / nsb, slot0 = (u % nsb) * SUB;
+  const bool corr = slot0 >= ls.c0;
+  const int R = p.R, segs = R >> 3;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // Masked pieces are not selected after the load (that would wait for it): their address is
+  // switched to a 16-byte constant instead, zeros for A and -inf for the logit tiles.
+  {
+    const int row = threadIdx.x >> 3;
+    const uint16_t ent = bias_list[slot0 + row];
+    const ReqMeta& m = req[ent != NO_ROW ? (ent >> 1) : 0];
+    const int pc = m.prev_c, pd = m.prev_d;
+    const int prev = (ent != NO_ROW) ? ((ent & 1) ? pc : pd) : -1;
+    const uint16_t* arow = (const uint16_t*)p.A + (size_t)prev * R;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int sg = (threadIdx.x & 7) + 8 * i;
+      P.a[i] = *((prev >= 0 && sg < segs) ? (const u32x4*)(arow + 8 * sg) : p.konst);
+    }
+  }
+  {
+    const int m = lane & 31, h = lane >> 5;
+    const uint16_t ent = bias_list[slot0 + m];
+    const int b = ent >> 1;
+    const int j = (ent & 1) ? s - 1 : s;
+    const int v0 = range * TILE_A + 64 * wave + 16 * h;   // + 32 f + 8 k
+    const uint16_t* xr = (const uint16_t*)p.base + ((size_t)b * p.K + j) * p.V;
+    const uint16_t* tr = (const uint16_t*)p.target + ((size_t)b * (p.K + 1) + j) * p.V;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int col = v0 + 32 * (i >> 1) + 8 * (i & 1);
+      const bool act = ent != NO_ROW && col < p.V;
+      P.x[i] = *(act ? (const u32x4*)(xr + col) : p.konst + 1);
+      if (corr) P.t[i] = *(act ? (const u32x4*)(tr + col) : p.konst + 1);
+    }
+  }
+}
+
+__device__ __forceinline__ void store_a(const Params& p, const UnitRegs& P, uint16_t (*sA)[MAX_R + A_PAD]) {
+  const int segs = p.R >> 3;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int sg = (threadIdx.x & 7) + 8 * i;
+    if (sg < segs) *(u32x4*)&sA[threadIdx.x >> 3][8 * sg] = P.a[i];
+  }
+}
+
+// bf16 pieces of the lane's 32 columns -> floats (element i: column v0 + 32 (i / 16) + i % 16)
+__device__ __forceinline__ void unpack32(const u32x4 (&w)[4], float (&o)[32]) {
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      o[8 * k + 2 * i] = bf16_lo(w[k][i]);
+      o[8 * k + 2 * i + 1] = bf16_hi(w[k][i]);
+    }
+  }
+}
+
+// best (score, index, aux) over an aligned group of 4 lanes, smaller index on ties; every lane of
+// the group gets the result
+template <int CTRL>
+__device__ __forceinline__ void argmax_round(float& sc, int& ix, float& aux) {
+  const float s2 = dpp<CTRL>(sc), a2 = dpp<CTRL>(aux);
+  const int i2 = __builtin_amdgcn_update_dpp(0, ix, CTRL, 0xF, 0xF, false);
+  if (i2 >= 0 && (ix < 0 || better(s2, i2, sc, ix))) {
+    sc = s2;
+    ix = i2;
+    aux = a2;
+  }
+}
+
+// Partials of one finished unit, by every wave: lane group g (4 lanes) of wave w takes row
+// 8 w + g % 8, record a in lanes 0..31 and record b (CORRECT units) in lanes 32..63; lane i of the
+// group holds the chunk record of wave i.
+__device__ __forceinline__ void fast_flush(const Params& p, const uint16_t* bias_list, const float4 (*red)[NT / 64][SUB],
+                                           int slot0, int range) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = 8 * wave + ((lane & 31) >> 2);
+  const int cw = lane & 3;
+  const bool second = lane >= 32;
+  const float4 h = red[second ? 1 : 0][cw][r];
+  float mx = fmaxf(h.x, dpp<0xB1>(h.x));
+  mx = fmaxf(mx, dpp<0x4E>(mx));
+  float e = (mx == -INFINITY) ? h.x : ex2((h.x - mx) * LOG2E);   // all -inf / NaN: keep a NaN visible
+  e += dpp<0xB1>(e);
+  e += dpp<0x4E>(e);
+  const float lse = (mx == -INFINITY) ? e : mx + lg2(e) * LN2;
+  float sc = h.y, aux = h.w;
+  int ix = __float_as_int(h.z);
+  argmax_round<0xB1>(sc, ix, aux);
+  argmax_round<0x4E>(sc, ix, aux);
+  if (cw == 0) {
+    const int slot = slot0 + r;
+    const uint16_t e16 = bias_list[slot];
+    if (e16 != NO_ROW) {
+      const float4 part = make_float4(lse, sc, __int_as_float(ix), aux);
+      if (!second) p.part_bias[(size_t)slot * p.nrA + range] = part;
+      else if (e16 & 1) p.part_bias2[(size_t)slot * p.nrA + range] = part;
+    }
+  }
+}
+
+// One unit u from stage ST.  Pcur holds unit u's logit tiles (its A rows are already in stage ST),
+// Pnext unit u + 1's.  Order: W fragments if the column range changes (drained on the spot, so no
+// later wait ever waits on them), flush unit u - 1, MFMA, element-wise part from Pcur, issue unit
+// u + 2 into Pcur (clamped to the last unit, so the wait counts are the same on every path), store
+// unit u + 1's A rows into the other stage, barrier.
+template <int NOISE, int ST>
+__device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
+                                          const ReqMeta* req, FastLds& L, int u, int u0, int u1, int nsb,
+                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, h = lane >> 5;
+  const int V = p.V;
+  const int range = u / nsb, slot0 = (u % nsb) * SUB;
+  if (u > u0 && range != (u - 1) / nsb) {
+    load_w(p, range, wf);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  if (u > u0) fast_flush(p, bias_list, L.red[ST ^ 1], ((u - 1) % nsb) * SUB, (u - 1) / nsb);
+  const RowMeta rm = row_meta(bias_list, req, s, slot0 + m);
+
+  float x[32];
+  mfma_bias(wf, L.sA[ST], p.R, x);
+  const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
+  const int chunk = vw / CHUNK;
+  const int v0 = vw + 16 * h;
+  {
+    float bx[32];
+    unpack32(Pcur.x, bx);
+#pragma unroll
+    for (int i = 0; i < 32; i++) x[i] = (bx[i] + x[i]) * rm.invT;
+  }
+  float4 oa, ob;
+  if (slot0 < ls.c0) {
+    oa = draft_part<NOISE>(x, rm, chunk, v0, V);
+    ob = empty_part();
+  } else {
+    float t[32];
+    unpack32(Pcur.t, t);
+#pragma unroll
+    for (int i = 0; i < 32; i++) t[i] *= rm.invT;
+    correct_part<NOISE>(x, t, rm, chunk, v0, V, oa, ob);
+  }
+  if (h == 0) {
+    L.red[ST][0][wave][m] = oa;
+    L.red[ST][1][wave][m] = ob;
+  }
+  fast_issue(p, s, ls, bias_list, req, min(u + 2, u1 - 1), nsb, Pcur);
+  if (u + 1 < u1) store_a(p, Pnext, L.sA[ST ^ 1]);
+  __syncthreads();
+}
+
+template <int NOISE>
+__device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const uint16_t* bias_list, const ReqMeta* req,
+                                FastLds& L) {
+  const int nsb = ls.n_sb;
+  const long long units = (long long)p.nrA * nsb;
+  const int u0 = (int)(units * blockIdx.x / gridDim.x);
+  const int u1 = (int)(units * (blockIdx.x + 1) / gridDim.x);
+  if (u0 >= u1) return;
+  if (p.R < MAX_R) {
+    // the MFMA loop always runs over the full rank: A columns past R must read as zero
+    uint32_t* z = (uint32_t*)&L.sA[0][0][0];
+    for (int i = threadIdx.x; i < (int)(sizeof(L.sA) / 4); i += NT) z[i] = 0u;
+    __syncthreads();
+  }
+  bf16x8 wf[2][16];
+  UnitRegs P0, P1;
+  load_w(p, u0 / nsb, wf);   // first: waiting for unit u0's tiles then covers W as well
+  fast_issue(p, s, ls, bias_list, req, u0, nsb, P0);
+  fast_issue(p, s, ls, bias_list, req, min(u0 + 1, u1 - 1), nsb, P1);
+  store_a(p, P0, L.sA[0]);
+  __syncthreads();
+  int last = 0;
+  for (int u = u0;; u += 2) {
+    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1);
+    if (u + 1 >= u1) { last = 0; break; }
+    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0);
+    if (u + 2 >= u1) { last = 1; break; }
+  }
+  fast_flush(p, bias_list, L.red[last], ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -899,29 +1042,43 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
   }
 }
 
-// Row sweeps of one step.  Every workgroup rebuilds the step's row lists from the role bytes,
-// then takes work items grid-stride.  k_bias takes the bias rows (MFMA, W fragments resident, two
-// workgroups per CU); k_plain streams the target rows of LSEP / BONUS roles at high occupancy.
-// For k_bias, items i and i + 8 run on one XCD, and consecutive items on an XCD are the
-// row-blocks of one column range, so its W tile is shared in that XCD's L2.
-// dynamic LDS of k_bias: row metadata of up to 2B bias rows (rounded to a sub-block), then the
-// bias list [2B] and plain list [B]
-__host__ __device__ constexpr size_t bias_meta_bytes(int B) { return (size_t)(2 * B + SUB) * sizeof(RowMeta); }
+// Row sweeps of one step.  Every workgroup rebuilds the step's row lists from the role bytes;
+// the bias-row sweep also stages each request's bias-row inputs.  k_bias runs one workgroup per
+// CU (its W fragments fill the register file); k_plain streams the target rows of LSEP / BONUS
+// roles at three workgroups per CU.
+// dynamic LDS of the bias-row sweeps: per-request table [B], then the bias and plain lists
+__host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
+  return (size_t)B * sizeof(ReqMeta) + (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t);
+}
+// dynamic LDS of the plain-row sweep: bias and plain lists
+__host__ __device__ constexpr size_t plain_dyn_bytes(int B) { return (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t); }
+
+template <int NOISE>
+__global__ __launch_bounds__(NT, 1) void k_bias_fast(Params p, int s) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
+  __shared__ uint64_t scan_tmp[NT / 64];
+  __shared__ FastLds lds_f;
+  ReqMeta* req = (ReqMeta*)dyn_bias;
+  uint16_t* bias_list = (uint16_t*)(dyn_bias + (size_t)p.B * sizeof(ReqMeta));
+  uint16_t* plain_list = bias_list + bias_slots_max(p.B);
+  const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
+  const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, req, true);
+  if (ls.n_draft + ls.n_correct == 0) return;
+  bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, lds_f);
+}
 
 template <int DT, int NOISE, bool VEC>
 __global__ __launch_bounds__(NT, 1) void k_bias(Params p, int s) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
   __shared__ uint64_t scan_tmp[NT / 64];
-  __shared__ BiasLds lds_a;
-  RowMeta* meta = (RowMeta*)dyn_bias;
-  uint16_t* bias_list = (uint16_t*)(dyn_bias + bias_meta_bytes(p.B));
-  uint16_t* plain_list = bias_list + 2 * p.B;
+  __shared__ GenericLds lds_g;
+  ReqMeta* req = (ReqMeta*)dyn_bias;
+  uint16_t* bias_list = (uint16_t*)(dyn_bias + (size_t)p.B * sizeof(ReqMeta));
+  uint16_t* plain_list = bias_list + bias_slots_max(p.B);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
-  const Lists ls = build_lists(p, roles, bias_list, plain_list, scan_tmp, true);
+  const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, req, true);
   if (ls.n_draft + ls.n_correct == 0) return;
-  fill_all_meta(p, s, ls, bias_list, meta);
-  __syncthreads();
-  bias_sweep<DT, NOISE, VEC>(p, s, ls, meta, lds_a);
+  bias_sweep_generic<DT, NOISE, VEC>(p, s, ls, bias_list, req, lds_g);
 }
 
 template <int DT, int NOISE, bool VEC>
@@ -930,9 +1087,9 @@ __global__ __launch_bounds__(NT, 3) void k_plain(Params p, int s) {
   __shared__ uint64_t scan_tmp[NT / 64];
   __shared__ float4 redb[NT / 64];
   uint16_t* bias_list = dyn_lists;
-  uint16_t* plain_list = dyn_lists + 2 * p.B;
+  uint16_t* plain_list = dyn_lists + bias_slots_max(p.B);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
-  const Lists ls = build_lists(p, roles, bias_list, plain_list, scan_tmp);
+  const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, nullptr, false);
   const int n_items = ls.n_plain * p.nrB;
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int pslot = it / p.nrB, range = it % p.nrB;
@@ -941,200 +1098,311 @@ __global__ __launch_bounds__(NT, 3) void k_plain(Params p, int s) {
 }
 
 // ------------------------------------------------------------------------------------------
-// merge: one workgroup per request
+// merge: one workgroup per request, three dependent memory rounds
+//   1. the partials of every row the request has this step, all loaded together and reduced;
+//   2. level two of the chunked sampler for the DRAFT row (threads 0..127) and for the CORRECT /
+//      BONUS row (threads 128..255) side by side: 64 columns x 2 threads each, every thread half
+//      of the Markov-bias dot product; the DRAFT half also reads the target values of its chunk,
+//      so the accept test needs no further load;
+//   3. decision, outputs and the roles of step s + 1.
 // ------------------------------------------------------------------------------------------
 
-// reduce n partial records with the whole workgroup; every thread gets the result
-__device__ float4 reduce_parts(const float4* parts, int n, float4* lds) {
-  float4 a = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f);
-  for (int i = threadIdx.x; i < n; i += NT) a = merge_part(a, parts[i]);
+// merge of four independent partial records over the workgroup; every thread gets the results
+__device__ __forceinline__ void reduce4(float4 (&a)[4], float4 (*lds)[NT / 64]) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    float4 y;
-    y.x = __shfl_xor(a.x, o, 64);
-    y.y = __shfl_xor(a.y, o, 64);
-    y.z = __shfl_xor(a.z, o, 64);
-    y.w = __shfl_xor(a.w, o, 64);
-    a = merge_part(a, y);
-  }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = a;
-  __syncthreads();
-  float4 r = lds[0];
 #pragma unroll
-  for (int w = 1; w < NT / 64; w++) r = merge_part(r, lds[w]);
-  return r;
-}
-
-// argmax over one wave (score, index), smallest index on ties; result in every lane
-__device__ __forceinline__ void wave_argmax(float& sc, int& ix, float& aux) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    float s2 = __shfl_xor(sc, o, 64);
-    int i2 = __shfl_xor(ix, o, 64);
-    float a2 = __shfl_xor(aux, o, 64);
-    if (i2 >= 0 && (ix < 0 || better(s2, i2, sc, ix))) {
-      sc = s2;
-      ix = i2;
-      aux = a2;
+    for (int k = 0; k < 4; k++) {
+      float4 y;
+      y.x = __shfl_xor(a[k].x, o, 64);
+      y.y = __shfl_xor(a[k].y, o, 64);
+      y.z = __shfl_xor(a[k].z, o, 64);
+      y.w = __shfl_xor(a[k].w, o, 64);
+      a[k] = merge_part(a[k], y);
     }
   }
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) lds[k][threadIdx.x >> 6] = a[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    float4 r = lds[k][0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; w++) r = merge_part(r, lds[k][w]);
+    a[k] = r;
+  }
 }
 
-// Markov bias of column v, the share of thread quarter q = 0..3 of the rank (fp32 accumulate)
+// half of the Markov-bias dot product A[prev] . W[v] (k in [hh R/2, (hh + 1) R/2)), fp32 accumulate
 template <int DT>
-__device__ float bias_quarter(const Params& p, int prev, int v, int q) {
+__device__ __forceinline__ float bias_half(const Params& p, int prev, int v, int hh) {
   float a = 0.0f;
-  const int R = p.R;
-  if (prev < 0) return a;
+  const int R = p.R, k0 = hh * (R >> 1), k1 = k0 + (R >> 1);
+  if (prev < 0 || v < 0 || v >= p.V) return a;
   if (DT == SPEC_BF16) {
     const uint16_t* ar = (const uint16_t*)p.A + (size_t)prev * R;
     const uint16_t* wr = (const uint16_t*)p.W + (size_t)v * R;
-    for (int k = 8 * q; k < R; k += 32) {
-      const u32x4 aw = *(const u32x4*)(ar + k);
-      const u32x4 ww = *(const u32x4*)(wr + k);
+    if ((R & 15) == 0) {
+      // fully unrolled to the largest rank, so every load is in flight before the first FMA
+      u32x4 aw[MAX_R / 16], ww[MAX_R / 16];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        a = fmaf(bf16_lo(aw[i]), bf16_lo(ww[i]), a);
-        a = fmaf(bf16_hi(aw[i]), bf16_hi(ww[i]), a);
+      for (int i = 0; i < MAX_R / 16; i++) {
+        const int k = k0 + 8 * i;
+        aw[i] = (k < k1) ? *(const u32x4*)(ar + k) : (u32x4){0, 0, 0, 0};
+        ww[i] = (k < k1) ? *(const u32x4*)(wr + k) : (u32x4){0, 0, 0, 0};
       }
+#pragma unroll
+      for (int i = 0; i < MAX_R / 16; i++) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          a = fmaf(bf16_lo(aw[i][q]), bf16_lo(ww[i][q]), a);
+          a = fmaf(bf16_hi(aw[i][q]), bf16_hi(ww[i][q]), a);
+        }
+      }
+    } else {
+      for (int k = k0; k < k1; k++) a = fmaf(bf16_to_f32(ar[k]), bf16_to_f32(wr[k]), a);
     }
   } else {
     const float* ar = (const float*)p.A + (size_t)prev * R;
     const float* wr = (const float*)p.W + (size_t)v * R;
-    for (int k = q; k < R; k += 4) a = fmaf(ar[k], wr[k], a);
+    for (int k = k0; k < k1; k++) a = fmaf(ar[k], wr[k], a);
   }
   return a;
 }
 
-enum { L2_DRAFT = 0, L2_TARGET = 1, L2_RESIDUAL = 2 };
+enum { L2_NONE = 0, L2_DRAFT = 1, L2_TARGET = 2, L2_RESIDUAL = 3 };
 
-// Level two of the CHUNKED sampler over chunk c, whole workgroup: argmax over the chunk's
-// columns of (score_v + G(key2, v)); thread t works on column 64c + t/4 with a quarter of the
-// rank.  Returns the column (-1 if none) and, for DRAFT, its scaled draft logit in *aux_out.
+struct L2Job {       // one level-two selection of a thread group
+  int kind;          // L2_*
+  int chunk;         // chunk of the winner of level one
+  int prev;          // previous token (Markov bias), -1 = none
+  uint64_t key;      // per-index noise key of the row
+  const void* base_row;
+  const void* targ_row;
+  float invT, lse_p, lse_q;
+  bool want_target;  // DRAFT: also return the target logit of the winner
+};
+
+struct L2Result {
+  int v;             // winning column, -1 = none
+  float sx;          // DRAFT: scaled draft logit of the winner
+  float tx;          // target logit (unscaled) of the winner, when asked for
+};
+
+// Level two over the 64 columns of one chunk by a group of 128 threads (2 waves); thread t of the
+// group takes column 64 c + t / 2 and half t % 2 of the rank.  Result in every thread of the group.
 template <int DT>
-__device__ int level_two(const Params& p, int kind, int c, uint64_t key2, const void* base_row,
-                         const void* targ_row, int prev, float invT, float lse_p, float lse_q, float* aux_out,
-                         float4* lds) {
-  const int q = threadIdx.x & 3;
-  const int v = c * CHUNK + (threadIdx.x >> 2);
-  const bool in = c >= 0 && v < p.V;
+__device__ L2Result level_two(const Params& p, const L2Job& jb, int gt, float4* lds2) {
+  const int hh = gt & 1;
+  const int v = jb.chunk * CHUNK + (gt >> 1);
+  const bool in = jb.kind != L2_NONE && jb.chunk >= 0 && v < p.V;
+  // the row values first (independent of the bias), then the bias dot product
+  const bool need_base = in && (jb.kind == L2_DRAFT || jb.kind == L2_RESIDUAL);
+  const bool need_targ = in && (jb.kind != L2_DRAFT || jb.want_target);
+  const float bv = need_base ? load1<DT>(jb.base_row, (size_t)v) : 0.0f;
+  const float tvr = need_targ ? load1<DT>(jb.targ_row, (size_t)v) : 0.0f;
   float bias = 0.0f;
-  if (in && kind != L2_TARGET) bias = bias_quarter<DT>(p, prev, v, q);
+  if (in && jb.kind != L2_TARGET) bias = bias_half<DT>(p, jb.prev, v, hh);
   bias += __shfl_xor(bias, 1, 64);
-  bias += __shfl_xor(bias, 2, 64);
-  float sc = -INFINITY, aux = 0.0f;
+  float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
   int ix = -1;
-  if (in && q == 0) {
-    const float g = gumbel_bits(bits_at(key2, (uint32_t)v));
-    if (kind == L2_DRAFT) {
-      const float sv = (load1<DT>(base_row, (size_t)v) + bias) * invT;
+  if (in && hh == 0) {
+    const float g = gumbel_bits(bits_at(jb.key, (uint32_t)v));
+    if (jb.kind == L2_DRAFT) {
+      const float sv = (bv + bias) * jb.invT;
+      if (jb.want_target) tx = tvr;
       if (sv > -INFINITY) {
         sc = sv + g;
         ix = v;
-        aux = sv;
+        sx = sv;
       }
-    } else if (kind == L2_TARGET) {
-      const float tv = load1<DT>(targ_row, (size_t)v) * invT;
+    } else if (jb.kind == L2_TARGET) {
+      const float tv = tvr * jb.invT;
       if (tv > -INFINITY) {
         sc = tv + g;
         ix = v;
       }
     } else {
-      const float sv = (load1<DT>(base_row, (size_t)v) + bias) * invT;
-      const float tv = load1<DT>(targ_row, (size_t)v) * invT;
-      const float lp = tv - lse_p, lq = sv - lse_q;
+      const float sv = (bv + bias) * jb.invT;
+      const float tv = tvr * jb.invT;
+      const float lp = tv - jb.lse_p, lq = sv - jb.lse_q;
       if (lp > lq) {
         sc = lp + logf(-expm1f(lq - lp)) + g;
         ix = v;
       }
     }
   }
-  wave_argmax(sc, ix, aux);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = make_float4(sc, aux, __int_as_float(ix), 0.0f);
-  __syncthreads();
-  float bs = lds[0].x, ba = lds[0].y;
-  int bi = __float_as_int(lds[0].z);
+  // argmax over the group's 2 waves, smallest index on ties; sx and tx ride along
 #pragma unroll
-  for (int w = 1; w < NT / 64; w++) {
-    const int i2 = __float_as_int(lds[w].z);
-    if (i2 >= 0 && (bi < 0 || better(lds[w].x, i2, bs, bi))) {
-      bs = lds[w].x;
-      bi = i2;
-      ba = lds[w].y;
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float s2 = __shfl_xor(sc, o, 64), x2 = __shfl_xor(sx, o, 64), t2 = __shfl_xor(tx, o, 64);
+    const int i2 = __shfl_xor(ix, o, 64);
+    if (i2 >= 0 && (ix < 0 || better(s2, i2, sc, ix))) {
+      sc = s2;
+      ix = i2;
+      sx = x2;
+      tx = t2;
     }
   }
-  if (aux_out) *aux_out = ba;
-  return bi;
+  const int wv = (gt >> 6) & 1;
+  if ((gt & 63) == 0) lds2[wv] = make_float4(sc, sx, __int_as_float(ix), tx);
+  __syncthreads();
+  L2Result r;
+  float4 a = lds2[0], c = lds2[1];
+  const int ia = __float_as_int(a.z), ic = __float_as_int(c.z);
+  if (ic >= 0 && (ia < 0 || better(c.x, ic, a.x, ia))) a = c;
+  r.v = __float_as_int(a.z);
+  r.sx = a.y;
+  r.tx = a.w;
+  return r;
 }
 
 template <int DT, int NOISE>
 __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
-  __shared__ float4 red[NT / 64];
+  __shared__ float4 red[4][NT / 64];
+  __shared__ float4 lds2[2][2];
   const int b = blockIdx.x;
   const int B = p.B, K = p.K, V = p.V;
+  // round 0: every per-request value that depends only on (b, s), loaded together with the roles
   const int roles = p.roles[(size_t)(s & 1) * B + b];
+  const float invT = 1.0f / p.temp[b];
+  const int x0 = p.x0 ? p.x0[b] : -1;
+  const int L = p.L[b];
+  int phase = p.phase[b];
+  int acc = p.acc[b];
+  const uint64_t kreq = p.kreq[b];
+  const int slot_d = p.slots[b], slot_c = p.slots[B + b], slot_p = p.slots[2 * B + b];
+  const int32_t* xr = p.xs + (size_t)b * K;
+  const int prev_d = (s == 0) ? x0 : xr[s - 1];                // token before position s
+  const int prev_c = (s <= 1) ? x0 : xr[s - 2];                // token before position s - 1
+  const int x_t = (threadIdx.x < K) ? xr[threadIdx.x] : -1;   // drafted tokens, for the output
+  const int jc0 = s > 0 ? s - 1 : 0;
+  const float lse_p_c = p.lse_p[(size_t)b * (K + 1) + jc0];    // read whether or not used
+  const float lse_q_c = p.lse_q[(size_t)b * K + jc0];
   uint8_t* roles_next = p.roles + (size_t)((s + 1) & 1) * B;
   if (roles == 0) {
     if (threadIdx.x == 0) roles_next[b] = 0;
     return;
   }
   const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
-  const float invT = 1.0f / p.temp[b];
-  const uint64_t g = (uint64_t)(p.req_off + b);
-  const int x0 = p.x0 ? p.x0[b] : -1;
-  const int L = p.L[b];
-  int phase = p.phase[b];
-  int acc = p.acc[b];
+  const bool hasD = roles & RO_DRAFT, hasC = roles & RO_CORRECT, hasP = roles & (RO_LSEP | RO_BONUS);
+
+  // ---- round 1: partials of every row
+  float4 t4[4] = {empty_part(), empty_part(), empty_part(), empty_part()};   // DRAFT, CORRECT, fallback, plain
+  for (int i0 = 0; i0 < p.nrA; i0 += 4 * NT) {
+    // four partials per thread and row in flight at once
+    float4 pd[4], pc[4], pc2[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int i = i0 + k * NT + threadIdx.x;
+      const bool in = i < p.nrA;
+      pd[k] = (hasD && in) ? p.part_bias[(size_t)slot_d * p.nrA + i] : empty_part();
+      pc[k] = (hasC && in) ? p.part_bias[(size_t)slot_c * p.nrA + i] : empty_part();
+      pc2[k] = (hasC && in) ? p.part_bias2[(size_t)slot_c * p.nrA + i] : empty_part();
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      t4[0] = merge_part(t4[0], pd[k]);
+      t4[1] = merge_part(t4[1], pc[k]);
+      t4[2] = merge_part(t4[2], pc2[k]);
+    }
+  }
+  for (int i = threadIdx.x; i < p.nrB; i += NT)
+    if (hasP) t4[3] = merge_part(t4[3], p.part_plain[(size_t)slot_p * p.nrB + i]);
+  reduce4(t4, red);
+  const float4 tot_d = t4[0], tot_c = t4[1], tot_c2 = t4[2], tot_p = t4[3];
+
+  // ---- round 2: level two (CHUNKED) or the single target value the accept test needs (FLAT)
+  const int j_c = s - 1;   // a CORRECT row is the position rejected at step s - 1
+  const bool residual = tot_c.x > -INFINITY;
+  L2Result rd = {-1, 0.0f, 0.0f}, rf = {-1, 0.0f, 0.0f};
+  const void* targ_s = (const char*)p.target + ((size_t)b * (K + 1) + s) * V * esz;
+  if (NOISE == SPEC_NOISE_CHUNKED) {
+    const int g = threadIdx.x >> 7, gt = threadIdx.x & 127;
+    L2Job jb;
+    jb.kind = L2_NONE;
+    jb.chunk = -1;
+    jb.prev = -1;
+    jb.key = 0;
+    jb.base_row = nullptr;
+    jb.targ_row = nullptr;
+    jb.invT = invT;
+    jb.lse_p = 0.0f;
+    jb.lse_q = 0.0f;
+    jb.want_target = false;
+    if (g == 0) {
+      if (hasD && isfinite(tot_d.x)) {
+        jb.kind = L2_DRAFT;
+        jb.chunk = __float_as_int(tot_d.z);
+        jb.prev = prev_d;
+        jb.key = key_from(kreq, s, ST_DRAFT);
+        jb.base_row = (const char*)p.base + ((size_t)b * K + s) * V * esz;
+        jb.targ_row = targ_s;
+        jb.want_target = (roles & RO_LSEP) != 0;
+      }
+    } else if (hasC) {
+      jb.chunk = __float_as_int(residual ? tot_c.z : tot_c2.z);
+      jb.key = key_from(kreq, j_c, ST_RESIDUAL);
+      jb.targ_row = (const char*)p.target + ((size_t)b * (K + 1) + j_c) * V * esz;
+      if (residual) {
+        jb.kind = L2_RESIDUAL;
+        jb.prev = prev_c;
+        jb.base_row = (const char*)p.base + ((size_t)b * K + j_c) * V * esz;
+        jb.lse_p = lse_p_c;
+        jb.lse_q = lse_q_c;
+      } else {
+        jb.kind = L2_TARGET;
+      }
+    } else if ((roles & RO_BONUS) && isfinite(tot_p.x)) {
+      jb.kind = L2_TARGET;
+      jb.chunk = __float_as_int(tot_p.z);
+      jb.key = key_from(kreq, s, ST_BONUS);
+      jb.targ_row = targ_s;
+    }
+    const L2Result r = level_two<DT>(p, jb, gt, lds2[g]);
+    // results of the other group through LDS
+    __shared__ L2Result res[2];
+    if (gt == 0) res[g] = r;
+    __syncthreads();
+    rd = res[0];
+    rf = res[1];
+  } else {
+    rd.v = hasD ? __float_as_int(tot_d.z) : -1;
+    rd.sx = tot_d.w;
+    if ((roles & RO_LSEP) && rd.v >= 0 && rd.v < V) rd.tx = load1<DT>(targ_s, (size_t)rd.v);
+    rf.v = hasC ? __float_as_int(residual ? tot_c.z : tot_c2.z) : ((roles & RO_BONUS) ? __float_as_int(tot_p.z) : -1);
+  }
+
+  // ---- round 3: decision and outputs (uniform across the workgroup; thread 0 writes scalars)
   bool invalid = false, rejected_now = false;
   int final_tok = -1;
   float logq_s = NAN;
   int x_s = -1;
-
-  if (roles & RO_DRAFT) {
-    const int slot = p.slots[b];
-    const float4 tot = reduce_parts(p.part_bias + (size_t)slot * p.nrA, p.nrA, red);
-    const float lse_q = tot.x;
-    if (!isfinite(lse_q)) {
+  if (hasD) {
+    const float lse_q = tot_d.x;
+    if (!isfinite(lse_q) || rd.v < 0) {
       invalid = true;
     } else {
-      float sx;
-      if (NOISE == SPEC_NOISE_CHUNKED) {
-        const int prev = (s == 0) ? x0 : p.xs[(size_t)b * K + s - 1];
-        const void* base_row = (const char*)p.base + ((size_t)b * K + s) * V * esz;
-        const uint64_t key2 = row_key(p.seed, g, (uint64_t)s, ST_DRAFT);
-        x_s = level_two<DT>(p, L2_DRAFT, __float_as_int(tot.z), key2, base_row, nullptr, prev, invT, 0.f, 0.f, &sx,
-                            red);
-      } else {
-        x_s = __float_as_int(tot.z);
-        sx = tot.w;
-      }
-      if (x_s < 0) {
-        invalid = true;
-      } else {
-        logq_s = sx - lse_q;
-        if (threadIdx.x == 0) {
-          p.xs[(size_t)b * K + s] = x_s;
-          p.lse_q[(size_t)b * K + s] = lse_q;
-          p.logq[(size_t)b * K + s] = logq_s;
-          if (p.d_draft) p.d_draft[(size_t)b * K + s] = x_s;
-          if (p.d_logq) p.d_logq[(size_t)b * K + s] = logq_s;
-        }
+      x_s = rd.v;
+      logq_s = rd.sx - lse_q;
+      if (threadIdx.x == 0) {
+        p.xs[(size_t)b * K + s] = x_s;
+        p.lse_q[(size_t)b * K + s] = lse_q;
+        p.logq[(size_t)b * K + s] = logq_s;
+        if (p.d_draft) p.d_draft[(size_t)b * K + s] = x_s;
+        if (p.d_logq) p.d_logq[(size_t)b * K + s] = logq_s;
       }
     }
   }
-
   if (!invalid && (roles & RO_LSEP)) {
-    const int slot = p.slots[2 * B + b];
-    const float4 tot = reduce_parts(p.part_plain + (size_t)slot * p.nrB, p.nrB, red);
-    const float lse_p = tot.x;
+    const float lse_p = tot_p.x;
     if (!isfinite(lse_p) || x_s < 0) {
       invalid = true;
     } else {
-      const void* targ_row = (const char*)p.target + ((size_t)b * (K + 1) + s) * V * esz;
-      const float logp_s = load1<DT>(targ_row, (size_t)x_s) * invT - lse_p;
-      const uint32_t ub = bits_at(row_key(p.seed, g, (uint64_t)s, ST_ACCEPT), 0);
+      const float logp_s = rd.tx * invT - lse_p;
+      const uint32_t ub = bits_at(key_from(kreq, s, ST_ACCEPT), 0);
       const double u = ((double)ub + 0.5) * 0x1p-32;
       const double ratio = exp((double)logp_s - (double)logq_s);
       if (u < ratio) {
@@ -1150,71 +1418,44 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
       }
     }
   }
-
   if (!invalid && (roles & RO_BONUS)) {
-    const int slot = p.slots[2 * B + b];
-    const float4 tot = reduce_parts(p.part_plain + (size_t)slot * p.nrB, p.nrB, red);
-    if (!isfinite(tot.x)) {
-      invalid = true;
-    } else {
-      if (NOISE == SPEC_NOISE_CHUNKED) {
-        const void* targ_row = (const char*)p.target + ((size_t)b * (K + 1) + s) * V * esz;
-        const uint64_t key2 = row_key(p.seed, g, (uint64_t)s, ST_BONUS);
-        final_tok = level_two<DT>(p, L2_TARGET, __float_as_int(tot.z), key2, nullptr, targ_row, -1, invT, 0.f, 0.f,
-                                  nullptr, red);
-      } else {
-        final_tok = __float_as_int(tot.z);
-      }
-      if (final_tok < 0) invalid = true;
-    }
+    if (!isfinite(tot_p.x)) invalid = true;
+    else final_tok = rf.v;
+    if (final_tok < 0) invalid = true;
   }
-
-  if (!invalid && (roles & RO_CORRECT)) {
-    const int j = acc;   // rejected position
-    const int slot = p.slots[B + b];
-    const float4 prim = reduce_parts(p.part_bias + (size_t)slot * p.nrA, p.nrA, red);
-    const float4 sec = reduce_parts(p.part_bias2 + (size_t)slot * p.nrA, p.nrA, red);
-    const bool residual = prim.x > -INFINITY;
-    if (NOISE == SPEC_NOISE_CHUNKED) {
-      const int prev = (j == 0) ? x0 : p.xs[(size_t)b * K + j - 1];
-      const void* base_row = (const char*)p.base + ((size_t)b * K + j) * V * esz;
-      const void* targ_row = (const char*)p.target + ((size_t)b * (K + 1) + j) * V * esz;
-      const uint64_t key2 = row_key(p.seed, g, (uint64_t)j, ST_RESIDUAL);
-      const float lse_p = p.lse_p[(size_t)b * (K + 1) + j];
-      const float lse_q = p.lse_q[(size_t)b * K + j];
-      final_tok = residual ? level_two<DT>(p, L2_RESIDUAL, __float_as_int(prim.z), key2, base_row, targ_row, prev,
-                                           invT, lse_p, lse_q, nullptr, red)
-                           : level_two<DT>(p, L2_TARGET, __float_as_int(sec.z), key2, nullptr, targ_row, -1, invT,
-                                           0.f, 0.f, nullptr, red);
-    } else {
-      final_tok = __float_as_int(residual ? prim.z : sec.z);
-    }
+  if (!invalid && hasC) {
+    final_tok = rf.v;
     if (final_tok < 0) invalid = true;
   }
 
-  if (threadIdx.x == 0) {
-    int nr = 0;
-    if (invalid) {
-      phase = PH_INVALID;
-      p.accepted_len[b] = -1;
-      for (int i = 0; i <= K; i++) p.tokens[(size_t)b * (K + 1) + i] = -1;
-      if (p.d_verify_len) p.d_verify_len[b] = -1;
-      for (int i = 0; i < K; i++) {
-        if (p.d_draft) p.d_draft[(size_t)b * K + i] = -1;
-        if (p.d_logq) p.d_logq[(size_t)b * K + i] = NAN;
-        if (p.d_logp) p.d_logp[(size_t)b * K + i] = NAN;
-      }
-    } else {
-      if (final_tok >= 0) {
-        for (int i = 0; i < acc; i++) p.tokens[(size_t)b * (K + 1) + i] = p.xs[(size_t)b * K + i];
-        p.tokens[(size_t)b * (K + 1) + acc] = final_tok;
-        p.accepted_len[b] = acc;
-        phase = PH_DONE;
-      }
-      if (s + 1 < L) nr |= RO_DRAFT;
-      if (phase == PH_ALIVE && acc == s + 1) nr |= (s + 1 < L) ? RO_LSEP : RO_BONUS;
-      if (rejected_now) nr |= RO_CORRECT;
+  const int t = threadIdx.x;
+  if (invalid) {
+    if (t <= K) p.tokens[(size_t)b * (K + 1) + t] = -1;
+    if (t < K) {
+      if (p.d_draft) p.d_draft[(size_t)b * K + t] = -1;
+      if (p.d_logq) p.d_logq[(size_t)b * K + t] = NAN;
+      if (p.d_logp) p.d_logp[(size_t)b * K + t] = NAN;
     }
+    if (t == 0) {
+      p.accepted_len[b] = -1;
+      if (p.d_verify_len) p.d_verify_len[b] = -1;
+      p.phase[b] = PH_INVALID;
+      p.acc[b] = acc;
+      roles_next[b] = 0;
+    }
+    return;
+  }
+  if (final_tok >= 0) {
+    phase = PH_DONE;
+    if (t < acc) p.tokens[(size_t)b * (K + 1) + t] = x_t;   // t < acc <= s: drafted before this step
+    if (t == acc) p.tokens[(size_t)b * (K + 1) + t] = final_tok;
+    if (t == 0) p.accepted_len[b] = acc;
+  }
+  if (t == 0) {
+    int nr = 0;
+    if (s + 1 < L) nr |= RO_DRAFT;
+    if (phase == PH_ALIVE && acc == s + 1) nr |= (s + 1 < L) ? RO_LSEP : RO_BONUS;
+    if (rejected_now) nr |= RO_CORRECT;
     p.phase[b] = phase;
     p.acc[b] = acc;
     roles_next[b] = (uint8_t)nr;
@@ -1226,8 +1467,8 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
 // ------------------------------------------------------------------------------------------
 struct Layout {
   size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
-      off_pbias, off_pbias2, off_pplain, total;
-  int nrA, nrB, nrA_xcd, nrb, gridA, gridB;
+      off_pbias, off_pbias2, off_pplain, off_konst, total;
+  int nrA, nrB, gridB;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1250,9 +1491,6 @@ static Layout layout(const spec_dims* d) {
   const size_t B = (size_t)d->B, K = (size_t)d->K;
   l.nrA = (d->V + TILE_A - 1) / TILE_A;
   l.nrB = (d->V + TILE_B - 1) / TILE_B;
-  l.nrA_xcd = (l.nrA + 7) / 8;
-  l.nrb = (int)((2 * B + RB - 1) / RB);
-  l.gridA = 8 * l.nrA_xcd * l.nrb;
   l.gridB = (int)B * l.nrB;
   size_t o = 0;
   l.off_L = o; o = align256(o + 4 * B);
@@ -1266,9 +1504,11 @@ static Layout layout(const spec_dims* d) {
   l.off_logq = o; o = align256(o + 4 * B * K);
   l.off_lse_p = o; o = align256(o + 4 * B * (K + 1));
   l.off_logp = o; o = align256(o + 4 * B * K);
-  l.off_pbias = o; o = align256(o + 16 * 2 * B * (size_t)l.nrA);
-  l.off_pbias2 = o; o = align256(o + 16 * 2 * B * (size_t)l.nrA);
+  const size_t nslots = (size_t)bias_slots_max(d->B);
+  l.off_pbias = o; o = align256(o + 16 * nslots * (size_t)l.nrA);
+  l.off_pbias2 = o; o = align256(o + 16 * nslots * (size_t)l.nrA);
   l.off_pplain = o; o = align256(o + 16 * B * (size_t)l.nrB);
+  l.off_konst = o; o = align256(o + 32);
   l.total = o;
   return l;
 }
@@ -1285,7 +1525,7 @@ static int cu_count() {
   return n;
 }
 
-// resident grids: k_bias holds two 256-thread workgroups per CU, k_plain three
+// resident grid of a kernel with per_cu workgroups per CU
 static int grid_for(int max_items, int per_cu) {
   const int resident = per_cu * cu_count();
   return max_items < resident ? max_items : resident;
@@ -1314,13 +1554,15 @@ struct Timing {
 
 template <int DT, int NOISE, bool VEC>
 static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const Timing& tm) {
-  const size_t lists = (size_t)6 * p.B;
   for (int s = 0; s <= p.K; s++) {
     const int k0 = 1 + 3 * s;
-    hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(cu_count()), dim3(NT), bias_meta_bytes(p.B) + lists, st,
-                          tm.start(k0),
-                          tm.stop(k0), 0, p, s);
-    hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 3)), dim3(NT), lists, st,
+    if (DT == SPEC_BF16 && VEC)
+      hipExtLaunchKernelGGL((k_bias_fast<NOISE>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st, tm.start(k0),
+                            tm.stop(k0), 0, p, s);
+    else
+      hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st,
+                            tm.start(k0), tm.stop(k0), 0, p, s);
+    hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 3)), dim3(NT), plain_dyn_bytes(p.B), st,
                           tm.start(k0 + 1), tm.stop(k0 + 1), 0, p, s);
     hipExtLaunchKernelGGL((k_merge<DT, NOISE>), dim3(p.B), dim3(NT), 0, st, tm.start(k0 + 2), tm.stop(k0 + 2), 0, p,
                           s);
@@ -1413,11 +1655,9 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
   p.part_bias = (float4*)(ws + l.off_pbias);
   p.part_bias2 = (float4*)(ws + l.off_pbias2);
   p.part_plain = (float4*)(ws + l.off_pplain);
+  p.konst = (const u32x4*)(ws + l.off_konst);
   p.nrA = l.nrA;
   p.nrB = l.nrB;
-  p.nrA_xcd = l.nrA_xcd;
-  p.nrb = l.nrb;
-  p.gridA = l.gridA;
 
   // vector loads need 16-byte aligned rows
   const size_t esz = d->dtype == SPEC_FP32 ? 4 : 2;
