@@ -549,6 +549,12 @@ __device__ __forceinline__ void load_w(const Params& p, int range, bf16x8 (&wf)[
     for (int t = 0; t < 16; t++)
       wf[f][t] = *((in && t < T16) ? (const bf16x8*)(wr + 8 * t) : (const bf16x8*)p.konst);
   }
+  // the fragments live in accumulation registers (the MFMA reads its A operand from there), which
+  // leaves the vector registers to the logit tiles and the B operands
+#pragma unroll
+  for (int f = 0; f < 2; f++)
+#pragma unroll
+    for (int t = 0; t < 16; t++) asm volatile("" : "+a"(wf[f][t]));
 }
 
 // Markov bias of the lane's 32 columns (element i: column v0 + 32 (i / 16) + i % 16) for row
@@ -560,12 +566,16 @@ __device__ __forceinline__ void mfma_bias(const bf16x8 (&wf)[2][16], const uint1
   const int T16 = R >> 4, kb = h * (R >> 1);
   f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   f32x16 acc1 = acc0;
+  // every B operand is read before the first MFMA, so the LDS latency is paid once
+  bf16x8 bop[16];
+#pragma unroll
+  for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)&sA[m][kb + 8 * (t < T16 ? t : 0)];
+  __builtin_amdgcn_sched_barrier(0);   // keep all reads ahead of the MFMA chain
 #pragma unroll
   for (int t = 0; t < 16; t++) {
     // for t >= R/16 both operands are zero (zero W fragments; sA zero past the rank)
-    const bf16x8 bop = *(const bf16x8*)&sA[m][kb + 8 * (t < T16 ? t : 0)];
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop[t], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop[t], acc1, 0, 0, 0);
   }
 #pragma unroll
   for (int q = 0; q < 16; q++) {
