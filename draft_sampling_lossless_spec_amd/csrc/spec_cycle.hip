@@ -40,7 +40,8 @@ enum : int { PH_ALIVE = 0, PH_REJECTED = 1, PH_DONE = 2, PH_INVALID = 3 };
 constexpr int NT = 256;             // threads per workgroup
 constexpr int SUB = 32;             // bias slots per MFMA sub-block
 constexpr int TILE_A = 256;         // vocabulary columns per bias-row unit: 4 waves x 64
-constexpr int TILE_B = NT * 2 * CHUNK;  // vocabulary columns per plain-row item: two chunks per thread
+constexpr int KB_LOADS = 8;                 // 16-byte loads per lane per plain-row item
+constexpr int TILE_B = KB_LOADS * 64 * 8;   // vocabulary columns per plain-row item (4096): one wave
 constexpr int MAX_B = 1024;
 constexpr int MAX_K = 32;
 constexpr int MAX_R = 256;
@@ -891,12 +892,12 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
 }
 
 // ------------------------------------------------------------------------------------------
-// kind B: plain target rows (LSEP / BONUS), 128 consecutive columns (two chunks) per thread,
-// every load of the item issued before any arithmetic
+// plain target rows (LSEP / BONUS): items of TILE_B columns, one wave each, no barrier; every load
+// of the item is issued before any arithmetic
 // ------------------------------------------------------------------------------------------
-// kind B layout: load k (0..15) of a thread covers 8 columns at 2048 k + 8 t of the item, so every
-// load instruction of a wave reads 1 KiB of contiguous memory; the 64 columns of a noise chunk
-// are the 8 values of 8 neighbouring lanes.
+// layout: load k (0 .. KB_LOADS - 1) of lane l covers 8 columns at 512 k + 8 l of the item, so
+// every load instruction reads 1 KiB of contiguous memory; the 64 columns of a noise chunk are the
+// 8 values of 8 neighbouring lanes, and lane l keeps the chunk of round l % 8.
 template <int DT>
 struct Raw8 {
   u32x4 w[DT == SPEC_BF16 ? 1 : 2];
@@ -911,20 +912,17 @@ __device__ __forceinline__ float raw8_at(const Raw8<DT>& r, int i) {
   return __uint_as_float(r.w[i >> 2][i & 3]);
 }
 
-
-constexpr int KB_LOADS = 16;   // loads of 8 columns per thread per kind-B item
-
 template <int DT, int NOISE, bool VEC>
-__device__ void kind_b(const Params& p, int s, int b, int pslot, int range, float4* redb) {
+__device__ void plain_item(const Params& p, int s, int b, int pslot, int range) {
   const int K = p.K, V = p.V;
+  const int lane = threadIdx.x & 63;
   const int role = p.roles[(size_t)(s & 1) * p.B + b] & (RO_LSEP | RO_BONUS);
   const int j = s;   // LSEP verifies position s; BONUS reads row L_b == s
   const float invT = 1.0f / p.temp[b];
   const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
   const void* row = (const char*)p.target + ((size_t)b * (K + 1) + j) * (size_t)V * esz;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vbase = range * TILE_B;
-  const int vt = vbase + 8 * threadIdx.x;           // + 2048 k
+  const int vt = vbase + 8 * lane;   // + 512 k
   Raw8<DT> r[KB_LOADS];
   if (VEC) {
     // rows are 16-byte aligned and V % 8 == 0 (bf16) / V % 4 == 0 (fp32), so each 16-byte load
@@ -932,10 +930,10 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
     const uint32_t ninf = (DT == SPEC_BF16) ? 0xFF80FF80u : 0xFF800000u;
 #pragma unroll
     for (int k = 0; k < KB_LOADS; k++) {
-      const u32x4* q = (const u32x4*)((const char*)row + (size_t)(vt + 2048 * k) * esz);
+      const u32x4* q = (const u32x4*)((const char*)row + (size_t)(vt + 512 * k) * esz);
 #pragma unroll
       for (int u = 0; u < (DT == SPEC_BF16 ? 1 : 2); u++) {
-        const int vv = vt + 2048 * k + 4 * u;
+        const int vv = vt + 512 * k + 4 * u;
         if (vv < V) r[k].w[u] = __builtin_nontemporal_load(q + u);
         else r[k].w[u] = (u32x4){ninf, ninf, ninf, ninf};
       }
@@ -946,7 +944,7 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
     for (int k = 0; k < KB_LOADS; k++) {
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const int v = vt + 2048 * k + i;
+        const int v = vt + 512 * k + i;
         const float x = (v < V) ? load1<DT>(row, (size_t)v) : -INFINITY;
         if (DT == SPEC_BF16) {
           const uint32_t hb = __float_as_uint(x) >> 16;   // exact: the value came from a bf16
@@ -960,9 +958,8 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
   }
   const uint64_t g = (uint64_t)(p.req_off + b);
   const float sc2 = invT * LOG2E;
-  // log-mass of each 64-column chunk (8 lanes x 8 values); the rounds are independent and every
-  // lane keeps the two chunks it owns: rounds k = lane % 8 and lane % 8 + 8
-  float own0 = -INFINITY, own1 = -INFINITY;
+  // log-mass of each 64-column chunk (8 lanes x 8 values); the rounds are independent
+  float own = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KB_LOADS; k++) {
     float mx = raw8_at<DT>(r[k], 0);
@@ -980,27 +977,16 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
     }
     sum = sum8(sum);
     const float lse = (mx == -INFINITY) ? sum : mx * invT + lg2(sum) * LN2;
-    if ((lane & 7) == (k & 7)) {
-      if (k < 8) own0 = lse;
-      else own1 = lse;
-    }
+    if ((lane & 7) == k) own = lse;
   }
-  float4 part = make_float4(lse2(own0, own1), -INFINITY, __int_as_float(-1), 0.0f);
+  float4 part = make_float4(own, -INFINITY, __int_as_float(-1), 0.0f);
   if (role == RO_BONUS) {
     if (NOISE == SPEC_NOISE_CHUNKED) {
       const uint64_t k1 = row_key(p.seed, g, (uint64_t)j, ST_BONUS_C);
-#pragma unroll
-      for (int o = 0; o < 2; o++) {
-        const float lse = o ? own1 : own0;
-        const int k = (lane & 7) + 8 * o;
-        const int c = (vbase + 2048 * k) / CHUNK + (lane >> 3) + 8 * wave;
-        if (lse > -INFINITY) {
-          const float sc = lse + gumbel_bits(bits_at(k1, (uint32_t)c));
-          if (better(sc, c, part.y, __float_as_int(part.z))) {
-            part.y = sc;
-            part.z = __int_as_float(c);
-          }
-        }
+      const int c = (vbase + 512 * (lane & 7)) / CHUNK + (lane >> 3);
+      if (own > -INFINITY) {
+        part.y = own + gumbel_bits(bits_at(k1, (uint32_t)c));
+        part.z = __int_as_float(c);
       }
     } else {
       const uint64_t k2 = row_key(p.seed, g, (uint64_t)j, ST_BONUS);
@@ -1008,7 +994,7 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
       int bv = -1;
 #pragma unroll 1
       for (int k = 0; k < KB_LOADS; k++) {
-        const int v0 = vt + 2048 * k;
+        const int v0 = vt + 512 * k;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
           const int v = v0 + i;
@@ -1031,7 +1017,7 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
       part.z = __int_as_float(bv);
     }
   }
-  // workgroup reduction
+  // wave reduction
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     float4 y;
@@ -1041,21 +1027,13 @@ __device__ void kind_b(const Params& p, int s, int b, int pslot, int range, floa
     y.w = __shfl_xor(part.w, o, 64);
     part = merge_part(part, y);
   }
-  __syncthreads();
-  if (lane == 0) redb[wave] = part;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float4 rr = redb[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; w++) rr = merge_part(rr, redb[w]);
-    p.part_plain[(size_t)pslot * p.nrB + range] = rr;
-  }
+  if (lane == 0) p.part_plain[(size_t)pslot * p.nrB + range] = part;
 }
 
 // Row sweeps of one step.  Every workgroup rebuilds the step's row lists from the role bytes;
 // the bias-row sweep also stages each request's bias-row inputs.  k_bias runs one workgroup per
 // CU (its W fragments fill the register file); k_plain streams the target rows of LSEP / BONUS
-// roles at three workgroups per CU.
+// roles, one wave per item, six workgroups per CU.
 // dynamic LDS of the bias-row sweeps: per-request table [B], then the bias and plain lists
 __host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
   return (size_t)B * sizeof(ReqMeta) + (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t);
@@ -1092,18 +1070,18 @@ __global__ __launch_bounds__(NT, 1) void k_bias(Params p, int s) {
 }
 
 template <int DT, int NOISE, bool VEC>
-__global__ __launch_bounds__(NT, 3) void k_plain(Params p, int s) {
+__global__ __launch_bounds__(NT, 6) void k_plain(Params p, int s) {
   extern __shared__ uint16_t dyn_lists[];
   __shared__ uint64_t scan_tmp[NT / 64];
-  __shared__ float4 redb[NT / 64];
   uint16_t* bias_list = dyn_lists;
   uint16_t* plain_list = dyn_lists + bias_slots_max(p.B);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
   const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, nullptr, false);
   const int n_items = ls.n_plain * p.nrB;
-  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+  const int nw = gridDim.x * (NT / 64);
+  for (int it = blockIdx.x * (NT / 64) + (threadIdx.x >> 6); it < n_items; it += nw) {
     const int pslot = it / p.nrB, range = it % p.nrB;
-    kind_b<DT, NOISE, VEC>(p, s, plain_list[pslot], pslot, range, redb);
+    plain_item<DT, NOISE, VEC>(p, s, plain_list[pslot], pslot, range);
   }
 }
 
@@ -1501,7 +1479,7 @@ static Layout layout(const spec_dims* d) {
   const size_t B = (size_t)d->B, K = (size_t)d->K;
   l.nrA = (d->V + TILE_A - 1) / TILE_A;
   l.nrB = (d->V + TILE_B - 1) / TILE_B;
-  l.gridB = (int)B * l.nrB;
+  l.gridB = (int)((B * l.nrB + NT / 64 - 1) / (NT / 64));
   size_t o = 0;
   l.off_L = o; o = align256(o + 4 * B);
   l.off_acc = o; o = align256(o + 4 * B);
@@ -1572,7 +1550,7 @@ static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const
     else
       hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st,
                             tm.start(k0), tm.stop(k0), 0, p, s);
-    hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 3)), dim3(NT), plain_dyn_bytes(p.B), st,
+    hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 6)), dim3(NT), plain_dyn_bytes(p.B), st,
                           tm.start(k0 + 1), tm.stop(k0 + 1), 0, p, s);
     hipExtLaunchKernelGGL((k_merge<DT, NOISE>), dim3(p.B), dim3(NT), 0, st, tm.start(k0 + 2), tm.stop(k0 + 2), 0, p,
                           s);
