@@ -1095,32 +1095,76 @@ __global__ __launch_bounds__(NT, 6) void k_plain(Params p, int s) {
 //   3. decision, outputs and the roles of step s + 1.
 // ------------------------------------------------------------------------------------------
 
-// merge of four independent partial records over the workgroup; every thread gets the results
-__device__ __forceinline__ void reduce4(float4 (&a)[4], float4 (*lds)[NT / 64]) {
+// Running reduction of partial records {log-mass, best score, best index, aux}: the log-mass is
+// kept as m + log(s) (one exponential per record instead of a full log-sum-exp), a NaN anywhere
+// is remembered in `nan`; the winner follows `better`.
+struct PartAcc {
+  float m, s, sc, aux;
+  int ix, nan;
+};
+
+__device__ __forceinline__ void pacc_init(PartAcc& a) {
+  a.m = -INFINITY;
+  a.s = 0.0f;
+  a.sc = -INFINITY;
+  a.aux = 0.0f;
+  a.ix = -1;
+  a.nan = 0;
+}
+
+__device__ __forceinline__ void pacc_mass(PartAcc& a, float m, float s, int nan) {
+  a.nan |= nan;
+  if (m > a.m) {
+    a.s = s + a.s * ex2((a.m - m) * LOG2E);   // a.m = -inf: the old sum is 0
+    a.m = m;
+  } else if (m > -INFINITY) {
+    a.s += s * ex2((m - a.m) * LOG2E);
+  }
+}
+
+__device__ __forceinline__ void pacc_best(PartAcc& a, float sc, int ix, float aux) {
+  if (ix >= 0 && (a.ix < 0 || better(sc, ix, a.sc, a.ix))) {
+    a.sc = sc;
+    a.ix = ix;
+    a.aux = aux;
+  }
+}
+
+__device__ __forceinline__ void pacc_add(PartAcc& a, float4 r) {
+  if (r.x != r.x) a.nan = 1;
+  else pacc_mass(a, r.x, 1.0f, 0);
+  pacc_best(a, r.y, __float_as_int(r.z), r.w);
+}
+
+__device__ __forceinline__ float4 pacc_final(const PartAcc& a) {
+  const float lse = a.nan ? NAN : (a.m == -INFINITY ? -INFINITY : a.m + lg2(a.s) * LN2);
+  return make_float4(lse, a.sc, __int_as_float(a.ix), a.aux);
+}
+
+// Reduce n partial records with one wave (up to 16 per lane in flight at once); result in every lane.
+__device__ __forceinline__ float4 wave_reduce_parts(const float4* parts, int n) {
+  const int lane = threadIdx.x & 63;
+  PartAcc a;
+  pacc_init(a);
+  for (int i0 = 0; i0 < n; i0 += 16 * 64) {
+    float4 buf[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      const int i = i0 + 64 * k + lane;
+      buf[k] = (i < n) ? parts[i] : empty_part();
+    }
+#pragma unroll
+    for (int k = 0; k < 16; k++) pacc_add(a, buf[k]);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      float4 y;
-      y.x = __shfl_xor(a[k].x, o, 64);
-      y.y = __shfl_xor(a[k].y, o, 64);
-      y.z = __shfl_xor(a[k].z, o, 64);
-      y.w = __shfl_xor(a[k].w, o, 64);
-      a[k] = merge_part(a[k], y);
-    }
+    const float m2 = __shfl_xor(a.m, o, 64), s2 = __shfl_xor(a.s, o, 64);
+    const float sc2 = __shfl_xor(a.sc, o, 64), aux2 = __shfl_xor(a.aux, o, 64);
+    const int ix2 = __shfl_xor(a.ix, o, 64), nan2 = __shfl_xor(a.nan, o, 64);
+    pacc_mass(a, m2, s2, nan2);
+    pacc_best(a, sc2, ix2, aux2);
   }
-  if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) lds[k][threadIdx.x >> 6] = a[k];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 4; k++) {
-    float4 r = lds[k][0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; w++) r = merge_part(r, lds[k][w]);
-    a[k] = r;
-  }
+  return pacc_final(a);
 }
 
 // half of the Markov-bias dot product A[prev] . W[v] (k in [hh R/2, (hh + 1) R/2)), fp32 accumulate
@@ -1277,30 +1321,18 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
   const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
   const bool hasD = roles & RO_DRAFT, hasC = roles & RO_CORRECT, hasP = roles & (RO_LSEP | RO_BONUS);
 
-  // ---- round 1: partials of every row
-  float4 t4[4] = {empty_part(), empty_part(), empty_part(), empty_part()};   // DRAFT, CORRECT, fallback, plain
-  for (int i0 = 0; i0 < p.nrA; i0 += 4 * NT) {
-    // four partials per thread and row in flight at once
-    float4 pd[4], pc[4], pc2[4];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int i = i0 + k * NT + threadIdx.x;
-      const bool in = i < p.nrA;
-      pd[k] = (hasD && in) ? p.part_bias[(size_t)slot_d * p.nrA + i] : empty_part();
-      pc[k] = (hasC && in) ? p.part_bias[(size_t)slot_c * p.nrA + i] : empty_part();
-      pc2[k] = (hasC && in) ? p.part_bias2[(size_t)slot_c * p.nrA + i] : empty_part();
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      t4[0] = merge_part(t4[0], pd[k]);
-      t4[1] = merge_part(t4[1], pc[k]);
-      t4[2] = merge_part(t4[2], pc2[k]);
-    }
+  // ---- round 1: partials of every row, one wave per record: DRAFT, CORRECT, its fallback, plain
+  {
+    const int w = threadIdx.x >> 6;
+    float4 r = empty_part();
+    if (w == 0 && hasD) r = wave_reduce_parts(p.part_bias + (size_t)slot_d * p.nrA, p.nrA);
+    if (w == 1 && hasC) r = wave_reduce_parts(p.part_bias + (size_t)slot_c * p.nrA, p.nrA);
+    if (w == 2 && hasC) r = wave_reduce_parts(p.part_bias2 + (size_t)slot_c * p.nrA, p.nrA);
+    if (w == 3 && hasP) r = wave_reduce_parts(p.part_plain + (size_t)slot_p * p.nrB, p.nrB);
+    if ((threadIdx.x & 63) == 0) red[0][w] = r;
   }
-  for (int i = threadIdx.x; i < p.nrB; i += NT)
-    if (hasP) t4[3] = merge_part(t4[3], p.part_plain[(size_t)slot_p * p.nrB + i]);
-  reduce4(t4, red);
-  const float4 tot_d = t4[0], tot_c = t4[1], tot_c2 = t4[2], tot_p = t4[3];
+  __syncthreads();
+  const float4 tot_d = red[0][0], tot_c = red[0][1], tot_c2 = red[0][2], tot_p = red[0][3];
 
   // ---- round 2: level two (CHUNKED) or the single target value the accept test needs (FLAT)
   const int j_c = s - 1;   // a CORRECT row is the position rejected at step s - 1
