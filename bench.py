@@ -47,6 +47,25 @@ def compulsory_bytes(cfg, L, a):
     return (e * V * (sL + sa1) + e * R * V + e * R * sL + 4 * B * K + 12 * B + 4 * B * (K + 1))
 
 
+def measured_traffic(kernel, workload, noise):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE / WRITE_SIZE record committed
+    under profiles/, scaled by a plain copy's readings; None unless the record was taken on the
+    current kernel source and on this workload."""
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "draft_sampling_lossless_spec_amd", "csrc", "spec_cycle.hip")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if noise != "chunked" or not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -58,7 +77,21 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = the whole batch of one cycle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
+    if args.copy_bytes > 0:
+        import torch
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": 5}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
               "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -190,6 +223,7 @@ def main():
                "sample": f"first {n} of {B} requests of one cycle of the same workload ({dt:.1f} s wall, "
                          f"fp64 C + OpenMP)"}
 
+    traffic = measured_traffic(dom, cfg.name, args.noise) if cfg.dtype == 1 else None
     line = {
         "metric": METRIC, "value": value, "unit": "verified draft tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -199,7 +233,9 @@ def main():
                    "steps_with_work": n_active},
         "hbm_frac_cycle": cbytes / t_cycle / HBM_PEAK,
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": None, "kernel": dom, "launches_per_cycle": K + 1},
+                     "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom, "launches_per_cycle": K + 1,
+                     "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"] / (K + 1)},
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
