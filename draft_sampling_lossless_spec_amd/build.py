@@ -12,6 +12,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     # no packed fp32 ops in any of this library's code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary vector registers: the element-wise epilogue then reads them
+    # directly instead of copying each one out of the accumulation registers first
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -331,6 +331,27 @@ __device__ __forceinline__ float pair_lse(const float* x) {
   return (mx == -INFINITY) ? sum : mx + lg2(sum) * LN2;
 }
 
+// log-sum-exp of invT * y over n values held by a lane and its partner lane (lane ^ 32), invT > 0:
+// the scale is folded into the exponent argument, max(invT y) = invT max(y); NaN-preserving
+template <int N>
+__device__ __forceinline__ float pair_lse_scaled(const float* y, float invT) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; i++) mx = fmaxf(mx, y[i]);
+  mx = fmaxf(mx, xor32f(mx));
+  float sum = 0.0f;
+  if (mx != -INFINITY) {
+    const float c = invT * LOG2E, mo = mx * c;
+#pragma unroll
+    for (int i = 0; i < N; i++) sum += ex2(fmaf(y[i], c, -mo));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i++) sum += y[i];   // every value -inf or NaN: keep a NaN visible
+  }
+  sum += xor32f(sum);
+  return (mx == -INFINITY) ? sum : mx * invT + lg2(sum) * LN2;
+}
+
 // best (score, index, aux) of a lane and its partner lane
 __device__ __forceinline__ void pair_best(float& sc, int& ix, float& aux) {
   const float s2 = xor32f(sc);
@@ -419,9 +440,9 @@ __device__ __forceinline__ RowMeta row_meta(const uint16_t* bias_list, const Req
 }
 
 // FLAT draft: best (s_v + G(key, v)) over the lane's 32 columns (element i is column
-// v0 + 32 (i / 16) + i % 16), s in x[]
-__device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint64_t key, float& best, int& bestv,
-                                            float& bests) {
+// v0 + 32 (i / 16) + i % 16), s = invT y with y in y[]
+__device__ __forceinline__ void flat_best32(const float* y, float invT, int v0, int V, uint64_t key, float& best,
+                                            int& bestv, float& bests) {
 #pragma unroll
   for (int i = 0; i < 32; i += 2) {
     const int v = v0 + 32 * (i >> 4) + (i & 15);
@@ -429,7 +450,7 @@ __device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint6
     const uint64_t w = pair_word(key, (uint32_t)v >> 1);
 #pragma unroll
     for (int e = 0; e < 2; e++) {
-      const float sv = x[i + e];
+      const float sv = y[i + e] * invT;
       const uint32_t bb = e ? (uint32_t)w : (uint32_t)(w >> 32);
       if (v + e >= V || !(sv > -INFINITY)) continue;
       if (sv + gumbel_bound(bb) + 1e-3f < best) continue;
@@ -443,11 +464,12 @@ __device__ __forceinline__ void flat_best32(const float* x, int v0, int V, uint6
   }
 }
 
-// DRAFT row over the 64 columns of a lane pair (lanes l and l ^ 32): x = draft logits / T of the
-// lane's 32 columns.  Every lane runs the cross-lane steps; inactive rows return an empty part.
+// DRAFT row over the 64 columns of a lane pair (lanes l and l ^ 32): y = draft logits of the lane's 32
+// columns, before the temperature (the row's logits are invT y).  Every lane runs the cross-lane
+// steps; inactive rows return an empty part.
 template <int NOISE>
-__device__ __forceinline__ float4 draft_part(const float (&x)[32], const RowMeta& rm, int chunk, int v0, int V) {
-  const float lse = pair_lse<32>(x);
+__device__ __forceinline__ float4 draft_part(const float (&y)[32], const RowMeta& rm, int chunk, int v0, int V) {
+  const float lse = pair_lse_scaled<32>(y, rm.invT);
   float4 o = empty_part();
   if (NOISE == SPEC_NOISE_CHUNKED) {
     if (rm.active) {
@@ -457,7 +479,7 @@ __device__ __forceinline__ float4 draft_part(const float (&x)[32], const RowMeta
   } else {
     float best = -INFINITY, bests = 0.0f;
     int bestv = -1;
-    if (rm.active) flat_best32(x, v0, V, rm.key, best, bestv, bests);
+    if (rm.active) flat_best32(y, rm.invT, v0, V, rm.key, best, bestv, bests);
     pair_best(best, bestv, bests);
     if (rm.active) o = make_float4(lse, best, __int_as_float(bestv), bests);
   }
@@ -465,18 +487,20 @@ __device__ __forceinline__ float4 draft_part(const float (&x)[32], const RowMeta
 }
 
 // CORRECT row at the rejected position: residual norm(max(0, p - q)) and, for a residual with no
-// mass, the target row itself.  x = draft logits / T, t = target logits / T of the lane's 32 columns.
+// mass, the target row itself.  y = draft logits, t = target logits of the lane's 32 columns, both
+// before the temperature.  Log-probabilities are formed in base 2 with one fused multiply-add each.
 template <int NOISE>
-__device__ __forceinline__ void correct_part(const float (&x)[32], const float (&t)[32], const RowMeta& rm, int chunk,
+__device__ __forceinline__ void correct_part(const float (&y)[32], const float (&t)[32], const RowMeta& rm, int chunk,
                                              int v0, int V, float4& oa, float4& ob) {
-  const float lse_t = pair_lse<32>(t);
+  const float lse_t = pair_lse_scaled<32>(t, rm.invT);
+  const float c = rm.invT * LOG2E, op = -rm.lse_p * LOG2E, oq = -rm.lse_q * LOG2E;
   float mass = 0.0f;
   float br = -INFINITY, bp = -INFINITY, dummy = 0.0f;
   int vr = -1, vp = -1;
 #pragma unroll
   for (int i = 0; i < 32; i++) {
-    const float lp = t[i] - rm.lse_p, lq = x[i] - rm.lse_q;
-    if (lp > lq) mass += ex2(lp * LOG2E) - ex2(lq * LOG2E);
+    const float lp2 = fmaf(t[i], c, op), lq2 = fmaf(y[i], c, oq);
+    if (lp2 > lq2) mass += ex2(lp2) - ex2(lq2);
   }
   if (NOISE == SPEC_NOISE_FLAT && rm.active) {
 #pragma unroll
@@ -484,12 +508,13 @@ __device__ __forceinline__ void correct_part(const float (&x)[32], const float (
       const int v = v0 + 32 * (i >> 4) + (i & 15);
       if (v >= V) continue;
       const float g = gumbel_bits(bits_at(rm.key, (uint32_t)v));
-      const float lp = t[i] - rm.lse_p, lq = x[i] - rm.lse_q;
+      const float ts = t[i] * rm.invT;
+      const float lp = ts - rm.lse_p, lq = y[i] * rm.invT - rm.lse_q;
       if (lp > lq) {
         const float sc = lp + logf(-expm1f(lq - lp)) + g;
         if (better(sc, v, br, vr)) { br = sc; vr = v; }
       }
-      if (t[i] > -INFINITY && better(t[i] + g, v, bp, vp)) { bp = t[i] + g; vp = v; }
+      if (ts > -INFINITY && better(ts + g, v, bp, vp)) { bp = ts + g; vp = v; }
     }
   }
   mass += xor32f(mass);
@@ -662,7 +687,7 @@ __device__ void bias_sweep_generic(const Params& p, int s, const Lists& ls, cons
         load16<DT, VEC>(base_row, v0 + 32, V, *(float(*)[16])(bx + 16));
       }
 #pragma unroll
-      for (int i = 0; i < 32; i++) x[i] = rm.active ? (bx[i] + x[i]) * rm.invT : -INFINITY;
+      for (int i = 0; i < 32; i++) x[i] = rm.active ? bx[i] + x[i] : -INFINITY;
     }
     WaveOut o;
     if (!corr_unit) {
@@ -678,7 +703,7 @@ __device__ void bias_sweep_generic(const Params& p, int s, const Lists& ls, cons
         load16<DT, VEC>(targ_row, v0 + 32, V, *(float(*)[16])(t + 16));
       }
 #pragma unroll
-      for (int i = 0; i < 32; i++) t[i] = rm.active ? t[i] * rm.invT : -INFINITY;
+      for (int i = 0; i < 32; i++) t[i] = rm.active ? t[i] : -INFINITY;
       correct_part<NOISE>(x, t, rm, chunk, v0, V, o.a, o.b);
     }
     if (h == 0) L.red[wave][m] = o;
@@ -739,7 +764,7 @@ __device__ __forceinline__ void fast_issue(const Params& p, int s, const Lists& 
       const int col = v0 + 32 * (i >> 1) + 8 * (i & 1);
       const bool act = ent != NO_ROW && col < p.V;
       P.x[i] = *(act ? (const u32x4*)(xr + col) : p.konst + 1);
-      if (corr) P.t[i] = *(act ? (const u32x4*)(tr + col) : p.konst + 1);
+      P.t[i] = *((act && corr) ? (const u32x4*)(tr + col) : p.konst + 1);   // same loads on every path
     }
   }
 }
@@ -780,14 +805,19 @@ __device__ __forceinline__ void argmax_round(float& sc, int& ix, float& aux) {
 
 // Partials of one finished unit, by every wave: lane group g (4 lanes) of wave w takes row
 // 8 w + g % 8, record a in lanes 0..31 and record b (CORRECT units) in lanes 32..63; lane i of the
-// group holds the chunk record of wave i.
-__device__ __forceinline__ void fast_flush(const Params& p, const uint16_t* bias_list, const float4 (*red)[NT / 64][SUB],
-                                           int slot0, int range) {
+// group holds the chunk record of wave i.  Split in the LDS read and the rest, so that the read can
+// be issued together with the MFMA operands and its latency hidden behind the MFMA chain.
+__device__ __forceinline__ float4 fast_flush_read(const float4 (*red)[NT / 64][SUB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return red[lane >= 32 ? 1 : 0][lane & 3][8 * wave + ((lane & 31) >> 2)];
+}
+
+__device__ __forceinline__ void fast_flush_finish(const Params& p, const uint16_t* bias_list, float4 h, int slot0,
+                                                  int range, bool valid) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = 8 * wave + ((lane & 31) >> 2);
   const int cw = lane & 3;
   const bool second = lane >= 32;
-  const float4 h = red[second ? 1 : 0][cw][r];
   float mx = fmaxf(h.x, dpp<0xB1>(h.x));
   mx = fmaxf(mx, dpp<0x4E>(mx));
   float e = (mx == -INFINITY) ? h.x : ex2((h.x - mx) * LOG2E);   // all -inf / NaN: keep a NaN visible
@@ -798,7 +828,7 @@ __device__ __forceinline__ void fast_flush(const Params& p, const uint16_t* bias
   int ix = __float_as_int(h.z);
   argmax_round<0xB1>(sc, ix, aux);
   argmax_round<0x4E>(sc, ix, aux);
-  if (cw == 0) {
+  if (valid && cw == 0) {
     const int slot = slot0 + r;
     const uint16_t e16 = bias_list[slot];
     if (e16 != NO_ROW) {
@@ -810,14 +840,16 @@ __device__ __forceinline__ void fast_flush(const Params& p, const uint16_t* bias
 }
 
 // One unit u from stage ST.  Pcur holds unit u's logit tiles (its A rows are already in stage ST),
-// Pnext unit u + 1's.  Order: W fragments if the column range changes (drained on the spot, so no
-// later wait ever waits on them), flush unit u - 1, MFMA, element-wise part from Pcur, issue unit
-// u + 2 into Pcur (clamped to the last unit, so the wait counts are the same on every path), store
-// unit u + 1's A rows into the other stage, barrier.
+// Pnext unit u + 1's; rm holds the row meta of unit u and leaves with unit u + 1's.  Order: W
+// fragments if the column range changes (drained on the spot, so no later wait ever waits on them);
+// every LDS read of the unit (B operands, unit u - 1's records, unit u + 1's row meta) ahead of the
+// MFMA chain; unit u - 1's partials; element-wise part from Pcur; issue unit u + 2 into Pcur
+// (clamped to the last unit, and with the same loads on every path, so the wait counts are the
+// same everywhere); store unit u + 1's A rows into the other stage; barrier.
 template <int NOISE, int ST>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
                                           const ReqMeta* req, FastLds& L, int u, int u0, int u1, int nsb,
-                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext) {
+                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext, RowMeta& rm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, h = lane >> 5;
   const int V = p.V;
@@ -826,37 +858,56 @@ __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& l
     load_w(p, range, wf);
     __builtin_amdgcn_s_waitcnt(0);
   }
-  if (u > u0) fast_flush(p, bias_list, L.red[ST ^ 1], ((u - 1) % nsb) * SUB, (u - 1) / nsb);
-  const RowMeta rm = row_meta(bias_list, req, s, slot0 + m);
-
-  float x[32];
-  mfma_bias(wf, L.sA[ST], p.R, x);
-  const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
-  const int chunk = vw / CHUNK;
-  const int v0 = vw + 16 * h;
+  const int T16 = p.R >> 4, kb = h * (p.R >> 1);
+  bf16x8 bop[16];
+#pragma unroll
+  for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)&L.sA[ST][m][kb + 8 * (t < T16 ? t : 0)];
+  const float4 hrec = fast_flush_read(L.red[ST ^ 1]);
+  const RowMeta rn = row_meta(bias_list, req, s, ((u + 1) % nsb) * SUB + m);
+  __builtin_amdgcn_sched_barrier(0);   // keep all reads ahead of the MFMA chain
+  // y = base logits + Markov bias: the accumulators start from the unit's base-logit tile
+  float y[32];
   {
     float bx[32];
     unpack32(Pcur.x, bx);
+    f32x16 acc0, acc1;
 #pragma unroll
-    for (int i = 0; i < 32; i++) x[i] = (bx[i] + x[i]) * rm.invT;
+    for (int q = 0; q < 16; q++) {
+      acc0[q] = bx[q];
+      acc1[q] = bx[16 + q];
+    }
+#pragma unroll
+    for (int t = 0; t < 16; t++) {
+      // for t >= R/16 both operands are zero (zero W fragments; sA zero past the rank)
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop[t], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop[t], acc1, 0, 0, 0);
+    }
+    fast_flush_finish(p, bias_list, hrec, ((u - 1) % nsb) * SUB, (u - 1) / nsb, u > u0);
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      y[q] = acc0[q];
+      y[16 + q] = acc1[q];
+    }
   }
+  const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
+  const int chunk = vw / CHUNK;
+  const int v0 = vw + 16 * h;
   float4 oa, ob;
   if (slot0 < ls.c0) {
-    oa = draft_part<NOISE>(x, rm, chunk, v0, V);
+    oa = draft_part<NOISE>(y, rm, chunk, v0, V);
     ob = empty_part();
   } else {
     float t[32];
     unpack32(Pcur.t, t);
-#pragma unroll
-    for (int i = 0; i < 32; i++) t[i] *= rm.invT;
-    correct_part<NOISE>(x, t, rm, chunk, v0, V, oa, ob);
+    correct_part<NOISE>(y, t, rm, chunk, v0, V, oa, ob);
   }
   if (h == 0) {
     L.red[ST][0][wave][m] = oa;
     L.red[ST][1][wave][m] = ob;
   }
+  rm = rn;
   fast_issue(p, s, ls, bias_list, req, min(u + 2, u1 - 1), nsb, Pcur);
-  if (u + 1 < u1) store_a(p, Pnext, L.sA[ST ^ 1]);
+  store_a(p, Pnext, L.sA[ST ^ 1]);   // past the last unit this stores a copy of it, never read
   __syncthreads();
 }
 
@@ -879,16 +930,17 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
   load_w(p, u0 / nsb, wf);   // first: waiting for unit u0's tiles then covers W as well
   fast_issue(p, s, ls, bias_list, req, u0, nsb, P0);
   fast_issue(p, s, ls, bias_list, req, min(u0 + 1, u1 - 1), nsb, P1);
+  RowMeta rm = row_meta(bias_list, req, s, (u0 % nsb) * SUB + (threadIdx.x & 31));
   store_a(p, P0, L.sA[0]);
   __syncthreads();
   int last = 0;
   for (int u = u0;; u += 2) {
-    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1);
+    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm);
     if (u + 1 >= u1) { last = 0; break; }
-    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0);
+    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0, rm);
     if (u + 2 >= u1) { last = 1; break; }
   }
-  fast_flush(p, bias_list, L.red[last], ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb);
+  fast_flush_finish(p, bias_list, fast_flush_read(L.red[last]), ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb, true);
 }
 
 // ------------------------------------------------------------------------------------------
