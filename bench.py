@@ -190,23 +190,34 @@ def main():
     value = sL / t_cycle
     kb_ms, kp_ms, km_ms = (float(x.sum(axis=1).mean()) for x in (kb, kp, km))
     n_active = int(L.max()) + 1
-    kernels = {
-        "k_bias": {"us_per_cycle": kb_ms * 1e3, "algorithmic_bytes": bias_bytes,
-                   "achieved_GBps": bias_bytes / (kb_ms * 1e-3) / 1e9},
-        "k_plain": {"us_per_cycle": kp_ms * 1e3, "algorithmic_bytes": plain_bytes,
-                    "achieved_GBps": plain_bytes / (kp_ms * 1e-3) / 1e9},
-        "k_merge": {"us_per_cycle": km_ms * 1e3},
-        "k_init": {"us_per_cycle": float(init.mean()) * 1e3},
-    }
-    dom = max(("k_bias", "k_plain"), key=lambda k: kernels[k]["us_per_cycle"])
+    if kp_ms < 2e-3:
+        # bf16 fast path: the plain rows run inside the sweep kernel (its plain slot is empty)
+        sweep_bytes = bias_bytes + plain_bytes
+        kernels = {
+            "k_sweep": {"us_per_cycle": kb_ms * 1e3, "algorithmic_bytes": sweep_bytes,
+                        "achieved_GBps": sweep_bytes / (kb_ms * 1e-3) / 1e9},
+            "k_merge": {"us_per_cycle": km_ms * 1e3},
+            "k_init": {"us_per_cycle": float(init.mean()) * 1e3},
+        }
+        dom = "k_sweep"
+    else:
+        kernels = {
+            "k_bias": {"us_per_cycle": kb_ms * 1e3, "algorithmic_bytes": bias_bytes,
+                       "achieved_GBps": bias_bytes / (kb_ms * 1e-3) / 1e9},
+            "k_plain": {"us_per_cycle": kp_ms * 1e3, "algorithmic_bytes": plain_bytes,
+                        "achieved_GBps": plain_bytes / (kp_ms * 1e-3) / 1e9},
+            "k_merge": {"us_per_cycle": km_ms * 1e3},
+            "k_init": {"us_per_cycle": float(init.mean()) * 1e3},
+        }
+        dom = max(("k_bias", "k_plain"), key=lambda k: kernels[k]["us_per_cycle"])
     achieved = kernels[dom]["achieved_GBps"] * 1e9
     print(f"[bench] sum L={sL} sum(a+1)={sa1} max L={int(L.max())} compulsory={cbytes / 1e6:.1f} MB",
           file=sys.stderr)
     print(f"[bench] wall {ms_per_step * 1e3:.1f} us/cycle ({ms_timed * 1e3:.1f} with events); event span "
           f"{span.mean() * 1e3:.1f} us; init "
-          f"{init.mean() * 1e3:.1f} us; bias {kb_ms * 1e3:.1f} us; plain {kp_ms * 1e3:.1f} us; merge {km_ms * 1e3:.1f} us",
+          f"{init.mean() * 1e3:.1f} us; sweep {kb_ms * 1e3:.1f} us; plain {kp_ms * 1e3:.1f} us; merge {km_ms * 1e3:.1f} us",
           file=sys.stderr)
-    for name, arr_ in (("bias", kb), ("plain", kp), ("merge", km)):
+    for name, arr_ in (("sweep", kb), ("plain", kp), ("merge", km)):
         print(f"[bench] per-step {name} us: " + " ".join(f"{x * 1e3:.1f}" for x in arr_.mean(axis=0)), file=sys.stderr)
 
     cpu = None

@@ -335,16 +335,29 @@ __device__ __forceinline__ float pair_lse(const float* x) {
 // the scale is folded into the exponent argument, max(invT y) = invT max(y); NaN-preserving
 template <int N>
 __device__ __forceinline__ float pair_lse_scaled(const float* y, float invT) {
-  float mx = -INFINITY;
+  // two max chains and four sum chains: independent partial results keep the pipeline busy
+  float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < N; i++) mx = fmaxf(mx, y[i]);
+  for (int i = 0; i < N; i += 2) {
+    m0 = fmaxf(m0, y[i]);
+    m1 = fmaxf(m1, y[i + 1]);
+  }
+  float mx = fmaxf(m0, m1);
   mx = fmaxf(mx, xor32f(mx));
-  float sum = 0.0f;
+  float sum;
   if (mx != -INFINITY) {
     const float c = invT * LOG2E, mo = mx * c;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < N; i++) sum += ex2(fmaf(y[i], c, -mo));
+    for (int i = 0; i < N; i += 4) {
+      s0 += ex2(fmaf(y[i], c, -mo));
+      s1 += ex2(fmaf(y[i + 1], c, -mo));
+      s2 += ex2(fmaf(y[i + 2], c, -mo));
+      s3 += ex2(fmaf(y[i + 3], c, -mo));
+    }
+    sum = (s0 + s1) + (s2 + s3);
   } else {
+    sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; i++) sum += y[i];   // every value -inf or NaN: keep a NaN visible
   }
@@ -796,11 +809,11 @@ template <int CTRL>
 __device__ __forceinline__ void argmax_round(float& sc, int& ix, float& aux) {
   const float s2 = dpp<CTRL>(sc), a2 = dpp<CTRL>(aux);
   const int i2 = __builtin_amdgcn_update_dpp(0, ix, CTRL, 0xF, 0xF, false);
-  if (i2 >= 0 && (ix < 0 || better(s2, i2, sc, ix))) {
-    sc = s2;
-    ix = i2;
-    aux = a2;
-  }
+  // the smaller index wins a tie; written without short-circuit so that it stays branch-free
+  const bool take = (i2 >= 0) & ((ix < 0) | (s2 > sc) | ((s2 == sc) & ((unsigned)i2 < (unsigned)ix)));
+  sc = take ? s2 : sc;
+  ix = take ? i2 : ix;
+  aux = take ? a2 : aux;
 }
 
 // Partials of one finished unit, by every wave: lane group g (4 lanes) of wave w takes row
@@ -812,12 +825,8 @@ __device__ __forceinline__ float4 fast_flush_read(const float4 (*red)[NT / 64][S
   return red[lane >= 32 ? 1 : 0][lane & 3][8 * wave + ((lane & 31) >> 2)];
 }
 
-__device__ __forceinline__ void fast_flush_finish(const Params& p, const uint16_t* bias_list, float4 h, int slot0,
-                                                  int range, bool valid) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = 8 * wave + ((lane & 31) >> 2);
-  const int cw = lane & 3;
-  const bool second = lane >= 32;
+// the merged record of the lane group (every lane of the group gets it)
+__device__ __forceinline__ float4 fast_flush_reduce(float4 h) {
   float mx = fmaxf(h.x, dpp<0xB1>(h.x));
   mx = fmaxf(mx, dpp<0x4E>(mx));
   float e = (mx == -INFINITY) ? h.x : ex2((h.x - mx) * LOG2E);   // all -inf / NaN: keep a NaN visible
@@ -828,14 +837,36 @@ __device__ __forceinline__ void fast_flush_finish(const Params& p, const uint16_
   int ix = __float_as_int(h.z);
   argmax_round<0xB1>(sc, ix, aux);
   argmax_round<0x4E>(sc, ix, aux);
-  if (valid && cw == 0) {
-    const int slot = slot0 + r;
-    const uint16_t e16 = bias_list[slot];
-    if (e16 != NO_ROW) {
-      const float4 part = make_float4(lse, sc, __int_as_float(ix), aux);
-      if (!second) p.part_bias[(size_t)slot * p.nrA + range] = part;
-      else if (e16 & 1) p.part_bias2[(size_t)slot * p.nrA + range] = part;
-    }
+  return make_float4(lse, sc, __int_as_float(ix), aux);
+}
+
+// bias-list entry of the lane group's row in the unit whose slots start at slot0
+__device__ __forceinline__ uint16_t fast_flush_entry(const uint16_t* bias_list, int slot0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return bias_list[slot0 + 8 * wave + ((lane & 31) >> 2)];
+}
+
+__device__ __forceinline__ void fast_flush_store(const Params& p, float4 part, uint16_t e16, int slot0, int range,
+                                                 bool valid) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = slot0 + 8 * wave + ((lane & 31) >> 2);
+  if (valid && (lane & 3) == 0 && e16 != NO_ROW) {
+    if (lane < 32) p.part_bias[(size_t)slot * p.nrA + range] = part;
+    else if (e16 & 1) p.part_bias2[(size_t)slot * p.nrA + range] = part;
+  }
+}
+
+// L2 prefetch of the W fragments of column range `range` (this wave's 64 columns): one dword per
+// 128-byte line, kept in pf until the range is loaded for real
+__device__ __forceinline__ void prefetch_w(const Params& p, int range, uint32_t (&pf)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vw = range * TILE_A + 64 * wave;
+  const size_t bytes = (size_t)min(64, p.V - vw) * p.R * 2;   // contiguous rows vw .. vw + 63
+  const char* base = (const char*)p.W + (size_t)vw * p.R * 2;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const size_t off = (size_t)(64 * i + lane) * 128;
+    pf[i] = *((off < bytes) ? (const uint32_t*)(base + off) : (const uint32_t*)p.konst);
   }
 }
 
@@ -849,12 +880,14 @@ __device__ __forceinline__ void fast_flush_finish(const Params& p, const uint16_
 template <int NOISE, int ST>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
                                           const ReqMeta* req, FastLds& L, int u, int u0, int u1, int nsb,
-                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext, RowMeta& rm) {
+                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext, RowMeta& rm,
+                                          uint32_t (&pf)[4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, h = lane >> 5;
   const int V = p.V;
   const int range = u / nsb, slot0 = (u % nsb) * SUB;
   if (u > u0 && range != (u - 1) / nsb) {
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));   // the prefetch has landed
     load_w(p, range, wf);
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -863,30 +896,35 @@ __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& l
 #pragma unroll
   for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)&L.sA[ST][m][kb + 8 * (t < T16 ? t : 0)];
   const float4 hrec = fast_flush_read(L.red[ST ^ 1]);
+  const int fslot0 = ((u - 1 + nsb) % nsb) * SUB, frange = (u - 1) / nsb;
+  const uint16_t fent = fast_flush_entry(bias_list, fslot0);
   const RowMeta rn = row_meta(bias_list, req, s, ((u + 1) % nsb) * SUB + m);
   __builtin_amdgcn_sched_barrier(0);   // keep all reads ahead of the MFMA chain
-  // y = base logits + Markov bias: the accumulators start from the unit's base-logit tile
+  // MFMA chain of unit u, with the previous unit's record merge and the base-logit unpack placed in
+  // its shadow (neither depends on the MFMA results)
   float y[32];
+  float4 fpart;
   {
-    float bx[32];
-    unpack32(Pcur.x, bx);
-    f32x16 acc0, acc1;
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      acc0[q] = bx[q];
-      acc1[q] = bx[16 + q];
-    }
+    f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    f32x16 acc1 = acc0;
 #pragma unroll
     for (int t = 0; t < 16; t++) {
       // for t >= R/16 both operands are zero (zero W fragments; sA zero past the rank)
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop[t], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop[t], acc1, 0, 0, 0);
     }
-    fast_flush_finish(p, bias_list, hrec, ((u - 1) % nsb) * SUB, (u - 1) / nsb, u > u0);
+    fpart = fast_flush_reduce(hrec);
+    float bx[32];
+    unpack32(Pcur.x, bx);
+#pragma unroll
+    for (int k = 0; k < 32; k++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);   // three vector ALU / transcendental
+    }
 #pragma unroll
     for (int q = 0; q < 16; q++) {
-      y[q] = acc0[q];
-      y[16 + q] = acc1[q];
+      y[q] = acc0[q] + bx[q];
+      y[16 + q] = acc1[q] + bx[16 + q];
     }
   }
   const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
@@ -906,6 +944,7 @@ __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& l
     L.red[ST][1][wave][m] = ob;
   }
   rm = rn;
+  fast_flush_store(p, fpart, fent, fslot0, frange, u > u0);
   fast_issue(p, s, ls, bias_list, req, min(u + 2, u1 - 1), nsb, Pcur);
   store_a(p, Pnext, L.sA[ST ^ 1]);   // past the last unit this stores a copy of it, never read
   __syncthreads();
@@ -931,16 +970,20 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
   fast_issue(p, s, ls, bias_list, req, u0, nsb, P0);
   fast_issue(p, s, ls, bias_list, req, min(u0 + 1, u1 - 1), nsb, P1);
   RowMeta rm = row_meta(bias_list, req, s, (u0 % nsb) * SUB + (threadIdx.x & 31));
+  uint32_t pf[4] = {0u, 0u, 0u, 0u};
+  if (u0 + 1 < u1 && (u0 + 1) / nsb != u0 / nsb) prefetch_w(p, (u0 + 1) / nsb, pf);
   store_a(p, P0, L.sA[0]);
   __syncthreads();
   int last = 0;
   for (int u = u0;; u += 2) {
-    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm);
+    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm, pf);
     if (u + 1 >= u1) { last = 0; break; }
-    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0, rm);
+    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0, rm, pf);
     if (u + 2 >= u1) { last = 1; break; }
   }
-  fast_flush_finish(p, bias_list, fast_flush_read(L.red[last]), ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb, true);
+  fast_flush_store(p, fast_flush_reduce(fast_flush_read(L.red[last])), fast_flush_entry(bias_list, ((u1 - 1) % nsb) * SUB),
+                   ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb, true);
+  asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1093,8 +1136,11 @@ __host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
 // dynamic LDS of the plain-row sweep: bias and plain lists
 __host__ __device__ constexpr size_t plain_dyn_bytes(int B) { return (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t); }
 
+// bf16 fast path: bias rows and plain rows of a step in one launch.  Every workgroup first sweeps
+// its share of the bias units, then its share of the plain items (one wave per item), so the plain
+// rows fill the time the bias rows leave and the step costs one dispatch less.
 template <int NOISE>
-__global__ __launch_bounds__(NT, 1) void k_bias_fast(Params p, int s) {
+__global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
   __shared__ uint64_t scan_tmp[NT / 64];
   __shared__ FastLds lds_f;
@@ -1103,8 +1149,13 @@ __global__ __launch_bounds__(NT, 1) void k_bias_fast(Params p, int s) {
   uint16_t* plain_list = bias_list + bias_slots_max(p.B);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
   const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, req, true);
-  if (ls.n_draft + ls.n_correct == 0) return;
-  bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, lds_f);
+  if (ls.n_draft + ls.n_correct > 0) bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, lds_f);
+  const long long n_items = (long long)ls.n_plain * p.nrB;
+  const int i0 = (int)(n_items * blockIdx.x / gridDim.x), i1 = (int)(n_items * (blockIdx.x + 1) / gridDim.x);
+  for (int it = i0 + (threadIdx.x >> 6); it < i1; it += NT / 64) {
+    const int pslot = it / p.nrB, range = it % p.nrB;
+    plain_item<SPEC_BF16, NOISE, true>(p, s, plain_list[pslot], pslot, range);
+  }
 }
 
 template <int DT, int NOISE, bool VEC>
@@ -1628,14 +1679,20 @@ template <int DT, int NOISE, bool VEC>
 static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const Timing& tm) {
   for (int s = 0; s <= p.K; s++) {
     const int k0 = 1 + 3 * s;
-    if (DT == SPEC_BF16 && VEC)
-      hipExtLaunchKernelGGL((k_bias_fast<NOISE>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st, tm.start(k0),
+    if (DT == SPEC_BF16 && VEC) {
+      hipExtLaunchKernelGGL((k_sweep_fast<NOISE>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st, tm.start(k0),
                             tm.stop(k0), 0, p, s);
-    else
+      // the plain rows ran inside the sweep: an empty interval keeps the timing slots in place
+      if (tm.start(k0 + 1)) {
+        hipEventRecord(tm.start(k0 + 1), st);
+        hipEventRecord(tm.stop(k0 + 1), st);
+      }
+    } else {
       hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st,
                             tm.start(k0), tm.stop(k0), 0, p, s);
-    hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 6)), dim3(NT), plain_dyn_bytes(p.B), st,
-                          tm.start(k0 + 1), tm.stop(k0 + 1), 0, p, s);
+      hipExtLaunchKernelGGL((k_plain<DT, NOISE, VEC>), dim3(grid_for(l.gridB, 6)), dim3(NT), plain_dyn_bytes(p.B), st,
+                            tm.start(k0 + 1), tm.stop(k0 + 1), 0, p, s);
+    }
     hipExtLaunchKernelGGL((k_merge<DT, NOISE>), dim3(p.B), dim3(NT), 0, st, tm.start(k0 + 2), tm.stop(k0 + 2), 0, p,
                           s);
   }
