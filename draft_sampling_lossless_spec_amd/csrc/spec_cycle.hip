@@ -7,17 +7,18 @@
 //
 // Device schedule.  The draft chain is sequential in the position (the bias of position s+1
 // needs x_s), and every position needs a full pass over the Markov factor W, so the cycle runs
-// as K+1 steps, two kernels each, all enqueued by one host call:
-//   k_sweep(s)  one pass over the rows active at step s.  "Bias rows" (DRAFT rows of position
-//               s and CORRECT rows of a position rejected at s-1) need A[prev] . W: a kind-A
-//               work item owns 256 vocabulary columns, keeps their W fragments in VGPRs and
-//               loops over up to 256 bias rows in sub-blocks of 32 (A rows staged in LDS),
-//               computing the bias with v_mfma_f32_32x32x16_bf16 directly in the layout the
-//               element-wise sweep consumes (bias never leaves registers).  "Plain rows"
-//               (LSEP: the target row of the position being verified; BONUS) are streamed by
-//               kind-B items of 16384 columns, 64 consecutive columns (one noise chunk) per
-//               thread.  Every item writes one 16-byte partial per row: the log-normaliser of
-//               its columns plus the best perturbed score and its index.
+// as k_init and then K+1 steps, all enqueued by one host call.  Per step:
+//   sweep       one pass over the rows active at step s.  "Bias rows" (DRAFT rows of position s
+//               and CORRECT rows of a position rejected at s-1) need A[prev] . W: a unit is one
+//               32-slot sub-block x one 256-column range; each of the 4 waves keeps the W
+//               fragments of its 64 columns in the accumulation registers and computes the bias
+//               with v_mfma_f32_32x32x16_bf16 directly in the layout the element-wise part
+//               consumes (the bias never leaves registers).  "Plain rows" (LSEP: the target row
+//               of the position being verified; BONUS) are streamed in 4096-column items, one
+//               wave each.  Every unit / item writes one 16-byte partial per row: the
+//               log-normaliser of its columns plus the best perturbed score and its index.
+//               bf16 rows with V % 8 == 0 run both parts in one kernel (k_sweep_fast); other
+//               inputs run k_bias and k_plain.
 //   k_merge(s)  one workgroup per request: reduces its rows' partials, finishes the sampler
 //               (CHUNKED: re-reads the winning 64-column chunk), takes the accept decision,
 //               finalises tokens, and writes the request's roles for step s+1.
@@ -1126,9 +1127,9 @@ __device__ void plain_item(const Params& p, int s, int b, int pslot, int range) 
 }
 
 // Row sweeps of one step.  Every workgroup rebuilds the step's row lists from the role bytes;
-// the bias-row sweep also stages each request's bias-row inputs.  k_bias runs one workgroup per
-// CU (its W fragments fill the register file); k_plain streams the target rows of LSEP / BONUS
-// roles, one wave per item, six workgroups per CU.
+// the bias-row sweep also stages each request's bias-row inputs.  The bias sweeps run one
+// workgroup per CU (the W fragments fill the register file); k_plain streams the target rows of
+// LSEP / BONUS roles, one wave per item, six workgroups per CU.
 // dynamic LDS of the bias-row sweeps: per-request table [B], then the bias and plain lists
 __host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
   return (size_t)B * sizeof(ReqMeta) + (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t);
