@@ -857,20 +857,6 @@ __device__ __forceinline__ void fast_flush_store(const Params& p, float4 part, u
   }
 }
 
-// L2 prefetch of the W fragments of column range `range` (this wave's 64 columns): one dword per
-// 128-byte line, kept in pf until the range is loaded for real
-__device__ __forceinline__ void prefetch_w(const Params& p, int range, uint32_t (&pf)[4]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int vw = range * TILE_A + 64 * wave;
-  const size_t bytes = (size_t)min(64, p.V - vw) * p.R * 2;   // contiguous rows vw .. vw + 63
-  const char* base = (const char*)p.W + (size_t)vw * p.R * 2;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const size_t off = (size_t)(64 * i + lane) * 128;
-    pf[i] = *((off < bytes) ? (const uint32_t*)(base + off) : (const uint32_t*)p.konst);
-  }
-}
-
 // One unit u from stage ST.  Pcur holds unit u's logit tiles (its A rows are already in stage ST),
 // Pnext unit u + 1's; rm holds the row meta of unit u and leaves with unit u + 1's.  Order: W
 // fragments if the column range changes (drained on the spot, so no later wait ever waits on them);
@@ -881,14 +867,12 @@ __device__ __forceinline__ void prefetch_w(const Params& p, int range, uint32_t 
 template <int NOISE, int ST>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
                                           const ReqMeta* req, FastLds& L, int u, int u0, int u1, int nsb,
-                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext, RowMeta& rm,
-                                          uint32_t (&pf)[4]) {
+                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext, RowMeta& rm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 31, h = lane >> 5;
   const int V = p.V;
   const int range = u / nsb, slot0 = (u % nsb) * SUB;
   if (u > u0 && range != (u - 1) / nsb) {
-    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));   // the prefetch has landed
     load_w(p, range, wf);
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -971,20 +955,20 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
   fast_issue(p, s, ls, bias_list, req, u0, nsb, P0);
   fast_issue(p, s, ls, bias_list, req, min(u0 + 1, u1 - 1), nsb, P1);
   RowMeta rm = row_meta(bias_list, req, s, (u0 % nsb) * SUB + (threadIdx.x & 31));
-  uint32_t pf[4] = {0u, 0u, 0u, 0u};
-  if (u0 + 1 < u1 && (u0 + 1) / nsb != u0 / nsb) prefetch_w(p, (u0 + 1) / nsb, pf);
   store_a(p, P0, L.sA[0]);
   __syncthreads();
-  int last = 0;
-  for (int u = u0;; u += 2) {
-    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm, pf);
-    if (u + 1 >= u1) { last = 0; break; }
-    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0, rm, pf);
-    if (u + 2 >= u1) { last = 1; break; }
+  int u = u0;
+  for (; u + 1 < u1; u += 2) {
+    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm);
+    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0, rm);
+  }
+  int last = 1;
+  if (u < u1) {
+    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm);
+    last = 0;
   }
   fast_flush_store(p, fast_flush_reduce(fast_flush_read(L.red[last])), fast_flush_entry(bias_list, ((u1 - 1) % nsb) * SUB),
                    ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb, true);
-  asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
 }
 
 // ------------------------------------------------------------------------------------------
