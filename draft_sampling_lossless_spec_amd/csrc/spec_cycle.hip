@@ -142,13 +142,21 @@ __global__ void k_init(Params p) {
   const float T = p.temp[b];
   const int x0 = p.x0 ? p.x0[b] : -1;
   const bool valid = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V;
-  // prefix cut: keep position j while the fp64 running product of confidences is >= threshold
+  // prefix cut: keep position j while the fp64 running product of confidences is >= threshold.
+  // The confidences are all loaded up front (in bounds whatever the cut), so the loop waits once.
+  float c[MAX_K];
+#pragma unroll
+  for (int j = 0; j < MAX_K; j++) c[j] = j < K ? p.conf[(size_t)b * K + j] : 0.0f;
   double P = 1.0;
   int L = 0;
-  for (int j = 0; j < K; j++) {
-    P *= (double)p.conf[(size_t)b * K + j];
-    if (!(P >= (double)p.threshold)) break;
-    L = j + 1;
+  bool go = true;
+#pragma unroll
+  for (int j = 0; j < MAX_K; j++) {
+    if (go && j < K) {
+      P *= (double)c[j];
+      go = P >= (double)p.threshold;   // NaN stops the cut
+      L = go ? j + 1 : L;
+    }
   }
   p.L[b] = L;
   p.kreq[b] = sm_first(sm_first(p.seed) ^ (uint64_t)(p.req_off + b));
