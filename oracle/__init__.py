@@ -82,6 +82,12 @@ def load(build_if_missing: bool = True) -> C.CDLL:
     lib.spec_cycle_ref_mc.restype = C.c_int
     lib.spec_cycle_ref_mc.argtypes = common + [C.c_int32, C.c_void_p, C.c_float, C.c_float, C.c_uint64,
                                                C.c_int64, C.c_int64, C.POINTER(Out), C.c_int]
+    lib.spec_accept_stats_ref.restype = C.c_int
+    lib.spec_accept_stats_ref.argtypes = common + [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                                   C.c_void_p, C.c_int]
+    lib.spec_calibration_error_ref.restype = C.c_double
+    lib.spec_calibration_error_ref.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                               C.POINTER(C.c_int64)]
     _lib = lib
     return lib
 
@@ -222,3 +228,43 @@ def table_index(prefix, V: int) -> int:
     for y in prefix:
         idx = idx * V + int(y)
     return off + idx
+
+
+# ----------------------------------------------------------------------------------------
+# acceptance statistics
+# ----------------------------------------------------------------------------------------
+def accept_stats_ref(base, target, A, W, x0, draft_tokens, temp, nthreads=0) -> dict:
+    """alpha [B,K] = sum_v min(p_j, q_j) = 1 - TV(p_j, q_j) at every drafted position (NaN
+    elsewhere), with the two log-normalisers lse_q and lse_p [B,K]; fp64."""
+    lib = load()
+    dt = _dtype_code(base)
+    B, K, V = base.shape
+    R = A.shape[1]
+    base, target, A, W = (np.ascontiguousarray(a) for a in (base, target, A, W))
+    draft = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, K)
+    temp = np.ascontiguousarray(temp, dtype=np.float32).reshape(B)
+    x0p = None
+    if x0 is not None:
+        x0 = np.ascontiguousarray(x0, dtype=np.int32).reshape(B)
+        x0p = x0.ctypes.data
+    out = {k: np.empty((B, K), dtype=np.float64) for k in ("alpha", "lse_q", "lse_p")}
+    d = Dims(B, K, V, R, dt, CHUNKED)
+    rc = lib.spec_accept_stats_ref(C.byref(d), base.ctypes.data, target.ctypes.data, A.ctypes.data, W.ctypes.data,
+                                   x0p, draft.ctypes.data, temp.ctypes.data, out["alpha"].ctypes.data,
+                                   out["lse_q"].ctypes.data, out["lse_p"].ctypes.data, nthreads)
+    if rc != 0:
+        raise ValueError(f"spec_accept_stats_ref rejected its arguments (code {rc})")
+    return out
+
+
+def calibration_error_ref(conf, verify_len, accepted_len, nbins=10):
+    """(ECE, number of pairs) of the confidences' prefix-survival product against realised
+    survival over every verified position of every valid request."""
+    lib = load()
+    conf = np.ascontiguousarray(conf, dtype=np.float32)
+    B, K = conf.shape
+    L = np.ascontiguousarray(verify_len, dtype=np.int32).reshape(B)
+    a = np.ascontiguousarray(accepted_len, dtype=np.int32).reshape(B)
+    n = C.c_int64(0)
+    e = lib.spec_calibration_error_ref(conf.ctypes.data, L.ctypes.data, a.ctypes.data, B, K, int(nbins), C.byref(n))
+    return float(e), int(n.value)

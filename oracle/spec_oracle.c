@@ -583,3 +583,124 @@ int oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Acceptance statistics.
+ *
+ * alpha_{b,j} = sum_v min(p_j(v), q_j(v)) = 1 - TV(p_j, q_j): the probability that a draft
+ * token drawn from q_j passes the accept test u < p/q, given that position j is reached.  The
+ * pages name this quantity twice: the drafter is trained on the total variation distance because
+ * it directly sets the acceptance rate, and the confidence head is supervised by this analytical
+ * per-step acceptance rate ("The Speed Claim Nobody's Really Questioning", sections "The
+ * Semi-Autoregressive Trick" and "The Real Innovation: Confidence-Scheduled Verification").
+ *
+ * Rows: every drafted position (draft_tokens[b][j] >= 0).  q_j = softmax((base row j + bias of
+ * prev) / T_b) with prev = x0[b] at j = 0 (none if x0 is NULL or -1), else draft_tokens[b][j-1];
+ * p_j = softmax(target row j / T_b).  Other positions, and every position of a request with a bad
+ * temperature or x0, get NaN.  lse_q / lse_p (may be NULL) receive the two log-normalisers.
+ * --------------------------------------------------------------------------------------- */
+static void stats_row(const oracle_dims* d, const void* base_logits, const void* target_logits,
+                      const void* A, const void* W, const int32_t* x0, const int32_t* draft_tokens,
+                      const float* temp, int64_t row, double* s, double* t, double* out3) {
+  const int32_t K = d->K, V = d->V, R = d->R;
+  const int32_t b = (int32_t)(row / K), j = (int32_t)(row % K);
+  out3[0] = out3[1] = out3[2] = NAN;
+  if (draft_tokens[row] < 0) return;
+  const double T = (double)temp[b];
+  const int32_t xb = x0 ? x0[b] : -1;
+  if (!(T > 0.0) || !isfinite(T) || xb < -1 || xb >= V) return;
+  const int32_t prev = (j == 0) ? xb : draft_tokens[row - 1];
+  if (j > 0 && prev < 0) return;
+  oracle_bias(A, W, d->dtype, V, R, prev, s);
+  for (int32_t v = 0; v < V; v++) {
+    s[v] = (load_elem(base_logits, d->dtype, ((size_t)b * K + j) * V + v) + s[v]) / T;
+    t[v] = load_elem(target_logits, d->dtype, ((size_t)b * (K + 1) + j) * V + v) / T;
+  }
+  const double lq = oracle_lse(s, V), lp = oracle_lse(t, V);
+  double a = 0.0;
+  for (int32_t v = 0; v < V; v++) {
+    const double q = exp(s[v] - lq), p = exp(t[v] - lp);
+    a += (p < q) ? p : q;
+  }
+  out3[0] = a;
+  out3[1] = lq;
+  out3[2] = lp;
+}
+
+int spec_accept_stats_ref(const oracle_dims* d, const void* base_logits, const void* target_logits,
+                          const void* A, const void* W, const int32_t* x0, const int32_t* draft_tokens,
+                          const float* temp, double* alpha, double* lse_q, double* lse_p, int nthreads) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!base_logits || !target_logits || !A || !W || !draft_tokens || !temp || !alpha) return -1;
+  const int64_t n = (int64_t)d->B * d->K;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)d->V);
+    double* t = (double*)malloc(sizeof(double) * (size_t)d->V);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int64_t row = 0; row < n; row++) {
+      double o[3];
+      stats_row(d, base_logits, target_logits, A, W, x0, draft_tokens, temp, row, s, t, o);
+      alpha[row] = o[0];
+      if (lse_q) lse_q[row] = o[1];
+      if (lse_p) lse_p[row] = o[2];
+    }
+    free(s);
+    free(t);
+  }
+  (void)nthreads;
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Expected calibration error of the confidences as prefix-survival estimates.
+ *
+ * The scheduler reads the running product of the per-position confidences as the probability
+ * that the draft prefix through position j survives verification, so it needs calibrated
+ * magnitudes, and the calibration error of that cumulative prefix probability is what sequential
+ * temperature scaling minimises ("DSpark turns speculation into a scheduler", section "Confidence
+ * is a serving primitive"; "The Speed Claim...", section "The Real Innovation": expected
+ * calibration error brought from 3-8 % down to about 1 %).
+ *
+ * Pairs: every verified position j < verify_len[b] of every valid request (accepted_len[b] >= 0).
+ * Prediction P_{b,j} = prod_{i<=j} conf[b][i] (fp64, left to right); outcome y_{b,j} = 1 when the
+ * prefix through j survived (j < accepted_len[b]), else 0.  nbins equal-width bins on [0, 1]:
+ * bin = floor(P * nbins) clamped to [0, nbins - 1].  ECE = sum over bins of
+ * (n_bin / N) * |mean P - mean y| over the bin's pairs; 0 when there is no pair.
+ * --------------------------------------------------------------------------------------- */
+double spec_calibration_error_ref(const float* conf, const int32_t* verify_len, const int32_t* accepted_len,
+                                  int32_t B, int32_t K, int32_t nbins, int64_t* n_pairs) {
+  if (nbins < 1) return NAN;
+  double* sp = (double*)calloc((size_t)nbins, sizeof(double));
+  double* sy = (double*)calloc((size_t)nbins, sizeof(double));
+  int64_t* cnt = (int64_t*)calloc((size_t)nbins, sizeof(int64_t));
+  int64_t N = 0;
+  for (int32_t b = 0; b < B; b++) {
+    if (accepted_len[b] < 0) continue;
+    double P = 1.0;
+    for (int32_t j = 0; j < verify_len[b] && j < K; j++) {
+      P *= (double)conf[(size_t)b * K + j];
+      int64_t m = (int64_t)floor(P * nbins);
+      if (m < 0) m = 0;
+      if (m > nbins - 1) m = nbins - 1;
+      sp[m] += P;
+      sy[m] += (j < accepted_len[b]) ? 1.0 : 0.0;
+      cnt[m] += 1;
+      N += 1;
+    }
+  }
+  double ece = 0.0;
+  for (int32_t m = 0; m < nbins; m++)
+    if (cnt[m] > 0) ece += ((double)cnt[m] / (double)N) * fabs(sp[m] / cnt[m] - sy[m] / cnt[m]);
+  if (n_pairs) *n_pairs = N;
+  free(sp);
+  free(sy);
+  free(cnt);
+  return N > 0 ? ece : 0.0;
+}
