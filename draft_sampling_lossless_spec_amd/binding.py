@@ -56,6 +56,13 @@ def _load():
     lib.spec_cycle_timed.argtypes = cycle_args + [C.c_void_p, C.c_int]
     lib.spec_cycle_kernel_count.restype = C.c_int
     lib.spec_cycle_kernel_count.argtypes = [C.POINTER(_Dims)]
+    lib.spec_stats_workspace_bytes.restype = C.c_size_t
+    lib.spec_stats_workspace_bytes.argtypes = [C.POINTER(_Dims)]
+    lib.spec_accept_stats.restype = C.c_int
+    lib.spec_accept_stats.argtypes = [C.POINTER(_Dims)] + [C.c_void_p] * 10 + [C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.spec_calibration_error.restype = C.c_int
+    lib.spec_calibration_error.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
+                                           C.c_void_p, C.c_void_p, C.c_void_p]
     _lib = lib
     return lib
 
@@ -156,3 +163,68 @@ def spec_cycle(base_logits, target_logits, A, W, conf, temp, threshold: float, s
     if rc != 0:
         raise SpecError(f"spec_cycle failed: {spec_error_string(rc)} (code {rc})")
     return out
+
+
+def spec_stats_workspace_bytes(B: int, K: int, V: int, R: int, dtype: int = BF16) -> int:
+    return int(_load().spec_stats_workspace_bytes(C.byref(_Dims(B, K, V, R, dtype, CHUNKED))))
+
+
+def spec_accept_stats(base_logits, target_logits, A, W, draft_tokens, temp, x0=None, workspace=None,
+                      out=None, stream=None) -> dict:
+    """Analytical acceptance rate alpha = sum_v min(p_j, q_j) = 1 - TV(p_j, q_j) of every drafted
+    position (draft_tokens [B, K] int32, -1 past the drafted prefix, as the cycle's diagnostics
+    give it), with the log-normalisers 'lse_q' and 'lse_p'; NaN elsewhere.  Asynchronous."""
+    import torch
+    B, K, V = base_logits.shape
+    R = A.shape[1]
+    dt = _dtype_code(base_logits)
+    _check(base_logits, "base_logits", (B, K, V))
+    _check(target_logits, "target_logits", (B, K + 1, V), base_logits.dtype)
+    _check(A, "A", (V, R), base_logits.dtype)
+    _check(W, "W", (V, R), base_logits.dtype)
+    _check(draft_tokens, "draft_tokens", (B, K), torch.int32)
+    _check(temp, "temp", (B,), torch.float32)
+    if x0 is not None:
+        _check(x0, "x0", (B,), torch.int32)
+    dev = base_logits.device
+    lib = _load()
+    d = _Dims(B, K, V, R, dt, CHUNKED)
+    need = int(lib.spec_stats_workspace_bytes(C.byref(d)))
+    if need == 0:
+        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {k: torch.empty((B, K), dtype=torch.float32, device=dev) for k in ("alpha", "lse_q", "lse_p")}
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib.spec_accept_stats(C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(),
+                               W.data_ptr(), x0.data_ptr() if x0 is not None else None, draft_tokens.data_ptr(),
+                               temp.data_ptr(), out["alpha"].data_ptr(),
+                               out["lse_q"].data_ptr() if "lse_q" in out else None,
+                               out["lse_p"].data_ptr() if "lse_p" in out else None,
+                               workspace.data_ptr(), workspace.numel(), C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_accept_stats failed: {spec_error_string(rc)} (code {rc})")
+    return out
+
+
+def spec_calibration_error(conf, verify_len, accepted_len, nbins: int = 10, stream=None):
+    """Expected calibration error of the confidences' prefix-survival product against realised
+    survival, and the number of (request, position) pairs; returns two device tensors (fp64 [1],
+    int64 [1]).  Asynchronous."""
+    import torch
+    B, K = conf.shape
+    _check(conf, "conf", (B, K), torch.float32)
+    _check(verify_len, "verify_len", (B,), torch.int32)
+    _check(accepted_len, "accepted_len", (B,), torch.int32)
+    dev = conf.device
+    ece = torch.empty(1, dtype=torch.float64, device=dev)
+    n = torch.empty(1, dtype=torch.int64, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = _load().spec_calibration_error(conf.data_ptr(), verify_len.data_ptr(), accepted_len.data_ptr(), B, K,
+                                        int(nbins), ece.data_ptr(), n.data_ptr(), C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_calibration_error failed: {spec_error_string(rc)} (code {rc})")
+    return ece, n

@@ -46,6 +46,7 @@ constexpr int TILE_B = KB_LOADS * 64 * 8;   // vocabulary columns per plain-row 
 constexpr int MAX_B = 1024;
 constexpr int MAX_K = 32;
 constexpr int MAX_R = 256;
+constexpr int MAX_BINS = 1024;      // calibration-error bins
 constexpr int A_PAD = 8;            // bf16 elements of LDS row padding (kills bank conflicts)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1581,6 +1582,291 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
 // ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
+// ==========================================================================================
+// Acceptance statistics: alpha_{b,j} = sum_v min(p_j(v), q_j(v)) = 1 - TV(p_j, q_j), the
+// analytical acceptance rate of every drafted position ("The Speed Claim Nobody's Really
+// Questioning", sections "The Semi-Autoregressive Trick" and "The Real Innovation:
+// Confidence-Scheduled Verification"), and the calibration error of the confidences' prefix
+// product ("DSpark turns speculation into a scheduler", section "Confidence is a serving
+// primitive").
+//   k_stats_prep       one workgroup: compact list of the drafted positions, their previous
+//                      token, NaN-filled outputs
+//   k_stats_sweep<1>   the (draft, target) row pairs in units of 32 rows x 256 columns with the
+//                      Markov bias on MFMA (bf16) or VALU dot products (fp32): per-range
+//                      log-normalisers of q and p
+//   k_stats_merge<1>   one wave per row: LSE_q, LSE_p
+//   k_stats_sweep<2>   same sweep: per-range sum of min(p, q) = exp2 of the smaller log2-probability
+//   k_stats_merge<2>   one wave per row: alpha
+// ==========================================================================================
+struct StatsParams {
+  Params c;                // dims, logits, factors, konst: what the shared sweep helpers read
+  const int32_t* draft;    // [B, K] drafted tokens, -1 past the drafted prefix
+  float* alpha;            // [B, K] out
+  float* o_lse_q;          // [B, K] out, may be null
+  float* o_lse_p;          // [B, K] out, may be null
+  int32_t* n_rows;         // [1] number of listed rows
+  int32_t* rows;           // [B K] listed row ids b K + j
+  int32_t* prev;           // [B K] previous token of each listed row (-1: none)
+  float* lse_q;            // [B K] per listed row
+  float* lse_p;            // [B K]
+  float2* part;            // [slots][nrA] per-range partials
+};
+
+// drafted position j of request b needs a valid temperature and x0, and a drafted token at j - 1
+__global__ __launch_bounds__(NT) void k_stats_prep(StatsParams sp) {
+  const Params& p = sp.c;
+  if (threadIdx.x < 2) {
+    const uint32_t w = threadIdx.x ? 0xFF80FF80u : 0u;
+    ((u32x4*)p.konst)[threadIdx.x] = (u32x4){w, w, w, w};
+  }
+  const int n = p.B * p.K, per = (n + NT - 1) / NT, i0 = threadIdx.x * per;
+  int cnt = 0;
+  for (int i = i0; i < min(i0 + per, n); i++) {
+    const int b = i / p.K, j = i - b * p.K;
+    const float T = p.temp[b];
+    const int x0 = p.x0 ? p.x0[b] : -1;
+    const bool ok = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V && sp.draft[i] >= 0 &&
+                    (j == 0 || (sp.draft[i - 1] >= 0 && sp.draft[i - 1] < p.V));
+    cnt += ok ? 1 : 0;
+    sp.alpha[i] = NAN;
+    if (sp.o_lse_q) sp.o_lse_q[i] = NAN;
+    if (sp.o_lse_p) sp.o_lse_p[i] = NAN;
+  }
+  // exclusive scan of the per-thread counts (one thread: NT entries)
+  __shared__ int cnts[NT];
+  cnts[threadIdx.x] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int t = 0; t < NT; t++) {
+      const int c = cnts[t];
+      cnts[t] = run;
+      run += c;
+    }
+    sp.n_rows[0] = run;
+  }
+  __syncthreads();
+  int k = cnts[threadIdx.x];
+  for (int i = i0; i < min(i0 + per, n); i++) {
+    const int b = i / p.K, j = i - b * p.K;
+    const float T = p.temp[b];
+    const int x0 = p.x0 ? p.x0[b] : -1;
+    const bool ok = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V && sp.draft[i] >= 0 &&
+                    (j == 0 || (sp.draft[i - 1] >= 0 && sp.draft[i - 1] < p.V));
+    if (ok) {
+      sp.rows[k] = i;
+      sp.prev[k] = j == 0 ? x0 : sp.draft[i - 1];
+      k++;
+    }
+  }
+}
+
+struct StatsLds {
+  uint16_t sA[SUB][MAX_R + A_PAD];   // A rows of the current unit (bf16)
+  float2 red[NT / 64][SUB];          // per-wave chunk results of the current unit
+};
+
+// per-range partials of one finished unit (threads 0..31): merge the four waves' chunk results
+template <int PASS>
+__device__ __forceinline__ void stats_flush(const StatsParams& sp, const float2 (*red)[SUB], int slot0, int range,
+                                            int n_rows) {
+  if (threadIdx.x < SUB && slot0 + (int)threadIdx.x < n_rows) {
+    const int r = threadIdx.x;
+    float2 a = red[0][r];
+#pragma unroll
+    for (int w = 1; w < NT / 64; w++) {
+      const float2 o = red[w][r];
+      if (PASS == 1) {
+        a.x = lse2(a.x, o.x);
+        a.y = lse2(a.y, o.y);
+      } else {
+        a.x += o.x;
+      }
+    }
+    sp.part[(size_t)(slot0 + r) * sp.c.nrA + range] = a;
+  }
+}
+
+template <int DT, int PASS, bool VEC>
+__global__ __launch_bounds__(NT, 1) void k_stats_sweep(StatsParams sp) {
+  __shared__ StatsLds L;
+  const Params& p = sp.c;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, h = lane >> 5;
+  const int V = p.V, R = p.R, K = p.K;
+  const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
+  const int n_rows = sp.n_rows[0];
+  const int nsb = (n_rows + SUB - 1) / SUB;
+  const long long units = (long long)p.nrA * nsb;
+  const int u0 = (int)(units * blockIdx.x / gridDim.x);
+  const int u1 = (int)(units * (blockIdx.x + 1) / gridDim.x);
+  if (u0 >= u1) return;
+  if (DT == SPEC_BF16 && R < MAX_R) {
+    // the MFMA loop runs over the full rank: A columns past R read as zero
+    uint32_t* z = (uint32_t*)&L.sA[0][0];
+    for (int i = threadIdx.x; i < (int)(sizeof(L.sA) / 4); i += NT) z[i] = 0u;
+  }
+  bf16x8 wf[2][16];
+  int w_range = -1;
+  for (int u = u0; u < u1; u++) {
+    const int range = u / nsb, slot0 = (u % nsb) * SUB;
+    __syncthreads();   // the previous unit is done with sA and red
+    if (u > u0) stats_flush<PASS>(sp, L.red, ((u - 1) % nsb) * SUB, (u - 1) / nsb, n_rows);
+    if (DT == SPEC_BF16) {
+      const int segs = R >> 3;
+      for (int e = threadIdx.x; e < SUB * segs; e += NT) {
+        const int row = e / segs, sg = e - row * segs;
+        const int slot = slot0 + row;
+        const int pv = slot < n_rows ? sp.prev[slot] : -1;
+        u32x4 val = {0, 0, 0, 0};
+        if (pv >= 0) val = *(const u32x4*)((const uint16_t*)p.A + (size_t)pv * R + 8 * sg);
+        *(u32x4*)&L.sA[row][8 * sg] = val;
+      }
+    }
+    __syncthreads();   // sA holds this unit's A rows; red is free
+    if (DT == SPEC_BF16 && range != w_range) load_w(p, range, wf);
+    w_range = range;
+
+    const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns
+    const int v0 = vw + 16 * h;
+    const int slot = slot0 + m;
+    const bool active = slot < n_rows;
+    const int rid = active ? sp.rows[slot] : 0;
+    const int b = rid / K, j = rid - b * K;
+    const int pv = active ? sp.prev[slot] : -1;
+    const float invT = active ? 1.0f / p.temp[b] : 1.0f;
+    float y[32], t[32];
+    if (DT == SPEC_BF16) {
+      mfma_bias(wf, L.sA, R, y);
+    } else {
+      fp32_bias16(p, pv, v0, y);
+      fp32_bias16(p, pv, v0 + 32, y + 16);
+    }
+    {
+      float bx[32];
+#pragma unroll
+      for (int i = 0; i < 32; i++) bx[i] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 32; i++) t[i] = -INFINITY;
+      const void* base_row = (const char*)p.base + ((size_t)b * K + j) * (size_t)V * esz;
+      const void* targ_row = (const char*)p.target + ((size_t)b * (K + 1) + j) * (size_t)V * esz;
+      if (active) {
+        load16<DT, VEC>(base_row, v0, V, *(float(*)[16])bx);
+        load16<DT, VEC>(base_row, v0 + 32, V, *(float(*)[16])(bx + 16));
+        load16<DT, VEC>(targ_row, v0, V, *(float(*)[16])t);
+        load16<DT, VEC>(targ_row, v0 + 32, V, *(float(*)[16])(t + 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 32; i++) y[i] = active ? bx[i] + y[i] : -INFINITY;
+    }
+    float2 o;
+    if (PASS == 1) {
+      o.x = pair_lse_scaled<32>(y, invT);
+      o.y = pair_lse_scaled<32>(t, invT);
+    } else {
+      // sum of min(p, q) over the lane pair's 64 columns: exp2 of the smaller base-2 log-probability
+      const float c = invT * LOG2E;
+      const float oq = active ? -sp.lse_q[slot] * LOG2E : 0.0f, op = active ? -sp.lse_p[slot] * LOG2E : 0.0f;
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; i += 2) {
+        a0 += ex2(fminf(fmaf(t[i], c, op), fmaf(y[i], c, oq)));
+        a1 += ex2(fminf(fmaf(t[i + 1], c, op), fmaf(y[i + 1], c, oq)));
+      }
+      o.x = a0 + a1;
+      o.x += xor32f(o.x);
+      o.y = 0.0f;
+    }
+    if (h == 0) L.red[wave][m] = o;
+  }
+  __syncthreads();
+  stats_flush<PASS>(sp, L.red, ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb, n_rows);
+}
+
+// one wave per listed row: reduce the row's per-range partials
+template <int PASS>
+__global__ __launch_bounds__(NT) void k_stats_merge(StatsParams sp) {
+  const int n_rows = sp.n_rows[0];
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * (NT / 64);
+  const int nrA = sp.c.nrA;
+  for (int slot = blockIdx.x * (NT / 64) + (threadIdx.x >> 6); slot < n_rows; slot += nw) {
+    const float2* pr = sp.part + (size_t)slot * nrA;
+    if (PASS == 1) {
+      // running {max, scaled sum} of both log-normalisers; a NaN anywhere stays visible
+      float mq = -INFINITY, sq = 0.0f, mp = -INFINITY, s_p = 0.0f;
+      for (int r = lane; r < nrA; r += 64) {
+        const float2 v = pr[r];
+        if (v.x > mq) { sq = sq * ex2((mq - v.x) * LOG2E) + 1.0f; mq = v.x; }
+        else if (v.x > -INFINITY) sq += ex2((v.x - mq) * LOG2E);
+        else if (isnan(v.x)) sq = NAN;
+        if (v.y > mp) { s_p = s_p * ex2((mp - v.y) * LOG2E) + 1.0f; mp = v.y; }
+        else if (v.y > -INFINITY) s_p += ex2((v.y - mp) * LOG2E);
+        else if (isnan(v.y)) s_p = NAN;
+      }
+      float lq = mq > -INFINITY ? mq + lg2(sq) * LN2 : (isnan(sq) ? NAN : -INFINITY);
+      float lp = mp > -INFINITY ? mp + lg2(s_p) * LN2 : (isnan(s_p) ? NAN : -INFINITY);
+      for (int o = 32; o > 0; o >>= 1) {
+        lq = lse2(lq, __shfl_xor(lq, o, 64));
+        lp = lse2(lp, __shfl_xor(lp, o, 64));
+      }
+      if (lane == 0) {
+        sp.lse_q[slot] = lq;
+        sp.lse_p[slot] = lp;
+        const int rid = sp.rows[slot];
+        if (sp.o_lse_q) sp.o_lse_q[rid] = lq;
+        if (sp.o_lse_p) sp.o_lse_p[rid] = lp;
+      }
+    } else {
+      float a = 0.0f;
+      for (int r = lane; r < nrA; r += 64) a += pr[r].x;
+      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+      if (lane == 0) sp.alpha[sp.rows[slot]] = a;
+    }
+  }
+}
+
+// Expected calibration error of the prefix product of the confidences against realised
+// survival: one workgroup; every verified position j < L_b of a valid request is one pair
+// (prediction: fp64 running product through j; outcome: j < a_b); nbins equal-width bins.
+__global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int32_t* verify_len,
+                                                   const int32_t* accepted_len, int B, int K, int nbins,
+                                                   double* ece, int64_t* n_pairs) {
+  __shared__ double sp_[MAX_BINS];
+  __shared__ double sy_[MAX_BINS];
+  __shared__ int cnt_[MAX_BINS];
+  for (int m = threadIdx.x; m < nbins; m += NT) {
+    sp_[m] = 0.0;
+    sy_[m] = 0.0;
+    cnt_[m] = 0;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += NT) {
+    const int a = accepted_len[b];
+    if (a < 0) continue;
+    const int L = min(verify_len[b], K);
+    double P = 1.0;
+    for (int j = 0; j < L; j++) {
+      P *= (double)conf[(size_t)b * K + j];
+      int m = (int)floor(P * nbins);
+      m = m < 0 ? 0 : (m > nbins - 1 ? nbins - 1 : m);
+      atomicAdd(&sp_[m], P);
+      atomicAdd(&sy_[m], j < a ? 1.0 : 0.0);
+      atomicAdd(&cnt_[m], 1);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long N = 0;
+    for (int m = 0; m < nbins; m++) N += cnt_[m];
+    double e = 0.0;
+    for (int m = 0; m < nbins; m++)
+      if (cnt_[m] > 0) e += ((double)cnt_[m] / (double)N) * fabs(sp_[m] / cnt_[m] - sy_[m] / cnt_[m]);
+    ece[0] = N > 0 ? e : 0.0;
+    n_pairs[0] = N;
+  }
+}
+
 struct Layout {
   size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
       off_pbias, off_pbias2, off_pplain, off_konst, total;
@@ -1818,4 +2104,114 @@ extern "C" int spec_cycle_timed(const spec_dims* d, const void* base_logits, con
   const Timing tm = {(hipEvent_t*)events, n_events};
   return cycle_impl(d, base_logits, target_logits, A, W, x0, conf, temp, threshold, seed, request_offset,
                     accepted_len, tokens, diag, workspace, workspace_bytes, stream, tm);
+}
+
+// ------------------------------------------------------------------------------------------
+// acceptance statistics: host side
+// ------------------------------------------------------------------------------------------
+struct StatsLayout {
+  size_t off_konst, off_n, off_rows, off_prev, off_lq, off_lp, off_part, total;
+  int nrA;
+};
+
+static StatsLayout stats_layout(const spec_dims* d) {
+  StatsLayout l;
+  const size_t n = (size_t)d->B * d->K;
+  const size_t slots = (n + SUB - 1) / SUB * SUB;
+  l.nrA = (d->V + TILE_A - 1) / TILE_A;
+  size_t o = 0;
+  l.off_konst = o; o = align256(o + 32);
+  l.off_n = o; o = align256(o + 4);
+  l.off_rows = o; o = align256(o + 4 * n);
+  l.off_prev = o; o = align256(o + 4 * n);
+  l.off_lq = o; o = align256(o + 4 * n);
+  l.off_lp = o; o = align256(o + 4 * n);
+  l.off_part = o; o = align256(o + 8 * slots * (size_t)l.nrA);
+  l.total = o;
+  return l;
+}
+
+extern "C" size_t spec_stats_workspace_bytes(const spec_dims* d) {
+  if (!dims_ok(d) || !dtype_ok(d)) return 0;
+  return stats_layout(d).total;
+}
+
+template <int DT, bool VEC>
+static void launch_stats(const StatsParams& sp, hipStream_t st) {
+  const int cu = cu_count();
+  const int n = sp.c.B * sp.c.K;
+  const int merge_grid = (n + NT / 64 - 1) / (NT / 64);
+  hipLaunchKernelGGL(k_stats_prep, dim3(1), dim3(NT), 0, st, sp);
+  hipLaunchKernelGGL((k_stats_sweep<DT, 1, VEC>), dim3(cu), dim3(NT), 0, st, sp);
+  hipLaunchKernelGGL((k_stats_merge<1>), dim3(merge_grid), dim3(NT), 0, st, sp);
+  hipLaunchKernelGGL((k_stats_sweep<DT, 2, VEC>), dim3(cu), dim3(NT), 0, st, sp);
+  hipLaunchKernelGGL((k_stats_merge<2>), dim3(merge_grid), dim3(NT), 0, st, sp);
+}
+
+extern "C" int spec_accept_stats(const spec_dims* d, const void* base_logits, const void* target_logits,
+                                 const void* A, const void* W, const int32_t* x0, const int32_t* draft_tokens,
+                                 const float* temp, float* alpha, float* lse_q, float* lse_p, void* workspace,
+                                 size_t workspace_bytes, spec_stream_t stream) {
+  if (!dims_ok(d)) return SPEC_E_INVAL;
+  if (!dtype_ok(d)) return SPEC_E_DTYPE;
+  if (!base_logits || !target_logits || !A || !W || !draft_tokens || !temp || !alpha) return SPEC_E_INVAL;
+  if ((((uintptr_t)A) | ((uintptr_t)W)) & 15) return SPEC_E_INVAL;
+  const StatsLayout l = stats_layout(d);
+  if (!workspace || workspace_bytes < l.total || (((uintptr_t)workspace) & 255)) return SPEC_E_WORKSPACE;
+  const int ac = arch_ok();
+  if (ac != SPEC_OK) return ac;
+  char* ws = (char*)workspace;
+  StatsParams sp;
+  memset(&sp.c, 0, sizeof(sp.c));
+  sp.c.B = d->B;
+  sp.c.K = d->K;
+  sp.c.V = d->V;
+  sp.c.R = d->R;
+  sp.c.dtype = d->dtype;
+  sp.c.noise = d->noise;
+  sp.c.base = base_logits;
+  sp.c.target = target_logits;
+  sp.c.A = A;
+  sp.c.W = W;
+  sp.c.x0 = x0;
+  sp.c.temp = temp;
+  sp.c.konst = (const u32x4*)(ws + l.off_konst);
+  sp.c.nrA = l.nrA;
+  sp.draft = draft_tokens;
+  sp.alpha = alpha;
+  sp.o_lse_q = lse_q;
+  sp.o_lse_p = lse_p;
+  sp.n_rows = (int32_t*)(ws + l.off_n);
+  sp.rows = (int32_t*)(ws + l.off_rows);
+  sp.prev = (int32_t*)(ws + l.off_prev);
+  sp.lse_q = (float*)(ws + l.off_lq);
+  sp.lse_p = (float*)(ws + l.off_lp);
+  sp.part = (float2*)(ws + l.off_part);
+  const size_t esz = d->dtype == SPEC_FP32 ? 4 : 2;
+  const bool vec = ((d->V * esz) % 16 == 0) && ((((uintptr_t)base_logits) | ((uintptr_t)target_logits)) & 15) == 0;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (d->dtype == SPEC_BF16) {
+    if (vec) launch_stats<SPEC_BF16, true>(sp, st);
+    else launch_stats<SPEC_BF16, false>(sp, st);
+  } else {
+    if (vec) launch_stats<SPEC_FP32, true>(sp, st);
+    else launch_stats<SPEC_FP32, false>(sp, st);
+  }
+  if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
+}
+
+extern "C" int spec_calibration_error(const float* conf, const int32_t* verify_len, const int32_t* accepted_len,
+                                      int32_t B, int32_t K, int32_t nbins, double* ece, int64_t* n_pairs,
+                                      spec_stream_t stream) {
+  if (!conf || !verify_len || !accepted_len || !ece || !n_pairs) return SPEC_E_INVAL;
+  if (B < 1 || B > MAX_B || K < 1 || K > MAX_K || nbins < 1 || nbins > MAX_BINS) return SPEC_E_INVAL;
+  const int ac = arch_ok();
+  if (ac != SPEC_OK) return ac;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_calibration, dim3(1), dim3(NT), 0, (hipStream_t)stream, conf, verify_len, accepted_len, B, K,
+                     nbins, ece, n_pairs);
+  if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
 }

@@ -112,7 +112,8 @@ int spec_cycle(const spec_dims* d, const void* base_logits, const void* target_l
  * of the cycle is launched with a start/stop hipEvent_t pair attached to its own dispatch (no
  * extra queue packets).  Kernel i is: 0 = set-up and prefix cut; 1 + 3s = sweep of the Markov-biased
  * rows of step s, 2 + 3s = sweep of the plain target rows of step s, 3 + 3s = per-request merge of
- * step s, for s = 0..K.  `events` is a host array of
+ * step s, for s = 0..K.  With bf16 rows and V % 8 == 0 the plain rows of step s run inside kernel
+ * 1 + 3s, and the event pair of slot 2 + 3s is recorded back to back (an empty interval).  `events` is a host array of
  * n_events >= 2 * spec_cycle_kernel_count(d) events created by the caller (hipEventCreate);
  * events[2i] / events[2i+1] bracket kernel i.  The caller reads hipEventElapsedTime after the
  * stream is synchronised.  Returns SPEC_E_INVAL when the array is missing or too short.
@@ -123,8 +124,55 @@ int spec_cycle_timed(const spec_dims* d, const void* base_logits, const void* ta
                      int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, void* workspace,
                      size_t workspace_bytes, spec_stream_t stream, void* const* events, int n_events);
 
-/* Number of kernels one spec_cycle call launches: 1 + 3 (K + 1); 0 for invalid dims. */
+/* Number of kernel slots of one spec_cycle call: 1 + 3 (K + 1); 0 for invalid dims. */
 int spec_cycle_kernel_count(const spec_dims* d);
+
+/* Bytes of device workspace spec_accept_stats needs (0 if dims are invalid; dims.noise unused). */
+size_t spec_stats_workspace_bytes(const spec_dims* d);
+
+/*
+ * Acceptance statistics of drafted positions: the analytical acceptance rate
+ *   alpha_{b,j} = sum_v min(p_j(v), q_j(v)) = 1 - TV(p_j, q_j),
+ * the probability that a draft token drawn from q_j passes the accept test given that position j
+ * is reached.  The drafter is trained on this total variation distance and the confidence head is
+ * supervised by this per-step rate ("The Speed Claim Nobody's Really Questioning", sections "The
+ * Semi-Autoregressive Trick" and "The Real Innovation: Confidence-Scheduled Verification").
+ *   q_j = softmax((base row j + A[prev] . W) / T_b), prev = x0[b] at j = 0 (none if x0 is NULL or
+ *         -1), else draft_tokens[b, j-1];   p_j = softmax(target row j / T_b).
+ *   base_logits, target_logits, A, W, x0, temp: as for spec_cycle (same dims, same layouts)
+ *   draft_tokens [B, K] int32  the drafted tokens (-1 past the drafted prefix), e.g. the
+ *                              draft_tokens diagnostic of a spec_cycle call
+ *   alpha        [B, K] fp32   out: alpha at every drafted position j (draft_tokens[b, j] >= 0,
+ *                              j = 0 or draft_tokens[b, j-1] in [0, V)), NaN elsewhere and at every
+ *                              position of a request whose temperature or x0 is invalid
+ *   lse_q, lse_p [B, K] fp32   out, may be NULL: log-normalisers of q_j and p_j (NaN where alpha is)
+ *   workspace                  device scratch of spec_stats_workspace_bytes(d) bytes, 256-byte
+ *                              aligned, no initialisation needed
+ * Asynchronous on `stream`, allocates nothing.  Returns SPEC_OK or a negative SPEC_E_* code
+ * (NULL required pointer, bad dims or misaligned A / W: SPEC_E_INVAL; workspace: SPEC_E_WORKSPACE).
+ */
+int spec_accept_stats(const spec_dims* d, const void* base_logits, const void* target_logits,
+                      const void* A, const void* W, const int32_t* x0, const int32_t* draft_tokens,
+                      const float* temp, float* alpha, float* lse_q, float* lse_p, void* workspace,
+                      size_t workspace_bytes, spec_stream_t stream);
+
+/*
+ * Expected calibration error of the confidences read as prefix-survival probabilities, the
+ * quantity sequential temperature scaling minimises ("DSpark turns speculation into a scheduler",
+ * section "Confidence is a serving primitive"; "The Speed Claim...", section "The Real Innovation":
+ * expected calibration error from 3-8 % down to about 1 %).  One pair per verified position
+ * j < verify_len[b] of every request with accepted_len[b] >= 0: prediction = fp64 running product
+ * of conf[b, 0..j]; outcome = 1 if j < accepted_len[b] (the prefix through j survived).  nbins
+ * equal-width bins on [0, 1] (1..1024); ECE = sum over bins of (pairs in bin / all pairs) *
+ * |mean prediction - mean outcome|, 0 when there is no pair.
+ *   conf [B, K] fp32, verify_len [B] int32, accepted_len [B] int32: device inputs (the cycle's
+ *   diagnostics and outputs);  ece [1] fp64 and n_pairs [1] int64: device outputs.
+ * Asynchronous on `stream`.  Returns SPEC_OK or SPEC_E_INVAL (NULL pointer, B outside 1..1024,
+ * K outside 1..32, nbins outside 1..1024).
+ */
+int spec_calibration_error(const float* conf, const int32_t* verify_len, const int32_t* accepted_len,
+                           int32_t B, int32_t K, int32_t nbins, double* ece, int64_t* n_pairs,
+                           spec_stream_t stream);
 
 /* Static description of an error code (never NULL). */
 const char* spec_error_string(int code);

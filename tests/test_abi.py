@@ -68,3 +68,28 @@ def test_error_strings(lib):
     for code in (0, -1, -2, -3, -4, -5, 42):
         assert isinstance(spec_error_string(code), str) and spec_error_string(code)
     assert spec_version() >= 100
+
+
+def test_stats_host_checks_reject_before_any_gpu_call(lib):
+    from draft_sampling_lossless_spec_amd.binding import _Dims
+    from draft_sampling_lossless_spec_amd import spec_stats_workspace_bytes, BF16, FP32
+    assert spec_stats_workspace_bytes(256, 16, 151936, 256, BF16) % 256 == 0
+    assert spec_stats_workspace_bytes(256, 16, 151936, 256, BF16) > spec_stats_workspace_bytes(64, 5, 151936, 256,
+                                                                                                BF16)
+    assert spec_stats_workspace_bytes(2, 4, 100, 24, BF16) == 0 and spec_stats_workspace_bytes(2, 4, 100, 24, FP32) > 0
+    d = _Dims(2, 4, 100, 16, 1, 1)
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    nulls = [None] * 10 + [None, C.c_size_t(0), None]
+    assert lib.spec_accept_stats(C.byref(d), *nulls) == -1              # NULL inputs
+    assert lib.spec_accept_stats(None, *nulls) == -1
+    full = [fake] * 4 + [None, fake, fake, fake, None, None, None, C.c_size_t(0), None]
+    assert lib.spec_accept_stats(C.byref(d), *full) == -3               # no workspace
+    bad = _Dims(2, 4, 100, 24, 1, 1)
+    assert lib.spec_accept_stats(C.byref(bad), *full) == -2             # bf16 with R % 16 != 0
+    mis = [fake, fake, C.c_void_p(4100)] + full[3:]
+    assert lib.spec_accept_stats(C.byref(d), *mis) == -1                # misaligned A
+    e = [fake, fake, fake]
+    assert lib.spec_calibration_error(*e, 0, 4, 10, fake, fake, None) == -1          # B < 1
+    assert lib.spec_calibration_error(*e, 2, 4, 0, fake, fake, None) == -1           # no bin
+    assert lib.spec_calibration_error(*e, 2, 4, 5000, fake, fake, None) == -1        # too many bins
+    assert lib.spec_calibration_error(None, fake, fake, 2, 4, 10, fake, fake, None) == -1
