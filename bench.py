@@ -77,6 +77,9 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=0,
                     help="requests in the oracle's timed sample (0 = the whole batch of one cycle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats", action="store_true",
+                    help="measure the acceptance-statistics call (alpha = 1 - TV per drafted position) on the drafts "
+                         "of one cycle of the workload instead of the cycle itself; prints its own JSON line")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -92,6 +95,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4, "copies": 5}), flush=True)
         return
+    if args.stats:
+        return bench_stats(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
               "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -190,8 +195,9 @@ def main():
     value = sL / t_cycle
     kb_ms, kp_ms, km_ms = (float(x.sum(axis=1).mean()) for x in (kb, kp, km))
     n_active = int(L.max()) + 1
-    if kp_ms < 2e-3:
-        # bf16 fast path: the plain rows run inside the sweep kernel (its plain slot is empty)
+    if cfg.dtype == 1 and cfg.V % 8 == 0:
+        # bf16 vector path: the plain rows run inside the sweep kernel (the plain slot's event pair
+        # brackets nothing but the events themselves)
         sweep_bytes = bias_bytes + plain_bytes
         kernels = {
             "k_sweep": {"us_per_cycle": kb_ms * 1e3, "algorithmic_bytes": sweep_bytes,
@@ -248,6 +254,75 @@ def main():
                      "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"] / (K + 1)},
         "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_stats(args):
+    """Acceptance statistics of one cycle's drafted positions: spec_accept_stats timed on its own
+    (plain calls, wall clock), HBM roofline of the whole call, the oracle beside it on a sample."""
+    import torch
+    from draft_sampling_lossless_spec_amd import CHUNKED, spec_accept_stats, spec_cycle, spec_stats_workspace_bytes
+    from draft_sampling_lossless_spec_amd import workloads as wl
+
+    w = wl.generate(args.config, threshold=args.threshold)
+    cfg = w.cfg
+    dev = torch.device("cuda:0")
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    base, target, A, W = t(w.base), t(w.target), t(w.A), t(w.W)
+    x0, conf, temp = t(w.x0), t(w.conf), t(w.temp)
+    B, K = cfg.B, cfg.K
+    diag = spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=CHUNKED, diag=True)
+    draft = diag["draft_tokens"]
+    torch.cuda.synchronize()
+    rows = int((draft >= 0).sum().item())
+    ws = torch.empty(spec_stats_workspace_bytes(B, K, cfg.V, cfg.R, cfg.dtype), dtype=torch.uint8, device=dev)
+    out = {k: torch.empty((B, K), dtype=torch.float32, device=dev) for k in ("alpha", "lse_q", "lse_p")}
+    run = lambda: spec_accept_stats(base, target, A, W, draft, temp, x0=x0, workspace=ws, out=out)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - ts) * 1e3 / args.steps
+    # the same calls again between events on the stream they run on: the call-level roofline
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    e = 2 if cfg.dtype == 1 else 4
+    alg = e * cfg.V * 2 * rows + e * cfg.R * cfg.V + e * cfg.R * rows + 4 * 3 * B * K
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        d_np = draft.cpu().numpy()
+        n = max(1, min(B, args.cpu_requests or B))
+        tc = time.perf_counter()
+        oracle.accept_stats_ref(w.base[:n], w.target[:n], w.A, w.W, w.x0[:n], d_np[:n], w.temp[:n])
+        dt = time.perf_counter() - tc
+        cpu = {"value": float((d_np[:n] >= 0).sum() / dt), "unit": "drafted positions/s", "cores": oracle.max_threads(),
+               "kind": "oracle", "sample": f"first {n} of {B} requests ({int((d_np[:n] >= 0).sum())} positions, "
+                                           f"{dt:.1f} s wall, fp64 C + OpenMP)"}
+    line = {
+        "metric": "acceptance statistics: drafted positions/s (alpha = 1 - TV per position)", "value": rows / (ms * 1e-3),
+        "unit": "drafted positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == 1 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "K": K, "V": cfg.V, "R": cfg.R, "rows": rows},
+        "roofline": {"bound": "hbm", "achieved": alg / (ms_ev * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": alg / (ms_ev * 1e-3) / HBM_PEAK, "traffic": None,
+                     "kernel": "spec_accept_stats (prep, 2 sweeps, 2 merges)", "algorithmic_bytes_per_call": alg},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
