@@ -88,6 +88,8 @@ def load(build_if_missing: bool = True) -> C.CDLL:
     lib.spec_calibration_error_ref.restype = C.c_double
     lib.spec_calibration_error_ref.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                                C.POINTER(C.c_int64)]
+    lib.spec_schedule_ref.restype = C.c_int
+    lib.spec_schedule_ref.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]
     _lib = lib
     return lib
 
@@ -268,3 +270,24 @@ def calibration_error_ref(conf, verify_len, accepted_len, nbins=10):
     n = C.c_int64(0)
     e = lib.spec_calibration_error_ref(conf.ctypes.data, L.ctypes.data, a.ctypes.data, B, K, int(nbins), C.byref(n))
     return float(e), int(n.value)
+
+
+# ----------------------------------------------------------------------------------------
+# prefix scheduler
+# ----------------------------------------------------------------------------------------
+def schedule_ref(conf, step_time, nbins=4096) -> dict:
+    """Hardware-aware prefix scheduler (definition in spec_oracle.c): per-request verify lengths
+    maximising expected emitted tokens per second of target step time."""
+    lib = load()
+    conf = np.ascontiguousarray(conf, dtype=np.float32)
+    B, K = conf.shape
+    T = np.ascontiguousarray(step_time, dtype=np.float64)
+    if T.shape != (B * K + 1,):
+        raise ValueError(f"step_time must have B*K+1 = {B * K + 1} entries")
+    L = np.empty(B, np.int32)
+    out = np.empty(4, np.float64)
+    rc = lib.spec_schedule_ref(conf.ctypes.data, B, K, T.ctypes.data, int(nbins), L.ctypes.data, out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"spec_schedule_ref rejected its arguments (code {rc})")
+    return {"verify_len": L, "threshold": float(out[0]), "n": int(out[1]), "expected_tokens": float(out[2]),
+            "goodput": float(out[3])}

@@ -704,3 +704,83 @@ double spec_calibration_error_ref(const float* conf, const int32_t* verify_len, 
   free(cnt);
   return N > 0 ? ece : 0.0;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Hardware-aware prefix scheduler.
+ *
+ * The scheduler reads the confidences as prefix-survival probabilities P_{b,j} = prod_{i<=j}
+ * c_{b,i}, weighs the expected accepted tokens of each verification position against a profiled
+ * throughput curve of the target engine, and picks per-request prefix lengths under the current
+ * batch pressure; an early-stopping rule (a request's prefix ends at its first position that
+ * fails) keeps it lossless ("DSpark turns speculation into a scheduler", section "Confidence is a
+ * serving primitive": which verification tokens have positive expected return given the batch
+ * pressure; "The Speed Claim...", section "The Real Innovation": verify more when GPUs are idle,
+ * fewer when they are busy, early stopping stays lossless).
+ *
+ * Reading written out here:
+ *   M_{b,j} = min_{i<=j} P_{b,i} (fp64): position j is kept at threshold tau iff M_{b,j} >= tau,
+ *     so every kept set is a prefix and a prefix ends at its first failing position;
+ *   thresholds on a grid: g = 1..nbins with position j kept iff bin(M) >= g, where
+ *     bin(M) = min(floor(fl(M * nbins)), nbins) (fp64 product), plus g = nbins + 1 = keep nothing;
+ *   n_g = kept positions, S_g = sum of P over them; expected emitted tokens E_g = B + S_g (one
+ *     correction or bonus token per request plus the expected accepted drafts);
+ *   step_time[n] (n = 0..B K) = seconds of one target verification step with n draft tokens in
+ *     the batch; goodput G_g = E_g / step_time[n_g];
+ *   g* = argmax G_g, ties to the larger g (fewer tokens); verify_len[b] = number of leading
+ *     positions with bin(M_{b,j}) >= g*.
+ * out[0] = g* / nbins (the threshold; > 1 when nothing is kept), out[1] = n*, out[2] = E*,
+ * out[3] = G*.  Returns 0, or -1 for bad arguments.
+ * --------------------------------------------------------------------------------------- */
+static int64_t sched_bin(double M, int32_t nbins) {
+  double f = floor(M * (double)nbins);
+  if (!(f >= 0.0)) return 0;                 /* NaN or negative: the lowest bin */
+  if (f > (double)nbins) return nbins;
+  return (int64_t)f;
+}
+
+int spec_schedule_ref(const float* conf, int32_t B, int32_t K, const double* step_time, int32_t nbins,
+                      int32_t* verify_len, double* out) {
+  if (!conf || !step_time || !verify_len || !out || B < 1 || K < 1 || nbins < 1) return -1;
+  int64_t* bins = (int64_t*)malloc(sizeof(int64_t) * (size_t)B * K);
+  double* P = (double*)malloc(sizeof(double) * (size_t)B * K);
+  for (int32_t b = 0; b < B; b++) {
+    double p = 1.0, m = INFINITY;
+    for (int32_t j = 0; j < K; j++) {
+      p *= (double)conf[(size_t)b * K + j];
+      if (p < m || isnan(p)) m = p;          /* running minimum; a NaN stays */
+      P[(size_t)b * K + j] = p;
+      bins[(size_t)b * K + j] = sched_bin(m, nbins);
+    }
+  }
+  int32_t best_g = nbins + 1;
+  double best_G = (double)B / step_time[0], best_E = (double)B;
+  int64_t best_n = 0;
+  for (int32_t g = nbins; g >= 1; g--) {       /* larger g first: ties keep the larger g */
+    int64_t n = 0;
+    double S = 0.0;
+    for (int64_t i = 0; i < (int64_t)B * K; i++)
+      if (bins[i] >= g) {
+        n++;
+        S += P[i];
+      }
+    const double E = (double)B + S, G = E / step_time[n];
+    if (G > best_G) {
+      best_G = G;
+      best_g = g;
+      best_n = n;
+      best_E = E;
+    }
+  }
+  for (int32_t b = 0; b < B; b++) {
+    int32_t L = 0;
+    while (L < K && bins[(size_t)b * K + L] >= best_g) L++;
+    verify_len[b] = L;
+  }
+  out[0] = (double)best_g / (double)nbins;
+  out[1] = (double)best_n;
+  out[2] = best_E;
+  out[3] = best_G;
+  free(bins);
+  free(P);
+  return 0;
+}

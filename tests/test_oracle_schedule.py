@@ -1,0 +1,114 @@
+"""Pins of the oracle's hardware-aware prefix scheduler (definition written out in
+oracle/spec_oracle.c, worked cases in tests/golden/schedule_cases.txt): hand-worked loads, an
+exact-rational brute force over every threshold of the grid, the early-stopping rule on
+confidences above 1, and the load response the pages describe (a busier engine never verifies
+more tokens)."""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "schedule_cases.txt")
+CONF = np.array([[0.9, 0.5, 0.9], [0.8, 0.8, 0.8]], np.float32)
+
+
+def _cases():
+    out = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        f = [x.split() for x in line.split("|")]
+        out.append((float(f[0][0]), float(f[0][1]), int(f[0][2]), [int(v) for v in f[1]], float(f[2][0]),
+                    int(f[3][0]), float(f[4][0]), float(f[5][0])))
+    return out
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_worked_loads(case):
+    t0, t1, nbins, L, tau, n, E, G = _cases()[case]
+    T = t0 + t1 * np.arange(CONF.size + 1, dtype=np.float64)
+    r = oracle.schedule_ref(CONF, T, nbins)
+    assert list(r["verify_len"]) == L
+    assert abs(r["threshold"] - tau) < 1e-12 and r["n"] == n
+    assert abs(r["expected_tokens"] - E) < 1e-6 and abs(r["goodput"] - G) < 1e-6
+
+
+def _brute(conf, T, nbins):
+    """every grid threshold in exact rational arithmetic (fp32 confidences taken exactly)"""
+    B, K = conf.shape
+    best = (Fraction(B) / Fraction(float(T[0])), nbins + 1, 0)
+    P, bins = [], []
+    for b in range(B):
+        p, m = Fraction(1), None
+        for j in range(K):
+            p *= Fraction(float(conf[b, j]))
+            m = p if m is None or p < m else m
+            P.append(p)
+            bins.append(min(math.floor(m * nbins), nbins))
+    for g in range(nbins, 0, -1):
+        kept = [i for i in range(B * K) if bins[i] >= g]
+        G = (B + sum((P[i] for i in kept), Fraction(0))) / Fraction(float(T[len(kept)]))
+        if G > best[0]:
+            best = (G, g, len(kept))
+    L = []
+    for b in range(B):
+        n = 0
+        while n < K and bins[b * K + n] >= best[1]:
+            n += 1
+        L.append(n)
+    return best, L
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_over_the_grid(seed):
+    rng = np.random.default_rng(seed)
+    B, K, nbins = int(rng.integers(1, 5)), int(rng.integers(1, 5)), int(rng.integers(5, 40))
+    conf = rng.beta(5, 2, (B, K)).astype(np.float32)
+    T = 1.0 + rng.uniform(0.05, 0.5) * np.arange(B * K + 1) + rng.uniform(0, 0.2, B * K + 1).cumsum()
+    (G, g, n), L = _brute(conf, T, nbins)
+    r = oracle.schedule_ref(conf, T, nbins)
+    # decisions equal unless the exact goodputs of two grid points tie to 1e-12
+    assert r["n"] == n and list(r["verify_len"]) == L and abs(r["threshold"] - g / nbins) < 1e-15
+    assert abs(r["goodput"] - float(G)) < 1e-12 * float(G)
+
+
+def test_constant_step_time_keeps_every_position_above_the_first_bin():
+    rng = np.random.default_rng(3)
+    conf = rng.uniform(0.3, 1.0, (8, 6)).astype(np.float32)
+    nbins = 64
+    r = oracle.schedule_ref(conf, np.full(conf.size + 1, 2.0), nbins)
+    P = np.cumprod(conf.astype(np.float64), axis=1)
+    M = np.minimum.accumulate(P, axis=1)
+    keep = np.floor(M * nbins) >= 1
+    assert abs(r["threshold"] - 1 / nbins) < 1e-15
+    assert list(r["verify_len"]) == list(np.cumprod(keep, axis=1).sum(axis=1))
+
+
+def test_confidence_above_one_cannot_reopen_a_failed_prefix():
+    # c = [0.5, 3.0]: P = 0.5, 1.5 but the running minimum is 0.5, 0.5 -- position 1 rides on
+    # position 0 (early stopping); kept together they add 0.5 + 1.5 expected tokens
+    conf = np.array([[0.5, 3.0]], np.float32)
+    T = np.array([1.0, 1.2, 1.4])
+    r = oracle.schedule_ref(conf, T, 100)
+    assert list(r["verify_len"]) == [2] and r["n"] == 2
+    assert abs(r["expected_tokens"] - 3.0) < 1e-12 and abs(r["threshold"] - 0.5) < 1e-15
+    # a load where one extra token is not worth it: both go, never position 1 alone
+    r = oracle.schedule_ref(conf, np.array([1.0, 1.2, 3.5]), 100)
+    assert list(r["verify_len"]) == [0] and r["n"] == 0
+
+
+def test_a_busier_engine_never_verifies_more():
+    rng = np.random.default_rng(9)
+    conf = rng.beta(6, 2, (64, 8)).astype(np.float32)
+    ns = []
+    for t1 in (0.0, 0.002, 0.01, 0.03, 0.1, 0.3, 1.0):
+        T = 1.0 + t1 * np.arange(conf.size + 1)
+        r = oracle.schedule_ref(conf, T, 1024)
+        assert r["n"] == int(r["verify_len"].sum())
+        ns.append(r["n"])
+    assert all(a >= b for a, b in zip(ns, ns[1:])) and ns[0] > ns[-1]
