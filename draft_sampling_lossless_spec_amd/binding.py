@@ -60,6 +60,9 @@ def _load():
     lib.spec_stats_workspace_bytes.argtypes = [C.POINTER(_Dims)]
     lib.spec_accept_stats.restype = C.c_int
     lib.spec_accept_stats.argtypes = [C.POINTER(_Dims)] + [C.c_void_p] * 10 + [C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.spec_schedule.restype = C.c_int
+    lib.spec_schedule.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                  C.c_void_p]
     lib.spec_calibration_error.restype = C.c_int
     lib.spec_calibration_error.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                            C.c_void_p, C.c_void_p, C.c_void_p]
@@ -228,3 +231,26 @@ def spec_calibration_error(conf, verify_len, accepted_len, nbins: int = 10, stre
     if rc != 0:
         raise SpecError(f"spec_calibration_error failed: {spec_error_string(rc)} (code {rc})")
     return ece, n
+
+
+def spec_schedule(conf, step_time, nbins: int = 4096, verify_len=None, out=None, stream=None):
+    """Hardware-aware prefix scheduler: per-request verify lengths ([B] int32 device tensor) and a
+    [4] fp64 device tensor (threshold, kept positions, expected emitted tokens, goodput) for the
+    confidences conf [B, K] fp32 and the target step-time curve step_time [B K + 1] fp64 (seconds
+    per verification step with n draft tokens).  Asynchronous."""
+    import torch
+    B, K = conf.shape
+    _check(conf, "conf", (B, K), torch.float32)
+    _check(step_time, "step_time", (B * K + 1,), torch.float64)
+    dev = conf.device
+    if verify_len is None:
+        verify_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty(4, dtype=torch.float64, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = _load().spec_schedule(conf.data_ptr(), B, K, step_time.data_ptr(), int(nbins), verify_len.data_ptr(),
+                               out.data_ptr(), C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_schedule failed: {spec_error_string(rc)} (code {rc})")
+    return verify_len, out

@@ -1867,6 +1867,141 @@ __global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int
   }
 }
 
+// ==========================================================================================
+// Hardware-aware prefix scheduler ("DSpark turns speculation into a scheduler", section
+// "Confidence is a serving primitive": per-request prefix lengths from prefix survival and a
+// profiled throughput curve, verification tokens with positive expected return under the batch
+// pressure; "The Speed Claim Nobody's Really Questioning", section "The Real Innovation": verify
+// more when the engine is idle, fewer when it is busy, early stopping keeps it lossless).
+// One workgroup: every position's running minimum of prefix survival is binned on a threshold
+// grid (counts and fp64 survival sums in LDS), suffix sums over the bins give the kept count n_g
+// and expected emitted tokens E_g = B + S_g of every threshold g / nbins, goodput
+// E_g / step_time[n_g] is maximised (ties to the larger g; g = nbins + 1 keeps nothing), and each
+// request's verify length is the length of its prefix at the chosen threshold.
+// ==========================================================================================
+constexpr int SCHED_NT = 1024;
+constexpr int MAX_SCHED_BINS = 4096;
+
+__device__ __forceinline__ int sched_bin(double M, int nbins) {
+  const double f = floor(M * (double)nbins);
+  if (!(f >= 0.0)) return 0;   // NaN or negative: the lowest bin
+  return f > (double)nbins ? nbins : (int)f;
+}
+
+__global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B, int K, const double* step_time,
+                                                     int nbins, int32_t* verify_len, double* out) {
+  __shared__ int cnt[MAX_SCHED_BINS + 1];
+  __shared__ double ssum[MAX_SCHED_BINS + 1];
+  __shared__ int tn[SCHED_NT];
+  __shared__ double ts[SCHED_NT];
+  __shared__ double bestG[SCHED_NT / 64];
+  __shared__ int bestg[SCHED_NT / 64];
+  __shared__ int g_star;
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= nbins; i += SCHED_NT) {
+    cnt[i] = 0;
+    ssum[i] = 0.0;
+  }
+  __syncthreads();
+  for (int b = tid; b < B; b += SCHED_NT) {
+    double P = 1.0, M = INFINITY;
+    for (int j = 0; j < K; j++) {
+      P *= (double)conf[(size_t)b * K + j];
+      if (P < M || isnan(P)) M = P;
+      const int k = sched_bin(M, nbins);
+      atomicAdd(&cnt[k], 1);
+      atomicAdd(&ssum[k], P);
+    }
+  }
+  __syncthreads();
+  // suffix sums over bins 1..nbins: thread t owns a contiguous chunk of bins
+  const int nb = nbins + 1, chunk = (nb + SCHED_NT - 1) / SCHED_NT;
+  const int lo = tid * chunk, hi = min(lo + chunk, nb);
+  int cn = 0;
+  double cs = 0.0;
+  for (int k = lo; k < hi; k++) {
+    cn += cnt[k];
+    cs += ssum[k];
+  }
+  tn[tid] = cn;
+  ts[tid] = cs;
+  __syncthreads();
+  // inclusive scan from the top (Hillis-Steele): tn[t] = sum over threads t' >= t
+  for (int o = 1; o < SCHED_NT; o <<= 1) {
+    const int an = tid + o < SCHED_NT ? tn[tid + o] : 0;
+    const double as = tid + o < SCHED_NT ? ts[tid + o] : 0.0;
+    __syncthreads();
+    tn[tid] += an;
+    ts[tid] += as;
+    __syncthreads();
+  }
+  // candidates of this chunk, top down; the suffix above the chunk is the next thread's total
+  int n = tid + 1 < SCHED_NT ? tn[tid + 1] : 0;
+  double S = tid + 1 < SCHED_NT ? ts[tid + 1] : 0.0;
+  double best = -INFINITY;
+  int bg = nbins + 1;
+  if (tid == 0) best = (double)B / step_time[0];   // keep nothing
+  for (int k = hi - 1; k >= lo; k--) {
+    n += cnt[k];
+    S += ssum[k];
+    if (k >= 1) {
+      const double G = ((double)B + S) / step_time[n];
+      if (G > best || (G == best && k > bg && bg <= nbins)) {
+        best = G;
+        bg = k;
+      }
+    }
+  }
+  // block argmax, ties to the larger g (nbins + 1 = keep nothing counts as the largest)
+  for (int o = 32; o > 0; o >>= 1) {
+    const double G2 = __shfl_xor(best, o, 64);
+    const int g2 = __shfl_xor(bg, o, 64);
+    if (G2 > best || (G2 == best && g2 > bg)) {
+      best = G2;
+      bg = g2;
+    }
+  }
+  if ((tid & 63) == 0) {
+    bestG[tid >> 6] = best;
+    bestg[tid >> 6] = bg;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double G = bestG[0];
+    int g = bestg[0];
+    for (int w = 1; w < SCHED_NT / 64; w++)
+      if (bestG[w] > G || (bestG[w] == G && bestg[w] > g)) {
+        G = bestG[w];
+        g = bestg[w];
+      }
+    g_star = g;
+    int nk = 0;
+    double Sk = 0.0;
+    for (int k = g; k <= nbins; k++) {
+      nk += cnt[k];
+      Sk += ssum[k];
+    }
+    out[0] = (double)g / (double)nbins;
+    out[1] = (double)nk;
+    out[2] = (double)B + Sk;
+    out[3] = G;
+  }
+  __syncthreads();
+  const int gs = g_star;
+  for (int b = tid; b < B; b += SCHED_NT) {
+    double P = 1.0, M = INFINITY;
+    int L = 0;
+    bool go = true;
+    for (int j = 0; j < K; j++) {
+      P *= (double)conf[(size_t)b * K + j];
+      if (P < M || isnan(P)) M = P;
+      go = go && sched_bin(M, nbins) >= gs;
+      L += go ? 1 : 0;
+    }
+    verify_len[b] = L;
+  }
+}
+
 struct Layout {
   size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
       off_pbias, off_pbias2, off_pplain, off_konst, total;
@@ -2212,6 +2347,19 @@ extern "C" int spec_calibration_error(const float* conf, const int32_t* verify_l
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_calibration, dim3(1), dim3(NT), 0, (hipStream_t)stream, conf, verify_len, accepted_len, B, K,
                      nbins, ece, n_pairs);
+  if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
+}
+
+extern "C" int spec_schedule(const float* conf, int32_t B, int32_t K, const double* step_time, int32_t nbins,
+                             int32_t* verify_len, double* out, spec_stream_t stream) {
+  if (!conf || !step_time || !verify_len || !out) return SPEC_E_INVAL;
+  if (B < 1 || B > MAX_B || K < 1 || K > MAX_K || nbins < 1 || nbins > MAX_SCHED_BINS) return SPEC_E_INVAL;
+  const int ac = arch_ok();
+  if (ac != SPEC_OK) return ac;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(SCHED_NT), 0, (hipStream_t)stream, conf, B, K, step_time, nbins,
+                     verify_len, out);
   if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
   return SPEC_OK;
 }

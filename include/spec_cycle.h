@@ -174,6 +174,31 @@ int spec_calibration_error(const float* conf, const int32_t* verify_len, const i
                            int32_t B, int32_t K, int32_t nbins, double* ece, int64_t* n_pairs,
                            spec_stream_t stream);
 
+/*
+ * Hardware-aware prefix scheduler: per-request verify lengths for the current batch pressure.
+ * The confidences are read as prefix-survival probabilities P_{b,j} = prod_{i<=j} conf[b, i];
+ * verification positions are weighed against a profiled throughput curve of the target engine
+ * ("DSpark turns speculation into a scheduler", section "Confidence is a serving primitive";
+ * "The Speed Claim...", section "The Real Innovation": verify more when the engine is idle, fewer
+ * when it is busy, an early-stopping rule keeps the schedule lossless).
+ *   Position j of request b is kept at threshold g / nbins iff bin(M_{b,j}) >= g, where M is the
+ *   fp64 running minimum of P (so a prefix ends at its first failing position) and
+ *   bin(M) = min(floor(M * nbins), nbins).  For g = 1..nbins (and g = nbins + 1: keep nothing):
+ *   n_g kept positions, expected emitted tokens E_g = B + sum of P over them, goodput
+ *   E_g / step_time[n_g].  The largest goodput wins, ties to the larger g.
+ *   conf       [B, K] fp32 device  confidences
+ *   step_time  [B K + 1] fp64 device  seconds of one target verification step carrying n draft
+ *              tokens, n = 0..B K (the profiled throughput curve), > 0
+ *   nbins      threshold grid, 1..4096
+ *   verify_len [B] int32 device out: each request's prefix length at the chosen threshold
+ *   out        [4] fp64 device out: threshold g / nbins (> 1 when nothing is kept), kept positions,
+ *              expected emitted tokens, goodput (tokens per second)
+ * Asynchronous on `stream`; one workgroup.  Returns SPEC_OK or SPEC_E_INVAL (NULL pointer, B
+ * outside 1..1024, K outside 1..32, nbins outside 1..4096).
+ */
+int spec_schedule(const float* conf, int32_t B, int32_t K, const double* step_time, int32_t nbins,
+                  int32_t* verify_len, double* out, spec_stream_t stream);
+
 /* Static description of an error code (never NULL). */
 const char* spec_error_string(int code);
 

@@ -93,3 +93,13 @@ def test_stats_host_checks_reject_before_any_gpu_call(lib):
     assert lib.spec_calibration_error(*e, 2, 4, 0, fake, fake, None) == -1           # no bin
     assert lib.spec_calibration_error(*e, 2, 4, 5000, fake, fake, None) == -1        # too many bins
     assert lib.spec_calibration_error(None, fake, fake, 2, 4, 10, fake, fake, None) == -1
+
+
+def test_schedule_host_checks_reject_before_any_gpu_call(lib):
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    assert lib.spec_schedule(None, 2, 4, fake, 64, fake, fake, None) == -1
+    assert lib.spec_schedule(fake, 0, 4, fake, 64, fake, fake, None) == -1          # B < 1
+    assert lib.spec_schedule(fake, 2, 33, fake, 64, fake, fake, None) == -1         # K > 32
+    assert lib.spec_schedule(fake, 2, 4, fake, 0, fake, fake, None) == -1           # no bin
+    assert lib.spec_schedule(fake, 2, 4, fake, 4097, fake, fake, None) == -1        # too many bins
+    assert lib.spec_schedule(fake, 2, 4, None, 64, fake, fake, None) == -1
