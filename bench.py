@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--stats", action="store_true",
                     help="measure the acceptance-statistics call (alpha = 1 - TV per drafted position) on the drafts "
                          "of one cycle of the workload instead of the cycle itself; prints its own JSON line")
+    ap.add_argument("--schedule", action="store_true",
+                    help="measure the prefix scheduler on the workload's confidences against a synthetic target "
+                         "step-time curve at several loads; prints its own JSON line")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -97,6 +100,8 @@ def main():
         return
     if args.stats:
         return bench_stats(args)
+    if args.schedule:
+        return bench_schedule(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
               "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -254,6 +259,77 @@ def main():
                      "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"] / (K + 1)},
         "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_schedule(args):
+    """Prefix scheduler: spec_schedule on the workload's confidences, timed with events on its
+    stream, against the target step-time curve t(n) = t0 + t1 n (seconds per verification step with
+    n draft tokens; t0 = the measured speculation cycle plus a fixed target cost, t1 the per-token
+    cost at a few loads), with the oracle beside it."""
+    import torch
+    from draft_sampling_lossless_spec_amd import spec_schedule
+    from draft_sampling_lossless_spec_amd import workloads as wl
+
+    w = wl.generate(args.config, threshold=args.threshold)
+    B, K = w.cfg.B, w.cfg.K
+    conf = torch.from_numpy(w.conf.astype(np.float32)).cuda()
+    n = np.arange(B * K + 1, dtype=np.float64)
+    loads = {}
+    for name, t1 in (("idle", 2e-7), ("moderate", 2e-6), ("busy", 2e-5)):
+        T = torch.from_numpy(0.02 + t1 * n).cuda()      # 20 ms per target step plus t1 per draft token
+        L, out = spec_schedule(conf, T, 4096)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        loads[name] = {"t1_s_per_token": t1, "verify_tokens": int(o[1]), "threshold": float(o[0]),
+                       "mean_verify_len": float(L.float().mean().item()), "expected_tokens": float(o[2])}
+    T = torch.from_numpy(0.02 + 2e-6 * n).cuda()
+    Lb = torch.empty(B, dtype=torch.int32, device="cuda")
+    ob = torch.empty(4, dtype=torch.float64, device="cuda")
+    for _ in range(args.warmup):
+        spec_schedule(conf, T, 4096, verify_len=Lb, out=ob)
+    torch.cuda.synchronize()
+    # one launch is a few microseconds, less than the Python call around it: the timed calls are
+    # captured into one graph and replayed once between events
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(args.steps):
+                spec_schedule(conf, T, 4096, verify_len=Lb, out=ob)
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        Tn = 0.02 + 2e-6 * n
+        reps = 0
+        tc = time.perf_counter()
+        while time.perf_counter() - tc < 2.0:
+            oracle.schedule_ref(w.conf.astype(np.float32), Tn, 4096)
+            reps += 1
+        dt = (time.perf_counter() - tc) / reps
+        cpu = {"value": 1.0 / dt, "unit": "schedules/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole batch, {reps} calls in {dt * reps:.1f} s (fp64 C, one thread)"}
+    byt = 4 * B * K + 8 * (B * K + 1) + 4 * B + 32
+    line = {
+        "metric": "prefix scheduler: schedules/s", "value": 1e6 / us, "unit": "schedules/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": w.cfg.name, "B": B, "K": K, "nbins": 4096, "loads": loads},
+        "roofline": {"bound": "hbm", "achieved": byt / (us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": byt / (us * 1e-6) / HBM_PEAK, "traffic": None, "kernel": "k_schedule",
+                     "note": "one workgroup over a few tens of KB: latency-bound, the HBM figure is for the record"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

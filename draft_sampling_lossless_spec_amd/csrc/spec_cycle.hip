@@ -1879,7 +1879,7 @@ __global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int
 // E_g / step_time[n_g] is maximised (ties to the larger g; g = nbins + 1 keeps nothing), and each
 // request's verify length is the length of its prefix at the chosen threshold.
 // ==========================================================================================
-constexpr int SCHED_NT = 1024;
+constexpr int SCHED_NT = 1024;   // >= MAX_B: one request per thread
 constexpr int MAX_SCHED_BINS = 4096;
 
 __device__ __forceinline__ int sched_bin(double M, int nbins) {
@@ -1896,6 +1896,8 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
   __shared__ double ts[SCHED_NT];
   __shared__ double bestG[SCHED_NT / 64];
   __shared__ int bestg[SCHED_NT / 64];
+  __shared__ int bestn[SCHED_NT / 64];
+  __shared__ double bestS[SCHED_NT / 64];
   __shared__ int g_star;
   const int tid = threadIdx.x;
   for (int i = tid; i <= nbins; i += SCHED_NT) {
@@ -1903,14 +1905,24 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
     ssum[i] = 0.0;
   }
   __syncthreads();
-  for (int b = tid; b < B; b += SCHED_NT) {
+  // one request per thread (B <= 1024): its confidences loaded at once, its bins kept in registers
+  const int b = tid;
+  int mb[MAX_K];
+  {
+    float c[MAX_K];
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) c[j] = (b < B && j < K) ? conf[(size_t)b * K + j] : 1.0f;
     double P = 1.0, M = INFINITY;
-    for (int j = 0; j < K; j++) {
-      P *= (double)conf[(size_t)b * K + j];
-      if (P < M || isnan(P)) M = P;
-      const int k = sched_bin(M, nbins);
-      atomicAdd(&cnt[k], 1);
-      atomicAdd(&ssum[k], P);
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) {
+      mb[j] = -1;
+      if (b < B && j < K) {
+        P *= (double)c[j];
+        if (P < M || isnan(P)) M = P;
+        mb[j] = sched_bin(M, nbins);
+        atomicAdd(&cnt[mb[j]], 1);
+        atomicAdd(&ssum[mb[j]], P);
+      }
     }
   }
   __syncthreads();
@@ -1938,64 +1950,58 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
   // candidates of this chunk, top down; the suffix above the chunk is the next thread's total
   int n = tid + 1 < SCHED_NT ? tn[tid + 1] : 0;
   double S = tid + 1 < SCHED_NT ? ts[tid + 1] : 0.0;
-  double best = -INFINITY;
-  int bg = nbins + 1;
+  double best = -INFINITY, bS = 0.0;
+  int bg = nbins + 1, bn = 0;
   if (tid == 0) best = (double)B / step_time[0];   // keep nothing
   for (int k = hi - 1; k >= lo; k--) {
     n += cnt[k];
     S += ssum[k];
     if (k >= 1) {
       const double G = ((double)B + S) / step_time[n];
-      if (G > best || (G == best && k > bg && bg <= nbins)) {
+      if (G > best) {   // top down: an equal goodput keeps the larger g found first
         best = G;
         bg = k;
+        bn = n;
+        bS = S;
       }
     }
   }
   // block argmax, ties to the larger g (nbins + 1 = keep nothing counts as the largest)
   for (int o = 32; o > 0; o >>= 1) {
-    const double G2 = __shfl_xor(best, o, 64);
-    const int g2 = __shfl_xor(bg, o, 64);
+    const double G2 = __shfl_xor(best, o, 64), S2 = __shfl_xor(bS, o, 64);
+    const int g2 = __shfl_xor(bg, o, 64), n2 = __shfl_xor(bn, o, 64);
     if (G2 > best || (G2 == best && g2 > bg)) {
       best = G2;
       bg = g2;
+      bn = n2;
+      bS = S2;
     }
   }
   if ((tid & 63) == 0) {
     bestG[tid >> 6] = best;
     bestg[tid >> 6] = bg;
+    bestn[tid >> 6] = bn;
+    bestS[tid >> 6] = bS;
   }
   __syncthreads();
   if (tid == 0) {
-    double G = bestG[0];
-    int g = bestg[0];
+    int w0 = 0;
     for (int w = 1; w < SCHED_NT / 64; w++)
-      if (bestG[w] > G || (bestG[w] == G && bestg[w] > g)) {
-        G = bestG[w];
-        g = bestg[w];
-      }
-    g_star = g;
-    int nk = 0;
-    double Sk = 0.0;
-    for (int k = g; k <= nbins; k++) {
-      nk += cnt[k];
-      Sk += ssum[k];
-    }
-    out[0] = (double)g / (double)nbins;
-    out[1] = (double)nk;
-    out[2] = (double)B + Sk;
-    out[3] = G;
+      if (bestG[w] > bestG[w0] || (bestG[w] == bestG[w0] && bestg[w] > bestg[w0])) w0 = w;
+    g_star = bestg[w0];
+    out[0] = (double)bestg[w0] / (double)nbins;
+    out[1] = (double)bestn[w0];
+    out[2] = (double)B + bestS[w0];
+    out[3] = bestG[w0];
   }
   __syncthreads();
   const int gs = g_star;
-  for (int b = tid; b < B; b += SCHED_NT) {
-    double P = 1.0, M = INFINITY;
+  if (b < B) {
     int L = 0;
     bool go = true;
-    for (int j = 0; j < K; j++) {
-      P *= (double)conf[(size_t)b * K + j];
-      if (P < M || isnan(P)) M = P;
-      go = go && sched_bin(M, nbins) >= gs;
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) {
+      go = go && j < K && mb[j] >= gs;   // bins are non-increasing along j: the prefix ends at its first failure
       L += go ? 1 : 0;
     }
     verify_len[b] = L;
