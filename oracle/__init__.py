@@ -79,6 +79,9 @@ def load(build_if_missing: bool = True) -> C.CDLL:
         fn.restype = C.c_int
         fn.argtypes = common + [C.c_void_p, C.c_void_p, C.c_void_p, C.c_float, C.c_uint64, C.c_int64,
                                 C.POINTER(Out), C.c_int]
+    lib.spec_cycle_ref_lengths.restype = C.c_int
+    lib.spec_cycle_ref_lengths.argtypes = common + [C.c_void_p, C.c_void_p, C.c_void_p, C.c_uint64, C.c_int64,
+                                                    C.POINTER(Out), C.c_int]
     lib.spec_cycle_ref_mc.restype = C.c_int
     lib.spec_cycle_ref_mc.argtypes = common + [C.c_int32, C.c_void_p, C.c_float, C.c_float, C.c_uint64,
                                                C.c_int64, C.c_int64, C.POINTER(Out), C.c_int]
@@ -195,6 +198,31 @@ def spec_cycle_ref(base, target, A, W, x0, conf, temp, threshold, seed, noise=CH
             C.c_int64(request_offset), C.byref(out), nthreads)
     if rc != 0:
         raise ValueError(f"spec_cycle_ref rejected its arguments (code {rc})")
+    return arrays
+
+
+def spec_cycle_ref_lengths(base, target, A, W, x0, verify_len, temp, seed, noise=CHUNKED, request_offset=0,
+                           nthreads=0) -> dict:
+    """The oracle cycle with given verify lengths [B] (0..K; others mark the request invalid)
+    instead of the prefix cut."""
+    lib = load()
+    dt = _dtype_code(base)
+    B, K, V = base.shape
+    R = A.shape[1]
+    base, target, A, W = (np.ascontiguousarray(a) for a in (base, target, A, W))
+    L = np.ascontiguousarray(verify_len, dtype=np.int32).reshape(B)
+    temp = np.ascontiguousarray(temp, dtype=np.float32).reshape(B)
+    x0p = None
+    if x0 is not None:
+        x0 = np.ascontiguousarray(x0, dtype=np.int32).reshape(B)
+        x0p = x0.ctypes.data
+    d = Dims(B, K, V, R, dt, noise)
+    arrays, out = _alloc_out(B, K)
+    rc = lib.spec_cycle_ref_lengths(C.byref(d), base.ctypes.data, target.ctypes.data, A.ctypes.data, W.ctypes.data,
+                                    x0p, L.ctypes.data, temp.ctypes.data, C.c_uint64(seed),
+                                    C.c_int64(request_offset), C.byref(out), nthreads)
+    if rc != 0:
+        raise ValueError(f"spec_cycle_ref_lengths rejected its arguments (code {rc})")
     return arrays
 
 

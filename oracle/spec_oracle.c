@@ -298,6 +298,7 @@ typedef struct {
   int32_t x0;               /* -1 = no bias at position 0 */
   const float* conf;        /* [K] */
   float temp, threshold;
+  int32_t has_L, L_given;   /* has_L: the verify length is given (the scheduler's), not cut */
   uint64_t seed, gid;       /* gid = global request id used in the hash */
   target_row_fn target_row;
   const void* target_ctx;
@@ -337,8 +338,12 @@ static void cycle_one(const req_in* in, req_out* o, double* s_rows, double* tmp,
     return;
   }
 
-  /* 1. prefix cut */
-  const int32_t L = oracle_cut(in->conf, K, in->threshold);
+  /* 1. prefix cut, or the verify length a scheduler chose (outside [0, K]: a bad request) */
+  if (in->has_L && (in->L_given < 0 || in->L_given > K)) {
+    set_invalid(in, o);
+    return;
+  }
+  const int32_t L = in->has_L ? in->L_given : oracle_cut(in->conf, K, in->threshold);
   o->L = L;
 
   /* 2. semi-autoregressive draft: x_j ~ softmax((base_j + A[x_{j-1}] W) / T) */
@@ -446,6 +451,7 @@ typedef struct {
   const float* temp;        /* [n] */
   int64_t temp_stride;
   float threshold;
+  const int32_t* L_in;      /* [n] given verify lengths, or NULL: the prefix cut */
   uint64_t seed;
   int64_t request_offset;
   target_row_fn target_row;
@@ -477,7 +483,9 @@ static void run_driver(const driver_in* di, int64_t n, const oracle_out* out, in
       in.base_req = (const char*)di->base + (size_t)(b * di->base_req_stride) * K * V * elem;
       in.A = di->A; in.W = di->W;
       in.x0 = di->x0 ? di->x0[b * di->x0_stride] : -1;
-      in.conf = di->conf + b * di->conf_stride * K;
+      in.conf = di->conf ? di->conf + b * di->conf_stride * K : NULL;
+      in.has_L = di->L_in != NULL;
+      in.L_given = di->L_in ? di->L_in[b] : 0;
       in.temp = di->temp[b * di->temp_stride];
       in.threshold = di->threshold;
       in.seed = di->seed;
@@ -533,7 +541,26 @@ int spec_cycle_ref(const oracle_dims* d, const void* base_logits, const void* ta
   if (!base_logits || !target_logits || !A || !W || !conf || !temp || !out || !out->accepted_len || !out->tokens)
     return -1;
   array_ctx ctx = {target_logits, d->K, d->V, d->dtype};
-  driver_in di = {d, base_logits, 1, A, W, x0, 1, conf, 1, temp, 1, threshold, seed, request_offset,
+  driver_in di = {d, base_logits, 1, A, W, x0, 1, conf, 1, temp, 1, threshold, NULL, seed, request_offset,
+                  target_from_array, &ctx, 1};
+  run_driver(&di, d->B, out, nthreads);
+  return 0;
+}
+
+/* The cycle with verify lengths given per request (a scheduler's, for instance) instead of the
+ * prefix cut: verify_len [B] in 0..K (other values mark the request invalid).  Everything after
+ * the cut is the same cycle. */
+int spec_cycle_ref_lengths(const oracle_dims* d, const void* base_logits, const void* target_logits,
+                           const void* A, const void* W, const int32_t* x0, const int32_t* verify_len,
+                           const float* temp, uint64_t seed, int64_t request_offset, const oracle_out* out,
+                           int nthreads) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!base_logits || !target_logits || !A || !W || !verify_len || !temp || !out || !out->accepted_len ||
+      !out->tokens)
+    return -1;
+  array_ctx ctx = {target_logits, d->K, d->V, d->dtype};
+  driver_in di = {d, base_logits, 1, A, W, x0, 1, NULL, 1, temp, 1, 0.0f, verify_len, seed, request_offset,
                   target_from_array, &ctx, 1};
   run_driver(&di, d->B, out, nthreads);
   return 0;
@@ -551,7 +578,7 @@ int spec_cycle_ref_table(const oracle_dims* d, const void* base_logits, const vo
   if (!base_logits || !target_table || !A || !W || !conf || !temp || !out || !out->accepted_len || !out->tokens)
     return -1;
   table_ctx ctx = {target_table, d->K, d->V, d->dtype};
-  driver_in di = {d, base_logits, 1, A, W, x0, 1, conf, 1, temp, 1, threshold, seed, request_offset,
+  driver_in di = {d, base_logits, 1, A, W, x0, 1, conf, 1, temp, 1, threshold, NULL, seed, request_offset,
                   target_from_table, &ctx, 1};
   run_driver(&di, d->B, out, nthreads);
   return 0;
@@ -569,7 +596,7 @@ int spec_cycle_ref_mc(const oracle_dims* d, const void* base_logits, const void*
   if (!base_logits || !target_table || !A || !W || !conf || !out || !out->accepted_len || !out->tokens)
     return -1;
   table_ctx ctx = {target_table, d->K, d->V, d->dtype};
-  driver_in di = {d, base_logits, 0, A, W, &x0, 0, conf, 0, &temp, 0, threshold, seed, request_offset,
+  driver_in di = {d, base_logits, 0, A, W, &x0, 0, conf, 0, &temp, 0, threshold, NULL, seed, request_offset,
                   target_from_table, &ctx, 0};
   run_driver(&di, n_trials, out, nthreads);
   return 0;
