@@ -52,6 +52,10 @@ def _load():
                   C.c_void_p, C.c_size_t, C.c_void_p]
     lib.spec_cycle.restype = C.c_int
     lib.spec_cycle.argtypes = cycle_args
+    lib.spec_cycle_lengths.restype = C.c_int
+    lib.spec_cycle_lengths.argtypes = [C.POINTER(_Dims), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                       C.c_void_p, C.c_void_p, C.c_uint64, C.c_int64, C.c_void_p, C.c_void_p,
+                                       C.POINTER(_Diag), C.c_void_p, C.c_size_t, C.c_void_p]
     lib.spec_cycle_timed.restype = C.c_int
     lib.spec_cycle_timed.argtypes = cycle_args + [C.c_void_p, C.c_int]
     lib.spec_cycle_kernel_count.restype = C.c_int
@@ -254,3 +258,52 @@ def spec_schedule(conf, step_time, nbins: int = 4096, verify_len=None, out=None,
     if rc != 0:
         raise SpecError(f"spec_schedule failed: {spec_error_string(rc)} (code {rc})")
     return verify_len, out
+
+
+def spec_cycle_lengths(base_logits, target_logits, A, W, verify_len, temp, seed: int, x0=None,
+                       request_offset: int = 0, noise: int = CHUNKED, diag: bool = False, workspace=None,
+                       out=None, stream=None) -> dict:
+    """One speculation cycle with per-request verify lengths (verify_len [B] int32 device tensor,
+    e.g. from spec_schedule) in place of the prefix cut.  Returns what spec_cycle returns."""
+    import torch
+    B, K, V = base_logits.shape
+    R = A.shape[1]
+    dt = _dtype_code(base_logits)
+    _check(base_logits, "base_logits", (B, K, V))
+    _check(target_logits, "target_logits", (B, K + 1, V), base_logits.dtype)
+    _check(A, "A", (V, R), base_logits.dtype)
+    _check(W, "W", (V, R), base_logits.dtype)
+    _check(verify_len, "verify_len", (B,), torch.int32)
+    _check(temp, "temp", (B,), torch.float32)
+    if x0 is not None:
+        _check(x0, "x0", (B,), torch.int32)
+    dev = base_logits.device
+    lib = _load()
+    d = _Dims(B, K, V, R, dt, noise)
+    need = int(lib.spec_workspace_bytes(C.byref(d)))
+    if need == 0:
+        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
+    dg = None
+    if diag:
+        for k, shp, ty in (("verify_len", (B,), torch.int32), ("draft_tokens", (B, K), torch.int32),
+                           ("logq", (B, K), torch.float32), ("logp", (B, K), torch.float32)):
+            if k not in out:
+                out[k] = torch.empty(shp, dtype=ty, device=dev)
+        dg = _Diag(out["verify_len"].data_ptr(), out["draft_tokens"].data_ptr(), out["logq"].data_ptr(),
+                   out["logp"].data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib.spec_cycle_lengths(C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(),
+                                W.data_ptr(), x0.data_ptr() if x0 is not None else None, verify_len.data_ptr(),
+                                temp.data_ptr(), C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), C.c_int64(request_offset),
+                                out["accepted_len"].data_ptr(), out["tokens"].data_ptr(),
+                                C.byref(dg) if dg is not None else None, workspace.data_ptr(), workspace.numel(),
+                                C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_cycle_lengths failed: {spec_error_string(rc)} (code {rc})")
+    return out

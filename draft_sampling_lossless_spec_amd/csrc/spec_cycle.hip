@@ -62,6 +62,7 @@ struct Params {
   const int32_t* x0;
   const float* conf;
   const float* temp;
+  const int32_t* L_in;   // [B] given verify lengths (a scheduler's), or null: the prefix cut
   float threshold;
   uint64_t seed;
   int64_t req_off;
@@ -142,21 +143,30 @@ __global__ void k_init(Params p) {
   const int K = p.K;
   const float T = p.temp[b];
   const int x0 = p.x0 ? p.x0[b] : -1;
-  const bool valid = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V;
+  bool valid = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V;
   // prefix cut: keep position j while the fp64 running product of confidences is >= threshold.
   // The confidences are all loaded up front (in bounds whatever the cut), so the loop waits once.
-  float c[MAX_K];
-#pragma unroll
-  for (int j = 0; j < MAX_K; j++) c[j] = j < K ? p.conf[(size_t)b * K + j] : 0.0f;
-  double P = 1.0;
   int L = 0;
-  bool go = true;
+  if (p.L_in) {
+    // verify length chosen by a scheduler: outside 0..K marks the request invalid
+    L = p.L_in[b];
+    if (L < 0 || L > K) {
+      valid = false;
+      L = 0;
+    }
+  } else {
+    float c[MAX_K];
 #pragma unroll
-  for (int j = 0; j < MAX_K; j++) {
-    if (go && j < K) {
-      P *= (double)c[j];
-      go = P >= (double)p.threshold;   // NaN stops the cut
-      L = go ? j + 1 : L;
+    for (int j = 0; j < MAX_K; j++) c[j] = j < K ? p.conf[(size_t)b * K + j] : 0.0f;
+    double P = 1.0;
+    bool go = true;
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) {
+      if (go && j < K) {
+        P *= (double)c[j];
+        go = P >= (double)p.threshold;   // NaN stops the cut
+        L = go ? j + 1 : L;
+      }
     }
   }
   p.L[b] = L;
@@ -2153,13 +2163,14 @@ extern "C" const char* spec_error_string(int code) {
 extern "C" int spec_version(void) { return 100; }
 
 static int cycle_impl(const spec_dims* d, const void* base_logits, const void* target_logits, const void* A,
-                      const void* W, const int32_t* x0, const float* conf, const float* temp, float threshold,
-                      uint64_t seed, int64_t request_offset, int32_t* accepted_len, int32_t* tokens,
-                      const spec_diag* diag, void* workspace, size_t workspace_bytes, spec_stream_t stream,
-                      const Timing& tm) {
+                      const void* W, const int32_t* x0, const float* conf, const int32_t* L_in, const float* temp,
+                      float threshold, uint64_t seed, int64_t request_offset, int32_t* accepted_len,
+                      int32_t* tokens, const spec_diag* diag, void* workspace, size_t workspace_bytes,
+                      spec_stream_t stream, const Timing& tm) {
   if (!dims_ok(d)) return SPEC_E_INVAL;
   if (!dtype_ok(d)) return SPEC_E_DTYPE;
-  if (!base_logits || !target_logits || !A || !W || !conf || !temp || !accepted_len || !tokens) return SPEC_E_INVAL;
+  if (!base_logits || !target_logits || !A || !W || !(conf || L_in) || !temp || !accepted_len || !tokens)
+    return SPEC_E_INVAL;
   if ((((uintptr_t)A) | ((uintptr_t)W)) & 15) return SPEC_E_INVAL;
   const Layout l = layout(d);
   if (!workspace || workspace_bytes < l.total || (((uintptr_t)workspace) & 255)) return SPEC_E_WORKSPACE;
@@ -2181,6 +2192,7 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
   p.x0 = x0;
   p.conf = conf;
   p.temp = temp;
+  p.L_in = L_in;
   p.threshold = threshold;
   p.seed = seed;
   p.req_off = request_offset;
@@ -2226,7 +2238,18 @@ extern "C" int spec_cycle(const spec_dims* d, const void* base_logits, const voi
                           uint64_t seed, int64_t request_offset, int32_t* accepted_len, int32_t* tokens,
                           const spec_diag* diag, void* workspace, size_t workspace_bytes, spec_stream_t stream) {
   const Timing tm = {nullptr, 0};
-  return cycle_impl(d, base_logits, target_logits, A, W, x0, conf, temp, threshold, seed, request_offset,
+  return cycle_impl(d, base_logits, target_logits, A, W, x0, conf, nullptr, temp, threshold, seed, request_offset,
+                    accepted_len, tokens, diag, workspace, workspace_bytes, stream, tm);
+}
+
+extern "C" int spec_cycle_lengths(const spec_dims* d, const void* base_logits, const void* target_logits,
+                                  const void* A, const void* W, const int32_t* x0, const int32_t* verify_len,
+                                  const float* temp, uint64_t seed, int64_t request_offset, int32_t* accepted_len,
+                                  int32_t* tokens, const spec_diag* diag, void* workspace, size_t workspace_bytes,
+                                  spec_stream_t stream) {
+  if (!verify_len) return SPEC_E_INVAL;
+  const Timing tm = {nullptr, 0};
+  return cycle_impl(d, base_logits, target_logits, A, W, x0, nullptr, verify_len, temp, 0.0f, seed, request_offset,
                     accepted_len, tokens, diag, workspace, workspace_bytes, stream, tm);
 }
 
@@ -2243,7 +2266,7 @@ extern "C" int spec_cycle_timed(const spec_dims* d, const void* base_logits, con
   if (!dims_ok(d)) return SPEC_E_INVAL;
   if (!events || n_events < 2 * spec_cycle_kernel_count(d)) return SPEC_E_INVAL;
   const Timing tm = {(hipEvent_t*)events, n_events};
-  return cycle_impl(d, base_logits, target_logits, A, W, x0, conf, temp, threshold, seed, request_offset,
+  return cycle_impl(d, base_logits, target_logits, A, W, x0, conf, nullptr, temp, threshold, seed, request_offset,
                     accepted_len, tokens, diag, workspace, workspace_bytes, stream, tm);
 }
 

@@ -108,6 +108,22 @@ int spec_cycle(const spec_dims* d, const void* base_logits, const void* target_l
                size_t workspace_bytes, spec_stream_t stream);
 
 /*
+ * The same cycle with per-request verify lengths chosen by a scheduler (spec_schedule, for
+ * instance) in place of the static-threshold prefix cut: step 1 of the cycle takes
+ * L_b = verify_len[b] ("DSpark turns speculation into a scheduler", section "Confidence is a
+ * serving primitive": the scheduler, not a fixed confidence threshold, sets each request's
+ * verification length).  Every other step, argument and convention is spec_cycle's.
+ *   verify_len [B] int32 device  L_b in 0..K; any other value marks request b invalid
+ *                               (accepted_len = -1, tokens -1)
+ * There is no conf or threshold argument.  Returns SPEC_OK or a negative SPEC_E_* code.
+ */
+int spec_cycle_lengths(const spec_dims* d, const void* base_logits, const void* target_logits,
+                       const void* A, const void* W, const int32_t* x0, const int32_t* verify_len,
+                       const float* temp, uint64_t seed, int64_t request_offset, int32_t* accepted_len,
+                       int32_t* tokens, const spec_diag* diag, void* workspace, size_t workspace_bytes,
+                       spec_stream_t stream);
+
+/*
  * Profiling variant of spec_cycle for benchmarks: identical work and results, and every kernel
  * of the cycle is launched with a start/stop hipEvent_t pair attached to its own dispatch (no
  * extra queue packets).  Kernel i is: 0 = set-up and prefix cut; 1 + 3s = sweep of the Markov-biased

@@ -103,3 +103,13 @@ def test_schedule_host_checks_reject_before_any_gpu_call(lib):
     assert lib.spec_schedule(fake, 2, 4, fake, 0, fake, fake, None) == -1           # no bin
     assert lib.spec_schedule(fake, 2, 4, fake, 4097, fake, fake, None) == -1        # too many bins
     assert lib.spec_schedule(fake, 2, 4, None, 64, fake, fake, None) == -1
+
+
+def test_cycle_lengths_host_checks(lib):
+    from draft_sampling_lossless_spec_amd.binding import _Dims
+    d = _Dims(2, 4, 100, 16, 1, 1)
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    args = [fake] * 5 + [None, fake, C.c_uint64(1), C.c_int64(0), fake, fake, None, None, C.c_size_t(0), None]
+    assert lib.spec_cycle_lengths(C.byref(d), *args) == -1              # no verify_len
+    args[5] = fake
+    assert lib.spec_cycle_lengths(C.byref(d), *args) == -3              # no workspace

@@ -74,3 +74,63 @@ def test_load_response_on_gpu():
         _, out = gpu_schedule(conf, _curve(conf.size, 1e-3, t1), 4096)
         ns.append(int(out[1]))
     assert all(a >= b for a, b in zip(ns, ns[1:])) and ns[0] > ns[-1]
+
+
+# ---- the cycle with the scheduler's verify lengths ----
+from draft_sampling_lossless_spec_amd import workloads as wl  # noqa: E402
+from gpu_util import to_device  # noqa: E402
+from parity import Report, compare  # noqa: E402
+
+
+def gpu_cycle_lengths(w, L, noise, dev=None):
+    import torch
+    from draft_sampling_lossless_spec_amd import spec_cycle_lengths
+    d = dev or to_device(w)
+    Lt = L if hasattr(L, "is_cuda") else torch.from_numpy(np.ascontiguousarray(L, dtype=np.int32)).cuda()
+    out = spec_cycle_lengths(d["base"], d["target"], d["A"], d["W"], Lt, d["temp"], w.seed, x0=d["x0"], noise=noise,
+                             diag=True)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("noise", [oracle.FLAT, oracle.CHUNKED])
+def test_cycle_lengths_matches_oracle(noise):
+    print(f"cycle with given lengths noise={noise}", flush=True)
+    w = wl.generate(wl.small_config(B=24, K=6, V=2000, R=32, threshold=0.1))
+    rng = np.random.default_rng(17)
+    L = rng.integers(0, 7, 24).astype(np.int32)
+    L[3], L[7] = -1, 7                      # bad lengths mark the request invalid
+    o = oracle.spec_cycle_ref_lengths(w.base, w.target, w.A, w.W, w.x0, L, w.temp, w.seed, noise=noise)
+    g = gpu_cycle_lengths(w, L, noise)
+    rep = compare(o, g)
+    print(rep.summary(), flush=True)
+    assert not rep.failures, "\n".join(rep.failures[:10])
+    assert np.array_equal(g["verify_len"], o["verify_len"])
+
+
+@pytest.mark.parametrize("noise", [oracle.CHUNKED])
+def test_schedule_then_cycle_on_device(noise):
+    # the whole scheduled cycle on the device (scheduler -> cycle, no host round trip) against the
+    # oracle's scheduler -> the oracle's cycle, on the long-block workload (sampled requests)
+    import torch
+    from draft_sampling_lossless_spec_amd import spec_schedule
+    print("scheduled long-block cycle", flush=True)
+    w = wl.generate("longblock")
+    B, K = w.cfg.B, w.cfg.K
+    T = _curve(B * K, 0.02, 2e-6)
+    d = to_device(w)
+    Lg, out = spec_schedule(d["conf"], torch.from_numpy(T).cuda(), 4096)
+    g = gpu_cycle_lengths(w, Lg, noise, dev=d)
+    o_s = oracle.schedule_ref(w.conf.astype(np.float32), T, 4096)
+    assert np.array_equal(Lg.cpu().numpy(), o_s["verify_len"])
+    assert np.array_equal(g["verify_len"], o_s["verify_len"])
+    sample = sorted(set([0, B - 1] + list(np.random.default_rng(4).choice(B, size=10, replace=False))))
+    rep = Report()
+    for b in sample:
+        o = oracle.spec_cycle_ref_lengths(w.base[b:b + 1], w.target[b:b + 1], w.A, w.W, w.x0[b:b + 1],
+                                          o_s["verify_len"][b:b + 1], w.temp[b:b + 1], w.seed, noise=noise,
+                                          request_offset=b)
+        compare(o, {k: v[b:b + 1] for k, v in g.items()}, report=rep)
+    print(rep.summary(), flush=True)
+    assert not rep.failures, "\n".join(rep.failures[:10])
+    print(f"scheduled verify tokens {int(g['verify_len'].sum())}, accepted {int(g['accepted_len'].sum())}", flush=True)
