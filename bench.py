@@ -309,6 +309,35 @@ def bench_schedule(args):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # the scheduled cycle at moderate load: scheduler -> cycle with its verify lengths, all on the device
+    from draft_sampling_lossless_spec_amd import spec_cycle_lengths, spec_workspace_bytes
+
+    def t_(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    base, target, A, W, x0, temp = (t_(a) for a in (w.base, w.target, w.A, w.W, w.x0, w.temp))
+    ws = torch.empty(spec_workspace_bytes(B, K, w.cfg.V, w.cfg.R, w.cfg.dtype), dtype=torch.uint8, device="cuda")
+    cyc_out = {"accepted_len": torch.empty(B, dtype=torch.int32, device="cuda"),
+               "tokens": torch.empty((B, K + 1), dtype=torch.int32, device="cuda")}
+
+    def scheduled():
+        spec_schedule(conf, T, 4096, verify_len=Lb, out=ob)
+        spec_cycle_lengths(base, target, A, W, Lb, temp, w.seed, x0=x0, workspace=ws, out=cyc_out)
+
+    for _ in range(3):
+        scheduled()
+    torch.cuda.synchronize()
+    tsc = time.perf_counter()
+    for _ in range(10):
+        scheduled()
+    torch.cuda.synchronize()
+    us_cycle = (time.perf_counter() - tsc) / 10 * 1e6
+    n_sched = int(Lb.sum().item())
+    sched_cycle = {"load": "moderate", "verify_tokens": n_sched, "us_per_cycle": us_cycle,
+                   "verified_draft_tokens_per_s": n_sched / (us_cycle * 1e-6),
+                   "emitted_tokens_per_cycle": int((cyc_out["accepted_len"] + 1).sum().item())}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -327,6 +356,7 @@ def bench_schedule(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": us * 1e-3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
         "config": {"workload": w.cfg.name, "B": B, "K": K, "nbins": 4096, "loads": loads},
+        "scheduled_cycle": sched_cycle,
         "roofline": {"bound": "hbm", "achieved": byt / (us * 1e-6) / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": byt / (us * 1e-6) / HBM_PEAK, "traffic": None, "kernel": "k_schedule",
                      "note": "one workgroup over a few tens of KB: latency-bound, the HBM figure is for the record"},
