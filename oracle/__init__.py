@@ -91,6 +91,9 @@ def load(build_if_missing: bool = True) -> C.CDLL:
     lib.spec_calibration_error_ref.restype = C.c_double
     lib.spec_calibration_error_ref.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                                C.POINTER(C.c_int64)]
+    lib.spec_temperature_scaling_ref.restype = C.c_int
+    lib.spec_temperature_scaling_ref.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
+                                                 C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.spec_schedule_ref.restype = C.c_int
     lib.spec_schedule_ref.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]
     _lib = lib
@@ -319,3 +322,31 @@ def schedule_ref(conf, step_time, nbins=4096) -> dict:
         raise ValueError(f"spec_schedule_ref rejected its arguments (code {rc})")
     return {"verify_len": L, "threshold": float(out[0]), "n": int(out[1]), "expected_tokens": float(out[2]),
             "goodput": float(out[3])}
+
+
+# ----------------------------------------------------------------------------------------
+# sequential temperature scaling
+# ----------------------------------------------------------------------------------------
+def temperature_grid(steps_per_octave=12, lo_octaves=-2, hi_octaves=3) -> np.ndarray:
+    """ascending grid T = 2^(m / steps_per_octave), m from lo_octaves to hi_octaves octaves: it holds
+    T = 1 exactly and doubling T moves exactly steps_per_octave entries"""
+    m = np.arange(lo_octaves * steps_per_octave, hi_octaves * steps_per_octave + 1)
+    return np.exp2(m / steps_per_octave)
+
+
+def temperature_scaling_ref(z, verify_len, accepted_len, grid, nbins=10) -> dict:
+    """Left-to-right per-position temperatures of the confidence logits z [N,K] minimising the
+    calibration error of the cumulative prefix probability (definition in spec_oracle.c)."""
+    lib = load()
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    N, K = z.shape
+    L = np.ascontiguousarray(verify_len, dtype=np.int32).reshape(N)
+    a = np.ascontiguousarray(accepted_len, dtype=np.int32).reshape(N)
+    g = np.ascontiguousarray(grid, dtype=np.float64)
+    out = {k: np.empty(K, np.float64) for k in ("T", "ece_before", "ece_after")}
+    rc = lib.spec_temperature_scaling_ref(z.ctypes.data, L.ctypes.data, a.ctypes.data, N, K, g.ctypes.data, len(g),
+                                          int(nbins), out["T"].ctypes.data, out["ece_before"].ctypes.data,
+                                          out["ece_after"].ctypes.data)
+    if rc != 0:
+        raise ValueError(f"spec_temperature_scaling_ref rejected its arguments (code {rc})")
+    return out

@@ -811,3 +811,95 @@ int spec_schedule_ref(const float* conf, int32_t B, int32_t K, const double* ste
   free(P);
   return 0;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * Sequential temperature scaling of the confidence head.
+ *
+ * Raw confidences tend to be overconfident; because prefix acceptance is a cumulative product,
+ * the calibration runs left to right on held-out data: with the temperatures of the earlier
+ * positions fixed, the temperature of the next position is the one that minimises the calibration
+ * error of the cumulative prefix probability ("DSpark turns speculation into a scheduler",
+ * section "Confidence is a serving primitive"; "The Speed Claim...", section "The Real Innovation":
+ * a post-hoc step that brings the expected calibration error from 3-8 % to about 1 %).
+ *
+ * Reading written out here:
+ *   z [N, K]: the head's raw logits, c_{n,k}(T) = 1 / (1 + exp(-z_{n,k} / T));
+ *   pairs of position k: sequences n with k < verify_len[n] and accepted_len[n] >= 0; prediction
+ *     P_{n,k} = prod_{i<=k} c_{n,i}(T_i) (fp64), outcome 1 if k < accepted_len[n];
+ *   ECE_k(T) over those pairs with nbins equal-width bins (the calibration error defined above,
+ *     restricted to position k);
+ *   T_k = the grid value with the smallest ECE_k (ties to the earlier grid entry), grid ascending;
+ *   out: T [K], ece_before [K] (all T = 1), ece_after [K] (fitted).
+ * --------------------------------------------------------------------------------------- */
+static double ece_of(const double* P, const int32_t* y, int64_t n, int32_t nbins, double* sp, double* sy,
+                     int64_t* cnt) {
+  for (int32_t m = 0; m < nbins; m++) {
+    sp[m] = 0.0;
+    sy[m] = 0.0;
+    cnt[m] = 0;
+  }
+  for (int64_t i = 0; i < n; i++) {
+    int64_t m = (int64_t)floor(P[i] * nbins);
+    if (m < 0) m = 0;
+    if (m > nbins - 1) m = nbins - 1;
+    sp[m] += P[i];
+    sy[m] += (double)y[i];
+    cnt[m] += 1;
+  }
+  double e = 0.0;
+  for (int32_t m = 0; m < nbins; m++)
+    if (cnt[m] > 0) e += ((double)cnt[m] / (double)n) * fabs(sp[m] / cnt[m] - sy[m] / cnt[m]);
+  return n > 0 ? e : 0.0;
+}
+
+int spec_temperature_scaling_ref(const float* z, const int32_t* verify_len, const int32_t* accepted_len,
+                                 int32_t N, int32_t K, const double* grid, int32_t G, int32_t nbins, double* T,
+                                 double* ece_before, double* ece_after) {
+  if (!z || !verify_len || !accepted_len || !grid || !T || N < 1 || K < 1 || G < 1 || nbins < 1) return -1;
+  double* run = (double*)malloc(sizeof(double) * (size_t)N);      /* fitted product through k - 1 */
+  double* run1 = (double*)malloc(sizeof(double) * (size_t)N);     /* product with every T = 1 */
+  double* P = (double*)malloc(sizeof(double) * (size_t)N);
+  int32_t* y = (int32_t*)malloc(sizeof(int32_t) * (size_t)N);
+  int64_t* idx = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+  double* sp = (double*)malloc(sizeof(double) * (size_t)nbins);
+  double* sy = (double*)malloc(sizeof(double) * (size_t)nbins);
+  int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * (size_t)nbins);
+  for (int32_t n = 0; n < N; n++) run[n] = run1[n] = 1.0;
+  for (int32_t k = 0; k < K; k++) {
+    int64_t m = 0;
+    for (int32_t n = 0; n < N; n++)
+      if (accepted_len[n] >= 0 && k < verify_len[n]) {
+        idx[m] = n;
+        y[m] = (k < accepted_len[n]) ? 1 : 0;
+        m++;
+      }
+    /* before: every temperature 1 */
+    for (int64_t i = 0; i < m; i++) {
+      const double zz = (double)z[(size_t)idx[i] * K + k];
+      P[i] = run1[idx[i]] * (1.0 / (1.0 + exp(-zz)));
+    }
+    if (ece_before) ece_before[k] = ece_of(P, y, m, nbins, sp, sy, cnt);
+    int32_t best = 0;
+    double best_e = INFINITY;
+    for (int32_t g = 0; g < G; g++) {
+      for (int64_t i = 0; i < m; i++) {
+        const double zz = (double)z[(size_t)idx[i] * K + k];
+        P[i] = run[idx[i]] * (1.0 / (1.0 + exp(-zz / grid[g])));
+      }
+      const double e = ece_of(P, y, m, nbins, sp, sy, cnt);
+      if (e < best_e) {
+        best_e = e;
+        best = g;
+      }
+    }
+    T[k] = grid[best];
+    if (ece_after) ece_after[k] = best_e;
+    for (int32_t n = 0; n < N; n++) {
+      const double zz = (double)z[(size_t)n * K + k];
+      run[n] *= 1.0 / (1.0 + exp(-zz / grid[best]));
+      run1[n] *= 1.0 / (1.0 + exp(-zz));
+    }
+  }
+  free(run); free(run1); free(P); free(y); free(idx); free(sp); free(sy); free(cnt);
+  return 0;
+}
