@@ -11,5 +11,5 @@ from .binding import (  # noqa: F401
     BF16, CHUNKED, FLAT, FP32, SpecError, lib_path, spec_accept_stats, spec_calibration_error, spec_cycle,
     spec_cycle_lengths,
     spec_cycle_kernel_count, spec_cycle_timed, spec_error_string, spec_schedule, spec_stats_workspace_bytes,
-    spec_version, spec_workspace_bytes,
+    spec_temperature_scaling, spec_version, spec_workspace_bytes,
 )

@@ -64,6 +64,12 @@ def _load():
     lib.spec_stats_workspace_bytes.argtypes = [C.POINTER(_Dims)]
     lib.spec_accept_stats.restype = C.c_int
     lib.spec_accept_stats.argtypes = [C.POINTER(_Dims)] + [C.c_void_p] * 10 + [C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.spec_temperature_scaling_workspace_bytes.restype = C.c_size_t
+    lib.spec_temperature_scaling_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+    lib.spec_temperature_scaling.restype = C.c_int
+    lib.spec_temperature_scaling.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
+                                             C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_size_t, C.c_void_p]
     lib.spec_schedule.restype = C.c_int
     lib.spec_schedule.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                   C.c_void_p]
@@ -306,4 +312,34 @@ def spec_cycle_lengths(base_logits, target_logits, A, W, verify_len, temp, seed:
                                 C.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise SpecError(f"spec_cycle_lengths failed: {spec_error_string(rc)} (code {rc})")
+    return out
+
+
+def spec_temperature_scaling(z, verify_len, accepted_len, grid, nbins: int = 10, workspace=None, stream=None) -> dict:
+    """Sequential temperature scaling: z [N, K] fp32 logits, verify_len / accepted_len [N] int32,
+    grid [G] fp64 ascending temperatures (device tensors).  Returns device tensors 'T',
+    'ece_before', 'ece_after' ([K] fp64).  Asynchronous."""
+    import torch
+    N, K = z.shape
+    _check(z, "z", (N, K), torch.float32)
+    _check(verify_len, "verify_len", (N,), torch.int32)
+    _check(accepted_len, "accepted_len", (N,), torch.int32)
+    G = grid.shape[0]
+    _check(grid, "grid", (G,), torch.float64)
+    dev = z.device
+    lib = _load()
+    need = int(lib.spec_temperature_scaling_workspace_bytes(N, G))
+    if need == 0:
+        raise SpecError(f"unsupported sizes N={N} G={G}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = {k: torch.empty(K, dtype=torch.float64, device=dev) for k in ("T", "ece_before", "ece_after")}
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib.spec_temperature_scaling(z.data_ptr(), verify_len.data_ptr(), accepted_len.data_ptr(), N, K,
+                                      grid.data_ptr(), G, int(nbins), out["T"].data_ptr(),
+                                      out["ece_before"].data_ptr(), out["ece_after"].data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_temperature_scaling failed: {spec_error_string(rc)} (code {rc})")
     return out

@@ -2018,6 +2018,93 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
   }
 }
 
+// ==========================================================================================
+// Sequential temperature scaling of the confidence head ("DSpark turns speculation into a
+// scheduler", section "Confidence is a serving primitive": left to right, each position's
+// temperature minimises the calibration error of the cumulative prefix probability with the
+// earlier positions fixed; "The Speed Claim...", section "The Real Innovation").  Per position k:
+//   k_sts_eval  one workgroup per grid temperature (and one more for unit temperatures): the
+//               calibration error of prod_{i<k} c_i(T_i) * sigmoid(z_k / T) over the sequences that
+//               verify position k, fp64 bin sums in LDS
+//   k_sts_pick  the smallest error (ties to the earlier grid entry), then every sequence's running
+//               products advanced with the chosen and with the unit temperature
+// ==========================================================================================
+constexpr int STS_NT = 256;
+constexpr int STS_MAX_BINS = 64;
+constexpr int STS_MAX_GRID = 1024;
+constexpr int STS_MAX_K = 256;
+
+__device__ __forceinline__ double sigmoid64(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+__global__ __launch_bounds__(STS_NT) void k_sts_init(int N, double* run, double* run1) {
+  for (int n = blockIdx.x * STS_NT + threadIdx.x; n < N; n += gridDim.x * STS_NT) {
+    run[n] = 1.0;
+    run1[n] = 1.0;
+  }
+}
+
+__global__ __launch_bounds__(STS_NT) void k_sts_eval(const float* z, const int32_t* verify_len,
+                                                   const int32_t* accepted_len, int N, int K, int k,
+                                                   const double* grid, int G, int nbins, const double* run,
+                                                   const double* run1, double* ece) {
+  __shared__ double sp[STS_MAX_BINS];
+  __shared__ double sy[STS_MAX_BINS];
+  __shared__ int cnt[STS_MAX_BINS];
+  const int tid = threadIdx.x, g = blockIdx.x;
+  for (int m = tid; m < nbins; m += STS_NT) {
+    sp[m] = 0.0;
+    sy[m] = 0.0;
+    cnt[m] = 0;
+  }
+  __syncthreads();
+  const bool unit = g == G;
+  const double T = unit ? 1.0 : grid[g];
+  const double* r = unit ? run1 : run;
+  for (int n = tid; n < N; n += STS_NT) {
+    const int a = accepted_len[n];
+    if (a < 0 || k >= verify_len[n]) continue;
+    const double P = r[n] * sigmoid64((double)z[(size_t)n * K + k] / T);
+    int m = (int)floor(P * nbins);
+    m = m < 0 ? 0 : (m > nbins - 1 ? nbins - 1 : m);
+    atomicAdd(&sp[m], P);
+    atomicAdd(&sy[m], k < a ? 1.0 : 0.0);
+    atomicAdd(&cnt[m], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long long tot = 0;
+    for (int m = 0; m < nbins; m++) tot += cnt[m];
+    double e = 0.0;
+    for (int m = 0; m < nbins; m++)
+      if (cnt[m] > 0) e += ((double)cnt[m] / (double)tot) * fabs(sp[m] / cnt[m] - sy[m] / cnt[m]);
+    ece[g] = tot > 0 ? e : 0.0;
+  }
+}
+
+__global__ __launch_bounds__(STS_NT) void k_sts_pick(const float* z, int N, int K, int k, const double* grid, int G,
+                                                   double* run, double* run1, const double* ece, double* T,
+                                                   double* ece_before, double* ece_after) {
+  __shared__ int best;
+  if (threadIdx.x == 0) {
+    int b = 0;
+    for (int g = 1; g < G; g++)
+      if (ece[g] < ece[b]) b = g;
+    best = b;
+    if (blockIdx.x == 0) {
+      T[k] = grid[b];
+      if (ece_after) ece_after[k] = ece[b];
+      if (ece_before) ece_before[k] = ece[G];
+    }
+  }
+  __syncthreads();
+  const double Tb = grid[best];
+  for (int n = blockIdx.x * STS_NT + threadIdx.x; n < N; n += gridDim.x * STS_NT) {
+    const double zz = (double)z[(size_t)n * K + k];
+    run[n] *= sigmoid64(zz / Tb);
+    run1[n] *= sigmoid64(zz);
+  }
+}
+
 struct Layout {
   size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
       off_pbias, off_pbias2, off_pplain, off_konst, total;
@@ -2389,6 +2476,41 @@ extern "C" int spec_schedule(const float* conf, int32_t B, int32_t K, const doub
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_schedule, dim3(1), dim3(SCHED_NT), 0, (hipStream_t)stream, conf, B, K, step_time, nbins,
                      verify_len, out);
+  if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
+}
+
+extern "C" size_t spec_temperature_scaling_workspace_bytes(int32_t N, int32_t G) {
+  if (N < 1 || N > (1 << 24) || G < 1 || G > STS_MAX_GRID) return 0;
+  return align256(8 * (size_t)N) * 2 + align256(8 * ((size_t)G + 1));
+}
+
+extern "C" int spec_temperature_scaling(const float* z, const int32_t* verify_len, const int32_t* accepted_len,
+                                        int32_t N, int32_t K, const double* grid, int32_t G, int32_t nbins,
+                                        double* T, double* ece_before, double* ece_after, void* workspace,
+                                        size_t workspace_bytes, spec_stream_t stream) {
+  if (!z || !verify_len || !accepted_len || !grid || !T) return SPEC_E_INVAL;
+  if (N < 1 || N > (1 << 24) || K < 1 || K > STS_MAX_K || G < 1 || G > STS_MAX_GRID || nbins < 1 ||
+      nbins > STS_MAX_BINS)
+    return SPEC_E_INVAL;
+  const size_t need = spec_temperature_scaling_workspace_bytes(N, G);
+  if (!workspace || workspace_bytes < need || (((uintptr_t)workspace) & 255)) return SPEC_E_WORKSPACE;
+  const int ac = arch_ok();
+  if (ac != SPEC_OK) return ac;
+  char* ws = (char*)workspace;
+  double* run = (double*)ws;
+  double* run1 = (double*)(ws + align256(8 * (size_t)N));
+  double* ece = (double*)(ws + 2 * align256(8 * (size_t)N));
+  hipStream_t st = (hipStream_t)stream;
+  const int blocks = min((N + STS_NT - 1) / STS_NT, 4 * cu_count());
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_sts_init, dim3(blocks), dim3(STS_NT), 0, st, N, run, run1);
+  for (int k = 0; k < K; k++) {
+    hipLaunchKernelGGL(k_sts_eval, dim3(G + 1), dim3(STS_NT), 0, st, z, verify_len, accepted_len, N, K, k, grid, G,
+                       nbins, run, run1, ece);
+    hipLaunchKernelGGL(k_sts_pick, dim3(blocks), dim3(STS_NT), 0, st, z, N, K, k, grid, G, run, run1, ece, T,
+                       ece_before, ece_after);
+  }
   if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
   return SPEC_OK;
 }

@@ -215,6 +215,35 @@ int spec_calibration_error(const float* conf, const int32_t* verify_len, const i
 int spec_schedule(const float* conf, int32_t B, int32_t K, const double* step_time, int32_t nbins,
                   int32_t* verify_len, double* out, spec_stream_t stream);
 
+/* Bytes of device workspace spec_temperature_scaling needs for N sequences and G grid entries
+ * (0 if N is outside 1..2^24 or G outside 1..1024). */
+size_t spec_temperature_scaling_workspace_bytes(int32_t N, int32_t G);
+
+/*
+ * Sequential temperature scaling of the confidence head: per-position temperatures fitted left to
+ * right on held-out sequences so that the cumulative prefix probability is calibrated ("DSpark
+ * turns speculation into a scheduler", section "Confidence is a serving primitive": with the
+ * earlier positions fixed, the next position's temperature minimises the calibration error of the
+ * cumulative prefix probability; "The Speed Claim...", section "The Real Innovation").
+ *   z            [N, K] fp32 device  the head's raw logits, c_{n,k}(T) = 1 / (1 + exp(-z_{n,k} / T))
+ *   verify_len   [N] int32 device    verified positions of each held-out sequence
+ *   accepted_len [N] int32 device    accepted drafts (-1: sequence left out); the prefix through k
+ *                                    survived iff k < accepted_len
+ *   grid         [G] fp64 device     candidate temperatures, ascending, G in 1..1024
+ *   nbins        bins of the calibration error, 1..64
+ *   T            [K] fp64 device out fitted temperatures: T_k is the grid value with the smallest
+ *                                    calibration error of prod_{i<=k} c_{n,i}(T_i) against survival
+ *                                    over the sequences with k < verify_len (ties: earlier entry)
+ *   ece_before, ece_after [K] fp64 device out (may be NULL): that error with every T = 1, and fitted
+ *   workspace    spec_temperature_scaling_workspace_bytes(N, G) bytes, 256-byte aligned
+ * Asynchronous on `stream` (2 K + 1 kernels).  Returns SPEC_OK, SPEC_E_INVAL (NULL pointer, N outside
+ * 1..2^24, K outside 1..256, G or nbins out of range) or SPEC_E_WORKSPACE.
+ */
+int spec_temperature_scaling(const float* z, const int32_t* verify_len, const int32_t* accepted_len,
+                             int32_t N, int32_t K, const double* grid, int32_t G, int32_t nbins, double* T,
+                             double* ece_before, double* ece_after, void* workspace, size_t workspace_bytes,
+                             spec_stream_t stream);
+
 /* Static description of an error code (never NULL). */
 const char* spec_error_string(int code);
 

@@ -113,3 +113,19 @@ def test_cycle_lengths_host_checks(lib):
     assert lib.spec_cycle_lengths(C.byref(d), *args) == -1              # no verify_len
     args[5] = fake
     assert lib.spec_cycle_lengths(C.byref(d), *args) == -3              # no workspace
+
+
+def test_temperature_scaling_host_checks(lib):
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    assert lib.spec_temperature_scaling_workspace_bytes(1000, 61) > 0
+    assert lib.spec_temperature_scaling_workspace_bytes(0, 61) == 0
+    assert lib.spec_temperature_scaling_workspace_bytes(1000, 2000) == 0
+    good = [fake, fake, fake, 1000, 4, fake, 61, 10, fake, None, None]
+    assert lib.spec_temperature_scaling(*good, None, C.c_size_t(0), None) == -3      # no workspace
+    assert lib.spec_temperature_scaling(None, *good[1:], fake, C.c_size_t(1 << 20), None) == -1
+    bad = list(good)
+    bad[7] = 65                                                         # too many bins
+    assert lib.spec_temperature_scaling(*bad, fake, C.c_size_t(1 << 20), None) == -1
+    bad = list(good)
+    bad[4] = 300                                                        # K > 256
+    assert lib.spec_temperature_scaling(*bad, fake, C.c_size_t(1 << 20), None) == -1
