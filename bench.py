@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--schedule", action="store_true",
                     help="measure the prefix scheduler on the workload's confidences against a synthetic target "
                          "step-time curve at several loads; prints its own JSON line")
+    ap.add_argument("--sts", action="store_true",
+                    help="measure sequential temperature scaling on synthetic held-out confidences (an "
+                         "overconfident head); prints its own JSON line")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -102,6 +105,8 @@ def main():
         return bench_stats(args)
     if args.schedule:
         return bench_schedule(args)
+    if args.sts:
+        return bench_sts(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
               "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -259,6 +264,62 @@ def main():
                      "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"] / (K + 1)},
         "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_sts(args):
+    """Sequential temperature scaling of a synthetic overconfident head: N = 100000 held-out
+    sequences of K = 16 positions (true logits N(1.5, 1), raw logits 2x, survival drawn from the
+    true probabilities, random verified lengths), 61-entry octave grid, 10 bins; timed with events
+    on its stream, the oracle beside it."""
+    import torch
+    from draft_sampling_lossless_spec_amd import spec_temperature_scaling
+    N, K = 100000, 16
+    rng = np.random.default_rng(1)
+    zt = rng.normal(1.5, 1.0, (N, K))
+    surv = rng.random((N, K)) < 1 / (1 + np.exp(-zt))
+    a = np.where(surv.all(axis=1), K, surv.argmin(axis=1)).astype(np.int32)
+    L = rng.integers(1, K + 1, N).astype(np.int32)
+    a = np.minimum(a, L).astype(np.int32)
+    z = (2.0 * zt).astype(np.float32)
+    grid = np.exp2(np.arange(-24, 37) / 12)   # 2^(m/12): a quarter to eight, T = 1 included
+    c = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    zd, Ld, ad, gd = c(z), c(L), c(a), c(grid)
+    for _ in range(args.warmup):
+        out = spec_temperature_scaling(zd, Ld, ad, gd, 10)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        out = spec_temperature_scaling(zd, Ld, ad, gd, 10)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        tc = time.perf_counter()
+        oracle.temperature_scaling_ref(z, L, a, grid, 10)
+        dt = time.perf_counter() - tc
+        cpu = {"value": 1.0 / dt, "unit": "fits/s", "cores": 1, "kind": "oracle",
+               "sample": f"the same fit ({dt:.1f} s wall, fp64 C, one thread)"}
+    pairs = int(np.minimum(L, K).sum())
+    byt = 2 * (len(grid) + 1) * (4 * N * K + 8 * N + 8 * N)   # per evaluation: z column, lengths, running product
+    line = {
+        "metric": "sequential temperature scaling: fits/s", "value": 1e3 / ms, "unit": "fits/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "held-out confidences, overconfident head x2", "N": N, "K": K, "grid": len(grid),
+                   "nbins": 10, "pairs": pairs,
+                   "T": [round(float(t), 3) for t in out["T"].cpu().numpy()],
+                   "ece_before": float(out["ece_before"].mean().item()),
+                   "ece_after": float(out["ece_after"].mean().item())},
+        "roofline": {"bound": "alu", "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None,
+                     "kernel": "k_sts_eval",
+                     "note": "fp64 sigmoid per (sequence, grid entry, position); byte count for the record: "
+                             f"{byt / 1e9:.2f} GB of L2-resident reads per fit"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

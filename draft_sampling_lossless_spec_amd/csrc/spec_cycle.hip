@@ -2023,9 +2023,10 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
 // scheduler", section "Confidence is a serving primitive": left to right, each position's
 // temperature minimises the calibration error of the cumulative prefix probability with the
 // earlier positions fixed; "The Speed Claim...", section "The Real Innovation").  Per position k:
-//   k_sts_eval  one workgroup per grid temperature (and one more for unit temperatures): the
-//               calibration error of prod_{i<k} c_i(T_i) * sigmoid(z_k / T) over the sequences that
+//   k_sts_eval  workgroups per (grid temperature or unit temperatures, slice of sequences): bin sums for
+//               the calibration error of prod_{i<k} c_i(T_i) * sigmoid(z_k / T) over the sequences that
 //               verify position k, fp64 bin sums in LDS
+//   k_sts_reduce the error of every grid entry from its slices' bin sums
 //   k_sts_pick  the smallest error (ties to the earlier grid entry), then every sequence's running
 //               products advanced with the chosen and with the unit temperature
 // ==========================================================================================
@@ -2043,14 +2044,15 @@ __global__ __launch_bounds__(STS_NT) void k_sts_init(int N, double* run, double*
   }
 }
 
+// bin sums of grid entry g = blockIdx.x over slice blockIdx.y of the sequences -> part[g][slice][bin]
 __global__ __launch_bounds__(STS_NT) void k_sts_eval(const float* z, const int32_t* verify_len,
                                                    const int32_t* accepted_len, int N, int K, int k,
                                                    const double* grid, int G, int nbins, const double* run,
-                                                   const double* run1, double* ece) {
+                                                   const double* run1, double* part) {
   __shared__ double sp[STS_MAX_BINS];
   __shared__ double sy[STS_MAX_BINS];
   __shared__ int cnt[STS_MAX_BINS];
-  const int tid = threadIdx.x, g = blockIdx.x;
+  const int tid = threadIdx.x, g = blockIdx.x, sl = blockIdx.y, ns = gridDim.y;
   for (int m = tid; m < nbins; m += STS_NT) {
     sp[m] = 0.0;
     sy[m] = 0.0;
@@ -2060,7 +2062,8 @@ __global__ __launch_bounds__(STS_NT) void k_sts_eval(const float* z, const int32
   const bool unit = g == G;
   const double T = unit ? 1.0 : grid[g];
   const double* r = unit ? run1 : run;
-  for (int n = tid; n < N; n += STS_NT) {
+  const int n0 = (int)((long long)N * sl / ns), n1 = (int)((long long)N * (sl + 1) / ns);
+  for (int n = n0 + tid; n < n1; n += STS_NT) {
     const int a = accepted_len[n];
     if (a < 0 || k >= verify_len[n]) continue;
     const double P = r[n] * sigmoid64((double)z[(size_t)n * K + k] / T);
@@ -2071,14 +2074,33 @@ __global__ __launch_bounds__(STS_NT) void k_sts_eval(const float* z, const int32
     atomicAdd(&cnt[m], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    long long tot = 0;
-    for (int m = 0; m < nbins; m++) tot += cnt[m];
-    double e = 0.0;
-    for (int m = 0; m < nbins; m++)
-      if (cnt[m] > 0) e += ((double)cnt[m] / (double)tot) * fabs(sp[m] / cnt[m] - sy[m] / cnt[m]);
-    ece[g] = tot > 0 ? e : 0.0;
+  double* o = part + ((size_t)g * ns + sl) * 3 * STS_MAX_BINS;
+  for (int m = tid; m < nbins; m += STS_NT) {
+    o[m] = sp[m];
+    o[STS_MAX_BINS + m] = sy[m];
+    o[2 * STS_MAX_BINS + m] = (double)cnt[m];
   }
+}
+
+// calibration error of every grid entry from its slices' bin sums (one thread per entry)
+__global__ __launch_bounds__(STS_NT) void k_sts_reduce(int G, int ns, int nbins, const double* part, double* ece) {
+  const int g = blockIdx.x * STS_NT + threadIdx.x;
+  if (g > G) return;
+  double sp[STS_MAX_BINS], sy[STS_MAX_BINS], cn[STS_MAX_BINS];
+  for (int m = 0; m < nbins; m++) sp[m] = sy[m] = cn[m] = 0.0;
+  for (int sl = 0; sl < ns; sl++) {
+    const double* o = part + ((size_t)g * ns + sl) * 3 * STS_MAX_BINS;
+    for (int m = 0; m < nbins; m++) {
+      sp[m] += o[m];
+      sy[m] += o[STS_MAX_BINS + m];
+      cn[m] += o[2 * STS_MAX_BINS + m];
+    }
+  }
+  double tot = 0.0, e = 0.0;
+  for (int m = 0; m < nbins; m++) tot += cn[m];
+  for (int m = 0; m < nbins; m++)
+    if (cn[m] > 0.0) e += (cn[m] / tot) * fabs(sp[m] / cn[m] - sy[m] / cn[m]);
+  ece[g] = tot > 0.0 ? e : 0.0;
 }
 
 __global__ __launch_bounds__(STS_NT) void k_sts_pick(const float* z, int N, int K, int k, const double* grid, int G,
@@ -2480,9 +2502,12 @@ extern "C" int spec_schedule(const float* conf, int32_t B, int32_t K, const doub
   return SPEC_OK;
 }
 
+constexpr int STS_SLICES = 8;   // sequence slices per grid entry: (G + 1) x 8 workgroups fill the chip
+
 extern "C" size_t spec_temperature_scaling_workspace_bytes(int32_t N, int32_t G) {
   if (N < 1 || N > (1 << 24) || G < 1 || G > STS_MAX_GRID) return 0;
-  return align256(8 * (size_t)N) * 2 + align256(8 * ((size_t)G + 1));
+  return align256(8 * (size_t)N) * 2 + align256(8 * ((size_t)G + 1)) +
+         align256(8 * (size_t)(G + 1) * STS_SLICES * 3 * STS_MAX_BINS);
 }
 
 extern "C" int spec_temperature_scaling(const float* z, const int32_t* verify_len, const int32_t* accepted_len,
@@ -2501,13 +2526,16 @@ extern "C" int spec_temperature_scaling(const float* z, const int32_t* verify_le
   double* run = (double*)ws;
   double* run1 = (double*)(ws + align256(8 * (size_t)N));
   double* ece = (double*)(ws + 2 * align256(8 * (size_t)N));
+  double* part = (double*)(ws + 2 * align256(8 * (size_t)N) + align256(8 * ((size_t)G + 1)));
   hipStream_t st = (hipStream_t)stream;
   const int blocks = min((N + STS_NT - 1) / STS_NT, 4 * cu_count());
   (void)hipGetLastError();
   hipLaunchKernelGGL(k_sts_init, dim3(blocks), dim3(STS_NT), 0, st, N, run, run1);
   for (int k = 0; k < K; k++) {
-    hipLaunchKernelGGL(k_sts_eval, dim3(G + 1), dim3(STS_NT), 0, st, z, verify_len, accepted_len, N, K, k, grid, G,
-                       nbins, run, run1, ece);
+    hipLaunchKernelGGL(k_sts_eval, dim3(G + 1, STS_SLICES), dim3(STS_NT), 0, st, z, verify_len, accepted_len, N, K,
+                       k, grid, G, nbins, run, run1, part);
+    hipLaunchKernelGGL(k_sts_reduce, dim3((G + 1 + STS_NT - 1) / STS_NT), dim3(STS_NT), 0, st, G, STS_SLICES, nbins,
+                       part, ece);
     hipLaunchKernelGGL(k_sts_pick, dim3(blocks), dim3(STS_NT), 0, st, z, N, K, k, grid, G, run, run1, ece, T,
                        ece_before, ece_after);
   }

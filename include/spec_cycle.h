@@ -236,7 +236,7 @@ size_t spec_temperature_scaling_workspace_bytes(int32_t N, int32_t G);
  *                                    over the sequences with k < verify_len (ties: earlier entry)
  *   ece_before, ece_after [K] fp64 device out (may be NULL): that error with every T = 1, and fitted
  *   workspace    spec_temperature_scaling_workspace_bytes(N, G) bytes, 256-byte aligned
- * Asynchronous on `stream` (2 K + 1 kernels).  Returns SPEC_OK, SPEC_E_INVAL (NULL pointer, N outside
+ * Asynchronous on `stream` (3 K + 1 kernels).  Returns SPEC_OK, SPEC_E_INVAL (NULL pointer, N outside
  * 1..2^24, K outside 1..256, G or nbins out of range) or SPEC_E_WORKSPACE.
  */
 int spec_temperature_scaling(const float* z, const int32_t* verify_len, const int32_t* accepted_len,
