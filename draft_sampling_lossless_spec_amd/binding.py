@@ -70,6 +70,8 @@ def _load():
     lib.spec_temperature_scaling.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p,
                                              C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                              C.c_size_t, C.c_void_p]
+    lib.spec_advance.restype = C.c_int
+    lib.spec_advance.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.spec_schedule.restype = C.c_int
     lib.spec_schedule.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                   C.c_void_p]
@@ -343,3 +345,21 @@ def spec_temperature_scaling(z, verify_len, accepted_len, grid, nbins: int = 10,
     if rc != 0:
         raise SpecError(f"spec_temperature_scaling failed: {spec_error_string(rc)} (code {rc})")
     return out
+
+
+def spec_advance(tokens, accepted_len, x0, emitted=None, stream=None):
+    """Next cycle's context in place: x0 [B] int32 <- the last token each valid request emitted;
+    emitted [B] int64 (optional) += accepted_len + 1.  Asynchronous."""
+    import torch
+    B, K1 = tokens.shape
+    _check(tokens, "tokens", (B, K1), torch.int32)
+    _check(accepted_len, "accepted_len", (B,), torch.int32)
+    _check(x0, "x0", (B,), torch.int32)
+    if emitted is not None:
+        _check(emitted, "emitted", (B,), torch.int64)
+    if stream is None:
+        stream = torch.cuda.current_stream(tokens.device)
+    rc = _load().spec_advance(tokens.data_ptr(), accepted_len.data_ptr(), B, K1 - 1, x0.data_ptr(),
+                              emitted.data_ptr() if emitted is not None else None, C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_advance failed: {spec_error_string(rc)} (code {rc})")

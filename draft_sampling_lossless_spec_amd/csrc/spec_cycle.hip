@@ -2127,6 +2127,22 @@ __global__ __launch_bounds__(STS_NT) void k_sts_pick(const float* z, int N, int 
   }
 }
 
+// ==========================================================================================
+// Decode loop glue: the context of the next cycle.  The cycle emits tokens[b, 0..a_b] (the
+// accepted drafts, then the correction or bonus), so the next cycle's Markov bias at position 0
+// starts from tokens[b, a_b], the last token emitted ("DSpark turns speculation into a scheduler",
+// opening section: draft, verify, keep the accepted prefix and continue from there).
+// ==========================================================================================
+__global__ __launch_bounds__(NT) void k_advance(const int32_t* tokens, const int32_t* accepted_len, int B, int K,
+                                                int32_t* x0, int64_t* emitted) {
+  const int b = blockIdx.x * NT + threadIdx.x;
+  if (b >= B) return;
+  const int a = accepted_len[b];
+  if (a < 0 || a > K) return;   // invalid request: its context stays
+  x0[b] = tokens[(size_t)b * (K + 1) + a];
+  if (emitted) emitted[b] += a + 1;
+}
+
 struct Layout {
   size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
       off_pbias, off_pbias2, off_pplain, off_konst, total;
@@ -2539,6 +2555,19 @@ extern "C" int spec_temperature_scaling(const float* z, const int32_t* verify_le
     hipLaunchKernelGGL(k_sts_pick, dim3(blocks), dim3(STS_NT), 0, st, z, N, K, k, grid, G, run, run1, ece, T,
                        ece_before, ece_after);
   }
+  if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
+}
+
+extern "C" int spec_advance(const int32_t* tokens, const int32_t* accepted_len, int32_t B, int32_t K, int32_t* x0,
+                            int64_t* emitted, spec_stream_t stream) {
+  if (!tokens || !accepted_len || !x0) return SPEC_E_INVAL;
+  if (B < 1 || B > MAX_B || K < 1 || K > MAX_K) return SPEC_E_INVAL;
+  const int ac = arch_ok();
+  if (ac != SPEC_OK) return ac;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(k_advance, dim3((B + NT - 1) / NT), dim3(NT), 0, (hipStream_t)stream, tokens, accepted_len, B, K,
+                     x0, emitted);
   if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
   return SPEC_OK;
 }

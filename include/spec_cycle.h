@@ -244,6 +244,18 @@ int spec_temperature_scaling(const float* z, const int32_t* verify_len, const in
                              double* ece_before, double* ece_after, void* workspace, size_t workspace_bytes,
                              spec_stream_t stream);
 
+/*
+ * Decode-loop glue: the next cycle's context.  For every request with accepted_len[b] in 0..K,
+ * x0[b] becomes tokens[b, accepted_len[b]], the last token the cycle emitted (the correction or
+ * bonus), and emitted[b] (may be NULL) grows by accepted_len[b] + 1; invalid requests keep their
+ * x0 ("DSpark turns speculation into a scheduler", opening section: keep the accepted prefix and
+ * continue from it).  tokens [B, K+1], accepted_len [B]: a spec_cycle call's outputs; x0 [B]
+ * int32 in/out; emitted [B] int64 in/out.  Asynchronous on `stream`.  Returns SPEC_OK or
+ * SPEC_E_INVAL (NULL pointer, B outside 1..1024, K outside 1..32).
+ */
+int spec_advance(const int32_t* tokens, const int32_t* accepted_len, int32_t B, int32_t K, int32_t* x0,
+                 int64_t* emitted, spec_stream_t stream);
+
 /* Static description of an error code (never NULL). */
 const char* spec_error_string(int code);
 

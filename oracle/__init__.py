@@ -350,3 +350,29 @@ def temperature_scaling_ref(z, verify_len, accepted_len, grid, nbins=10) -> dict
     if rc != 0:
         raise ValueError(f"spec_temperature_scaling_ref rejected its arguments (code {rc})")
     return out
+
+
+# ----------------------------------------------------------------------------------------
+# decode loop
+# ----------------------------------------------------------------------------------------
+def advance_ref(tokens, accepted_len, x0):
+    """next context: the last token each valid request emitted (tokens[b, a_b]); invalid keep x0"""
+    x = np.array(x0, dtype=np.int32, copy=True)
+    for b, a in enumerate(accepted_len):
+        if 0 <= a < tokens.shape[1]:
+            x[b] = tokens[b, a]
+    return x
+
+
+def decode_ref(base_sets, target_sets, A, W, x0, conf_sets, temp, threshold, seed, n_cycles, noise=CHUNKED):
+    """the oracle's decode loop: cycle c reads row set c % len(base_sets), seed + c, and the
+    previous cycle's last emitted tokens as x0"""
+    x = np.array(x0, dtype=np.int32, copy=True)
+    outs = []
+    for c in range(n_cycles):
+        i = c % len(base_sets)
+        r = spec_cycle_ref(base_sets[i], target_sets[i], A, W, x, conf_sets[i], temp, threshold, seed + c, noise=noise)
+        r["x0"] = x.copy()
+        outs.append(r)
+        x = advance_ref(r["tokens"], r["accepted_len"], x)
+    return outs

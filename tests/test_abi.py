@@ -129,3 +129,11 @@ def test_temperature_scaling_host_checks(lib):
     bad = list(good)
     bad[4] = 300                                                        # K > 256
     assert lib.spec_temperature_scaling(*bad, fake, C.c_size_t(1 << 20), None) == -1
+
+
+def test_advance_host_checks(lib):
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    assert lib.spec_advance(None, fake, 2, 4, fake, None, None) == -1
+    assert lib.spec_advance(fake, fake, 0, 4, fake, None, None) == -1
+    assert lib.spec_advance(fake, fake, 2, 33, fake, None, None) == -1
+    assert lib.spec_advance(fake, fake, 2, 4, None, None, None) == -1
