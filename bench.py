@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--sts", action="store_true",
                     help="measure sequential temperature scaling on synthetic held-out confidences (an "
                          "overconfident head); prints its own JSON line")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="chain this many scheduled cycles (scheduler, cycle, next context, all on the device) over "
+                         "two alternating row sets and report tokens per cycle and the modelled latency per token")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -107,6 +110,8 @@ def main():
         return bench_schedule(args)
     if args.sts:
         return bench_sts(args)
+    if args.decode > 0:
+        return bench_decode(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
               "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -265,6 +270,73 @@ def main():
                      "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"] / (K + 1)},
         "kernels": kernels,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_decode(args):
+    """Multi-cycle decode: per cycle the scheduler picks verify lengths from the confidences and
+    the target step-time curve t(n) = 20 ms + 2 us n, the cycle runs with them, and each request's
+    last emitted token becomes the next cycle's context; two synthetic row sets alternate and the
+    seed advances per cycle.  Reports tokens per request per cycle (tau), the measured cycle time
+    and the modelled latency per token (cycle + target step) / tau."""
+    import torch
+    from draft_sampling_lossless_spec_amd import (spec_advance, spec_cycle_lengths, spec_schedule,
+                                                  spec_workspace_bytes)
+    from draft_sampling_lossless_spec_amd import workloads as wl
+    sets = [wl.generate(args.config, gen_seed=s, threshold=args.threshold) for s in (1, 2)]
+    w = sets[0]
+    B, K = w.cfg.B, w.cfg.K
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    rows = [(t(s.base), t(s.target), t(s.conf.astype(np.float32))) for s in sets]
+    A, W, temp = t(w.A), t(w.W), t(w.temp)
+    x0 = t(w.x0.astype(np.int32))
+    emitted = torch.zeros(B, dtype=torch.int64, device="cuda")
+    T = torch.from_numpy(0.02 + 2e-6 * np.arange(B * K + 1, dtype=np.float64)).cuda()
+    L = torch.empty(B, dtype=torch.int32, device="cuda")
+    so = torch.empty(4, dtype=torch.float64, device="cuda")
+    ws = torch.empty(spec_workspace_bytes(B, K, w.cfg.V, w.cfg.R, w.cfg.dtype), dtype=torch.uint8, device="cuda")
+    out = {"accepted_len": torch.empty(B, dtype=torch.int32, device="cuda"),
+           "tokens": torch.empty((B, K + 1), dtype=torch.int32, device="cuda")}
+    verify = torch.zeros(B, dtype=torch.int64, device="cuda")
+
+    def cycle(c):
+        base, target, conf = rows[c % 2]
+        spec_schedule(conf, T, 4096, verify_len=L, out=so)
+        spec_cycle_lengths(base, target, A, W, L, temp, w.seed + c, x0=x0, workspace=ws, out=out)
+        spec_advance(out["tokens"], out["accepted_len"], x0, emitted)
+        verify.add_(L.to(torch.int64))
+
+    for c in range(2):
+        cycle(c)
+    torch.cuda.synchronize()
+    emitted.zero_()
+    verify.zero_()
+    n = args.decode
+    ts = time.perf_counter()
+    for c in range(n):
+        cycle(c)
+    torch.cuda.synchronize()
+    t_cycle = (time.perf_counter() - ts) / n
+    tau = float(emitted.sum().item()) / (n * B)
+    n_verify = float(verify.sum().item()) / n
+    t_target = 0.02 + 2e-6 * n_verify
+    line = {
+        "metric": "scheduled decode: emitted tokens per request per cycle (tau)", "value": tau,
+        "unit": "tokens/request/cycle", "n_gpus": 1, "steps": n, "warmup": 2, "ms_per_step": t_cycle * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.cfg.name, "B": B, "K": K, "row_sets": 2, "target_step_model": "20 ms + 2 us per draft token"},
+        "decode": {"verify_tokens_per_cycle": n_verify, "cycle_us": t_cycle * 1e6,
+                   "modelled_target_step_ms": t_target * 1e3,
+                   "latency_per_token_ms": (t_cycle + t_target) / tau * 1e3,
+                   "emitted_tokens_per_s_modelled": tau * B / (t_cycle + t_target),
+                   "speculation_overhead_frac": t_cycle / (t_cycle + t_target)},
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
