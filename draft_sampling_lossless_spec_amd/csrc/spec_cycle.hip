@@ -144,8 +144,6 @@ __global__ void k_init(Params p) {
   const float T = p.temp[b];
   const int x0 = p.x0 ? p.x0[b] : -1;
   bool valid = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V;
-  // prefix cut: keep position j while the fp64 running product of confidences is >= threshold.
-  // The confidences are all loaded up front (in bounds whatever the cut), so the loop waits once.
   int L = 0;
   if (p.L_in) {
     // verify length chosen by a scheduler: outside 0..K marks the request invalid
@@ -155,18 +153,12 @@ __global__ void k_init(Params p) {
       L = 0;
     }
   } else {
-    float c[MAX_K];
-#pragma unroll
-    for (int j = 0; j < MAX_K; j++) c[j] = j < K ? p.conf[(size_t)b * K + j] : 0.0f;
+    // prefix cut: keep position j while the fp64 running product of confidences is >= threshold
     double P = 1.0;
-    bool go = true;
-#pragma unroll
-    for (int j = 0; j < MAX_K; j++) {
-      if (go && j < K) {
-        P *= (double)c[j];
-        go = P >= (double)p.threshold;   // NaN stops the cut
-        L = go ? j + 1 : L;
-      }
+    for (int j = 0; j < K; j++) {
+      P *= (double)p.conf[(size_t)b * K + j];
+      if (!(P >= (double)p.threshold)) break;   // the first failure ends the prefix; NaN fails
+      L = j + 1;
     }
   }
   p.L[b] = L;
