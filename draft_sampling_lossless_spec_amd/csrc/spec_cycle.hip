@@ -9,16 +9,17 @@
 // needs x_s), and every position needs a full pass over the Markov factor W, so the cycle runs
 // as k_init and then K+1 steps, all enqueued by one host call.  Per step:
 //   sweep       one pass over the rows active at step s.  "Bias rows" (DRAFT rows of position s
-//               and CORRECT rows of a position rejected at s-1) need A[prev] . W: a unit is one
-//               32-slot sub-block x one 256-column range; each of the 4 waves keeps the W
-//               fragments of its 64 columns in the accumulation registers and computes the bias
-//               with v_mfma_f32_32x32x16_bf16 directly in the layout the element-wise part
-//               consumes (the bias never leaves registers).  "Plain rows" (LSEP: the target row
-//               of the position being verified; BONUS) are streamed in 4096-column items, one
-//               wave each.  Every unit / item writes one 16-byte partial per row: the
-//               log-normaliser of its columns plus the best perturbed score and its index.
-//               bf16 rows with V % 8 == 0 run both parts in one kernel (k_sweep_fast); other
-//               inputs run k_bias and k_plain.
+//               and CORRECT rows of a position rejected at s-1) need A[prev] . W.  On the bf16
+//               fast path (k_sweep_fast, V % 8 == 0) the gathered A rows of up to 256 bias slots
+//               are staged in LDS once per step; then every wave runs on its own over units of
+//               one 64-column noise chunk x one 32-slot sub-block, keeping the chunk's W
+//               fragments in the accumulation registers and computing the bias with
+//               v_mfma_f32_32x32x16_bf16 directly in the layout the element-wise part consumes
+//               (the bias never leaves registers); each unit writes one record per row (8 bytes
+//               {log-mass, score} for chunked noise).  The general path (k_bias: fp32 factors or
+//               unaligned rows) uses 32-slot x 256-column units with 16-byte records.  "Plain
+//               rows" (LSEP: the target row of the position being verified; BONUS) are streamed
+//               in 4096-column items, one wave each (inside k_sweep_fast, or k_plain).
 //   k_merge(s)  one workgroup per request: reduces its rows' partials, finishes the sampler
 //               (CHUNKED: re-reads the winning 64-column chunk), takes the accept decision,
 //               finalises tokens, and writes the request's roles for step s+1.
@@ -86,6 +87,9 @@ struct Params {
   float* logp;         // [B][K]
   float4* part_bias;   // [bias slots][nrA]
   float4* part_bias2;  // [bias slots][nrA]  CORRECT rows: target-row fallback
+  // bias-row partials of the chunked fast sweep: 8-byte {log-mass, score} records (the record's
+  // index is its noise chunk), same row stride nrA, in the same buffers
+  int part8;
   float4* part_plain;  // [B][nrB]
   const u32x4* konst;  // [2]: 16 zero bytes, then 8 bf16 -inf (stand-in source of masked tile loads)
   int nrA, nrB;
@@ -738,68 +742,127 @@ __device__ void bias_sweep_generic(const Params& p, int s, const Lists& ls, cons
 }
 
 // ---- fast sweep: bf16, 16-byte aligned rows, V % 8 == 0 ----
-// One workgroup of 4 waves per CU (one wave per SIMD, the full register file each).  Wave w owns
-// columns 64 w .. 64 w + 63 of the unit's 256: one noise chunk, held as two 32 x 32 MFMA tiles,
-// with its W fragments in registers (128 registers).  Per unit only the 32 gathered A rows go
-// through LDS (two stages); the draft and target logits are loaded straight into registers in the
-// accumulator layout (each lane reads 32 bytes of one row per fragment, which streams about as fast
-// as fully coalesced reads), two units ahead.  One barrier per unit.
-struct FastLds {
-  uint16_t sA[2][SUB][MAX_R + A_PAD];   // A rows of the unit's 32 slots, two stages
-  float4 red[2][2][NT / 64][SUB];       // [stage][record a / b][wave][row]
+// One workgroup of 4 waves per CU (one wave per SIMD, the full register file each).  The gathered
+// A rows of a group of up to 256 bias slots are staged in LDS once per step (one barrier per
+// group); after that every wave runs on its own: a unit is (noise chunk of 64 columns, sub-block of
+// 32 slots), the wave holds the chunk's W fragments in accumulation registers (128 of them for
+// R = 256), reads the sub-block's B operands from LDS, loads the draft / target logits straight into
+// registers in the accumulator layout two units ahead, and writes the chunk record of each row
+// directly to the partials.  The units of a group are split evenly over all waves of the grid in
+// chunk-major order, so a wave reloads W only when it crosses into the next chunk, and it issues
+// that reload right after the last MFMA chain on the old fragments.
+
+// dynamic LDS of the bias-row sweeps: per-request table [B], then the bias and plain lists
+__host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
+  return (size_t)B * sizeof(ReqMeta) + (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t);
+}
+constexpr int SA_STRIDE = MAX_R + A_PAD;   // bf16 elements per staged A row
+// dynamic LDS of k_sweep_fast with A-row groups of g slots
+__host__ __device__ constexpr size_t fast_dyn_bytes(int B, int g) {
+  return (bias_dyn_bytes(B) + 15) / 16 * 16 + (size_t)g * SA_STRIDE * sizeof(uint16_t);
+}
+
+// draft-logit tiles are prefetched FAST_DEPTH units ahead (two measured faster than three to six)
+constexpr int FAST_DEPTH = 2;
+struct TileRegs {
+  u32x4 x[4];   // logits of the lane's 32 columns of one row (two pieces per MFMA tile)
 };
 
-struct UnitRegs {
-  u32x4 a[4];   // A rows: thread t holds row t / 8, 16-byte pieces (t % 8) + 8 i
-  u32x4 x[4];   // draft logits of the lane's 32 columns (two pieces per fragment)
-  u32x4 t[4];   // target logits (CORRECT units)
-};
-
-__device__ __forceinline__ void fast_issue(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
-                                           const ReqMeta* req, int u, int nsb, UnitRegs& P) {
-  const int range = u / nsb, slot0 = (u % nsb) * SUB;
-  const bool corr = slot0 >= ls.c0;
-  const int R = p.R, segs = R >> 3;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // Masked pieces are not selected after the load (that would wait for it): their address is
-  // switched to a 16-byte constant instead, zeros for A and -inf for the logit tiles.
-  {
-    const int row = threadIdx.x >> 3;
-    const uint16_t ent = bias_list[slot0 + row];
-    const ReqMeta& m = req[ent != NO_ROW ? (ent >> 1) : 0];
-    const int pc = m.prev_c, pd = m.prev_d;
-    const int prev = (ent != NO_ROW) ? ((ent & 1) ? pc : pd) : -1;
-    const uint16_t* arow = (const uint16_t*)p.A + (size_t)prev * R;
+// W fragments of noise chunk c: MFMA A-operand row i of fragment f is column 64 c + 32 f + perm(i),
+// perm chosen so that accumulator q of lane l holds column 64 c + 32 f + 16 (l / 32) + q; lane half
+// l / 32 covers k in [R/2 (l/32), R/2 (l/32 + 1)).  Columns past V read row 0 of W (finite values
+// whose products land in columns whose logits are -inf); fragments past the rank are zero.
+__device__ __forceinline__ void load_w_chunk(const Params& p, int c, bf16x8 (&wf)[2][16]) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, h = lane >> 5;
+  const int R = p.R, T16 = R >> 4, kb = h * (R >> 1);
+  const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int sg = (threadIdx.x & 7) + 8 * i;
-      P.a[i] = *((prev >= 0 && sg < segs) ? (const u32x4*)(arow + 8 * sg) : p.konst);
-    }
-  }
-  {
-    const int m = lane & 31, h = lane >> 5;
-    const uint16_t ent = bias_list[slot0 + m];
-    const int b = ent >> 1;
-    const int j = (ent & 1) ? s - 1 : s;
-    const int v0 = range * TILE_A + 64 * wave + 16 * h;   // + 32 f + 8 k
-    const uint16_t* xr = (const uint16_t*)p.base + ((size_t)b * p.K + j) * p.V;
-    const uint16_t* tr = (const uint16_t*)p.target + ((size_t)b * (p.K + 1) + j) * p.V;
+  for (int f = 0; f < 2; f++) {
+    const int v = CHUNK * c + 32 * f + col_in;
+    const bf16x8* wr = (const bf16x8*)((const uint16_t*)p.W + (size_t)(v < p.V ? v : 0) * R + kb);
+    if (T16 == 16) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int col = v0 + 32 * (i >> 1) + 8 * (i & 1);
-      const bool act = ent != NO_ROW && col < p.V;
-      P.x[i] = *(act ? (const u32x4*)(xr + col) : p.konst + 1);
-      P.t[i] = *((act && corr) ? (const u32x4*)(tr + col) : p.konst + 1);   // same loads on every path
+      for (int t = 0; t < 16; t++) wf[f][t] = wr[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; t++) wf[f][t] = *(t < T16 ? wr + t : (const bf16x8*)p.konst);
     }
   }
 }
 
-__device__ __forceinline__ void store_a(const Params& p, const UnitRegs& P, uint16_t (*sA)[MAX_R + A_PAD]) {
-  const int segs = p.R >> 3;
+// A rows of bias slots g0 .. g0 + rows - 1 into sA (every thread; rows without a Markov bias and
+// the alignment gaps read zeros), 8 loads per thread in flight
+__device__ __forceinline__ void stage_a(const Params& p, const uint16_t* bias_list, const ReqMeta* req, int g0, int rows,
+                                        uint16_t* sA) {
+  const int segs = p.R >> 3, n = rows * segs;
+  for (int e0 = 0; e0 < n; e0 += 8 * NT) {
+    u32x4 v[8];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int sg = (threadIdx.x & 7) + 8 * i;
-    if (sg < segs) *(u32x4*)&sA[threadIdx.x >> 3][8 * sg] = P.a[i];
+    for (int i = 0; i < 8; i++) {
+      const int e = e0 + i * NT + (int)threadIdx.x;
+      int prev = -1, sg = 0;
+      if (e < n) {
+        const int row = e / segs;
+        sg = e - row * segs;
+        const uint16_t ent = bias_list[g0 + row];
+        if (ent != NO_ROW) prev = (ent & 1) ? req[ent >> 1].prev_c : req[ent >> 1].prev_d;
+      }
+      v[i] = *((prev >= 0) ? (const u32x4*)((const uint16_t*)p.A + (size_t)prev * p.R + 8 * sg) : p.konst);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int e = e0 + i * NT + (int)threadIdx.x;
+      if (e < n) {
+        const int row = e / segs;
+        *(u32x4*)&sA[row * SA_STRIDE + 8 * (e - row * segs)] = v[i];
+      }
+    }
+  }
+}
+
+// A unit's place in the wave's span: index, noise chunk, sub-block (all wave-uniform)
+struct UPos {
+  int u, c, k;
+};
+
+// the unit after q, or q itself at the end of the span
+__device__ __forceinline__ UPos upos_next(UPos q, int nsbg, int u1) {
+  if (q.u + 1 < u1) {
+    q.u++;
+    if (++q.k == nsbg) {
+      q.k = 0;
+      q.c++;
+    }
+  }
+  return q;
+}
+
+// Logit tiles of unit q (sub-block q.k of the group starting at slot g0, chunk q.c): the draft row
+// (target = false) or the target row (target = true, CORRECT units).  A slot without a row loads
+// request 0's row (its results are never stored); columns past V (a partial last chunk only) read
+// the 16-byte -inf constant instead.
+__device__ __forceinline__ void tile_issue(const Params& p, int s, const uint16_t* bias_list, int g0, UPos q,
+                                           bool target, TileRegs& T) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, h = lane >> 5;
+  const uint16_t ent = bias_list[g0 + q.k * SUB + m];
+  // a slot without a row (NO_ROW has its low bit set too) reads row 0 of request 0: always in bounds
+  const bool has = ent != NO_ROW;
+  const int b = has ? (ent >> 1) : 0;
+  const int j = !has ? 0 : ((ent & 1) ? s - 1 : s);   // CORRECT rows (s >= 1): position s - 1
+  const int v0 = CHUNK * q.c + 16 * h;   // + 32 (i / 2) + 8 (i % 2)
+  const u32x4* row = target ? (const u32x4*)((const uint16_t*)p.target + (size_t)(b * (p.K + 1) + j) * p.V + v0)
+                            : (const u32x4*)((const uint16_t*)p.base + (size_t)(b * p.K + j) * p.V + v0);
+  if (CHUNK * (q.c + 1) <= p.V) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) T.x[i] = row[4 * (i >> 1) + (i & 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int col = v0 + 32 * (i >> 1) + 8 * (i & 1);
+      T.x[i] = *(col < p.V ? row + 4 * (i >> 1) + (i & 1) : p.konst + 1);
+    }
   }
 }
 
@@ -815,171 +878,118 @@ __device__ __forceinline__ void unpack32(const u32x4 (&w)[4], float (&o)[32]) {
   }
 }
 
-// best (score, index, aux) over an aligned group of 4 lanes, smaller index on ties; every lane of
-// the group gets the result
-template <int CTRL>
-__device__ __forceinline__ void argmax_round(float& sc, int& ix, float& aux) {
-  const float s2 = dpp<CTRL>(sc), a2 = dpp<CTRL>(aux);
-  const int i2 = __builtin_amdgcn_update_dpp(0, ix, CTRL, 0xF, 0xF, false);
-  // the smaller index wins a tie; written without short-circuit so that it stays branch-free
-  const bool take = (i2 >= 0) & ((ix < 0) | (s2 > sc) | ((s2 == sc) & ((unsigned)i2 < (unsigned)ix)));
-  sc = take ? s2 : sc;
-  ix = take ? i2 : ix;
-  aux = take ? a2 : aux;
-}
-
-// Partials of one finished unit, by every wave: lane group g (4 lanes) of wave w takes row
-// 8 w + g % 8, record a in lanes 0..31 and record b (CORRECT units) in lanes 32..63; lane i of the
-// group holds the chunk record of wave i.  Split in the LDS read and the rest, so that the read can
-// be issued together with the MFMA operands and its latency hidden behind the MFMA chain.
-__device__ __forceinline__ float4 fast_flush_read(const float4 (*red)[NT / 64][SUB]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return red[lane >= 32 ? 1 : 0][lane & 3][8 * wave + ((lane & 31) >> 2)];
-}
-
-// the merged record of the lane group (every lane of the group gets it)
-__device__ __forceinline__ float4 fast_flush_reduce(float4 h) {
-  float mx = fmaxf(h.x, dpp<0xB1>(h.x));
-  mx = fmaxf(mx, dpp<0x4E>(mx));
-  float e = (mx == -INFINITY) ? h.x : ex2((h.x - mx) * LOG2E);   // all -inf / NaN: keep a NaN visible
-  e += dpp<0xB1>(e);
-  e += dpp<0x4E>(e);
-  const float lse = (mx == -INFINITY) ? e : mx + lg2(e) * LN2;
-  float sc = h.y, aux = h.w;
-  int ix = __float_as_int(h.z);
-  argmax_round<0xB1>(sc, ix, aux);
-  argmax_round<0x4E>(sc, ix, aux);
-  return make_float4(lse, sc, __int_as_float(ix), aux);
-}
-
-// bias-list entry of the lane group's row in the unit whose slots start at slot0
-__device__ __forceinline__ uint16_t fast_flush_entry(const uint16_t* bias_list, int slot0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return bias_list[slot0 + 8 * wave + ((lane & 31) >> 2)];
-}
-
-__device__ __forceinline__ void fast_flush_store(const Params& p, float4 part, uint16_t e16, int slot0, int range,
-                                                 bool valid) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = slot0 + 8 * wave + ((lane & 31) >> 2);
-  if (valid && (lane & 3) == 0 && e16 != NO_ROW) {
-    if (lane < 32) p.part_bias[(size_t)slot * p.nrA + range] = part;
-    else if (e16 & 1) p.part_bias2[(size_t)slot * p.nrA + range] = part;
-  }
-}
-
-// One unit u from stage ST.  Pcur holds unit u's logit tiles (its A rows are already in stage ST),
-// Pnext unit u + 1's; rm holds the row meta of unit u and leaves with unit u + 1's.  Order: W
-// fragments if the column range changes (drained on the spot, so no later wait ever waits on them);
-// every LDS read of the unit (B operands, unit u - 1's records, unit u + 1's row meta) ahead of the
-// MFMA chain; unit u - 1's partials; element-wise part from Pcur; issue unit u + 2 into Pcur
-// (clamped to the last unit, and with the same loads on every path, so the wait counts are the
-// same everywhere); store unit u + 1's A rows into the other stage; barrier.
-template <int NOISE, int ST>
+// One unit cur of the wave's span (nx = the unit after it, is = the unit FAST_DEPTH after it, both
+// clamped to the span) in a group of nsbg sub-blocks starting at slot g0.  Tcur holds cur's draft
+// tiles and receives is's; Tt holds cur's target tiles if cur is a CORRECT unit and receives nx's if
+// that one is; rm holds cur's row meta and leaves with nx's.  Order: B operands and the next row
+// meta from LDS; the MFMA chain with the tile unpack in its shadow; the next chunk's W fragments if
+// the chunk changes; the element-wise part; the records; the next loads.
+template <int NOISE>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
-                                          const ReqMeta* req, FastLds& L, int u, int u0, int u1, int nsb,
-                                          bf16x8 (&wf)[2][16], UnitRegs& Pcur, UnitRegs& Pnext, RowMeta& rm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                          const ReqMeta* req, const uint16_t* sA, int g0, UPos cur, UPos nx, UPos is,
+                                          bool last, bf16x8 (&wf)[2][16], TileRegs& Tcur, TileRegs& Tt, RowMeta& rm) {
+  const int lane = threadIdx.x & 63;
   const int m = lane & 31, h = lane >> 5;
-  const int V = p.V;
-  const int range = u / nsb, slot0 = (u % nsb) * SUB;
-  if (u > u0 && range != (u - 1) / nsb) {
-    load_w(p, range, wf);
-    __builtin_amdgcn_s_waitcnt(0);
-  }
+  const int c = cur.c;
+  const int slot0 = g0 + cur.k * SUB;
   const int T16 = p.R >> 4, kb = h * (p.R >> 1);
   bf16x8 bop[16];
+  const uint16_t* arow = sA + (cur.k * SUB + m) * SA_STRIDE + kb;
 #pragma unroll
-  for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)&L.sA[ST][m][kb + 8 * (t < T16 ? t : 0)];
-  const float4 hrec = fast_flush_read(L.red[ST ^ 1]);
-  const int fslot0 = ((u - 1 + nsb) % nsb) * SUB, frange = (u - 1) / nsb;
-  const uint16_t fent = fast_flush_entry(bias_list, fslot0);
-  const RowMeta rn = row_meta(bias_list, req, s, ((u + 1) % nsb) * SUB + m);
+  for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)(arow + 8 * (t < T16 ? t : 0));
+  const RowMeta rn = row_meta(bias_list, req, s, g0 + nx.k * SUB + m);
   __builtin_amdgcn_sched_barrier(0);   // keep all reads ahead of the MFMA chain
-  // MFMA chain of unit u, with the previous unit's record merge and the base-logit unpack placed in
-  // its shadow (neither depends on the MFMA results)
+  // the W fragments live in accumulation registers (the MFMA reads its A operand from there), which
+  // leaves the vector registers to the logit tiles and the B operands
+#pragma unroll
+  for (int f = 0; f < 2; f++)
+#pragma unroll
+    for (int t = 0; t < 16; t++) asm volatile("" : "+a"(wf[f][t]));
   float y[32];
-  float4 fpart;
   {
     f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     f32x16 acc1 = acc0;
 #pragma unroll
     for (int t = 0; t < 16; t++) {
-      // for t >= R/16 both operands are zero (zero W fragments; sA zero past the rank)
+      // for t >= R/16 both operands are zero (zero W fragments; the B operand of t = 0 repeated)
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop[t], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop[t], acc1, 0, 0, 0);
     }
-    fpart = fast_flush_reduce(hrec);
     float bx[32];
-    unpack32(Pcur.x, bx);
-#pragma unroll
-    for (int k = 0; k < 32; k++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);   // three vector ALU / transcendental
-    }
+    unpack32(Tcur.x, bx);
 #pragma unroll
     for (int q = 0; q < 16; q++) {
       y[q] = acc0[q] + bx[q];
       y[16 + q] = acc1[q] + bx[16 + q];
     }
   }
-  const int vw = range * TILE_A + 64 * wave;   // this wave's 64 columns: one noise chunk
-  const int chunk = vw / CHUNK;
-  const int v0 = vw + 16 * h;
+  // the next unit's chunk: its W fragments load while this unit's element-wise part runs
+  if (!last && nx.c != c) load_w_chunk(p, nx.c, wf);
+  const int v0 = CHUNK * c + 16 * h;
   float4 oa, ob;
   if (slot0 < ls.c0) {
-    oa = draft_part<NOISE>(y, rm, chunk, v0, V);
+    oa = draft_part<NOISE>(y, rm, c, v0, p.V);
     ob = empty_part();
   } else {
     float t[32];
-    unpack32(Pcur.t, t);
-    correct_part<NOISE>(y, t, rm, chunk, v0, V, oa, ob);
+    unpack32(Tt.x, t);
+    correct_part<NOISE>(y, t, rm, c, v0, p.V, oa, ob);
   }
-  if (h == 0) {
-    L.red[ST][0][wave][m] = oa;
-    L.red[ST][1][wave][m] = ob;
+  if (h == 0 && rm.active) {
+    const size_t i = (size_t)(slot0 + m) * p.nrA + c;
+    if (NOISE == SPEC_NOISE_CHUNKED) {
+      // the chunk index is the record's place in the row
+      ((float2*)p.part_bias)[i] = make_float2(oa.x, oa.y);
+      if (rm.corr) ((float2*)p.part_bias2)[i] = make_float2(ob.x, ob.y);
+    } else {
+      p.part_bias[i] = oa;
+      if (rm.corr) p.part_bias2[i] = ob;
+    }
   }
   rm = rn;
-  fast_flush_store(p, fpart, fent, fslot0, frange, u > u0);
-  fast_issue(p, s, ls, bias_list, req, min(u + 2, u1 - 1), nsb, Pcur);
-  store_a(p, Pnext, L.sA[ST ^ 1]);   // past the last unit this stores a copy of it, never read
-  __syncthreads();
+  tile_issue(p, s, bias_list, g0, is, false, Tcur);
+  if (!last && g0 + nx.k * SUB >= ls.c0) tile_issue(p, s, bias_list, g0, nx, true, Tt);
 }
 
 template <int NOISE>
 __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const uint16_t* bias_list, const ReqMeta* req,
-                                FastLds& L) {
-  const int nsb = ls.n_sb;
-  const long long units = (long long)p.nrA * nsb;
-  const int u0 = (int)(units * blockIdx.x / gridDim.x);
-  const int u1 = (int)(units * (blockIdx.x + 1) / gridDim.x);
-  if (u0 >= u1) return;
-  if (p.R < MAX_R) {
-    // the MFMA loop always runs over the full rank: A columns past R must read as zero
-    uint32_t* z = (uint32_t*)&L.sA[0][0][0];
-    for (int i = threadIdx.x; i < (int)(sizeof(L.sA) / 4); i += NT) z[i] = 0u;
+                                uint16_t* sA, int G) {
+  const int nslots = ls.n_sb * SUB;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
+  const int gw = blockIdx.x * (NT / 64) + wave, nw = gridDim.x * (NT / 64);
+  for (int g0 = 0; g0 < nslots; g0 += G) {
+    const int nsbg = min(G, nslots - g0) / SUB;
+    stage_a(p, bias_list, req, g0, nsbg * SUB, sA);
     __syncthreads();
+    const long long units = (long long)p.nrA * nsbg;
+    const int u0 = (int)(units * gw / nw), u1 = (int)(units * (gw + 1) / nw);
+    if (u0 < u1) {
+      bf16x8 wf[2][16];
+      TileRegs T[FAST_DEPTH], Tt;
+      UPos cur = {u0, u0 / nsbg, u0 % nsbg};
+      UPos is = cur;
+      load_w_chunk(p, cur.c, wf);
+#pragma unroll
+      for (int d = 0; d < FAST_DEPTH; d++) {
+        tile_issue(p, s, bias_list, g0, is, false, T[d]);
+        is = upos_next(is, nsbg, u1);
+      }
+      if (g0 + cur.k * SUB >= ls.c0) tile_issue(p, s, bias_list, g0, cur, true, Tt);
+      RowMeta rm = row_meta(bias_list, req, s, g0 + cur.k * SUB + (threadIdx.x & 31));
+      for (int u = u0; u < u1; u += FAST_DEPTH) {
+#pragma unroll
+        for (int d = 0; d < FAST_DEPTH; d++) {
+          if (u + d < u1) {
+            const UPos nx = upos_next(cur, nsbg, u1);
+            fast_unit<NOISE>(p, s, ls, bias_list, req, sA, g0, cur, nx, is, u + d + 1 == u1, wf, T[d], Tt, rm);
+            cur = nx;
+            is = upos_next(is, nsbg, u1);
+          }
+        }
+      }
+    }
+    __syncthreads();   // every wave is done with sA
   }
-  bf16x8 wf[2][16];
-  UnitRegs P0, P1;
-  load_w(p, u0 / nsb, wf);   // first: waiting for unit u0's tiles then covers W as well
-  fast_issue(p, s, ls, bias_list, req, u0, nsb, P0);
-  fast_issue(p, s, ls, bias_list, req, min(u0 + 1, u1 - 1), nsb, P1);
-  RowMeta rm = row_meta(bias_list, req, s, (u0 % nsb) * SUB + (threadIdx.x & 31));
-  store_a(p, P0, L.sA[0]);
-  __syncthreads();
-  int u = u0;
-  for (; u + 1 < u1; u += 2) {
-    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm);
-    fast_unit<NOISE, 1>(p, s, ls, bias_list, req, L, u + 1, u0, u1, nsb, wf, P1, P0, rm);
-  }
-  int last = 1;
-  if (u < u1) {
-    fast_unit<NOISE, 0>(p, s, ls, bias_list, req, L, u, u0, u1, nsb, wf, P0, P1, rm);
-    last = 0;
-  }
-  fast_flush_store(p, fast_flush_reduce(fast_flush_read(L.red[last])), fast_flush_entry(bias_list, ((u1 - 1) % nsb) * SUB),
-                   ((u1 - 1) % nsb) * SUB, (u1 - 1) / nsb, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1003,18 +1013,21 @@ __device__ __forceinline__ float raw8_at(const Raw8<DT>& r, int i) {
   return __uint_as_float(r.w[i >> 2][i & 3]);
 }
 
-template <int DT, int NOISE, bool VEC>
-__device__ void plain_item(const Params& p, int s, int b, int pslot, int range) {
+// The target-row pieces of one plain item: load k of lane l covers columns 512 k + 8 l of the item.
+template <int DT>
+struct PlainRaw {
+  Raw8<DT> r[KB_LOADS];
+};
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void plain_load(const Params& p, int s, int b, int range, PlainRaw<DT>& R) {
   const int K = p.K, V = p.V;
   const int lane = threadIdx.x & 63;
-  const int role = p.roles[(size_t)(s & 1) * p.B + b] & (RO_LSEP | RO_BONUS);
   const int j = s;   // LSEP verifies position s; BONUS reads row L_b == s
-  const float invT = 1.0f / p.temp[b];
   const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
   const void* row = (const char*)p.target + ((size_t)b * (K + 1) + j) * (size_t)V * esz;
-  const int vbase = range * TILE_B;
-  const int vt = vbase + 8 * lane;   // + 512 k
-  Raw8<DT> r[KB_LOADS];
+  const int vt = range * TILE_B + 8 * lane;   // + 512 k
+  Raw8<DT>* r = R.r;
   if (VEC) {
     // rows are 16-byte aligned and V % 8 == 0 (bf16) / V % 4 == 0 (fp32), so each 16-byte load
     // is wholly inside or wholly past the row end: predicate the loads, pad with -inf
@@ -1047,6 +1060,20 @@ __device__ void plain_item(const Params& p, int s, int b, int pslot, int range) 
       }
     }
   }
+}
+
+// the log-mass (and for a BONUS row the Gumbel winner) of one plain item from its loaded pieces
+template <int DT, int NOISE>
+__device__ __forceinline__ void plain_finish(const Params& p, int s, int b, int pslot, int range,
+                                             const PlainRaw<DT>& R) {
+  const int V = p.V;
+  const int lane = threadIdx.x & 63;
+  const int role = p.roles[(size_t)(s & 1) * p.B + b] & (RO_LSEP | RO_BONUS);
+  const int j = s;
+  const float invT = 1.0f / p.temp[b];
+  const int vbase = range * TILE_B;
+  const int vt = vbase + 8 * lane;   // + 512 k
+  const Raw8<DT>* r = R.r;
   const uint64_t g = (uint64_t)(p.req_off + b);
   const float sc2 = invT * LOG2E;
   // log-mass of each 64-column chunk (8 lanes x 8 values); the rounds are independent
@@ -1121,36 +1148,57 @@ __device__ void plain_item(const Params& p, int s, int b, int pslot, int range) 
   if (lane == 0) p.part_plain[(size_t)pslot * p.nrB + range] = part;
 }
 
+template <int DT, int NOISE, bool VEC>
+__device__ __forceinline__ void plain_item(const Params& p, int s, int b, int pslot, int range) {
+  PlainRaw<DT> R;
+  plain_load<DT, VEC>(p, s, b, range, R);
+  plain_finish<DT, NOISE>(p, s, b, pslot, range, R);
+}
+
 // Row sweeps of one step.  Every workgroup rebuilds the step's row lists from the role bytes;
 // the bias-row sweep also stages each request's bias-row inputs.  The bias sweeps run one
 // workgroup per CU (the W fragments fill the register file); k_plain streams the target rows of
 // LSEP / BONUS roles, one wave per item, six workgroups per CU.
-// dynamic LDS of the bias-row sweeps: per-request table [B], then the bias and plain lists
-__host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
-  return (size_t)B * sizeof(ReqMeta) + (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t);
-}
 // dynamic LDS of the plain-row sweep: bias and plain lists
 __host__ __device__ constexpr size_t plain_dyn_bytes(int B) { return (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t); }
 
-// bf16 fast path: bias rows and plain rows of a step in one launch.  Every workgroup first sweeps
-// its share of the bias units, then its share of the plain items (one wave per item), so the plain
-// rows fill the time the bias rows leave and the step costs one dispatch less.
+// bf16 fast path: bias rows and plain rows of a step in one launch.  Every wave first sweeps its
+// share of the bias units, then its workgroup's share of the plain items (one wave per item), so the
+// plain rows fill the time the bias rows leave and the step costs one dispatch less.  Dynamic LDS:
+// the per-request table, the lists, then the A rows of G bias slots.
 template <int NOISE>
-__global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s) {
+__global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s, int G) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
   __shared__ uint64_t scan_tmp[NT / 64];
-  __shared__ FastLds lds_f;
   ReqMeta* req = (ReqMeta*)dyn_bias;
   uint16_t* bias_list = (uint16_t*)(dyn_bias + (size_t)p.B * sizeof(ReqMeta));
   uint16_t* plain_list = bias_list + bias_slots_max(p.B);
+  uint16_t* sA = (uint16_t*)(dyn_bias + (bias_dyn_bytes(p.B) + 15) / 16 * 16);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
   const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, req, true);
-  if (ls.n_draft + ls.n_correct > 0) bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, lds_f);
+  if (ls.n_draft + ls.n_correct > 0) bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, sA, G);
+  // plain items: each wave keeps PLAIN_DEPTH items' loads in flight
   const long long n_items = (long long)ls.n_plain * p.nrB;
   const int i0 = (int)(n_items * blockIdx.x / gridDim.x), i1 = (int)(n_items * (blockIdx.x + 1) / gridDim.x);
-  for (int it = i0 + (threadIdx.x >> 6); it < i1; it += NT / 64) {
-    const int pslot = it / p.nrB, range = it % p.nrB;
-    plain_item<SPEC_BF16, NOISE, true>(p, s, plain_list[pslot], pslot, range);
+  constexpr int PLAIN_DEPTH = 3, STRIDE = NT / 64;
+  PlainRaw<SPEC_BF16> R[PLAIN_DEPTH];
+  const int first = i0 + (threadIdx.x >> 6);
+#pragma unroll
+  for (int d = 0; d < PLAIN_DEPTH; d++) {
+    const int it = first + STRIDE * d;
+    if (it < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[it / p.nrB], it % p.nrB, R[d]);
+  }
+  for (int it0 = first; it0 < i1; it0 += STRIDE * PLAIN_DEPTH) {
+#pragma unroll
+    for (int d = 0; d < PLAIN_DEPTH; d++) {
+      const int it = it0 + STRIDE * d;
+      if (it < i1) {
+        const int pslot = it / p.nrB;
+        plain_finish<SPEC_BF16, NOISE>(p, s, plain_list[pslot], pslot, it % p.nrB, R[d]);
+        const int nx = it + STRIDE * PLAIN_DEPTH;
+        if (nx < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[nx / p.nrB], nx % p.nrB, R[d]);
+      }
+    }
   }
 }
 
@@ -1240,21 +1288,8 @@ __device__ __forceinline__ float4 pacc_final(const PartAcc& a) {
   return make_float4(lse, a.sc, __int_as_float(a.ix), a.aux);
 }
 
-// Reduce n partial records with one wave (up to 16 per lane in flight at once); result in every lane.
-__device__ __forceinline__ float4 wave_reduce_parts(const float4* parts, int n) {
-  const int lane = threadIdx.x & 63;
-  PartAcc a;
-  pacc_init(a);
-  for (int i0 = 0; i0 < n; i0 += 16 * 64) {
-    float4 buf[16];
-#pragma unroll
-    for (int k = 0; k < 16; k++) {
-      const int i = i0 + 64 * k + lane;
-      buf[k] = (i < n) ? parts[i] : empty_part();
-    }
-#pragma unroll
-    for (int k = 0; k < 16; k++) pacc_add(a, buf[k]);
-  }
+// running record of every lane of a wave merged into every lane
+__device__ __forceinline__ void wave_reduce_acc(PartAcc& a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float m2 = __shfl_xor(a.m, o, 64), s2 = __shfl_xor(a.s, o, 64);
@@ -1263,7 +1298,49 @@ __device__ __forceinline__ float4 wave_reduce_parts(const float4* parts, int n) 
     pacc_mass(a, m2, s2, nan2);
     pacc_best(a, sc2, ix2, aux2);
   }
-  return pacc_final(a);
+}
+
+// records per row and thread in one round of the merge's partial reduction
+constexpr int MERGE_BATCH = 10;
+
+// records i0 + NT k + thread (k < MERGE_BATCH) of a row's n partials, empty past n; 8-byte
+// records {log-mass, score} take their index from their place
+__device__ __forceinline__ void load_parts(const char* parts, int rec8, int n, int i0, float4 (&b)[MERGE_BATCH]) {
+#pragma unroll
+  for (int k = 0; k < MERGE_BATCH; k++) {
+    const int i = i0 + NT * k + (int)threadIdx.x;
+    if (rec8) {
+      const float2 r = (i < n) ? ((const float2*)parts)[i] : make_float2(-INFINITY, -INFINITY);
+      b[k] = make_float4(r.x, r.y, __int_as_float(i < n ? i : -1), 0.0f);
+    } else {
+      b[k] = (i < n) ? ((const float4*)parts)[i] : empty_part();
+    }
+  }
+}
+
+// a batch of records into a running record: the batch's maximum first, then one scaled sum of
+// exponentials, merged once; the winner by branch-free selects (smaller index on equal scores)
+__device__ __forceinline__ void add_parts(PartAcc& a, const float4 (&b)[MERGE_BATCH]) {
+  float mx = -INFINITY;
+  int nan = 0;
+#pragma unroll
+  for (int k = 0; k < MERGE_BATCH; k++) {
+    nan |= (b[k].x != b[k].x);
+    mx = fmaxf(mx, b[k].x);
+  }
+  float sum = 0.0f;
+  const float mo = (mx == -INFINITY) ? 0.0f : mx * LOG2E;
+#pragma unroll
+  for (int k = 0; k < MERGE_BATCH; k++) sum += ex2(fmaf(b[k].x, LOG2E, -mo));   // -inf: 0; NaN: flagged
+  pacc_mass(a, mx, nan ? 0.0f : sum, nan);
+#pragma unroll
+  for (int k = 0; k < MERGE_BATCH; k++) {
+    const int ix = __float_as_int(b[k].z);
+    const bool take = (ix >= 0) & ((a.ix < 0) | (b[k].y > a.sc) | ((b[k].y == a.sc) & ((unsigned)ix < (unsigned)a.ix)));
+    a.sc = take ? b[k].y : a.sc;
+    a.aux = take ? b[k].w : a.aux;
+    a.ix = take ? ix : a.ix;
+  }
 }
 
 // half of the Markov-bias dot product A[prev] . W[v] (k in [hh R/2, (hh + 1) R/2)), fp32 accumulate
@@ -1393,6 +1470,7 @@ __device__ L2Result level_two(const Params& p, const L2Job& jb, int gt, float4* 
 template <int DT, int NOISE>
 __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
   __shared__ float4 red[4][NT / 64];
+  __shared__ PartAcc racc[4][NT / 64];
   __shared__ float4 lds2[2][2];
   const int b = blockIdx.x;
   const int B = p.B, K = p.K, V = p.V;
@@ -1420,15 +1498,63 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
   const size_t esz = (DT == SPEC_FP32) ? 4 : 2;
   const bool hasD = roles & RO_DRAFT, hasC = roles & RO_CORRECT, hasP = roles & (RO_LSEP | RO_BONUS);
 
-  // ---- round 1: partials of every row, one wave per record: DRAFT, CORRECT, its fallback, plain
+  // ---- round 1: partials of every row (DRAFT, CORRECT, its fallback, plain), each row's records
+  // split over the whole workgroup: every thread keeps one running record per row and issues its
+  // loads of all rows together (MERGE_BATCH per row and round), then the wave and the workgroup
+  // reduce them
   {
+    const int esz = p.part8 ? 8 : 16;
+    const char* pd = (const char*)p.part_bias + (size_t)(hasD ? slot_d : 0) * p.nrA * esz;
+    const char* pc = (const char*)p.part_bias + (size_t)(hasC ? slot_c : 0) * p.nrA * esz;
+    const char* pc2 = (const char*)p.part_bias2 + (size_t)(hasC ? slot_c : 0) * p.nrA * esz;
+    const char* pp = (const char*)(p.part_plain + (size_t)(hasP ? slot_p : 0) * p.nrB);
+    const int nD = hasD ? p.nrA : 0, nC = hasC ? p.nrA : 0, nP = hasP ? p.nrB : 0;
+    const int nmax = max(max(nD, nC), nP);
+    PartAcc ad, ac, ac2, ap;
+    pacc_init(ad);
+    pacc_init(ac);
+    pacc_init(ac2);
+    pacc_init(ap);
+    // the row kinds are uniform over the workgroup: absent rows cost neither loads nor arithmetic
+    for (int i0 = 0; i0 < nmax; i0 += MERGE_BATCH * NT) {
+      float4 bd[MERGE_BATCH], bc[MERGE_BATCH], bc2[MERGE_BATCH], bp[MERGE_BATCH];
+      if (hasD) load_parts(pd, p.part8, nD, i0, bd);
+      if (hasC) {
+        load_parts(pc, p.part8, nC, i0, bc);
+        load_parts(pc2, p.part8, nC, i0, bc2);
+      }
+      if (hasP) load_parts(pp, 0, nP, i0, bp);
+      if (hasD) add_parts(ad, bd);
+      if (hasC) {
+        add_parts(ac, bc);
+        add_parts(ac2, bc2);
+      }
+      if (hasP) add_parts(ap, bp);
+    }
+    if (hasD) wave_reduce_acc(ad);
+    if (hasC) {
+      wave_reduce_acc(ac);
+      wave_reduce_acc(ac2);
+    }
+    if (hasP) wave_reduce_acc(ap);
     const int w = threadIdx.x >> 6;
-    float4 r = empty_part();
-    if (w == 0 && hasD) r = wave_reduce_parts(p.part_bias + (size_t)slot_d * p.nrA, p.nrA);
-    if (w == 1 && hasC) r = wave_reduce_parts(p.part_bias + (size_t)slot_c * p.nrA, p.nrA);
-    if (w == 2 && hasC) r = wave_reduce_parts(p.part_bias2 + (size_t)slot_c * p.nrA, p.nrA);
-    if (w == 3 && hasP) r = wave_reduce_parts(p.part_plain + (size_t)slot_p * p.nrB, p.nrB);
-    if ((threadIdx.x & 63) == 0) red[0][w] = r;
+    if ((threadIdx.x & 63) == 0) {
+      racc[0][w] = ad;
+      racc[1][w] = ac;
+      racc[2][w] = ac2;
+      racc[3][w] = ap;
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+      PartAcc a = racc[threadIdx.x][0];
+#pragma unroll
+      for (int v = 1; v < NT / 64; v++) {
+        const PartAcc& o = racc[threadIdx.x][v];
+        pacc_mass(a, o.m, o.s, o.nan);
+        pacc_best(a, o.sc, o.ix, o.aux);
+      }
+      red[0][threadIdx.x] = pacc_final(a);
+    }
   }
   __syncthreads();
   const float4 tot_d = red[0][0], tot_c = red[0][1], tot_c2 = red[0][2], tot_p = red[0][3];
@@ -2159,7 +2285,9 @@ static int dtype_ok(const spec_dims* d) {
 static Layout layout(const spec_dims* d) {
   Layout l;
   const size_t B = (size_t)d->B, K = (size_t)d->K;
-  l.nrA = (d->V + TILE_A - 1) / TILE_A;
+  // partial records per bias row: room for the fast sweep's one record per noise chunk (the general
+  // path's TILE_A-column ranges need fewer)
+  l.nrA = (d->V + CHUNK - 1) / CHUNK;
   l.nrB = (d->V + TILE_B - 1) / TILE_B;
   l.gridB = (int)((B * l.nrB + NT / 64 - 1) / (NT / 64));
   size_t o = 0;
@@ -2213,6 +2341,15 @@ static int arch_ok() {
   return ok > 0 ? SPEC_OK : SPEC_E_ARCH;
 }
 
+// k_sweep_fast: A-row group of the step, the largest of 256 / 128 / 64 / 32 slots whose LDS fits
+// in the 160 KiB of a workgroup
+static int sweep_fast_group(int B) {
+  const size_t cap = (size_t)160 * 1024 - sizeof(uint64_t) * (NT / 64);
+  int g = 8 * SUB;
+  while (g > SUB && fast_dyn_bytes(B, g) > cap) g /= 2;
+  return g;
+}
+
 // Kernel i of a cycle (0 = init; 1 + 3s, 2 + 3s, 3 + 3s = bias sweep, plain sweep, merge of step s)
 // may carry a start/stop event pair, attached to its own dispatch.
 struct Timing {
@@ -2224,11 +2361,15 @@ struct Timing {
 
 template <int DT, int NOISE, bool VEC>
 static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const Timing& tm) {
+  const int G = sweep_fast_group(p.B);
+  if (DT == SPEC_BF16 && VEC)
+    (void)hipFuncSetAttribute((const void*)k_sweep_fast<NOISE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)fast_dyn_bytes(p.B, G));
   for (int s = 0; s <= p.K; s++) {
     const int k0 = 1 + 3 * s;
     if (DT == SPEC_BF16 && VEC) {
-      hipExtLaunchKernelGGL((k_sweep_fast<NOISE>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st, tm.start(k0),
-                            tm.stop(k0), 0, p, s);
+      hipExtLaunchKernelGGL((k_sweep_fast<NOISE>), dim3(cu_count()), dim3(NT), fast_dyn_bytes(p.B, G), st, tm.start(k0),
+                            tm.stop(k0), 0, p, s, G);
       // the plain rows ran inside the sweep: an empty interval keeps the timing slots in place
       if (tm.start(k0 + 1)) {
         hipEventRecord(tm.start(k0 + 1), st);
@@ -2334,12 +2475,14 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
   p.part_bias2 = (float4*)(ws + l.off_pbias2);
   p.part_plain = (float4*)(ws + l.off_pplain);
   p.konst = (const u32x4*)(ws + l.off_konst);
-  p.nrA = l.nrA;
   p.nrB = l.nrB;
 
   // vector loads need 16-byte aligned rows
   const size_t esz = d->dtype == SPEC_FP32 ? 4 : 2;
   const bool vec = ((d->V * esz) % 16 == 0) && ((((uintptr_t)base_logits) | ((uintptr_t)target_logits)) & 15) == 0;
+  // column ranges of the bias-row partials: one noise chunk on the bf16 fast sweep, TILE_A on the general path
+  p.nrA = (d->dtype == SPEC_BF16 && vec) ? (d->V + CHUNK - 1) / CHUNK : (d->V + TILE_A - 1) / TILE_A;
+  p.part8 = (d->dtype == SPEC_BF16 && vec && d->noise == SPEC_NOISE_CHUNKED) ? 1 : 0;
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
