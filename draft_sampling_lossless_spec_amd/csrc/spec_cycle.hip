@@ -792,14 +792,16 @@ __device__ __forceinline__ void load_w_chunk(const Params& p, int c, bf16x8 (&wf
 }
 
 // A rows of bias slots g0 .. g0 + rows - 1 into sA (every thread; rows without a Markov bias and
-// the alignment gaps read zeros), 8 loads per thread in flight
+// the alignment gaps read zeros), STAGE_BATCH loads per thread in flight (32, one round for a full
+// group, measured no faster)
+constexpr int STAGE_BATCH = 8;
 __device__ __forceinline__ void stage_a(const Params& p, const uint16_t* bias_list, const ReqMeta* req, int g0, int rows,
                                         uint16_t* sA) {
   const int segs = p.R >> 3, n = rows * segs;
-  for (int e0 = 0; e0 < n; e0 += 8 * NT) {
-    u32x4 v[8];
+  for (int e0 = 0; e0 < n; e0 += STAGE_BATCH * NT) {
+    u32x4 v[STAGE_BATCH];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < STAGE_BATCH; i++) {
       const int e = e0 + i * NT + (int)threadIdx.x;
       int prev = -1, sg = 0;
       if (e < n) {
@@ -811,7 +813,7 @@ __device__ __forceinline__ void stage_a(const Params& p, const uint16_t* bias_li
       v[i] = *((prev >= 0) ? (const u32x4*)((const uint16_t*)p.A + (size_t)prev * p.R + 8 * sg) : p.konst);
     }
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < STAGE_BATCH; i++) {
       const int e = e0 + i * NT + (int)threadIdx.x;
       if (e < n) {
         const int row = e / segs;
@@ -884,6 +886,15 @@ __device__ __forceinline__ void unpack32(const u32x4 (&w)[4], float (&o)[32]) {
 // that one is; rm holds cur's row meta and leaves with nx's.  Order: B operands and the next row
 // meta from LDS; the MFMA chain with the tile unpack in its shadow; the next chunk's W fragments if
 // the chunk changes; the element-wise part; the records; the next loads.
+// B operands of sub-block k at constant offsets: for t >= R/16 they read the zeroed columns
+// [R, MAX_R) of the row
+__device__ __forceinline__ void read_bop(const Params& p, const uint16_t* sA, int k, bf16x8 (&bop)[16]) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* arow = sA + (k * SUB + (lane & 31)) * SA_STRIDE + (lane >> 5) * (p.R >> 1);
+#pragma unroll
+  for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)(arow + 8 * t);
+}
+
 template <int NOISE>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
                                           const ReqMeta* req, const uint16_t* sA, int g0, UPos cur, UPos nx, UPos is,
@@ -892,11 +903,8 @@ __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& l
   const int m = lane & 31, h = lane >> 5;
   const int c = cur.c;
   const int slot0 = g0 + cur.k * SUB;
-  const int T16 = p.R >> 4, kb = h * (p.R >> 1);
   bf16x8 bop[16];
-  const uint16_t* arow = sA + (cur.k * SUB + m) * SA_STRIDE + kb;
-#pragma unroll
-  for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)(arow + 8 * (t < T16 ? t : 0));
+  read_bop(p, sA, cur.k, bop);
   const RowMeta rn = row_meta(bias_list, req, s, g0 + nx.k * SUB + m);
   __builtin_amdgcn_sched_barrier(0);   // keep all reads ahead of the MFMA chain
   // the W fragments live in accumulation registers (the MFMA reads its A operand from there), which
@@ -907,20 +915,26 @@ __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& l
     for (int t = 0; t < 16; t++) asm volatile("" : "+a"(wf[f][t]));
   float y[32];
   {
-    f32x16 acc0 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    f32x16 acc1 = acc0;
+    // the accumulators start from the draft logits, so the chain leaves base + bias (its unpack runs
+    // while the B operands arrive from LDS)
+    float bx[32];
+    unpack32(Tcur.x, bx);
+    f32x16 acc0, acc1;
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      acc0[q] = bx[q];
+      acc1[q] = bx[16 + q];
+    }
 #pragma unroll
     for (int t = 0; t < 16; t++) {
-      // for t >= R/16 both operands are zero (zero W fragments; the B operand of t = 0 repeated)
+      // for t >= R/16 both operands are zero (zero W fragments; zeroed A columns)
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop[t], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop[t], acc1, 0, 0, 0);
     }
-    float bx[32];
-    unpack32(Tcur.x, bx);
 #pragma unroll
     for (int q = 0; q < 16; q++) {
-      y[q] = acc0[q] + bx[q];
-      y[16 + q] = acc1[q] + bx[16 + q];
+      y[q] = acc0[q];
+      y[16 + q] = acc1[q];
     }
   }
   // the next unit's chunk: its W fragments load while this unit's element-wise part runs
@@ -956,6 +970,13 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
                                 uint16_t* sA, int G) {
   const int nslots = ls.n_sb * SUB;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
+  if (p.R < MAX_R) {
+    // the MFMA chain always runs over the full rank: A columns [R, MAX_R) of every staged row read
+    // as zero (stage_a writes only the first R)
+    const int zc = (MAX_R - p.R) / 8;
+    for (int e = threadIdx.x; e < G * zc; e += NT)
+      *(u32x4*)&sA[(e / zc) * SA_STRIDE + p.R + 8 * (e % zc)] = (u32x4){0u, 0u, 0u, 0u};
+  }
   const int gw = blockIdx.x * (NT / 64) + wave, nw = gridDim.x * (NT / 64);
   for (int g0 = 0; g0 < nslots; g0 += G) {
     const int nsbg = min(G, nslots - g0) / SUB;
@@ -1038,7 +1059,7 @@ __device__ __forceinline__ void plain_load(const Params& p, int s, int b, int ra
 #pragma unroll
       for (int u = 0; u < (DT == SPEC_BF16 ? 1 : 2); u++) {
         const int vv = vt + 512 * k + 4 * u;
-        if (vv < V) r[k].w[u] = __builtin_nontemporal_load(q + u);
+        if (vv < V) r[k].w[u] = q[u];   // ordinary loads: non-temporal ones stream at about half the rate
         else r[k].w[u] = (u32x4){ninf, ninf, ninf, ninf};
       }
     }
