@@ -327,25 +327,6 @@ __device__ __forceinline__ float4 merge_part(float4 x, float4 y) {
 
 __device__ __forceinline__ float4 empty_part() { return make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f); }
 
-// log-sum-exp of n values held by a lane and its partner lane (lane ^ 32); NaN-preserving
-template <int N>
-__device__ __forceinline__ float pair_lse(const float* x) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < N; i++) mx = fmaxf(mx, x[i]);
-  mx = fmaxf(mx, xor32f(mx));
-  float sum = 0.0f;
-  if (mx != -INFINITY) {
-    const float mo = mx * LOG2E;
-#pragma unroll
-    for (int i = 0; i < N; i++) sum += ex2(fmaf(x[i], LOG2E, -mo));
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; i++) sum += x[i];   // every value -inf or NaN: keep a NaN visible
-  }
-  sum += xor32f(sum);
-  return (mx == -INFINITY) ? sum : mx + lg2(sum) * LN2;
-}
 
 // log-sum-exp of invT * y over n values held by a lane and its partner lane (lane ^ 32), invT > 0:
 // the scale is folded into the exponent argument, max(invT y) = invT max(y); NaN-preserving
@@ -393,51 +374,12 @@ __device__ __forceinline__ void pair_best(float& sc, int& ix, float& aux) {
   }
 }
 
-// 16 consecutive bf16 / fp32 values of a row as raw words (bf16: 8 words, fp32: 16 words)
-template <int DT>
-struct Raw16 {
-  u32x4 w[DT == SPEC_BF16 ? 2 : 4];
-};
-
-// 16 columns of one row per lane; the lanes of one load instruction span 32 rows, so these are
-// ordinary (temporal) loads: the other pieces of each cache line arrive from neighbouring
-// instructions through the caches
-template <int DT>
-__device__ __forceinline__ void raw_load(const void* row, int v, Raw16<DT>& r) {
-  const u32x4* q = (const u32x4*)((const char*)row + (size_t)v * (DT == SPEC_BF16 ? 2 : 4));
-#pragma unroll
-  for (int k = 0; k < (DT == SPEC_BF16 ? 2 : 4); k++) r.w[k] = q[k];
-}
-
-// as raw_load, for rows whose 16-byte pieces are each wholly inside or wholly past column V
-// (aligned rows, V % 8 == 0 for bf16, V % 4 == 0 for fp32): the pieces past V read as -inf
-template <int DT>
-__device__ __forceinline__ void raw_load_pred(const void* row, int v, int V, Raw16<DT>& r) {
-  const u32x4* q = (const u32x4*)((const char*)row + (size_t)v * (DT == SPEC_BF16 ? 2 : 4));
-  const uint32_t ninf = (DT == SPEC_BF16) ? 0xFF80FF80u : 0xFF800000u;
-  constexpr int per = (DT == SPEC_BF16) ? 8 : 4;
-#pragma unroll
-  for (int k = 0; k < (DT == SPEC_BF16 ? 2 : 4); k++) {
-    if (v + per * k < V) r.w[k] = q[k];
-    else r.w[k] = (u32x4){ninf, ninf, ninf, ninf};
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ float raw_at(const Raw16<DT>& r, int i) {
-  if (DT == SPEC_BF16) {
-    const uint32_t w = r.w[i >> 3][(i >> 1) & 3];
-    return (i & 1) ? bf16_hi(w) : bf16_lo(w);
-  }
-  return __uint_as_float(r.w[i >> 2][i & 3]);
-}
-
 // ------------------------------------------------------------------------------------------
 // bias rows (DRAFT / CORRECT): the Markov bias A[prev] . W of every column, never written out,
-// plus the element-wise work of the row.  A unit is (column range of 256, sub-block of 32 bias
-// slots); a sub-block holds one role only.  The units of a step are split evenly over one
-// workgroup per CU in range-major order, so a workgroup reloads its W fragments only when it
-// crosses into the next column range.
+// plus the element-wise work of the row; a 32-slot sub-block holds one role only.  General path
+// (k_bias: fp32 factors or unaligned rows): a unit is (column range of 256, sub-block), the units of
+// a step are split evenly over one workgroup per CU in range-major order, so a workgroup reloads its
+// W fragments only when it crosses into the next column range.  The bf16 fast path follows below.
 // ------------------------------------------------------------------------------------------
 struct WaveOut {        // one wave's result for one row over its 64 columns (one noise chunk)
   float4 a;             // {log-mass, best score, best index (bits), aux}
@@ -880,12 +822,6 @@ __device__ __forceinline__ void unpack32(const u32x4 (&w)[4], float (&o)[32]) {
   }
 }
 
-// One unit cur of the wave's span (nx = the unit after it, is = the unit FAST_DEPTH after it, both
-// clamped to the span) in a group of nsbg sub-blocks starting at slot g0.  Tcur holds cur's draft
-// tiles and receives is's; Tt holds cur's target tiles if cur is a CORRECT unit and receives nx's if
-// that one is; rm holds cur's row meta and leaves with nx's.  Order: B operands and the next row
-// meta from LDS; the MFMA chain with the tile unpack in its shadow; the next chunk's W fragments if
-// the chunk changes; the element-wise part; the records; the next loads.
 // B operands of sub-block k at constant offsets: for t >= R/16 they read the zeroed columns
 // [R, MAX_R) of the row
 __device__ __forceinline__ void read_bop(const Params& p, const uint16_t* sA, int k, bf16x8 (&bop)[16]) {
@@ -895,6 +831,13 @@ __device__ __forceinline__ void read_bop(const Params& p, const uint16_t* sA, in
   for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)(arow + 8 * t);
 }
 
+// One unit cur of the wave's span (nx = the unit after it, is = the unit FAST_DEPTH after it, both
+// clamped to the span) in a group of nsbg sub-blocks starting at slot g0.  Tcur holds cur's draft
+// tiles and receives is's; Tt holds cur's target tiles if cur is a CORRECT unit and receives nx's if
+// that one is; rm holds cur's row meta and leaves with nx's.  Order: B operands and the next row
+// meta from LDS, the draft tile unpacked into the accumulators (while those reads land); the MFMA
+// chain; the next chunk's W fragments if the chunk changes; the element-wise part; the records; the
+// next loads.
 template <int NOISE>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
                                           const ReqMeta* req, const uint16_t* sA, int g0, UPos cur, UPos nx, UPos is,
@@ -1298,11 +1241,6 @@ __device__ __forceinline__ void pacc_best(PartAcc& a, float sc, int ix, float au
   }
 }
 
-__device__ __forceinline__ void pacc_add(PartAcc& a, float4 r) {
-  if (r.x != r.x) a.nan = 1;
-  else pacc_mass(a, r.x, 1.0f, 0);
-  pacc_best(a, r.y, __float_as_int(r.z), r.w);
-}
 
 __device__ __forceinline__ float4 pacc_final(const PartAcc& a) {
   const float lse = a.nan ? NAN : (a.m == -INFINITY ? -INFINITY : a.m + lg2(a.s) * LN2);
