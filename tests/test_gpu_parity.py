@@ -43,6 +43,12 @@ SMALL = {
     "k1_b1": lambda: wl.generate(wl.small_config(B=1, K=1, V=4096, R=256, threshold=0.1)),
     "temp06_k8": lambda: wl.generate(wl.small_config(B=16, K=8, V=5000, R=32, threshold=0.05, temp=0.6,
                                                       sigma=(1.5,))),
+    # the longest draft block the library takes (K = 32: 33 steps), close drafts so that requests
+    # survive to late steps, full rank on the bf16 fast path
+    "k32_max_positions": lambda: wl.generate(wl.small_config(B=8, K=32, V=3008, R=256, threshold=1e-6,
+                                                              sigma=(0.3,))),
+    # the largest batch (1024 requests): A-row groups of 128 slots on the fast path, many sub-blocks
+    "b1024_small_v": lambda: wl.generate(wl.small_config(B=1024, K=2, V=1024, R=32, threshold=0.05)),
 }
 
 
