@@ -956,6 +956,44 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
   }
 }
 
+// Wave-wide reductions (every lane gets the result): DPP within each 16-lane row (xor 1, xor 2, half-
+// row mirror, row mirror), one lane shuffle across rows (xor 16), one lane swap across halves (xor 32).
+__device__ __forceinline__ float wave_max64(float x) {
+  x = max8(x);
+  x = fmaxf(x, dpp<0x140>(x));
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, xor32f(x));
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+  x = sum8(x);
+  x += dpp<0x140>(x);
+  x += __shfl_xor(x, 16, 64);
+  return x + xor32f(x);
+}
+
+// one all-reduce step of the winner (larger score, smaller index on ties, index < 0 = none) with the
+// partner values sc2, ix2, aux2
+__device__ __forceinline__ void argmax_take(float& sc, int& ix, float& aux, float sc2, int ix2, float aux2) {
+  const bool take = (ix2 >= 0) & ((ix < 0) | (sc2 > sc) | ((sc2 == sc) & ((unsigned)ix2 < (unsigned)ix)));
+  sc = take ? sc2 : sc;
+  ix = take ? ix2 : ix;
+  aux = take ? aux2 : aux;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& sc, int& ix, float& aux) {
+  argmax_take(sc, ix, aux, dpp<CTRL>(sc), __builtin_amdgcn_update_dpp(0, ix, CTRL, 0xF, 0xF, false), dpp<CTRL>(aux));
+}
+
+__device__ __forceinline__ void wave_argmax64(float& sc, int& ix, float& aux) {
+  argmax_dpp<0xB1>(sc, ix, aux);
+  argmax_dpp<0x4E>(sc, ix, aux);
+  argmax_dpp<0x141>(sc, ix, aux);
+  argmax_dpp<0x140>(sc, ix, aux);
+  argmax_take(sc, ix, aux, __shfl_xor(sc, 16, 64), __shfl_xor(ix, 16, 64), __shfl_xor(aux, 16, 64));
+  argmax_take(sc, ix, aux, xor32f(sc), xor32i(ix), xor32f(aux));
+}
+
 // ------------------------------------------------------------------------------------------
 // plain target rows (LSEP / BONUS): items of TILE_B columns, one wave each, no barrier; every load
 // of the item is issued before any arithmetic
@@ -981,6 +1019,8 @@ __device__ __forceinline__ float raw8_at(const Raw8<DT>& r, int i) {
 template <int DT>
 struct PlainRaw {
   Raw8<DT> r[KB_LOADS];
+  int role;     // the request's role byte at this step and its temperature, loaded with the pieces
+  float temp;   // (used right after they land, they would otherwise cost a memory round per item)
 };
 
 template <int DT, bool VEC>
@@ -992,6 +1032,8 @@ __device__ __forceinline__ void plain_load(const Params& p, int s, int b, int ra
   const void* row = (const char*)p.target + ((size_t)b * (K + 1) + j) * (size_t)V * esz;
   const int vt = range * TILE_B + 8 * lane;   // + 512 k
   Raw8<DT>* r = R.r;
+  R.role = p.roles[(size_t)(s & 1) * p.B + b];
+  R.temp = p.temp[b];
   if (VEC) {
     // rows are 16-byte aligned and V % 8 == 0 (bf16) / V % 4 == 0 (fp32), so each 16-byte load
     // is wholly inside or wholly past the row end: predicate the loads, pad with -inf
@@ -1032,15 +1074,17 @@ __device__ __forceinline__ void plain_finish(const Params& p, int s, int b, int 
                                              const PlainRaw<DT>& R) {
   const int V = p.V;
   const int lane = threadIdx.x & 63;
-  const int role = p.roles[(size_t)(s & 1) * p.B + b] & (RO_LSEP | RO_BONUS);
+  const int role = R.role & (RO_LSEP | RO_BONUS);
   const int j = s;
-  const float invT = 1.0f / p.temp[b];
+  const float invT = 1.0f / R.temp;
   const int vbase = range * TILE_B;
   const int vt = vbase + 8 * lane;   // + 512 k
   const Raw8<DT>* r = R.r;
   const uint64_t g = (uint64_t)(p.req_off + b);
   const float sc2 = invT * LOG2E;
-  // log-mass of each 64-column chunk (8 lanes x 8 values); the rounds are independent
+  // log-mass of each 64-column chunk (8 lanes x 8 values).  The rounds are independent and written
+  // without branches, so that they interleave: with a finite maximum the arithmetic is the plain
+  // scaled sum; every value -inf gives -inf, and a NaN among -inf values gives NaN.
   float own = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KB_LOADS; k++) {
@@ -1048,18 +1092,16 @@ __device__ __forceinline__ void plain_finish(const Params& p, int s, int b, int 
 #pragma unroll
     for (int i = 1; i < 8; i++) mx = fmaxf(mx, raw8_at<DT>(r[k], i));
     mx = max8(mx);
-    float sum = 0.0f;
-    if (mx != -INFINITY) {
-      const float mo = mx * sc2;
+    const float mo = (mx == -INFINITY) ? 0.0f : mx * sc2;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; i++) sum += ex2(fmaf(raw8_at<DT>(r[k], i), sc2, -mo));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i++) sum += raw8_at<DT>(r[k], i);   // every value -inf or NaN: keep a NaN visible
+    for (int i = 0; i < 8; i += 2) {
+      s0 += ex2(fmaf(raw8_at<DT>(r[k], i), sc2, -mo));
+      s1 += ex2(fmaf(raw8_at<DT>(r[k], i + 1), sc2, -mo));
     }
-    sum = sum8(sum);
-    const float lse = (mx == -INFINITY) ? sum : mx * invT + lg2(sum) * LN2;
-    if ((lane & 7) == k) own = lse;
+    const float sum = sum8(s0 + s1);
+    const float lse = (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
+    own = ((lane & 7) == k) ? lse : own;
   }
   float4 part = make_float4(own, -INFINITY, __int_as_float(-1), 0.0f);
   if (role == RO_BONUS) {
@@ -1099,15 +1141,22 @@ __device__ __forceinline__ void plain_finish(const Params& p, int s, int b, int 
       part.z = __int_as_float(bv);
     }
   }
-  // wave reduction
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    float4 y;
-    y.x = __shfl_xor(part.x, o, 64);
-    y.y = __shfl_xor(part.y, o, 64);
-    y.z = __shfl_xor(part.z, o, 64);
-    y.w = __shfl_xor(part.w, o, 64);
-    part = merge_part(part, y);
+  // wave reduction: the log-mass as one maximum and one scaled sum over the 64 lanes (every value
+  // -inf gives -inf, a NaN gives NaN); for a BONUS row also the winner (the role is the same for the
+  // whole wave)
+  {
+    const float mx = wave_max64(part.x);
+    const float mo = (mx == -INFINITY) ? 0.0f : mx * LOG2E;
+    const float sum = wave_sum64(ex2(fmaf(part.x, LOG2E, -mo)));
+    part.x = (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx + lg2(sum) * LN2;
+  }
+  if (role == RO_BONUS) {
+    float sc = part.y, aux = part.w;
+    int ix = __float_as_int(part.z);
+    wave_argmax64(sc, ix, aux);
+    part.y = sc;
+    part.z = __int_as_float(ix);
+    part.w = aux;
   }
   if (lane == 0) p.part_plain[(size_t)pslot * p.nrB + range] = part;
 }
