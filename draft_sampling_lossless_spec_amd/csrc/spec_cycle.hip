@@ -908,9 +908,10 @@ __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& l
   if (!last && g0 + nx.k * SUB >= ls.c0) tile_issue(p, s, bias_list, g0, nx, true, Tt);
 }
 
-template <int NOISE>
+// `between` runs after every FAST_DEPTH units of a wave (the fused kernel puts one plain item there)
+template <int NOISE, typename Between>
 __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const uint16_t* bias_list, const ReqMeta* req,
-                                uint16_t* sA, int G) {
+                                uint16_t* sA, int G, Between& between) {
   const int nslots = ls.n_sb * SUB;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
   if (p.R < MAX_R) {
@@ -950,6 +951,7 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
             is = upos_next(is, nsbg, u1);
           }
         }
+        between();
       }
     }
     __syncthreads();   // every wave is done with sA
@@ -1189,27 +1191,57 @@ __global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s, int G) {
   uint16_t* sA = (uint16_t*)(dyn_bias + (bias_dyn_bytes(p.B) + 15) / 16 * 16);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
   const Lists ls = build_lists<NOISE, NT>(p, s, roles, bias_list, plain_list, scan_tmp, req, true);
-  if (ls.n_draft + ls.n_correct > 0) bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, sA, G);
-  // plain items: each wave keeps PLAIN_DEPTH items' loads in flight
+  // Plain items of this workgroup, wave w taking items i0 + w, i0 + w + 4, ...: one after every pair of
+  // bias units (its row loads issued a pair of units earlier, so their latency passes under the bias
+  // work), the rest afterwards with PLAIN_DEPTH items' loads in flight.  Item positions (plain slot,
+  // 4096-column range) are wave-uniform and stepped without division.
   const long long n_items = (long long)ls.n_plain * p.nrB;
   const int i0 = (int)(n_items * blockIdx.x / gridDim.x), i1 = (int)(n_items * (blockIdx.x + 1) / gridDim.x);
   constexpr int PLAIN_DEPTH = 3, STRIDE = NT / 64;
+  const int nrB = p.nrB;
+  auto advance = [nrB](int& sl, int& rg, int by) {
+    rg += by;
+    while (rg >= nrB) {
+      rg -= nrB;
+      sl++;
+    }
+  };
+  int pit = i0 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int psl = pit / nrB, prg = pit - (pit / nrB) * nrB;
+  PlainRaw<SPEC_BF16> pb;
+  if (pit < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[psl], prg, pb);
+  auto between = [&]() {
+    if (pit < i1) {
+      plain_finish<SPEC_BF16, NOISE>(p, s, plain_list[psl], psl, prg, pb);
+      pit += STRIDE;
+      advance(psl, prg, STRIDE);
+      if (pit < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[psl], prg, pb);
+    }
+  };
+  if (ls.n_draft + ls.n_correct > 0) bias_sweep_fast<NOISE>(p, s, ls, bias_list, req, sA, G, between);
   PlainRaw<SPEC_BF16> R[PLAIN_DEPTH];
-  const int first = i0 + (threadIdx.x >> 6);
+  int slot[PLAIN_DEPTH], rng[PLAIN_DEPTH];
+  R[0] = pb;
+  slot[0] = psl;
+  rng[0] = prg;
+  {
+    int sl = psl, rg = prg;
 #pragma unroll
-  for (int d = 0; d < PLAIN_DEPTH; d++) {
-    const int it = first + STRIDE * d;
-    if (it < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[it / p.nrB], it % p.nrB, R[d]);
+    for (int d = 1; d < PLAIN_DEPTH; d++) {
+      advance(sl, rg, STRIDE);
+      slot[d] = sl;
+      rng[d] = rg;
+      if (pit + STRIDE * d < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[sl], rg, R[d]);
+    }
   }
-  for (int it0 = first; it0 < i1; it0 += STRIDE * PLAIN_DEPTH) {
+  for (int it0 = pit; it0 < i1; it0 += STRIDE * PLAIN_DEPTH) {
 #pragma unroll
     for (int d = 0; d < PLAIN_DEPTH; d++) {
       const int it = it0 + STRIDE * d;
       if (it < i1) {
-        const int pslot = it / p.nrB;
-        plain_finish<SPEC_BF16, NOISE>(p, s, plain_list[pslot], pslot, it % p.nrB, R[d]);
-        const int nx = it + STRIDE * PLAIN_DEPTH;
-        if (nx < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[nx / p.nrB], nx % p.nrB, R[d]);
+        plain_finish<SPEC_BF16, NOISE>(p, s, plain_list[slot[d]], slot[d], rng[d], R[d]);
+        advance(slot[d], rng[d], STRIDE * PLAIN_DEPTH);
+        if (it + STRIDE * PLAIN_DEPTH < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[slot[d]], rng[d], R[d]);
       }
     }
   }
