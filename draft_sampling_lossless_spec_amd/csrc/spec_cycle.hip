@@ -329,7 +329,8 @@ __device__ __forceinline__ float4 empty_part() { return make_float4(-INFINITY, -
 
 
 // log-sum-exp of invT * y over n values held by a lane and its partner lane (lane ^ 32), invT > 0:
-// the scale is folded into the exponent argument, max(invT y) = invT max(y); NaN-preserving
+// the scale is folded into the exponent argument, max(invT y) = invT max(y).  Branch-free, so that
+// it schedules with independent work: every value -inf gives -inf, a NaN gives NaN.
 template <int N>
 __device__ __forceinline__ float pair_lse_scaled(const float* y, float invT) {
   // two max chains and four sum chains: independent partial results keep the pipeline busy
@@ -341,25 +342,19 @@ __device__ __forceinline__ float pair_lse_scaled(const float* y, float invT) {
   }
   float mx = fmaxf(m0, m1);
   mx = fmaxf(mx, xor32f(mx));
-  float sum;
-  if (mx != -INFINITY) {
-    const float c = invT * LOG2E, mo = mx * c;
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  // with no finite maximum the offset is 0: the terms are 0 (-inf) or NaN
+  const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < N; i += 4) {
-      s0 += ex2(fmaf(y[i], c, -mo));
-      s1 += ex2(fmaf(y[i + 1], c, -mo));
-      s2 += ex2(fmaf(y[i + 2], c, -mo));
-      s3 += ex2(fmaf(y[i + 3], c, -mo));
-    }
-    sum = (s0 + s1) + (s2 + s3);
-  } else {
-    sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < N; i++) sum += y[i];   // every value -inf or NaN: keep a NaN visible
+  for (int i = 0; i < N; i += 4) {
+    s0 += ex2(fmaf(y[i], c, -mo));
+    s1 += ex2(fmaf(y[i + 1], c, -mo));
+    s2 += ex2(fmaf(y[i + 2], c, -mo));
+    s3 += ex2(fmaf(y[i + 3], c, -mo));
   }
+  float sum = (s0 + s1) + (s2 + s3);
   sum += xor32f(sum);
-  return (mx == -INFINITY) ? sum : mx * invT + lg2(sum) * LN2;
+  return (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
 }
 
 // best (score, index, aux) of a lane and its partner lane
@@ -440,20 +435,21 @@ __device__ __forceinline__ void flat_best32(const float* y, float invT, int v0, 
 // steps; inactive rows return an empty part.
 template <int NOISE>
 __device__ __forceinline__ float4 draft_part(const float (&y)[32], const RowMeta& rm, int chunk, int v0, int V) {
-  const float lse = pair_lse_scaled<32>(y, rm.invT);
   float4 o = empty_part();
   if (NOISE == SPEC_NOISE_CHUNKED) {
-    if (rm.active) {
-      const float score = (lse > -INFINITY) ? lse + gumbel_bits(bits_at(rm.key, (uint32_t)chunk)) : lse;
-      o = make_float4(lse, score, __int_as_float(chunk), 0.0f);
-    }
-  } else {
-    float best = -INFINITY, bests = 0.0f;
-    int bestv = -1;
-    if (rm.active) flat_best32(y, rm.invT, v0, V, rm.key, best, bestv, bests);
-    pair_best(best, bestv, bests);
-    if (rm.active) o = make_float4(lse, best, __int_as_float(bestv), bests);
+    // the chunk's noise does not depend on the logits: computed first, it overlaps the log-sum-exp
+    const float g = gumbel_bits(bits_at(rm.key, (uint32_t)chunk));
+    const float lse = pair_lse_scaled<32>(y, rm.invT);
+    const float score = (lse > -INFINITY) ? lse + g : lse;
+    o = rm.active ? make_float4(lse, score, __int_as_float(chunk), 0.0f) : o;
+    return o;
   }
+  const float lse = pair_lse_scaled<32>(y, rm.invT);
+  float best = -INFINITY, bests = 0.0f;
+  int bestv = -1;
+  if (rm.active) flat_best32(y, rm.invT, v0, V, rm.key, best, bestv, bests);
+  pair_best(best, bestv, bests);
+  if (rm.active) o = make_float4(lse, best, __int_as_float(bestv), bests);
   return o;
 }
 
