@@ -681,14 +681,15 @@ __device__ void bias_sweep_generic(const Params& p, int s, const Lists& ls, cons
 
 // ---- fast sweep: bf16, 16-byte aligned rows, V % 8 == 0 ----
 // One workgroup of 4 waves per CU (one wave per SIMD, the full register file each).  The gathered
-// A rows of a group of up to 256 bias slots are staged in LDS once per step (one barrier per
-// group); after that every wave runs on its own: a unit is (noise chunk of 64 columns, sub-block of
-// 32 slots), the wave holds the chunk's W fragments in accumulation registers (128 of them for
-// R = 256), reads the sub-block's B operands from LDS, loads the draft / target logits straight into
-// registers in the accumulator layout two units ahead, and writes the chunk record of each row
-// directly to the partials.  The units of a group are split evenly over all waves of the grid in
-// chunk-major order, so a wave reloads W only when it crosses into the next chunk, and it issues
-// that reload right after the last MFMA chain on the old fragments.
+// A rows of the first bias slots (up to 288, as many as LDS holds) are staged in LDS once per step,
+// then one barrier; after that every wave runs on its own: a unit is (noise chunk of 64 columns,
+// sub-block of 32 slots), the wave holds the chunk's W fragments in accumulation registers (128 of
+// them for R = 256), reads the sub-block's B operands from LDS (from the A table for sub-blocks past
+// the staged ones), loads the draft / target logits straight into registers in the accumulator
+// layout two units ahead, and writes the chunk record of each row directly to the partials.  All
+// units of the step are split evenly over all waves of the grid in chunk-major order, so W streams
+// once per step, a wave reloads W only when it crosses into the next chunk, and it issues that
+// reload right after the last MFMA chain on the old fragments.
 
 // dynamic LDS of the bias-row sweeps: per-request table [B], then the bias and plain lists
 __host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
@@ -826,6 +827,16 @@ __device__ __forceinline__ void read_bop(const Params& p, const uint16_t* sA, in
 #pragma unroll
   for (int t = 0; t < 16; t++) bop[t] = *(const bf16x8*)(arow + 8 * t);
 }
+// the same B operands for a sub-block past the staged ones, straight from the A table (its rows are
+// hot in L2: every workgroup reads them); prev < 0 and the columns past the rank read zeros
+__device__ __forceinline__ void read_bop_global(const Params& p, int prev, bf16x8 (&bop)[16]) {
+  const int lane = threadIdx.x & 63;
+  const int T16 = p.R >> 4;
+  const uint16_t* ar = (const uint16_t*)p.A + (size_t)(prev >= 0 ? prev : 0) * p.R + (lane >> 5) * (p.R >> 1);
+#pragma unroll
+  for (int t = 0; t < 16; t++)
+    bop[t] = *((prev >= 0 && t < T16) ? (const bf16x8*)(ar + 8 * t) : (const bf16x8*)p.konst);
+}
 
 // One unit cur of the wave's span (nx = the unit after it, is = the unit FAST_DEPTH after it, both
 // clamped to the span) in a group of nsbg sub-blocks starting at slot g0.  Tcur holds cur's draft
@@ -836,14 +847,16 @@ __device__ __forceinline__ void read_bop(const Params& p, const uint16_t* sA, in
 // next loads.
 template <int NOISE>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
-                                          const ReqMeta* req, const uint16_t* sA, int g0, UPos cur, UPos nx, UPos is,
-                                          bool last, bf16x8 (&wf)[2][16], TileRegs& Tcur, TileRegs& Tt, RowMeta& rm) {
+                                          const ReqMeta* req, const uint16_t* sA, int kst, int g0, UPos cur, UPos nx,
+                                          UPos is, bool last, bf16x8 (&wf)[2][16], TileRegs& Tcur, TileRegs& Tt,
+                                          RowMeta& rm) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, h = lane >> 5;
   const int c = cur.c;
   const int slot0 = g0 + cur.k * SUB;
   bf16x8 bop[16];
-  read_bop(p, sA, cur.k, bop);
+  if (cur.k < kst) read_bop(p, sA, cur.k, bop);
+  else read_bop_global(p, rm.prev, bop);
   const RowMeta rn = row_meta(bias_list, req, s, g0 + nx.k * SUB + m);
   __builtin_amdgcn_sched_barrier(0);   // keep all reads ahead of the MFMA chain
   // the W fragments live in accumulation registers (the MFMA reads its A operand from there), which
@@ -918,9 +931,11 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
       *(u32x4*)&sA[(e / zc) * SA_STRIDE + p.R + 8 * (e % zc)] = (u32x4){0u, 0u, 0u, 0u};
   }
   const int gw = blockIdx.x * (NT / 64) + wave, nw = gridDim.x * (NT / 64);
-  for (int g0 = 0; g0 < nslots; g0 += G) {
-    const int nsbg = min(G, nslots - g0) / SUB;
-    stage_a(p, bias_list, req, g0, nsbg * SUB, sA);
+  // one pass over every sub-block, so W streams once per step: the A rows of the first G slots are
+  // staged in LDS, the sub-blocks past them read their B operands from the A table
+  {
+    const int g0 = 0, nsbg = ls.n_sb, kst = min(G, nslots) / SUB;
+    stage_a(p, bias_list, req, g0, kst * SUB, sA);
     __syncthreads();
     const long long units = (long long)p.nrA * nsbg;
     const int u0 = (int)(units * gw / nw), u1 = (int)(units * (gw + 1) / nw);
@@ -942,7 +957,7 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
         for (int d = 0; d < FAST_DEPTH; d++) {
           if (u + d < u1) {
             const UPos nx = upos_next(cur, nsbg, u1);
-            fast_unit<NOISE>(p, s, ls, bias_list, req, sA, g0, cur, nx, is, u + d + 1 == u1, wf, T[d], Tt, rm);
+            fast_unit<NOISE>(p, s, ls, bias_list, req, sA, kst, g0, cur, nx, is, u + d + 1 == u1, wf, T[d], Tt, rm);
             cur = nx;
             is = upos_next(is, nsbg, u1);
           }
@@ -950,7 +965,6 @@ __device__ void bias_sweep_fast(const Params& p, int s, const Lists& ls, const u
         between();
       }
     }
-    __syncthreads();   // every wave is done with sA
   }
 }
 
@@ -2380,9 +2394,10 @@ static int arch_ok() {
 // k_sweep_fast: A-row group of the step, the largest of 256 / 128 / 64 / 32 slots whose LDS fits
 // in the 160 KiB of a workgroup
 static int sweep_fast_group(int B) {
+  // the largest whole number of sub-blocks whose A rows fit in LDS (nine at B <= 256)
   const size_t cap = (size_t)160 * 1024 - sizeof(uint64_t) * (NT / 64);
-  int g = 8 * SUB;
-  while (g > SUB && fast_dyn_bytes(B, g) > cap) g /= 2;
+  int g = 16 * SUB;
+  while (g > SUB && fast_dyn_bytes(B, g) > cap) g -= SUB;
   return g;
 }
 
