@@ -47,7 +47,7 @@ SMALL = {
     # survive to late steps, full rank on the bf16 fast path
     "k32_max_positions": lambda: wl.generate(wl.small_config(B=8, K=32, V=3008, R=256, threshold=1e-6,
                                                               sigma=(0.3,))),
-    # the largest batch (1024 requests): A-row groups of 128 slots on the fast path, many sub-blocks
+    # the largest batch (1024 requests): 224 slots staged on the fast path, most sub-blocks past them
     "b1024_small_v": lambda: wl.generate(wl.small_config(B=1024, K=2, V=1024, R=32, threshold=0.05)),
 }
 
