@@ -1338,16 +1338,17 @@ __device__ __forceinline__ float4 pacc_final(const PartAcc& a) {
   return make_float4(lse, a.sc, __int_as_float(a.ix), a.aux);
 }
 
-// running record of every lane of a wave merged into every lane
+// running record of every lane of a wave merged into every lane.  The mass as one wave maximum, each
+// lane's sum rescaled to it (a lane at the maximum adds its sum as it is, a lane at -inf adds
+// nothing) and one wave sum; the NaN flag by ballot; the winner by the DPP argmax (the same take
+// rule as pacc_best).
 __device__ __forceinline__ void wave_reduce_acc(PartAcc& a) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(a.m, o, 64), s2 = __shfl_xor(a.s, o, 64);
-    const float sc2 = __shfl_xor(a.sc, o, 64), aux2 = __shfl_xor(a.aux, o, 64);
-    const int ix2 = __shfl_xor(a.ix, o, 64), nan2 = __shfl_xor(a.nan, o, 64);
-    pacc_mass(a, m2, s2, nan2);
-    pacc_best(a, sc2, ix2, aux2);
-  }
+  const float M = wave_max64(a.m);
+  const float sl = (a.m == M) ? a.s : ((a.m == -INFINITY) ? 0.0f : a.s * ex2((a.m - M) * LOG2E));
+  a.s = wave_sum64(sl);
+  a.m = M;
+  a.nan = __ballot(a.nan != 0) != 0ull;
+  wave_argmax64(a.sc, a.ix, a.aux);
 }
 
 // records per row and thread in one round of the merge's partial reduction
