@@ -1464,7 +1464,7 @@ __device__ L2Result level_two(const Params& p, const L2Job& jb, int gt, float4* 
   const float tvr = need_targ ? load1<DT>(jb.targ_row, (size_t)v) : 0.0f;
   float bias = 0.0f;
   if (in && jb.kind != L2_TARGET) bias = bias_half<DT>(p, jb.prev, v, hh);
-  bias += __shfl_xor(bias, 1, 64);
+  bias += dpp<0xB1>(bias);   // the partner lane (xor 1) holds the other half
   float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
   int ix = -1;
   if (in && hh == 0) {
@@ -1493,17 +1493,14 @@ __device__ L2Result level_two(const Params& p, const L2Job& jb, int gt, float4* 
       }
     }
   }
-  // argmax over the group's 2 waves, smallest index on ties; sx and tx ride along
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float s2 = __shfl_xor(sc, o, 64), x2 = __shfl_xor(sx, o, 64), t2 = __shfl_xor(tx, o, 64);
-    const int i2 = __shfl_xor(ix, o, 64);
-    if (i2 >= 0 && (ix < 0 || better(s2, i2, sc, ix))) {
-      sc = s2;
-      ix = i2;
-      sx = x2;
-      tx = t2;
-    }
+  // argmax over the wave by DPP (larger score, smallest index on ties), sx riding along; tx is read
+  // from the winner's lane, the only one holding that column
+  const int ix0 = ix;
+  const float tx0 = tx;
+  wave_argmax64(sc, ix, sx);
+  {
+    const unsigned long long wm = __ballot(ix >= 0 && ix0 == ix);
+    tx = __shfl(tx0, wm ? __ffsll(wm) - 1 : 0, 64);
   }
   const int wv = (gt >> 6) & 1;
   if ((gt & 63) == 0) lds2[wv] = make_float4(sc, sx, __int_as_float(ix), tx);
