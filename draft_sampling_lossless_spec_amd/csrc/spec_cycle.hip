@@ -696,7 +696,7 @@ __host__ __device__ constexpr size_t bias_dyn_bytes(int B) {
   return (size_t)B * sizeof(ReqMeta) + (size_t)(bias_slots_max(B) + B) * sizeof(uint16_t);
 }
 constexpr int SA_STRIDE = MAX_R + A_PAD;   // bf16 elements per staged A row
-// dynamic LDS of k_sweep_fast with A-row groups of g slots
+// dynamic LDS of k_sweep_fast with the A rows of g slots staged
 __host__ __device__ constexpr size_t fast_dyn_bytes(int B, int g) {
   return (bias_dyn_bytes(B) + 15) / 16 * 16 + (size_t)g * SA_STRIDE * sizeof(uint16_t);
 }
@@ -839,12 +839,12 @@ __device__ __forceinline__ void read_bop_global(const Params& p, int prev, bf16x
 }
 
 // One unit cur of the wave's span (nx = the unit after it, is = the unit FAST_DEPTH after it, both
-// clamped to the span) in a group of nsbg sub-blocks starting at slot g0.  Tcur holds cur's draft
-// tiles and receives is's; Tt holds cur's target tiles if cur is a CORRECT unit and receives nx's if
-// that one is; rm holds cur's row meta and leaves with nx's.  Order: B operands and the next row
-// meta from LDS, the draft tile unpacked into the accumulators (while those reads land); the MFMA
-// chain; the next chunk's W fragments if the chunk changes; the element-wise part; the records; the
-// next loads.
+// clamped to the span) over nsbg sub-blocks starting at slot g0, the first kst of them staged in LDS.
+// Tcur holds cur's draft tiles and receives is's; Tt holds cur's target tiles if cur is a CORRECT
+// unit and receives nx's if that one is; rm holds cur's row meta and leaves with nx's.  Order: B
+// operands (from LDS, or from the A table past the staged sub-blocks) and the next row meta, the
+// draft tile unpacked into the accumulators (while those reads land); the MFMA chain; the next
+// chunk's W fragments if the chunk changes; the element-wise part; the records; the next loads.
 template <int NOISE>
 __device__ __forceinline__ void fast_unit(const Params& p, int s, const Lists& ls, const uint16_t* bias_list,
                                           const ReqMeta* req, const uint16_t* sA, int kst, int g0, UPos cur, UPos nx,
@@ -2389,10 +2389,9 @@ static int arch_ok() {
   return ok > 0 ? SPEC_OK : SPEC_E_ARCH;
 }
 
-// k_sweep_fast: A-row group of the step, the largest of 256 / 128 / 64 / 32 slots whose LDS fits
-// in the 160 KiB of a workgroup
+// k_sweep_fast: bias slots whose A rows are staged in LDS, the largest whole number of sub-blocks
+// that fits next to the per-request table in the 160 KiB of a workgroup (nine at B <= 256)
 static int sweep_fast_group(int B) {
-  // the largest whole number of sub-blocks whose A rows fit in LDS (nine at B <= 256)
   const size_t cap = (size_t)160 * 1024 - sizeof(uint64_t) * (NT / 64);
   int g = 16 * SUB;
   while (g > SUB && fast_dyn_bytes(B, g) > cap) g -= SUB;
