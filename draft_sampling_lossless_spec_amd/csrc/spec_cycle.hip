@@ -1080,8 +1080,10 @@ __device__ __forceinline__ void plain_load(const Params& p, int s, int b, int ra
   }
 }
 
-// the log-mass (and for a BONUS row the Gumbel winner) of one plain item from its loaded pieces
-template <int DT, int NOISE>
+// the log-mass (and for a BONUS row the Gumbel winner) of one plain item from its loaded pieces.
+// DIRECT: an LSEP item's log-mass in one pass over the item instead of chunk by chunk (fewer
+// instructions, more live registers: only where the register file allows it)
+template <int DT, int NOISE, bool DIRECT = false>
 __device__ __forceinline__ void plain_finish(const Params& p, int s, int b, int pslot, int range,
                                              const PlainRaw<DT>& R) {
   const int V = p.V;
@@ -1094,6 +1096,35 @@ __device__ __forceinline__ void plain_finish(const Params& p, int s, int b, int 
   const Raw8<DT>* r = R.r;
   const uint64_t g = (uint64_t)(p.req_off + b);
   const float sc2 = invT * LOG2E;
+  if (DIRECT && role != RO_BONUS) {
+    // LSEP: only the item's log-mass is needed, as one maximum and one scaled sum over the lane's 64
+    // values and then over the wave (with a finite maximum the plain scaled sum; every value -inf
+    // gives -inf, a NaN gives NaN)
+    float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KB_LOADS; k++)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        m0 = fmaxf(m0, raw8_at<DT>(r[k], i));
+        m1 = fmaxf(m1, raw8_at<DT>(r[k], i + 1));
+      }
+    const float mx = wave_max64(fmaxf(m0, m1));
+    const float mo = (mx == -INFINITY) ? 0.0f : mx * sc2;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KB_LOADS; k++)
+#pragma unroll
+      for (int i = 0; i < 8; i += 4) {
+        s0 += ex2(fmaf(raw8_at<DT>(r[k], i), sc2, -mo));
+        s1 += ex2(fmaf(raw8_at<DT>(r[k], i + 1), sc2, -mo));
+        s2 += ex2(fmaf(raw8_at<DT>(r[k], i + 2), sc2, -mo));
+        s3 += ex2(fmaf(raw8_at<DT>(r[k], i + 3), sc2, -mo));
+      }
+    const float sum = wave_sum64((s0 + s1) + (s2 + s3));
+    const float lse = (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
+    if (lane == 0) p.part_plain[(size_t)pslot * p.nrB + range] = make_float4(lse, -INFINITY, __int_as_float(-1), 0.0f);
+    return;
+  }
   // log-mass of each 64-column chunk (8 lanes x 8 values).  The rounds are independent and written
   // without branches, so that they interleave: with a finite maximum the arithmetic is the plain
   // scaled sum; every value -inf gives -inf, and a NaN among -inf values gives NaN.
@@ -1222,7 +1253,7 @@ __global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s, int G) {
   if (pit < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[psl], prg, pb);
   auto between = [&]() {
     if (pit < i1) {
-      plain_finish<SPEC_BF16, NOISE>(p, s, plain_list[psl], psl, prg, pb);
+      plain_finish<SPEC_BF16, NOISE, true>(p, s, plain_list[psl], psl, prg, pb);
       pit += STRIDE;
       advance(psl, prg, STRIDE);
       if (pit < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[psl], prg, pb);
@@ -1249,7 +1280,7 @@ __global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s, int G) {
     for (int d = 0; d < PLAIN_DEPTH; d++) {
       const int it = it0 + STRIDE * d;
       if (it < i1) {
-        plain_finish<SPEC_BF16, NOISE>(p, s, plain_list[slot[d]], slot[d], rng[d], R[d]);
+        plain_finish<SPEC_BF16, NOISE, true>(p, s, plain_list[slot[d]], slot[d], rng[d], R[d]);
         advance(slot[d], rng[d], STRIDE * PLAIN_DEPTH);
         if (it + STRIDE * PLAIN_DEPTH < i1) plain_load<SPEC_BF16, true>(p, s, plain_list[slot[d]], rng[d], R[d]);
       }
