@@ -1238,7 +1238,7 @@ __global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s, int G) {
   // 4096-column range) are wave-uniform and stepped without division.
   const long long n_items = (long long)ls.n_plain * p.nrB;
   const int i0 = (int)(n_items * blockIdx.x / gridDim.x), i1 = (int)(n_items * (blockIdx.x + 1) / gridDim.x);
-  constexpr int PLAIN_DEPTH = 3, STRIDE = NT / 64;
+  constexpr int PLAIN_DEPTH = 2, STRIDE = NT / 64;   // 2 measured as fast as 1, 3 and 4 slower
   const int nrB = p.nrB;
   auto advance = [nrB](int& sl, int& rg, int by) {
     rg += by;
