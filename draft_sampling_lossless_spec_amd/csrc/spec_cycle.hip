@@ -78,6 +78,9 @@ struct Params {
   int32_t* acc;
   int32_t* phase;
   uint8_t* roles;      // [2][B], step parity
+  int32_t* live;       // [K + 2]: nonzero when some request has a row at step s (step 0 always; later
+                       // steps set by the merge of the step before); the step kernels of a step with
+                       // none return at once, and its stale role bytes are never read
   int32_t* slots;      // [3][B]: bias slot of DRAFT row, bias slot of CORRECT row, plain slot
   int32_t* xs;         // [B][K]
   uint64_t* kreq;      // [B] noise-key prefix of each request: first(first(seed) ^ global id)
@@ -142,6 +145,7 @@ __global__ void k_init(Params p) {
     const uint32_t w = threadIdx.x ? 0xFF80FF80u : 0u;
     ((u32x4*)p.konst)[threadIdx.x] = (u32x4){w, w, w, w};
   }
+  if (blockIdx.x == 0 && (int)threadIdx.x < p.K + 2) p.live[threadIdx.x] = (threadIdx.x == 0) ? 1 : 0;
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= p.B) return;
   const int K = p.K;
@@ -1226,6 +1230,7 @@ template <int NOISE>
 __global__ __launch_bounds__(NT, 1) void k_sweep_fast(Params p, int s, int G) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
   __shared__ uint64_t scan_tmp[NT / 64];
+  if (p.live[s] == 0) return;
   ReqMeta* req = (ReqMeta*)dyn_bias;
   uint16_t* bias_list = (uint16_t*)(dyn_bias + (size_t)p.B * sizeof(ReqMeta));
   uint16_t* plain_list = bias_list + bias_slots_max(p.B);
@@ -1293,6 +1298,7 @@ __global__ __launch_bounds__(NT, 1) void k_bias(Params p, int s) {
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_bias[];
   __shared__ uint64_t scan_tmp[NT / 64];
   __shared__ GenericLds lds_g;
+  if (p.live[s] == 0) return;
   ReqMeta* req = (ReqMeta*)dyn_bias;
   uint16_t* bias_list = (uint16_t*)(dyn_bias + (size_t)p.B * sizeof(ReqMeta));
   uint16_t* plain_list = bias_list + bias_slots_max(p.B);
@@ -1306,6 +1312,7 @@ template <int DT, int NOISE, bool VEC>
 __global__ __launch_bounds__(NT, 6) void k_plain(Params p, int s) {
   extern __shared__ uint16_t dyn_lists[];
   __shared__ uint64_t scan_tmp[NT / 64];
+  if (p.live[s] == 0) return;
   uint16_t* bias_list = dyn_lists;
   uint16_t* plain_list = dyn_lists + bias_slots_max(p.B);
   const uint8_t* roles = p.roles + (size_t)(s & 1) * p.B;
@@ -1553,6 +1560,7 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
   __shared__ float4 lds2[2][2];
   const int b = blockIdx.x;
   const int B = p.B, K = p.K, V = p.V;
+  if (p.live[s] == 0) return;
   // round 0: every per-request value that depends only on (b, s), loaded together with the roles
   const int roles = p.roles[(size_t)(s & 1) * B + b];
   const float invT = 1.0f / p.temp[b];
@@ -1783,6 +1791,7 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
     p.phase[b] = phase;
     p.acc[b] = acc;
     roles_next[b] = (uint8_t)nr;
+    if (nr) p.live[s + 1] = 1;
   }
 }
 
@@ -2342,7 +2351,7 @@ __global__ __launch_bounds__(NT) void k_advance(const int32_t* tokens, const int
 
 struct Layout {
   size_t off_L, off_acc, off_phase, off_roles, off_slots, off_xs, off_kreq, off_lse_q, off_logq, off_lse_p, off_logp,
-      off_pbias, off_pbias2, off_pplain, off_konst, total;
+      off_pbias, off_pbias2, off_pplain, off_konst, off_live, total;
   int nrA, nrB, gridB;
 };
 
@@ -2386,6 +2395,7 @@ static Layout layout(const spec_dims* d) {
   l.off_pbias2 = o; o = align256(o + 16 * nslots * (size_t)l.nrA);
   l.off_pplain = o; o = align256(o + 16 * B * (size_t)l.nrB);
   l.off_konst = o; o = align256(o + 32);
+  l.off_live = o; o = align256(o + 4 * (K + 2));
   l.total = o;
   return l;
 }
@@ -2543,6 +2553,7 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
   p.acc = (int32_t*)(ws + l.off_acc);
   p.phase = (int32_t*)(ws + l.off_phase);
   p.roles = (uint8_t*)(ws + l.off_roles);
+  p.live = (int32_t*)(ws + l.off_live);
   p.slots = (int32_t*)(ws + l.off_slots);
   p.xs = (int32_t*)(ws + l.off_xs);
   p.kreq = (uint64_t*)(ws + l.off_kreq);
