@@ -5,9 +5,11 @@ verification, correction / bonus) over one batch of synthetic inputs already res
 Default workload: the 16-position long-block cycle, B=256, K=16, V=151936, rank 256, bf16.
 
 Prints one JSON line: throughput in verified draft tokens/s (sum of per-request verify lengths
-per second), the roofline of the dominant kernel (the per-step row sweep) from HIP events
-attached to its dispatches inside the timed region, and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+per second, wall clock of back-to-back cycles), the per-cycle p10/p50/p90 and the same with the
+last-level cache flushed between cycles, the roofline of the dominant kernel from HIP events
+attached to its dispatches, the fp64 CPU oracle on the whole batch (all host threads, plus one
+thread on a sample) with the parity counts of the GPU's first cycle against it, and the same
+figures for the other four synthetic workloads under `configs`.
 """
 import argparse
 import ctypes as C
@@ -66,66 +68,43 @@ def measured_traffic(kernel, workload, noise):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="longblock")
-    ap.add_argument("--threshold", type=float, default=None)
-    ap.add_argument("--noise", choices=["chunked", "flat"], default="chunked")
-    ap.add_argument("--cpu-requests", type=int, default=0,
-                    help="requests in the oracle's timed sample (0 = the whole batch of one cycle)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stats", action="store_true",
-                    help="measure the acceptance-statistics call (alpha = 1 - TV per drafted position) on the drafts "
-                         "of one cycle of the workload instead of the cycle itself; prints its own JSON line")
-    ap.add_argument("--schedule", action="store_true",
-                    help="measure the prefix scheduler on the workload's confidences against a synthetic target "
-                         "step-time curve at several loads; prints its own JSON line")
-    ap.add_argument("--sts", action="store_true",
-                    help="measure sequential temperature scaling on synthetic held-out confidences (an "
-                         "overconfident head); prints its own JSON line")
-    ap.add_argument("--decode", type=int, default=0,
-                    help="chain this many scheduled cycles (scheduler, cycle, next context, all on the device) over "
-                         "two alternating row sets and report tokens per cycle and the modelled latency per token")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
-                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
-    args = ap.parse_args()
-    if args.copy_bytes > 0:
-        import torch
-        n = args.copy_bytes // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n * 4, "copies": 5}), flush=True)
-        return
-    if args.stats:
-        return bench_stats(args)
-    if args.schedule:
-        return bench_schedule(args)
-    if args.sts:
-        return bench_sts(args)
-    if args.decode > 0:
-        return bench_decode(args)
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
-              "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def pct(x, q):
+    return float(np.percentile(np.asarray(x, dtype=np.float64), q))
+
+
+def parity_counts(orc, diag):
+    """The oracle's outputs against the GPU's first cycle under the parity rule of the tests."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import compare
+    rep = compare(orc, diag)
+    return {"requests": rep.requests, "matched": rep.matched, "excused": rep.excused,
+            "failures": len(rep.failures), "decisions": rep.decisions, "near_ties": rep.near_ties,
+            "near_tie_rate": rep.near_tie_rate, "max_prob_err": rep.max_prob_err,
+            "first_failures": rep.failures[:3]}
+
+
+def measure(name, threshold, steps, warmup, noise, with_oracle, flush_only=False, seed=1, events=True):
+    """One workload: timed cycles (back to back and with the cache flushed between cycles), the
+    dominant kernel's event-timed launches, and the oracle beside it with the parity counts of the
+    first cycle.  Returns (summary dict, diagnostics for the main line)."""
     import torch
-    from draft_sampling_lossless_spec_amd import CHUNKED, FLAT, spec_cycle, spec_cycle_kernel_count, spec_workspace_bytes
+    from draft_sampling_lossless_spec_amd import CHUNKED, spec_cycle, spec_cycle_kernel_count, spec_workspace_bytes
     from draft_sampling_lossless_spec_amd import workloads as wl
 
-    noise = CHUNKED if args.noise == "chunked" else FLAT
     t0 = time.time()
-    w = wl.generate(args.config, threshold=args.threshold)
+    w = wl.generate(name, gen_seed=seed, cycle_seed=seed, threshold=threshold)
     cfg = w.cfg
-    print(f"[bench] generated {args.config} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    print(f"[bench] {name} thr={w.threshold}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
 
     def t(a):
@@ -141,139 +120,253 @@ def main():
            "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
     run = lambda **kw: spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise,
                                   workspace=ws, out=out, **kw)
-    diag = spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise, workspace=ws,
-                      diag=True)
+    dg = spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise, workspace=ws,
+                    diag=True)
     torch.cuda.synchronize()
-    L = diag["verify_len"].cpu().numpy()
-    a = diag["accepted_len"].cpu().numpy()
+    diag = {k: v.cpu().numpy() for k, v in dg.items()}
+    L, a = diag["verify_len"], diag["accepted_len"]
     assert np.all(a >= 0), "synthetic workload produced invalid requests"
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    res = {"B": B, "K": K, "V": cfg.V, "R": cfg.R, "threshold": w.threshold, "sum_verify_len": int(L.sum()),
+           "sum_emitted": int((a + 1).sum()), "max_verify_len": int(L.max())}
+    cb = compulsory_bytes(cfg, L, a)
+    res["compulsory_bytes"] = cb
 
-    # the timed region: plain calls, nothing attached to the dispatches
-    torch.cuda.synchronize()
-    ts = time.perf_counter()
-    for i in range(args.steps):
+    ms = None
+    if not flush_only:
+        # back to back: the wall clock of `steps` plain calls is the figure; an event pair between
+        # calls gives the per-cycle spread
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ts = time.perf_counter()
+        evs[0].record()
+        for i in range(steps):
+            run()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - ts) * 1e3 / steps
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        res.update({"us_per_cycle": ms * 1e3, "p10_us": pct(per, 10) * 1e3, "p50_us": pct(per, 50) * 1e3,
+                    "p90_us": pct(per, 90) * 1e3, "value": int(L.sum()) / (ms * 1e-3),
+                    "hbm_frac_cycle": cb / (ms * 1e-3) / HBM_PEAK})
+    # flushed: a 1 GiB write between cycles evicts the 256 MB last-level cache; only the cycle is timed
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    fl = []
+    for i in range(steps):
+        scratch.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         run()
-    torch.cuda.synchronize()
-    te = time.perf_counter()
-    ms_per_step = (te - ts) * 1e3 / args.steps
+        e1.record()
+        e1.synchronize()
+        fl.append(e0.elapsed_time(e1))
+    del scratch
+    res.update({"flushed_p10_us": pct(fl, 10) * 1e3, "flushed_p50_us": pct(fl, 50) * 1e3,
+                "flushed_p90_us": pct(fl, 90) * 1e3,
+                "flushed_value": int(L.sum()) / (pct(fl, 50) * 1e-3),
+                "flushed_hbm_frac_cycle": cb / (pct(fl, 50) * 1e-3) / HBM_PEAK})
 
-    # kernel breakdown: the same number of cycles again, with start/stop events attached to every
-    # kernel dispatch
-    hip = hip_runtime()
-    nk = spec_cycle_kernel_count(K)
-    ev = [(C.c_void_p * (2 * nk))() for _ in range(args.steps)]
-    for arr in ev:
-        for i in range(2 * nk):
-            h = C.c_void_p()
-            assert hip.hipEventCreate(C.byref(h)) == 0
-            arr[i] = h.value
-    torch.cuda.synchronize()
-    tse = time.perf_counter()
-    for i in range(args.steps):
-        run(_events=ev[i])
-    torch.cuda.synchronize()
-    ms_timed = (time.perf_counter() - tse) * 1e3 / args.steps
+    kern = None
+    if events:
+        # start/stop events attached to every kernel dispatch of the cycle (same work, own pass)
+        hip = hip_runtime()
+        nk = spec_cycle_kernel_count(K)
+        nrep = max(3, min(steps, 10))
+        ev = [(C.c_void_p * (2 * nk))() for _ in range(nrep)]
+        for arr in ev:
+            for i in range(2 * nk):
+                h = C.c_void_p()
+                assert hip.hipEventCreate(C.byref(h)) == 0
+                arr[i] = h.value
+        torch.cuda.synchronize()
+        for i in range(nrep):
+            run(_events=ev[i])
+        torch.cuda.synchronize()
 
-    def el(e0, e1):
-        f = C.c_float()
-        assert hip.hipEventElapsedTime(C.byref(f), C.c_void_p(e0), C.c_void_p(e1)) == 0
-        return f.value
+        def el(e0, e1):
+            f = C.c_float()
+            assert hip.hipEventElapsedTime(C.byref(f), C.c_void_p(e0), C.c_void_p(e1)) == 0
+            return f.value
 
-    # kernel i: 0 = init; 1 + 3s / 2 + 3s / 3 + 3s = bias-row sweep / plain-row sweep / merge of step s
-    kb = np.zeros((args.steps, K + 1))
-    kp = np.zeros((args.steps, K + 1))
-    km = np.zeros((args.steps, K + 1))
-    init = np.zeros(args.steps)
-    span = np.zeros(args.steps)
-    for i, arr in enumerate(ev):
-        init[i] = el(arr[0], arr[1])
-        for s in range(K + 1):
-            k0 = 1 + 3 * s
-            kb[i, s] = el(arr[2 * k0], arr[2 * k0 + 1])
-            kp[i, s] = el(arr[2 * (k0 + 1)], arr[2 * (k0 + 1) + 1])
-            km[i, s] = el(arr[2 * (k0 + 2)], arr[2 * (k0 + 2) + 1])
-        span[i] = el(arr[0], arr[2 * nk - 1])
-    for arr in ev:
-        for i in range(2 * nk):
-            hip.hipEventDestroy(C.c_void_p(arr[i]))
+        d = np.array([[el(arr[2 * k], arr[2 * k + 1]) for k in range(nk)] for arr in ev])   # ms [rep, kernel]
+        for arr in ev:
+            for i in range(2 * nk):
+                hip.hipEventDestroy(C.c_void_p(arr[i]))
+        kern = kernel_breakdown(cfg, L, a, d, nk)
+        res["kernels"] = {k: {kk: vv for kk, vv in v.items() if kk != "per_step_us"} for k, v in kern.items()}
 
-    sL = int(L.sum())
-    sa1 = int((a + 1).sum())
+    if with_oracle:
+        import oracle
+        tc = time.perf_counter()
+        r = oracle.spec_cycle_ref(w.base, w.target, w.A, w.W, w.x0, w.conf, w.temp, w.threshold, w.seed,
+                                  noise=noise)
+        dt = time.perf_counter() - tc
+        res["oracle"] = {"seconds": dt, "threads": oracle.max_threads(),
+                         "value": float(r["verify_len"][r["verify_len"] > 0].sum() / dt)}
+        res["parity"] = parity_counts(r, diag)
+    return res, (w, cfg, L, a, kern)
+
+
+def kernel_breakdown(cfg, L, a, d, nk):
+    """Per-kernel times (us per cycle) from the event-timed pass, and the algorithmic bytes of the
+    kernels that stream rows.  d: [repetitions, dispatch] milliseconds."""
     e = 2 if cfg.dtype == 1 else 4
-    cbytes = compulsory_bytes(cfg, L, a)
+    sL, sa1 = int(L.sum()), int((a + 1).sum())
     bias_bytes = e * cfg.V * sL + e * cfg.R * cfg.V + e * cfg.R * sL      # draft rows, W once, gathered A rows
     plain_bytes = e * cfg.V * sa1                                        # decided target rows + bonus rows
-    t_cycle = ms_per_step * 1e-3
-    value = sL / t_cycle
-    kb_ms, kp_ms, km_ms = (float(x.sum(axis=1).mean()) for x in (kb, kp, km))
-    n_active = int(L.max()) + 1
-    if cfg.dtype == 1 and cfg.V % 8 == 0:
-        # bf16 vector path: the plain rows run inside the sweep kernel (the plain slot's event pair
-        # brackets nothing but the events themselves)
-        sweep_bytes = bias_bytes + plain_bytes
-        kernels = {
-            "k_sweep": {"us_per_cycle": kb_ms * 1e3, "algorithmic_bytes": sweep_bytes,
-                        "achieved_GBps": sweep_bytes / (kb_ms * 1e-3) / 1e9},
-            "k_merge": {"us_per_cycle": km_ms * 1e3},
-            "k_init": {"us_per_cycle": float(init.mean()) * 1e3},
-        }
-        dom = "k_sweep"
-    else:
-        kernels = {
-            "k_bias": {"us_per_cycle": kb_ms * 1e3, "algorithmic_bytes": bias_bytes,
-                       "achieved_GBps": bias_bytes / (kb_ms * 1e-3) / 1e9},
-            "k_plain": {"us_per_cycle": kp_ms * 1e3, "algorithmic_bytes": plain_bytes,
-                        "achieved_GBps": plain_bytes / (kp_ms * 1e-3) / 1e9},
-            "k_merge": {"us_per_cycle": km_ms * 1e3},
-            "k_init": {"us_per_cycle": float(init.mean()) * 1e3},
-        }
-        dom = max(("k_bias", "k_plain"), key=lambda k: kernels[k]["us_per_cycle"])
-    achieved = kernels[dom]["achieved_GBps"] * 1e9
-    print(f"[bench] sum L={sL} sum(a+1)={sa1} max L={int(L.max())} compulsory={cbytes / 1e6:.1f} MB",
-          file=sys.stderr)
+    mean = d.mean(axis=0) * 1e3                                          # us per dispatch
+    if nk == 1:
+        # one persistent launch runs the whole cycle
+        cb = compulsory_bytes(cfg, L, a)
+        return {"k_cycle": {"us_per_cycle": float(mean[0]), "algorithmic_bytes": cb, "launches_per_cycle": 1,
+                            "achieved_GBps": cb / (mean[0] * 1e-6) / 1e9}}
+    K = cfg.K
+    steps = np.arange(K + 1)
+    kb, kp, km = mean[1 + 3 * steps], mean[2 + 3 * steps], mean[3 + 3 * steps]
     fused = cfg.dtype == 1 and cfg.V % 8 == 0
-    # on the fused path the plain rows run inside the sweep; their event slot brackets no kernel
-    plain_txt = "inside the sweep" if fused else f"{kp_ms * 1e3:.1f} us"
-    print(f"[bench] wall {ms_per_step * 1e3:.1f} us/cycle ({ms_timed * 1e3:.1f} with events); event span "
-          f"{span.mean() * 1e3:.1f} us; init "
-          f"{init.mean() * 1e3:.1f} us; sweep {kb_ms * 1e3:.1f} us; plain {plain_txt}; merge {km_ms * 1e3:.1f} us",
-          file=sys.stderr)
-    rows = (("sweep", kb), ("merge", km)) if fused else (("sweep", kb), ("plain", kp), ("merge", km))
-    for name, arr_ in rows:
-        print(f"[bench] per-step {name} us: " + " ".join(f"{x * 1e3:.1f}" for x in arr_.mean(axis=0)), file=sys.stderr)
+    out = {"k_init": {"us_per_cycle": float(mean[0]), "launches_per_cycle": 1}}
+    if fused:
+        sb = bias_bytes + plain_bytes
+        out["k_sweep"] = {"us_per_cycle": float(kb.sum()), "algorithmic_bytes": sb, "launches_per_cycle": K + 1,
+                          "achieved_GBps": sb / (kb.sum() * 1e-6) / 1e9, "per_step_us": kb.tolist()}
+    else:
+        out["k_bias"] = {"us_per_cycle": float(kb.sum()), "algorithmic_bytes": bias_bytes,
+                         "launches_per_cycle": K + 1, "achieved_GBps": bias_bytes / (kb.sum() * 1e-6) / 1e9}
+        out["k_plain"] = {"us_per_cycle": float(kp.sum()), "algorithmic_bytes": plain_bytes,
+                          "launches_per_cycle": K + 1, "achieved_GBps": plain_bytes / (kp.sum() * 1e-6) / 1e9}
+    out["k_merge"] = {"us_per_cycle": float(km.sum()), "launches_per_cycle": K + 1, "per_step_us": km.tolist()}
+    return out
+
+
+# the five synthetic workloads; the long-block one is the headline line, the others go into `configs`
+OTHER_CONFIGS = [("tiny", None), ("dspark5", None), ("highconc", 0.05), ("highconc", 0.2), ("highconc", 0.5),
+                 ("highconc", 0.8), ("mixed", None)]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="longblock")
+    ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--noise", choices=["chunked", "flat"], default="chunked")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only (no `configs`)")
+    ap.add_argument("--cpu-sample", type=int, default=16,
+                    help="requests in the single-threaded oracle sample of the headline workload")
+    ap.add_argument("--stats", action="store_true",
+                    help="measure the acceptance-statistics call (alpha = 1 - TV per drafted position) on the drafts "
+                         "of one cycle of the workload instead of the cycle itself; prints its own JSON line")
+    ap.add_argument("--schedule", action="store_true",
+                    help="measure the prefix scheduler on the workload's confidences against a synthetic target "
+                         "step-time curve at several loads; prints its own JSON line")
+    ap.add_argument("--sts", action="store_true",
+                    help="measure sequential temperature scaling on synthetic held-out confidences (an "
+                         "overconfident head); prints its own JSON line")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="chain this many scheduled cycles (scheduler, cycle, next context, all on the device) over "
+                         "two alternating row sets and report tokens per cycle and the modelled latency per token")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many bytes (5 times) and exit: the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+    ap.add_argument("--cpu-requests", type=int, default=0,
+                    help="(--stats) requests in the oracle's timed sample (0 = the whole batch)")
+    args = ap.parse_args()
+    if args.copy_bytes > 0:
+        import torch
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": 5}), flush=True)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requests shard with "
+              "request_offset and no collective; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.stats:
+        return bench_stats(args)
+    if args.schedule:
+        return bench_schedule(args)
+    if args.sts:
+        return bench_sts(args)
+    if args.decode > 0:
+        return bench_decode(args)
+
+    from draft_sampling_lossless_spec_amd import CHUNKED, FLAT
+    noise = CHUNKED if args.noise == "chunked" else FLAT
+    with_oracle = not args.no_cpu_baseline
+    res, (w, cfg, L, a, kern) = measure(args.config, args.threshold, args.steps, args.warmup, noise, with_oracle)
+    ms_per_step = res["us_per_cycle"] * 1e-3
+    print(f"[bench] {args.config}: sum L={res['sum_verify_len']} sum(a+1)={res['sum_emitted']} "
+          f"max L={res['max_verify_len']} compulsory={res['compulsory_bytes'] / 1e6:.1f} MB; wall "
+          f"{res['us_per_cycle']:.1f} us/cycle (p10/p50/p90 {res['p10_us']:.1f}/{res['p50_us']:.1f}/"
+          f"{res['p90_us']:.1f}); flushed p50 {res['flushed_p50_us']:.1f} us", file=sys.stderr, flush=True)
+    for k, v in kern.items():
+        extra = f" per-step {' '.join(f'{x:.1f}' for x in v['per_step_us'])}" if "per_step_us" in v else ""
+        print(f"[bench]   {k}: {v['us_per_cycle']:.1f} us/cycle{extra}", file=sys.stderr, flush=True)
+
+    dom = max((k for k in kern if "algorithmic_bytes" in kern[k]), key=lambda k: kern[k]["us_per_cycle"])
+    nl = kern[dom]["launches_per_cycle"]
+    achieved = kern[dom]["achieved_GBps"] * 1e9
+    traffic = measured_traffic(dom, cfg.name, args.noise) if cfg.dtype == 1 else None
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_oracle:
         import oracle
-        n = min(args.cpu_requests, B) if args.cpu_requests > 0 else B
-        sub = slice(0, n)
+        n = max(1, min(args.cpu_sample, cfg.B))
         tc = time.perf_counter()
-        r = oracle.spec_cycle_ref(w.base[sub], w.target[sub], w.A, w.W, w.x0[sub], w.conf[sub], w.temp[sub],
-                                  w.threshold, w.seed, noise=noise)
-        dt = time.perf_counter() - tc
-        cpu = {"value": float(r["verify_len"][r["verify_len"] > 0].sum() / dt), "unit": "verified draft tokens/s",
-               "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"first {n} of {B} requests of one cycle of the same workload ({dt:.1f} s wall, "
-                         f"fp64 C + OpenMP)"}
+        r1 = oracle.spec_cycle_ref(w.base[:n], w.target[:n], w.A, w.W, w.x0[:n], w.conf[:n], w.temp[:n],
+                                   w.threshold, w.seed, noise=noise, nthreads=1)
+        dt1 = time.perf_counter() - tc
+        o = res["oracle"]
+        cpu = {"value": o["value"], "unit": "verified draft tokens/s", "cores": o["threads"], "kind": "oracle",
+               "sample": f"the whole batch of one cycle of the same workload ({cfg.B} requests, "
+                         f"{res['sum_verify_len']} verified draft tokens, {o['seconds']:.1f} s wall, fp64 C + "
+                         f"OpenMP over requests)",
+               "value_1thread": float(r1["verify_len"].sum() / dt1),
+               "sample_1thread": f"first {n} requests ({int(r1['verify_len'].sum())} verified draft tokens, "
+                                 f"{dt1:.1f} s wall, one thread)",
+               "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
 
-    traffic = measured_traffic(dom, cfg.name, args.noise) if cfg.dtype == 1 else None
+    configs = {}
+    if not args.only and args.config == "longblock":
+        for name, thr in OTHER_CONFIGS:
+            steps = max(5, min(args.steps, 10))
+            r, _ = measure(name, thr, steps, 2, noise, with_oracle, flush_only=(name == "dspark5"), events=False)
+            key = name if thr is None else f"{name}_tau{thr}"
+            configs[key] = r
+            print(f"[bench] {key}: " + json.dumps({k: r.get(k) for k in ("us_per_cycle", "flushed_p50_us",
+                                                                            "hbm_frac_cycle",
+                                                                            "flushed_hbm_frac_cycle")})
+                  + (f" parity {r['parity']['matched']}/{r['parity']['requests']}" if "parity" in r else ""),
+                  file=sys.stderr, flush=True)
+
     line = {
-        "metric": METRIC, "value": value, "unit": "verified draft tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == 1 else "f32", "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "K": K, "V": cfg.V, "R": cfg.R, "threshold": w.threshold,
-                   "noise": args.noise, "sum_verify_len": sL, "sum_emitted": int((a + 1).sum()),
-                   "steps_with_work": n_active},
-        "hbm_frac_cycle": cbytes / t_cycle / HBM_PEAK,
+        "metric": METRIC, "value": res["value"], "unit": "verified draft tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.dtype == 1 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "K": cfg.K, "V": cfg.V, "R": cfg.R, "threshold": w.threshold,
+                   "noise": args.noise, "sum_verify_len": res["sum_verify_len"], "sum_emitted": res["sum_emitted"],
+                   "max_verify_len": res["max_verify_len"]},
+        "hbm_frac_cycle": res["hbm_frac_cycle"],
+        "cycle_us": {k: res[k] for k in ("us_per_cycle", "p10_us", "p50_us", "p90_us", "flushed_p10_us",
+                                        "flushed_p50_us", "flushed_p90_us")},
+        "flushed_value": res["flushed_value"], "flushed_hbm_frac_cycle": res["flushed_hbm_frac_cycle"],
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom, "launches_per_cycle": K + 1,
+                     "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom, "launches_per_cycle": nl,
                      "traffic_unit": "HBM bytes per launch",
-                     "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes"] / (K + 1)},
-        "kernels": kernels,
+                     "algorithmic_bytes_per_launch": kern[dom]["algorithmic_bytes"] / nl},
+        "kernels": res["kernels"],
+        "parity": res.get("parity"),
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
 

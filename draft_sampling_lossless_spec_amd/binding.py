@@ -32,6 +32,15 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def _held(stream, *tensors):
+    """Tensors this binding allocated for a call enqueued on `stream`: the caching allocator must
+    not hand their blocks to another stream's allocation while the call's kernels still use them,
+    so every one is recorded as in use on `stream` (a no-op cost when it is the current stream)."""
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _load():
     global _lib
     if _lib is not None:
@@ -150,21 +159,26 @@ def spec_cycle(base_logits, target_logits, A, W, conf, temp, threshold: float, s
     need = int(lib.spec_workspace_bytes(C.byref(d)))
     if need == 0:
         raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    made = []
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if out is None:
         out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
                "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
+        made += [out["accepted_len"], out["tokens"]]
     dg = None
     if diag:
         for k, shp, ty in (("verify_len", (B,), torch.int32), ("draft_tokens", (B, K), torch.int32),
                            ("logq", (B, K), torch.float32), ("logp", (B, K), torch.float32)):
             if k not in out:
                 out[k] = torch.empty(shp, dtype=ty, device=dev)
+                made.append(out[k])
         dg = _Diag(out["verify_len"].data_ptr(), out["draft_tokens"].data_ptr(), out["logq"].data_ptr(),
                    out["logp"].data_ptr())
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
+    _held(stream, *made)
     args = (C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(), W.data_ptr(),
             x0.data_ptr() if x0 is not None else None, conf.data_ptr(), temp.data_ptr(),
             C.c_float(threshold), C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), C.c_int64(request_offset),
@@ -207,12 +221,14 @@ def spec_accept_stats(base_logits, target_logits, A, W, draft_tokens, temp, x0=N
     need = int(lib.spec_stats_workspace_bytes(C.byref(d)))
     if need == 0:
         raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt}")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if out is None:
-        out = {k: torch.empty((B, K), dtype=torch.float32, device=dev) for k in ("alpha", "lse_q", "lse_p")}
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _held(stream, workspace)
+    if out is None:
+        out = {k: torch.empty((B, K), dtype=torch.float32, device=dev) for k in ("alpha", "lse_q", "lse_p")}
+        _held(stream, *out.values())
     rc = lib.spec_accept_stats(C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(),
                                W.data_ptr(), x0.data_ptr() if x0 is not None else None, draft_tokens.data_ptr(),
                                temp.data_ptr(), out["alpha"].data_ptr(),
@@ -238,6 +254,7 @@ def spec_calibration_error(conf, verify_len, accepted_len, nbins: int = 10, stre
     n = torch.empty(1, dtype=torch.int64, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    _held(stream, ece, n)
     rc = _load().spec_calibration_error(conf.data_ptr(), verify_len.data_ptr(), accepted_len.data_ptr(), B, K,
                                         int(nbins), ece.data_ptr(), n.data_ptr(), C.c_void_p(stream.cuda_stream))
     if rc != 0:
@@ -255,12 +272,14 @@ def spec_schedule(conf, step_time, nbins: int = 4096, verify_len=None, out=None,
     _check(conf, "conf", (B, K), torch.float32)
     _check(step_time, "step_time", (B * K + 1,), torch.float64)
     dev = conf.device
-    if verify_len is None:
-        verify_len = torch.empty(B, dtype=torch.int32, device=dev)
-    if out is None:
-        out = torch.empty(4, dtype=torch.float64, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if verify_len is None:
+        verify_len = torch.empty(B, dtype=torch.int32, device=dev)
+        _held(stream, verify_len)
+    if out is None:
+        out = torch.empty(4, dtype=torch.float64, device=dev)
+        _held(stream, out)
     rc = _load().spec_schedule(conf.data_ptr(), B, K, step_time.data_ptr(), int(nbins), verify_len.data_ptr(),
                                out.data_ptr(), C.c_void_p(stream.cuda_stream))
     if rc != 0:
@@ -291,21 +310,26 @@ def spec_cycle_lengths(base_logits, target_logits, A, W, verify_len, temp, seed:
     need = int(lib.spec_workspace_bytes(C.byref(d)))
     if need == 0:
         raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise}")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    made = []
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        made.append(workspace)
     if out is None:
         out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
                "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
+        made += [out["accepted_len"], out["tokens"]]
     dg = None
     if diag:
         for k, shp, ty in (("verify_len", (B,), torch.int32), ("draft_tokens", (B, K), torch.int32),
                            ("logq", (B, K), torch.float32), ("logp", (B, K), torch.float32)):
             if k not in out:
                 out[k] = torch.empty(shp, dtype=ty, device=dev)
+                made.append(out[k])
         dg = _Diag(out["verify_len"].data_ptr(), out["draft_tokens"].data_ptr(), out["logq"].data_ptr(),
                    out["logp"].data_ptr())
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
+    _held(stream, *made)
     rc = lib.spec_cycle_lengths(C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(),
                                 W.data_ptr(), x0.data_ptr() if x0 is not None else None, verify_len.data_ptr(),
                                 temp.data_ptr(), C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), C.c_int64(request_offset),
@@ -333,11 +357,13 @@ def spec_temperature_scaling(z, verify_len, accepted_len, grid, nbins: int = 10,
     need = int(lib.spec_temperature_scaling_workspace_bytes(N, G))
     if need == 0:
         raise SpecError(f"unsupported sizes N={N} G={G}")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    out = {k: torch.empty(K, dtype=torch.float64, device=dev) for k in ("T", "ece_before", "ece_after")}
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _held(stream, workspace)
+    out = {k: torch.empty(K, dtype=torch.float64, device=dev) for k in ("T", "ece_before", "ece_after")}
+    _held(stream, *out.values())
     rc = lib.spec_temperature_scaling(z.data_ptr(), verify_len.data_ptr(), accepted_len.data_ptr(), N, K,
                                       grid.data_ptr(), G, int(nbins), out["T"].data_ptr(),
                                       out["ece_before"].data_ptr(), out["ece_after"].data_ptr(), workspace.data_ptr(),

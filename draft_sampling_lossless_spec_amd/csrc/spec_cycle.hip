@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "spec_cycle.h"
 #include "device_common.h"
 
@@ -2042,18 +2044,53 @@ __global__ __launch_bounds__(NT) void k_stats_merge(StatsParams sp) {
   }
 }
 
+// Order-independent fp64 bin sums.  A value x is split into two integer limbs on the grids 2^-24
+// and 2^-64 (h = floor(x 2^24), l = floor(frac(x 2^24) 2^40): exact for |x| < 2^16 down to 2^-64,
+// the bits below truncated), the limbs are added with 64-bit integer LDS atomics, and the sum is
+// rebuilt once from them.  Integer addition is associative, so the result is the same whatever
+// order the threads add in (bit-identical from run to run), and it differs from an exact sum by
+// at most 2^-64 per term.  Up to 2^20 terms per bin fit the limbs.  A term that is not finite
+// makes the bin's sum NaN.
+struct FxBin {
+  long long hi, lo;
+  int bad;
+};
+
+__device__ __forceinline__ void fx_clear(FxBin& f) {
+  f.hi = 0;
+  f.lo = 0;
+  f.bad = 0;
+}
+
+__device__ __forceinline__ void fx_add(FxBin& f, double x) {
+  if (!isfinite(x)) {
+    atomicAdd(&f.bad, 1);
+    return;
+  }
+  const double y = x * 0x1p24;
+  const double h = floor(y);
+  const double l = floor((y - h) * 0x1p40);   // y - h in [0, 1) is exact
+  atomicAdd((unsigned long long*)&f.hi, (unsigned long long)(long long)h);
+  atomicAdd((unsigned long long*)&f.lo, (unsigned long long)(long long)l);
+}
+
+__device__ __forceinline__ double fx_value(const FxBin& f) {
+  return f.bad ? (double)NAN : (double)f.hi * 0x1p-24 + (double)f.lo * 0x1p-64;
+}
+
 // Expected calibration error of the prefix product of the confidences against realised
 // survival: one workgroup; every verified position j < L_b of a valid request is one pair
 // (prediction: fp64 running product through j; outcome: j < a_b); nbins equal-width bins.
 __global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int32_t* verify_len,
                                                    const int32_t* accepted_len, int B, int K, int nbins,
                                                    double* ece, int64_t* n_pairs) {
-  __shared__ double sp_[MAX_BINS];
-  __shared__ double sy_[MAX_BINS];
+  // per bin: the predictions' sum (order-independent limbs), survivals and pairs (integers)
+  __shared__ FxBin sp_[MAX_BINS];
+  __shared__ int sy_[MAX_BINS];
   __shared__ int cnt_[MAX_BINS];
   for (int m = threadIdx.x; m < nbins; m += NT) {
-    sp_[m] = 0.0;
-    sy_[m] = 0.0;
+    fx_clear(sp_[m]);
+    sy_[m] = 0;
     cnt_[m] = 0;
   }
   __syncthreads();
@@ -2066,8 +2103,8 @@ __global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int
       P *= (double)conf[(size_t)b * K + j];
       int m = (int)floor(P * nbins);
       m = m < 0 ? 0 : (m > nbins - 1 ? nbins - 1 : m);
-      atomicAdd(&sp_[m], P);
-      atomicAdd(&sy_[m], j < a ? 1.0 : 0.0);
+      fx_add(sp_[m], P);
+      if (j < a) atomicAdd(&sy_[m], 1);
       atomicAdd(&cnt_[m], 1);
     }
   }
@@ -2077,7 +2114,7 @@ __global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int
     for (int m = 0; m < nbins; m++) N += cnt_[m];
     double e = 0.0;
     for (int m = 0; m < nbins; m++)
-      if (cnt_[m] > 0) e += ((double)cnt_[m] / (double)N) * fabs(sp_[m] / cnt_[m] - sy_[m] / cnt_[m]);
+      if (cnt_[m] > 0) e += ((double)cnt_[m] / (double)N) * fabs(fx_value(sp_[m]) / cnt_[m] - (double)sy_[m] / cnt_[m]);
     ece[0] = N > 0 ? e : 0.0;
     n_pairs[0] = N;
   }
@@ -2090,7 +2127,7 @@ __global__ __launch_bounds__(NT) void k_calibration(const float* conf, const int
 // pressure; "The Speed Claim Nobody's Really Questioning", section "The Real Innovation": verify
 // more when the engine is idle, fewer when it is busy, early stopping keeps it lossless).
 // One workgroup: every position's running minimum of prefix survival is binned on a threshold
-// grid (counts and fp64 survival sums in LDS), suffix sums over the bins give the kept count n_g
+// grid (counts and order-independent survival sums in LDS), suffix sums over the bins give the kept count n_g
 // and expected emitted tokens E_g = B + S_g of every threshold g / nbins, goodput
 // E_g / step_time[n_g] is maximised (ties to the larger g; g = nbins + 1 keeps nothing), and each
 // request's verify length is the length of its prefix at the chosen threshold.
@@ -2107,7 +2144,7 @@ __device__ __forceinline__ int sched_bin(double M, int nbins) {
 __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B, int K, const double* step_time,
                                                      int nbins, int32_t* verify_len, double* out) {
   __shared__ int cnt[MAX_SCHED_BINS + 1];
-  __shared__ double ssum[MAX_SCHED_BINS + 1];
+  __shared__ FxBin ssum[MAX_SCHED_BINS + 1];   // survival sums, order-independent limbs
   __shared__ int tn[SCHED_NT];
   __shared__ double ts[SCHED_NT];
   __shared__ double bestG[SCHED_NT / 64];
@@ -2118,7 +2155,7 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
   const int tid = threadIdx.x;
   for (int i = tid; i <= nbins; i += SCHED_NT) {
     cnt[i] = 0;
-    ssum[i] = 0.0;
+    fx_clear(ssum[i]);
   }
   __syncthreads();
   // one request per thread (B <= 1024): its confidences loaded at once, its bins kept in registers
@@ -2137,7 +2174,7 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
         if (P < M || isnan(P)) M = P;
         mb[j] = sched_bin(M, nbins);
         atomicAdd(&cnt[mb[j]], 1);
-        atomicAdd(&ssum[mb[j]], P);
+        fx_add(ssum[mb[j]], P);
       }
     }
   }
@@ -2149,7 +2186,7 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
   double cs = 0.0;
   for (int k = lo; k < hi; k++) {
     cn += cnt[k];
-    cs += ssum[k];
+    cs += fx_value(ssum[k]);
   }
   tn[tid] = cn;
   ts[tid] = cs;
@@ -2171,7 +2208,7 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
   if (tid == 0) best = (double)B / step_time[0];   // keep nothing
   for (int k = hi - 1; k >= lo; k--) {
     n += cnt[k];
-    S += ssum[k];
+    S += fx_value(ssum[k]);
     if (k >= 1) {
       const double G = ((double)B + S) / step_time[n];
       if (G > best) {   // top down: an equal goodput keeps the larger g found first
@@ -2231,7 +2268,7 @@ __global__ __launch_bounds__(SCHED_NT) void k_schedule(const float* conf, int B,
 // earlier positions fixed; "The Speed Claim...", section "The Real Innovation").  Per position k:
 //   k_sts_eval  workgroups per (grid temperature or unit temperatures, slice of sequences): bin sums for
 //               the calibration error of prod_{i<k} c_i(T_i) * sigmoid(z_k / T) over the sequences that
-//               verify position k, fp64 bin sums in LDS
+//               verify position k, order-independent bin sums in LDS
 //   k_sts_reduce the error of every grid entry from its slices' bin sums
 //   k_sts_pick  the smallest error (ties to the earlier grid entry), then every sequence's running
 //               products advanced with the chosen and with the unit temperature
@@ -2255,13 +2292,13 @@ __global__ __launch_bounds__(STS_NT) void k_sts_eval(const float* z, const int32
                                                    const int32_t* accepted_len, int N, int K, int k,
                                                    const double* grid, int G, int nbins, const double* run,
                                                    const double* run1, double* part) {
-  __shared__ double sp[STS_MAX_BINS];
-  __shared__ double sy[STS_MAX_BINS];
+  __shared__ FxBin sp[STS_MAX_BINS];   // prediction sums, order-independent limbs
+  __shared__ int sy[STS_MAX_BINS];
   __shared__ int cnt[STS_MAX_BINS];
   const int tid = threadIdx.x, g = blockIdx.x, sl = blockIdx.y, ns = gridDim.y;
   for (int m = tid; m < nbins; m += STS_NT) {
-    sp[m] = 0.0;
-    sy[m] = 0.0;
+    fx_clear(sp[m]);
+    sy[m] = 0;
     cnt[m] = 0;
   }
   __syncthreads();
@@ -2275,15 +2312,15 @@ __global__ __launch_bounds__(STS_NT) void k_sts_eval(const float* z, const int32
     const double P = r[n] * sigmoid64((double)z[(size_t)n * K + k] / T);
     int m = (int)floor(P * nbins);
     m = m < 0 ? 0 : (m > nbins - 1 ? nbins - 1 : m);
-    atomicAdd(&sp[m], P);
-    atomicAdd(&sy[m], k < a ? 1.0 : 0.0);
+    fx_add(sp[m], P);
+    if (k < a) atomicAdd(&sy[m], 1);
     atomicAdd(&cnt[m], 1);
   }
   __syncthreads();
   double* o = part + ((size_t)g * ns + sl) * 3 * STS_MAX_BINS;
   for (int m = tid; m < nbins; m += STS_NT) {
-    o[m] = sp[m];
-    o[STS_MAX_BINS + m] = sy[m];
+    o[m] = fx_value(sp[m]);
+    o[STS_MAX_BINS + m] = (double)sy[m];
     o[2 * STS_MAX_BINS + m] = (double)cnt[m];
   }
 }
@@ -2400,14 +2437,19 @@ static Layout layout(const spec_dims* d) {
   return l;
 }
 
+// Per-device caches of device properties.  Each slot is an atomic written with the value the
+// runtime reports, so concurrent first calls on one device store the same value and a reader
+// sees either 0 (unknown yet) or that value.
+constexpr int MAX_DEV = 64;
+
 static int cu_count() {
-  static int ncu[64] = {0};
+  static std::atomic<int> ncu[MAX_DEV];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  int n = (dev >= 0 && dev < 64) ? ncu[dev] : 0;
+  int n = (dev >= 0 && dev < MAX_DEV) ? ncu[dev].load(std::memory_order_relaxed) : 0;
   if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    if (dev >= 0 && dev < 64) ncu[dev] = n;
+    if (dev >= 0 && dev < MAX_DEV) ncu[dev].store(n, std::memory_order_relaxed);
   }
   return n;
 }
@@ -2419,21 +2461,25 @@ static int grid_for(int max_items, int per_cu) {
 }
 
 static int arch_ok() {
-  static int cache[64] = {0};   // 0 unknown, 1 gfx950, -1 other
+  static std::atomic<int> cache[MAX_DEV];   // 0 unknown, 1 gfx950, -1 other
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_HIP;
-  if (dev >= 0 && dev < 64 && cache[dev] != 0) return cache[dev] > 0 ? SPEC_OK : SPEC_E_ARCH;
+  const int c = (dev >= 0 && dev < MAX_DEV) ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (c != 0) return c > 0 ? SPEC_OK : SPEC_E_ARCH;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SPEC_E_HIP;
   const int ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-  if (dev >= 0 && dev < 64) cache[dev] = ok;
+  if (dev >= 0 && dev < MAX_DEV) cache[dev].store(ok, std::memory_order_relaxed);
   return ok > 0 ? SPEC_OK : SPEC_E_ARCH;
 }
 
 // k_sweep_fast: bias slots whose A rows are staged in LDS, the largest whole number of sub-blocks
 // that fits next to the per-request table in the 160 KiB of a workgroup (nine at B <= 256)
+// dynamic LDS ceiling of k_sweep_fast: the 160 KiB of a workgroup less its static scan buffer
+constexpr size_t FAST_LDS_CAP = (size_t)160 * 1024 - sizeof(uint64_t) * (NT / 64);
+
 static int sweep_fast_group(int B) {
-  const size_t cap = (size_t)160 * 1024 - sizeof(uint64_t) * (NT / 64);
+  const size_t cap = FAST_LDS_CAP;
   int g = 16 * SUB;
   while (g > SUB && fast_dyn_bytes(B, g) > cap) g -= SUB;
   return g;
@@ -2451,9 +2497,17 @@ struct Timing {
 template <int DT, int NOISE, bool VEC>
 static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const Timing& tm) {
   const int G = sweep_fast_group(p.B);
-  if (DT == SPEC_BF16 && VEC)
-    (void)hipFuncSetAttribute((const void*)k_sweep_fast<NOISE>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)fast_dyn_bytes(p.B, G));
+  if (DT == SPEC_BF16 && VEC) {
+    // the largest dynamic LDS any call can ask for, set once per device (the attribute is per device)
+    static std::atomic<int> set[MAX_DEV];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= MAX_DEV || set[dev].load(std::memory_order_acquire) == 0) {
+      (void)hipFuncSetAttribute((const void*)k_sweep_fast<NOISE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)FAST_LDS_CAP);
+      if (dev >= 0 && dev < MAX_DEV) set[dev].store(1, std::memory_order_release);
+    }
+  }
   for (int s = 0; s <= p.K; s++) {
     const int k0 = 1 + 3 * s;
     if (DT == SPEC_BF16 && VEC) {
@@ -2461,8 +2515,8 @@ static void launch_steps(const Params& p, const Layout& l, hipStream_t st, const
                             tm.stop(k0), 0, p, s, G);
       // the plain rows ran inside the sweep: an empty interval keeps the timing slots in place
       if (tm.start(k0 + 1)) {
-        hipEventRecord(tm.start(k0 + 1), st);
-        hipEventRecord(tm.stop(k0 + 1), st);
+        (void)hipEventRecord(tm.start(k0 + 1), st);
+        (void)hipEventRecord(tm.stop(k0 + 1), st);
       }
     } else {
       hipExtLaunchKernelGGL((k_bias<DT, NOISE, VEC>), dim3(cu_count()), dim3(NT), bias_dyn_bytes(p.B), st,

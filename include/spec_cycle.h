@@ -175,8 +175,8 @@ int spec_accept_stats(const spec_dims* d, const void* base_logits, const void* t
 /*
  * Expected calibration error of the confidences read as prefix-survival probabilities, the
  * quantity sequential temperature scaling minimises ("DSpark turns speculation into a scheduler",
- * section "Confidence is a serving primitive"; "The Speed Claim...", section "The Real Innovation":
- * expected calibration error from 3-8 % down to about 1 %).  One pair per verified position
+ * section "Confidence is a serving primitive"; "The Speed Claim...", section "The Real Innovation",
+ * where the fit takes this error from several percent to around one percent).  One pair per verified position
  * j < verify_len[b] of every request with accepted_len[b] >= 0: prediction = fp64 running product
  * of conf[b, 0..j]; outcome = 1 if j < accepted_len[b] (the prefix through j survived).  nbins
  * equal-width bins on [0, 1] (1..1024); ECE = sum over bins of (pairs in bin / all pairs) *

@@ -24,8 +24,8 @@
  *                         prefix-dependent bias before each token is sampled).
  *   3. verify          -- accept x_j while u_j < p_j(x_j)/q_j(x_j); stop at the first reject
  *                         ("DSpark turns speculation into a scheduler", opening section and
- *                         "Caveats": the rejection-sampling rule preserves the target
- *                         distribution; "The Speed Claim...", section "Speculative Decoding in
+ *                         "Caveats": with this accept/reject rule the emitted tokens follow
+ *                         the target model's own distribution; "The Speed Claim...", section "Speculative Decoding in
  *                         Two Sentences": accept the longest valid prefix).
  *   4. correct / bonus -- on reject at position a: one token from norm(max(0, p_a - q_a));
  *                         when the whole prefix survives: one bonus token from p at position
@@ -692,8 +692,8 @@ int spec_accept_stats_ref(const oracle_dims* d, const void* base_logits, const v
  * that the draft prefix through position j survives verification, so it needs calibrated
  * magnitudes, and the calibration error of that cumulative prefix probability is what sequential
  * temperature scaling minimises ("DSpark turns speculation into a scheduler", section "Confidence
- * is a serving primitive"; "The Speed Claim...", section "The Real Innovation": expected
- * calibration error brought from 3-8 % down to about 1 %).
+ * is a serving primitive"; "The Speed Claim...", section "The Real Innovation": the pages report
+ * the calibration error falling from several percent to around one percent).
  *
  * Pairs: every verified position j < verify_len[b] of every valid request (accepted_len[b] >= 0).
  * Prediction P_{b,j} = prod_{i<=j} conf[b][i] (fp64, left to right); outcome y_{b,j} = 1 when the
@@ -815,12 +815,13 @@ int spec_schedule_ref(const float* conf, int32_t B, int32_t K, const double* ste
 /* ---------------------------------------------------------------------------------------
  * Sequential temperature scaling of the confidence head.
  *
- * Raw confidences tend to be overconfident; because prefix acceptance is a cumulative product,
- * the calibration runs left to right on held-out data: with the temperatures of the earlier
- * positions fixed, the temperature of the next position is the one that minimises the calibration
- * error of the cumulative prefix probability ("DSpark turns speculation into a scheduler",
- * section "Confidence is a serving primitive"; "The Speed Claim...", section "The Real Innovation":
- * a post-hoc step that brings the expected calibration error from 3-8 % to about 1 %).
+ * The head's raw confidences come out too high.  A prefix survives with the product of its
+ * positions' confidences, so the temperatures are fitted one position at a time, first to last:
+ * each one is the grid temperature giving the smallest calibration error of the running product
+ * on a held-out set, with the positions before it kept at their fitted values ("DSpark turns
+ * speculation into a scheduler", section "Confidence is a serving primitive"; "The Speed
+ * Claim...", section "The Real Innovation", which reports the error falling from several percent
+ * to around one percent after this post-hoc fit).
  *
  * Reading written out here:
  *   z [N, K]: the head's raw logits, c_{n,k}(T) = 1 / (1 + exp(-z_{n,k} / T));

@@ -3,11 +3,12 @@
 against the fp64 oracle on the same seeded inputs.  The drafted tokens are a seeded input (a
 random prefix length and random tokens per request), not an output of either side.
 
-Tolerances (fp32 kernels against fp64): the log-normalisers within 1e-4 * max(1, |value|) (fp32
-sums of up to 1.5e5 terms merged per 256 columns, fp32 Markov bias from exact bf16 products);
-alpha within 1e-4 absolute (each term min(p, q) carries the relative error of its log-normaliser,
-about 1e-5); the calibration error is fp64 on both sides (only the summation order differs):
-1e-12."""
+Tolerances (fp32 kernels against fp64): the log-normalisers within 1e-4 absolute, the cycle's own
+bar on log-probabilities (|exp(error) - 1| <= 1e-4 on every probability built from them; fp32 sums
+of up to 1.5e5 terms merged per 256 columns, fp32 Markov bias from exact bf16 products); alpha
+within 1e-4 absolute (each term min(p, q) carries the relative error of its log-normaliser); the
+calibration error is fp64 on both sides and summed in a fixed order: 1e-12.  Every request of the
+full-size workloads is compared."""
 import numpy as np
 import pytest
 
@@ -47,8 +48,8 @@ def assert_stats_match(o, g):
         assert np.array_equal(np.isnan(o[k]), np.isnan(g[k])), f"{k}: NaN pattern differs"
     m = ~np.isnan(o["alpha"])
     for k in ("lse_q", "lse_p"):
-        err = np.abs(o[k][m] - g[k][m]) / np.maximum(1.0, np.abs(o[k][m]))
-        assert err.max(initial=0.0) < 1e-4, f"{k}: max scaled error {err.max():.3g}"
+        err = np.abs(o[k][m] - g[k][m])
+        assert err.max(initial=0.0) < 1e-4, f"{k}: max error {err.max():.3g}"
     err = np.abs(o["alpha"][m] - g["alpha"][m])
     assert err.max(initial=0.0) < 1e-4, f"alpha: max error {err.max():.3g}"
     print(f"rows {int(m.sum())}: max |alpha err| {err.max(initial=0.0):.2e}", flush=True)
@@ -100,11 +101,7 @@ def test_full_size_stats(name):
     B, K, V = w.cfg.B, w.cfg.K, w.cfg.V
     draft = seeded_draft(B, K, V, 11)
     g = gpu_stats(w, draft)
-    sample = sorted(set([0, B - 1] + list(np.random.default_rng(B).choice(B, size=10, replace=False))))
-    sub = wl.Workload(w.cfg, w.base[sample], w.target[sample], w.A, w.W, w.x0[sample], w.conf[sample],
-                      w.temp[sample], w.threshold, w.seed, w.request_ids[sample])
-    o = ref_stats(sub, draft[sample])
-    assert_stats_match(o, {k: v[sample] for k, v in g.items()})
+    assert_stats_match(ref_stats(w, draft), g)
     # every drafted position is finite and a probability
     m = draft >= 0
     assert np.isfinite(g["alpha"][m]).all() and np.isnan(g["alpha"][~m]).all()
@@ -128,3 +125,8 @@ def test_calibration_error_matches_oracle(nbins):
     torch.cuda.synchronize()
     assert int(gn.item()) == n
     assert abs(float(e.item()) - want) < 1e-12
+    # order-independent bin sums: bit-identical from run to run
+    e2, _ = spec_calibration_error(torch.from_numpy(conf).cuda(), torch.from_numpy(L).cuda(),
+                                   torch.from_numpy(a).cuda(), nbins)
+    torch.cuda.synchronize()
+    assert float(e2.item()) == float(e.item())

@@ -1,7 +1,8 @@
 """GPU parity of sequential temperature scaling (spec_temperature_scaling through the C ABI)
 against the oracle on seeded held-out data.  Both sides evaluate the calibration errors in fp64
-(bin sums in LDS on the GPU: only the summation order and the last bit of exp differ), so the
-fitted temperatures must be equal and the errors agree to 1e-12."""
+(order-independent bin sums on the GPU, bit-identical from run to run; the oracle sums in order;
+the last bit of exp may differ), so the fitted temperatures must be equal and the errors agree to
+1e-12."""
 import math
 
 import numpy as np
@@ -50,6 +51,9 @@ def test_sts_matches_oracle(name, seed, N, K, scale, nbins):
     assert np.array_equal(g["T"], o["T"]), (g["T"], o["T"])
     for k in ("ece_before", "ece_after"):
         assert np.max(np.abs(g[k] - o[k])) < 1e-12, k
+    g2 = gpu_sts(z, L, a, grid, nbins)
+    for k in g:
+        assert np.array_equal(g[k], g2[k]), f"{k} differs between runs"
     print(f"  T={np.round(g['T'], 3)} ece {o['ece_before'].mean():.4f} -> {o['ece_after'].mean():.4f}", flush=True)
 
 

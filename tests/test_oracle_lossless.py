@@ -10,7 +10,7 @@ sampling.  The exact enumeration below is an independent statement of the reject
 mathematics ("DSpark turns speculation into a scheduler", opening section: accept, or reject at
 the first bad position and sample a correction from the target; "The Speed Claim Nobody's Really
 Questioning", section "Speculative Decoding in Two Sentences": accept the longest valid prefix
-and append one bonus token; rejection sampling preserves the target distribution)."""
+and append one bonus token; with this accept/reject rule the emitted tokens follow the target's own distribution)."""
 import itertools
 import math
 from collections import Counter
