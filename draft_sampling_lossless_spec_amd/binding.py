@@ -65,6 +65,8 @@ def _load():
     lib.spec_cycle_lengths.argtypes = [C.POINTER(_Dims), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_void_p, C.c_uint64, C.c_int64, C.c_void_p, C.c_void_p,
                                        C.POINTER(_Diag), C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.spec_cycle_noalloc.restype = C.c_int
+    lib.spec_cycle_noalloc.argtypes = cycle_args[:14] + [C.c_void_p]
     lib.spec_cycle_timed.restype = C.c_int
     lib.spec_cycle_timed.argtypes = cycle_args + [C.c_void_p, C.c_int]
     lib.spec_cycle_kernel_count.restype = C.c_int
@@ -191,6 +193,51 @@ def spec_cycle(base_logits, target_logits, A, W, conf, temp, threshold: float, s
         rc = lib.spec_cycle_timed(*args, C.cast(_events, C.c_void_p), len(_events))
     if rc != 0:
         raise SpecError(f"spec_cycle failed: {spec_error_string(rc)} (code {rc})")
+    return out
+
+
+SPEC_SCRATCH_BYTES = 64 << 20
+
+
+def spec_cycle_noalloc(base_logits, target_logits, A, W, conf, temp, threshold: float, seed: int, out: dict,
+                       x0=None, request_offset: int = 0, noise: int = CHUNKED, stream=None) -> dict:
+    """spec_cycle through the allocation-free entry point: the library's static per-GPU scratch
+    array replaces the workspace, and the caller passes every output tensor in `out`
+    ('accepted_len', 'tokens', and optionally 'verify_len', 'draft_tokens', 'logq', 'logp' for the
+    diagnostics).  Neither this function nor the library allocates device memory.  Calls that
+    overlap on one GPU race on the shared array."""
+    import torch
+    B, K, V = base_logits.shape
+    R = A.shape[1]
+    dt = _dtype_code(base_logits)
+    _check(base_logits, "base_logits", (B, K, V))
+    _check(target_logits, "target_logits", (B, K + 1, V), base_logits.dtype)
+    _check(A, "A", (V, R), base_logits.dtype)
+    _check(W, "W", (V, R), base_logits.dtype)
+    _check(conf, "conf", (B, K), torch.float32)
+    _check(temp, "temp", (B,), torch.float32)
+    if x0 is not None:
+        _check(x0, "x0", (B,), torch.int32)
+    _check(out["accepted_len"], "accepted_len", (B,), torch.int32)
+    _check(out["tokens"], "tokens", (B, K + 1), torch.int32)
+    dg = None
+    if "verify_len" in out:
+        for k, shp, ty in (("verify_len", (B,), torch.int32), ("draft_tokens", (B, K), torch.int32),
+                           ("logq", (B, K), torch.float32), ("logp", (B, K), torch.float32)):
+            _check(out[k], k, shp, ty)
+        dg = _Diag(out["verify_len"].data_ptr(), out["draft_tokens"].data_ptr(), out["logq"].data_ptr(),
+                   out["logp"].data_ptr())
+    lib = _load()
+    d = _Dims(B, K, V, R, dt, noise)
+    if stream is None:
+        stream = torch.cuda.current_stream(base_logits.device)
+    rc = lib.spec_cycle_noalloc(C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(),
+                                W.data_ptr(), x0.data_ptr() if x0 is not None else None, conf.data_ptr(),
+                                temp.data_ptr(), C.c_float(threshold), C.c_uint64(seed & 0xFFFFFFFFFFFFFFFF),
+                                C.c_int64(request_offset), out["accepted_len"].data_ptr(), out["tokens"].data_ptr(),
+                                C.byref(dg) if dg is not None else None, C.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise SpecError(f"spec_cycle_noalloc failed: {spec_error_string(rc)} (code {rc})")
     return out
 
 

@@ -2557,6 +2557,7 @@ extern "C" const char* spec_error_string(int code) {
     case SPEC_E_WORKSPACE: return "workspace missing, misaligned or smaller than spec_workspace_bytes()";
     case SPEC_E_ARCH: return "current HIP device is not gfx950";
     case SPEC_E_HIP: return "HIP runtime error";
+    case SPEC_E_SCRATCH: return "dimensions need more scratch than the static array of spec_cycle_noalloc holds";
     default: return "unknown error code";
   }
 }
@@ -2655,6 +2656,46 @@ extern "C" int spec_cycle_lengths(const spec_dims* d, const void* base_logits, c
   const Timing tm = {nullptr, 0};
   return cycle_impl(d, base_logits, target_logits, A, W, x0, nullptr, verify_len, temp, 0.0f, seed, request_offset,
                     accepted_len, tokens, diag, workspace, workspace_bytes, stream, tm);
+}
+
+// ------------------------------------------------------------------------------------------
+// allocation-free variant: the workspace is a static device array, one per GPU
+// ------------------------------------------------------------------------------------------
+namespace spec {
+static __device__ __align__(256) char scratch[SPEC_SCRATCH_BYTES];
+
+// Device address of this device's copy of `scratch`, looked up once per device with that device
+// current.  The array's name in host code is only a handle for the lookup, never an address.
+static void* scratch_address(int dev) {
+  static std::atomic<void*> addr[MAX_DEV];
+  if (dev < 0 || dev >= MAX_DEV) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  addr[dev].store(q, std::memory_order_release);
+  return q;
+}
+}  // namespace spec
+
+extern "C" int spec_cycle_noalloc(const spec_dims* d, const void* base_logits, const void* target_logits,
+                                  const void* A, const void* W, const int32_t* x0, const float* conf,
+                                  const float* temp, float threshold, uint64_t seed, int64_t request_offset,
+                                  int32_t* accepted_len, int32_t* tokens, const spec_diag* diag,
+                                  spec_stream_t stream) {
+  if (!dims_ok(d)) return SPEC_E_INVAL;
+  if (!dtype_ok(d)) return SPEC_E_DTYPE;
+  const size_t need = layout(d).total;
+  if (need > SPEC_SCRATCH_BYTES) return SPEC_E_SCRATCH;
+  const int ac = arch_ok();
+  if (ac != SPEC_OK) return ac;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_HIP;
+  void* ws = scratch_address(dev);
+  if (!ws) return SPEC_E_HIP;
+  const Timing tm = {nullptr, 0};
+  return cycle_impl(d, base_logits, target_logits, A, W, x0, conf, nullptr, temp, threshold, seed, request_offset,
+                    accepted_len, tokens, diag, ws, SPEC_SCRATCH_BYTES, stream, tm);
 }
 
 extern "C" int spec_cycle_kernel_count(const spec_dims* d) {

@@ -52,7 +52,8 @@ enum {
   SPEC_E_DTYPE = -2,     /* unsupported dtype / noise scheme / dimension combination          */
   SPEC_E_WORKSPACE = -3, /* workspace NULL or smaller than spec_workspace_bytes()             */
   SPEC_E_ARCH = -4,      /* current device is not gfx950                                      */
-  SPEC_E_HIP = -5        /* a HIP runtime call or kernel launch failed                        */
+  SPEC_E_HIP = -5,       /* a HIP runtime call or kernel launch failed                        */
+  SPEC_E_SCRATCH = -6    /* spec_cycle_noalloc: the dims need more than SPEC_SCRATCH_BYTES    */
 };
 
 enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };          /* element type of logits, A and W           */
@@ -139,6 +140,27 @@ int spec_cycle_timed(const spec_dims* d, const void* base_logits, const void* ta
                      const float* temp, float threshold, uint64_t seed, int64_t request_offset,
                      int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, void* workspace,
                      size_t workspace_bytes, spec_stream_t stream, void* const* events, int n_events);
+
+/*
+ * spec_cycle for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Identical work, arguments and results, with no
+ * workspace argument: the scratch memory is a static device array of SPEC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  Its address on the current
+ * device is looked up once per device on the first call there; after that the call allocates
+ * nothing and frees nothing.
+ *   Limit: dims whose spec_workspace_bytes() exceeds SPEC_SCRATCH_BYTES are rejected with
+ *   SPEC_E_SCRATCH before anything is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's one array, so calls that overlap on one GPU
+ *   (different streams or threads, not ordered against each other) race and corrupt each other's
+ *   results; order them on one stream.  A call leaves its state in the array; the next call sets
+ *   up everything it reads, so nothing needs clearing in between.
+ * Returns SPEC_OK, SPEC_E_SCRATCH, SPEC_E_HIP (the symbol lookup failed) or spec_cycle's codes.
+ */
+#define SPEC_SCRATCH_BYTES ((size_t)64 << 20)
+int spec_cycle_noalloc(const spec_dims* d, const void* base_logits, const void* target_logits,
+                       const void* A, const void* W, const int32_t* x0, const float* conf,
+                       const float* temp, float threshold, uint64_t seed, int64_t request_offset,
+                       int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, spec_stream_t stream);
 
 /* Number of kernel slots of one spec_cycle call: 1 + 3 (K + 1); 0 for invalid dims. */
 int spec_cycle_kernel_count(const spec_dims* d);

@@ -137,3 +137,25 @@ def test_advance_host_checks(lib):
     assert lib.spec_advance(fake, fake, 0, 4, fake, None, None) == -1
     assert lib.spec_advance(fake, fake, 2, 33, fake, None, None) == -1
     assert lib.spec_advance(fake, fake, 2, 4, None, None, None) == -1
+
+
+def test_noalloc_host_checks(lib):
+    """spec_cycle_noalloc: dims that need more than the static scratch array are rejected with
+    SPEC_E_SCRATCH on the host, before the device is touched."""
+    from draft_sampling_lossless_spec_amd import SPEC_SCRATCH_BYTES, spec_workspace_bytes
+    from draft_sampling_lossless_spec_amd.binding import _Dims
+    assert SPEC_SCRATCH_BYTES == 64 << 20
+    hdr = open(HEADER).read()
+    assert "#define SPEC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+    fake = C.c_void_p(4096)                                             # never dereferenced
+    args = [fake] * 4 + [None, fake, fake, C.c_float(0.5), C.c_uint64(1), C.c_int64(0), fake, fake, None, None]
+    over = [dims for dims in [(1024, 32, 151936, 256), (1024, 32, 1 << 22, 256)]
+            if spec_workspace_bytes(*dims, 1, 1) > SPEC_SCRATCH_BYTES]
+    assert over, "no test shape exceeds the static scratch array"
+    big = _Dims(*over[0], 1, 1)
+    assert lib.spec_cycle_noalloc(C.byref(big), *args) == -6
+    assert lib.spec_cycle_noalloc(None, *args) == -1
+    bad = _Dims(2, 4, 100, 24, 1, 1)
+    assert lib.spec_cycle_noalloc(C.byref(bad), *args) == -2            # bf16 with R % 16 != 0
+    from draft_sampling_lossless_spec_amd import spec_error_string
+    assert "scratch" in spec_error_string(-6)
