@@ -93,17 +93,23 @@ def parity_counts(orc, diag):
             "first_failures": rep.failures[:3]}
 
 
-def measure(name, threshold, steps, warmup, noise, with_oracle, flush_only=False, seed=1, events=True):
+def measure(name, threshold, steps, warmup, noise, with_oracle, flush_only=False, seed=1, events=True, path=0):
     """One workload: timed cycles (back to back and with the cache flushed between cycles), the
     dominant kernel's event-timed launches, and the oracle beside it with the parity counts of the
     first cycle.  Returns (summary dict, diagnostics for the main line)."""
     import torch
-    from draft_sampling_lossless_spec_amd import CHUNKED, spec_cycle, spec_cycle_kernel_count, spec_workspace_bytes
+    from draft_sampling_lossless_spec_amd import (spec_cycle, spec_cycle_kernel_count, spec_cycle_path,
+                                                  spec_workspace_bytes)
     from draft_sampling_lossless_spec_amd import workloads as wl
 
     t0 = time.time()
     w = wl.generate(name, gen_seed=seed, cycle_seed=seed, threshold=threshold)
     cfg = w.cfg
+    from draft_sampling_lossless_spec_amd import SpecError
+    try:
+        spec_cycle_path(cfg.B, cfg.K, cfg.V, cfg.R, cfg.dtype, noise, path)
+    except SpecError:
+        path = 0   # a workload the requested path does not take (fp32 rows, say): the automatic choice
     print(f"[bench] {name} thr={w.threshold}: generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
 
@@ -115,13 +121,13 @@ def measure(name, threshold, steps, warmup, noise, with_oracle, flush_only=False
     base, target, A, W = t(w.base), t(w.target), t(w.A), t(w.W)
     x0, conf, temp = t(w.x0), t(w.conf), t(w.temp)
     B, K = cfg.B, cfg.K
-    ws = torch.empty(spec_workspace_bytes(B, K, cfg.V, cfg.R, cfg.dtype, noise), dtype=torch.uint8, device=dev)
+    ws = torch.empty(spec_workspace_bytes(B, K, cfg.V, cfg.R, cfg.dtype, noise, path), dtype=torch.uint8, device=dev)
     out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
            "tokens": torch.empty((B, K + 1), dtype=torch.int32, device=dev)}
     run = lambda **kw: spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise,
-                                  workspace=ws, out=out, **kw)
+                                  workspace=ws, out=out, path=path, **kw)
     dg = spec_cycle(base, target, A, W, conf, temp, w.threshold, w.seed, x0=x0, noise=noise, workspace=ws,
-                    diag=True)
+                    diag=True, path=path)
     torch.cuda.synchronize()
     diag = {k: v.cpu().numpy() for k, v in dg.items()}
     L, a = diag["verify_len"], diag["accepted_len"]
@@ -129,8 +135,10 @@ def measure(name, threshold, steps, warmup, noise, with_oracle, flush_only=False
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    taken = spec_cycle_path(B, K, cfg.V, cfg.R, cfg.dtype, noise, path)
     res = {"B": B, "K": K, "V": cfg.V, "R": cfg.R, "threshold": w.threshold, "sum_verify_len": int(L.sum()),
-           "sum_emitted": int((a + 1).sum()), "max_verify_len": int(L.max())}
+           "sum_emitted": int((a + 1).sum()), "max_verify_len": int(L.max()),
+           "path": {1: "stepwise", 2: "resident"}[taken]}
     cb = compulsory_bytes(cfg, L, a)
     res["compulsory_bytes"] = cb
 
@@ -172,7 +180,7 @@ def measure(name, threshold, steps, warmup, noise, with_oracle, flush_only=False
     if events:
         # start/stop events attached to every kernel dispatch of the cycle (same work, own pass)
         hip = hip_runtime()
-        nk = spec_cycle_kernel_count(K)
+        nk = spec_cycle_kernel_count(B, K, cfg.V, cfg.R, cfg.dtype, noise, path)
         nrep = max(3, min(steps, 10))
         ev = [(C.c_void_p * (2 * nk))() for _ in range(nrep)]
         for arr in ev:
@@ -253,6 +261,8 @@ def main():
     ap.add_argument("--config", default="longblock")
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--noise", choices=["chunked", "flat"], default="chunked")
+    ap.add_argument("--path", choices=["auto", "stepwise", "resident"], default="auto",
+                    help="execution path of the cycle (auto: the resident one whenever the call qualifies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true", help="measure the headline workload only (no `configs`)")
     ap.add_argument("--cpu-sample", type=int, default=16,
@@ -302,7 +312,9 @@ def main():
     from draft_sampling_lossless_spec_amd import CHUNKED, FLAT
     noise = CHUNKED if args.noise == "chunked" else FLAT
     with_oracle = not args.no_cpu_baseline
-    res, (w, cfg, L, a, kern) = measure(args.config, args.threshold, args.steps, args.warmup, noise, with_oracle)
+    path = {"auto": 0, "stepwise": 1, "resident": 2}[args.path]
+    res, (w, cfg, L, a, kern) = measure(args.config, args.threshold, args.steps, args.warmup, noise, with_oracle,
+                                        path=path)
     ms_per_step = res["us_per_cycle"] * 1e-3
     print(f"[bench] {args.config}: sum L={res['sum_verify_len']} sum(a+1)={res['sum_emitted']} "
           f"max L={res['max_verify_len']} compulsory={res['compulsory_bytes'] / 1e6:.1f} MB; wall "
@@ -339,7 +351,8 @@ def main():
     if not args.only and args.config == "longblock":
         for name, thr in OTHER_CONFIGS:
             steps = max(5, min(args.steps, 10))
-            r, _ = measure(name, thr, steps, 2, noise, with_oracle, flush_only=(name == "dspark5"), events=False)
+            r, _ = measure(name, thr, steps, 2, noise, with_oracle, flush_only=(name == "dspark5"), events=False,
+                           path=path)
             key = name if thr is None else f"{name}_tau{thr}"
             configs[key] = r
             print(f"[bench] {key}: " + json.dumps({k: r.get(k) for k in ("us_per_cycle", "flushed_p50_us",
@@ -353,7 +366,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.dtype == 1 else "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "K": cfg.K, "V": cfg.V, "R": cfg.R, "threshold": w.threshold,
-                   "noise": args.noise, "sum_verify_len": res["sum_verify_len"], "sum_emitted": res["sum_emitted"],
+                   "noise": args.noise, "path": res["path"], "sum_verify_len": res["sum_verify_len"],
+                   "sum_emitted": res["sum_emitted"],
                    "max_verify_len": res["max_verify_len"]},
         "hbm_frac_cycle": res["hbm_frac_cycle"],
         "cycle_us": {k: res[k] for k in ("us_per_cycle", "p10_us", "p50_us", "p90_us", "flushed_p10_us",

@@ -8,7 +8,7 @@ device tensors into the C call.  It raises if the library has not been built
 (``python -m draft_sampling_lossless_spec_amd.build``) -- there is no CPU fallback.
 """
 from .binding import (  # noqa: F401
-    BF16, CHUNKED, FLAT, FP32, SpecError, lib_path, spec_accept_stats, spec_advance, spec_calibration_error, spec_cycle,
+    BF16, CHUNKED, FLAT, FP32, PATH_AUTO, PATH_RESIDENT, PATH_STEPWISE, SpecError, spec_cycle_path, lib_path, spec_accept_stats, spec_advance, spec_calibration_error, spec_cycle,
     spec_cycle_lengths, spec_cycle_noalloc, SPEC_SCRATCH_BYTES,
     spec_cycle_kernel_count, spec_cycle_timed, spec_error_string, spec_schedule, spec_stats_workspace_bytes,
     spec_temperature_scaling, spec_version, spec_workspace_bytes,

@@ -8,6 +8,7 @@ import os
 
 FP32, BF16 = 0, 1
 FLAT, CHUNKED = 0, 1
+PATH_AUTO, PATH_STEPWISE, PATH_RESIDENT = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libspeccycle.so")
@@ -20,7 +21,7 @@ class SpecError(RuntimeError):
 
 class _Dims(C.Structure):
     _fields_ = [("B", C.c_int32), ("K", C.c_int32), ("V", C.c_int32), ("R", C.c_int32),
-                ("dtype", C.c_int32), ("noise", C.c_int32)]
+                ("dtype", C.c_int32), ("noise", C.c_int32), ("path", C.c_int32)]
 
 
 class _Diag(C.Structure):
@@ -71,6 +72,8 @@ def _load():
     lib.spec_cycle_timed.argtypes = cycle_args + [C.c_void_p, C.c_int]
     lib.spec_cycle_kernel_count.restype = C.c_int
     lib.spec_cycle_kernel_count.argtypes = [C.POINTER(_Dims)]
+    lib.spec_cycle_path.restype = C.c_int
+    lib.spec_cycle_path.argtypes = [C.POINTER(_Dims)]
     lib.spec_stats_workspace_bytes.restype = C.c_size_t
     lib.spec_stats_workspace_bytes.argtypes = [C.POINTER(_Dims)]
     lib.spec_accept_stats.restype = C.c_int
@@ -101,9 +104,20 @@ def spec_error_string(code: int) -> str:
     return _load().spec_error_string(code).decode()
 
 
-def spec_workspace_bytes(B: int, K: int, V: int, R: int, dtype: int = BF16, noise: int = CHUNKED) -> int:
-    d = _Dims(B, K, V, R, dtype, noise)
+def spec_workspace_bytes(B: int, K: int, V: int, R: int, dtype: int = BF16, noise: int = CHUNKED,
+                         path: int = PATH_AUTO) -> int:
+    d = _Dims(B, K, V, R, dtype, noise, path)
     return int(_load().spec_workspace_bytes(C.byref(d)))
+
+
+def spec_cycle_path(B: int, K: int, V: int, R: int, dtype: int = BF16, noise: int = CHUNKED,
+                    path: int = PATH_AUTO) -> int:
+    """The path (PATH_STEPWISE or PATH_RESIDENT) spec_cycle takes for these dims on the current
+    device; raises on a negative code."""
+    rc = int(_load().spec_cycle_path(C.byref(_Dims(B, K, V, R, dtype, noise, path))))
+    if rc < 0:
+        raise SpecError(f"spec_cycle_path: {spec_error_string(rc)} (code {rc})")
+    return rc
 
 
 def _dtype_code(t) -> int:
@@ -126,8 +140,9 @@ def _check(t, name, shape, dtype=None):
         raise SpecError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def spec_cycle_kernel_count(K: int) -> int:
-    d = _Dims(1, K, 2, 16, BF16, CHUNKED)
+def spec_cycle_kernel_count(B: int, K: int, V: int, R: int, dtype: int = BF16, noise: int = CHUNKED,
+                            path: int = PATH_AUTO) -> int:
+    d = _Dims(B, K, V, R, dtype, noise, path)
     return int(_load().spec_cycle_kernel_count(C.byref(d)))
 
 
@@ -139,10 +154,11 @@ def spec_cycle_timed(*args, events, **kw) -> dict:
 
 def spec_cycle(base_logits, target_logits, A, W, conf, temp, threshold: float, seed: int, x0=None,
                request_offset: int = 0, noise: int = CHUNKED, diag: bool = False, workspace=None,
-               out=None, stream=None, _events=None) -> dict:
+               out=None, stream=None, path: int = PATH_AUTO, _events=None) -> dict:
     """Run one speculation cycle on the current HIP stream (or `stream`).  Returns a dict with
     'accepted_len' [B] and 'tokens' [B, K+1] (int32 device tensors) and, with diag=True,
-    'verify_len', 'draft_tokens', 'logq', 'logp'.  Asynchronous like the C call."""
+    'verify_len', 'draft_tokens', 'logq', 'logp'.  `path` selects the execution path (PATH_AUTO,
+    PATH_STEPWISE, PATH_RESIDENT; results are the same).  Asynchronous like the C call."""
     import torch
     B, K, V = base_logits.shape
     R = A.shape[1]
@@ -157,10 +173,10 @@ def spec_cycle(base_logits, target_logits, A, W, conf, temp, threshold: float, s
         _check(x0, "x0", (B,), torch.int32)
     dev = base_logits.device
     lib = _load()
-    d = _Dims(B, K, V, R, dt, noise)
+    d = _Dims(B, K, V, R, dt, noise, path)
     need = int(lib.spec_workspace_bytes(C.byref(d)))
     if need == 0:
-        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise}")
+        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise} path={path}")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     made = []
@@ -200,7 +216,8 @@ SPEC_SCRATCH_BYTES = 64 << 20
 
 
 def spec_cycle_noalloc(base_logits, target_logits, A, W, conf, temp, threshold: float, seed: int, out: dict,
-                       x0=None, request_offset: int = 0, noise: int = CHUNKED, stream=None) -> dict:
+                       x0=None, request_offset: int = 0, noise: int = CHUNKED, stream=None,
+                       path: int = PATH_AUTO) -> dict:
     """spec_cycle through the allocation-free entry point: the library's static per-GPU scratch
     array replaces the workspace, and the caller passes every output tensor in `out`
     ('accepted_len', 'tokens', and optionally 'verify_len', 'draft_tokens', 'logq', 'logp' for the
@@ -228,7 +245,7 @@ def spec_cycle_noalloc(base_logits, target_logits, A, W, conf, temp, threshold: 
         dg = _Diag(out["verify_len"].data_ptr(), out["draft_tokens"].data_ptr(), out["logq"].data_ptr(),
                    out["logp"].data_ptr())
     lib = _load()
-    d = _Dims(B, K, V, R, dt, noise)
+    d = _Dims(B, K, V, R, dt, noise, path)
     if stream is None:
         stream = torch.cuda.current_stream(base_logits.device)
     rc = lib.spec_cycle_noalloc(C.byref(d), base_logits.data_ptr(), target_logits.data_ptr(), A.data_ptr(),
@@ -336,7 +353,7 @@ def spec_schedule(conf, step_time, nbins: int = 4096, verify_len=None, out=None,
 
 def spec_cycle_lengths(base_logits, target_logits, A, W, verify_len, temp, seed: int, x0=None,
                        request_offset: int = 0, noise: int = CHUNKED, diag: bool = False, workspace=None,
-                       out=None, stream=None) -> dict:
+                       out=None, stream=None, path: int = PATH_AUTO) -> dict:
     """One speculation cycle with per-request verify lengths (verify_len [B] int32 device tensor,
     e.g. from spec_schedule) in place of the prefix cut.  Returns what spec_cycle returns."""
     import torch
@@ -353,10 +370,10 @@ def spec_cycle_lengths(base_logits, target_logits, A, W, verify_len, temp, seed:
         _check(x0, "x0", (B,), torch.int32)
     dev = base_logits.device
     lib = _load()
-    d = _Dims(B, K, V, R, dt, noise)
+    d = _Dims(B, K, V, R, dt, noise, path)
     need = int(lib.spec_workspace_bytes(C.byref(d)))
     if need == 0:
-        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise}")
+        raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt} noise={noise} path={path}")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     made = []

@@ -5,7 +5,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "spec_cycle.hip")
+SRCS = [os.path.join(HERE, "csrc", "spec_cycle.hip"), os.path.join(HERE, "csrc", "cycle_resident.hip")]
 OUT = os.path.join(HERE, "libspeccycle.so")
 
 HIPCC_FLAGS = [
@@ -21,7 +21,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           SRC, "-o", OUT + ".tmp"]
+           *SRCS, "-o", OUT + ".tmp"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)

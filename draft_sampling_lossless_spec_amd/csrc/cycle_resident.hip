@@ -1,0 +1,1604 @@
+// cycle_resident.hip -- the speculation cycle as ONE persistent launch with the Markov output
+// factor W resident on chip (gfx950, bf16 rows, chunked noise).
+//
+// The cycle is sequential in the draft position (the Markov bias of position s + 1 needs the token
+// drawn at s), and every position needs the whole of W (bias_v = A[prev] . W[v] for every v).
+// Instead of streaming W from memory once per step, every workgroup owns a fixed slice of the
+// vocabulary (at most ten 64-column chunks, see resident.h) and keeps that slice of W in its
+// accumulation registers and LDS for the whole cycle: W crosses HBM once per cycle.  The grid is
+// one workgroup per CU, launched cooperatively so that all of them are resident together.
+//
+// One step s (s = 0 .. K) of the cycle:
+//   1. every workgroup rebuilds the step's row lists from the per-request roles (a block scan):
+//      bias rows (DRAFT: position s of a request with s < L_b; CORRECT: the position rejected at
+//      step s - 1) in 32-row sub-blocks, and plain rows (LSEP: the target row of the position
+//      verified at step s; BONUS: the target row L_b of a request whose drafts all survived);
+//   2. bias sub-blocks: the gathered A rows of the sub-block are staged in LDS (the MFMA B
+//      operands), each wave runs v_mfma_f32_32x32x16_bf16 chains over its W tiles with the
+//      accumulators seeded by the draft logits, so the chain leaves base + bias in registers;
+//      the element-wise part gives, per row and 64-column chunk, the chunk log-mass and its
+//      Gumbel score (DRAFT), or the residual mass sum max(0, p - q) and the target chunk log-mass
+//      (CORRECT); the four waves' results are merged into ONE record per (row, workgroup);
+//   3. plain rows: each workgroup streams its slice of every plain row: the row log-mass, and for
+//      BONUS rows the chunk scores too; one record per (row, workgroup);
+//   4. grid barrier;
+//   5. merge: request b is finished by workgroup b % G (its requests one after another): it reduces the G
+//      records of each of its rows, draws level two of the chunked sampler inside the winning
+//      chunk (re-reading that chunk's 64 columns and W rows), takes the accept decision, writes
+//      the outputs and the request's roles of step s + 1;
+//   6. grid barrier.
+// The step loop ends when no request has a role left; every workgroup sees the same roles, so
+// they all leave together.
+//
+// Grid barrier: once every wave's stores of the phase have completed, every workgroup stores a
+// 64-bit token (a per-call nonce plus the barrier's index) into its own flag word, then one wave
+// polls all G flags until each is within [token, token + 2^16) (a workgroup can be at most one
+// barrier ahead).  Everything exchanged across workgroups goes through device-coherent loads and
+// stores (see st_u64 / ld_u64 below), so the barrier needs no cache write-back or invalidation.  Flags left from
+// earlier calls never fall in that window (the nonce differs), so nothing is cleared between
+// calls.  A wait that has not finished after about a second sets the workspace's error word and
+// gives up; every later barrier then passes at once and the merges mark every request invalid, so
+// a synchronisation fault ends the kernel with invalid outputs instead of hanging the GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <time.h>
+#include <unistd.h>
+
+#include <atomic>
+
+#include "device_common.h"
+#include "resident.h"
+#include "spec_cycle.h"
+
+namespace spec {
+namespace res {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Masked 16-byte loads are still issued, at an address clamped inside their tensor, so that every
+// load is an unconditional global load with nothing waiting on it until its value is used.  Where
+// the value matters it is replaced at its use by one of these (eight bf16 -inf, or zeros): pieces
+// past V, past the workgroup's slice, A rows of a position without a previous token.  Tiles of a
+// slot without a row, or of a chunk the workgroup does not own, are computed on whatever the
+// clamped loads return and their results are discarded.
+constexpr u32x4 kNegInf = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
+
+enum : int { RO_DRAFT = 1, RO_CORRECT = 2, RO_LSEP = 4, RO_BONUS = 8 };
+enum : int { PH_ALIVE = 0, PH_REJECTED = 1, PH_DONE = 2, PH_INVALID = 3 };
+enum : int { ST_L = 0, ST_ACC = 1, ST_PHASE = 2, ST_ROLES = 3 /* and 4: two step parities */ };
+// A bias-slot entry: bit 0 CORRECT, bits 1..10 the request, bits 11.. the previous token + 1 (0 =
+// no Markov bias); a slot without a row holds NO_ENT.
+constexpr uint32_t NO_ENT = 0xFFFFFFFFu;
+__device__ __forceinline__ uint32_t ent_make(int b, bool corr, int prev) {
+  return ((uint32_t)(prev + 1) << 11) | ((uint32_t)b << 1) | (corr ? 1u : 0u);
+}
+__device__ __forceinline__ int ent_req(uint32_t e) { return (int)((e >> 1) & 1023u); }
+__device__ __forceinline__ int ent_prev(uint32_t e) { return (int)(e >> 11) - 1; }
+constexpr uint64_t TOKEN_WINDOW = 1ull << 16;
+constexpr int PLAIN_INFLIGHT = 1;   // plain-row items whose loads a wave keeps in flight
+constexpr uint64_t WAIT_TICKS = 100000000ull;   // s_memrealtime runs at 100 MHz: one second
+
+// per-request inputs of the step's bias rows, rebuilt by every workgroup at every step
+struct ReqMeta {
+  int prev_d;        // token before position s (x0 at s = 0); -1 = no Markov bias
+  int prev_c;        // token before position s - 1
+  float invT;
+  float lse_p_c;     // log-normalisers of the target and draft rows at position s - 1
+  float lse_q_c;
+  uint32_t key_d[2]; // DRAFT_C noise key of position s
+  uint32_t key_c[2]; // RESIDUAL_C noise key of position s - 1
+};
+
+struct Lists {
+  int n_draft, n_correct, n_plain, c0, n_sb;
+};
+
+// per-wave result of one bias row over the wave's tiles (LDS, merged by the workgroup)
+struct WaveRec {
+  float4 a;   // DRAFT: {log-mass of the wave's chunks, best chunk score, best chunk, half-tile log-mass}
+              // CORRECT: {log residual mass, best score, best chunk, half-tile residual mass (linear)}
+  float4 t;   // CORRECT: {target log-mass, best score, best chunk, half-tile target log-mass}
+};
+
+// ------------------------------------------------------------------------------------------
+// small helpers
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t key_of(const uint32_t (&k)[2]) { return (uint64_t)k[0] | ((uint64_t)k[1] << 32); }
+__device__ __forceinline__ void put_key(uint32_t (&k)[2], uint64_t v) {
+  k[0] = (uint32_t)v;
+  k[1] = (uint32_t)(v >> 32);
+}
+__device__ __forceinline__ uint64_t req_key(uint64_t seed, int64_t gid) { return sm_first(sm_first(seed) ^ (uint64_t)gid); }
+__device__ __forceinline__ uint64_t pos_key(uint64_t kreq, int pos, uint64_t stream) {
+  return sm_first(sm_first(kreq ^ (uint64_t)pos) ^ stream);
+}
+
+// threadIdx.x behind an opaque copy: values derived from it are rebuilt where they are used
+// instead of being hoisted out of the (long) step loop and kept in registers
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// 16-byte load of global memory at `p` (the cast keeps it a global load when `p` itself was read
+// from memory, where the compiler no longer knows its address space)
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *(const __attribute__((address_space(1))) u32x4*)p;
+}
+
+// log(exp(a) + exp(b)), -inf aware, NaN propagating
+__device__ __forceinline__ float lse_add(float a, float b) { return lse2(a, b); }
+
+// argmax take rule: larger score, smaller chunk / index on ties, index < 0 = none
+__device__ __forceinline__ bool takes(float s2, int i2, float s1, int i1) {
+  return i2 >= 0 && (i1 < 0 || s2 > s1 || (s2 == s1 && (unsigned)i2 < (unsigned)i1));
+}
+
+// Lane exchanges without address registers: DPP within 16-lane rows, a swizzle across the two
+// rows of each 32-lane half (lane ^ 16), a permlane swap across the halves (lane ^ 32).
+__device__ __forceinline__ int xor16i(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x401F); }
+__device__ __forceinline__ float xor16f(float x) { return __int_as_float(xor16i(__float_as_int(x))); }
+template <int CTRL>
+__device__ __forceinline__ int dppi(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+// wave-wide reductions (every lane gets the result): xor 1, xor 2, half-row mirror, row mirror,
+// then xor 16 and xor 32
+__device__ __forceinline__ float wmax(float x) {
+  x = max8(x);
+  x = fmaxf(x, dpp<0x140>(x));
+  x = fmaxf(x, xor16f(x));
+  return fmaxf(x, xor32f(x));
+}
+__device__ __forceinline__ float wsum(float x) {
+  x = sum8(x);
+  x += dpp<0x140>(x);
+  x += xor16f(x);
+  return x + xor32f(x);
+}
+
+// one argmax step against the partner values
+__device__ __forceinline__ void am_take(float& sc, int& ix, float& aux, float s2, int i2, float a2) {
+  const bool t = takes(s2, i2, sc, ix);
+  sc = t ? s2 : sc;
+  ix = t ? i2 : ix;
+  aux = t ? a2 : aux;
+}
+template <int CTRL>
+__device__ __forceinline__ void am_dpp(float& sc, int& ix, float& aux) {
+  am_take(sc, ix, aux, dpp<CTRL>(sc), dppi<CTRL>(ix), dpp<CTRL>(aux));
+}
+// wave argmax of (score, index) with a float payload; every lane gets the winner (the take rule
+// is commutative, so the mirror steps reduce like the xor steps)
+__device__ __forceinline__ void wargmax(float& sc, int& ix, float& aux) {
+  am_dpp<0xB1>(sc, ix, aux);    // xor 1
+  am_dpp<0x4E>(sc, ix, aux);    // xor 2
+  am_dpp<0x141>(sc, ix, aux);   // half-row mirror
+  am_dpp<0x140>(sc, ix, aux);   // row mirror
+  am_take(sc, ix, aux, xor16f(sc), xor16i(ix), xor16f(aux));
+  am_take(sc, ix, aux, xor32f(sc), xor32i(ix), xor32f(aux));
+}
+
+// log-sum-exp of invT * y over N values of a lane and its partner lane (lane ^ 32): every -inf
+// gives -inf, a NaN gives NaN
+template <int N>
+__device__ __forceinline__ float pair_lse(const float* y, float invT) {
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    m0 = fmaxf(m0, y[i]);
+    m1 = fmaxf(m1, y[i + 1]);
+  }
+  float mx = fmaxf(m0, m1);
+  mx = fmaxf(mx, xor32f(mx));
+  const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    s0 += ex2(fmaf(y[i], c, -mo));
+    s1 += ex2(fmaf(y[i + 1], c, -mo));
+    s2 += ex2(fmaf(y[i + 2], c, -mo));
+    s3 += ex2(fmaf(y[i + 3], c, -mo));
+  }
+  float sum = (s0 + s1) + (s2 + s3);
+  sum += xor32f(sum);
+  return (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
+}
+
+// log-sum-exp of invT * x over the values of NT tiles (16 per lane each) of a lane and its
+// partner lane, read straight from the accumulators
+template <int NTL>
+__device__ __forceinline__ float tiles_lse(const f32x16* a, float invT) {
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NTL; t++)
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) {
+      m0 = fmaxf(m0, a[t][q]);
+      m1 = fmaxf(m1, a[t][q + 1]);
+    }
+  float mx = fmaxf(m0, m1);
+  mx = fmaxf(mx, xor32f(mx));
+  const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NTL; t++)
+#pragma unroll
+    for (int q = 0; q < 16; q += 4) {
+      s0 += ex2(fmaf(a[t][q], c, -mo));
+      s1 += ex2(fmaf(a[t][q + 1], c, -mo));
+      s2 += ex2(fmaf(a[t][q + 2], c, -mo));
+      s3 += ex2(fmaf(a[t][q + 3], c, -mo));
+    }
+  float sum = (s0 + s1) + (s2 + s3);
+  sum += xor32f(sum);
+  return (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
+}
+
+// residual mass sum max(0, p - q) over N values of a lane and its partner lane; t = target logits,
+// y = draft logits (before the temperature), lse_p / lse_q the rows' log-normalisers
+template <int N>
+__device__ __forceinline__ float pair_residual(const float* t, const float* y, float invT, float lse_p, float lse_q) {
+  const float c = invT * LOG2E, op = -lse_p * LOG2E, oq = -lse_q * LOG2E;
+  float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    const float a2 = fmaf(t[i], c, op), b2 = fmaf(y[i], c, oq);
+    const float a3 = fmaf(t[i + 1], c, op), b3 = fmaf(y[i + 1], c, oq);
+    if (a2 > b2) m0 += ex2(a2) - ex2(b2);
+    if (a3 > b3) m1 += ex2(a3) - ex2(b3);
+  }
+  float m = m0 + m1;
+  return m + xor32f(m);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// bf16 value i (0..8NP-1) of NP packed 16-byte pieces
+template <int NP>
+__device__ __forceinline__ float pk(const u32x4* t, int i) {
+  const uint32_t w = t[i >> 3][(i >> 1) & 3];
+  return (i & 1) ? bf_hi(w) : bf_lo(w);
+}
+
+// draft value i (0..31) of a chunk held in two accumulator tiles
+__device__ __forceinline__ float acc2(const f32x16& a0, const f32x16& a1, int i) { return i < 16 ? a0[i] : a1[i - 16]; }
+// target value i (0..31) of a chunk held in four packed pieces (two per tile)
+__device__ __forceinline__ float tgt4(const u32x4& t0, const u32x4& t1, const u32x4& t2, const u32x4& t3, int i) {
+  const u32x4& t = i < 8 ? t0 : (i < 16 ? t1 : (i < 24 ? t2 : t3));
+  const uint32_t w = t[(i >> 1) & 3];
+  return (i & 1) ? bf_hi(w) : bf_lo(w);
+}
+
+// CORRECT element-wise part of one chunk (two tiles) of a lane and its partner lane: the residual
+// mass sum max(0, p - q) (linear) and the target log-mass, straight from the accumulators and the
+// packed target logits
+__device__ __forceinline__ void chunk_correct(const f32x16& a0, const f32x16& a1, const u32x4& t0, const u32x4& t1,
+                                              const u32x4& t2, const u32x4& t3, float invT, float lse_p, float lse_q,
+                                              float& mass, float& tlse) {
+  const float c = invT * LOG2E, op = -lse_p * LOG2E, oq = -lse_q * LOG2E;
+  float tm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 32; i++) tm = fmaxf(tm, tgt4(t0, t1, t2, t3, i));
+  tm = fmaxf(tm, xor32f(tm));
+  const float mo = (tm == -INFINITY) ? 0.0f : tm * c;
+  float m0 = 0.0f, m1 = 0.0f, s0 = 0.0f, s1 = 0.0f;
+  // in groups of eight values, each group scheduled on its own: the register peak stays small
+#pragma unroll
+  for (int g8 = 0; g8 < 32; g8 += 8) {
+#pragma unroll
+    for (int i = g8; i < g8 + 8; i += 2) {
+      const float ta = tgt4(t0, t1, t2, t3, i), tb = tgt4(t0, t1, t2, t3, i + 1);
+      const float pa = fmaf(ta, c, op), qa = fmaf(acc2(a0, a1, i), c, oq);
+      const float pb = fmaf(tb, c, op), qb = fmaf(acc2(a0, a1, i + 1), c, oq);
+      if (pa > qa) m0 += ex2(pa) - ex2(qa);
+      if (pb > qb) m1 += ex2(pb) - ex2(qb);
+      s0 += ex2(fmaf(ta, c, -mo));
+      s1 += ex2(fmaf(tb, c, -mo));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float m = m0 + m1, sm = s0 + s1;
+  mass = m + xor32f(m);
+  sm += xor32f(sm);
+  tlse = (tm == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : tm * invT + lg2(sm) * LN2;
+}
+
+// CORRECT element-wise part over 8 NP values of a lane and its partner lane, the target values
+// unpacked on the fly from NP 16-byte pieces: the residual mass sum max(0, p - q) (linear) and the
+// target log-mass
+template <int NP>
+__device__ __forceinline__ void pair_correct(const float* y, const u32x4* tp, float invT, float lse_p, float lse_q,
+                                             float& mass, float& tlse) {
+  constexpr int N = 8 * NP;
+  const float c = invT * LOG2E, op = -lse_p * LOG2E, oq = -lse_q * LOG2E;
+  float tm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; i++) tm = fmaxf(tm, pk<NP>(tp, i));
+  tm = fmaxf(tm, xor32f(tm));
+  const float mo = (tm == -INFINITY) ? 0.0f : tm * c;
+  float m0 = 0.0f, m1 = 0.0f, s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i += 2) {
+    const float t0 = pk<NP>(tp, i), t1 = pk<NP>(tp, i + 1);
+    const float a0 = fmaf(t0, c, op), b0 = fmaf(y[i], c, oq);
+    const float a1 = fmaf(t1, c, op), b1 = fmaf(y[i + 1], c, oq);
+    if (a0 > b0) m0 += ex2(a0) - ex2(b0);
+    if (a1 > b1) m1 += ex2(a1) - ex2(b1);
+    s0 += ex2(fmaf(t0, c, -mo));
+    s1 += ex2(fmaf(t1, c, -mo));
+  }
+  float m = m0 + m1, sm = s0 + s1;
+  mass = m + xor32f(m);
+  sm += xor32f(sm);
+  tlse = (tm == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : tm * invT + lg2(sm) * LN2;
+}
+
+// 16 logits of a lane (two 16-byte pieces) -> floats
+__device__ __forceinline__ void unpack16(u32x4 a, u32x4 b, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    o[2 * i] = bf_lo(a[i]);
+    o[2 * i + 1] = bf_hi(a[i]);
+    o[8 + 2 * i] = bf_lo(b[i]);
+    o[8 + 2 * i + 1] = bf_hi(b[i]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Data exchanged between workgroups (records, roles, drafted tokens, log-normalisers) is written
+// and read only through these device-coherent accessors: relaxed agent-scope atomics, which the
+// gfx950 code generator emits as sc1 loads and stores that are coherent across the XCDs without
+// any cache write-back or invalidation.  The grid barrier then only has to order them (each wave
+// waits for its own stores to complete before its workgroup announces arrival).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ void st_u64(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_u64(const void* p) {
+  return __hip_atomic_load((uint64_t*)const_cast<void*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_i32(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_i32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_f32(float* p, float v) { st_i32((int32_t*)p, __float_as_int(v)); }
+__device__ __forceinline__ float ld_f32(const float* p) { return __int_as_float(ld_i32((const int32_t*)p)); }
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+  return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+}
+// a 16-byte record as two coherent 8-byte words (x, y) and (z, w)
+__device__ __forceinline__ void rec_store(float4* p, float4 v) {
+  st_u64(p, pack2(v.x, v.y));
+  st_u64((char*)p + 8, pack2(v.z, v.w));
+}
+__device__ __forceinline__ float4 rec_load(const float4* p) {
+  const uint64_t a = ld_u64(p), b = ld_u64((const char*)p + 8);
+  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
+                     __uint_as_float((uint32_t)(b >> 32)));
+}
+
+// ------------------------------------------------------------------------------------------
+// grid barrier on per-workgroup flags (see the file header)
+// ------------------------------------------------------------------------------------------
+// the error word holds the nonce of a call whose barrier timed out (any other value: no error)
+__device__ __forceinline__ bool failed(const uint64_t* err, uint64_t nonce) {
+  return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nonce;
+}
+
+__device__ void grid_barrier(uint64_t* flags, uint64_t* err, uint64_t nonce, int G, uint64_t token) {
+  // every wave's coherent stores of this phase have completed before its workgroup announces
+  // arrival (the clobber keeps the compiler from moving memory operations across the wait)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int tid = opaque_tid();
+  if (tid < 64) {
+    const int lane = tid;
+    if (lane == 0)
+      __hip_atomic_store(&flags[(size_t)blockIdx.x * FLAG_STRIDE], token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      bool ok = true;
+      for (int i = lane; i < G; i += 64) {
+        const uint64_t f = __hip_atomic_load(&flags[(size_t)i * FLAG_STRIDE], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = ok && (f - token) < TOKEN_WINDOW;
+      }
+      if (__all(ok)) break;
+      if (failed(err, nonce)) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
+        if (lane == 0) __hip_atomic_store(err, nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  // the coherent loads of the next phase are issued after every workgroup has arrived
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
+// LDS of the resident kernel (dynamic; carved in this order)
+// ------------------------------------------------------------------------------------------
+struct Smem {
+  bf16x8* wl;        // [4 tiles][KSTEPS][64]: W tiles of the workgroup's LDS chunks (MFMA A operands)
+  bf16x8* sA;        // [2][KSTEPS][64]: B operands (gathered A rows) of the current / next sub-block
+  ReqMeta* req;      // [B]
+  uint8_t* role;     // [B] roles of the step
+  uint8_t* Lq;       // [B] verify lengths
+  uint16_t* slot;    // [3][B]: DRAFT bias slot, CORRECT bias slot, plain slot (0xFFFF = none)
+  uint32_t* blist;   // [max bias slots]: entries (ent_make), NO_ENT in gaps
+  uint16_t* plist;   // [B]
+  int4* wcnt;        // [NW] per-wave row counts of a list-building round
+};
+
+__host__ __device__ inline size_t smem_bytes(int B) {
+  size_t o = 0;
+  o += (size_t)4 * KSTEPS * 64 * 16;                 // wl
+  o += (size_t)2 * KSTEPS * 64 * 16;                 // sA
+  o += (size_t)B * sizeof(ReqMeta);                  // req
+  o += (size_t)B * 2;                                // role, Lq
+  o += (size_t)3 * B * 2;                            // slot
+  o += (size_t)max_bias_slots(B) * 4 + (size_t)B * 2; // blist, plist
+  o = (o + 15) & ~(size_t)15;
+  o += NW * 16;                                      // wcnt
+  return o;
+}
+
+__device__ inline Smem carve(char* base, int B) {
+  Smem m;
+  char* p = base;
+  m.wl = (bf16x8*)p; p += (size_t)4 * KSTEPS * 64 * 16;
+  m.sA = (bf16x8*)p; p += (size_t)2 * KSTEPS * 64 * 16;
+  m.req = (ReqMeta*)p; p += (size_t)B * sizeof(ReqMeta);
+  m.role = (uint8_t*)p; p += B;
+  m.Lq = (uint8_t*)p; p += B;
+  m.slot = (uint16_t*)p; p += (size_t)3 * B * 2;
+  m.blist = (uint32_t*)p; p += (size_t)max_bias_slots(B) * 4;
+  m.plist = (uint16_t*)p; p += (size_t)B * 2;
+  p = (char*)(((uintptr_t)p + 15) & ~(uintptr_t)15);
+  m.wcnt = (int4*)p;
+  return m;
+}
+
+// ------------------------------------------------------------------------------------------
+// kernel parameters (device view of the workspace)
+// ------------------------------------------------------------------------------------------
+struct KP {
+  Args a;
+  int32_t* st;        // [6][B]
+  int32_t* xs;        // [B][K]
+  float* lse_q;       // [B][K]
+  float* logq;        // [B][K]
+  float* lse_p;       // [B][K+1]
+  float* logp;        // [B][K]
+  float4* rec_d;      // [slots][G][NW]: per-wave records of bias rows
+  float4* rec_c;      // [slots][G][NW]: CORRECT rows' target-row records
+  float4* rec_p;      // [B][MAX_G]: records of the plain rows' items (ceil(V / TP) <= MAX_G per row)
+  uint64_t* flags;    // [G][FLAG_STRIDE]
+  uint64_t* err;
+};
+
+// W fragment f (tile f of a chunk: 32 columns) at k-step t for lane l: row i = l % 32 of the MFMA
+// A operand is column 64 c + 32 f + perm(i), perm chosen so that accumulator q of lane l holds
+// column 64 c + 32 f + 16 (l / 32) + q; lane half l / 32 covers k in [R/2 (l/32), R/2 (l/32 + 1)).
+// Columns past V and k-steps past the rank read zeros.
+__device__ __forceinline__ bf16x8 w_frag(const KP& p, int c, int f, int t) {
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 31, h = lane >> 5;
+  const int R = p.a.R;
+  const int col_in = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+  const int v = CH * c + 32 * f + col_in;
+  const bool in = c >= 0 && v < p.a.V && t < (R >> 4);
+  // out of range: read row 0 and zero the value (no branch around the load)
+  const u32x4 x = *(const u32x4*)((const uint16_t*)p.a.W + (in ? (size_t)v * R + h * (R >> 1) + 8 * t : 0));
+  const u32x4 z = in ? x : (u32x4){0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// ------------------------------------------------------------------------------------------
+// merge of one request by one wave
+// ------------------------------------------------------------------------------------------
+// running reduction of records {log-mass, best score, best chunk}: the mass kept as m + log(s)
+struct PAcc {
+  float m, s, sc;
+  int ix, nan;
+};
+
+__device__ __forceinline__ void pacc_init(PAcc& a) {
+  a.m = -INFINITY;
+  a.s = 0.0f;
+  a.sc = -INFINITY;
+  a.ix = -1;
+  a.nan = 0;
+}
+
+__device__ __forceinline__ void pacc_add(PAcc& a, float4 r) {
+  const float m = r.x;
+  if (m != m) {
+    a.nan = 1;
+  } else if (m > a.m) {
+    a.s = 1.0f + a.s * ex2((a.m - m) * LOG2E);   // a.m = -inf: the old sum is 0
+    a.m = m;
+  } else if (m > -INFINITY) {
+    a.s += ex2((m - a.m) * LOG2E);
+  }
+  const int ix = __float_as_int(r.z);
+  if (takes(r.y, ix, a.sc, a.ix)) {
+    a.sc = r.y;
+    a.ix = ix;
+  }
+}
+
+// every lane's running record merged into every lane; returns {log-mass, best score, best chunk}
+__device__ __forceinline__ float4 pacc_wave(PAcc a) {
+  const float M = wmax(a.m);
+  const float sl = (a.m == -INFINITY) ? 0.0f : a.s * ex2((a.m - M) * LOG2E);
+  const float S_ = wsum(sl);
+  const int nan = __ballot(a.nan != 0) != 0ull;
+  float aux = 0.0f;
+  wargmax(a.sc, a.ix, aux);
+  const float lse = nan ? NAN : (M == -INFINITY ? -INFINITY : M + lg2(S_) * LN2);
+  return make_float4(lse, a.sc, __int_as_float(a.ix), 0.0f);
+}
+
+enum { L2_NONE = 0, L2_DRAFT = 1, L2_TARGET = 2, L2_RESIDUAL = 3 };
+
+struct Job {
+  int kind;              // L2_*
+  int chunk;             // winning chunk of level one
+  int prev;              // previous token of the Markov bias, -1 = none
+  uint64_t key;          // per-index noise key of the row
+  const uint16_t* base;  // draft row
+  const uint16_t* targ;  // target row
+  float lse_p, lse_q;
+  bool want_target;      // DRAFT: also return the target logit of the winner
+};
+
+struct L2Out {
+  int v;      // winning column, -1 = none
+  float sx;   // DRAFT: scaled draft logit of the winner
+  float tx;   // target logit (unscaled) of the winner, when asked for
+};
+
+// LDS scratch of the merge phase (it lives in the B-operand buffers, idle between the barriers)
+struct MergeLds {
+  uint16_t arow[2][256];   // A rows of the two level-two jobs
+  float4 rec[4][NW];       // per-wave reductions of the records of the request's four row kinds
+  float4 win[2][NW];       // per-wave level-two winners {score, index, scaled draft logit, target logit}
+};
+
+// Level two of the chunked sampler for two jobs at once by the whole workgroup: wave w takes
+// columns 64 chunk + 16 w .. + 16, four lanes per column, each lane a quarter of the rank (eight
+// 16-byte pieces of the column's W row and the staged A row); the quarters are summed across the
+// lane quad, the winner is found per wave, then across the waves.  Result uniform.
+__device__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int V = p.a.V, R = p.a.R, P16 = R >> 3;
+  if (tid < 128) {
+    const int q = tid >> 6, l = tid & 63;
+    const bool ld = jb[q].kind != L2_NONE && jb[q].kind != L2_TARGET && jb[q].prev >= 0 && 4 * l < R;
+    const uint2 w = *(const uint2*)((const uint16_t*)p.a.A + (ld ? (size_t)jb[q].prev * R + 4 * l : 0));
+    *(uint2*)&ml->arow[q][4 * l] = ld ? w : make_uint2(0u, 0u);
+  }
+  const int col = 16 * wave + (lane >> 2), kq = lane & 3;
+  int v[2];
+  bool in[2];
+  float bv[2], tv[2], bias[2];
+  u32x4 wv[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    v[q] = jb[q].chunk * CH + col;
+    in[q] = jb[q].kind != L2_NONE && jb[q].chunk >= 0 && v[q] < V;
+    const bool need_base = in[q] && (jb[q].kind == L2_DRAFT || jb[q].kind == L2_RESIDUAL);
+    const bool need_targ = in[q] && (jb[q].kind != L2_DRAFT || jb[q].want_target);
+    const bool need_bias = in[q] && jb[q].kind != L2_TARGET && jb[q].prev >= 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const int pc = 8 * kq + i;
+      const bool ld = need_bias && pc < P16;
+      const u32x4 x = *(const u32x4*)((const uint16_t*)p.a.W + (ld ? (size_t)v[q] * R + 8 * pc : 0));
+      wv[q][i] = ld ? x : kZero;
+    }
+    bv[q] = need_base ? bf16_to_f32(jb[q].base[v[q]]) : 0.0f;
+    tv[q] = need_targ ? bf16_to_f32(jb[q].targ[v[q]]) : 0.0f;
+  }
+  __syncthreads();   // the A rows are staged
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const u32x4 ar = *(const u32x4*)&ml->arow[q][64 * kq + 8 * i];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        a = fmaf(bf_lo(ar[e]), bf_lo(wv[q][i][e]), a);
+        a = fmaf(bf_hi(ar[e]), bf_hi(wv[q][i][e]), a);
+      }
+    }
+    a += dpp<0xB1>(a);   // quad sum: xor 1, xor 2
+    a += dpp<0x4E>(a);
+    bias[q] = a;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
+    int ix = -1;
+    if (in[q] && kq == 0) {
+      const float gg = gumbel_bits(bits_at(jb[q].key, (uint32_t)v[q]));
+      if (jb[q].kind == L2_DRAFT) {
+        const float sv = (bv[q] + bias[q]) * invT;
+        if (jb[q].want_target) tx = tv[q];
+        if (sv > -INFINITY) {
+          sc = sv + gg;
+          ix = v[q];
+          sx = sv;
+        }
+      } else if (jb[q].kind == L2_TARGET) {
+        const float t = tv[q] * invT;
+        if (t > -INFINITY) {
+          sc = t + gg;
+          ix = v[q];
+        }
+      } else {
+        const float sv = (bv[q] + bias[q]) * invT, t = tv[q] * invT;
+        const float lp = t - jb[q].lse_p, lq = sv - jb[q].lse_q;
+        if (lp > lq) {
+          sc = lp + logf(-expm1f(lq - lp)) + gg;
+          ix = v[q];
+        }
+      }
+    }
+    // the winner's target logit rides along as a second payload: pack (sx, tx) through the argmax
+    // by carrying tx in a separate argmax with the same take decisions is not possible, so the
+    // winning lane is found by ballot after the wave argmax
+    const int ix0 = ix;
+    const float tx0 = tx;
+    wargmax(sc, ix, sx);
+    const unsigned long long wm = __ballot(ix >= 0 && ix0 == ix);
+    const int src = __builtin_amdgcn_readfirstlane(wm ? __ffsll(wm) - 1 : 0);
+    tx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx0), src));
+    if (lane == 0) ml->win[q][wave] = make_float4(sc, __int_as_float(ix), sx, tx);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    float4 bw = ml->win[q][0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) {
+      const float4 c = ml->win[q][w];
+      if (takes(c.x, __float_as_int(c.y), bw.x, __float_as_int(bw.y))) bw = c;
+    }
+    out[q].v = __float_as_int(bw.y);
+    out[q].sx = bw.z;
+    out[q].tx = bw.w;
+  }
+}
+
+// The four wave records of one workgroup (cb: its first chunk, nl: its LDS chunks) for one bias
+// row, combined into that workgroup's {log-mass, best chunk score, best chunk}.  A wave record
+// holds the log-mass of the wave's register chunks, their best score and chunk, and the log-mass
+// of the wave's half of an LDS chunk; the halves of LDS chunk i are in waves 2i and 2i + 1, and
+// the chunk's Gumbel score is formed here from the whole chunk.
+__device__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, uint64_t key) {
+  float lse = -INFINITY, bs = -INFINITY;
+  int bc = -1;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    lse = lse_add(lse, a[w].x);
+    if (takes(a[w].y, __float_as_int(a[w].z), bs, bc)) {
+      bs = a[w].y;
+      bc = __float_as_int(a[w].z);
+    }
+  }
+  for (int i = 0; i < nl; i++) {
+    const float hc = lse_add(a[2 * i].w, a[2 * i + 1].w);
+    lse = lse_add(lse, hc);
+    const int cgl = cb + NW * AG_CHUNKS + i;
+    const float sc = hc > -INFINITY ? hc + gumbel_bits(bits_at(key, (uint32_t)cgl)) : -INFINITY;
+    if (hc > -INFINITY && takes(sc, cgl, bs, bc)) {
+      bs = sc;
+      bc = cgl;
+    }
+  }
+  return make_float4(lse, bs, __int_as_float(bc), 0.0f);
+}
+
+// The same for a CORRECT row: the residual records a (log residual mass of the register chunks,
+// best score, best chunk, LINEAR residual mass of the LDS half) and the target records t (target
+// log-mass, best score, best chunk, target log-mass of the LDS half); both draws use `key`.
+__device__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb, int nl, uint64_t key, float4& rd,
+                           float4& rt) {
+  float ms = 0.0f, lt = -INFINITY, bs = -INFINITY, bt = -INFINITY;
+  int bc = -1, btc = -1;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    ms += a[w].x > -INFINITY ? ex2(a[w].x * LOG2E) : 0.0f;
+    if (takes(a[w].y, __float_as_int(a[w].z), bs, bc)) {
+      bs = a[w].y;
+      bc = __float_as_int(a[w].z);
+    }
+    lt = lse_add(lt, t[w].x);
+    if (takes(t[w].y, __float_as_int(t[w].z), bt, btc)) {
+      bt = t[w].y;
+      btc = __float_as_int(t[w].z);
+    }
+  }
+  for (int i = 0; i < nl; i++) {
+    const int cgl = cb + NW * AG_CHUNKS + i;
+    const float gg = gumbel_bits(bits_at(key, (uint32_t)cgl));
+    const float mc = a[2 * i].w + a[2 * i + 1].w;
+    ms += mc;
+    const float lmc = mc > 0.0f ? lg2(mc) * LN2 : -INFINITY;
+    if (lmc > -INFINITY && takes(lmc + gg, cgl, bs, bc)) {
+      bs = lmc + gg;
+      bc = cgl;
+    }
+    const float tc = lse_add(t[2 * i].w, t[2 * i + 1].w);
+    lt = lse_add(lt, tc);
+    if (tc > -INFINITY && takes(tc + gg, cgl, bt, btc)) {
+      bt = tc + gg;
+      btc = cgl;
+    }
+  }
+  rd = make_float4(ms > 0.0f ? lg2(ms) * LN2 : -INFINITY, bs, __int_as_float(bc), 0.0f);
+  rt = make_float4(lt, bt, __int_as_float(btc), 0.0f);
+}
+
+// Request b at step s, by the whole workgroup: reduce its rows' records, level two, accept
+// decision, outputs, roles of step s + 1.  The request's state is touched by this workgroup only.
+__device__ void merge_request(const KP& p, const Smem& S, int b, int s) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int B = p.a.B, K = p.a.K, V = p.a.V, G = p.a.G;
+  MergeLds* ml = (MergeLds*)S.sA;
+  int32_t* roles_next = p.st + (size_t)(ST_ROLES + ((s + 1) & 1)) * B;
+  const int roles = S.role[b];
+  __syncthreads();   // the scratch of the previous request's merge is no longer read
+  if (roles == 0) {
+    if (tid == 0) st_i32(&roles_next[b], 0);
+    return;
+  }
+  const ReqMeta rm = S.req[b];
+  const float invT = rm.invT;
+  const int L = S.Lq[b];
+  int phase = p.st[ST_PHASE * B + b];
+  int acc = p.st[ST_ACC * B + b];
+  const uint64_t kreq = req_key(p.a.seed, p.a.req_off + b);
+  const bool hasD = roles & RO_DRAFT, hasC = roles & RO_CORRECT, hasP = roles & (RO_LSEP | RO_BONUS);
+  const int sd = S.slot[b], sc_ = S.slot[B + b], sp = S.slot[2 * B + b];
+  const int x_t = tid < K ? p.xs[(size_t)b * K + tid] : -1;   // drafted tokens, for the output
+  // ---- records of every row of the request: thread t takes record t, then waves, then LDS ----
+  {
+    PAcc a4[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) pacc_init(a4[r]);
+    const uint64_t key_d = pos_key(kreq, s, ST_DRAFT_C), key_c = pos_key(kreq, s > 0 ? s - 1 : 0, ST_RESIDUAL_C);
+    for (int i = tid; i < G; i += NT) {
+      const int cb = chunk_begin(i, G, V), ncw = chunks_of(i, G, V);
+      const int nl = ncw > NW * AG_CHUNKS ? ncw - NW * AG_CHUNKS : 0;
+      if (hasD) {
+        float4 a[NW];
+#pragma unroll
+        for (int w = 0; w < NW; w++) a[w] = rec_load(&p.rec_d[((size_t)sd * G + i) * NW + w]);
+        pacc_add(a4[0], wg_draft(a, cb, nl, key_d));
+      }
+      if (hasC) {
+        float4 a[NW], t[NW];
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+          a[w] = rec_load(&p.rec_d[((size_t)sc_ * G + i) * NW + w]);
+          t[w] = rec_load(&p.rec_c[((size_t)sc_ * G + i) * NW + w]);
+        }
+        float4 rd, rt;
+        wg_correct(a, t, cb, nl, key_c, rd, rt);
+        pacc_add(a4[1], rd);
+        pacc_add(a4[2], rt);
+      }
+    }
+    if (hasP) {
+      const int nrP = (V + TP - 1) / TP;
+      for (int i = tid; i < nrP; i += NT) pacc_add(a4[3], rec_load(&p.rec_p[(size_t)sp * MAX_G + i]));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const float4 t = pacc_wave(a4[r]);
+      if (lane == 0) ml->rec[r][wave] = t;
+    }
+  }
+  __syncthreads();
+  float4 tot[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    // merge of the four waves' {log-mass, best score, best chunk}
+    float4 x = ml->rec[r][0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) {
+      const float4 c = ml->rec[r][w];
+      x.x = lse_add(x.x, c.x);
+      if (takes(c.y, __float_as_int(c.z), x.y, __float_as_int(x.z))) {
+        x.y = c.y;
+        x.z = c.z;
+      }
+    }
+    tot[r] = x;
+  }
+  const float4 tot_d = tot[0], tot_c = tot[1], tot_c2 = tot[2], tot_p = tot[3];
+
+  // ---- level two: the DRAFT row and the CORRECT / BONUS row side by side ----
+  const int j_c = s - 1;
+  const bool residual = tot_c.x > -INFINITY;
+  const uint16_t* targ_s = (const uint16_t*)p.a.target + ((size_t)b * (K + 1) + s) * V;
+  Job jb[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    jb[q].kind = L2_NONE;
+    jb[q].chunk = -1;
+    jb[q].prev = -1;
+    jb[q].key = 0;
+    jb[q].base = nullptr;
+    jb[q].targ = nullptr;
+    jb[q].lse_p = 0.0f;
+    jb[q].lse_q = 0.0f;
+    jb[q].want_target = false;
+  }
+  if (hasD && isfinite(tot_d.x)) {
+    jb[0].kind = L2_DRAFT;
+    jb[0].chunk = __float_as_int(tot_d.z);
+    jb[0].prev = rm.prev_d;
+    jb[0].key = pos_key(kreq, s, ST_DRAFT);
+    jb[0].base = (const uint16_t*)p.a.base + ((size_t)b * K + s) * V;
+    jb[0].targ = targ_s;
+    jb[0].want_target = (roles & RO_LSEP) != 0;
+  }
+  if (hasC) {
+    jb[1].chunk = __float_as_int(residual ? tot_c.z : tot_c2.z);
+    jb[1].key = pos_key(kreq, j_c, ST_RESIDUAL);
+    jb[1].targ = (const uint16_t*)p.a.target + ((size_t)b * (K + 1) + j_c) * V;
+    if (residual) {
+      jb[1].kind = L2_RESIDUAL;
+      jb[1].prev = rm.prev_c;
+      jb[1].base = (const uint16_t*)p.a.base + ((size_t)b * K + j_c) * V;
+      jb[1].lse_p = rm.lse_p_c;
+      jb[1].lse_q = rm.lse_q_c;
+    } else {
+      jb[1].kind = L2_TARGET;
+    }
+  } else if ((roles & RO_BONUS) && isfinite(tot_p.x)) {
+    jb[1].kind = L2_TARGET;
+    jb[1].chunk = __float_as_int(tot_p.z);
+    jb[1].key = pos_key(kreq, s, ST_BONUS);
+    jb[1].targ = targ_s;
+  }
+  L2Out r2[2];
+  level_two(p, jb, invT, ml, r2);
+  const L2Out rd = r2[0], rf = r2[1];
+
+  // ---- decision and outputs (uniform over the workgroup; thread 0 writes scalars) ----
+  bool invalid = false, rejected_now = false;
+  int final_tok = -1, x_s = -1;
+  float logq_s = NAN;
+  if (hasD) {
+    const float lse_q = tot_d.x;
+    if (!isfinite(lse_q) || rd.v < 0) {
+      invalid = true;
+    } else {
+      x_s = rd.v;
+      logq_s = rd.sx - lse_q;
+      if (tid == 0) {
+        st_i32(&p.xs[(size_t)b * K + s], x_s);
+        st_f32(&p.lse_q[(size_t)b * K + s], lse_q);
+        if (p.a.d_draft) p.a.d_draft[(size_t)b * K + s] = x_s;
+        if (p.a.d_logq) p.a.d_logq[(size_t)b * K + s] = logq_s;
+      }
+    }
+  }
+  if (!invalid && (roles & RO_LSEP)) {
+    const float lse_p = tot_p.x;
+    if (!isfinite(lse_p) || x_s < 0) {
+      invalid = true;
+    } else {
+      const float logp_s = rd.tx * invT - lse_p;
+      const uint32_t ub = bits_at(pos_key(kreq, s, ST_ACCEPT), 0);
+      const double u = ((double)ub + 0.5) * 0x1p-32;
+      const double ratio = exp((double)logp_s - (double)logq_s);
+      if (u < ratio) {
+        acc = s + 1;
+      } else {
+        phase = PH_REJECTED;
+        rejected_now = true;
+      }
+      if (tid == 0) {
+        st_f32(&p.lse_p[(size_t)b * (K + 1) + s], lse_p);
+        if (p.a.d_logp) p.a.d_logp[(size_t)b * K + s] = logp_s;
+      }
+    }
+  }
+  if (!invalid && (roles & RO_BONUS)) {
+    if (!isfinite(tot_p.x)) invalid = true;
+    else final_tok = rf.v;
+    if (final_tok < 0) invalid = true;
+  }
+  if (!invalid && hasC) {
+    final_tok = rf.v;
+    if (final_tok < 0) invalid = true;
+  }
+  if (invalid) {
+    if (tid <= K) p.a.tokens[(size_t)b * (K + 1) + tid] = -1;
+    if (tid < K) {
+      if (p.a.d_draft) p.a.d_draft[(size_t)b * K + tid] = -1;
+      if (p.a.d_logq) p.a.d_logq[(size_t)b * K + tid] = NAN;
+      if (p.a.d_logp) p.a.d_logp[(size_t)b * K + tid] = NAN;
+    }
+    if (tid == 0) {
+      p.a.accepted_len[b] = -1;
+      if (p.a.d_verify_len) p.a.d_verify_len[b] = -1;
+      p.st[ST_PHASE * B + b] = PH_INVALID;
+      p.st[ST_ACC * B + b] = acc;
+      st_i32(&roles_next[b], 0);
+    }
+    return;
+  }
+  if (final_tok >= 0) {
+    phase = PH_DONE;
+    if (tid < acc) p.a.tokens[(size_t)b * (K + 1) + tid] = x_t;   // tid < acc <= s: drafted before this step
+    if (tid == acc) p.a.tokens[(size_t)b * (K + 1) + tid] = final_tok;
+    if (tid == 0) p.a.accepted_len[b] = acc;
+  }
+  if (tid == 0) {
+    int nr = 0;
+    if (s + 1 < L) nr |= RO_DRAFT;
+    if (phase == PH_ALIVE && acc == s + 1) nr |= (s + 1 < L) ? RO_LSEP : RO_BONUS;
+    if (rejected_now) nr |= RO_CORRECT;
+    p.st[ST_PHASE * B + b] = phase;
+    p.st[ST_ACC * B + b] = acc;
+    st_i32(&roles_next[b], nr);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// the kernel
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  const int B = p.a.B, K = p.a.K, V = p.a.V, G = p.a.G;
+  Smem S = carve(smem_raw, B);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int g = blockIdx.x;
+  const int cbeg = chunk_begin(g, G, V), nch = chunks_of(g, G, V);
+  const int n_lds = nch > NW * AG_CHUNKS ? nch - NW * AG_CHUNKS : 0;   // 0..2 LDS chunks
+
+  // ---- W slice on chip: this wave's two register chunks, and the workgroup's LDS tiles ----
+  bf16x8 wf[4][KSTEPS];   // [tile: chunk 2 wave + tile / 2, half tile % 2][k-step]
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int cl = AG_CHUNKS * wave + (i >> 1);
+    const int c = cl < nch ? cbeg + cl : -1;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; t++) wf[i][t] = w_frag(p, c, i & 1, t);
+  }
+  // LDS tile u = 2 (local chunk - 8) + half, processed by wave u
+  for (int e = threadIdx.x; e < 4 * KSTEPS * 64; e += NT) {
+    const int u = e / (KSTEPS * 64), t = (e / 64) % KSTEPS, l = e % 64;
+    const int cl = NW * AG_CHUNKS + (u >> 1);
+    const int c = cl < nch ? cbeg + cl : -1;
+    // the fragment of lane l: same mapping as w_frag, computed for lane l
+    const int mm = l & 31, hh = l >> 5;
+    const int col_in = 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
+    const int v = CH * c + 32 * (u & 1) + col_in;
+    bf16x8 z;
+#pragma unroll
+    for (int i = 0; i < 8; i++) z[i] = (__bf16)0.0f;
+    if (c >= 0 && v < V && t < (p.a.R >> 4))
+      z = *(const bf16x8*)((const uint16_t*)p.a.W + (size_t)v * p.a.R + hh * (p.a.R >> 1) + 8 * t);
+    S.wl[e] = z;
+  }
+
+  // ---- set-up: verify lengths and validity of every request (every workgroup, redundantly);
+  // the merge wave of a request initialises its outputs ----
+  const uint64_t seed = p.a.seed;
+  for (int b = threadIdx.x; b < B; b += NT) {
+    const float T = p.a.temp[b];
+    const int x0 = p.a.x0 ? p.a.x0[b] : -1;
+    bool valid = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < V;
+    int L = 0;
+    if (p.a.L_in) {
+      L = p.a.L_in[b];
+      if (L < 0 || L > K) {
+        valid = false;
+        L = 0;
+      }
+    } else {
+      double P = 1.0;
+      for (int j = 0; j < K; j++) {
+        P *= (double)p.a.conf[(size_t)b * K + j];
+        if (!(P >= (double)p.a.threshold)) break;
+        L = j + 1;
+      }
+    }
+    S.Lq[b] = (uint8_t)L;
+    S.role[b] = valid ? (uint8_t)(L > 0 ? (RO_DRAFT | RO_LSEP) : RO_BONUS) : (uint8_t)0;
+  }
+  __syncthreads();
+  // outputs and state of the requests this workgroup merges (request b: workgroup b % G, wave b / G)
+  for (int i = threadIdx.x; i < NW * (K + 1); i += NT) {
+    const int w = i / (K + 1), j = i % (K + 1);
+    const int b = g + G * w;
+    if (b >= B) continue;
+    p.a.tokens[(size_t)b * (K + 1) + j] = -1;
+    if (j < K) {
+      if (p.a.d_draft) p.a.d_draft[(size_t)b * K + j] = -1;
+      if (p.a.d_logq) p.a.d_logq[(size_t)b * K + j] = NAN;
+      if (p.a.d_logp) p.a.d_logp[(size_t)b * K + j] = NAN;
+    }
+    if (j == 0) {
+      const bool valid = S.role[b] != 0;
+      p.a.accepted_len[b] = -1;
+      if (p.a.d_verify_len) p.a.d_verify_len[b] = valid ? (int)S.Lq[b] : -1;
+      p.st[ST_ACC * B + b] = 0;
+      p.st[ST_PHASE * B + b] = valid ? PH_ALIVE : PH_INVALID;
+    }
+  }
+
+  uint64_t token = p.a.nonce;
+  for (int s = 0; s <= K; s++) {
+    // lane-derived values are redefined opaquely at every step, so that addresses built from them
+    // are computed where they are used instead of being kept in registers across the whole loop
+    int tid = opaque_tid();
+#define lane (tid & 63)
+#define m32 (tid & 31)
+#define h ((tid >> 5) & 1)
+    // ---- 1. roles of step s -> lists and the per-request table ----
+    if (s > 0) {
+      for (int b = tid; b < B; b += NT) S.role[b] = (uint8_t)ld_i32(&p.st[(ST_ROLES + (s & 1)) * B + b]);
+      __syncthreads();
+    }
+    Lists ls;
+    {
+      // requests in rounds of NT (request i NT + tid in round i); within a round every wave counts
+      // its rows with ballots, the waves' counts are combined in LDS; slots follow the order
+      // (round, wave, lane).  CORRECT slots are taken relative first and moved behind the DRAFT
+      // rows once their number is known.
+      int nd = 0, nc = 0, np = 0;
+      const int rounds = (B + NT - 1) / NT;
+      for (int i = 0; i < rounds; i++) {
+        const int b = i * NT + tid;
+        const int r = b < B ? S.role[b] : 0;
+        const uint64_t md = __ballot((r & RO_DRAFT) != 0), mc = __ballot((r & RO_CORRECT) != 0),
+                       mp = __ballot((r & (RO_LSEP | RO_BONUS)) != 0);
+        auto below = [&](uint64_t m) {   // set bits of m in lanes below this one
+          return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        };
+        if (lane == 0) S.wcnt[wave] = make_int4(__popcll(md), __popcll(mc), __popcll(mp), 0);
+        __syncthreads();
+        int od = nd, oc = nc, op = np;
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+          const int4 c = S.wcnt[w];
+          if (w < wave) {
+            od += c.x;
+            oc += c.y;
+            op += c.z;
+          }
+          nd += c.x;
+          nc += c.y;
+          np += c.z;
+        }
+        if (b < B) {
+          uint16_t sd = 0xFFFF, sc = 0xFFFF, sp = 0xFFFF;
+          if (r & RO_DRAFT) sd = (uint16_t)(od + below(md));
+          if (r & RO_CORRECT) sc = (uint16_t)(oc + below(mc));   // relative to the first CORRECT slot
+          if (r & (RO_LSEP | RO_BONUS)) {
+            sp = (uint16_t)(op + below(mp));
+            S.plist[sp] = (uint16_t)b;
+          }
+          S.slot[b] = sd;
+          S.slot[B + b] = sc;
+          S.slot[2 * B + b] = sp;
+          if (r) {
+            const int x0 = p.a.x0 ? p.a.x0[b] : -1;
+            const int32_t* xr = p.xs + (size_t)b * K;
+            ReqMeta m;
+            m.prev_d = (s == 0) ? x0 : ld_i32(&xr[s - 1]);
+            m.prev_c = (s <= 1) ? x0 : ld_i32(&xr[s - 2]);
+            m.invT = 1.0f / p.a.temp[b];
+            const int jc = s > 0 ? s - 1 : 0;
+            m.lse_p_c = ld_f32(&p.lse_p[(size_t)b * (K + 1) + jc]);
+            m.lse_q_c = ld_f32(&p.lse_q[(size_t)b * K + jc]);
+            const uint64_t kr = req_key(seed, p.a.req_off + b);
+            put_key(m.key_d, pos_key(kr, s, ST_DRAFT_C));
+            put_key(m.key_c, pos_key(kr, jc, ST_RESIDUAL_C));
+            S.req[b] = m;
+            if (r & RO_DRAFT) S.blist[sd] = ent_make(b, false, m.prev_d);
+          }
+        }
+        __syncthreads();   // the wave counts are read before the next round writes them
+      }
+      ls.n_draft = nd;
+      ls.n_correct = nc;
+      ls.n_plain = np;
+      ls.c0 = (nd + SUB - 1) / SUB * SUB;
+      ls.n_sb = (ls.c0 + nc + SUB - 1) / SUB;
+      for (int b = tid; b < B; b += NT) {
+        const uint16_t rc = S.slot[B + b];
+        if (rc != 0xFFFF) {
+          S.slot[B + b] = (uint16_t)(ls.c0 + rc);
+          S.blist[ls.c0 + rc] = ent_make(b, true, S.req[b].prev_c);
+        }
+      }
+      if (tid < SUB) {
+        const int gi = ls.n_draft + tid;
+        if (gi < ls.c0) S.blist[gi] = NO_ENT;
+        const int ti = ls.c0 + ls.n_correct + tid;
+        if (ti < ls.n_sb * SUB) S.blist[ti] = NO_ENT;
+      }
+      __syncthreads();
+    }
+    if (ls.n_sb == 0 && ls.n_plain == 0) break;   // uniform over the grid: every workgroup read the same roles
+
+    // ---- 2. bias sub-blocks ----
+    // row of sub-block k for this lane, and its tile loads
+    auto row_of = [&](int k, int& b, int& j, bool& corr) {
+      const uint32_t e = S.blist[k * SUB + m32];
+      const bool has = e != NO_ENT;
+      b = has ? ent_req(e) : -1;
+      corr = has && (e & 1u);
+      j = corr ? s - 1 : s;
+    };
+    // stage the B operands of sub-block k into sA[k & 1] (every thread 4 of the 1024 16-byte entries);
+    // a slot without a row, or k-steps past the rank, read row 0 and take zeros (the load address
+    // stays inside A, so every load is an ordinary global load)
+    auto stage_issue = [&](int k, u32x4 (&v)[4], int& vin) {
+      vin = 0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int e = tid + NT * i;
+        const int t = e >> 6, l = e & 63;
+        const uint32_t ent = (k < ls.n_sb) ? S.blist[k * SUB + (l & 31)] : NO_ENT;
+        const int prev = ent == NO_ENT ? -1 : ent_prev(ent);
+        const bool in = prev >= 0 && t < (p.a.R >> 4);
+        v[i] = ldg16((const uint16_t*)p.a.A + (in ? (size_t)prev * p.a.R + (l >> 5) * (p.a.R >> 1) + 8 * t : 0));
+        vin |= in ? (1 << i) : 0;
+      }
+    };
+    auto stage_store = [&](int k, const u32x4 (&v)[4], int vin) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int e = tid + NT * i;
+        ((u32x4*)S.sA)[(k & 1) * KSTEPS * 64 + e] = ((vin >> i) & 1) ? v[i] : kZero;
+      }
+    };
+    // the lane's logits of tile i (0..3: register chunks of this wave; 4: its LDS tile) in row (b, j):
+    // 16 columns starting at 64 c + 32 f + 16 h as two 16-byte pieces; columns past V, past the
+    // workgroup's chunks, or of a slot without a row read -inf (the address is clamped to the
+    // tensor's first element and the value replaced)
+    auto tile_cols = [&](int i) -> int {
+      int cl, f;
+      if (i < 4) {
+        cl = AG_CHUNKS * wave + (i >> 1);
+        f = i & 1;
+      } else {
+        cl = NW * AG_CHUNKS + (wave >> 1);
+        f = wave & 1;
+      }
+      if (cl >= nch) return -1;
+      return CH * (cbeg + cl) + 32 * f + 16 * h;
+    };
+    auto load_tile = [&](const void* rows, int b, int j, int nrow, int i, u32x4 (&T)[2]) {
+      const int v0 = tile_cols(i);
+      const bool in = b >= 0 && v0 >= 0 && v0 < V;
+      const bool in2 = in && v0 + 8 < V;
+      const uint16_t* r = (const uint16_t*)rows + ((size_t)(b >= 0 ? b : 0) * nrow + j) * V;
+      T[0] = ldg16(r + (in ? v0 : 0));
+      T[1] = ldg16(r + (in2 ? v0 + 8 : 0));
+    };
+    auto load_tiles = [&](const void* rows, int b, int j, int nrow, u32x4 (&T)[5][2]) {
+#pragma unroll
+      for (int i = 0; i < 5; i++) load_tile(rows, b, j, nrow, i, T[i]);
+    };
+    // columns of tile i past V read -inf (bit 2i: the first 8 columns are inside, bit 2i+1: the
+    // last 8); the same for every row, so the mask is built once
+    int colmask = 0;
+#pragma unroll
+    for (int i = 0; i < 5; i++) {
+      const int v0 = tile_cols(i);
+      colmask |= (v0 >= 0 && v0 < V) ? (1 << (2 * i)) : 0;
+      colmask |= (v0 >= 0 && v0 + 8 < V) ? (2 << (2 * i)) : 0;
+    }
+    auto seed_acc = [&](const u32x4 (&tt)[2], int i) -> f32x16 {
+      float x[16];
+      const u32x4 t0 = ((colmask >> (2 * i)) & 1) ? tt[0] : kNegInf;
+      const u32x4 t1 = ((colmask >> (2 * i)) & 2) ? tt[1] : kNegInf;
+      unpack16(t0, t1, x);
+      f32x16 a;
+#pragma unroll
+      for (int q = 0; q < 16; q++) a[q] = x[q];
+      return a;
+    };
+
+    // Per sub-block, three MFMA passes in turn: register chunk 0 (tiles 0, 1), register chunk 1
+    // (tiles 2, 3), the LDS half chunk (tile 4; waves without one run it on zero W and -inf
+    // logits, which costs no time: the workgroup waits for the waves that have one).  The
+    // element-wise part of each pass follows the next pass's MFMA chain in program order, so the
+    // two overlap; only 2 or 3 tiles of accumulators are live at a time.
+    const bool wave_lds = 2 * n_lds > wave;     // this wave has an LDS tile (wave-uniform)
+    const int cg0 = cbeg + AG_CHUNKS * wave;   // global chunk of this wave's register chunk 0
+    const bool has0 = AG_CHUNKS * wave < nch, has1 = AG_CHUNKS * wave + 1 < nch;
+    const bf16x8* wlw = S.wl + (size_t)wave * KSTEPS * 64;
+    u32x4 Tc[5][2];                            // draft logits of the current sub-block
+    if (ls.n_sb > 0) {
+      u32x4 sv[4];
+      int vin;
+      stage_issue(0, sv, vin);
+      int b, j;
+      bool corr;
+      row_of(0, b, j, corr);
+      load_tiles(p.a.base, b, j, K, Tc);
+      stage_store(0, sv, vin);
+    }
+    __syncthreads();
+    for (int k = 0; k < ls.n_sb; k++) {
+      tid = opaque_tid();
+        int b, j;
+      bool corr;
+      row_of(k, b, j, corr);
+      const bool is_corr_sb = k * SUB >= ls.c0;     // uniform: no sub-block mixes DRAFT and CORRECT rows
+      const ReqMeta rm = S.req[b >= 0 ? b : 0];
+      const float invT = b >= 0 ? rm.invT : 1.0f;
+      const bf16x8* sAk = S.sA + (size_t)(k & 1) * KSTEPS * 64;
+      // in flight during this sub-block: the next sub-block's B operands, and its draft logits,
+      // each tile loaded into the registers its predecessor leaves when it seeds its pass (a
+      // CORRECT sub-block loads its own target logits instead and the next draft logits last)
+      u32x4 sv[4];
+      int vin;
+      stage_issue(k + 1, sv, vin);
+      u32x4 Tt[5][2];
+      int b2 = -1, j2 = 0;
+      bool c2 = false;
+      if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
+      const bool pre = !is_corr_sb;                 // uniform
+      if (!pre) load_tiles(p.a.target, b, j, K + 1, Tt);
+      if (is_corr_sb) {
+        // target pieces past V read -inf (their residual and target mass are then zero)
+#pragma unroll
+        for (int i = 0; i < 5; i++) {
+          Tt[i][0] = ((colmask >> (2 * i)) & 1) ? Tt[i][0] : kNegInf;
+          Tt[i][1] = ((colmask >> (2 * i)) & 2) ? Tt[i][1] : kNegInf;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) asm volatile("" : "+a"(wf[i][t]));
+
+      // pass 0: register chunk 0
+      f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
+      if (pre) {
+        load_tile(p.a.base, b2, j2, K, 0, Tc[0]);
+        load_tile(p.a.base, b2, j2, K, 1, Tc[1]);
+      }
+      {
+        bf16x8 bop = sAk[lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          const bf16x8 bop_n = (t + 1 < KSTEPS) ? sAk[(t + 1) * 64 + lane] : bop;
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, a1, 0, 0, 0);
+          bop = bop_n;
+        }
+      }
+      // pass 1: register chunk 1, with the element-wise part of pass 0 after it
+      f32x16 a2 = seed_acc(Tc[2], 2), a3 = seed_acc(Tc[3], 3);
+      if (pre) {
+        load_tile(p.a.base, b2, j2, K, 2, Tc[2]);
+        load_tile(p.a.base, b2, j2, K, 3, Tc[3]);
+      }
+      {
+        bf16x8 bop = sAk[lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          const bf16x8 bop_n = (t + 1 < KSTEPS) ? sAk[(t + 1) * 64 + lane] : bop;
+          a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[2][t], bop, a2, 0, 0, 0);
+          a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[3][t], bop, a3, 0, 0, 0);
+          bop = bop_n;
+        }
+      }
+      WaveRec wr;
+      const uint64_t key = is_corr_sb ? key_of(rm.key_c) : key_of(rm.key_d);
+      const float g0 = gumbel_bits(bits_at(key, (uint32_t)cg0));
+      const float g1 = gumbel_bits(bits_at(key, (uint32_t)(cg0 + 1)));
+      float l0 = -INFINITY, m0 = 0.0f, t0 = -INFINITY;
+      if (!is_corr_sb) {
+        f32x16 aa[2] = {a0, a1};
+        l0 = tiles_lse<2>(aa, invT);
+      } else {
+        chunk_correct(a0, a1, Tt[0][0], Tt[0][1], Tt[1][0], Tt[1][1], invT, rm.lse_p_c, rm.lse_q_c, m0, t0);
+      }
+      // pass L: the LDS half chunk, with the element-wise part of pass 1 after it
+      f32x16 a4 = seed_acc(Tc[4], 4);
+      if (pre) load_tile(p.a.base, b2, j2, K, 4, Tc[4]);
+      {
+        bf16x8 bop = sAk[lane], wl = wlw[lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          const bf16x8 bop_n = (t + 1 < KSTEPS) ? sAk[(t + 1) * 64 + lane] : bop;
+          const bf16x8 wl_n = (t + 1 < KSTEPS) ? wlw[(t + 1) * 64 + lane] : wl;
+          a4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, bop, a4, 0, 0, 0);
+          bop = bop_n;
+          wl = wl_n;
+        }
+      }
+      float l1 = -INFINITY, m1 = 0.0f, t1 = -INFINITY, hl = -INFINITY, mh = 0.0f, th = -INFINITY;
+      if (!is_corr_sb) {
+        f32x16 aa[2] = {a2, a3};
+        l1 = tiles_lse<2>(aa, invT);
+        hl = tiles_lse<1>(&a4, invT);
+      } else {
+        chunk_correct(a2, a3, Tt[2][0], Tt[2][1], Tt[3][0], Tt[3][1], invT, rm.lse_p_c, rm.lse_q_c, m1, t1);
+        float yl[16];
+#pragma unroll
+        for (int q = 0; q < 16; q++) yl[q] = a4[q];
+        pair_correct<2>(yl, Tt[4], invT, rm.lse_p_c, rm.lse_q_c, mh, th);
+      }
+      if (!has0) {
+        l0 = -INFINITY;
+        m0 = 0.0f;
+        t0 = -INFINITY;
+      }
+      if (!has1) {
+        l1 = -INFINITY;
+        m1 = 0.0f;
+        t1 = -INFINITY;
+      }
+      if (!wave_lds) {
+        hl = -INFINITY;
+        mh = 0.0f;
+        th = -INFINITY;
+      }
+      if (!is_corr_sb) {
+        const float s0 = (l0 > -INFINITY) ? l0 + g0 : -INFINITY;
+        const float s1 = (l1 > -INFINITY) ? l1 + g1 : -INFINITY;
+        float bs = -INFINITY;
+        int bc = -1;
+        if (has0 && !(l0 != l0)) { bs = s0; bc = cg0; }
+        if (has1 && takes(s1, cg0 + 1, bs, bc)) { bs = s1; bc = cg0 + 1; }
+        wr.a = make_float4(lse_add(l0, l1), bs, __int_as_float(bc), hl);
+        wr.t = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), -INFINITY);
+      } else {
+        const float lm0 = m0 > 0.0f ? lg2(m0) * LN2 : -INFINITY;
+        const float lm1 = m1 > 0.0f ? lg2(m1) * LN2 : -INFINITY;
+        float bs = -INFINITY, bt = -INFINITY;
+        int bc = -1, btc = -1;
+        if (lm0 > -INFINITY) { bs = lm0 + g0; bc = cg0; }
+        if (lm1 > -INFINITY && takes(lm1 + g1, cg0 + 1, bs, bc)) { bs = lm1 + g1; bc = cg0 + 1; }
+        if (has0 && t0 > -INFINITY) { bt = t0 + g0; btc = cg0; }
+        if (has1 && t1 > -INFINITY && takes(t1 + g1, cg0 + 1, bt, btc)) { bt = t1 + g1; btc = cg0 + 1; }
+        const float msum = m0 + m1;
+        wr.a = make_float4(msum > 0.0f ? lg2(msum) * LN2 : -INFINITY, bs, __int_as_float(bc), mh);
+        wr.t = make_float4(lse_add(t0, t1), bt, __int_as_float(btc), th);
+        // the next (CORRECT) sub-block's draft logits: its latency is not hidden, CORRECT
+        // sub-blocks are few
+        load_tiles(p.a.base, b2, j2, K, Tc);
+      }
+      // this wave's record of each row of the sub-block (the merge combines the waves)
+      if (h == 0 && b >= 0) {
+        const size_t ri = ((size_t)(k * SUB + m32) * G + g) * NW + wave;
+        rec_store(&p.rec_d[ri], wr.a);
+        if (is_corr_sb) rec_store(&p.rec_c[ri], wr.t);
+      }
+      stage_store(k + 1, sv, vin);
+      __syncthreads();
+    }
+
+    // ---- 3. plain rows: every LSEP / BONUS target row in contiguous items of TP columns, the
+    //         items of all plain rows spread over all waves of the grid (target rows need no W,
+    //         so they are not tied to a workgroup's vocabulary slice) ----
+    {
+      const int nrP = (V + TP - 1) / TP;
+      const int n_items = ls.n_plain * nrP;
+      const int GW = G * NW;
+      constexpr int NQ = PLAIN_INFLIGHT;
+      for (int it0 = g * NW + wave; it0 < n_items; it0 += NQ * GW) {
+        u32x4 x[NQ][TP / 512];
+        int ps[NQ], rb[NQ], t[NQ], xin[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; q++) {
+          const int it = it0 + q * GW;
+          ps[q] = it < n_items ? it / nrP : -1;
+          t[q] = it < n_items ? it - ps[q] * nrP : 0;
+          rb[q] = ps[q] >= 0 ? S.plist[ps[q]] : -1;
+          const uint16_t* row = (const uint16_t*)p.a.target + ((size_t)(rb[q] >= 0 ? rb[q] : 0) * (K + 1) + s) * V;
+          xin[q] = 0;
+#pragma unroll
+          for (int i = 0; i < TP / 512; i++) {
+            const int col = t[q] * TP + (i * 64 + lane) * 8;
+            const bool in = rb[q] >= 0 && col < V;
+            x[q][i] = ldg16(row + (in ? col : 0));
+            xin[q] |= in ? (1 << i) : 0;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; q++) {
+          if (rb[q] < 0) continue;   // wave-uniform
+          const int rr = S.role[rb[q]];
+          const float invT = S.req[rb[q]].invT;
+          const float c = invT * LOG2E;
+          float4 rec;
+          if (rr & RO_LSEP) {
+            // the item's log-mass in one pass: lane maximum, wave maximum, one scaled sum
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < TP / 512; i++) {
+              const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
+#pragma unroll
+              for (int e = 0; e < 4; e++) mx = fmaxf(mx, fmaxf(bf_lo(w[e]), bf_hi(w[e])));
+            }
+            mx = wmax(mx);
+            const float mo = (mx == -INFINITY) ? 0.0f : mx * c;
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < TP / 512; i++) {
+              const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
+#pragma unroll
+              for (int e = 0; e < 4; e++) {
+                s0 += ex2(fmaf(bf_lo(w[e]), c, -mo));
+                s1 += ex2(fmaf(bf_hi(w[e]), c, -mo));
+              }
+            }
+            const float sm = wsum(s0 + s1);
+            const float lse = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
+            rec = make_float4(lse, -INFINITY, __int_as_float(-1), 0.0f);
+          } else {
+            // BONUS: the log-mass of each 64-column chunk (8 lanes per chunk in every load), its
+            // Gumbel score, the best chunk, and the item's log-mass from the chunks'
+            const uint64_t key = pos_key(req_key(seed, p.a.req_off + rb[q]), s, ST_BONUS_C);
+            float lse_tot = -INFINITY, bs = -INFINITY, dummy = 0.0f;
+            int bc = -1;
+#pragma unroll
+            for (int i = 0; i < TP / 512; i++) {
+              const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
+              float mx = -INFINITY;
+#pragma unroll
+              for (int e = 0; e < 4; e++) mx = fmaxf(mx, fmaxf(bf_lo(w[e]), bf_hi(w[e])));
+              mx = max8(mx);
+              const float mo = (mx == -INFINITY) ? 0.0f : mx * c;
+              float sm = 0.0f;
+#pragma unroll
+              for (int e = 0; e < 4; e++) sm += ex2(fmaf(bf_lo(w[e]), c, -mo)) + ex2(fmaf(bf_hi(w[e]), c, -mo));
+              sm = sum8(sm);
+              const float lc = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
+              const int cg = (t[q] * TP + (i * 64 + lane) * 8) / CH;   // global chunk of this lane's piece
+              const bool own = ((lane & 7) == 0) && cg * CH < V;
+              if (own) {
+                lse_tot = lse_add(lse_tot, lc);
+                const float sc = lc > -INFINITY ? lc + gumbel_bits(bits_at(key, (uint32_t)cg)) : -INFINITY;
+                if (lc > -INFINITY && takes(sc, cg, bs, bc)) {
+                  bs = sc;
+                  bc = cg;
+                }
+              }
+            }
+            // wave log-sum-exp of the owners' chunk masses and the wave argmax of their scores
+            {
+              const float M = wmax(lse_tot);
+              const float e = (lse_tot == -INFINITY) ? 0.0f : ex2((lse_tot - (M == -INFINITY ? 0.0f : M)) * LOG2E);
+              const int nan = __ballot(lse_tot != lse_tot) != 0ull;
+              const float S_ = wsum(e);
+              lse_tot = nan ? NAN : (M == -INFINITY ? -INFINITY : M + lg2(S_) * LN2);
+            }
+            wargmax(bs, bc, dummy);
+            rec = make_float4(lse_tot, bs, __int_as_float(bc), 0.0f);
+          }
+          if (lane == 0) rec_store(&p.rec_p[(size_t)ps[q] * MAX_G + t[q]], rec);
+        }
+      }
+    }
+
+    // ---- 4. grid barrier: every record of step s is written ----
+    grid_barrier(p.flags, p.err, p.a.nonce, G, token++);
+
+    // ---- 5. merges: this workgroup's requests b = g, g + G, ... one after another ----
+    for (int r = 0; r < NW; r++) {
+      const int b = g + G * r;
+      if (b >= B) break;
+      merge_request(p, S, b, s);
+    }
+
+    // ---- 6. grid barrier: roles, drafted tokens and log-normalisers of step s are written ----
+    grid_barrier(p.flags, p.err, p.a.nonce, G, token++);
+  }
+#undef lane
+#undef m32
+#undef h
+  // a synchronisation fault: every request this workgroup merges is marked invalid
+  if (failed(p.err, p.a.nonce)) {
+    for (int i = threadIdx.x; i < NW * (K + 1); i += NT) {
+      const int w = i / (K + 1), j = i % (K + 1);
+      const int b = g + G * w;
+      if (b >= B) continue;
+      p.a.tokens[(size_t)b * (K + 1) + j] = -1;
+      if (j == 0) p.a.accepted_len[b] = -1;
+    }
+  }
+}
+
+}  // namespace res
+}  // namespace spec
+
+// ------------------------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------------------------
+namespace spec {
+namespace res {
+
+// Barrier tokens of one call are nonce + i (i < 2^16).  Nonces are distinct across the calls of a
+// process (a counter) and across processes (the counter starts from a hash of the time, the
+// process id and an address), with the low 16 bits zero.
+static uint64_t next_nonce() {
+  static std::atomic<uint64_t> ctr{0};
+  static const uint64_t salt = [] {
+    uint64_t x = (uint64_t)time(nullptr) * 0x9E3779B97F4A7C15ull;
+    x ^= (uint64_t)getpid() << 32;
+    x ^= (uint64_t)(uintptr_t)&ctr;
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    return x ^ (x >> 31);
+  }();
+  uint64_t z = salt + (ctr.fetch_add(1, std::memory_order_relaxed) + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z & ~(TOKEN_WINDOW - 1);
+}
+
+int launch(const Args& a_in, void* stream, void* ev_start, void* ev_stop) {
+  Args a = a_in;
+  a.nonce = next_nonce();
+  const Layout l = layout(a.B, a.K);
+  KP p;
+  p.a = a;
+  char* ws = a.ws;
+  p.st = (int32_t*)(ws + l.off_state);
+  p.xs = (int32_t*)(ws + l.off_xs);
+  float* f = (float*)(ws + l.off_f);
+  const size_t nf = (size_t)a.B * (a.K + 1);
+  p.lse_q = f;
+  p.logq = f + nf;
+  p.lse_p = f + 2 * nf;
+  p.logp = f + 3 * nf;
+  p.rec_d = (float4*)(ws + l.off_rec_d);
+  p.rec_c = (float4*)(ws + l.off_rec_c);
+  p.rec_p = (float4*)(ws + l.off_rec_p);
+  p.flags = (uint64_t*)(ws + l.off_flags);
+  p.err = p.flags + (size_t)MAX_G * FLAG_STRIDE;
+  const size_t lds = smem_bytes(a.B);
+  // the dynamic LDS ceiling, once per device
+  static std::atomic<int> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_HIP;
+  if (dev < 0 || dev >= 64 || attr_set[dev].load(std::memory_order_acquire) == 0) {
+    if (hipFuncSetAttribute((const void*)k_resident, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)smem_bytes(MAX_B)) != hipSuccess)
+      return SPEC_E_HIP;
+    if (dev >= 0 && dev < 64) attr_set[dev].store(1, std::memory_order_release);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (ev_start && hipEventRecord((hipEvent_t)ev_start, st) != hipSuccess) return SPEC_E_HIP;
+  void* args[] = {&p};
+  if (hipLaunchCooperativeKernel((const void*)k_resident, dim3(a.G), dim3(NT), args, (unsigned)lds, st) != hipSuccess)
+    return SPEC_E_HIP;
+  if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, st) != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
+}
+
+
+}  // namespace res
+}  // namespace spec

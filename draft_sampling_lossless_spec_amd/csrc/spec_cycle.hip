@@ -35,6 +35,7 @@
 
 #include "spec_cycle.h"
 #include "device_common.h"
+#include "resident.h"
 
 namespace spec {
 
@@ -2473,6 +2474,40 @@ static int arch_ok() {
   return ok > 0 ? SPEC_OK : SPEC_E_ARCH;
 }
 
+// Cooperative launches on the current device (the resident path needs its whole grid resident).
+static bool coop_ok() {
+  static std::atomic<int> cache[MAX_DEV];   // 0 unknown, 1 supported, -1 not
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  int c = (dev >= 0 && dev < MAX_DEV) ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (c == 0) {
+    int v = 0;
+    c = (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && v != 0) ? 1 : -1;
+    if (dev >= 0 && dev < MAX_DEV) cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c > 0;
+}
+
+// The path a call takes: SPEC_PATH_STEPWISE, SPEC_PATH_RESIDENT, or a negative error code.
+// `aligned`: the logit rows allow 16-byte vector loads.
+static int resolve_path(const spec_dims* d, bool aligned) {
+  if (d->path == SPEC_PATH_STEPWISE) return SPEC_PATH_STEPWISE;
+  const bool fits = aligned && res::eligible(d->B, d->K, d->V, d->R, d->dtype, d->noise, cu_count()) && coop_ok();
+  if (d->path == SPEC_PATH_RESIDENT) return fits ? SPEC_PATH_RESIDENT : SPEC_E_DTYPE;
+  if (d->path != SPEC_PATH_AUTO) return SPEC_E_INVAL;
+  // the automatic choice: the resident path once it is the faster one on the workloads measured
+  constexpr bool AUTO_RESIDENT = false;
+  return (AUTO_RESIDENT && fits) ? SPEC_PATH_RESIDENT : SPEC_PATH_STEPWISE;
+}
+
+// Workspace of a call on `path` (SPEC_PATH_AUTO: enough for either path).
+static size_t need_bytes(const spec_dims* d, int path) {
+  const size_t st = layout(d).total, rs = res::workspace_bytes(d->B, d->K);
+  if (path == SPEC_PATH_STEPWISE) return st;
+  if (path == SPEC_PATH_RESIDENT) return rs;
+  return st > rs ? st : rs;
+}
+
 // k_sweep_fast: bias slots whose A rows are staged in LDS, the largest whole number of sub-blocks
 // that fits next to the per-request table in the 160 KiB of a workgroup (nine at B <= 256)
 // dynamic LDS ceiling of k_sweep_fast: the 160 KiB of a workgroup less its static scan buffer
@@ -2546,7 +2581,14 @@ using namespace spec;
 
 extern "C" size_t spec_workspace_bytes(const spec_dims* d) {
   if (!dims_ok(d) || !dtype_ok(d)) return 0;
-  return layout(d).total;
+  if (d->path != SPEC_PATH_AUTO && d->path != SPEC_PATH_STEPWISE && d->path != SPEC_PATH_RESIDENT) return 0;
+  return need_bytes(d, d->path);
+}
+
+extern "C" int spec_cycle_path(const spec_dims* d) {
+  if (!dims_ok(d)) return SPEC_E_INVAL;
+  if (!dtype_ok(d)) return SPEC_E_DTYPE;
+  return resolve_path(d, true);
 }
 
 extern "C" const char* spec_error_string(int code) {
@@ -2575,9 +2617,48 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
     return SPEC_E_INVAL;
   if ((((uintptr_t)A) | ((uintptr_t)W)) & 15) return SPEC_E_INVAL;
   const Layout l = layout(d);
-  if (!workspace || workspace_bytes < l.total || (((uintptr_t)workspace) & 255)) return SPEC_E_WORKSPACE;
+  // vector loads need 16-byte aligned rows
+  const size_t esz = d->dtype == SPEC_FP32 ? 4 : 2;
+  const bool vec = ((d->V * esz) % 16 == 0) && ((((uintptr_t)base_logits) | ((uintptr_t)target_logits)) & 15) == 0;
+  if (d->path != SPEC_PATH_AUTO && d->path != SPEC_PATH_STEPWISE && d->path != SPEC_PATH_RESIDENT)
+    return SPEC_E_INVAL;
+  // the workspace the caller sized for the path it asked for (AUTO: either path)
+  if (!workspace || workspace_bytes < need_bytes(d, d->path) || (((uintptr_t)workspace) & 255))
+    return SPEC_E_WORKSPACE;
   const int ac = arch_ok();
   if (ac != SPEC_OK) return ac;
+  const int path = resolve_path(d, vec);
+  if (path < 0) return path;
+  hipStream_t st = (hipStream_t)stream;
+  if (path == SPEC_PATH_RESIDENT) {
+    res::Args a;
+    a.B = d->B;
+    a.K = d->K;
+    a.V = d->V;
+    a.R = d->R;
+    a.base = base_logits;
+    a.target = target_logits;
+    a.A = A;
+    a.W = W;
+    a.x0 = x0;
+    a.conf = conf;
+    a.temp = temp;
+    a.L_in = L_in;
+    a.threshold = threshold;
+    a.seed = seed;
+    a.req_off = request_offset;
+    a.accepted_len = accepted_len;
+    a.tokens = tokens;
+    a.d_verify_len = diag ? diag->verify_len : nullptr;
+    a.d_draft = diag ? diag->draft_tokens : nullptr;
+    a.d_logq = diag ? diag->logq : nullptr;
+    a.d_logp = diag ? diag->logp : nullptr;
+    a.ws = (char*)workspace;
+    a.nonce = 0;
+    a.G = cu_count();
+    (void)hipGetLastError();
+    return res::launch(a, st, tm.start(0), tm.stop(0));
+  }
 
   char* ws = (char*)workspace;
   Params p;
@@ -2622,14 +2703,10 @@ static int cycle_impl(const spec_dims* d, const void* base_logits, const void* t
   p.konst = (const u32x4*)(ws + l.off_konst);
   p.nrB = l.nrB;
 
-  // vector loads need 16-byte aligned rows
-  const size_t esz = d->dtype == SPEC_FP32 ? 4 : 2;
-  const bool vec = ((d->V * esz) % 16 == 0) && ((((uintptr_t)base_logits) | ((uintptr_t)target_logits)) & 15) == 0;
   // column ranges of the bias-row partials: one noise chunk on the bf16 fast sweep, TILE_A on the general path
   p.nrA = (d->dtype == SPEC_BF16 && vec) ? (d->V + CHUNK - 1) / CHUNK : (d->V + TILE_A - 1) / TILE_A;
   p.part8 = (d->dtype == SPEC_BF16 && vec && d->noise == SPEC_NOISE_CHUNKED) ? 1 : 0;
 
-  hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
   hipExtLaunchKernelGGL(k_init, dim3((d->B + NT - 1) / NT), dim3(NT), 0, st, tm.start(0), tm.stop(0), 0, p);
   if (d->dtype == SPEC_BF16) launch_all<SPEC_BF16>(p, l, vec, st, tm);
@@ -2685,7 +2762,9 @@ extern "C" int spec_cycle_noalloc(const spec_dims* d, const void* base_logits, c
                                   spec_stream_t stream) {
   if (!dims_ok(d)) return SPEC_E_INVAL;
   if (!dtype_ok(d)) return SPEC_E_DTYPE;
-  const size_t need = layout(d).total;
+  if (d->path != SPEC_PATH_AUTO && d->path != SPEC_PATH_STEPWISE && d->path != SPEC_PATH_RESIDENT)
+    return SPEC_E_INVAL;
+  const size_t need = need_bytes(d, d->path);
   if (need > SPEC_SCRATCH_BYTES) return SPEC_E_SCRATCH;
   const int ac = arch_ok();
   if (ac != SPEC_OK) return ac;
@@ -2699,8 +2778,10 @@ extern "C" int spec_cycle_noalloc(const spec_dims* d, const void* base_logits, c
 }
 
 extern "C" int spec_cycle_kernel_count(const spec_dims* d) {
-  if (!dims_ok(d)) return 0;
-  return 1 + 3 * (d->K + 1);
+  if (!dims_ok(d) || !dtype_ok(d)) return 0;
+  const int path = resolve_path(d, true);
+  if (path < 0) return 0;
+  return path == SPEC_PATH_RESIDENT ? 1 : 1 + 3 * (d->K + 1);
 }
 
 extern "C" int spec_cycle_timed(const spec_dims* d, const void* base_logits, const void* target_logits,

@@ -59,6 +59,23 @@ enum {
 enum { SPEC_FP32 = 0, SPEC_BF16 = 1 };          /* element type of logits, A and W           */
 enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
 
+/*
+ * Execution paths of one cycle; both give identical results for the same inputs.
+ *   SPEC_PATH_STEPWISE  k_init, then per position s = 0..K one sweep and one merge kernel: W
+ *                       streams from memory once per position that has work.
+ *   SPEC_PATH_RESIDENT  the whole cycle as ONE persistent launch (one workgroup per compute unit,
+ *                       launched cooperatively so that all are resident together): every workgroup
+ *                       keeps its slice of W in registers and LDS for all positions, so W crosses
+ *                       HBM once per cycle, and the positions are separated by grid barriers
+ *                       instead of kernel boundaries.  Needs bf16 rows, chunked noise, V % 8 == 0,
+ *                       16-byte aligned logits, B <= 4 x compute units and at most 640 vocabulary
+ *                       columns per compute unit (V <= 163840 on a 256-CU gfx950).  A grid barrier
+ *                       that does not complete within about a second (only if the device cannot
+ *                       keep the grid resident) marks every request invalid instead of hanging.
+ *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies, else the stepwise one.
+ */
+enum { SPEC_PATH_AUTO = 0, SPEC_PATH_STEPWISE = 1, SPEC_PATH_RESIDENT = 2 };
+
 typedef struct spec_dims {
   int32_t B;      /* requests, 1..1024                                                      */
   int32_t K;      /* draft positions per request, 1..32                                     */
@@ -67,6 +84,8 @@ typedef struct spec_dims {
   int32_t dtype;  /* SPEC_FP32 or SPEC_BF16                                                 */
   int32_t noise;  /* SPEC_NOISE_FLAT: one Gumbel per vocabulary index;                      */
                   /* SPEC_NOISE_CHUNKED: exact two-level Gumbel-max over 64-wide chunks     */
+  int32_t path;   /* SPEC_PATH_*: 0 (AUTO) picks; forcing RESIDENT on a call that does not  */
+                  /* qualify returns SPEC_E_DTYPE.  Ignored by spec_accept_stats.           */
 } spec_dims;
 
 typedef struct spec_diag {   /* optional per-position diagnostics; any field may be NULL     */
@@ -76,8 +95,13 @@ typedef struct spec_diag {   /* optional per-position diagnostics; any field may
   float* logp;               /* [B,K] log p_j(x_j) for decided positions (j <= a_b, j < L_b), else NaN */
 } spec_diag;
 
-/* Bytes of device workspace spec_cycle needs for these dimensions (0 if dims are invalid). */
+/* Bytes of device workspace spec_cycle needs for these dimensions (0 if dims are invalid); with
+ * SPEC_PATH_AUTO enough for either path. */
 size_t spec_workspace_bytes(const spec_dims* d);
+
+/* The path (SPEC_PATH_STEPWISE or SPEC_PATH_RESIDENT) spec_cycle takes for these dims on the
+ * current device with 16-byte aligned logits, or a negative SPEC_E_* code. */
+int spec_cycle_path(const spec_dims* d);
 
 /*
  * One speculation cycle.
@@ -127,7 +151,8 @@ int spec_cycle_lengths(const spec_dims* d, const void* base_logits, const void* 
 /*
  * Profiling variant of spec_cycle for benchmarks: identical work and results, and every kernel
  * of the cycle is launched with a start/stop hipEvent_t pair attached to its own dispatch (no
- * extra queue packets).  Kernel i is: 0 = set-up and prefix cut; 1 + 3s = sweep of the Markov-biased
+ * extra queue packets; on the resident path the pair is recorded around its one launch).  On the
+ * stepwise path kernel i is: 0 = set-up and prefix cut; 1 + 3s = sweep of the Markov-biased
  * rows of step s, 2 + 3s = sweep of the plain target rows of step s, 3 + 3s = per-request merge of
  * step s, for s = 0..K.  With bf16 rows and V % 8 == 0 the plain rows of step s run inside kernel
  * 1 + 3s, and the event pair of slot 2 + 3s is recorded back to back (an empty interval).  `events` is a host array of
@@ -162,7 +187,8 @@ int spec_cycle_noalloc(const spec_dims* d, const void* base_logits, const void* 
                        const float* temp, float threshold, uint64_t seed, int64_t request_offset,
                        int32_t* accepted_len, int32_t* tokens, const spec_diag* diag, spec_stream_t stream);
 
-/* Number of kernel slots of one spec_cycle call: 1 + 3 (K + 1); 0 for invalid dims. */
+/* Number of kernel slots of one spec_cycle call: 1 on the resident path (the whole cycle is
+ * slot 0), 1 + 3 (K + 1) on the stepwise path; 0 for invalid dims. */
 int spec_cycle_kernel_count(const spec_dims* d);
 
 /* Bytes of device workspace spec_accept_stats needs (0 if dims are invalid; dims.noise unused). */

@@ -8,17 +8,18 @@ import pytest
 
 import oracle
 from draft_sampling_lossless_spec_amd import workloads as wl
-from gpu_util import to_device
+from gpu_util import PATH_AUTO, PATH_RESIDENT, PATH_STEPWISE, to_device
 from parity import Report, compare
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("noise", [oracle.FLAT, oracle.CHUNKED])
-def test_decode_chain_matches_oracle(noise):
+@pytest.mark.parametrize("noise,path", [(oracle.FLAT, PATH_AUTO), (oracle.CHUNKED, PATH_STEPWISE),
+                                        (oracle.CHUNKED, PATH_RESIDENT)])
+def test_decode_chain_matches_oracle(noise, path):
     import torch
     from draft_sampling_lossless_spec_amd import spec_advance, spec_cycle
-    print(f"decode chain noise={noise}", flush=True)
+    print(f"decode chain noise={noise} path={path}", flush=True)
     sets = [wl.generate(wl.small_config(B=32, K=6, V=3000, R=32, threshold=0.1), gen_seed=s) for s in (1, 2)]
     w = sets[0]
     n_cycles, seed = 5, 11
@@ -32,7 +33,7 @@ def test_decode_chain_matches_oracle(noise):
     for c in range(n_cycles):
         d = devs[c % 2]
         g = spec_cycle(d["base"], d["target"], A, W, d["conf"], d["temp"], w.threshold, seed + c, x0=x0, noise=noise,
-                       diag=True)
+                       diag=True, path=path)
         spec_advance(g["tokens"], g["accepted_len"], x0, emitted)
         torch.cuda.synchronize()
         gn = {k: v.cpu().numpy() for k, v in g.items()}

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from draft_sampling_lossless_spec_amd import workloads as wl
-from gpu_util import run_gpu, to_device
+from gpu_util import PATH_AUTO, PATH_STEPWISE, paths_for, run_gpu, taken_path, to_device
 from conftest import record_parity
 from parity import Report, check_structure, compare
 
@@ -31,9 +31,12 @@ def assert_parity(rep: Report, case: str = ""):
 
 
 def full_compare(w, noise, **kw):
-    g = run_gpu(w, noise, **kw)
+    """Every path of this noise scheme against one oracle run; returns the last path's outputs."""
     o = ref(w, noise, **({"x0": kw["x0"]} if "x0" in kw else {}))
-    assert_parity(compare(o, g))
+    for path in paths_for(w, noise):
+        print(f"  path {taken_path(w, noise, path)}", flush=True)
+        g = run_gpu(w, noise, path=path, **kw)
+        assert_parity(compare(o, g))
     return g, o
 
 
@@ -101,16 +104,18 @@ def test_invalid_requests(noise):
 @pytest.mark.parametrize("noise", NOISES)
 def test_determinism_and_sharding(noise):
     w = wl.generate(wl.small_config(B=20, K=5, V=4000, R=32, threshold=0.1))
-    g1 = run_gpu(w, noise)
-    g2 = run_gpu(w, noise)
-    for k in g1:
-        np.testing.assert_array_equal(g1[k], g2[k])
     h = 7
     half = wl.Workload(w.cfg, w.base[h:], w.target[h:], w.A, w.W, w.x0[h:], w.conf[h:], w.temp[h:], w.threshold,
                        w.seed, w.request_ids[h:])
-    g3 = run_gpu(half, noise, request_offset=h)
-    for k in g1:
-        np.testing.assert_array_equal(g1[k][h:], g3[k])
+    for path in paths_for(w, noise):
+        print(f"  path {taken_path(w, noise, path)}", flush=True)
+        g1 = run_gpu(w, noise, path=path)
+        g2 = run_gpu(w, noise, path=path)
+        for k in g1:
+            np.testing.assert_array_equal(g1[k], g2[k])
+        g3 = run_gpu(half, noise, request_offset=h, path=path)
+        for k in g1:
+            np.testing.assert_array_equal(g1[k][h:], g3[k])
 
 
 # (workload, threshold or None for its own, generator and cycle seed); cases of one workload and
@@ -138,13 +143,19 @@ def test_full_size_workloads(name, thr, seed, noise):
     print(f"full {case}", flush=True)
     w = _full_workload(name, seed)
     w.threshold = w.cfg.threshold if thr is None else thr
-    g = run_gpu(w, noise)
-    errs = check_structure(w, g, oracle.cut)
-    assert not errs, "\n".join(errs[:10])
-    # every request of the batch against the oracle
+    paths = paths_for(w, noise)
+    if noise == oracle.CHUNKED:
+        # the full-size chunked workloads are what the one-launch resident cycle is for
+        assert len(paths) == 2
+    # every request of the batch against the oracle, on every path of this noise scheme
     o = ref(w, noise)
-    assert_parity(compare(o, g), case)
-    print(f"{name}: sum L={int(g['verify_len'].sum())} sum a={int(g['accepted_len'].sum())}", flush=True)
+    for path in paths:
+        pname = taken_path(w, noise, path)
+        g = run_gpu(w, noise, path=path)
+        errs = check_structure(w, g, oracle.cut)
+        assert not errs, "\n".join(errs[:10])
+        assert_parity(compare(o, g), f"{case} path={pname}")
+        print(f"{name} {pname}: sum L={int(g['verify_len'].sum())} sum a={int(g['accepted_len'].sum())}", flush=True)
 
 
 def test_side_stream_matches_default_stream():

@@ -68,18 +68,18 @@ def test_load_response_on_gpu():
 
 # ---- the cycle with the scheduler's verify lengths ----
 from draft_sampling_lossless_spec_amd import workloads as wl  # noqa: E402
-from gpu_util import to_device  # noqa: E402
+from gpu_util import PATH_NAMES, paths_for, to_device  # noqa: E402
 from conftest import record_parity  # noqa: E402
 from parity import compare  # noqa: E402
 
 
-def gpu_cycle_lengths(w, L, noise, dev=None):
+def gpu_cycle_lengths(w, L, noise, dev=None, path=0):
     import torch
     from draft_sampling_lossless_spec_amd import spec_cycle_lengths
     d = dev or to_device(w)
     Lt = L if hasattr(L, "is_cuda") else torch.from_numpy(np.ascontiguousarray(L, dtype=np.int32)).cuda()
     out = spec_cycle_lengths(d["base"], d["target"], d["A"], d["W"], Lt, d["temp"], w.seed, x0=d["x0"], noise=noise,
-                             diag=True)
+                             diag=True, path=path)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -92,12 +92,13 @@ def test_cycle_lengths_matches_oracle(noise):
     L = rng.integers(0, 7, 24).astype(np.int32)
     L[3], L[7] = -1, 7                      # bad lengths mark the request invalid
     o = oracle.spec_cycle_ref_lengths(w.base, w.target, w.A, w.W, w.x0, L, w.temp, w.seed, noise=noise)
-    g = gpu_cycle_lengths(w, L, noise)
-    rep = compare(o, g)
-    print(rep.summary(), flush=True)
-    record_parity(f"cycle with given lengths noise={noise}", rep.summary())
-    assert not rep.failures, "\n".join(rep.failures[:10])
-    assert np.array_equal(g["verify_len"], o["verify_len"])
+    for path in paths_for(w, noise):
+        g = gpu_cycle_lengths(w, L, noise, path=path)
+        rep = compare(o, g)
+        print(rep.summary(), flush=True)
+        record_parity(f"cycle with given lengths noise={noise} path={PATH_NAMES[path]}", rep.summary())
+        assert not rep.failures, "\n".join(rep.failures[:10])
+        assert np.array_equal(g["verify_len"], o["verify_len"])
 
 
 @pytest.mark.parametrize("noise", [oracle.CHUNKED])
@@ -112,16 +113,18 @@ def test_schedule_then_cycle_on_device(noise):
     T = _curve(B * K, 0.02, 2e-6)
     d = to_device(w)
     Lg, out = spec_schedule(d["conf"], torch.from_numpy(T).cuda(), 4096)
-    g = gpu_cycle_lengths(w, Lg, noise, dev=d)
     o_s = oracle.schedule_ref(w.conf.astype(np.float32), T, 4096)
     assert np.array_equal(Lg.cpu().numpy(), o_s["verify_len"])
-    assert np.array_equal(g["verify_len"], o_s["verify_len"])
     # every request against the oracle's cycle at the oracle's own verify lengths
     o = oracle.spec_cycle_ref_lengths(w.base, w.target, w.A, w.W, w.x0, o_s["verify_len"], w.temp, w.seed,
                                       noise=noise)
-    rep = compare(o, g)
-    print(rep.summary(), flush=True)
-    record_parity("scheduled longblock cycle", rep.summary())
-    assert not rep.failures, "\n".join(rep.failures[:10])
-    assert rep.near_tie_rate < 1e-3
-    print(f"scheduled verify tokens {int(g['verify_len'].sum())}, accepted {int(g['accepted_len'].sum())}", flush=True)
+    for path in paths_for(w, noise):
+        g = gpu_cycle_lengths(w, Lg, noise, dev=d, path=path)
+        assert np.array_equal(g["verify_len"], o_s["verify_len"])
+        rep = compare(o, g)
+        print(rep.summary(), flush=True)
+        record_parity(f"scheduled longblock cycle path={PATH_NAMES[path]}", rep.summary())
+        assert not rep.failures, "\n".join(rep.failures[:10])
+        assert rep.near_tie_rate < 1e-3
+        print(f"scheduled verify tokens {int(g['verify_len'].sum())}, accepted {int(g['accepted_len'].sum())}",
+              flush=True)

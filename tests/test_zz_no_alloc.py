@@ -7,12 +7,12 @@ import pytest
 
 import oracle
 from draft_sampling_lossless_spec_amd import workloads as wl
-from gpu_util import run_gpu, to_device
+from gpu_util import PATH_AUTO, PATH_RESIDENT, PATH_STEPWISE, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
 
-def _noalloc(w, noise):
+def _noalloc(w, noise, path):
     import torch
     from draft_sampling_lossless_spec_amd import spec_cycle_noalloc
     d = to_device(w)
@@ -25,7 +25,7 @@ def _noalloc(w, noise):
            "logp": torch.empty((B, K), dtype=torch.float32, device="cuda")}
     torch.cuda.synchronize()
     spec_cycle_noalloc(d["base"], d["target"], d["A"], d["W"], d["conf"], d["temp"], w.threshold, w.seed, out,
-                       x0=d["x0"], noise=noise)
+                       x0=d["x0"], noise=noise, path=path)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -40,10 +40,11 @@ def _same(a, b):
             np.testing.assert_array_equal(a[k], b[k])
 
 
-@pytest.mark.parametrize("noise", [oracle.CHUNKED, oracle.FLAT])
-def test_noalloc_matches_workspace_entry_point(noise):
-    print(f"noalloc noise={noise}", flush=True)
+@pytest.mark.parametrize("noise,path", [(oracle.CHUNKED, PATH_RESIDENT), (oracle.CHUNKED, PATH_STEPWISE),
+                                        (oracle.FLAT, PATH_AUTO)])
+def test_noalloc_matches_workspace_entry_point(noise, path):
+    print(f"noalloc noise={noise} path={path}", flush=True)
     big = wl.generate(wl.small_config(B=48, K=6, V=6000, R=64, threshold=0.05))
     small = wl.generate(wl.small_config(B=9, K=3, V=2048, R=32, threshold=0.1), gen_seed=2, cycle_seed=5)
     for w in (big, small):
-        _same(run_gpu(w, noise), _noalloc(w, noise))
+        _same(run_gpu(w, noise, path=path), _noalloc(w, noise, path))
