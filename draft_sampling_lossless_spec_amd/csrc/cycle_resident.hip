@@ -377,15 +377,22 @@ __device__ __forceinline__ float ld_f32(const float* p) { return __int_as_float(
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
   return (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
 }
-// a 16-byte record as two coherent 8-byte words (x, y) and (z, w)
-__device__ __forceinline__ void rec_store(float4* p, float4 v) {
-  st_u64(p, pack2(v.x, v.y));
-  st_u64((char*)p + 8, pack2(v.z, v.w));
+// Records (16 bytes) move through buffer loads and stores with the device-scope cache policy
+// (sc1): the same coherence as the atomics above, one 16-byte access per lane, and lanes that read
+// consecutive records coalesce.  The descriptor covers one record area (out-of-range offsets read
+// zero and drop writes).
+constexpr int CPOL_SC1 = 16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ float4 rec_load(const float4* p) {
-  const uint64_t a = ld_u64(p), b = ld_u64((const char*)p + 8);
-  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
-                     __uint_as_float((uint32_t)(b >> 32)));
+__device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t r, size_t idx, float4 v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)(idx * 16), 0, CPOL_SC1);
+}
+__device__ __forceinline__ float4 rec_load(__amdgpu_buffer_rsrc_t r, size_t idx) {
+  const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(idx * 16), 0, CPOL_SC1);
+  return make_float4(x[0], x[1], x[2], x[3]);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -481,8 +488,8 @@ struct KP {
   float* logq;        // [B][K]
   float* lse_p;       // [B][K+1]
   float* logp;        // [B][K]
-  float4* rec_d;      // [slots][G][NW]: per-wave records of bias rows
-  float4* rec_c;      // [slots][G][NW]: CORRECT rows' target-row records
+  float4* rec_d;      // [slots][NW][MAX_G]: per-wave records of bias rows
+  float4* rec_c;      // [CORRECT slot - c0][NW][MAX_G]: CORRECT rows' target-row records
   float4* rec_p;      // [B][MAX_G]: records of the plain rows' items (ceil(V / TP) <= MAX_G per row)
   uint64_t* flags;    // [G][FLAG_STRIDE]
   uint64_t* err;
@@ -581,37 +588,47 @@ struct MergeLds {
 // columns 64 chunk + 16 w .. + 16, four lanes per column, each lane a quarter of the rank (eight
 // 16-byte pieces of the column's W row and the staged A row); the quarters are summed across the
 // lane quad, the winner is found per wave, then across the waves.  Result uniform.
-__device__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
+__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int V = p.a.V, R = p.a.R, P16 = R >> 3;
-  if (tid < 128) {
-    const int q = tid >> 6, l = tid & 63;
-    const bool ld = jb[q].kind != L2_NONE && jb[q].kind != L2_TARGET && jb[q].prev >= 0 && 4 * l < R;
-    const uint2 w = *(const uint2*)((const uint16_t*)p.a.A + (ld ? (size_t)jb[q].prev * R + 4 * l : 0));
-    *(uint2*)&ml->arow[q][4 * l] = ld ? w : make_uint2(0u, 0u);
-  }
+  // every load of the round is issued before any of them is waited for: the A rows (staged in
+  // LDS below), the W rows, the draft and target logits of the 64 candidate columns
+  const int qa = (tid >> 6) & 1, la = tid & 63;
+  const bool lda = tid < 128 && jb[qa].kind != L2_NONE && jb[qa].kind != L2_TARGET && jb[qa].prev >= 0 && 4 * la < R;
+  const uint2 arow_v = *(const uint2*)((const uint16_t*)p.a.A + (lda ? (size_t)jb[qa].prev * R + 4 * la : 0));
   const int col = 16 * wave + (lane >> 2), kq = lane & 3;
   int v[2];
-  bool in[2];
+  bool in[2], need_base[2], need_targ[2], wld[2][8];
   float bv[2], tv[2], bias[2];
   u32x4 wv[2][8];
+  uint16_t bvr[2], tvr[2];
 #pragma unroll
   for (int q = 0; q < 2; q++) {
     v[q] = jb[q].chunk * CH + col;
     in[q] = jb[q].kind != L2_NONE && jb[q].chunk >= 0 && v[q] < V;
-    const bool need_base = in[q] && (jb[q].kind == L2_DRAFT || jb[q].kind == L2_RESIDUAL);
-    const bool need_targ = in[q] && (jb[q].kind != L2_DRAFT || jb[q].want_target);
+    need_base[q] = in[q] && (jb[q].kind == L2_DRAFT || jb[q].kind == L2_RESIDUAL);
+    need_targ[q] = in[q] && (jb[q].kind != L2_DRAFT || jb[q].want_target);
     const bool need_bias = in[q] && jb[q].kind != L2_TARGET && jb[q].prev >= 0;
+    // unconditional loads at addresses clamped inside their tensors; values not needed are
+    // replaced after the loads
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const int pc = 8 * kq + i;
-      const bool ld = need_bias && pc < P16;
-      const u32x4 x = *(const u32x4*)((const uint16_t*)p.a.W + (ld ? (size_t)v[q] * R + 8 * pc : 0));
-      wv[q][i] = ld ? x : kZero;
+      wld[q][i] = need_bias && pc < P16;
+      wv[q][i] = *(const u32x4*)((const uint16_t*)p.a.W + (wld[q][i] ? (size_t)v[q] * R + 8 * pc : 0));
     }
-    bv[q] = need_base ? bf16_to_f32(jb[q].base[v[q]]) : 0.0f;
-    tv[q] = need_targ ? bf16_to_f32(jb[q].targ[v[q]]) : 0.0f;
+    bvr[q] = *(need_base[q] ? jb[q].base + v[q] : (const uint16_t*)p.a.base);
+    tvr[q] = *(need_targ[q] ? jb[q].targ + v[q] : (const uint16_t*)p.a.target);
   }
+  __builtin_amdgcn_sched_barrier(0);   // every load of the round is in flight before any is used
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) wv[q][i] = wld[q][i] ? wv[q][i] : kZero;
+    bv[q] = need_base[q] ? bf16_to_f32(bvr[q]) : 0.0f;
+    tv[q] = need_targ[q] ? bf16_to_f32(tvr[q]) : 0.0f;
+  }
+  if (tid < 128) *(uint2*)&ml->arow[qa][4 * la] = lda ? arow_v : make_uint2(0u, 0u);
   __syncthreads();   // the A rows are staged
 #pragma unroll
   for (int q = 0; q < 2; q++) {
@@ -689,7 +706,7 @@ __device__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds*
 // holds the log-mass of the wave's register chunks, their best score and chunk, and the log-mass
 // of the wave's half of an LDS chunk; the halves of LDS chunk i are in waves 2i and 2i + 1, and
 // the chunk's Gumbel score is formed here from the whole chunk.
-__device__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, uint64_t key) {
+__device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, uint64_t key) {
   float lse = -INFINITY, bs = -INFINITY;
   int bc = -1;
 #pragma unroll
@@ -700,7 +717,10 @@ __device__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, uint64_t key) 
       bc = __float_as_int(a[w].z);
     }
   }
-  for (int i = 0; i < nl; i++) {
+  // constant indices (the bound is the largest LDS chunk count) keep the records in registers
+#pragma unroll
+  for (int i = 0; i < LDS_CHUNKS; i++) {
+    if (i >= nl) break;
     const float hc = lse_add(a[2 * i].w, a[2 * i + 1].w);
     lse = lse_add(lse, hc);
     const int cgl = cb + NW * AG_CHUNKS + i;
@@ -716,7 +736,7 @@ __device__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, uint64_t key) 
 // The same for a CORRECT row: the residual records a (log residual mass of the register chunks,
 // best score, best chunk, LINEAR residual mass of the LDS half) and the target records t (target
 // log-mass, best score, best chunk, target log-mass of the LDS half); both draws use `key`.
-__device__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb, int nl, uint64_t key, float4& rd,
+__device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb, int nl, uint64_t key, float4& rd,
                            float4& rt) {
   float ms = 0.0f, lt = -INFINITY, bs = -INFINITY, bt = -INFINITY;
   int bc = -1, btc = -1;
@@ -733,7 +753,9 @@ __device__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb,
       btc = __float_as_int(t[w].z);
     }
   }
-  for (int i = 0; i < nl; i++) {
+#pragma unroll
+  for (int i = 0; i < LDS_CHUNKS; i++) {
+    if (i >= nl) break;
     const int cgl = cb + NW * AG_CHUNKS + i;
     const float gg = gumbel_bits(bits_at(key, (uint32_t)cgl));
     const float mc = a[2 * i].w + a[2 * i + 1].w;
@@ -756,7 +778,7 @@ __device__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb,
 
 // Request b at step s, by the whole workgroup: reduce its rows' records, level two, accept
 // decision, outputs, roles of step s + 1.  The request's state is touched by this workgroup only.
-__device__ void merge_request(const KP& p, const Smem& S, int b, int s) {
+__device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int B = p.a.B, K = p.a.K, V = p.a.V, G = p.a.G;
   MergeLds* ml = (MergeLds*)S.sA;
@@ -782,31 +804,41 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s) {
 #pragma unroll
     for (int r = 0; r < 4; r++) pacc_init(a4[r]);
     const uint64_t key_d = pos_key(kreq, s, ST_DRAFT_C), key_c = pos_key(kreq, s > 0 ? s - 1 : 0, ST_RESIDUAL_C);
-    for (int i = tid; i < G; i += NT) {
-      const int cb = chunk_begin(i, G, V), ncw = chunks_of(i, G, V);
-      const int nl = ncw > NW * AG_CHUNKS ? ncw - NW * AG_CHUNKS : 0;
-      if (hasD) {
-        float4 a[NW];
+    // thread t takes workgroup t's records of each row kind (G <= NT) and plain item t
+    // (ceil(V / TP) <= NT); the DRAFT and plain records are loaded together (one round trip; a
+    // kind the request does not have reads row 0 and is ignored), the CORRECT ones (a request
+    // has them at most once) on their own, so few records are held in registers at a time
+    const int nrP = (V + TP - 1) / TP;
+    const int gi = tid < G ? tid : 0;
+    const int cb = chunk_begin(gi, G, V), ncw = chunks_of(gi, G, V);
+    const int nl = ncw > NW * AG_CHUNKS ? ncw - NW * AG_CHUNKS : 0;
+    if (hasD || hasP) {
+      const auto rs_d = rec_rsrc(p.rec_d, rec_d_bytes(B)), rs_p = rec_rsrc(p.rec_p, rec_p_bytes(B));
+      const size_t rd_base = (size_t)(hasD ? sd : 0) * NW * MAX_G + gi;
+      float4 ad[NW];
 #pragma unroll
-        for (int w = 0; w < NW; w++) a[w] = rec_load(&p.rec_d[((size_t)sd * G + i) * NW + w]);
-        pacc_add(a4[0], wg_draft(a, cb, nl, key_d));
+      for (int w = 0; w < NW; w++) ad[w] = rec_load(rs_d, rd_base + (size_t)w * MAX_G);
+      const float4 ap = rec_load(rs_p, (size_t)(hasP ? sp : 0) * MAX_G + (tid < nrP ? tid : 0));
+      __builtin_amdgcn_sched_barrier(0);   // the five loads are in flight before any is used
+      if (hasD && tid < G) pacc_add(a4[0], wg_draft(ad, cb, nl, key_d));
+      if (hasP && tid < nrP) pacc_add(a4[3], ap);
+    }
+    if (hasC) {
+      const auto rs_d = rec_rsrc(p.rec_d, rec_d_bytes(B)), rs_c = rec_rsrc(p.rec_c, rec_c_bytes(B));
+      const size_t rc_base = (size_t)sc_ * NW * MAX_G + gi, rt_base = (size_t)(sc_ - c0) * NW * MAX_G + gi;
+      float4 ac[NW], at[NW];
+#pragma unroll
+      for (int w = 0; w < NW; w++) {
+        ac[w] = rec_load(rs_d, rc_base + (size_t)w * MAX_G);
+        at[w] = rec_load(rs_c, rt_base + (size_t)w * MAX_G);
       }
-      if (hasC) {
-        float4 a[NW], t[NW];
-#pragma unroll
-        for (int w = 0; w < NW; w++) {
-          a[w] = rec_load(&p.rec_d[((size_t)sc_ * G + i) * NW + w]);
-          t[w] = rec_load(&p.rec_c[((size_t)sc_ * G + i) * NW + w]);
-        }
+      __builtin_amdgcn_sched_barrier(0);
+      if (tid < G) {
         float4 rd, rt;
-        wg_correct(a, t, cb, nl, key_c, rd, rt);
+        wg_correct(ac, at, cb, nl, key_c, rd, rt);
         pacc_add(a4[1], rd);
         pacc_add(a4[2], rt);
       }
-    }
-    if (hasP) {
-      const int nrP = (V + TP - 1) / TP;
-      for (int i = tid; i < nrP; i += NT) pacc_add(a4[3], rec_load(&p.rec_p[(size_t)sp * MAX_G + i]));
     }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -1266,6 +1298,9 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
       const bool pre = !is_corr_sb;                 // uniform
       if (!pre) load_tiles(p.a.target, b, j, K + 1, Tt);
+      // the loads above stay here, a whole sub-block ahead of their use (the scheduler would
+      // otherwise sink them towards it)
+      __builtin_amdgcn_sched_barrier(0);
       if (is_corr_sb) {
         // target pieces past V read -inf (their residual and target mass are then zero)
 #pragma unroll
@@ -1279,20 +1314,21 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
 #pragma unroll
         for (int t = 0; t < KSTEPS; t++) asm volatile("" : "+a"(wf[i][t]));
 
-      // pass 0: register chunk 0
+      // pass 0: register chunk 0 (B operands read from LDS two k-steps ahead of their MFMAs)
       f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
       if (pre) {
         load_tile(p.a.base, b2, j2, K, 0, Tc[0]);
         load_tile(p.a.base, b2, j2, K, 1, Tc[1]);
       }
       {
-        bf16x8 bop = sAk[lane];
+        bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane];
 #pragma unroll
         for (int t = 0; t < KSTEPS; t++) {
-          const bf16x8 bop_n = (t + 1 < KSTEPS) ? sAk[(t + 1) * 64 + lane] : bop;
+          const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
           a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, a0, 0, 0, 0);
           a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, a1, 0, 0, 0);
-          bop = bop_n;
+          bop = bop1;
+          bop1 = bop2;
         }
       }
       // pass 1: register chunk 1, with the element-wise part of pass 0 after it
@@ -1302,13 +1338,14 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         load_tile(p.a.base, b2, j2, K, 3, Tc[3]);
       }
       {
-        bf16x8 bop = sAk[lane];
+        bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane];
 #pragma unroll
         for (int t = 0; t < KSTEPS; t++) {
-          const bf16x8 bop_n = (t + 1 < KSTEPS) ? sAk[(t + 1) * 64 + lane] : bop;
+          const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
           a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[2][t], bop, a2, 0, 0, 0);
           a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[3][t], bop, a3, 0, 0, 0);
-          bop = bop_n;
+          bop = bop1;
+          bop1 = bop2;
         }
       }
       WaveRec wr;
@@ -1326,14 +1363,16 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       f32x16 a4 = seed_acc(Tc[4], 4);
       if (pre) load_tile(p.a.base, b2, j2, K, 4, Tc[4]);
       {
-        bf16x8 bop = sAk[lane], wl = wlw[lane];
+        bf16x8 bop = sAk[lane], wl = wlw[lane], bop1 = sAk[64 + lane], wl1 = wlw[64 + lane];
 #pragma unroll
         for (int t = 0; t < KSTEPS; t++) {
-          const bf16x8 bop_n = (t + 1 < KSTEPS) ? sAk[(t + 1) * 64 + lane] : bop;
-          const bf16x8 wl_n = (t + 1 < KSTEPS) ? wlw[(t + 1) * 64 + lane] : wl;
+          const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
+          const bf16x8 wl2 = (t + 2 < KSTEPS) ? wlw[(t + 2) * 64 + lane] : wl;
           a4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, bop, a4, 0, 0, 0);
-          bop = bop_n;
-          wl = wl_n;
+          bop = bop1;
+          bop1 = bop2;
+          wl = wl1;
+          wl1 = wl2;
         }
       }
       float l1 = -INFINITY, m1 = 0.0f, t1 = -INFINITY, hl = -INFINITY, mh = 0.0f, th = -INFINITY;
@@ -1388,13 +1427,16 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         // sub-blocks are few
         load_tiles(p.a.base, b2, j2, K, Tc);
       }
+      stage_store(k + 1, sv, vin);
       // this wave's record of each row of the sub-block (the merge combines the waves)
       if (h == 0 && b >= 0) {
-        const size_t ri = ((size_t)(k * SUB + m32) * G + g) * NW + wave;
-        rec_store(&p.rec_d[ri], wr.a);
-        if (is_corr_sb) rec_store(&p.rec_c[ri], wr.t);
+        const size_t ri = ((size_t)(k * SUB + m32) * NW + wave) * MAX_G + g;
+        rec_store(rec_rsrc(p.rec_d, rec_d_bytes(B)), ri, wr.a);
+        if (is_corr_sb) {
+          const size_t rc = ((size_t)(k * SUB + m32 - ls.c0) * NW + wave) * MAX_G + g;
+          rec_store(rec_rsrc(p.rec_c, rec_c_bytes(B)), rc, wr.t);
+        }
       }
-      stage_store(k + 1, sv, vin);
       __syncthreads();
     }
 
@@ -1497,7 +1539,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
             wargmax(bs, bc, dummy);
             rec = make_float4(lse_tot, bs, __int_as_float(bc), 0.0f);
           }
-          if (lane == 0) rec_store(&p.rec_p[(size_t)ps[q] * MAX_G + t[q]], rec);
+          if (lane == 0) rec_store(rec_rsrc(p.rec_p, rec_p_bytes(B)), (size_t)ps[q] * MAX_G + t[q], rec);
         }
       }
     }
@@ -1509,7 +1551,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     for (int r = 0; r < NW; r++) {
       const int b = g + G * r;
       if (b >= B) break;
-      merge_request(p, S, b, s);
+      merge_request(p, S, b, s, ls.c0);
     }
 
     // ---- 6. grid barrier: roles, drafted tokens and log-normalisers of step s are written ----

@@ -40,13 +40,19 @@ __host__ __device__ constexpr int chunk_begin(int g, int G, int V) {
 // bias slots: DRAFT rows from 0, CORRECT rows from the next multiple of SUB (no sub-block mixes)
 __host__ __device__ constexpr int max_bias_slots(int B) { return 2 * B + 2 * SUB; }
 
+// record areas (bytes)
+__host__ __device__ constexpr size_t rec_d_bytes(int B) { return 16 * (size_t)max_bias_slots(B) * NW * MAX_G; }
+__host__ __device__ constexpr size_t rec_c_bytes(int B) { return 16 * (size_t)(B + SUB) * NW * MAX_G; }
+__host__ __device__ constexpr size_t rec_p_bytes(int B) { return 16 * (size_t)B * MAX_G; }
+
 // Workspace of the resident cycle (offsets in bytes from the workspace base, 256-byte aligned).
 struct Layout {
   size_t off_state;    // per-request int32 [6][B]: L, acc, phase, roles (two step parities), valid
   size_t off_xs;       // int32 [B][K]: drafted tokens
   size_t off_f;        // fp32 [4][B][K+1]: lse_q, logq, lse_p, logp
-  size_t off_rec_d;    // float4 [bias slots][G][NW]: per-wave records of bias rows
-  size_t off_rec_c;    // float4 [bias slots][G][NW]: CORRECT rows' target-row records
+  size_t off_rec_d;    // float4 [bias slots][NW][MAX_G]: per-wave records of bias rows
+  size_t off_rec_c;    // float4 [B + SUB][NW][MAX_G]: CORRECT rows' target-row records, indexed
+                       // from the first CORRECT slot
   size_t off_rec_p;    // float4 [B][MAX_G]: plain-row item records (ceil(V / TP) <= MAX_G items)
   size_t off_flags;    // uint64 [G][FLAG_STRIDE]: grid-barrier flags; uint64 [2]: error word
   size_t total;
@@ -60,9 +66,9 @@ __host__ __device__ inline Layout layout(int B, int K) {
   l.off_state = o; o = align256(o + 4 * (size_t)6 * B);
   l.off_xs = o; o = align256(o + 4 * (size_t)B * K);
   l.off_f = o; o = align256(o + 4 * (size_t)4 * B * (K + 1));
-  l.off_rec_d = o; o = align256(o + 16 * (size_t)max_bias_slots(B) * MAX_G * NW);
-  l.off_rec_c = o; o = align256(o + 16 * (size_t)max_bias_slots(B) * MAX_G * NW);
-  l.off_rec_p = o; o = align256(o + 16 * (size_t)B * MAX_G);
+  l.off_rec_d = o; o = align256(o + rec_d_bytes(B));
+  l.off_rec_c = o; o = align256(o + rec_c_bytes(B));
+  l.off_rec_p = o; o = align256(o + rec_p_bytes(B));
   l.off_flags = o; o = align256(o + 8 * (size_t)(MAX_G * FLAG_STRIDE + 2));
   l.total = o;
   return l;

@@ -72,7 +72,9 @@ enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
  *                       columns per compute unit (V <= 163840 on a 256-CU gfx950).  A grid barrier
  *                       that does not complete within about a second (only if the device cannot
  *                       keep the grid resident) marks every request invalid instead of hanging.
- *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies, else the stepwise one.
+ *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies and B <= 2 x compute
+ *                       units (it finishes a workgroup's requests one after another), else the
+ *                       stepwise one.
  */
 enum { SPEC_PATH_AUTO = 0, SPEC_PATH_STEPWISE = 1, SPEC_PATH_RESIDENT = 2 };
 
