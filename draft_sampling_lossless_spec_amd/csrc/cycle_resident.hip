@@ -59,12 +59,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Masked 16-byte loads are still issued, at an address clamped inside their tensor, so that every
-// load is an unconditional global load with nothing waiting on it until its value is used.  Where
-// the value matters it is replaced at its use by one of these (eight bf16 -inf, or zeros): pieces
-// past V, past the workgroup's slice, A rows of a position without a previous token.  Tiles of a
-// slot without a row, or of a chunk the workgroup does not own, are computed on whatever the
-// clamped loads return and their results are discarded.
+// Masked 16-byte loads are still issued, at an address clamped inside their tensor (or, for
+// buffer loads, past its end, which reads zeros), so that every load is unconditional with nothing
+// waiting on it until its value is used.  Where the value matters it is replaced at its use by one
+// of these (eight bf16 -inf, or zeros).  Tiles of a slot without a row, or of a chunk the
+// workgroup does not own, are computed on whatever their loads return and their results are
+// discarded.
 constexpr u32x4 kNegInf = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
 constexpr u32x4 kZero = {0u, 0u, 0u, 0u};
 
@@ -81,6 +81,7 @@ __device__ __forceinline__ int ent_req(uint32_t e) { return (int)((e >> 1) & 102
 __device__ __forceinline__ int ent_prev(uint32_t e) { return (int)(e >> 11) - 1; }
 constexpr uint64_t TOKEN_WINDOW = 1ull << 16;
 constexpr int PLAIN_INFLIGHT = 1;   // plain-row items whose loads a wave keeps in flight
+
 constexpr uint64_t WAIT_TICKS = 100000000ull;   // s_memrealtime runs at 100 MHz: one second
 
 // per-request inputs of the step's bias rows, rebuilt by every workgroup at every step
@@ -126,6 +127,24 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
+// Gumbel noise from 32 random bits without branches: the same three cases and the same
+// arithmetic as gumbel_bits (series for u < 1/64, -log(1 - u) below 1/2, the exact complement
+// above), with the logarithm's argument selected instead of the code path, so the results are
+// identical and the whole element-wise part stays straight-line code.
+__device__ __forceinline__ float gumbel_bf(uint32_t b) {
+  const bool lo = b < 0x80000000u;
+  const float u = ((float)b + 0.5f) * 0x1p-32f;
+  const float c = (float)(~b) + 0.5f;
+  float series = u * fmaf(u, fmaf(u, fmaf(u, fmaf(u, 0.2f, 0.25f), 0.33333334f), 0.5f), 1.0f);
+  const float lg = lg2(lo ? 1.0f - u : c);
+  float e_lo = -lg * LN2, e_hi = (32.0f - lg) * LN2;
+  // every candidate is computed on every lane, so the selects below stay selects (no exec-masked
+  // blocks, which would split the scheduling region this runs in)
+  asm volatile("" : "+v"(series), "+v"(e_lo), "+v"(e_hi));
+  const float e = lo ? (u < 0.015625f ? series : e_lo) : e_hi;
+  return -lg2(e) * LN2;
+}
+
 // 16-byte load of global memory at `p` (the cast keeps it a global load when `p` itself was read
 // from memory, where the compiler no longer knows its address space)
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
@@ -144,6 +163,21 @@ __device__ __forceinline__ bool takes(float s2, int i2, float s1, int i1) {
 // rows of each 32-lane half (lane ^ 16), a permlane swap across the halves (lane ^ 32).
 __device__ __forceinline__ int xor16i(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x401F); }
 __device__ __forceinline__ float xor16f(float x) { return __int_as_float(xor16i(__float_as_int(x))); }
+// A value and its partner lane's (lane ^ 32) from one v_permlane32_swap: .x holds the value of the
+// lower lane of the pair, .y that of the upper, in both lanes (so reductions need no select).
+__device__ __forceinline__ float2 pair32(float x) {
+  const int xi = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return make_float2(__int_as_float((int)r[0]), __int_as_float((int)r[1]));
+}
+__device__ __forceinline__ float pmax32(float x) {
+  const float2 r = pair32(x);
+  return fmaxf(r.x, r.y);
+}
+__device__ __forceinline__ float psum32(float x) {
+  const float2 r = pair32(x);
+  return r.x + r.y;
+}
 template <int CTRL>
 __device__ __forceinline__ int dppi(int x) {
   return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
@@ -155,13 +189,13 @@ __device__ __forceinline__ float wmax(float x) {
   x = max8(x);
   x = fmaxf(x, dpp<0x140>(x));
   x = fmaxf(x, xor16f(x));
-  return fmaxf(x, xor32f(x));
+  return pmax32(x);
 }
 __device__ __forceinline__ float wsum(float x) {
   x = sum8(x);
   x += dpp<0x140>(x);
   x += xor16f(x);
-  return x + xor32f(x);
+  return psum32(x);
 }
 
 // one argmax step against the partner values
@@ -197,7 +231,7 @@ __device__ __forceinline__ float pair_lse(const float* y, float invT) {
     m1 = fmaxf(m1, y[i + 1]);
   }
   float mx = fmaxf(m0, m1);
-  mx = fmaxf(mx, xor32f(mx));
+  mx = pmax32(mx);
   const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
@@ -208,7 +242,7 @@ __device__ __forceinline__ float pair_lse(const float* y, float invT) {
     s3 += ex2(fmaf(y[i + 3], c, -mo));
   }
   float sum = (s0 + s1) + (s2 + s3);
-  sum += xor32f(sum);
+  sum = psum32(sum);
   return (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
 }
 
@@ -225,7 +259,7 @@ __device__ __forceinline__ float tiles_lse(const f32x16* a, float invT) {
       m1 = fmaxf(m1, a[t][q + 1]);
     }
   float mx = fmaxf(m0, m1);
-  mx = fmaxf(mx, xor32f(mx));
+  mx = pmax32(mx);
   const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
@@ -238,8 +272,150 @@ __device__ __forceinline__ float tiles_lse(const f32x16* a, float invT) {
       s3 += ex2(fmaf(a[t][q + 3], c, -mo));
     }
   float sum = (s0 + s1) + (s2 + s3);
-  sum += xor32f(sum);
+  sum = psum32(sum);
   return (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
+}
+
+// log-sum-exp of invT * x over the 32 values of two accumulator tiles of a lane and its partner
+// lane (lane ^ 32); -inf everywhere gives -inf, a NaN gives NaN
+__device__ __forceinline__ float lse_two(const f32x16& x, const f32x16& y, float invT) {
+  float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 16; q += 2) {
+    m0 = fmaxf(m0, fmaxf(x[q], y[q]));
+    m1 = fmaxf(m1, fmaxf(x[q + 1], y[q + 1]));
+  }
+  const float mx = pmax32(fmaxf(m0, m1));
+  const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; q += 2) {
+    s0 += ex2(fmaf(x[q], c, -mo));
+    s1 += ex2(fmaf(x[q + 1], c, -mo));
+    s2 += ex2(fmaf(y[q], c, -mo));
+    s3 += ex2(fmaf(y[q + 1], c, -mo));
+  }
+  const float sum = psum32((s0 + s1) + (s2 + s3));
+  return (mx == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sum) * LN2;
+}
+
+// Scheduling helpers.  vfence(x) is an empty statement with side effects that reads and redefines
+// x: work that produces x stays before it, work that consumes it after it.  interleave<M, D, V>()
+// asks the scheduler for 16 groups of (M MFMAs, D LDS reads, V VALU instructions) in the current
+// region, the shape of one 16-k-step chain with its shadow work.
+template <class T>
+__device__ __forceinline__ void vfence(T& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void vfence(u32x4 (&x)[2]) {
+  asm volatile("" : "+v"(x[0]));
+  asm volatile("" : "+v"(x[1]));
+}
+template <int M, int D, int V>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int t = 0; t < KSTEPS; t++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, D, 0);   // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // VALU
+  }
+}
+
+
+// The element-wise work of a bias sub-block, cut into slices that run one per k-step of an MFMA
+// chain.  Each slice's state is fenced at the k-step boundary (fence_*), which pins the slice to its
+// k-step: its inputs are defined at the step's start and its outputs consumed at its end.
+//
+// Log-sum-exp of invT * x over the 32 values of two accumulator tiles (x, y) of a lane and its
+// partner lane: the maximum in steps 0..3 (8 values each), the exchange in step 4, the scaled
+// exponential sums in steps 5..12 (4 values each), the result in step 13.  -inf everywhere gives
+// -inf, a NaN gives NaN.
+struct Lse2 {
+  float m0, m1, mo, s0, s1, s2, s3, r;
+};
+__device__ __forceinline__ void lse2_init(Lse2& st) {
+  st.m0 = st.m1 = -INFINITY;
+  st.mo = st.s0 = st.s1 = st.s2 = st.s3 = st.r = 0.0f;
+}
+__device__ __forceinline__ void lse2_step(Lse2& st, int t, const f32x16& x, const f32x16& y, float c, float invT) {
+  if (t < 4) {
+#pragma unroll
+    for (int q = 4 * t; q < 4 * t + 4; q += 2) {
+      st.m0 = fmaxf(st.m0, fmaxf(x[q], y[q]));
+      st.m1 = fmaxf(st.m1, fmaxf(x[q + 1], y[q + 1]));
+    }
+  } else if (t == 4) {
+    st.m0 = pmax32(fmaxf(st.m0, st.m1));
+    st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
+  } else if (t < 13) {
+    const int q = 2 * (t - 5);
+    st.s0 += ex2(fmaf(x[q], c, -st.mo));
+    st.s1 += ex2(fmaf(x[q + 1], c, -st.mo));
+    st.s2 += ex2(fmaf(y[q], c, -st.mo));
+    st.s3 += ex2(fmaf(y[q + 1], c, -st.mo));
+  } else if (t == 13) {
+    const float sum = psum32((st.s0 + st.s1) + (st.s2 + st.s3));
+    st.r = (st.m0 == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : st.m0 * invT + lg2(sum) * LN2;
+  }
+}
+__device__ __forceinline__ void lse2_fence(Lse2& st, int t) {
+  if (t < 4) {
+    vfence(st.m0);
+    vfence(st.m1);
+  } else if (t == 4) {
+    vfence(st.m0);
+    vfence(st.mo);
+  } else if (t < 13) {
+    vfence(st.s0);
+    vfence(st.s1);
+    vfence(st.s2);
+    vfence(st.s3);
+  } else if (t == 13) {
+    vfence(st.r);
+  }
+}
+
+// Gumbel noise of index i of a noise row (the same arithmetic as gumbel_bf(bits_at(key, i))) in
+// four slices: the two SplitMix64 rounds, the uniform and the logarithm's argument, the result.
+struct GumbelStage {
+  uint32_t lo, hi;
+  float u, lg, series, r;
+};
+__device__ __forceinline__ void gumbel_step(GumbelStage& g, int t, uint64_t key, uint32_t i) {
+  if (t == 0) {
+    uint64_t z = key + (uint64_t)((i >> 1) + 1u) * SM_GAMMA;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    g.lo = (uint32_t)z;
+    g.hi = (uint32_t)(z >> 32);
+  } else if (t == 1) {
+    uint64_t z = (uint64_t)g.lo | ((uint64_t)g.hi << 32);
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    g.lo = (i & 1u) ? (uint32_t)z : (uint32_t)(z >> 32);   // the index's 32 bits
+  } else if (t == 2) {
+    const uint32_t b = g.lo;
+    const bool lo = b < 0x80000000u;
+    g.u = ((float)b + 0.5f) * 0x1p-32f;
+    const float c = (float)(~b) + 0.5f;
+    g.series = g.u * fmaf(g.u, fmaf(g.u, fmaf(g.u, fmaf(g.u, 0.2f, 0.25f), 0.33333334f), 0.5f), 1.0f);
+    g.lg = lg2(lo ? 1.0f - g.u : c);
+  } else if (t == 3) {
+    const bool lo = g.lo < 0x80000000u;
+    const float e = lo ? (g.u < 0.015625f ? g.series : -g.lg * LN2) : (32.0f - g.lg) * LN2;
+    g.r = -lg2(e) * LN2;
+  }
+}
+__device__ __forceinline__ void gumbel_fence(GumbelStage& g, int t) {
+  if (t == 0) {
+    vfence(g.lo);
+    vfence(g.hi);
+  } else if (t == 1) {
+    vfence(g.lo);
+  } else if (t == 2) {
+    vfence(g.u);
+    vfence(g.lg);
+    vfence(g.series);
+  } else if (t == 3) {
+    vfence(g.r);
+  }
 }
 
 // residual mass sum max(0, p - q) over N values of a lane and its partner lane; t = target logits,
@@ -256,11 +432,21 @@ __device__ __forceinline__ float pair_residual(const float* t, const float* y, f
     if (a3 > b3) m1 += ex2(a3) - ex2(b3);
   }
   float m = m0 + m1;
-  return m + xor32f(m);
+  return psum32(m);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// bf16 logits of one 16-byte piece into half `hf` of a tile's 16 accumulator values
+__device__ __forceinline__ void seed_piece(f32x16& a, const u32x4& w, int hf) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    a[8 * hf + 2 * e] = bf_lo(w[e]);
+    a[8 * hf + 2 * e + 1] = bf_hi(w[e]);
+  }
+}
+
 
 // bf16 value i (0..8NP-1) of NP packed 16-byte pieces
 template <int NP>
@@ -288,7 +474,7 @@ __device__ __forceinline__ void chunk_correct(const f32x16& a0, const f32x16& a1
   float tm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 32; i++) tm = fmaxf(tm, tgt4(t0, t1, t2, t3, i));
-  tm = fmaxf(tm, xor32f(tm));
+  tm = pmax32(tm);
   const float mo = (tm == -INFINITY) ? 0.0f : tm * c;
   float m0 = 0.0f, m1 = 0.0f, s0 = 0.0f, s1 = 0.0f;
   // in groups of eight values, each group scheduled on its own: the register peak stays small
@@ -307,8 +493,8 @@ __device__ __forceinline__ void chunk_correct(const f32x16& a0, const f32x16& a1
     __builtin_amdgcn_sched_barrier(0);
   }
   float m = m0 + m1, sm = s0 + s1;
-  mass = m + xor32f(m);
-  sm += xor32f(sm);
+  mass = psum32(m);
+  sm = psum32(sm);
   tlse = (tm == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : tm * invT + lg2(sm) * LN2;
 }
 
@@ -323,7 +509,7 @@ __device__ __forceinline__ void pair_correct(const float* y, const u32x4* tp, fl
   float tm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < N; i++) tm = fmaxf(tm, pk<NP>(tp, i));
-  tm = fmaxf(tm, xor32f(tm));
+  tm = pmax32(tm);
   const float mo = (tm == -INFINITY) ? 0.0f : tm * c;
   float m0 = 0.0f, m1 = 0.0f, s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
@@ -337,8 +523,8 @@ __device__ __forceinline__ void pair_correct(const float* y, const u32x4* tp, fl
     s1 += ex2(fmaf(t1, c, -mo));
   }
   float m = m0 + m1, sm = s0 + s1;
-  mass = m + xor32f(m);
-  sm += xor32f(sm);
+  mass = psum32(m);
+  sm = psum32(sm);
   tlse = (tm == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : tm * invT + lg2(sm) * LN2;
 }
 
@@ -393,6 +579,16 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t r, size_t idx, 
 __device__ __forceinline__ float4 rec_load(__amdgpu_buffer_rsrc_t r, size_t idx) {
   const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(idx * 16), 0, CPOL_SC1);
   return make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// Read-only operand loads (logits, A rows) through a descriptor over a whole tensor of `bytes`
+// bytes (< 4 GiB): ordinary cache policy; offsets at or past `bytes` read zeros.
+constexpr uint32_t OOB_OFF = 0x80000000u;   // past the end of A (the resident cycle takes A below 2 GiB)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ld_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ldb16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1185,71 +1381,50 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       corr = has && (e & 1u);
       j = corr ? s - 1 : s;
     };
-    // stage the B operands of sub-block k into sA[k & 1] (every thread 4 of the 1024 16-byte entries);
-    // a slot without a row, or k-steps past the rank, read row 0 and take zeros (the load address
-    // stays inside A, so every load is an ordinary global load)
-    auto stage_issue = [&](int k, u32x4 (&v)[4], int& vin) {
-      vin = 0;
+    // Operand loads are buffer loads over whole tensors (each smaller than 4 GiB, so a 32-bit byte
+    // offset reaches all of it): an offset past the end reads zeros instead of faulting, so no
+    // address is clamped and no value selected where the value is not used.
+    //
+    // B operands of sub-block k into sA[k & 1]: lane l of k-step t takes rank entries
+    // (l >> 5) R/2 + 8 t ... + 7 of the A row of its slot (l & 31); wave w stages k-steps w, w + 4,
+    // w + 8, w + 12 that lie below the rank (the rest hold zeros, written at the step's start).  A
+    // slot without a previous token reads past the end of A, i.e. zeros.
+    const int nks = p.a.R >> 4;
+    auto stage_issue = [&](int k, u32x4 (&v)[4]) {
+      const __amdgpu_buffer_rsrc_t rsA = ld_rsrc(p.a.A, (uint32_t)V * (uint32_t)p.a.R * 2u);
+      const uint32_t ent = (k < ls.n_sb) ? S.blist[k * SUB + m32] : NO_ENT;
+      const int prev = ent == NO_ENT ? -1 : ent_prev(ent);
+      const uint32_t vo = prev >= 0 ? 2u * (uint32_t)(prev * p.a.R + h * (p.a.R >> 1) + 8 * wave) : OOB_OFF;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int e = tid + NT * i;
-        const int t = e >> 6, l = e & 63;
-        const uint32_t ent = (k < ls.n_sb) ? S.blist[k * SUB + (l & 31)] : NO_ENT;
-        const int prev = ent == NO_ENT ? -1 : ent_prev(ent);
-        const bool in = prev >= 0 && t < (p.a.R >> 4);
-        v[i] = ldg16((const uint16_t*)p.a.A + (in ? (size_t)prev * p.a.R + (l >> 5) * (p.a.R >> 1) + 8 * t : 0));
-        vin |= in ? (1 << i) : 0;
-      }
+      for (int i = 0; i < 4; i++) v[i] = ldb16(rsA, vo + 64u * i, 0u);
     };
-    auto stage_store = [&](int k, const u32x4 (&v)[4], int vin) {
+    auto stage_store = [&](int k, const u32x4 (&v)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int e = tid + NT * i;
-        ((u32x4*)S.sA)[(k & 1) * KSTEPS * 64 + e] = ((vin >> i) & 1) ? v[i] : kZero;
-      }
+      for (int i = 0; i < 4; i++)
+        if (4 * i + wave < nks) ((u32x4*)S.sA)[(k & 1) * KSTEPS * 64 + (4 * i + wave) * 64 + lane] = v[i];
     };
-    // the lane's logits of tile i (0..3: register chunks of this wave; 4: its LDS tile) in row (b, j):
-    // 16 columns starting at 64 c + 32 f + 16 h as two 16-byte pieces; columns past V, past the
-    // workgroup's chunks, or of a slot without a row read -inf (the address is clamped to the
-    // tensor's first element and the value replaced)
-    auto tile_cols = [&](int i) -> int {
-      int cl, f;
-      if (i < 4) {
-        cl = AG_CHUNKS * wave + (i >> 1);
-        f = i & 1;
-      } else {
-        cl = NW * AG_CHUNKS + (wave >> 1);
-        f = wave & 1;
-      }
-      if (cl >= nch) return -1;
-      return CH * (cbeg + cl) + 32 * f + 16 * h;
+    // The lane's logits of tile i (0..3: register chunks of this wave; 4: its LDS tile) in a row
+    // are the 16 columns from 64 c + 32 f + 16 h, two 16-byte pieces.  V is a multiple of the
+    // chunk width, so no piece crosses V; tiles of chunks the workgroup does not own read whatever
+    // lies there (zeros past the tensor) and their results are discarded.  row_off is the byte
+    // offset of the lane's first register-tile piece in row j of request b (rows of nrow
+    // positions); the LDS tile lies a wave-uniform distance dlds further.
+    const uint32_t Vb = 2u * (uint32_t)V;
+    const uint32_t dlds = 2u * (uint32_t)(CH * (NW * AG_CHUNKS - AG_CHUNKS * wave + (wave >> 1)) + 32 * (wave & 1));
+    auto row_off = [&](int b, int j, int nrow) -> uint32_t {
+      return (uint32_t)((b >= 0 ? b : 0) * nrow + j) * Vb + 2u * (uint32_t)(CH * (cbeg + AG_CHUNKS * wave) + 16 * h);
     };
-    auto load_tile = [&](const void* rows, int b, int j, int nrow, int i, u32x4 (&T)[2]) {
-      const int v0 = tile_cols(i);
-      const bool in = b >= 0 && v0 >= 0 && v0 < V;
-      const bool in2 = in && v0 + 8 < V;
-      const uint16_t* r = (const uint16_t*)rows + ((size_t)(b >= 0 ? b : 0) * nrow + j) * V;
-      T[0] = ldg16(r + (in ? v0 : 0));
-      T[1] = ldg16(r + (in2 ? v0 + 8 : 0));
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int i, u32x4 (&T)[2]) {
+      const uint32_t off = i < 4 ? (uint32_t)((i >> 1) * 2 * CH + (i & 1) * 64) : 0u;
+      const uint32_t so = i < 4 ? 0u : dlds;
+      T[0] = ldb16(rs, vo + off, so);
+      T[1] = ldb16(rs, vo + off + 16u, so);
     };
-    auto load_tiles = [&](const void* rows, int b, int j, int nrow, u32x4 (&T)[5][2]) {
-#pragma unroll
-      for (int i = 0; i < 5; i++) load_tile(rows, b, j, nrow, i, T[i]);
-    };
-    // columns of tile i past V read -inf (bit 2i: the first 8 columns are inside, bit 2i+1: the
-    // last 8); the same for every row, so the mask is built once
-    int colmask = 0;
-#pragma unroll
-    for (int i = 0; i < 5; i++) {
-      const int v0 = tile_cols(i);
-      colmask |= (v0 >= 0 && v0 < V) ? (1 << (2 * i)) : 0;
-      colmask |= (v0 >= 0 && v0 + 8 < V) ? (2 << (2 * i)) : 0;
-    }
+    const __amdgpu_buffer_rsrc_t rs_base = ld_rsrc(p.a.base, (uint32_t)B * (uint32_t)K * Vb);
+    const __amdgpu_buffer_rsrc_t rs_tgt = ld_rsrc(p.a.target, (uint32_t)B * (uint32_t)(K + 1) * Vb);
     auto seed_acc = [&](const u32x4 (&tt)[2], int i) -> f32x16 {
       float x[16];
-      const u32x4 t0 = ((colmask >> (2 * i)) & 1) ? tt[0] : kNegInf;
-      const u32x4 t1 = ((colmask >> (2 * i)) & 2) ? tt[1] : kNegInf;
-      unpack16(t0, t1, x);
+      unpack16(tt[0], tt[1], x);
       f32x16 a;
 #pragma unroll
       for (int q = 0; q < 16; q++) a[q] = x[q];
@@ -1259,184 +1434,273 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     // Per sub-block, three MFMA passes in turn: register chunk 0 (tiles 0, 1), register chunk 1
     // (tiles 2, 3), the LDS half chunk (tile 4; waves without one run it on zero W and -inf
     // logits, which costs no time: the workgroup waits for the waves that have one).  The
-    // element-wise part of each pass follows the next pass's MFMA chain in program order, so the
-    // two overlap; only 2 or 3 tiles of accumulators are live at a time.
+    // element-wise part of each pass follows the next pass's MFMA chain in straight-line code, so
+    // the two can overlap; only 2 or 3 tiles of accumulators are live at a time.  DRAFT and
+    // CORRECT sub-blocks (the latter after all the former) run in separate loops.
     const bool wave_lds = 2 * n_lds > wave;     // this wave has an LDS tile (wave-uniform)
     const int cg0 = cbeg + AG_CHUNKS * wave;   // global chunk of this wave's register chunk 0
     const bool has0 = AG_CHUNKS * wave < nch, has1 = AG_CHUNKS * wave + 1 < nch;
     const bf16x8* wlw = S.wl + (size_t)wave * KSTEPS * 64;
-    u32x4 Tc[5][2];                            // draft logits of the current sub-block
-    if (ls.n_sb > 0) {
-      u32x4 sv[4];
-      int vin;
-      stage_issue(0, sv, vin);
-      int b, j;
-      bool corr;
-      row_of(0, b, j, corr);
-      load_tiles(p.a.base, b, j, K, Tc);
-      stage_store(0, sv, vin);
-    }
-    __syncthreads();
-    for (int k = 0; k < ls.n_sb; k++) {
-      tid = opaque_tid();
-        int b, j;
-      bool corr;
-      row_of(k, b, j, corr);
-      const bool is_corr_sb = k * SUB >= ls.c0;     // uniform: no sub-block mixes DRAFT and CORRECT rows
-      const ReqMeta rm = S.req[b >= 0 ? b : 0];
-      const float invT = b >= 0 ? rm.invT : 1.0f;
-      const bf16x8* sAk = S.sA + (size_t)(k & 1) * KSTEPS * 64;
-      // in flight during this sub-block: the next sub-block's B operands, and its draft logits,
-      // each tile loaded into the registers its predecessor leaves when it seeds its pass (a
-      // CORRECT sub-block loads its own target logits instead and the next draft logits last)
-      u32x4 sv[4];
-      int vin;
-      stage_issue(k + 1, sv, vin);
-      u32x4 Tt[5][2];
-      int b2 = -1, j2 = 0;
-      bool c2 = false;
-      if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
-      const bool pre = !is_corr_sb;                 // uniform
-      if (!pre) load_tiles(p.a.target, b, j, K + 1, Tt);
-      // the loads above stay here, a whole sub-block ahead of their use (the scheduler would
-      // otherwise sink them towards it)
-      __builtin_amdgcn_sched_barrier(0);
-      if (is_corr_sb) {
-        // target pieces past V read -inf (their residual and target mass are then zero)
+    const int n_dsb = ls.c0 / SUB;             // DRAFT sub-blocks [0, n_dsb), CORRECT [n_dsb, n_sb)
+    auto chain_reg = [&](f32x16& x, f32x16& y, const bf16x8 (&w0)[KSTEPS], const bf16x8 (&w1)[KSTEPS],
+                         const bf16x8* sAk) {
+      bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane];
 #pragma unroll
-        for (int i = 0; i < 5; i++) {
-          Tt[i][0] = ((colmask >> (2 * i)) & 1) ? Tt[i][0] : kNegInf;
-          Tt[i][1] = ((colmask >> (2 * i)) & 2) ? Tt[i][1] : kNegInf;
-        }
+      for (int t = 0; t < KSTEPS; t++) {
+        const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0[t], bop, x, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1[t], bop, y, 0, 0, 0);
+        bop = bop1;
+        bop1 = bop2;
       }
+    };
+    auto chain_lds = [&](f32x16& x, const bf16x8* sAk) {
+      bf16x8 bop = sAk[lane], wl = wlw[lane], bop1 = sAk[64 + lane], wl1 = wlw[64 + lane];
+#pragma unroll
+      for (int t = 0; t < KSTEPS; t++) {
+        const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
+        const bf16x8 wl2 = (t + 2 < KSTEPS) ? wlw[(t + 2) * 64 + lane] : wl;
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, bop, x, 0, 0, 0);
+        bop = bop1;
+        bop1 = bop2;
+        wl = wl1;
+        wl1 = wl2;
+      }
+    };
+    auto pin_w = [&]() {
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int t = 0; t < KSTEPS; t++) asm volatile("" : "+a"(wf[i][t]));
-
-      // pass 0: register chunk 0 (B operands read from LDS two k-steps ahead of their MFMAs)
-      f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
-      if (pre) {
-        load_tile(p.a.base, b2, j2, K, 0, Tc[0]);
-        load_tile(p.a.base, b2, j2, K, 1, Tc[1]);
-      }
-      {
-        bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane];
-#pragma unroll
-        for (int t = 0; t < KSTEPS; t++) {
-          const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
-          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, a1, 0, 0, 0);
-          bop = bop1;
-          bop1 = bop2;
-        }
-      }
-      // pass 1: register chunk 1, with the element-wise part of pass 0 after it
-      f32x16 a2 = seed_acc(Tc[2], 2), a3 = seed_acc(Tc[3], 3);
-      if (pre) {
-        load_tile(p.a.base, b2, j2, K, 2, Tc[2]);
-        load_tile(p.a.base, b2, j2, K, 3, Tc[3]);
-      }
-      {
-        bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane];
-#pragma unroll
-        for (int t = 0; t < KSTEPS; t++) {
-          const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
-          a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[2][t], bop, a2, 0, 0, 0);
-          a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[3][t], bop, a3, 0, 0, 0);
-          bop = bop1;
-          bop1 = bop2;
-        }
-      }
-      WaveRec wr;
-      const uint64_t key = is_corr_sb ? key_of(rm.key_c) : key_of(rm.key_d);
-      const float g0 = gumbel_bits(bits_at(key, (uint32_t)cg0));
-      const float g1 = gumbel_bits(bits_at(key, (uint32_t)(cg0 + 1)));
-      float l0 = -INFINITY, m0 = 0.0f, t0 = -INFINITY;
-      if (!is_corr_sb) {
-        f32x16 aa[2] = {a0, a1};
-        l0 = tiles_lse<2>(aa, invT);
-      } else {
-        chunk_correct(a0, a1, Tt[0][0], Tt[0][1], Tt[1][0], Tt[1][1], invT, rm.lse_p_c, rm.lse_q_c, m0, t0);
-      }
-      // pass L: the LDS half chunk, with the element-wise part of pass 1 after it
-      f32x16 a4 = seed_acc(Tc[4], 4);
-      if (pre) load_tile(p.a.base, b2, j2, K, 4, Tc[4]);
-      {
-        bf16x8 bop = sAk[lane], wl = wlw[lane], bop1 = sAk[64 + lane], wl1 = wlw[64 + lane];
-#pragma unroll
-        for (int t = 0; t < KSTEPS; t++) {
-          const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
-          const bf16x8 wl2 = (t + 2 < KSTEPS) ? wlw[(t + 2) * 64 + lane] : wl;
-          a4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, bop, a4, 0, 0, 0);
-          bop = bop1;
-          bop1 = bop2;
-          wl = wl1;
-          wl1 = wl2;
-        }
-      }
-      float l1 = -INFINITY, m1 = 0.0f, t1 = -INFINITY, hl = -INFINITY, mh = 0.0f, th = -INFINITY;
-      if (!is_corr_sb) {
-        f32x16 aa[2] = {a2, a3};
-        l1 = tiles_lse<2>(aa, invT);
-        hl = tiles_lse<1>(&a4, invT);
-      } else {
-        chunk_correct(a2, a3, Tt[2][0], Tt[2][1], Tt[3][0], Tt[3][1], invT, rm.lse_p_c, rm.lse_q_c, m1, t1);
-        float yl[16];
-#pragma unroll
-        for (int q = 0; q < 16; q++) yl[q] = a4[q];
-        pair_correct<2>(yl, Tt[4], invT, rm.lse_p_c, rm.lse_q_c, mh, th);
-      }
-      if (!has0) {
-        l0 = -INFINITY;
-        m0 = 0.0f;
-        t0 = -INFINITY;
-      }
-      if (!has1) {
-        l1 = -INFINITY;
-        m1 = 0.0f;
-        t1 = -INFINITY;
-      }
-      if (!wave_lds) {
-        hl = -INFINITY;
-        mh = 0.0f;
-        th = -INFINITY;
-      }
-      if (!is_corr_sb) {
-        const float s0 = (l0 > -INFINITY) ? l0 + g0 : -INFINITY;
-        const float s1 = (l1 > -INFINITY) ? l1 + g1 : -INFINITY;
-        float bs = -INFINITY;
-        int bc = -1;
-        if (has0 && !(l0 != l0)) { bs = s0; bc = cg0; }
-        if (has1 && takes(s1, cg0 + 1, bs, bc)) { bs = s1; bc = cg0 + 1; }
-        wr.a = make_float4(lse_add(l0, l1), bs, __int_as_float(bc), hl);
-        wr.t = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), -INFINITY);
-      } else {
-        const float lm0 = m0 > 0.0f ? lg2(m0) * LN2 : -INFINITY;
-        const float lm1 = m1 > 0.0f ? lg2(m1) * LN2 : -INFINITY;
-        float bs = -INFINITY, bt = -INFINITY;
-        int bc = -1, btc = -1;
-        if (lm0 > -INFINITY) { bs = lm0 + g0; bc = cg0; }
-        if (lm1 > -INFINITY && takes(lm1 + g1, cg0 + 1, bs, bc)) { bs = lm1 + g1; bc = cg0 + 1; }
-        if (has0 && t0 > -INFINITY) { bt = t0 + g0; btc = cg0; }
-        if (has1 && t1 > -INFINITY && takes(t1 + g1, cg0 + 1, bt, btc)) { bt = t1 + g1; btc = cg0 + 1; }
-        const float msum = m0 + m1;
-        wr.a = make_float4(msum > 0.0f ? lg2(msum) * LN2 : -INFINITY, bs, __int_as_float(bc), mh);
-        wr.t = make_float4(lse_add(t0, t1), bt, __int_as_float(btc), th);
-        // the next (CORRECT) sub-block's draft logits: its latency is not hidden, CORRECT
-        // sub-blocks are few
-        load_tiles(p.a.base, b2, j2, K, Tc);
-      }
-      stage_store(k + 1, sv, vin);
-      // this wave's record of each row of the sub-block (the merge combines the waves)
+    };
+    auto store_records = [&](int k, bool corr_sb, int b, const WaveRec& wr) {
       if (h == 0 && b >= 0) {
         const size_t ri = ((size_t)(k * SUB + m32) * NW + wave) * MAX_G + g;
         rec_store(rec_rsrc(p.rec_d, rec_d_bytes(B)), ri, wr.a);
-        if (is_corr_sb) {
+        if (corr_sb) {
           const size_t rc = ((size_t)(k * SUB + m32 - ls.c0) * NW + wave) * MAX_G + g;
           rec_store(rec_rsrc(p.rec_c, rec_c_bytes(B)), rc, wr.t);
         }
       }
+    };
+    u32x4 Tc[5][2];                            // draft logits of the current sub-block
+    if (ls.n_sb > 0) {
+      // k-steps past the rank read zeros (the merges reuse this LDS, so they are rewritten here)
+      if (nks < KSTEPS)
+        for (int e = tid; e < 2 * KSTEPS * 64; e += NT)
+          if (((e >> 6) & (KSTEPS - 1)) >= nks) ((u32x4*)S.sA)[e] = kZero;
+      u32x4 sv[4];
+      stage_issue(0, sv);
+      int b, j;
+      bool corr;
+      row_of(0, b, j, corr);
+      const uint32_t vo = row_off(b, j, K);
+#pragma unroll
+      for (int i = 0; i < 5; i++) load_tile(rs_base, vo, i, Tc[i]);
+      stage_store(0, sv);
+    }
+    __syncthreads();
+
+    // DRAFT sub-blocks: chunk log-masses and Gumbel scores of position s
+    for (int k = 0; k < n_dsb; k++) {
+      tid = opaque_tid();
+      int b, j;
+      bool corr;
+      row_of(k, b, j, corr);
+      const ReqMeta rm = S.req[b >= 0 ? b : 0];
+      const float invT = b >= 0 ? rm.invT : 1.0f;
+      const uint64_t key = key_of(rm.key_d);
+      const bf16x8* sAk = S.sA + (size_t)(k & 1) * KSTEPS * 64;
+      // in flight during this sub-block: the next sub-block's B operands, and its draft logits,
+      // each tile loaded into the registers its predecessor leaves when it seeds its pass
+      u32x4 sv[4];
+      stage_issue(k + 1, sv);
+      int b2 = -1, j2 = 0;
+      bool c2 = false;
+      if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
+      const uint32_t vo2 = row_off(b2, j2, K);
+      f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
+      load_tile(rs_base, vo2, 0, Tc[0]);
+      load_tile(rs_base, vo2, 1, Tc[1]);
+      const float lc = invT * LOG2E;
+      __builtin_amdgcn_sched_barrier(0);
+      // Three MFMA chains, each k-step a scheduling region of its own: the chain's MFMAs, the LDS
+      // read two k-steps ahead, and one slice of element-wise work that does not depend on the
+      // chain, so that the VALU issues while the matrix core runs.
+      // chain 0: register chunk 0; slices: the seeds of chain 1, the noise of chunk cg0 + h
+      pin_w();
+      vfence(a0);
+      vfence(a1);
+      vfence(Tc[2]);
+      vfence(Tc[3]);
+      f32x16 a2, a3;
+      GumbelStage gs;
+      {
+        bf16x8 bq[KSTEPS];
+#pragma unroll
+        for (int u = 0; u < 4; u++) bq[u] = sAk[u * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          if (t + 4 < KSTEPS) bq[t + 4] = sAk[(t + 4) * 64 + lane];
+          const bf16x8 bop = bq[t];
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bop, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, a1, 0, 0, 0);
+          if (t < 2) { vfence(Tc[2][t]); seed_piece(a2, Tc[2][t], t); }
+          else if (t < 4) { vfence(Tc[3][t - 2]); seed_piece(a3, Tc[3][t - 2], t - 2); }
+          else if (t < 8) gumbel_step(gs, t - 4, key, (uint32_t)(cg0 + h));
+          if (t >= 4 && t < 8) gumbel_fence(gs, t - 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      float gm = gs.r;
+      load_tile(rs_base, vo2, 2, Tc[2]);
+      load_tile(rs_base, vo2, 3, Tc[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      // chain 1: register chunk 1; slices: chunk 0's log-mass, the seed of the LDS chain
+      vfence(a0);
+      vfence(a1);
+      vfence(Tc[4]);
+      f32x16 a4;
+      Lse2 st0;
+      lse2_init(st0);
+      {
+        bf16x8 bq[KSTEPS];
+#pragma unroll
+        for (int u = 0; u < 4; u++) bq[u] = sAk[u * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          if (t + 4 < KSTEPS) bq[t + 4] = sAk[(t + 4) * 64 + lane];
+          const bf16x8 bop = bq[t];
+          a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[2][t], bop, a2, 0, 0, 0);
+          a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[3][t], bop, a3, 0, 0, 0);
+          if (t < 14) {
+            lse2_step(st0, t, a0, a1, lc, invT);
+            lse2_fence(st0, t);
+          } else {
+            vfence(Tc[4][t - 14]);
+            seed_piece(a4, Tc[4][t - 14], t - 14);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      float l0 = st0.r;
+      load_tile(rs_base, vo2, 4, Tc[4]);
+      __builtin_amdgcn_sched_barrier(0);
+      // chain L: the LDS half chunk; slices: chunk 1's log-mass
+      vfence(a2);
+      vfence(a3);
+      Lse2 st1;
+      lse2_init(st1);
+      {
+        bf16x8 bq[KSTEPS], wq[KSTEPS];
+#pragma unroll
+        for (int u = 0; u < 4; u++) { bq[u] = sAk[u * 64 + lane]; wq[u] = wlw[u * 64 + lane]; }
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          if (t + 4 < KSTEPS) bq[t + 4] = sAk[(t + 4) * 64 + lane];
+          const bf16x8 bop = bq[t];
+          if (t + 4 < KSTEPS) wq[t + 4] = wlw[(t + 4) * 64 + lane];
+          const bf16x8 wl = wq[t];
+          a4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, bop, a4, 0, 0, 0);
+          if (t < 14) {
+            lse2_step(st1, t, a2, a3, lc, invT);
+            lse2_fence(st1, t);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      float l1 = st1.r;
+      const float2 gp = pair32(gm);
+      const float g0 = gp.x, g1 = gp.y;
+      float hl = tiles_lse<1>(&a4, invT);
+      l0 = has0 ? l0 : -INFINITY;
+      l1 = has1 ? l1 : -INFINITY;
+      hl = wave_lds ? hl : -INFINITY;
+      const float s0 = (l0 > -INFINITY) ? l0 + g0 : -INFINITY;
+      const float s1 = (l1 > -INFINITY) ? l1 + g1 : -INFINITY;
+      // best of the two register chunks: larger score, the smaller chunk on ties, a NaN log-mass
+      // never wins (it makes the row invalid through the log-mass)
+      const bool t0 = has0 && !(l0 != l0);
+      float bs = t0 ? s0 : -INFINITY;
+      int bc = t0 ? cg0 : -1;
+      const bool t1 = has1 && takes(s1, cg0 + 1, bs, bc);
+      bs = t1 ? s1 : bs;
+      bc = t1 ? cg0 + 1 : bc;
+      WaveRec wr;
+      wr.a = make_float4(lse_add(l0, l1), bs, __int_as_float(bc), hl);
+      wr.t = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), -INFINITY);
+      stage_store(k + 1, sv);
+      store_records(k, false, b, wr);
+      __syncthreads();
+    }
+
+    // CORRECT sub-blocks: residual mass max(0, p - q) of position s - 1 per chunk with its score,
+    // and the target row's chunk log-masses (the draw falls back to p when no residual is left)
+    for (int k = n_dsb; k < ls.n_sb; k++) {
+      tid = opaque_tid();
+      int b, j;
+      bool corr;
+      row_of(k, b, j, corr);
+      const ReqMeta rm = S.req[b >= 0 ? b : 0];
+      const float invT = b >= 0 ? rm.invT : 1.0f;
+      const uint64_t key = key_of(rm.key_c);
+      const bf16x8* sAk = S.sA + (size_t)(k & 1) * KSTEPS * 64;
+      u32x4 sv[4];
+      stage_issue(k + 1, sv);
+      int b2 = -1, j2 = 0;
+      bool c2 = false;
+      if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
+      const uint32_t vo2 = row_off(b2, j2, K);
+      u32x4 Tt[5][2];
+      const uint32_t vot = row_off(b, j, K + 1);
+#pragma unroll
+      for (int i = 0; i < 5; i++) load_tile(rs_tgt, vot, i, Tt[i]);
+      __builtin_amdgcn_sched_barrier(0);
+      pin_w();
+      f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
+      load_tile(rs_base, vo2, 0, Tc[0]);
+      load_tile(rs_base, vo2, 1, Tc[1]);
+      chain_reg(a0, a1, wf[0], wf[1], sAk);
+      f32x16 a2 = seed_acc(Tc[2], 2), a3 = seed_acc(Tc[3], 3);
+      load_tile(rs_base, vo2, 2, Tc[2]);
+      load_tile(rs_base, vo2, 3, Tc[3]);
+      chain_reg(a2, a3, wf[2], wf[3], sAk);
+      const float gm = gumbel_bf(bits_at(key, (uint32_t)(cg0 + h)));
+      const float2 gp = pair32(gm);
+      const float g0 = gp.x, g1 = gp.y;
+      const float lp = rm.lse_p_c, lq = rm.lse_q_c;
+      float m0, t0, m1, t1, mh, th;
+      chunk_correct(a0, a1, Tt[0][0], Tt[0][1], Tt[1][0], Tt[1][1], invT, lp, lq, m0, t0);
+      f32x16 a4 = seed_acc(Tc[4], 4);
+      load_tile(rs_base, vo2, 4, Tc[4]);
+      chain_lds(a4, sAk);
+      chunk_correct(a2, a3, Tt[2][0], Tt[2][1], Tt[3][0], Tt[3][1], invT, lp, lq, m1, t1);
+      {
+        float yl[16];
+#pragma unroll
+        for (int q = 0; q < 16; q++) yl[q] = a4[q];
+        pair_correct<2>(yl, Tt[4], invT, lp, lq, mh, th);
+      }
+      m0 = has0 ? m0 : 0.0f;
+      t0 = has0 ? t0 : -INFINITY;
+      m1 = has1 ? m1 : 0.0f;
+      t1 = has1 ? t1 : -INFINITY;
+      mh = wave_lds ? mh : 0.0f;
+      th = wave_lds ? th : -INFINITY;
+      const float lm0 = m0 > 0.0f ? lg2(m0) * LN2 : -INFINITY;
+      const float lm1 = m1 > 0.0f ? lg2(m1) * LN2 : -INFINITY;
+      float bs = -INFINITY, bt = -INFINITY;
+      int bc = -1, btc = -1;
+      if (lm0 > -INFINITY) { bs = lm0 + g0; bc = cg0; }
+      if (lm1 > -INFINITY && takes(lm1 + g1, cg0 + 1, bs, bc)) { bs = lm1 + g1; bc = cg0 + 1; }
+      if (has0 && t0 > -INFINITY) { bt = t0 + g0; btc = cg0; }
+      if (has1 && t1 > -INFINITY && takes(t1 + g1, cg0 + 1, bt, btc)) { bt = t1 + g1; btc = cg0 + 1; }
+      const float msum = m0 + m1;
+      WaveRec wr;
+      wr.a = make_float4(msum > 0.0f ? lg2(msum) * LN2 : -INFINITY, bs, __int_as_float(bc), mh);
+      wr.t = make_float4(lse_add(t0, t1), bt, __int_as_float(btc), th);
+      stage_store(k + 1, sv);
+      store_records(k, true, b, wr);
       __syncthreads();
     }
 

@@ -102,8 +102,10 @@ struct Args {
 // Does the resident cycle take these dimensions on a device with G compute units?
 __host__ __device__ inline bool eligible(int B, int K, int V, int R, int dtype, int noise, int G) {
   if (dtype != SPEC_BF16 || noise != SPEC_NOISE_CHUNKED) return false;
-  if (V % 8 != 0 || R % 16 != 0 || R > 256 || G < 1 || G > MAX_G) return false;
+  if (V % CH != 0 || R % 16 != 0 || R > 256 || G < 1 || G > MAX_G) return false;
   if (B < 1 || B > NW * G || B > MAX_B || K < 1 || K > MAX_K) return false;
+  // logit tensors below 4 GiB and A below 2 GiB: their loads use 32-bit byte offsets
+  if ((size_t)B * (K + 1) * V * 2 >= ((size_t)1 << 32) || (size_t)V * R * 2 >= ((size_t)1 << 31)) return false;
   return (n_chunks(V) + G - 1) / G <= MAX_CHUNKS && (V + TP - 1) / TP <= MAX_G;
 }
 

@@ -44,6 +44,8 @@ SMALL = {
     "tiny_fp32": lambda: wl.generate("tiny"),
     "ragged_v333_bf16": lambda: wl.generate(wl.small_config(B=12, K=6, V=333, R=32, threshold=0.15)),
     "v20000_bf16_two_plain_items": lambda: wl.generate(wl.small_config(B=40, K=5, V=20000, R=64, threshold=0.1)),
+    # the same on whole 64-column chunks, which the resident cycle also takes
+    "v20032_bf16_five_plain_items": lambda: wl.generate(wl.small_config(B=40, K=5, V=20032, R=64, threshold=0.1)),
     "b300_two_row_blocks": lambda: wl.generate(wl.small_config(B=300, K=3, V=2048, R=16, threshold=0.05)),
     "fp32_v1001": lambda: wl.generate(wl.small_config(B=5, K=4, V=1001, R=8, dtype=wl.FP32, threshold=0.1)),
     "k1_b1": lambda: wl.generate(wl.small_config(B=1, K=1, V=4096, R=256, threshold=0.1)),
@@ -67,7 +69,7 @@ def test_small_cases_match_oracle(case, noise):
 
 @pytest.mark.parametrize("noise", NOISES)
 def test_no_previous_token_and_cut_extremes(noise):
-    w = wl.generate(wl.small_config(B=8, K=4, V=3000, R=32, threshold=0.2))
+    w = wl.generate(wl.small_config(B=8, K=4, V=3008, R=32, threshold=0.2))
     full_compare(w, noise, x0=False)
     w.threshold = 2.0   # nothing survives the cut: one bonus token per request
     g, _ = full_compare(w, noise)
@@ -79,7 +81,7 @@ def test_no_previous_token_and_cut_extremes(noise):
 
 @pytest.mark.parametrize("noise", NOISES)
 def test_identical_draft_and_target_accept_all(noise):
-    w = wl.generate(wl.small_config(B=8, K=5, V=2000, R=16, threshold=0.05))
+    w = wl.generate(wl.small_config(B=8, K=5, V=2048, R=16, threshold=0.05))
     w.base[:] = w.target[:, :5]
     w.A[:] = 0
     w.W[:] = 0
@@ -103,7 +105,7 @@ def test_invalid_requests(noise):
 
 @pytest.mark.parametrize("noise", NOISES)
 def test_determinism_and_sharding(noise):
-    w = wl.generate(wl.small_config(B=20, K=5, V=4000, R=32, threshold=0.1))
+    w = wl.generate(wl.small_config(B=20, K=5, V=4032, R=32, threshold=0.1))
     h = 7
     half = wl.Workload(w.cfg, w.base[h:], w.target[h:], w.A, w.W, w.x0[h:], w.conf[h:], w.temp[h:], w.threshold,
                        w.seed, w.request_ids[h:])
@@ -164,7 +166,7 @@ def test_side_stream_matches_default_stream():
     import torch
     from draft_sampling_lossless_spec_amd import spec_cycle
     print("side stream", flush=True)
-    w = wl.generate(wl.small_config(B=20, K=5, V=4000, R=32, threshold=0.1))
+    w = wl.generate(wl.small_config(B=20, K=5, V=4032, R=32, threshold=0.1))
     g1 = run_gpu(w, oracle.CHUNKED)
     d = to_device(w)
     torch.cuda.synchronize()

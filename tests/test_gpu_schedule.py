@@ -87,7 +87,7 @@ def gpu_cycle_lengths(w, L, noise, dev=None, path=0):
 @pytest.mark.parametrize("noise", [oracle.FLAT, oracle.CHUNKED])
 def test_cycle_lengths_matches_oracle(noise):
     print(f"cycle with given lengths noise={noise}", flush=True)
-    w = wl.generate(wl.small_config(B=24, K=6, V=2000, R=32, threshold=0.1))
+    w = wl.generate(wl.small_config(B=24, K=6, V=2048, R=32, threshold=0.1))
     rng = np.random.default_rng(17)
     L = rng.integers(0, 7, 24).astype(np.int32)
     L[3], L[7] = -1, 7                      # bad lengths mark the request invalid

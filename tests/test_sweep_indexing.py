@@ -172,9 +172,44 @@ def resident_smem(B):
     return o + NW * 16
 
 
-def resident_eligible(B, K, V, G):
-    return (V % 8 == 0 and 1 <= B <= NW * G and B <= 1024 and 1 <= K <= 32
+def resident_eligible(B, K, V, G, R=256):
+    return (V % CHUNK == 0 and R % 16 == 0 and R <= 256 and 1 <= B <= NW * G and B <= 1024
+            and 1 <= K <= 32 and B * (K + 1) * V * 2 < 1 << 32 and V * R * 2 < 1 << 31
             and -(-n_chunks(V) // G) <= MAX_CHUNKS and -(-V // TP) <= MAX_G)
+
+
+@pytest.mark.parametrize("B,K,V", [(64, 5, 151936), (256, 16, 151936), (1024, 5, 129280), (512, 16, 151936),
+                                   (1024, 32, 151936), (2, 4, 1024), (1024, 12, 163840)])
+def test_resident_tile_offsets_fit(B, K, V):
+    """The bias tiles are buffer loads with 32-bit byte offsets: row offset + the lane's column base
+    + a per-tile immediate (register tiles) or the wave's LDS-tile distance.  For every eligible
+    shape the largest offset stays below 2^32, owned pieces lie inside their row, and the A-row
+    staging offsets of a previous token stay below the 2^31 marker that reads zeros."""
+    G, R = 256, 256
+    if not resident_eligible(B, K, V, G):
+        assert B * (K + 1) * V * 2 >= 1 << 32 or V % CHUNK or B > NW * G
+        pytest.skip("not eligible")
+    cb = np.array([chunk_begin(g, G, V) for g in range(G)])
+    nc = np.array([chunks_of(g, G, V) for g in range(G)])
+    for nrow in (K, K + 1):
+        last_row = B * nrow - 1
+        for w in range(NW):
+            dlds = 2 * (CHUNK * (NW * AG_CHUNKS - AG_CHUNKS * w + (w >> 1)) + 32 * (w & 1))
+            assert dlds > 0
+            for h in (0, 1):
+                col = 2 * (CHUNK * (cb + AG_CHUNKS * w) + 16 * h)           # per workgroup
+                base = last_row * 2 * V + col
+                for i in range(5):
+                    off = ((i >> 1) * 2 * CHUNK + (i & 1) * 64) if i < 4 else dlds
+                    top = base + off + 16 + 16
+                    assert top.max() < 1 << 32
+                    cl = AG_CHUNKS * w + (i >> 1) if i < 4 else NW * AG_CHUNKS + (w >> 1)
+                    own = cl < nc
+                    # an owned piece ends inside its row
+                    assert np.all((col + off + 32)[own] <= 2 * V)
+    # A rows: prev * R + h R/2 + 8 w entries, plus 32 i (i < 4) entries, 16 bytes each read
+    top = 2 * ((V - 1) * R + R // 2 + 8 * 3) + 64 * 3 + 16
+    assert top <= V * R * 2 and V * R * 2 < 1 << 31
 
 
 @pytest.mark.parametrize("V", [8, 1024, 2048, 3000, 3008, 20000, 129280, 151936, 163840])
