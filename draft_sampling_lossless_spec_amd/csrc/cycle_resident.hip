@@ -776,7 +776,8 @@ struct L2Out {
 // LDS scratch of the merge phase (it lives in the B-operand buffers, idle between the barriers)
 struct MergeLds {
   uint16_t arow[2][256];   // A rows of the two level-two jobs
-  float4 rec[4][NW];       // per-wave reductions of the records of the request's four row kinds
+  float4 part[4][NT];      // per-workgroup records of the request's four row kinds (thread t: workgroup t)
+  float4 rec[4][NW];       // the four kinds' totals (entry [r][0])
   float4 win[2][NW];       // per-wave level-two winners {score, index, scaled draft logit, target logit}
 };
 
@@ -784,14 +785,14 @@ struct MergeLds {
 // columns 64 chunk + 16 w .. + 16, four lanes per column, each lane a quarter of the rank (eight
 // 16-byte pieces of the column's W row and the staged A row); the quarters are summed across the
 // lane quad, the winner is found per wave, then across the waves.  Result uniform.
-__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
+__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, uint2 arow_v,
+                                          L2Out (&out)[2]) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int V = p.a.V, R = p.a.R, P16 = R >> 3;
   // every load of the round is issued before any of them is waited for: the A rows (staged in
   // LDS below), the W rows, the draft and target logits of the 64 candidate columns
   const int qa = (tid >> 6) & 1, la = tid & 63;
   const bool lda = tid < 128 && jb[qa].kind != L2_NONE && jb[qa].kind != L2_TARGET && jb[qa].prev >= 0 && 4 * la < R;
-  const uint2 arow_v = *(const uint2*)((const uint16_t*)p.a.A + (lda ? (size_t)jb[qa].prev * R + 4 * la : 0));
   const int col = 16 * wave + (lane >> 2), kq = lane & 3;
   int v[2];
   bool in[2], need_base[2], need_targ[2], wld[2][8];
@@ -847,7 +848,7 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
     float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
     int ix = -1;
     if (in[q] && kq == 0) {
-      const float gg = gumbel_bits(bits_at(jb[q].key, (uint32_t)v[q]));
+      const float gg = gumbel_bf(bits_at(jb[q].key, (uint32_t)v[q]));
       if (jb[q].kind == L2_DRAFT) {
         const float sv = (bv[q] + bias[q]) * invT;
         if (jb[q].want_target) tx = tv[q];
@@ -920,7 +921,7 @@ __device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl
     const float hc = lse_add(a[2 * i].w, a[2 * i + 1].w);
     lse = lse_add(lse, hc);
     const int cgl = cb + NW * AG_CHUNKS + i;
-    const float sc = hc > -INFINITY ? hc + gumbel_bits(bits_at(key, (uint32_t)cgl)) : -INFINITY;
+    const float sc = hc > -INFINITY ? hc + gumbel_bf(bits_at(key, (uint32_t)cgl)) : -INFINITY;
     if (hc > -INFINITY && takes(sc, cgl, bs, bc)) {
       bs = sc;
       bc = cgl;
@@ -953,7 +954,7 @@ __device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (
   for (int i = 0; i < LDS_CHUNKS; i++) {
     if (i >= nl) break;
     const int cgl = cb + NW * AG_CHUNKS + i;
-    const float gg = gumbel_bits(bits_at(key, (uint32_t)cgl));
+    const float gg = gumbel_bf(bits_at(key, (uint32_t)cgl));
     const float mc = a[2 * i].w + a[2 * i + 1].w;
     ms += mc;
     const float lmc = mc > 0.0f ? lg2(mc) * LN2 : -INFINITY;
@@ -994,71 +995,77 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
   const bool hasD = roles & RO_DRAFT, hasC = roles & RO_CORRECT, hasP = roles & (RO_LSEP | RO_BONUS);
   const int sd = S.slot[b], sc_ = S.slot[B + b], sp = S.slot[2 * B + b];
   const int x_t = tid < K ? p.xs[(size_t)b * K + tid] : -1;   // drafted tokens, for the output
-  // ---- records of every row of the request: thread t takes record t, then waves, then LDS ----
+  // ---- records of every row of the request: thread t combines workgroup t's wave records of
+  //      each row kind (G <= NT) and takes plain item t (ceil(V / TP) <= NT); the combined records
+  //      go to LDS, where wave r reduces kind r (DRAFT, CORRECT residual, CORRECT target, plain) ----
+  // A rows of the two level-two jobs (DRAFT: the token before position s; CORRECT: the token before
+  // s - 1), loaded now so that their latency hides behind the records'; thread t < 128 takes four
+  // entries of job t / 64 (a job without a previous token reads past the end of A: zeros)
+  uint2 arow_v;
   {
-    PAcc a4[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) pacc_init(a4[r]);
-    const uint64_t key_d = pos_key(kreq, s, ST_DRAFT_C), key_c = pos_key(kreq, s > 0 ? s - 1 : 0, ST_RESIDUAL_C);
-    // thread t takes workgroup t's records of each row kind (G <= NT) and plain item t
-    // (ceil(V / TP) <= NT); the DRAFT and plain records are loaded together (one round trip; a
-    // kind the request does not have reads row 0 and is ignored), the CORRECT ones (a request
-    // has them at most once) on their own, so few records are held in registers at a time
+    const int qa = (tid >> 6) & 1, la = tid & 63;
+    const int prev = qa == 0 ? (hasD ? rm.prev_d : -1) : (hasC ? rm.prev_c : -1);
+    const __amdgpu_buffer_rsrc_t rsA = ld_rsrc(p.a.A, (uint32_t)V * (uint32_t)p.a.R * 2u);
+    const bool in = tid < 128 && prev >= 0 && 4 * la < p.a.R;
+    const uint32_t vo = in ? 2u * (uint32_t)(prev * p.a.R + 4 * la) : OOB_OFF;
+    arow_v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsA, (int)vo, 0, 0));
+  }
+  uint64_t key_l2d, key_l2r, key_l2b, key_acc;   // per-index noise keys of the level-two rows and the accept draw
+  {
+    const uint64_t key_d = key_of(rm.key_d), key_c = key_of(rm.key_c);
     const int nrP = (V + TP - 1) / TP;
     const int gi = tid < G ? tid : 0;
     const int cb = chunk_begin(gi, G, V), ncw = chunks_of(gi, G, V);
     const int nl = ncw > NW * AG_CHUNKS ? ncw - NW * AG_CHUNKS : 0;
-    if (hasD || hasP) {
-      const auto rs_d = rec_rsrc(p.rec_d, rec_d_bytes(B)), rs_p = rec_rsrc(p.rec_p, rec_p_bytes(B));
-      const size_t rd_base = (size_t)(hasD ? sd : 0) * NW * MAX_G + gi;
-      float4 ad[NW];
+    const float4 none = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f);
+    // every load of the request's records is issued before any is used (a kind the request does
+    // not have reads row 0 and is ignored)
+    const auto rs_d = rec_rsrc(p.rec_d, rec_d_bytes(B)), rs_p = rec_rsrc(p.rec_p, rec_p_bytes(B)),
+               rs_c = rec_rsrc(p.rec_c, rec_c_bytes(B));
+    const size_t rd_base = (size_t)(hasD ? sd : 0) * NW * MAX_G + gi;
+    const size_t rc_base = (size_t)(hasC ? sc_ : 0) * NW * MAX_G + gi;
+    const size_t rt_base = (size_t)(hasC ? sc_ - c0 : 0) * NW * MAX_G + gi;
+    float4 ad[NW], ac[NW], at[NW];
 #pragma unroll
-      for (int w = 0; w < NW; w++) ad[w] = rec_load(rs_d, rd_base + (size_t)w * MAX_G);
-      const float4 ap = rec_load(rs_p, (size_t)(hasP ? sp : 0) * MAX_G + (tid < nrP ? tid : 0));
-      __builtin_amdgcn_sched_barrier(0);   // the five loads are in flight before any is used
-      if (hasD && tid < G) pacc_add(a4[0], wg_draft(ad, cb, nl, key_d));
-      if (hasP && tid < nrP) pacc_add(a4[3], ap);
-    }
+    for (int w = 0; w < NW; w++) ad[w] = rec_load(rs_d, rd_base + (size_t)w * MAX_G);
+    const float4 ap = rec_load(rs_p, (size_t)(hasP ? sp : 0) * MAX_G + (tid < nrP ? tid : 0));
     if (hasC) {
-      const auto rs_d = rec_rsrc(p.rec_d, rec_d_bytes(B)), rs_c = rec_rsrc(p.rec_c, rec_c_bytes(B));
-      const size_t rc_base = (size_t)sc_ * NW * MAX_G + gi, rt_base = (size_t)(sc_ - c0) * NW * MAX_G + gi;
-      float4 ac[NW], at[NW];
 #pragma unroll
       for (int w = 0; w < NW; w++) {
         ac[w] = rec_load(rs_d, rc_base + (size_t)w * MAX_G);
         at[w] = rec_load(rs_c, rt_base + (size_t)w * MAX_G);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (tid < G) {
-        float4 rd, rt;
-        wg_correct(ac, at, cb, nl, key_c, rd, rt);
-        pacc_add(a4[1], rd);
-        pacc_add(a4[2], rt);
-      }
     }
+    key_l2d = pos_key(kreq, s, ST_DRAFT);
+    key_l2r = pos_key(kreq, s > 0 ? s - 1 : 0, ST_RESIDUAL);
+    key_l2b = pos_key(kreq, s, ST_BONUS);
+    key_acc = pos_key(kreq, s, ST_ACCEPT);
+    __builtin_amdgcn_sched_barrier(0);   // the loads are in flight before any is used
+    ml->part[0][tid] = (hasD && tid < G) ? wg_draft(ad, cb, nl, key_d) : none;
+    ml->part[3][tid] = (hasP && tid < nrP) ? ap : none;
+    if (hasC) {
+      float4 rd = none, rt = none;
+      if (tid < G) wg_correct(ac, at, cb, nl, key_c, rd, rt);
+      ml->part[1][tid] = rd;
+      ml->part[2][tid] = rt;
+    }
+    __syncthreads();
+    const bool kind_on = wave == 0 ? hasD : (wave == 3 ? hasP : hasC);   // wave-uniform
+    if (kind_on) {
+      PAcc a;
+      pacc_init(a);
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const float4 t = pacc_wave(a4[r]);
-      if (lane == 0) ml->rec[r][wave] = t;
+      for (int i = 0; i < NT / 64; i++) pacc_add(a, ml->part[wave][64 * i + lane]);
+      const float4 t = pacc_wave(a);
+      if (lane == 0) ml->rec[wave][0] = t;
+    } else if (lane == 0) {
+      ml->rec[wave][0] = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f);
     }
   }
   __syncthreads();
   float4 tot[4];
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
-    // merge of the four waves' {log-mass, best score, best chunk}
-    float4 x = ml->rec[r][0];
-#pragma unroll
-    for (int w = 1; w < NW; w++) {
-      const float4 c = ml->rec[r][w];
-      x.x = lse_add(x.x, c.x);
-      if (takes(c.y, __float_as_int(c.z), x.y, __float_as_int(x.z))) {
-        x.y = c.y;
-        x.z = c.z;
-      }
-    }
-    tot[r] = x;
-  }
+  for (int r = 0; r < 4; r++) tot[r] = ml->rec[r][0];
   const float4 tot_d = tot[0], tot_c = tot[1], tot_c2 = tot[2], tot_p = tot[3];
 
   // ---- level two: the DRAFT row and the CORRECT / BONUS row side by side ----
@@ -1082,14 +1089,14 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     jb[0].kind = L2_DRAFT;
     jb[0].chunk = __float_as_int(tot_d.z);
     jb[0].prev = rm.prev_d;
-    jb[0].key = pos_key(kreq, s, ST_DRAFT);
+    jb[0].key = key_l2d;
     jb[0].base = (const uint16_t*)p.a.base + ((size_t)b * K + s) * V;
     jb[0].targ = targ_s;
     jb[0].want_target = (roles & RO_LSEP) != 0;
   }
   if (hasC) {
     jb[1].chunk = __float_as_int(residual ? tot_c.z : tot_c2.z);
-    jb[1].key = pos_key(kreq, j_c, ST_RESIDUAL);
+    jb[1].key = key_l2r;
     jb[1].targ = (const uint16_t*)p.a.target + ((size_t)b * (K + 1) + j_c) * V;
     if (residual) {
       jb[1].kind = L2_RESIDUAL;
@@ -1103,11 +1110,11 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
   } else if ((roles & RO_BONUS) && isfinite(tot_p.x)) {
     jb[1].kind = L2_TARGET;
     jb[1].chunk = __float_as_int(tot_p.z);
-    jb[1].key = pos_key(kreq, s, ST_BONUS);
+    jb[1].key = key_l2b;
     jb[1].targ = targ_s;
   }
   L2Out r2[2];
-  level_two(p, jb, invT, ml, r2);
+  level_two(p, jb, invT, ml, arow_v, r2);
   const L2Out rd = r2[0], rf = r2[1];
 
   // ---- decision and outputs (uniform over the workgroup; thread 0 writes scalars) ----
@@ -1135,7 +1142,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
       invalid = true;
     } else {
       const float logp_s = rd.tx * invT - lse_p;
-      const uint32_t ub = bits_at(pos_key(kreq, s, ST_ACCEPT), 0);
+      const uint32_t ub = bits_at(key_acc, 0);
       const double u = ((double)ub + 0.5) * 0x1p-32;
       const double ratio = exp((double)logp_s - (double)logq_s);
       if (u < ratio) {
