@@ -464,6 +464,43 @@ __device__ __forceinline__ float tgt4(const u32x4& t0, const u32x4& t1, const u3
   return (i & 1) ? bf_hi(w) : bf_lo(w);
 }
 
+// CORRECT element-wise slice: values i0, i0 + 1 of a chunk held in two accumulator tiles (x, y:
+// draft logits with the Markov bias) and four packed target pieces.  With p = exp2(t c + op) and
+// q = exp2(x c + oq) the normalised target and draft probabilities (op, oq: minus the rows'
+// log-normalisers in base 2), it adds max(p - q, 0) to the residual sums and p to the target sums.
+struct Corr2 {
+  float r0, r1, p0, p1;
+};
+__device__ __forceinline__ void corr_step(Corr2& st, int i0, const f32x16& x, const f32x16& y, const u32x4& t0,
+                                          const u32x4& t1, const u32x4& t2, const u32x4& t3, float c, float op,
+                                          float oq) {
+#pragma unroll
+  for (int i = i0; i < i0 + 2; i++) {
+    const float ep = ex2(fmaf(tgt4(t0, t1, t2, t3, i), c, op));
+    const float eq = ex2(fmaf(acc2(x, y, i), c, oq));
+    if (i & 1) {
+      st.r1 += fmaxf(ep - eq, 0.0f);
+      st.p1 += ep;
+    } else {
+      st.r0 += fmaxf(ep - eq, 0.0f);
+      st.p0 += ep;
+    }
+  }
+}
+__device__ __forceinline__ void corr_fence(Corr2& st) {
+  vfence(st.r0);
+  vfence(st.r1);
+  vfence(st.p0);
+  vfence(st.p1);
+}
+// residual mass (linear) and target log-mass of a lane pair's sums; lse_p: the target row's
+// log-normaliser (natural units)
+__device__ __forceinline__ void corr_end(const Corr2& st, float lse_p, float& mass, float& tlse) {
+  mass = psum32(st.r0 + st.r1);
+  const float sp = psum32(st.p0 + st.p1);
+  tlse = sp > 0.0f ? lse_p + lg2(sp) * LN2 : (sp == 0.0f ? -INFINITY : NAN);
+}
+
 // CORRECT element-wise part of one chunk (two tiles) of a lane and its partner lane: the residual
 // mass sum max(0, p - q) (linear) and the target log-mass, straight from the accumulators and the
 // packed target logits
@@ -1658,35 +1695,113 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       bool c2 = false;
       if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
       const uint32_t vo2 = row_off(b2, j2, K);
+      // target logits of the row, each tile loaded a chain ahead of its use
       u32x4 Tt[5][2];
       const uint32_t vot = row_off(b, j, K + 1);
-#pragma unroll
-      for (int i = 0; i < 5; i++) load_tile(rs_tgt, vot, i, Tt[i]);
-      __builtin_amdgcn_sched_barrier(0);
-      pin_w();
+      load_tile(rs_tgt, vot, 0, Tt[0]);
+      load_tile(rs_tgt, vot, 1, Tt[1]);
       f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
       load_tile(rs_base, vo2, 0, Tc[0]);
       load_tile(rs_base, vo2, 1, Tc[1]);
-      chain_reg(a0, a1, wf[0], wf[1], sAk);
-      f32x16 a2 = seed_acc(Tc[2], 2), a3 = seed_acc(Tc[3], 3);
+      const float lp = rm.lse_p_c;
+      const float c = invT * LOG2E, op = -rm.lse_p_c * LOG2E, oq = -rm.lse_q_c * LOG2E;
+      __builtin_amdgcn_sched_barrier(0);
+      // chain 0: register chunk 0; slices: the seeds of chain 1, the noise of chunk cg0 + h
+      pin_w();
+      vfence(a0);
+      vfence(a1);
+      f32x16 a2, a3;
+      GumbelStage gs;
+      {
+        bf16x8 bq[KSTEPS];
+#pragma unroll
+        for (int u = 0; u < 4; u++) bq[u] = sAk[u * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          if (t + 4 < KSTEPS) bq[t + 4] = sAk[(t + 4) * 64 + lane];
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[0][t], bq[t], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bq[t], a1, 0, 0, 0);
+          if (t < 2) {
+            vfence(Tc[2][t]);
+            seed_piece(a2, Tc[2][t], t);
+          } else if (t < 4) {
+            vfence(Tc[3][t - 2]);
+            seed_piece(a3, Tc[3][t - 2], t - 2);
+          } else if (t < 8) {
+            gumbel_step(gs, t - 4, key, (uint32_t)(cg0 + h));
+            gumbel_fence(gs, t - 4);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      float gm = gs.r;
       load_tile(rs_base, vo2, 2, Tc[2]);
       load_tile(rs_base, vo2, 3, Tc[3]);
-      chain_reg(a2, a3, wf[2], wf[3], sAk);
-      const float gm = gumbel_bf(bits_at(key, (uint32_t)(cg0 + h)));
+      load_tile(rs_tgt, vot, 2, Tt[2]);
+      load_tile(rs_tgt, vot, 3, Tt[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      // chain 1: register chunk 1; slices: chunk 0's residual and target sums, the LDS seed
+      vfence(a0);
+      vfence(a1);
+      f32x16 a4;
+      Corr2 c0s = {0.0f, 0.0f, 0.0f, 0.0f};
+      {
+        bf16x8 bq[KSTEPS];
+#pragma unroll
+        for (int u = 0; u < 4; u++) bq[u] = sAk[u * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          if (t + 4 < KSTEPS) bq[t + 4] = sAk[(t + 4) * 64 + lane];
+          a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[2][t], bq[t], a2, 0, 0, 0);
+          a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[3][t], bq[t], a3, 0, 0, 0);
+          corr_step(c0s, 2 * t, a0, a1, Tt[0][0], Tt[0][1], Tt[1][0], Tt[1][1], c, op, oq);
+          corr_fence(c0s);
+          if (t >= 14) {
+            vfence(Tc[4][t - 14]);
+            seed_piece(a4, Tc[4][t - 14], t - 14);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      load_tile(rs_base, vo2, 4, Tc[4]);
+      load_tile(rs_tgt, vot, 4, Tt[4]);
+      __builtin_amdgcn_sched_barrier(0);
+      // chain L: the LDS half chunk; slices: chunk 1's residual and target sums
+      vfence(a2);
+      vfence(a3);
+      Corr2 c1s = {0.0f, 0.0f, 0.0f, 0.0f};
+      {
+        bf16x8 bq[KSTEPS], wq[KSTEPS];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          bq[u] = sAk[u * 64 + lane];
+          wq[u] = wlw[u * 64 + lane];
+        }
+#pragma unroll
+        for (int t = 0; t < KSTEPS; t++) {
+          if (t + 4 < KSTEPS) {
+            bq[t + 4] = sAk[(t + 4) * 64 + lane];
+            wq[t + 4] = wlw[(t + 4) * 64 + lane];
+          }
+          a4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wq[t], bq[t], a4, 0, 0, 0);
+          corr_step(c1s, 2 * t, a2, a3, Tt[2][0], Tt[2][1], Tt[3][0], Tt[3][1], c, op, oq);
+          corr_fence(c1s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       const float2 gp = pair32(gm);
       const float g0 = gp.x, g1 = gp.y;
-      const float lp = rm.lse_p_c, lq = rm.lse_q_c;
       float m0, t0, m1, t1, mh, th;
-      chunk_correct(a0, a1, Tt[0][0], Tt[0][1], Tt[1][0], Tt[1][1], invT, lp, lq, m0, t0);
-      f32x16 a4 = seed_acc(Tc[4], 4);
-      load_tile(rs_base, vo2, 4, Tc[4]);
-      chain_lds(a4, sAk);
-      chunk_correct(a2, a3, Tt[2][0], Tt[2][1], Tt[3][0], Tt[3][1], invT, lp, lq, m1, t1);
+      corr_end(c0s, lp, m0, t0);
+      corr_end(c1s, lp, m1, t1);
       {
-        float yl[16];
+        // the LDS half tile: 16 values against two target pieces
+        Corr2 hs = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x16 zero = {};
 #pragma unroll
-        for (int q = 0; q < 16; q++) yl[q] = a4[q];
-        pair_correct<2>(yl, Tt[4], invT, lp, lq, mh, th);
+        for (int i = 0; i < 16; i += 2)
+          corr_step(hs, i, a4, zero, Tt[4][0], Tt[4][1], Tt[4][0], Tt[4][1], c, op, oq);
+        corr_end(hs, lp, mh, th);
       }
       m0 = has0 ? m0 : 0.0f;
       t0 = has0 ? t0 : -INFINITY;
