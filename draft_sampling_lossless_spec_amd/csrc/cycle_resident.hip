@@ -373,6 +373,44 @@ __device__ __forceinline__ void lse2_fence(Lse2& st, int t) {
   }
 }
 
+// The same for the 16 values of one tile (steps 0..6; the result in step 6).
+__device__ __forceinline__ void lse1_step(Lse2& st, int t, const f32x16& x, float c, float invT) {
+  if (t < 2) {
+#pragma unroll
+    for (int q = 8 * t; q < 8 * t + 8; q += 2) {
+      st.m0 = fmaxf(st.m0, x[q]);
+      st.m1 = fmaxf(st.m1, x[q + 1]);
+    }
+    if (t == 1) {
+      st.m0 = pmax32(fmaxf(st.m0, st.m1));
+      st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
+    }
+  } else if (t < 6) {
+    const int q = 4 * (t - 2);
+    st.s0 += ex2(fmaf(x[q], c, -st.mo));
+    st.s1 += ex2(fmaf(x[q + 1], c, -st.mo));
+    st.s2 += ex2(fmaf(x[q + 2], c, -st.mo));
+    st.s3 += ex2(fmaf(x[q + 3], c, -st.mo));
+  } else if (t == 6) {
+    const float sum = psum32((st.s0 + st.s1) + (st.s2 + st.s3));
+    st.r = (st.m0 == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : st.m0 * invT + lg2(sum) * LN2;
+  }
+}
+__device__ __forceinline__ void lse1_fence(Lse2& st, int t) {
+  if (t < 2) {
+    vfence(st.m0);
+    vfence(st.m1);
+    if (t == 1) vfence(st.mo);
+  } else if (t < 6) {
+    vfence(st.s0);
+    vfence(st.s1);
+    vfence(st.s2);
+    vfence(st.s3);
+  } else if (t == 6) {
+    vfence(st.r);
+  }
+}
+
 // Gumbel noise of index i of a noise row (the same arithmetic as gumbel_bf(bits_at(key, i))) in
 // four slices: the two SplitMix64 rounds, the uniform and the logarithm's argument, the result.
 struct GumbelStage {
@@ -1545,7 +1583,34 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     }
     __syncthreads();
 
-    // DRAFT sub-blocks: chunk log-masses and Gumbel scores of position s
+    // DRAFT sub-blocks: chunk log-masses and Gumbel scores of position s.  The last part of a
+    // sub-block (its LDS tile's log-mass and its records) runs in the next sub-block's first chain,
+    // which has VALU issue slots to spare; the state of that part is carried over.
+    // record of DRAFT sub-block kk from its scalars and LDS-tile log-mass
+    auto draft_record = [&](int kk, int bb, float l0, float l1, float gm, float hl) __attribute__((always_inline)) {
+      const float2 gp = pair32(gm);
+      const float g0 = gp.x, g1 = gp.y;
+      l0 = has0 ? l0 : -INFINITY;
+      l1 = has1 ? l1 : -INFINITY;
+      hl = wave_lds ? hl : -INFINITY;
+      const float s0 = (l0 > -INFINITY) ? l0 + g0 : -INFINITY;
+      const float s1 = (l1 > -INFINITY) ? l1 + g1 : -INFINITY;
+      // best of the two register chunks: larger score, the smaller chunk on ties, a NaN log-mass
+      // never wins (it makes the row invalid through the log-mass)
+      const bool t0 = has0 && !(l0 != l0);
+      float bs = t0 ? s0 : -INFINITY;
+      int bc = t0 ? cg0 : -1;
+      const bool t1 = has1 && takes(s1, cg0 + 1, bs, bc);
+      bs = t1 ? s1 : bs;
+      bc = t1 ? cg0 + 1 : bc;
+      WaveRec wr;
+      wr.a = make_float4(lse_add(l0, l1), bs, __int_as_float(bc), hl);
+      wr.t = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), -INFINITY);
+      store_records(kk, false, bb, wr);
+    };
+    f32x16 a4p = {};                     // the previous sub-block's LDS-tile accumulators
+    float l0p = 0.0f, l1p = 0.0f, gmp = 0.0f, invTp = 1.0f;
+    int bp = -1;                         // its row (-1: none, or no previous sub-block)
     for (int k = 0; k < n_dsb; k++) {
       tid = opaque_tid();
       int b, j;
@@ -1571,14 +1636,18 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       // Three MFMA chains, each k-step a scheduling region of its own: the chain's MFMAs, the LDS
       // read two k-steps ahead, and one slice of element-wise work that does not depend on the
       // chain, so that the VALU issues while the matrix core runs.
-      // chain 0: register chunk 0; slices: the seeds of chain 1, the noise of chunk cg0 + h
+      // chain 0: register chunk 0; slices: the seeds of chain 1, the noise of chunk cg0 + h, the
+      // previous sub-block's LDS-tile log-mass and records
       pin_w();
       vfence(a0);
       vfence(a1);
       vfence(Tc[2]);
       vfence(Tc[3]);
+      vfence(a4p);
       f32x16 a2, a3;
       GumbelStage gs;
+      Lse2 stp;
+      lse2_init(stp);
       {
         bf16x8 bq[KSTEPS];
 #pragma unroll
@@ -1592,7 +1661,10 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           if (t < 2) { vfence(Tc[2][t]); seed_piece(a2, Tc[2][t], t); }
           else if (t < 4) { vfence(Tc[3][t - 2]); seed_piece(a3, Tc[3][t - 2], t - 2); }
           else if (t < 8) gumbel_step(gs, t - 4, key, (uint32_t)(cg0 + h));
+          else if (t < 15) lse1_step(stp, t - 8, a4p, invTp * LOG2E, invTp);
+          else draft_record(k - 1, bp, l0p, l1p, gmp, stp.r);   // stores nothing for bp < 0
           if (t >= 4 && t < 8) gumbel_fence(gs, t - 4);
+          else if (t >= 8 && t < 15) lse1_fence(stp, t - 8);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1654,29 +1726,16 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         }
       }
       float l1 = st1.r;
-      const float2 gp = pair32(gm);
-      const float g0 = gp.x, g1 = gp.y;
-      float hl = tiles_lse<1>(&a4, invT);
-      l0 = has0 ? l0 : -INFINITY;
-      l1 = has1 ? l1 : -INFINITY;
-      hl = wave_lds ? hl : -INFINITY;
-      const float s0 = (l0 > -INFINITY) ? l0 + g0 : -INFINITY;
-      const float s1 = (l1 > -INFINITY) ? l1 + g1 : -INFINITY;
-      // best of the two register chunks: larger score, the smaller chunk on ties, a NaN log-mass
-      // never wins (it makes the row invalid through the log-mass)
-      const bool t0 = has0 && !(l0 != l0);
-      float bs = t0 ? s0 : -INFINITY;
-      int bc = t0 ? cg0 : -1;
-      const bool t1 = has1 && takes(s1, cg0 + 1, bs, bc);
-      bs = t1 ? s1 : bs;
-      bc = t1 ? cg0 + 1 : bc;
-      WaveRec wr;
-      wr.a = make_float4(lse_add(l0, l1), bs, __int_as_float(bc), hl);
-      wr.t = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), -INFINITY);
+      a4p = a4;
+      l0p = l0;
+      l1p = l1;
+      gmp = gm;
+      invTp = invT;
+      bp = b;
       stage_store(k + 1, sv);
-      store_records(k, false, b, wr);
       __syncthreads();
     }
+    if (bp >= 0) draft_record(n_dsb - 1, bp, l0p, l1p, gmp, tiles_lse<1>(&a4p, invTp));
 
     // CORRECT sub-blocks: residual mass max(0, p - q) of position s - 1 per chunk with its score,
     // and the target row's chunk log-masses (the draw falls back to p when no residual is left)
