@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12        # MI355X HBM3E, bytes/s
+MFMA_PEAK = 2.5e15       # MI355X dense bf16 matrix peak, flop/s
 METRIC = "verified draft tokens/sec per MI355X + % HBM roofline (B=256,K=16,V=151936)"
 
 
@@ -49,13 +50,19 @@ def compulsory_bytes(cfg, L, a):
     return (e * V * (sL + sa1) + e * R * V + e * R * sL + 4 * B * K + 12 * B + 4 * B * (K + 1))
 
 
+def bias_flops(cfg, L, a):
+    """Flops of the Markov-bias contraction the cycle must do: one [R] x [R, V] product per draft
+    row of a verified position and per correction row (a request rejected before its last
+    position)."""
+    rows = int(L.sum()) + int((a < L).sum())
+    return 2 * cfg.R * cfg.V * rows
+
+
 def measured_traffic(kernel, workload, noise):
     """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE / WRITE_SIZE record committed
     under profiles/, scaled by a plain copy's readings; None unless the record was taken on the
     current kernel source and on this workload."""
-    import hashlib
     import re
-    src = os.path.join(ROOT, "draft_sampling_lossless_spec_amd", "csrc", "spec_cycle.hip")
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if noise != "chunked" or not os.path.exists(path):
         return None
@@ -63,9 +70,22 @@ def measured_traffic(kernel, workload, noise):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def kernel_source_hash(kernel):
+    """SHA-256 over the sources a kernel is built from (a traffic record holds only while they are
+    unchanged)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "draft_sampling_lossless_spec_amd", "csrc")
+    files = (["cycle_resident.hip", "resident.h", "device_common.h"] if kernel == "k_resident"
+             else ["spec_cycle.hip"])
+    h = hashlib.sha256()
+    for fn in files:
+        h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
 
 
 def cpu_model() -> str:
@@ -228,8 +248,9 @@ def kernel_breakdown(cfg, L, a, d, nk):
     if nk == 1:
         # one persistent launch runs the whole cycle
         cb = compulsory_bytes(cfg, L, a)
-        return {"k_cycle": {"us_per_cycle": float(mean[0]), "algorithmic_bytes": cb, "launches_per_cycle": 1,
-                            "achieved_GBps": cb / (mean[0] * 1e-6) / 1e9}}
+        return {"k_resident": {"us_per_cycle": float(mean[0]), "algorithmic_bytes": cb, "launches_per_cycle": 1,
+                               "achieved_GBps": cb / (mean[0] * 1e-6) / 1e9,
+                               "bias_flops": bias_flops(cfg, L, a)}}
     K = cfg.K
     steps = np.arange(K + 1)
     kb, kp, km = mean[1 + 3 * steps], mean[2 + 3 * steps], mean[3 + 3 * steps]
@@ -373,16 +394,37 @@ def main():
         "cycle_us": {k: res[k] for k in ("us_per_cycle", "p10_us", "p50_us", "p90_us", "flushed_p10_us",
                                         "flushed_p50_us", "flushed_p90_us")},
         "flushed_value": res["flushed_value"], "flushed_hbm_frac_cycle": res["flushed_hbm_frac_cycle"],
-        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom, "launches_per_cycle": nl,
-                     "traffic_unit": "HBM bytes per launch",
-                     "algorithmic_bytes_per_launch": kern[dom]["algorithmic_bytes"] / nl},
+        "roofline": roofline_obj(kern, dom, nl, achieved, traffic),
         "kernels": res["kernels"],
         "parity": res.get("parity"),
         "cpu_baseline": cpu,
         "configs": configs,
     }
     print(json.dumps(line), flush=True)
+
+
+def roofline_obj(kern, dom, nl, achieved, traffic):
+    """The dominant kernel against its roofline.  For the one-launch cycle both floors are given: the
+    HBM floor of its algorithmic bytes and the MFMA floor of its bias contraction; `bound` names the
+    larger one."""
+    k = kern[dom]
+    r = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+         "frac": achieved / HBM_PEAK, "traffic": traffic, "kernel": dom, "launches_per_cycle": nl,
+         "traffic_unit": "HBM bytes per launch", "algorithmic_bytes_per_launch": k["algorithmic_bytes"] / nl}
+    if "bias_flops" in k:
+        t = k["us_per_cycle"] * 1e-6
+        hbm_floor, mfma_floor = k["algorithmic_bytes"] / HBM_PEAK, k["bias_flops"] / MFMA_PEAK
+        r["floors_us"] = {"hbm": hbm_floor * 1e6, "mfma": mfma_floor * 1e6}
+        mf = {"achieved": k["bias_flops"] / t / 1e12, "peak": MFMA_PEAK / 1e12, "unit": "TFLOP/s",
+              "frac": k["bias_flops"] / t / MFMA_PEAK, "flops_per_launch": k["bias_flops"]}
+        if mfma_floor > hbm_floor:
+            # the contraction's floor is the higher one: the primary fields are the MFMA figures
+            r["hbm"] = {kk: r[kk] for kk in ("achieved", "peak", "unit", "frac")}
+            r.update({kk: mf[kk] for kk in ("achieved", "peak", "unit", "frac")})
+            r["bound"] = "mfma"
+        else:
+            r["mfma"] = mf
+    return r
 
 
 def bench_decode(args):
