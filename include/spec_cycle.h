@@ -67,9 +67,11 @@ enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
  *                       launched cooperatively so that all are resident together): every workgroup
  *                       keeps its slice of W in registers and LDS for all positions, so W crosses
  *                       HBM once per cycle, and the positions are separated by grid barriers
- *                       instead of kernel boundaries.  Needs bf16 rows, chunked noise, V % 8 == 0,
- *                       16-byte aligned logits, B <= 4 x compute units and at most 640 vocabulary
- *                       columns per compute unit (V <= 163840 on a 256-CU gfx950).  A grid barrier
+ *                       instead of kernel boundaries.  Needs bf16 rows, chunked noise, whole
+ *                       64-column chunks (V % 64 == 0), 16-byte aligned logits, B <= 4 x compute
+ *                       units, at most 640 vocabulary columns per compute unit (V <= 163840 on a
+ *                       256-CU gfx950), logit tensors below 4 GiB (B (K + 1) V 2 bytes) and A below
+ *                       2 GiB (V R 2 bytes): its loads use 32-bit byte offsets.  A grid barrier
  *                       that does not complete within about a second (only if the device cannot
  *                       keep the grid resident) marks every request invalid instead of hanging.
  *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies and B <= 2 x compute
