@@ -3,9 +3,12 @@
 Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import this package.  The product path (the HIP library and its binding) never touches it.
 
-This module is a thin ctypes loader around ``liboracle.so`` (built from ``spec_oracle.c`` by
-``oracle/build.py``): argument marshalling from numpy arrays, nothing else.  Every arithmetic
-step lives in the C file, which cites the passages of the DSpark pages it follows.
+This module is a ctypes loader around ``liboracle.so`` (built from ``spec_oracle.c`` by
+``oracle/build.py``): argument marshalling from numpy arrays.  Every arithmetic step of the cycle
+and of the statistics lives in the C file, which cites the passages of the DSpark pages it
+follows.  Three small pieces are Python here: ``temperature_grid`` (the candidate temperatures,
+powers of two on an even grid), ``advance_ref`` (the next cycle's context: the last token a
+request emitted) and ``decode_ref`` (the loop that chains oracle cycles with them).
 """
 from __future__ import annotations
 
