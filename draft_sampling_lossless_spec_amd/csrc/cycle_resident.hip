@@ -163,6 +163,11 @@ __device__ __forceinline__ bool takes(float s2, int i2, float s1, int i1) {
 // rows of each 32-lane half (lane ^ 16), a permlane swap across the halves (lane ^ 32).
 __device__ __forceinline__ int xor16i(int x) { return __builtin_amdgcn_ds_swizzle(x, 0x401F); }
 __device__ __forceinline__ float xor16f(float x) { return __int_as_float(xor16i(__float_as_int(x))); }
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950).  Unlike fmaxf it needs no quieting of
+// operands the compiler cannot prove canonical (accumulators, unpacked bf16), which would cost one
+// more instruction per operand; where the maxima below are taken, a NaN in the values makes the
+// result NaN either way (it reaches the sum of exponentials).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 // A value and its partner lane's (lane ^ 32) from one v_permlane32_swap: .x holds the value of the
 // lower lane of the pair, .y that of the upper, in both lanes (so reductions need no select).
 __device__ __forceinline__ float2 pair32(float x) {
@@ -172,7 +177,7 @@ __device__ __forceinline__ float2 pair32(float x) {
 }
 __device__ __forceinline__ float pmax32(float x) {
   const float2 r = pair32(x);
-  return fmaxf(r.x, r.y);
+  return vmax(r.x, r.y);
 }
 __device__ __forceinline__ float psum32(float x) {
   const float2 r = pair32(x);
@@ -186,9 +191,11 @@ __device__ __forceinline__ int dppi(int x) {
 // wave-wide reductions (every lane gets the result): xor 1, xor 2, half-row mirror, row mirror,
 // then xor 16 and xor 32
 __device__ __forceinline__ float wmax(float x) {
-  x = max8(x);
-  x = fmaxf(x, dpp<0x140>(x));
-  x = fmaxf(x, xor16f(x));
+  x = vmax(x, dpp<0xB1>(x));
+  x = vmax(x, dpp<0x4E>(x));
+  x = vmax(x, dpp<0x141>(x));
+  x = vmax(x, dpp<0x140>(x));
+  x = vmax(x, xor16f(x));
   return pmax32(x);
 }
 __device__ __forceinline__ float wsum(float x) {
@@ -227,10 +234,10 @@ __device__ __forceinline__ float pair_lse(const float* y, float invT) {
   float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
   for (int i = 0; i < N; i += 2) {
-    m0 = fmaxf(m0, y[i]);
-    m1 = fmaxf(m1, y[i + 1]);
+    m0 = vmax(m0, y[i]);
+    m1 = vmax(m1, y[i + 1]);
   }
-  float mx = fmaxf(m0, m1);
+  float mx = vmax(m0, m1);
   mx = pmax32(mx);
   const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
@@ -255,10 +262,10 @@ __device__ __forceinline__ float tiles_lse(const f32x16* a, float invT) {
   for (int t = 0; t < NTL; t++)
 #pragma unroll
     for (int q = 0; q < 16; q += 2) {
-      m0 = fmaxf(m0, a[t][q]);
-      m1 = fmaxf(m1, a[t][q + 1]);
+      m0 = vmax(m0, a[t][q]);
+      m1 = vmax(m1, a[t][q + 1]);
     }
-  float mx = fmaxf(m0, m1);
+  float mx = vmax(m0, m1);
   mx = pmax32(mx);
   const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
@@ -282,10 +289,10 @@ __device__ __forceinline__ float lse_two(const f32x16& x, const f32x16& y, float
   float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
   for (int q = 0; q < 16; q += 2) {
-    m0 = fmaxf(m0, fmaxf(x[q], y[q]));
-    m1 = fmaxf(m1, fmaxf(x[q + 1], y[q + 1]));
+    m0 = vmax(m0, vmax(x[q], y[q]));
+    m1 = vmax(m1, vmax(x[q + 1], y[q + 1]));
   }
-  const float mx = pmax32(fmaxf(m0, m1));
+  const float mx = pmax32(vmax(m0, m1));
   const float c = invT * LOG2E, mo = (mx == -INFINITY) ? 0.0f : mx * c;
   float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
 #pragma unroll
@@ -339,11 +346,11 @@ __device__ __forceinline__ void lse2_step(Lse2& st, int t, const f32x16& x, cons
   if (t < 4) {
 #pragma unroll
     for (int q = 4 * t; q < 4 * t + 4; q += 2) {
-      st.m0 = fmaxf(st.m0, fmaxf(x[q], y[q]));
-      st.m1 = fmaxf(st.m1, fmaxf(x[q + 1], y[q + 1]));
+      st.m0 = vmax(st.m0, vmax(x[q], y[q]));
+      st.m1 = vmax(st.m1, vmax(x[q + 1], y[q + 1]));
     }
   } else if (t == 4) {
-    st.m0 = pmax32(fmaxf(st.m0, st.m1));
+    st.m0 = pmax32(vmax(st.m0, st.m1));
     st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
   } else if (t < 13) {
     const int q = 2 * (t - 5);
@@ -378,11 +385,11 @@ __device__ __forceinline__ void lse1_step(Lse2& st, int t, const f32x16& x, floa
   if (t < 2) {
 #pragma unroll
     for (int q = 8 * t; q < 8 * t + 8; q += 2) {
-      st.m0 = fmaxf(st.m0, x[q]);
-      st.m1 = fmaxf(st.m1, x[q + 1]);
+      st.m0 = vmax(st.m0, x[q]);
+      st.m1 = vmax(st.m1, x[q + 1]);
     }
     if (t == 1) {
-      st.m0 = pmax32(fmaxf(st.m0, st.m1));
+      st.m0 = pmax32(vmax(st.m0, st.m1));
       st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
     }
   } else if (t < 6) {
@@ -516,11 +523,14 @@ __device__ __forceinline__ void corr_step(Corr2& st, int i0, const f32x16& x, co
   for (int i = i0; i < i0 + 2; i++) {
     const float ep = ex2(fmaf(tgt4(t0, t1, t2, t3, i), c, op));
     const float eq = ex2(fmaf(acc2(x, y, i), c, oq));
+    // max(p - q, 0) as the subtraction's result clamped to [0, 1] (p and q lie in [0, 1]; a NaN
+    // clamps to 0, as the maximum with 0 would give)
+    const float r = __builtin_amdgcn_fmed3f(ep - eq, 0.0f, 1.0f);
     if (i & 1) {
-      st.r1 += fmaxf(ep - eq, 0.0f);
+      st.r1 += r;
       st.p1 += ep;
     } else {
-      st.r0 += fmaxf(ep - eq, 0.0f);
+      st.r0 += r;
       st.p0 += ep;
     }
   }
@@ -1926,7 +1936,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
             for (int i = 0; i < TP / 512; i++) {
               const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
 #pragma unroll
-              for (int e = 0; e < 4; e++) mx = fmaxf(mx, fmaxf(bf_lo(w[e]), bf_hi(w[e])));
+              for (int e = 0; e < 4; e++) mx = vmax(mx, vmax(bf_lo(w[e]), bf_hi(w[e])));
             }
             mx = wmax(mx);
             const float mo = (mx == -INFINITY) ? 0.0f : mx * c;
@@ -1954,8 +1964,10 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
               const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
               float mx = -INFINITY;
 #pragma unroll
-              for (int e = 0; e < 4; e++) mx = fmaxf(mx, fmaxf(bf_lo(w[e]), bf_hi(w[e])));
-              mx = max8(mx);
+              for (int e = 0; e < 4; e++) mx = vmax(mx, vmax(bf_lo(w[e]), bf_hi(w[e])));
+              mx = vmax(mx, dpp<0xB1>(mx));   // over the 8 lanes of the chunk
+              mx = vmax(mx, dpp<0x4E>(mx));
+              mx = vmax(mx, dpp<0x141>(mx));
               const float mo = (mx == -INFINITY) ? 0.0f : mx * c;
               float sm = 0.0f;
 #pragma unroll
