@@ -1482,13 +1482,15 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     // w + 8, w + 12 that lie below the rank (the rest hold zeros, written at the step's start).  A
     // slot without a previous token reads past the end of A, i.e. zeros.
     const int nks = p.a.R >> 4;
-    auto stage_issue = [&](int k, u32x4 (&v)[4]) {
+    auto stage_issue_ent = [&](uint32_t ent, u32x4 (&v)[4]) {
       const __amdgpu_buffer_rsrc_t rsA = ld_rsrc(p.a.A, (uint32_t)V * (uint32_t)p.a.R * 2u);
-      const uint32_t ent = (k < ls.n_sb) ? S.blist[k * SUB + m32] : NO_ENT;
       const int prev = ent == NO_ENT ? -1 : ent_prev(ent);
       const uint32_t vo = prev >= 0 ? 2u * (uint32_t)(prev * p.a.R + h * (p.a.R >> 1) + 8 * wave) : OOB_OFF;
 #pragma unroll
       for (int i = 0; i < 4; i++) v[i] = ldb16(rsA, vo + 64u * i, 0u);
+    };
+    auto stage_issue = [&](int k, u32x4 (&v)[4]) {
+      stage_issue_ent((k < ls.n_sb) ? S.blist[k * SUB + m32] : NO_ENT, v);
     };
     auto stage_store = [&](int k, const u32x4 (&v)[4]) {
 #pragma unroll
@@ -1621,23 +1623,37 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     f32x16 a4p = {};                     // the previous sub-block's LDS-tile accumulators
     float l0p = 0.0f, l1p = 0.0f, gmp = 0.0f, invTp = 1.0f;
     int bp = -1;                         // its row (-1: none, or no previous sub-block)
+    // the row of the lane's slot in the next sub-block, with its temperature and noise key (read
+    // one sub-block ahead, so that no sub-block waits on its own)
+    int bn, jn;
+    {
+      bool cn;
+      row_of(0, bn, jn, cn);
+    }
+    float invTn = S.req[bn >= 0 ? bn : 0].invT;
+    uint32_t kn0 = S.req[bn >= 0 ? bn : 0].key_d[0], kn1 = S.req[bn >= 0 ? bn : 0].key_d[1];
     for (int k = 0; k < n_dsb; k++) {
       tid = opaque_tid();
-      int b, j;
-      bool corr;
-      row_of(k, b, j, corr);
-      const ReqMeta rm = S.req[b >= 0 ? b : 0];
-      const float invT = b >= 0 ? rm.invT : 1.0f;
-      const uint64_t key = key_of(rm.key_d);
+      const int b = bn, j = jn;
+      const float invT = b >= 0 ? invTn : 1.0f;
+      const uint64_t key = (uint64_t)kn0 | ((uint64_t)kn1 << 32);
       const bf16x8* sAk = S.sA + (size_t)(k & 1) * KSTEPS * 64;
       // in flight during this sub-block: the next sub-block's B operands, and its draft logits,
       // each tile loaded into the registers its predecessor leaves when it seeds its pass
+      const uint32_t ent2 = (k + 1 < ls.n_sb) ? S.blist[(k + 1) * SUB + m32] : NO_ENT;
       u32x4 sv[4];
-      stage_issue(k + 1, sv);
-      int b2 = -1, j2 = 0;
-      bool c2 = false;
-      if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
+      stage_issue_ent(ent2, sv);
+      const int b2 = ent2 == NO_ENT ? -1 : ent_req(ent2);
+      const int j2 = (ent2 != NO_ENT && (ent2 & 1u)) ? s - 1 : s;
       const uint32_t vo2 = row_off(b2, j2, K);
+      {
+        const ReqMeta& rq = S.req[b2 >= 0 ? b2 : 0];
+        invTn = rq.invT;
+        kn0 = rq.key_d[0];
+        kn1 = rq.key_d[1];
+      }
+      bn = b2;
+      jn = j2;
       f32x16 a0 = seed_acc(Tc[0], 0), a1 = seed_acc(Tc[1], 1);
       load_tile(rs_base, vo2, 0, Tc[0]);
       load_tile(rs_base, vo2, 1, Tc[1]);
