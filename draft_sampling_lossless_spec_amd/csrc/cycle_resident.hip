@@ -1377,10 +1377,6 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
 #define m32 (tid & 31)
 #define h ((tid >> 5) & 1)
     // ---- 1. roles of step s -> lists and the per-request table ----
-    if (s > 0) {
-      for (int b = tid; b < B; b += NT) S.role[b] = (uint8_t)ld_i32(&p.st[(ST_ROLES + (s & 1)) * B + b]);
-      __syncthreads();
-    }
     Lists ls;
     {
       // requests in rounds of NT (request i NT + tid in round i); within a round every wave counts
@@ -1391,7 +1387,22 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       const int rounds = (B + NT - 1) / NT;
       for (int i = 0; i < rounds; i++) {
         const int b = i * NT + tid;
-        const int r = b < B ? S.role[b] : 0;
+        // the request's role and every input of its table row in one round trip (the inputs are
+        // loaded whatever the role; a request without one does not use them)
+        int r = 0, x0 = -1, xd = -1, xc = -1;
+        float T = 1.0f, lpc = 0.0f, lqc = 0.0f;
+        const int jc = s > 0 ? s - 1 : 0;
+        if (b < B) {
+          r = s > 0 ? ld_i32(&p.st[(ST_ROLES + (s & 1)) * B + b]) : S.role[b];
+          x0 = p.a.x0 ? p.a.x0[b] : -1;
+          const int32_t* xr = p.xs + (size_t)b * K;
+          xd = s >= 1 ? ld_i32(&xr[s - 1]) : x0;
+          xc = s >= 2 ? ld_i32(&xr[s - 2]) : x0;
+          T = p.a.temp[b];
+          lpc = ld_f32(&p.lse_p[(size_t)b * (K + 1) + jc]);
+          lqc = ld_f32(&p.lse_q[(size_t)b * K + jc]);
+          if (s > 0) S.role[b] = (uint8_t)r;
+        }
         const uint64_t md = __ballot((r & RO_DRAFT) != 0), mc = __ballot((r & RO_CORRECT) != 0),
                        mp = __ballot((r & (RO_LSEP | RO_BONUS)) != 0);
         auto below = [&](uint64_t m) {   // set bits of m in lanes below this one
@@ -1424,15 +1435,12 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           S.slot[B + b] = sc;
           S.slot[2 * B + b] = sp;
           if (r) {
-            const int x0 = p.a.x0 ? p.a.x0[b] : -1;
-            const int32_t* xr = p.xs + (size_t)b * K;
             ReqMeta m;
-            m.prev_d = (s == 0) ? x0 : ld_i32(&xr[s - 1]);
-            m.prev_c = (s <= 1) ? x0 : ld_i32(&xr[s - 2]);
-            m.invT = 1.0f / p.a.temp[b];
-            const int jc = s > 0 ? s - 1 : 0;
-            m.lse_p_c = ld_f32(&p.lse_p[(size_t)b * (K + 1) + jc]);
-            m.lse_q_c = ld_f32(&p.lse_q[(size_t)b * K + jc]);
+            m.prev_d = xd;
+            m.prev_c = xc;
+            m.invT = 1.0f / T;
+            m.lse_p_c = lpc;
+            m.lse_q_c = lqc;
             const uint64_t kr = req_key(seed, p.a.req_off + b);
             put_key(m.key_d, pos_key(kr, s, ST_DRAFT_C));
             put_key(m.key_c, pos_key(kr, jc, ST_RESIDUAL_C));
