@@ -877,7 +877,9 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
   // every load of the round is issued before any of them is waited for: the A rows (staged in
   // LDS below), the W rows, the draft and target logits of the 64 candidate columns
   const int qa = (tid >> 6) & 1, la = tid & 63;
-  const bool lda = tid < 128 && jb[qa].kind != L2_NONE && jb[qa].kind != L2_TARGET && jb[qa].prev >= 0 && 4 * la < R;
+  // (the job is picked by select, not by a run-time index: that would put the jobs in scratch memory)
+  auto needs_a = [&](const Job& j) { return j.kind != L2_NONE && j.kind != L2_TARGET && j.prev >= 0; };
+  const bool lda = tid < 128 && (qa == 0 ? needs_a(jb[0]) : needs_a(jb[1])) && 4 * la < R;
   const int col = 16 * wave + (lane >> 2), kq = lane & 3;
   int v[2];
   bool in[2], need_base[2], need_targ[2], wld[2][8];
@@ -1126,8 +1128,12 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     key_l2b = pos_key(kreq, s, ST_BONUS);
     key_acc = pos_key(kreq, s, ST_ACCEPT);
     __builtin_amdgcn_sched_barrier(0);   // the loads are in flight before any is used
-    ml->part[0][tid] = (hasD && tid < G) ? wg_draft(ad, cb, nl, key_d) : none;
-    ml->part[3][tid] = (hasP && tid < nrP) ? ap : none;
+    // (component-wise selects: a select of whole structs goes through scratch memory)
+    auto sel4 = [](bool c, float4 a, float4 b) {
+      return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+    };
+    ml->part[0][tid] = sel4(hasD && tid < G, wg_draft(ad, cb, nl, key_d), none);
+    ml->part[3][tid] = sel4(hasP && tid < nrP, ap, none);
     if (hasC) {
       float4 rd = none, rt = none;
       if (tid < G) wg_correct(ac, at, cb, nl, key_c, rd, rt);
