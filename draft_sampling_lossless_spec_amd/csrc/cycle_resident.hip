@@ -336,84 +336,132 @@ __device__ __forceinline__ void interleave() {
 // exponential sums in steps 5..12 (4 values each), the result in step 13.  -inf everywhere gives
 // -inf, a NaN gives NaN.
 struct Lse2 {
-  float m0, m1, mo, s0, s1, s2, s3, r;
+  float m0, m1, m2, m3, mo;   // running maxima, then the maximum (m0) and its scaled value
+  float f0, f1, f2, f3;       // scaled exponents of the group in flight
+  float e0, e1, e2, e3;       // their exponentials
+  float s0, s1, s2, s3;       // running sums
+  float r;                    // the result
 };
 __device__ __forceinline__ void lse2_init(Lse2& st) {
-  st.m0 = st.m1 = -INFINITY;
-  st.mo = st.s0 = st.s1 = st.s2 = st.s3 = st.r = 0.0f;
+  st.m0 = st.m1 = st.m2 = st.m3 = -INFINITY;
+  st.mo = st.f0 = st.f1 = st.f2 = st.f3 = st.e0 = st.e1 = st.e2 = st.e3 = 0.0f;
+  st.s0 = st.s1 = st.s2 = st.s3 = st.r = 0.0f;
 }
+// Software-pipelined exponential sums: in one slice the scaled exponents of group g, the
+// exponentials of group g - 1 and the additions of group g - 2, so that no instruction of a slice
+// waits on another of the same slice (one wave per SIMD has no other wave to hide that latency).
+// v(g, i): value i (0..3) of group g.
+template <class VF>
+__device__ __forceinline__ void lse_pipe(Lse2& st, int g, int ng, VF v, float c) {
+  if (g >= 2 && g - 2 < ng) {
+    st.s0 += st.e0;
+    st.s1 += st.e1;
+    st.s2 += st.e2;
+    st.s3 += st.e3;
+  }
+  if (g >= 1 && g - 1 < ng) {
+    st.e0 = ex2(st.f0);
+    st.e1 = ex2(st.f1);
+    st.e2 = ex2(st.f2);
+    st.e3 = ex2(st.f3);
+  }
+  if (g < ng) {
+    st.f0 = fmaf(v(g, 0), c, -st.mo);
+    st.f1 = fmaf(v(g, 1), c, -st.mo);
+    st.f2 = fmaf(v(g, 2), c, -st.mo);
+    st.f3 = fmaf(v(g, 3), c, -st.mo);
+  }
+}
+__device__ __forceinline__ void lse_pipe_fence(Lse2& st, int g, int ng) {
+  if (g >= 2 && g - 2 < ng) {
+    vfence(st.s0);
+    vfence(st.s1);
+    vfence(st.s2);
+    vfence(st.s3);
+  }
+  if (g >= 1 && g - 1 < ng) {
+    vfence(st.e0);
+    vfence(st.e1);
+    vfence(st.e2);
+    vfence(st.e3);
+  }
+  if (g < ng) {
+    vfence(st.f0);
+    vfence(st.f1);
+    vfence(st.f2);
+    vfence(st.f3);
+  }
+}
+__device__ __forceinline__ void lse_fold_max(Lse2& st, float c) {
+  st.m0 = pmax32(vmax(vmax(st.m0, st.m1), vmax(st.m2, st.m3)));
+  st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
+}
+__device__ __forceinline__ void lse_result(Lse2& st, float invT) {
+  const float sum = psum32((st.s0 + st.s1) + (st.s2 + st.s3));
+  st.r = (st.m0 == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : st.m0 * invT + lg2(sum) * LN2;
+}
+
+// Log-sum-exp of invT * x over the 32 values of two accumulator tiles (x, y) of a lane and its
+// partner lane, in 16 slices: the maximum in slices 0..3 (8 values each, four chains), the
+// exchange with the partner in slice 4, the pipelined exponential sums (eight groups of four) in
+// slices 5..14, the result in slice 15.  -inf everywhere gives -inf, a NaN gives NaN.
 __device__ __forceinline__ void lse2_step(Lse2& st, int t, const f32x16& x, const f32x16& y, float c, float invT) {
   if (t < 4) {
-#pragma unroll
-    for (int q = 4 * t; q < 4 * t + 4; q += 2) {
-      st.m0 = vmax(st.m0, vmax(x[q], y[q]));
-      st.m1 = vmax(st.m1, vmax(x[q + 1], y[q + 1]));
-    }
+    const int q = 4 * t;
+    st.m0 = vmax(st.m0, vmax(x[q], y[q]));
+    st.m1 = vmax(st.m1, vmax(x[q + 1], y[q + 1]));
+    st.m2 = vmax(st.m2, vmax(x[q + 2], y[q + 2]));
+    st.m3 = vmax(st.m3, vmax(x[q + 3], y[q + 3]));
   } else if (t == 4) {
-    st.m0 = pmax32(vmax(st.m0, st.m1));
-    st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
-  } else if (t < 13) {
-    const int q = 2 * (t - 5);
-    st.s0 += ex2(fmaf(x[q], c, -st.mo));
-    st.s1 += ex2(fmaf(x[q + 1], c, -st.mo));
-    st.s2 += ex2(fmaf(y[q], c, -st.mo));
-    st.s3 += ex2(fmaf(y[q + 1], c, -st.mo));
-  } else if (t == 13) {
-    const float sum = psum32((st.s0 + st.s1) + (st.s2 + st.s3));
-    st.r = (st.m0 == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : st.m0 * invT + lg2(sum) * LN2;
+    lse_fold_max(st, c);
+  } else if (t < 15) {
+    lse_pipe(st, t - 5, 8, [&](int g, int i) { return (i < 2) ? x[2 * g + i] : y[2 * g + i - 2]; }, c);
+  } else {
+    lse_result(st, invT);
   }
 }
 __device__ __forceinline__ void lse2_fence(Lse2& st, int t) {
   if (t < 4) {
     vfence(st.m0);
     vfence(st.m1);
+    vfence(st.m2);
+    vfence(st.m3);
   } else if (t == 4) {
     vfence(st.m0);
     vfence(st.mo);
-  } else if (t < 13) {
-    vfence(st.s0);
-    vfence(st.s1);
-    vfence(st.s2);
-    vfence(st.s3);
-  } else if (t == 13) {
+  } else if (t < 15) {
+    lse_pipe_fence(st, t - 5, 8);
+  } else {
     vfence(st.r);
   }
 }
 
-// The same for the 16 values of one tile (steps 0..6; the result in step 6).
+// The same for the 16 values of one tile, in 9 slices: the maximum in slices 0 and 1 (and the
+// exchange in 1), the exponential sums (four groups) in slices 2..7, the result in slice 8.
 __device__ __forceinline__ void lse1_step(Lse2& st, int t, const f32x16& x, float c, float invT) {
   if (t < 2) {
-#pragma unroll
-    for (int q = 8 * t; q < 8 * t + 8; q += 2) {
-      st.m0 = vmax(st.m0, x[q]);
-      st.m1 = vmax(st.m1, x[q + 1]);
-    }
-    if (t == 1) {
-      st.m0 = pmax32(vmax(st.m0, st.m1));
-      st.mo = (st.m0 == -INFINITY) ? 0.0f : st.m0 * c;
-    }
-  } else if (t < 6) {
-    const int q = 4 * (t - 2);
-    st.s0 += ex2(fmaf(x[q], c, -st.mo));
-    st.s1 += ex2(fmaf(x[q + 1], c, -st.mo));
-    st.s2 += ex2(fmaf(x[q + 2], c, -st.mo));
-    st.s3 += ex2(fmaf(x[q + 3], c, -st.mo));
-  } else if (t == 6) {
-    const float sum = psum32((st.s0 + st.s1) + (st.s2 + st.s3));
-    st.r = (st.m0 == -INFINITY) ? (sum == 0.0f ? -INFINITY : NAN) : st.m0 * invT + lg2(sum) * LN2;
+    const int q = 8 * t;
+    st.m0 = vmax(st.m0, vmax(x[q], x[q + 4]));
+    st.m1 = vmax(st.m1, vmax(x[q + 1], x[q + 5]));
+    st.m2 = vmax(st.m2, vmax(x[q + 2], x[q + 6]));
+    st.m3 = vmax(st.m3, vmax(x[q + 3], x[q + 7]));
+    if (t == 1) lse_fold_max(st, c);
+  } else if (t < 8) {
+    lse_pipe(st, t - 2, 4, [&](int g, int i) { return x[4 * g + i]; }, c);
+  } else if (t == 8) {
+    lse_result(st, invT);
   }
 }
 __device__ __forceinline__ void lse1_fence(Lse2& st, int t) {
   if (t < 2) {
     vfence(st.m0);
     vfence(st.m1);
+    vfence(st.m2);
+    vfence(st.m3);
     if (t == 1) vfence(st.mo);
-  } else if (t < 6) {
-    vfence(st.s0);
-    vfence(st.s1);
-    vfence(st.s2);
-    vfence(st.s3);
-  } else if (t == 6) {
+  } else if (t < 8) {
+    lse_pipe_fence(st, t - 2, 4);
+  } else if (t == 8) {
     vfence(st.r);
   }
 }
@@ -916,16 +964,17 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
   __syncthreads();   // the A rows are staged
 #pragma unroll
   for (int q = 0; q < 2; q++) {
-    float a = 0.0f;
+    float ac[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent chains: the FMAs pipeline
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const u32x4 ar = *(const u32x4*)&ml->arow[q][64 * kq + 8 * i];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        a = fmaf(bf_lo(ar[e]), bf_lo(wv[q][i][e]), a);
-        a = fmaf(bf_hi(ar[e]), bf_hi(wv[q][i][e]), a);
+        ac[e] = fmaf(bf_lo(ar[e]), bf_lo(wv[q][i][e]), ac[e]);
+        ac[e] = fmaf(bf_hi(ar[e]), bf_hi(wv[q][i][e]), ac[e]);
       }
     }
+    float a = (ac[0] + ac[1]) + (ac[2] + ac[3]);
     a += dpp<0xB1>(a);   // quad sum: xor 1, xor 2
     a += dpp<0x4E>(a);
     bias[q] = a;
@@ -1700,11 +1749,15 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[1][t], bop, a1, 0, 0, 0);
           if (t < 2) { vfence(Tc[2][t]); seed_piece(a2, Tc[2][t], t); }
           else if (t < 4) { vfence(Tc[3][t - 2]); seed_piece(a3, Tc[3][t - 2], t - 2); }
-          else if (t < 8) gumbel_step(gs, t - 4, key, (uint32_t)(cg0 + h));
-          else if (t < 15) lse1_step(stp, t - 8, a4p, invTp * LOG2E, invTp);
-          else draft_record(k - 1, bp, l0p, l1p, gmp, stp.r);   // stores nothing for bp < 0
-          if (t >= 4 && t < 8) gumbel_fence(gs, t - 4);
-          else if (t >= 8 && t < 15) lse1_fence(stp, t - 8);
+          if (t < 4) {
+            gumbel_step(gs, t, key, (uint32_t)(cg0 + h));
+            gumbel_fence(gs, t);
+          } else if (t < 13) {
+            lse1_step(stp, t - 4, a4p, invTp * LOG2E, invTp);
+            lse1_fence(stp, t - 4);
+          } else if (t == 13) {
+            draft_record(k - 1, bp, l0p, l1p, gmp, stp.r);   // stores nothing for bp < 0
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1729,10 +1782,9 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           const bf16x8 bop = bq[t];
           a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[2][t], bop, a2, 0, 0, 0);
           a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[3][t], bop, a3, 0, 0, 0);
-          if (t < 14) {
-            lse2_step(st0, t, a0, a1, lc, invT);
-            lse2_fence(st0, t);
-          } else {
+          lse2_step(st0, t, a0, a1, lc, invT);
+          lse2_fence(st0, t);
+          if (t >= 14) {
             vfence(Tc[4][t - 14]);
             seed_piece(a4, Tc[4][t - 14], t - 14);
           }
@@ -1758,10 +1810,8 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           if (t + 4 < KSTEPS) wq[t + 4] = wlw[(t + 4) * 64 + lane];
           const bf16x8 wl = wq[t];
           a4 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, bop, a4, 0, 0, 0);
-          if (t < 14) {
-            lse2_step(st1, t, a2, a3, lc, invT);
-            lse2_fence(st1, t);
-          }
+          lse2_step(st1, t, a2, a3, lc, invT);
+          lse2_fence(st1, t);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
