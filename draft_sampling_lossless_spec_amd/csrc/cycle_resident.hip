@@ -80,7 +80,6 @@ __device__ __forceinline__ uint32_t ent_make(int b, bool corr, int prev) {
 __device__ __forceinline__ int ent_req(uint32_t e) { return (int)((e >> 1) & 1023u); }
 __device__ __forceinline__ int ent_prev(uint32_t e) { return (int)(e >> 11) - 1; }
 constexpr uint64_t TOKEN_WINDOW = 1ull << 16;
-constexpr int PLAIN_INFLIGHT = 1;   // plain-row items whose loads a wave keeps in flight
 
 constexpr uint64_t WAIT_TICKS = 100000000ull;   // s_memrealtime runs at 100 MHz: one second
 
@@ -1505,9 +1504,10 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         }
         __syncthreads();   // the wave counts are read before the next round writes them
       }
-      ls.n_draft = nd;
-      ls.n_correct = nc;
-      ls.n_plain = np;
+      // the counts are uniform over the workgroup (every wave read the same LDS words)
+      ls.n_draft = __builtin_amdgcn_readfirstlane(nd);
+      ls.n_correct = __builtin_amdgcn_readfirstlane(nc);
+      ls.n_plain = __builtin_amdgcn_readfirstlane(np);
       ls.c0 = (nd + SUB - 1) / SUB * SUB;
       ls.n_sb = (ls.c0 + nc + SUB - 1) / SUB;
       for (int b = tid; b < B; b += NT) {
@@ -1979,105 +1979,123 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     //         items of all plain rows spread over all waves of the grid (target rows need no W,
     //         so they are not tied to a workgroup's vocabulary slice) ----
     {
+      // Wave w takes items w, w + GW, w + 2 GW, ... (GW: all waves of the grid).  Every piece of
+      // an item is used once (LSEP: a running lane maximum with a rescaled sum; BONUS: per-chunk
+      // masses), and the piece of the wave's next item is loaded into its registers right after,
+      // so that one item's loads are in flight during the whole of the previous item's arithmetic.
+      tid = opaque_tid();
       const int nrP = (V + TP - 1) / TP;
       const int n_items = ls.n_plain * nrP;
       const int GW = G * NW;
-      constexpr int NQ = PLAIN_INFLIGHT;
-      for (int it0 = g * NW + wave; it0 < n_items; it0 += NQ * GW) {
-        u32x4 x[NQ][TP / 512];
-        int ps[NQ], rb[NQ], t[NQ], xin[NQ];
+      constexpr int NP = TP / 512;   // 16-byte pieces per lane
+      struct PItem {
+        int ps, t, rb, xin;          // plain slot, item of the row, request (-1: none), pieces inside V
+      };
+      auto item_of = [&](int it) {
+        PItem q;
+        q.ps = it < n_items ? it / nrP : -1;
+        q.t = q.ps >= 0 ? it - q.ps * nrP : 0;
+        q.rb = q.ps >= 0 ? __builtin_amdgcn_readfirstlane((int)S.plist[q.ps]) : -1;
+        q.xin = 0;
 #pragma unroll
-        for (int q = 0; q < NQ; q++) {
-          const int it = it0 + q * GW;
-          ps[q] = it < n_items ? it / nrP : -1;
-          t[q] = it < n_items ? it - ps[q] * nrP : 0;
-          rb[q] = ps[q] >= 0 ? S.plist[ps[q]] : -1;
-          const uint16_t* row = (const uint16_t*)p.a.target + ((size_t)(rb[q] >= 0 ? rb[q] : 0) * (K + 1) + s) * V;
-          xin[q] = 0;
+        for (int i = 0; i < NP; i++) q.xin |= (q.t * TP + (i * 64 + lane) * 8 < V) ? (1 << i) : 0;
+        return q;
+      };
+      // the lane's piece i of item q (a piece past V reads column 0 of the row and is masked; no
+      // item: an offset past the tensor, which reads zeros without a memory access)
+      const uint32_t tgt_bytes = (uint32_t)B * (uint32_t)(K + 1) * Vb;
+      auto load_piece = [&](const PItem& q, int i) -> u32x4 {
+        const int col = ((q.xin >> i) & 1) ? q.t * TP + (i * 64 + lane) * 8 : 0;
+        const uint32_t off = q.rb >= 0 ? (uint32_t)(q.rb * (K + 1) + s) * Vb + 2u * (uint32_t)col : tgt_bytes;
+        return ldb16(rs_tgt, off, 0u);
+      };
+      int it = g * NW + wave;
+      PItem cur = item_of(it);
+      u32x4 x[NP];
+      if (cur.rb >= 0) {   // wave-uniform conditions throughout
 #pragma unroll
-          for (int i = 0; i < TP / 512; i++) {
-            const int col = t[q] * TP + (i * 64 + lane) * 8;
-            const bool in = rb[q] >= 0 && col < V;
-            x[q][i] = ldg16(row + (in ? col : 0));
-            xin[q] |= in ? (1 << i) : 0;
-          }
-        }
+        for (int i = 0; i < NP; i++) x[i] = load_piece(cur, i);
+      }
+      while (cur.rb >= 0) {
+        const PItem nxt = item_of(it + GW);
+        const int rr = __builtin_amdgcn_readfirstlane((int)S.role[cur.rb]);
+        const float invT = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, S.req[cur.rb].invT)));
+        const float c = invT * LOG2E;
+        float4 rec;
+        if (rr & RO_LSEP) {
+          // the item's log-mass: per lane a running maximum m and the sum of exp(c (v - m)),
+          // rescaled whenever m grows; then the wave maximum and the rescaled lane sums
+          float m = -INFINITY, s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-        for (int q = 0; q < NQ; q++) {
-          if (rb[q] < 0) continue;   // wave-uniform
-          const int rr = S.role[rb[q]];
-          const float invT = S.req[rb[q]].invT;
-          const float c = invT * LOG2E;
-          float4 rec;
-          if (rr & RO_LSEP) {
-            // the item's log-mass in one pass: lane maximum, wave maximum, one scaled sum
-            float mx = -INFINITY;
+          for (int i = 0; i < NP; i++) {
+            const u32x4 w = ((cur.xin >> i) & 1) ? x[i] : kNegInf;
+            x[i] = load_piece(nxt, i);   // unconditional, so that every wait counts the same loads
+            float pm = vmax(bf_lo(w[0]), bf_hi(w[0]));
 #pragma unroll
-            for (int i = 0; i < TP / 512; i++) {
-              const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
+            for (int e = 1; e < 4; e++) pm = vmax(pm, vmax(bf_lo(w[e]), bf_hi(w[e])));
+            const float mn = vmax(m, pm);
+            const float mo = (mn == -INFINITY) ? 0.0f : mn * c;
+            const float sc = (m == -INFINITY) ? 0.0f : ex2(fmaf(m, c, -mo));
+            float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-              for (int e = 0; e < 4; e++) mx = vmax(mx, vmax(bf_lo(w[e]), bf_hi(w[e])));
+            for (int e = 0; e < 4; e++) {
+              a0 += ex2(fmaf(bf_lo(w[e]), c, -mo));
+              a1 += ex2(fmaf(bf_hi(w[e]), c, -mo));
             }
-            mx = wmax(mx);
+            s0 = fmaf(s0, sc, a0);
+            s1 = fmaf(s1, sc, a1);
+            m = mn;
+          }
+          const float mx = wmax(m);
+          const float Mo = (mx == -INFINITY) ? 0.0f : mx * c;
+          const float sm = wsum(m == -INFINITY ? 0.0f : (s0 + s1) * ex2(fmaf(m, c, -Mo)));
+          const float lse = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
+          rec = make_float4(lse, -INFINITY, __int_as_float(-1), 0.0f);
+        } else {
+          // BONUS: the log-mass of each 64-column chunk (8 lanes per chunk in every piece, all
+          // eight holding it after the group reductions); then lane l takes chunk
+          // 8 (l mod 8) + l / 8 of the item, i.e. piece l mod 8 of its lane group, for the
+          // item's log-mass, the chunk's Gumbel score and the best chunk
+          float lcs[NP];
+#pragma unroll
+          for (int i = 0; i < NP; i++) {
+            const u32x4 w = ((cur.xin >> i) & 1) ? x[i] : kNegInf;
+            x[i] = load_piece(nxt, i);   // unconditional, so that every wait counts the same loads
+            float mx = vmax(bf_lo(w[0]), bf_hi(w[0]));
+#pragma unroll
+            for (int e = 1; e < 4; e++) mx = vmax(mx, vmax(bf_lo(w[e]), bf_hi(w[e])));
+            mx = vmax(mx, dpp<0xB1>(mx));   // over the 8 lanes of the chunk
+            mx = vmax(mx, dpp<0x4E>(mx));
+            mx = vmax(mx, dpp<0x141>(mx));
             const float mo = (mx == -INFINITY) ? 0.0f : mx * c;
-            float s0 = 0.0f, s1 = 0.0f;
+            float sm = 0.0f;
 #pragma unroll
-            for (int i = 0; i < TP / 512; i++) {
-              const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
-#pragma unroll
-              for (int e = 0; e < 4; e++) {
-                s0 += ex2(fmaf(bf_lo(w[e]), c, -mo));
-                s1 += ex2(fmaf(bf_hi(w[e]), c, -mo));
-              }
-            }
-            const float sm = wsum(s0 + s1);
-            const float lse = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
-            rec = make_float4(lse, -INFINITY, __int_as_float(-1), 0.0f);
-          } else {
-            // BONUS: the log-mass of each 64-column chunk (8 lanes per chunk in every load), its
-            // Gumbel score, the best chunk, and the item's log-mass from the chunks'
-            const uint64_t key = pos_key(req_key(seed, p.a.req_off + rb[q]), s, ST_BONUS_C);
-            float lse_tot = -INFINITY, bs = -INFINITY, dummy = 0.0f;
-            int bc = -1;
-#pragma unroll
-            for (int i = 0; i < TP / 512; i++) {
-              const u32x4 w = ((xin[q] >> i) & 1) ? x[q][i] : kNegInf;
-              float mx = -INFINITY;
-#pragma unroll
-              for (int e = 0; e < 4; e++) mx = vmax(mx, vmax(bf_lo(w[e]), bf_hi(w[e])));
-              mx = vmax(mx, dpp<0xB1>(mx));   // over the 8 lanes of the chunk
-              mx = vmax(mx, dpp<0x4E>(mx));
-              mx = vmax(mx, dpp<0x141>(mx));
-              const float mo = (mx == -INFINITY) ? 0.0f : mx * c;
-              float sm = 0.0f;
-#pragma unroll
-              for (int e = 0; e < 4; e++) sm += ex2(fmaf(bf_lo(w[e]), c, -mo)) + ex2(fmaf(bf_hi(w[e]), c, -mo));
-              sm = sum8(sm);
-              const float lc = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
-              const int cg = (t[q] * TP + (i * 64 + lane) * 8) / CH;   // global chunk of this lane's piece
-              const bool own = ((lane & 7) == 0) && cg * CH < V;
-              if (own) {
-                lse_tot = lse_add(lse_tot, lc);
-                const float sc = lc > -INFINITY ? lc + gumbel_bits(bits_at(key, (uint32_t)cg)) : -INFINITY;
-                if (lc > -INFINITY && takes(sc, cg, bs, bc)) {
-                  bs = sc;
-                  bc = cg;
-                }
-              }
-            }
-            // wave log-sum-exp of the owners' chunk masses and the wave argmax of their scores
-            {
-              const float M = wmax(lse_tot);
-              const float e = (lse_tot == -INFINITY) ? 0.0f : ex2((lse_tot - (M == -INFINITY ? 0.0f : M)) * LOG2E);
-              const int nan = __ballot(lse_tot != lse_tot) != 0ull;
-              const float S_ = wsum(e);
-              lse_tot = nan ? NAN : (M == -INFINITY ? -INFINITY : M + lg2(S_) * LN2);
-            }
-            wargmax(bs, bc, dummy);
-            rec = make_float4(lse_tot, bs, __int_as_float(bc), 0.0f);
+            for (int e = 0; e < 4; e++) sm += ex2(fmaf(bf_lo(w[e]), c, -mo)) + ex2(fmaf(bf_hi(w[e]), c, -mo));
+            sm = sum8(sm);
+            lcs[i] = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
           }
-          if (lane == 0) rec_store(rec_rsrc(p.rec_p, rec_p_bytes(B)), (size_t)ps[q] * MAX_G + t[q], rec);
+          float lc = lcs[0];
+#pragma unroll
+          for (int i = 1; i < NP; i++) lc = ((lane & 7) == i) ? lcs[i] : lc;
+          const int cg = cur.t * (TP / CH) + 8 * (lane & 7) + (lane >> 3);   // global chunk of the lane
+          lc = cg * CH < V ? lc : -INFINITY;
+          // wave log-sum-exp of the chunk masses
+          const float M = wmax(lc);
+          const float e = (lc == -INFINITY) ? 0.0f : ex2((lc - (M == -INFINITY ? 0.0f : M)) * LOG2E);
+          const int nan = __ballot(lc != lc) != 0ull;
+          const float S_ = wsum(e);
+          const float lse_tot = nan ? NAN : (M == -INFINITY ? -INFINITY : M + lg2(S_) * LN2);
+          // the chunk's score and the wave argmax
+          const uint64_t key = pos_key(req_key(seed, p.a.req_off + cur.rb), s, ST_BONUS_C);
+          const float gn = gumbel_bits(bits_at(key, (uint32_t)cg));
+          float bs = lc > -INFINITY ? lc + gn : -INFINITY, dummy = 0.0f;
+          int bc = lc > -INFINITY ? cg : -1;
+          wargmax(bs, bc, dummy);
+          rec = make_float4(lse_tot, bs, __int_as_float(bc), 0.0f);
         }
+        if (lane == 0) rec_store(rec_rsrc(p.rec_p, rec_p_bytes(B)), (size_t)cur.ps * MAX_G + cur.t, rec);
+        cur = nxt;
+        it += GW;
       }
     }
 
