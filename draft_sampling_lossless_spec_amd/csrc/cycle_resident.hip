@@ -1281,10 +1281,12 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
       invalid = true;
     } else {
       const float logp_s = rd.tx * invT - lse_p;
+      // accept when u = (ub + 1/2) 2^-32 < p / q = exp(logp - logq): the ratio in fp32 (its relative
+      // error, about 1e-7, is below that of the fp32 log-probabilities it comes from), compared
+      // exactly with u in fp64 as (ub + 1/2) < ratio 2^32
       const uint32_t ub = bits_at(key_acc, 0);
-      const double u = ((double)ub + 0.5) * 0x1p-32;
-      const double ratio = exp((double)logp_s - (double)logq_s);
-      if (u < ratio) {
+      const float ratio32 = __builtin_amdgcn_ldexpf(ex2((logp_s - logq_s) * LOG2E), 32);
+      if ((double)ub + 0.5 < (double)ratio32) {
         acc = s + 1;
       } else {
         phase = PH_REJECTED;
@@ -1505,9 +1507,9 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         __syncthreads();   // the wave counts are read before the next round writes them
       }
       // the counts are uniform over the workgroup (every wave read the same LDS words)
-      ls.n_draft = __builtin_amdgcn_readfirstlane(nd);
-      ls.n_correct = __builtin_amdgcn_readfirstlane(nc);
-      ls.n_plain = __builtin_amdgcn_readfirstlane(np);
+      ls.n_draft = nd;
+      ls.n_correct = nc;
+      ls.n_plain = np;
       ls.c0 = (nd + SUB - 1) / SUB * SUB;
       ls.n_sb = (ls.c0 + nc + SUB - 1) / SUB;
       for (int b = tid; b < B; b += NT) {
@@ -2001,12 +2003,13 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         for (int i = 0; i < NP; i++) q.xin |= (q.t * TP + (i * 64 + lane) * 8 < V) ? (1 << i) : 0;
         return q;
       };
-      // the lane's piece i of item q (a piece past V reads column 0 of the row and is masked; no
-      // item: an offset past the tensor, which reads zeros without a memory access)
+      // the lane's piece i of item q; a piece past V, or of no item, is read at an offset past the
+      // tensor (zeros, no memory access) and its results are masked
       const uint32_t tgt_bytes = (uint32_t)B * (uint32_t)(K + 1) * Vb;
       auto load_piece = [&](const PItem& q, int i) -> u32x4 {
-        const int col = ((q.xin >> i) & 1) ? q.t * TP + (i * 64 + lane) * 8 : 0;
-        const uint32_t off = q.rb >= 0 ? (uint32_t)(q.rb * (K + 1) + s) * Vb + 2u * (uint32_t)col : tgt_bytes;
+        const uint32_t off = (q.rb >= 0 && ((q.xin >> i) & 1))
+                                 ? (uint32_t)(q.rb * (K + 1) + s) * Vb + 2u * (uint32_t)(q.t * TP + (i * 64 + lane) * 8)
+                                 : tgt_bytes;
         return ldb16(rs_tgt, off, 0u);
       };
       int it = g * NW + wave;
@@ -2028,12 +2031,15 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           float m = -INFINITY, s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
           for (int i = 0; i < NP; i++) {
-            const u32x4 w = ((cur.xin >> i) & 1) ? x[i] : kNegInf;
-            x[i] = load_piece(nxt, i);   // unconditional, so that every wait counts the same loads
+            // piece i of the next item replaces this one as soon as it is read (unconditionally,
+            // so that every wait counts the same loads); the pieces are pinned in order
+            const u32x4 w = x[i];
+            x[i] = load_piece(nxt, i);
+            const bool in = (cur.xin >> i) & 1;
             float pm = vmax(bf_lo(w[0]), bf_hi(w[0]));
 #pragma unroll
             for (int e = 1; e < 4; e++) pm = vmax(pm, vmax(bf_lo(w[e]), bf_hi(w[e])));
-            const float mn = vmax(m, pm);
+            const float mn = vmax(m, in ? pm : -INFINITY);
             const float mo = (mn == -INFINITY) ? 0.0f : mn * c;
             const float sc = (m == -INFINITY) ? 0.0f : ex2(fmaf(m, c, -mo));
             float a0 = 0.0f, a1 = 0.0f;
@@ -2042,9 +2048,10 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
               a0 += ex2(fmaf(bf_lo(w[e]), c, -mo));
               a1 += ex2(fmaf(bf_hi(w[e]), c, -mo));
             }
-            s0 = fmaf(s0, sc, a0);
-            s1 = fmaf(s1, sc, a1);
+            s0 = fmaf(s0, sc, in ? a0 : 0.0f);
+            s1 = fmaf(s1, sc, in ? a1 : 0.0f);
             m = mn;
+            __builtin_amdgcn_sched_barrier(0);
           }
           const float mx = wmax(m);
           const float Mo = (mx == -INFINITY) ? 0.0f : mx * c;
@@ -2059,8 +2066,8 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           float lcs[NP];
 #pragma unroll
           for (int i = 0; i < NP; i++) {
-            const u32x4 w = ((cur.xin >> i) & 1) ? x[i] : kNegInf;
-            x[i] = load_piece(nxt, i);   // unconditional, so that every wait counts the same loads
+            const u32x4 w = x[i];
+            x[i] = load_piece(nxt, i);
             float mx = vmax(bf_lo(w[0]), bf_hi(w[0]));
 #pragma unroll
             for (int e = 1; e < 4; e++) mx = vmax(mx, vmax(bf_lo(w[e]), bf_hi(w[e])));
@@ -2073,6 +2080,8 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
             for (int e = 0; e < 4; e++) sm += ex2(fmaf(bf_lo(w[e]), c, -mo)) + ex2(fmaf(bf_hi(w[e]), c, -mo));
             sm = sum8(sm);
             lcs[i] = (mx == -INFINITY) ? (sm == 0.0f ? -INFINITY : NAN) : mx * invT + lg2(sm) * LN2;
+            lcs[i] = ((cur.xin >> i) & 1) ? lcs[i] : -INFINITY;
+            __builtin_amdgcn_sched_barrier(0);
           }
           float lc = lcs[0];
 #pragma unroll

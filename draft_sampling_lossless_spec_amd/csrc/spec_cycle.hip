@@ -1737,10 +1737,12 @@ __global__ __launch_bounds__(NT) void k_merge(Params p, int s) {
       invalid = true;
     } else {
       const float logp_s = rd.tx * invT - lse_p;
+      // accept when u = (ub + 1/2) 2^-32 < p / q = exp(logp - logq): the ratio in fp32 (its relative
+      // error, about 1e-7, is below that of the fp32 log-probabilities it comes from), compared
+      // exactly with u in fp64 as (ub + 1/2) < ratio 2^32
       const uint32_t ub = bits_at(key_from(kreq, s, ST_ACCEPT), 0);
-      const double u = ((double)ub + 0.5) * 0x1p-32;
-      const double ratio = exp((double)logp_s - (double)logq_s);
-      if (u < ratio) {
+      const float ratio32 = __builtin_amdgcn_ldexpf(ex2((logp_s - logq_s) * LOG2E), 32);
+      if ((double)ub + 0.5 < (double)ratio32) {
         acc = s + 1;
       } else {
         phase = PH_REJECTED;
