@@ -263,10 +263,12 @@ def spec_stats_workspace_bytes(B: int, K: int, V: int, R: int, dtype: int = BF16
 
 
 def spec_accept_stats(base_logits, target_logits, A, W, draft_tokens, temp, x0=None, workspace=None,
-                      out=None, stream=None) -> dict:
+                      out=None, stream=None, path: int = 0) -> dict:
     """Analytical acceptance rate alpha = sum_v min(p_j, q_j) = 1 - TV(p_j, q_j) of every drafted
     position (draft_tokens [B, K] int32, -1 past the drafted prefix, as the cycle's diagnostics
-    give it), with the log-normalisers 'lse_q' and 'lse_p'; NaN elsewhere.  Asynchronous."""
+    give it), with the log-normalisers 'lse_q' and 'lse_p'; NaN elsewhere.  path: 0 picks (the
+    W-resident kernel where the shape allows it), 1 the sweep kernels, 2 the W-resident kernel.
+    Asynchronous."""
     import torch
     B, K, V = base_logits.shape
     R = A.shape[1]
@@ -281,7 +283,7 @@ def spec_accept_stats(base_logits, target_logits, A, W, draft_tokens, temp, x0=N
         _check(x0, "x0", (B,), torch.int32)
     dev = base_logits.device
     lib = _load()
-    d = _Dims(B, K, V, R, dt, CHUNKED)
+    d = _Dims(B, K, V, R, dt, CHUNKED, path)
     need = int(lib.spec_stats_workspace_bytes(C.byref(d)))
     if need == 0:
         raise SpecError(f"unsupported dimensions B={B} K={K} V={V} R={R} dtype={dt}")

@@ -2136,6 +2136,393 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
   }
 }
 
+
+// ==========================================================================================
+// Acceptance statistics with W on chip: alpha_{b,j} = sum_v min(p_j(v), q_j(v)) of every listed
+// drafted position ("The Speed Claim Nobody's Really Questioning", sections "The Semi-Autoregressive
+// Trick" and "The Real Innovation: Confidence-Scheduled Verification").  One cooperative launch
+// with the vocabulary partition and W layout of k_resident.  The listed rows go in batches of
+// nbr rows (a multiple of SUB, their logits sized to stay in the Infinity Cache), each in four
+// phases:
+//   1. every workgroup, every sub-block of 32 rows: q = base + A[prev] . W (MFMA) and p over its
+//      slice -> per-workgroup log-normalisers of q and p;
+//   2. (grid barrier) one wave per row: the rows' log-normalisers;
+//   3. (grid barrier) every workgroup again: sum over its slice of min(p, q), the smaller of the two
+//      probabilities taken in the log domain;
+//   4. one wave per row: alpha, summed over the workgroups in a fixed order.  It runs after the
+//      next batch's first barrier, beside that batch's phase 2 (after a last barrier for the last
+//      batch): phases 1 and 2 of a batch touch other arrays than phase 4 of the one before.
+// ==========================================================================================
+struct StatsKP {
+  int B, K, V, R, G, nbr;
+  const void* base;
+  const void* target;
+  const void* A;
+  const void* W;
+  const float* temp;
+  const int32_t* n_rows;   // [1] listed rows
+  const int32_t* rows;     // [n] row id b K + j of each listed row
+  const int32_t* prev;     // [n] its previous token (-1: none)
+  float* alpha;            // [B, K] out
+  float* o_lse_q;          // [B, K] out, may be null
+  float* o_lse_p;          // [B, K] out, may be null
+  float* lq;               // [nbr] log-normalisers of the batch's rows
+  float* lp;               // [nbr]
+  float2* part1;           // [nbr][MAX_G] per-workgroup log-normalisers
+  float* part2;            // [nbr][MAX_G] per-workgroup sums of min(p, q)
+  uint64_t* flags;         // [MAX_G][FLAG_STRIDE]
+  uint64_t* err;
+  uint64_t nonce;
+};
+
+__host__ __device__ inline size_t stats_smem_bytes() {
+  return (size_t)4 * KSTEPS * 64 * 16 + (size_t)2 * KSTEPS * 64 * 16 + (size_t)2 * NW * SUB * 8;
+}
+
+__global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  bf16x8* wl = (bf16x8*)smem_raw;                             // [4][KSTEPS][64] W tiles of the LDS chunks
+  bf16x8* sA = wl + 4 * KSTEPS * 64;                          // [2][KSTEPS][64] B operands
+  float2* red = (float2*)(sA + 2 * KSTEPS * 64);              // [2][NW][SUB] wave results
+  const int K = p.K, V = p.V, R = p.R, G = p.G;
+  const int tid = threadIdx.x, lane = tid & 63, m32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x;
+  const int cbeg = chunk_begin(g, G, V), nch = chunks_of(g, G, V);
+  const int n_lds = nch > NW * AG_CHUNKS ? nch - NW * AG_CHUNKS : 0;
+  const int nks = R >> 4;
+
+  // ---- W slice on chip (the layout of k_resident): register chunks 2 wave, 2 wave + 1 and the
+  //      LDS tiles of local chunks 8 and 9 ----
+  bf16x8 wf[4][KSTEPS];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int cl = AG_CHUNKS * wave + (i >> 1);
+    const int c = cl < nch ? cbeg + cl : -1;
+    const int col_in = 16 * ((m32 >> 2) & 1) + 4 * (m32 >> 3) + (m32 & 3);
+    const int v = CH * c + 32 * (i & 1) + col_in;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; t++) {
+      const bool in = c >= 0 && v < V && t < nks;
+      const u32x4 x = *(const u32x4*)((const uint16_t*)p.W + (in ? (size_t)v * R + h * (R >> 1) + 8 * t : 0));
+      wf[i][t] = __builtin_bit_cast(bf16x8, in ? x : kZero);
+    }
+  }
+  for (int e = tid; e < 4 * KSTEPS * 64; e += NT) {
+    const int u = e / (KSTEPS * 64), t = (e / 64) % KSTEPS, l = e % 64;
+    const int cl = NW * AG_CHUNKS + (u >> 1);
+    const int c = cl < nch ? cbeg + cl : -1;
+    const int mm = l & 31, hh = l >> 5;
+    const int col_in = 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
+    const int v = CH * c + 32 * (u & 1) + col_in;
+    u32x4 z = kZero;
+    if (c >= 0 && v < V && t < nks) z = *(const u32x4*)((const uint16_t*)p.W + (size_t)v * R + hh * (R >> 1) + 8 * t);
+    ((u32x4*)wl)[e] = z;
+  }
+  // k-steps past the rank read zeros
+  for (int e = tid; e < 2 * KSTEPS * 64; e += NT)
+    if (((e >> 6) & (KSTEPS - 1)) >= nks) ((u32x4*)sA)[e] = kZero;
+
+  const int n = p.n_rows[0];
+  const int nbr = p.nbr;
+  const uint32_t Vb = 2u * (uint32_t)V;
+  const __amdgpu_buffer_rsrc_t rs_base = ld_rsrc(p.base, (uint32_t)p.B * (uint32_t)K * Vb);
+  const __amdgpu_buffer_rsrc_t rs_tgt = ld_rsrc(p.target, (uint32_t)p.B * (uint32_t)(K + 1) * Vb);
+  const __amdgpu_buffer_rsrc_t rsA = ld_rsrc(p.A, (uint32_t)V * (uint32_t)R * 2u);
+  const uint32_t dlds = 2u * (uint32_t)(CH * (NW * AG_CHUNKS - AG_CHUNKS * wave + (wave >> 1)) + 32 * (wave & 1));
+  const uint32_t col0 = 2u * (uint32_t)(CH * (cbeg + AG_CHUNKS * wave) + 16 * h);
+  // tile i of this wave (0..3: register chunks; 4: its LDS tile) exists in the workgroup's slice
+  const bool has0 = AG_CHUNKS * wave < nch, has1 = AG_CHUNKS * wave + 1 < nch, wave_lds = 2 * n_lds > wave;
+  auto tile_on = [&](int i) { return i < 2 ? has0 : (i < 4 ? has1 : wave_lds); };
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int i, u32x4 (&T)[2]) {
+    const uint32_t off = i < 4 ? (uint32_t)((i >> 1) * 2 * CH + (i & 1) * 64) : 0u;
+    const uint32_t so = i < 4 ? 0u : dlds;
+    T[0] = ldb16(rs, vo + off, so);
+    T[1] = ldb16(rs, vo + off + 16u, so);
+  };
+  auto load_tiles = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, u32x4 (&T)[5][2]) {
+#pragma unroll
+    for (int i = 0; i < 5; i++) load_tile(rs, vo, i, T[i]);
+  };
+  // the listed row of the lane's slot in sub-block k of the batch from r0
+  struct RowIn {
+    int lr, rid, prev;
+    float invT;
+    uint32_t vb, vt;   // byte offsets of the lane's first piece in the base and target rows
+  };
+  auto row_in = [&](int r0, int nb, int k) {
+    RowIn r;
+    r.lr = k * SUB + m32;
+    const bool act = r.lr < nb;
+    r.rid = act ? p.rows[r0 + r.lr] : -1;
+    r.prev = act ? p.prev[r0 + r.lr] : -1;
+    const int b = act ? r.rid / K : 0, j = act ? r.rid - b * K : 0;
+    r.invT = act ? 1.0f / p.temp[b] : 1.0f;
+    r.vb = act ? (uint32_t)(b * K + j) * Vb + col0 : STATS_PAST;   // inactive: past both tensors
+    r.vt = act ? (uint32_t)(b * (K + 1) + j) * Vb + col0 : STATS_PAST;
+    return r;
+  };
+  auto stage_issue = [&](int prev, u32x4 (&v)[4]) {
+    const uint32_t vo = prev >= 0 ? 2u * (uint32_t)(prev * R + h * (R >> 1) + 8 * wave) : OOB_OFF;
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = ldb16(rsA, vo + 64u * i, 0u);
+  };
+  auto stage_store = [&](int k, const u32x4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (4 * i + wave < nks) ((u32x4*)sA)[(k & 1) * KSTEPS * 64 + (4 * i + wave) * 64 + lane] = v[i];
+  };
+  // MFMA chains of register chunk ci (tiles 2 ci, 2 ci + 1) and of the LDS tile over the rank,
+  // LDS operands read two k-steps ahead
+  auto chain_reg = [&](f32x16& x, f32x16& y, int ci, const bf16x8* sAk) {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int t = 0; t < KSTEPS; t++) asm volatile("" : "+a"(wf[i][t]));
+    bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; t++) {
+      const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ci == 0 ? wf[0][t] : wf[2][t], bop, x, 0, 0, 0);
+      y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ci == 0 ? wf[1][t] : wf[3][t], bop, y, 0, 0, 0);
+      bop = bop1;
+      bop1 = bop2;
+    }
+  };
+  auto chain_lds = [&](f32x16& x, const bf16x8* sAk) {
+    const bf16x8* wlw = wl + (size_t)wave * KSTEPS * 64;
+    bf16x8 bop = sAk[lane], bop1 = sAk[64 + lane], wv = wlw[lane], wv1 = wlw[64 + lane];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; t++) {
+      const bf16x8 bop2 = (t + 2 < KSTEPS) ? sAk[(t + 2) * 64 + lane] : bop;
+      const bf16x8 wv2 = (t + 2 < KSTEPS) ? wlw[(t + 2) * 64 + lane] : wv;
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, bop, x, 0, 0, 0);
+      bop = bop1;
+      bop1 = bop2;
+      wv = wv1;
+      wv1 = wv2;
+    }
+  };
+  // accumulators seeded with the draft logits of tile i; a tile outside the workgroup's slice
+  // starts at -inf, so that its values drop out of every sum below without a test there
+  auto seed = [&](const u32x4 (&T)[2], int i) {
+    float x[16];
+    unpack16(T[0], T[1], x);
+    const bool on = tile_on(i);
+    f32x16 a;
+#pragma unroll
+    for (int q = 0; q < 16; q++) a[q] = on ? x[q] : -INFINITY;
+    return a;
+  };
+  // word e (two target logits) of tile i; -inf outside the slice
+  auto tword = [&](const u32x4 (&Tt)[5][2], int i, int e) -> uint32_t {
+    return tile_on(i) ? Tt[i][e >> 2][e & 3] : 0xFF80FF80u;
+  };
+
+  // One pass over the batch's sub-blocks.  Per sub-block three MFMA groups in turn (register
+  // chunk 0, register chunk 1, the LDS tile), each followed by its element-wise part:
+  // EW(row, x, y, i0, two, Tt, aux) -> float2 over tiles i0 (x) and i0 + 1 (y, if two) of the
+  // lane's row, CB(a, b) combines two groups' results, FL(k, row) the four waves' results of
+  // sub-block k (wave 0, lanes below SUB).  AUX(row) -> float2 is loaded a sub-block ahead and
+  // handed to EW.  Every tile is reloaded with the next sub-block's logits as soon as it has been
+  // used (draft logits: when seeded; target logits: after their element-wise part), so that each
+  // load has a whole sub-block to arrive; scheduling barriers keep the loads in place.
+  auto pass = [&](int r0, int nb, auto EW, auto CB, auto FL, auto AUX) __attribute__((always_inline)) {
+    const int nsb = (nb + SUB - 1) / SUB;
+    u32x4 Tb[5][2], Tt[5][2], sv[4];
+    RowIn rw = row_in(r0, nb, 0);
+    stage_issue(rw.prev, sv);
+    load_tiles(rs_base, rw.vb, Tb);
+    load_tiles(rs_tgt, rw.vt, Tt);
+    float2 ax = AUX(rw);
+    stage_store(0, sv);
+    __syncthreads();
+    for (int k = 0; k < nsb; k++) {
+      const bf16x8* sAk = sA + (size_t)(k & 1) * KSTEPS * 64;
+      const RowIn rn = row_in(r0, nb, k + 1);   // rows past the batch read past both tensors
+      const float2 axn = AUX(rn);
+      f32x16 a0 = seed(Tb[0], 0), a1 = seed(Tb[1], 1);
+      load_tile(rs_base, rn.vb, 0, Tb[0]);
+      load_tile(rs_base, rn.vb, 1, Tb[1]);
+      stage_issue(rn.prev, sv);
+      __builtin_amdgcn_sched_barrier(0);
+      chain_reg(a0, a1, 0, sAk);
+      f32x16 a2 = seed(Tb[2], 2), a3 = seed(Tb[3], 3), a4 = seed(Tb[4], 4);
+      load_tile(rs_base, rn.vb, 2, Tb[2]);
+      load_tile(rs_base, rn.vb, 3, Tb[3]);
+      load_tile(rs_base, rn.vb, 4, Tb[4]);
+      __builtin_amdgcn_sched_barrier(0);
+      // each group's element-wise part shares a scheduling region with the next group's MFMA chain
+      chain_reg(a2, a3, 1, sAk);
+      float2 o = EW(rw, a0, a1, 0, true, Tt, ax);
+      load_tile(rs_tgt, rn.vt, 0, Tt[0]);
+      load_tile(rs_tgt, rn.vt, 1, Tt[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      chain_lds(a4, sAk);
+      o = CB(o, EW(rw, a2, a3, 2, true, Tt, ax));
+      load_tile(rs_tgt, rn.vt, 2, Tt[2]);
+      load_tile(rs_tgt, rn.vt, 3, Tt[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      o = CB(o, EW(rw, a4, a4, 4, false, Tt, ax));
+      load_tile(rs_tgt, rn.vt, 4, Tt[4]);
+      if (h == 0) red[((k & 1) * NW + wave) * SUB + m32] = o;
+      if (k + 1 < nsb) stage_store(k + 1, sv);
+      __syncthreads();
+      if (wave == 0 && lane < SUB) FL(k, rw);
+      rw = rn;
+      ax = axn;
+    }
+    // nothing of the last (empty) prefetch is left in flight past the pass
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  uint64_t token = p.nonce;
+  const int GW = G * NW;
+  // alpha of the nb rows of the batch from r0: one wave per row, the workgroups' sums in a fixed
+  // order (phase 4 of a batch runs in phase 2 of the next, which reads other arrays)
+  auto merge2 = [&](int r0, int nb) {
+    for (int lr = g * NW + wave; lr < nb; lr += GW) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < MAX_G / 64; i++) {
+        const int w = lane + 64 * i;
+        a += w < G ? ld_f32(&p.part2[(size_t)lr * MAX_G + w]) : 0.0f;
+      }
+      a = wsum(a);
+      if (lane == 0) p.alpha[p.rows[r0 + lr]] = failed(p.err, p.nonce) ? NAN : a;
+    }
+  };
+  for (int r0 = 0; r0 < n; r0 += nbr) {
+    const int nb = min(nbr, n - r0);
+    // ---- 1. per-workgroup log-normalisers of q and p ----
+    pass(r0, nb,
+         [&](const RowIn& rw, const f32x16& x, const f32x16& y, int i0, bool two, const u32x4 (&Tt)[5][2], float2 ax) -> float2 {
+           const float c = rw.invT * LOG2E;
+           float mq = -INFINITY, mp = -INFINITY;
+#pragma unroll
+           for (int e = 0; e < 8; e++) {
+             const uint32_t tw = tword(Tt, i0, e);
+             mq = vmax(mq, vmax(x[2 * e], x[2 * e + 1]));
+             mp = vmax(mp, vmax(bf_lo(tw), bf_hi(tw)));
+             if (two) {
+               const uint32_t tv = tword(Tt, i0 + 1, e);
+               mq = vmax(mq, vmax(y[2 * e], y[2 * e + 1]));
+               mp = vmax(mp, vmax(bf_lo(tv), bf_hi(tv)));
+             }
+           }
+           mq = pmax32(mq);
+           mp = pmax32(mp);
+           const float oq = (mq == -INFINITY) ? 0.0f : mq * c, op = (mp == -INFINITY) ? 0.0f : mp * c;
+           float sq0 = 0.0f, sq1 = 0.0f, sp0 = 0.0f, sp1 = 0.0f;
+#pragma unroll
+           for (int e = 0; e < 8; e++) {
+             const uint32_t tw = tword(Tt, i0, e);
+             sq0 += ex2(fmaf(x[2 * e], c, -oq));
+             sq1 += ex2(fmaf(x[2 * e + 1], c, -oq));
+             sp0 += ex2(fmaf(bf_lo(tw), c, -op));
+             sp1 += ex2(fmaf(bf_hi(tw), c, -op));
+             if (two) {
+               const uint32_t tv = tword(Tt, i0 + 1, e);
+               sq0 += ex2(fmaf(y[2 * e], c, -oq));
+               sq1 += ex2(fmaf(y[2 * e + 1], c, -oq));
+               sp0 += ex2(fmaf(bf_lo(tv), c, -op));
+               sp1 += ex2(fmaf(bf_hi(tv), c, -op));
+             }
+           }
+           const float sq = psum32(sq0 + sq1), sp = psum32(sp0 + sp1);
+           const float lq = (mq == -INFINITY) ? (sq == 0.0f ? -INFINITY : NAN) : mq * rw.invT + lg2(sq) * LN2;
+           const float lp = (mp == -INFINITY) ? (sp == 0.0f ? -INFINITY : NAN) : mp * rw.invT + lg2(sp) * LN2;
+           return make_float2(lq, lp);
+         },
+         [](float2 a, float2 b) { return make_float2(lse2(a.x, b.x), lse2(a.y, b.y)); },
+         [&](int k, const RowIn& rw) {
+           if (rw.lr >= nb) return;
+           float2 a = red[((k & 1) * NW + 0) * SUB + m32];
+#pragma unroll
+           for (int w = 1; w < NW; w++) {
+             const float2 o = red[((k & 1) * NW + w) * SUB + m32];
+             a.x = lse2(a.x, o.x);
+             a.y = lse2(a.y, o.y);
+           }
+           float* pr = (float*)&p.part1[(size_t)rw.lr * MAX_G + g];
+           st_f32(pr, a.x);
+           st_f32(pr + 1, a.y);
+         },
+         [](const RowIn&) { return make_float2(0.0f, 0.0f); });
+    grid_barrier(p.flags, p.err, p.nonce, G, token++);
+    // ---- 2. the rows' log-normalisers: one wave per row (and phase 4 of the previous batch) ----
+    if (r0 > 0) merge2(r0 - nbr, nbr);
+    for (int lr = g * NW + wave; lr < nb; lr += GW) {
+      float mq = -INFINITY, mp = -INFINITY;
+      float2 v[MAX_G / 64];
+#pragma unroll
+      for (int i = 0; i < MAX_G / 64; i++) {
+        const int w = lane + 64 * i;
+        const float* pr = (const float*)&p.part1[(size_t)lr * MAX_G + (w < G ? w : 0)];
+        v[i] = w < G ? make_float2(ld_f32(pr), ld_f32(pr + 1)) : make_float2(-INFINITY, -INFINITY);
+        mq = vmax(mq, v[i].x);
+        mp = vmax(mp, v[i].y);
+      }
+      const float Mq = wmax(mq), Mp = wmax(mp);
+      const float bq = Mq == -INFINITY ? 0.0f : Mq, bp = Mp == -INFINITY ? 0.0f : Mp;
+      float sq = 0.0f, sp = 0.0f;
+#pragma unroll
+      for (int i = 0; i < MAX_G / 64; i++) {
+        sq += ex2((v[i].x - bq) * LOG2E);
+        sp += ex2((v[i].y - bp) * LOG2E);
+      }
+      sq = wsum(sq);
+      sp = wsum(sp);
+      const float lq = (Mq == -INFINITY) ? -INFINITY : Mq + lg2(sq) * LN2;
+      const float lpv = (Mp == -INFINITY) ? -INFINITY : Mp + lg2(sp) * LN2;
+      if (lane == 0) {
+        st_f32(&p.lq[lr], lq);
+        st_f32(&p.lp[lr], lpv);
+        const int rid = p.rows[r0 + lr];
+        if (p.o_lse_q) p.o_lse_q[rid] = lq;
+        if (p.o_lse_p) p.o_lse_p[rid] = lpv;
+      }
+    }
+    grid_barrier(p.flags, p.err, p.nonce, G, token++);
+    // ---- 3. per-workgroup sums of min(p, q) ----
+    pass(r0, nb,
+         [&](const RowIn& rw, const f32x16& x, const f32x16& y, int i0, bool two, const u32x4 (&Tt)[5][2], float2 ax) -> float2 {
+           // min(p, q) as the smaller base-2 log-probability: p if p < q, else q
+           const float c = rw.invT * LOG2E;
+           const float oq = -ax.x * LOG2E, op = -ax.y * LOG2E;
+           auto lmin = [](float lp2, float lq2) { return lp2 < lq2 ? lp2 : lq2; };
+           float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+           for (int e = 0; e < 8; e++) {
+             const uint32_t tw = tword(Tt, i0, e);
+             a0 += ex2(lmin(fmaf(bf_lo(tw), c, op), fmaf(x[2 * e], c, oq)));
+             a1 += ex2(lmin(fmaf(bf_hi(tw), c, op), fmaf(x[2 * e + 1], c, oq)));
+             if (two) {
+               const uint32_t tv = tword(Tt, i0 + 1, e);
+               a0 += ex2(lmin(fmaf(bf_lo(tv), c, op), fmaf(y[2 * e], c, oq)));
+               a1 += ex2(lmin(fmaf(bf_hi(tv), c, op), fmaf(y[2 * e + 1], c, oq)));
+             }
+           }
+           return make_float2(psum32(a0 + a1), 0.0f);
+         },
+         [](float2 a, float2 b) { return make_float2(a.x + b.x, 0.0f); },
+         [&](int k, const RowIn& rw) {
+           if (rw.lr >= nb) return;
+           float a = red[((k & 1) * NW + 0) * SUB + m32].x;
+#pragma unroll
+           for (int w = 1; w < NW; w++) a += red[((k & 1) * NW + w) * SUB + m32].x;
+           st_f32(&p.part2[(size_t)rw.lr * MAX_G + g], a);
+         },
+         [&](const RowIn& rw) {   // the row's log-normalisers (written before the last barrier)
+           const bool act = rw.lr < nb;
+           return make_float2(act ? ld_f32(&p.lq[rw.lr]) : 0.0f, act ? ld_f32(&p.lp[rw.lr]) : 0.0f);
+         });
+  }
+  // ---- 4. alpha of the last batch ----
+  grid_barrier(p.flags, p.err, p.nonce, G, token++);
+  if (n > 0) merge2((n - 1) / nbr * nbr, n - (n - 1) / nbr * nbr);
+}
+
 }  // namespace res
 }  // namespace spec
 
@@ -2202,6 +2589,49 @@ int launch(const Args& a_in, void* stream, void* ev_start, void* ev_stop) {
   if (hipLaunchCooperativeKernel((const void*)k_resident, dim3(a.G), dim3(NT), args, (unsigned)lds, st) != hipSuccess)
     return SPEC_E_HIP;
   if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, st) != hipSuccess) return SPEC_E_HIP;
+  return SPEC_OK;
+}
+
+int launch_stats(const StatsArgs& a, void* stream) {
+  const StatsLayout l = stats_layout(a.V, a.B * a.K);
+  StatsKP p;
+  p.B = a.B;
+  p.K = a.K;
+  p.V = a.V;
+  p.R = a.R;
+  p.G = a.G;
+  p.nbr = l.nbr;
+  p.base = a.base;
+  p.target = a.target;
+  p.A = a.A;
+  p.W = a.W;
+  p.temp = a.temp;
+  p.n_rows = a.n_rows;
+  p.rows = a.rows;
+  p.prev = a.prev;
+  p.alpha = a.alpha;
+  p.o_lse_q = a.o_lse_q;
+  p.o_lse_p = a.o_lse_p;
+  p.lq = (float*)(a.ws + l.off_lq);
+  p.lp = (float*)(a.ws + l.off_lp);
+  p.part1 = (float2*)(a.ws + l.off_part1);
+  p.part2 = (float*)(a.ws + l.off_part2);
+  p.flags = (uint64_t*)(a.ws + l.off_flags);
+  p.err = p.flags + (size_t)MAX_G * FLAG_STRIDE;
+  p.nonce = next_nonce();
+  static std::atomic<int> attr_set[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_HIP;
+  if (dev < 0 || dev >= 64 || attr_set[dev].load(std::memory_order_acquire) == 0) {
+    if (hipFuncSetAttribute((const void*)k_stats_res, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)stats_smem_bytes()) != hipSuccess)
+      return SPEC_E_HIP;
+    if (dev >= 0 && dev < 64) attr_set[dev].store(1, std::memory_order_release);
+  }
+  void* args[] = {&p};
+  if (hipLaunchCooperativeKernel((const void*)k_stats_res, dim3(a.G), dim3(NT), args, (unsigned)stats_smem_bytes(),
+                                 (hipStream_t)stream) != hipSuccess)
+    return SPEC_E_HIP;
   return SPEC_OK;
 }
 

@@ -109,6 +109,61 @@ __host__ __device__ inline bool eligible(int B, int K, int V, int R, int dtype, 
   return (n_chunks(V) + G - 1) / G <= MAX_CHUNKS && (V + TP - 1) / TP <= MAX_G;
 }
 
+// ---- acceptance statistics with W on chip ----
+// Listed rows go in batches whose base and target logits (4 V bytes a row) fit in this many bytes
+// of the Infinity Cache, so that the second pass over a batch finds them there.
+constexpr size_t STATS_BATCH_BYTES = (size_t)160 << 20;
+// byte offset past both logit tensors: the rows of inactive slots read zeros there
+constexpr uint32_t STATS_PAST = 0xFFFF0000u;
+
+__host__ __device__ inline bool stats_eligible(int B, int K, int V, int R, int dtype, int G) {
+  if (dtype != SPEC_BF16 || V % CH != 0 || R % 16 != 0 || R > 256 || G < 1 || G > MAX_G) return false;
+  if (B < 1 || K < 1) return false;
+  if ((size_t)B * (K + 1) * V * 2 >= (size_t)STATS_PAST - 4096 || (size_t)V * R * 2 >= ((size_t)1 << 31)) return false;
+  return (n_chunks(V) + G - 1) / G <= MAX_CHUNKS;
+}
+
+// workspace of the statistics kernel (offsets from its base, 256-byte aligned); n: B K rows
+struct StatsLayout {
+  int nbr;             // listed rows per batch (a multiple of SUB)
+  size_t off_lq, off_lp, off_part1, off_part2, off_flags, total;
+};
+__host__ __device__ inline StatsLayout stats_layout(int V, int n) {
+  StatsLayout l;
+  const size_t per = STATS_BATCH_BYTES / ((size_t)4 * (size_t)(V > 0 ? V : 1));
+  size_t nbr = per / SUB * SUB;
+  const size_t cap = ((size_t)(n > 0 ? n : 1) + SUB - 1) / SUB * SUB;
+  if (nbr < SUB) nbr = SUB;
+  if (nbr > cap) nbr = cap;
+  l.nbr = (int)nbr;
+  size_t o = 0;
+  l.off_lq = o; o = align256(o + 4 * nbr);
+  l.off_lp = o; o = align256(o + 4 * nbr);
+  l.off_part1 = o; o = align256(o + 8 * nbr * MAX_G);
+  l.off_part2 = o; o = align256(o + 4 * nbr * MAX_G);
+  l.off_flags = o; o = align256(o + 8 * (size_t)(MAX_G * FLAG_STRIDE + 2));
+  l.total = o;
+  return l;
+}
+
+// Arguments of one statistics launch (device pointers; see spec_accept_stats in spec_cycle.h).
+// n_rows, rows and prev are the listed drafted positions (written by the list kernel before).
+struct StatsArgs {
+  int B, K, V, R, G;
+  const void* base;
+  const void* target;
+  const void* A;
+  const void* W;
+  const float* temp;
+  const int32_t* n_rows;
+  const int32_t* rows;
+  const int32_t* prev;
+  float* alpha;
+  float* o_lse_q;
+  float* o_lse_p;
+  char* ws;                // stats_layout(V, B K).total bytes
+};
+
 }  // namespace res
 }  // namespace spec
 
@@ -118,6 +173,9 @@ namespace res {
 // Enqueue one resident cycle on `stream` (a hipStream_t); ev_start / ev_stop (hipEvent_t, may be
 // null) are recorded around the launch.  Returns SPEC_OK or SPEC_E_HIP.
 int launch(const Args& a, void* stream, void* ev_start, void* ev_stop);
+// Enqueue the statistics of the listed rows (one cooperative launch of G workgroups).  Returns
+// SPEC_OK or SPEC_E_HIP.
+int launch_stats(const StatsArgs& a, void* stream);
 inline size_t workspace_bytes(int B, int K) { return layout(B, K).total; }
 }  // namespace res
 }  // namespace spec

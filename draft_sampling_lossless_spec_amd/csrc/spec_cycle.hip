@@ -2803,7 +2803,7 @@ extern "C" int spec_cycle_timed(const spec_dims* d, const void* base_logits, con
 // acceptance statistics: host side
 // ------------------------------------------------------------------------------------------
 struct StatsLayout {
-  size_t off_konst, off_n, off_rows, off_prev, off_lq, off_lp, off_part, total;
+  size_t off_konst, off_n, off_rows, off_prev, off_lq, off_lp, off_part, off_res, total;
   int nrA;
 };
 
@@ -2820,6 +2820,9 @@ static StatsLayout stats_layout(const spec_dims* d) {
   l.off_lq = o; o = align256(o + 4 * n);
   l.off_lp = o; o = align256(o + 4 * n);
   l.off_part = o; o = align256(o + 8 * slots * (size_t)l.nrA);
+  // the W-resident statistics kernel's batch arrays and barrier flags (bf16 only)
+  l.off_res = o;
+  if (d->dtype == SPEC_BF16) o = align256(o + res::stats_layout(d->V, (int)n).total);
   l.total = o;
   return l;
 }
@@ -2884,6 +2887,35 @@ extern "C" int spec_accept_stats(const spec_dims* d, const void* base_logits, co
   const bool vec = ((d->V * esz) % 16 == 0) && ((((uintptr_t)base_logits) | ((uintptr_t)target_logits)) & 15) == 0;
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();
+  // the W-resident kernel where the shape allows it (d->path: AUTO or RESIDENT picks it, STEPWISE
+  // the sweep kernels; RESIDENT on a shape that does not qualify is SPEC_E_DTYPE)
+  const int G = cu_count() < res::MAX_G ? cu_count() : res::MAX_G;
+  const bool res_ok = vec && res::stats_eligible(d->B, d->K, d->V, d->R, d->dtype, G) && coop_ok();
+  if (d->path == SPEC_PATH_RESIDENT && !res_ok) return SPEC_E_DTYPE;
+  if (d->path != SPEC_PATH_AUTO && d->path != SPEC_PATH_RESIDENT && d->path != SPEC_PATH_STEPWISE) return SPEC_E_INVAL;
+  if (res_ok && d->path != SPEC_PATH_STEPWISE) {
+    hipLaunchKernelGGL(k_stats_prep, dim3(1), dim3(NT), 0, st, sp);
+    if (hipGetLastError() != hipSuccess) return SPEC_E_HIP;
+    res::StatsArgs a;
+    a.B = d->B;
+    a.K = d->K;
+    a.V = d->V;
+    a.R = d->R;
+    a.G = G;
+    a.base = base_logits;
+    a.target = target_logits;
+    a.A = A;
+    a.W = W;
+    a.temp = temp;
+    a.n_rows = sp.n_rows;
+    a.rows = sp.rows;
+    a.prev = sp.prev;
+    a.alpha = alpha;
+    a.o_lse_q = lse_q;
+    a.o_lse_p = lse_p;
+    a.ws = ws + l.off_res;
+    return res::launch_stats(a, st);
+  }
   if (d->dtype == SPEC_BF16) {
     if (vec) launch_stats<SPEC_BF16, true>(sp, st);
     else launch_stats<SPEC_BF16, false>(sp, st);

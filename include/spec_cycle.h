@@ -89,7 +89,7 @@ typedef struct spec_dims {
   int32_t noise;  /* SPEC_NOISE_FLAT: one Gumbel per vocabulary index;                      */
                   /* SPEC_NOISE_CHUNKED: exact two-level Gumbel-max over 64-wide chunks     */
   int32_t path;   /* SPEC_PATH_*: 0 (AUTO) picks; forcing RESIDENT on a call that does not  */
-                  /* qualify returns SPEC_E_DTYPE.  Ignored by spec_accept_stats.           */
+                  /* qualify returns SPEC_E_DTYPE (spec_accept_stats: see there).           */
 } spec_dims;
 
 typedef struct spec_diag {   /* optional per-position diagnostics; any field may be NULL     */
@@ -216,6 +216,11 @@ size_t spec_stats_workspace_bytes(const spec_dims* d);
  *   lse_q, lse_p [B, K] fp32   out, may be NULL: log-normalisers of q_j and p_j (NaN where alpha is)
  *   workspace                  device scratch of spec_stats_workspace_bytes(d) bytes, 256-byte
  *                              aligned, no initialisation needed
+ * d->path: SPEC_PATH_AUTO or SPEC_PATH_RESIDENT take one cooperative launch with W held on chip
+ * (bf16, V a multiple of 64, R <= 256 and a multiple of 16, logit tensors below 4 GiB, 16-byte
+ * aligned logits; RESIDENT on other dims returns SPEC_E_DTYPE, AUTO falls back); the rows go in
+ * batches whose logits stay in the Infinity Cache between the two passes.  SPEC_PATH_STEPWISE
+ * takes the sweep kernels (two passes over the logits, any dtype and V).
  * Asynchronous on `stream`, allocates nothing.  Returns SPEC_OK or a negative SPEC_E_* code
  * (NULL required pointer, bad dims or misaligned A / W: SPEC_E_INVAL; workspace: SPEC_E_WORKSPACE).
  */

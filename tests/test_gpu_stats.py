@@ -27,13 +27,13 @@ def seeded_draft(B, K, V, seed):
     return d
 
 
-def gpu_stats(w, draft, x0=True, temp=None):
+def gpu_stats(w, draft, x0=True, temp=None, path=0):
     import torch
     from draft_sampling_lossless_spec_amd import spec_accept_stats
     d = to_device(w)
     t = d["temp"] if temp is None else torch.from_numpy(temp.astype(np.float32)).cuda()
     out = spec_accept_stats(d["base"], d["target"], d["A"], d["W"], torch.from_numpy(draft).cuda(), t,
-                            x0=d["x0"] if x0 else None)
+                            x0=d["x0"] if x0 else None, path=path)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
 
@@ -64,7 +64,15 @@ SMALL = {
     "k1_b1_r256": lambda: wl.generate(wl.small_config(B=1, K=1, V=4096, R=256, threshold=0.1)),
     "temp06_k8": lambda: wl.generate(wl.small_config(B=16, K=8, V=5000, R=32, threshold=0.05, temp=0.6,
                                                       sigma=(1.5,))),
+    # whole 64-column chunks in bf16: the W-resident kernel takes these (AUTO and forced), the
+    # sweep kernels are run on them too
+    "v20032_bf16": lambda: wl.generate(wl.small_config(B=40, K=5, V=20032, R=64, threshold=0.1)),
+    "temp06_k8_v4992": lambda: wl.generate(wl.small_config(B=16, K=8, V=4992, R=32, threshold=0.05, temp=0.6,
+                                                            sigma=(1.5,))),
+    "k32_b9_v64": lambda: wl.generate(wl.small_config(B=9, K=32, V=64, R=16, threshold=0.01)),
 }
+# cases on which both statistics paths run (the W-resident kernel needs bf16 and whole chunks)
+BOTH = ("b300_many_row_blocks", "k1_b1_r256", "v20032_bf16", "temp06_k8_v4992", "k32_b9_v64")
 
 
 @pytest.mark.parametrize("case", sorted(SMALL))
@@ -72,7 +80,10 @@ def test_small_stats_match_oracle(case):
     print(f"stats {case}", flush=True)
     w = SMALL[case]()
     draft = seeded_draft(w.cfg.B, w.cfg.K, w.cfg.V, 7)
-    assert_stats_match(ref_stats(w, draft), gpu_stats(w, draft))
+    o = ref_stats(w, draft)
+    for path in ((0, 1, 2) if case in BOTH else (0,)):
+        print(f"  path {path}", flush=True)
+        assert_stats_match(o, gpu_stats(w, draft, path=path))
 
 
 def test_stats_edge_cases():
@@ -86,10 +97,23 @@ def test_stats_edge_cases():
     temp[2] = 0.0                       # invalid temperature: every position NaN
     for x0 in (True, False):
         assert_stats_match(ref_stats(w, draft, x0=x0, temp=temp), gpu_stats(w, draft, x0=x0, temp=temp))
+    # the same on whole 64-column chunks, both paths
+    wc = wl.generate(wl.small_config(B=6, K=4, V=1024, R=32, threshold=0.1))
+    tc = wc.temp.copy()
+    tc[2] = 0.0
+    for x0 in (True, False):
+        oc = ref_stats(wc, draft, x0=x0, temp=tc)
+        for path in (1, 2):
+            assert_stats_match(oc, gpu_stats(wc, draft, x0=x0, temp=tc, path=path))
     # identical draft and target rows and no bias: alpha = 1
     w2 = wl.Workload(w.cfg, w.target[:, :K].copy(), w.target, np.zeros_like(w.A), np.zeros_like(w.W), w.x0, w.conf,
                      w.temp, w.threshold, w.seed, w.request_ids)
     g = gpu_stats(w2, draft)
+    a = g["alpha"][~np.isnan(g["alpha"])]
+    assert np.all(np.abs(a - 1.0) < 1e-4)
+    wc2 = wl.Workload(wc.cfg, wc.target[:, :K].copy(), wc.target, np.zeros_like(wc.A), np.zeros_like(wc.W), wc.x0,
+                      wc.conf, wc.temp, wc.threshold, wc.seed, wc.request_ids)
+    g = gpu_stats(wc2, draft, path=2)
     a = g["alpha"][~np.isnan(g["alpha"])]
     assert np.all(np.abs(a - 1.0) < 1e-4)
 
@@ -101,7 +125,10 @@ def test_full_size_stats(name):
     B, K, V = w.cfg.B, w.cfg.K, w.cfg.V
     draft = seeded_draft(B, K, V, 11)
     g = gpu_stats(w, draft)
-    assert_stats_match(ref_stats(w, draft), g)
+    o = ref_stats(w, draft)
+    assert_stats_match(o, g)
+    if V % 64 == 0:
+        assert_stats_match(o, gpu_stats(w, draft, path=1))   # the sweep kernels as well
     # every drafted position is finite and a probability
     m = draft >= 0
     assert np.isfinite(g["alpha"][m]).all() and np.isnan(g["alpha"][~m]).all()

@@ -290,3 +290,79 @@ def test_resident_records_in_bounds(B, K):
             assert np.all(col[inside] + 8 <= V)
     # the library sizes the workspace to hold every record area
     assert workspace_bytes(B, K, V, R, 2) >= rec_d + rec_c + rec_p
+
+
+# ---------------------------------------------------------------------------------------------
+# W-resident acceptance statistics (k_stats_res)
+# ---------------------------------------------------------------------------------------------
+STATS_BATCH_BYTES = 160 << 20
+STATS_PAST = 0xFFFF0000
+FLAG_STRIDE = 2
+
+
+def stats_eligible(B, K, V, R, G=256):
+    return (V % CHUNK == 0 and R % 16 == 0 and R <= 256 and B >= 1 and K >= 1
+            and B * (K + 1) * V * 2 < STATS_PAST - 4096 and V * R * 2 < 1 << 31
+            and -(-n_chunks(V) // G) <= MAX_CHUNKS)
+
+
+def stats_layout(V, n):
+    """Batch rows and the offsets of the statistics kernel's arrays (the formulas of
+    resident.h's stats_layout, restated)."""
+    a256 = lambda x: -(-x // 256) * 256
+    nbr = STATS_BATCH_BYTES // (4 * V) // SUB * SUB
+    nbr = min(max(nbr, SUB), -(-max(n, 1) // SUB) * SUB)
+    o, off = 0, {}
+    for name, size in (("lq", 4 * nbr), ("lp", 4 * nbr), ("part1", 8 * nbr * MAX_G), ("part2", 4 * nbr * MAX_G),
+                       ("flags", 8 * (MAX_G * FLAG_STRIDE + 2))):
+        off[name] = (o, size)
+        o = a256(o + size)
+    return nbr, off, o
+
+
+@pytest.mark.parametrize("B,K,V,R", [(256, 16, 151936, 256), (64, 5, 151936, 256), (300, 3, 2048, 16),
+                                     (1, 1, 4096, 256), (9, 32, 64, 16), (1024, 32, 20032, 64),
+                                     (40, 5, 20032, 64), (1024, 32, 151936, 256)])
+def test_stats_batches_offsets_and_workspace(B, K, V, R):
+    """Every listed row falls in exactly one batch; a batch's logits fit the cache budget (or it is
+    one sub-block); per-batch arrays are indexed below nbr and MAX_G; the byte offsets of active
+    rows stay inside their tensors and those of inactive slots lie past both tensors without
+    wrapping; the library's workspace holds the statistics arrays."""
+    from draft_sampling_lossless_spec_amd import binding
+    if not stats_eligible(B, K, V, R):
+        assert B * (K + 1) * V * 2 >= STATS_PAST - 4096
+        pytest.skip("not eligible")
+    n = B * K
+    nbr, off, total = stats_layout(V, n)
+    assert nbr % SUB == 0 and nbr >= SUB
+    assert nbr * 4 * V <= STATS_BATCH_BYTES or nbr == SUB
+    covered = np.zeros(n, int)
+    for r0 in range(0, n, nbr):
+        nb = min(nbr, n - r0)
+        assert 0 < nb <= nbr
+        covered[r0:r0 + nb] += 1
+        lr = np.arange(-(-nb // SUB) * SUB)   # slots of the batch's sub-blocks (the last one ragged)
+        assert lr[lr < nb].max() < nbr
+    assert np.all(covered == 1)
+    # the last batch of the merge after the final barrier
+    last_r0 = (n - 1) // nbr * nbr
+    assert 0 < n - last_r0 <= nbr
+    # record offsets: part1 / part2 [nbr][MAX_G], flags [MAX_G][FLAG_STRIDE] + error word
+    assert (nbr - 1) * MAX_G + (MAX_G - 1) < off["part1"][1] // 8
+    assert (nbr - 1) * MAX_G + (MAX_G - 1) < off["part2"][1] // 4
+    assert MAX_G * FLAG_STRIDE + 1 < off["flags"][1] // 8
+    ends = sorted((o, o + s) for o, s in off.values())
+    assert all(a[1] <= b[0] for a, b in zip(ends, ends[1:])) and ends[-1][1] <= total
+    # logit offsets (bytes): the last row of each tensor, every wave's tiles, plus the inactive marker
+    G = 256
+    cb = np.array([chunk_begin(g, G, V) for g in range(G)])
+    for nrow in (K, K + 1):
+        size = B * nrow * 2 * V
+        for w in range(NW):
+            dlds = 2 * (CHUNK * (NW * AG_CHUNKS - AG_CHUNKS * w + (w >> 1)) + 32 * (w & 1))
+            top = (B * nrow - 1) * 2 * V + 2 * (CHUNK * (cb + AG_CHUNKS * w) + 16) + max(3 * 64 + 64, dlds) + 32
+            assert top.max() < 1 << 32
+        assert size <= STATS_PAST and STATS_PAST + 2 * 2 * CHUNK + 64 + 32 + 2 * CHUNK * NW * AG_CHUNKS + 64 < 1 << 32
+    # the library's statistics workspace holds these arrays after its sweep arrays
+    ws = binding.spec_stats_workspace_bytes(B, K, V, R)
+    assert ws >= total
