@@ -2327,7 +2327,9 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
   // handed to EW.  Every tile is reloaded with the next sub-block's logits as soon as it has been
   // used (draft logits: when seeded; target logits: after their element-wise part), so that each
   // load has a whole sub-block to arrive; scheduling barriers keep the loads in place.
-  auto pass = [&](int r0, int nb, auto EW, auto CB, auto FL, auto AUX) __attribute__((always_inline)) {
+  // PRE(row, Tt) -> float runs beside the first MFMA chain on the target logits alone; with
+  // pre_all it uses all five target tiles, which are then reloaded right after it.
+  auto pass = [&](int r0, int nb, auto EW, auto CB, auto FL, auto AUX, auto PRE, bool pre_all) __attribute__((always_inline)) {
     const int nsb = (nb + SUB - 1) / SUB;
     u32x4 Tb[5][2], Tt[5][2], sv[4];
     RowIn rw = row_in(r0, nb, 0);
@@ -2347,6 +2349,8 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
       stage_issue(rn.prev, sv);
       __builtin_amdgcn_sched_barrier(0);
       chain_reg(a0, a1, 0, sAk);
+      const float pre = PRE(rw, Tt);
+      if (pre_all) load_tiles(rs_tgt, rn.vt, Tt);
       f32x16 a2 = seed(Tb[2], 2), a3 = seed(Tb[3], 3), a4 = seed(Tb[4], 4);
       load_tile(rs_base, rn.vb, 2, Tb[2]);
       load_tile(rs_base, rn.vb, 3, Tb[3]);
@@ -2355,16 +2359,21 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
       // each group's element-wise part shares a scheduling region with the next group's MFMA chain
       chain_reg(a2, a3, 1, sAk);
       float2 o = EW(rw, a0, a1, 0, true, Tt, ax);
-      load_tile(rs_tgt, rn.vt, 0, Tt[0]);
-      load_tile(rs_tgt, rn.vt, 1, Tt[1]);
+      if (!pre_all) {
+        load_tile(rs_tgt, rn.vt, 0, Tt[0]);
+        load_tile(rs_tgt, rn.vt, 1, Tt[1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       chain_lds(a4, sAk);
       o = CB(o, EW(rw, a2, a3, 2, true, Tt, ax));
-      load_tile(rs_tgt, rn.vt, 2, Tt[2]);
-      load_tile(rs_tgt, rn.vt, 3, Tt[3]);
+      if (!pre_all) {
+        load_tile(rs_tgt, rn.vt, 2, Tt[2]);
+        load_tile(rs_tgt, rn.vt, 3, Tt[3]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       o = CB(o, EW(rw, a4, a4, 4, false, Tt, ax));
-      load_tile(rs_tgt, rn.vt, 4, Tt[4]);
+      if (!pre_all) load_tile(rs_tgt, rn.vt, 4, Tt[4]);
+      o.y = pre_all ? pre : o.y;
       if (h == 0) red[((k & 1) * NW + wave) * SUB + m32] = o;
       if (k + 1 < nsb) stage_store(k + 1, sv);
       __syncthreads();
@@ -2394,47 +2403,33 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
   };
   for (int r0 = 0; r0 < n; r0 += nbr) {
     const int nb = min(nbr, n - r0);
-    // ---- 1. per-workgroup log-normalisers of q and p ----
+    // ---- 1. per-workgroup log-normalisers of q (per MFMA group) and p (beside the first chain) ----
     pass(r0, nb,
-         [&](const RowIn& rw, const f32x16& x, const f32x16& y, int i0, bool two, const u32x4 (&Tt)[5][2], float2 ax) -> float2 {
+         [&](const RowIn& rw, const f32x16& x, const f32x16& y, int, bool two, const u32x4 (&)[5][2], float2) -> float2 {
            const float c = rw.invT * LOG2E;
-           float mq = -INFINITY, mp = -INFINITY;
+           float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-           for (int e = 0; e < 8; e++) {
-             const uint32_t tw = tword(Tt, i0, e);
-             mq = vmax(mq, vmax(x[2 * e], x[2 * e + 1]));
-             mp = vmax(mp, vmax(bf_lo(tw), bf_hi(tw)));
+           for (int q = 0; q < 16; q += 2) {
+             m0 = vmax(m0, vmax(x[q], x[q + 1]));
+             if (two) m1 = vmax(m1, vmax(y[q], y[q + 1]));
+           }
+           const float mq = pmax32(vmax(m0, m1));
+           const float oq = (mq == -INFINITY) ? 0.0f : mq * c;
+           float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+           for (int q = 0; q < 16; q += 2) {
+             s0 += ex2(fmaf(x[q], c, -oq));
+             s1 += ex2(fmaf(x[q + 1], c, -oq));
              if (two) {
-               const uint32_t tv = tword(Tt, i0 + 1, e);
-               mq = vmax(mq, vmax(y[2 * e], y[2 * e + 1]));
-               mp = vmax(mp, vmax(bf_lo(tv), bf_hi(tv)));
+               s2 += ex2(fmaf(y[q], c, -oq));
+               s3 += ex2(fmaf(y[q + 1], c, -oq));
              }
            }
-           mq = pmax32(mq);
-           mp = pmax32(mp);
-           const float oq = (mq == -INFINITY) ? 0.0f : mq * c, op = (mp == -INFINITY) ? 0.0f : mp * c;
-           float sq0 = 0.0f, sq1 = 0.0f, sp0 = 0.0f, sp1 = 0.0f;
-#pragma unroll
-           for (int e = 0; e < 8; e++) {
-             const uint32_t tw = tword(Tt, i0, e);
-             sq0 += ex2(fmaf(x[2 * e], c, -oq));
-             sq1 += ex2(fmaf(x[2 * e + 1], c, -oq));
-             sp0 += ex2(fmaf(bf_lo(tw), c, -op));
-             sp1 += ex2(fmaf(bf_hi(tw), c, -op));
-             if (two) {
-               const uint32_t tv = tword(Tt, i0 + 1, e);
-               sq0 += ex2(fmaf(y[2 * e], c, -oq));
-               sq1 += ex2(fmaf(y[2 * e + 1], c, -oq));
-               sp0 += ex2(fmaf(bf_lo(tv), c, -op));
-               sp1 += ex2(fmaf(bf_hi(tv), c, -op));
-             }
-           }
-           const float sq = psum32(sq0 + sq1), sp = psum32(sp0 + sp1);
+           const float sq = psum32((s0 + s1) + (s2 + s3));
            const float lq = (mq == -INFINITY) ? (sq == 0.0f ? -INFINITY : NAN) : mq * rw.invT + lg2(sq) * LN2;
-           const float lp = (mp == -INFINITY) ? (sp == 0.0f ? -INFINITY : NAN) : mp * rw.invT + lg2(sp) * LN2;
-           return make_float2(lq, lp);
+           return make_float2(lq, 0.0f);
          },
-         [](float2 a, float2 b) { return make_float2(lse2(a.x, b.x), lse2(a.y, b.y)); },
+         [](float2 a, float2 b) { return make_float2(lse2(a.x, b.x), 0.0f); },
          [&](int k, const RowIn& rw) {
            if (rw.lr >= nb) return;
            float2 a = red[((k & 1) * NW + 0) * SUB + m32];
@@ -2448,7 +2443,35 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
            st_f32(pr, a.x);
            st_f32(pr + 1, a.y);
          },
-         [](const RowIn&) { return make_float2(0.0f, 0.0f); });
+         [](const RowIn&) { return make_float2(0.0f, 0.0f); },
+         [&](const RowIn& rw, const u32x4 (&Tt)[5][2]) -> float {
+           const float c = rw.invT * LOG2E;
+           float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+           for (int i = 0; i < 5; i++)
+#pragma unroll
+             for (int e = 0; e < 8; e += 2) {
+               const uint32_t t0 = tword(Tt, i, e), t1 = tword(Tt, i, e + 1);
+               m0 = vmax(m0, vmax(bf_lo(t0), bf_hi(t0)));
+               m1 = vmax(m1, vmax(bf_lo(t1), bf_hi(t1)));
+             }
+           const float mp = pmax32(vmax(m0, m1));
+           const float op = (mp == -INFINITY) ? 0.0f : mp * c;
+           float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+           for (int i = 0; i < 5; i++)
+#pragma unroll
+             for (int e = 0; e < 8; e += 2) {
+               const uint32_t t0 = tword(Tt, i, e), t1 = tword(Tt, i, e + 1);
+               s0 += ex2(fmaf(bf_lo(t0), c, -op));
+               s1 += ex2(fmaf(bf_hi(t0), c, -op));
+               s2 += ex2(fmaf(bf_lo(t1), c, -op));
+               s3 += ex2(fmaf(bf_hi(t1), c, -op));
+             }
+           const float sp = psum32((s0 + s1) + (s2 + s3));
+           return (mp == -INFINITY) ? (sp == 0.0f ? -INFINITY : NAN) : mp * rw.invT + lg2(sp) * LN2;
+         },
+         true);
     grid_barrier(p.flags, p.err, p.nonce, G, token++);
     // ---- 2. the rows' log-normalisers: one wave per row (and phase 4 of the previous batch) ----
     if (r0 > 0) merge2(r0 - nbr, nbr);
@@ -2516,7 +2539,8 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
          [&](const RowIn& rw) {   // the row's log-normalisers (written before the last barrier)
            const bool act = rw.lr < nb;
            return make_float2(act ? ld_f32(&p.lq[rw.lr]) : 0.0f, act ? ld_f32(&p.lp[rw.lr]) : 0.0f);
-         });
+         },
+         [](const RowIn&, const u32x4 (&)[5][2]) { return 0.0f; }, false);
   }
   // ---- 4. alpha of the last batch ----
   grid_barrier(p.flags, p.err, p.nonce, G, token++);
