@@ -952,6 +952,11 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
     tvr[q] = *(need_targ[q] ? jb[q].targ + v[q] : (const uint16_t*)p.a.target);
   }
   __builtin_amdgcn_sched_barrier(0);   // every load of the round is in flight before any is used
+  // the candidates' Gumbel noise while the loads are in flight
+  float gg[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) gg[q] = gumbel_bf(bits_at(jb[q].key, (uint32_t)v[q]));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 0; q < 2; q++) {
 #pragma unroll
@@ -983,26 +988,25 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
     float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
     int ix = -1;
     if (in[q] && kq == 0) {
-      const float gg = gumbel_bf(bits_at(jb[q].key, (uint32_t)v[q]));
       if (jb[q].kind == L2_DRAFT) {
         const float sv = (bv[q] + bias[q]) * invT;
         if (jb[q].want_target) tx = tv[q];
         if (sv > -INFINITY) {
-          sc = sv + gg;
+          sc = sv + gg[q];
           ix = v[q];
           sx = sv;
         }
       } else if (jb[q].kind == L2_TARGET) {
         const float t = tv[q] * invT;
         if (t > -INFINITY) {
-          sc = t + gg;
+          sc = t + gg[q];
           ix = v[q];
         }
       } else {
         const float sv = (bv[q] + bias[q]) * invT, t = tv[q] * invT;
         const float lp = t - jb[q].lse_p, lq = sv - jb[q].lse_q;
         if (lp > lq) {
-          sc = lp + logf(-expm1f(lq - lp)) + gg;
+          sc = lp + logf(-expm1f(lq - lp)) + gg[q];
           ix = v[q];
         }
       }
@@ -1038,7 +1042,7 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
 // holds the log-mass of the wave's register chunks, their best score and chunk, and the log-mass
 // of the wave's half of an LDS chunk; the halves of LDS chunk i are in waves 2i and 2i + 1, and
 // the chunk's Gumbel score is formed here from the whole chunk.
-__device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, uint64_t key) {
+__device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, const float (&gl)[LDS_CHUNKS]) {
   float lse = -INFINITY, bs = -INFINITY;
   int bc = -1;
 #pragma unroll
@@ -1056,7 +1060,7 @@ __device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl
     const float hc = lse_add(a[2 * i].w, a[2 * i + 1].w);
     lse = lse_add(lse, hc);
     const int cgl = cb + NW * AG_CHUNKS + i;
-    const float sc = hc > -INFINITY ? hc + gumbel_bf(bits_at(key, (uint32_t)cgl)) : -INFINITY;
+    const float sc = hc > -INFINITY ? hc + gl[i] : -INFINITY;
     if (hc > -INFINITY && takes(sc, cgl, bs, bc)) {
       bs = sc;
       bc = cgl;
@@ -1068,8 +1072,8 @@ __device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl
 // The same for a CORRECT row: the residual records a (log residual mass of the register chunks,
 // best score, best chunk, LINEAR residual mass of the LDS half) and the target records t (target
 // log-mass, best score, best chunk, target log-mass of the LDS half); both draws use `key`.
-__device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb, int nl, uint64_t key, float4& rd,
-                           float4& rt) {
+__device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb, int nl,
+                                           const float (&gl)[LDS_CHUNKS], float4& rd, float4& rt) {
   float ms = 0.0f, lt = -INFINITY, bs = -INFINITY, bt = -INFINITY;
   int bc = -1, btc = -1;
 #pragma unroll
@@ -1089,7 +1093,7 @@ __device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (
   for (int i = 0; i < LDS_CHUNKS; i++) {
     if (i >= nl) break;
     const int cgl = cb + NW * AG_CHUNKS + i;
-    const float gg = gumbel_bf(bits_at(key, (uint32_t)cgl));
+    const float gg = gl[i];
     const float mc = a[2 * i].w + a[2 * i + 1].w;
     ms += mc;
     const float lmc = mc > 0.0f ? lg2(mc) * LN2 : -INFINITY;
@@ -1175,16 +1179,24 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     key_l2r = pos_key(kreq, s > 0 ? s - 1 : 0, ST_RESIDUAL);
     key_l2b = pos_key(kreq, s, ST_BONUS);
     key_acc = pos_key(kreq, s, ST_ACCEPT);
+    // the Gumbel noise of workgroup gi's LDS chunks for both row kinds, while the loads are in flight
+    float gld[LDS_CHUNKS], glc[LDS_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < LDS_CHUNKS; i++) {
+      const uint32_t cgl = (uint32_t)(cb + NW * AG_CHUNKS + i);
+      gld[i] = gumbel_bf(bits_at(key_d, cgl));
+      glc[i] = gumbel_bf(bits_at(key_c, cgl));
+    }
     __builtin_amdgcn_sched_barrier(0);   // the loads are in flight before any is used
     // (component-wise selects: a select of whole structs goes through scratch memory)
     auto sel4 = [](bool c, float4 a, float4 b) {
       return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
     };
-    ml->part[0][tid] = sel4(hasD && tid < G, wg_draft(ad, cb, nl, key_d), none);
+    ml->part[0][tid] = sel4(hasD && tid < G, wg_draft(ad, cb, nl, gld), none);
     ml->part[3][tid] = sel4(hasP && tid < nrP, ap, none);
     if (hasC) {
       float4 rd = none, rt = none;
-      if (tid < G) wg_correct(ac, at, cb, nl, key_c, rd, rt);
+      if (tid < G) wg_correct(ac, at, cb, nl, glc, rd, rt);
       ml->part[1][tid] = rd;
       ml->part[2][tid] = rt;
     }
