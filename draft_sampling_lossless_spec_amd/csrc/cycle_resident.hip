@@ -1583,13 +1583,13 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     const uint32_t Vb = 2u * (uint32_t)V;
     const uint32_t dlds = 2u * (uint32_t)(CH * (NW * AG_CHUNKS - AG_CHUNKS * wave + (wave >> 1)) + 32 * (wave & 1));
     auto row_off = [&](int b, int j, int nrow) -> uint32_t {
-      return (uint32_t)((b >= 0 ? b : 0) * nrow + j) * Vb + 2u * (uint32_t)(CH * (cbeg + AG_CHUNKS * wave) + 16 * h);
+      return b >= 0 ? (uint32_t)(b * nrow + j) * Vb + 2u * (uint32_t)(CH * (cbeg + AG_CHUNKS * wave) + 16 * h)
+                    : PAST_END;   // an empty slot reads zeros, without a memory access
     };
     auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int i, u32x4 (&T)[2]) {
-      const uint32_t off = i < 4 ? (uint32_t)((i >> 1) * 2 * CH + (i & 1) * 64) : 0u;
-      const uint32_t so = i < 4 ? 0u : dlds;
-      T[0] = ldb16(rs, vo + off, so);
-      T[1] = ldb16(rs, vo + off + 16u, so);
+      const uint32_t off = i < 4 ? (uint32_t)((i >> 1) * 2 * CH + (i & 1) * 64) : dlds;
+      T[0] = ldb16(rs, vo + off, 0u);
+      T[1] = ldb16(rs, vo + off + 16u, 0u);
     };
     const __amdgpu_buffer_rsrc_t rs_base = ld_rsrc(p.a.base, (uint32_t)B * (uint32_t)K * Vb);
     const __amdgpu_buffer_rsrc_t rs_tgt = ld_rsrc(p.a.target, (uint32_t)B * (uint32_t)(K + 1) * Vb);
@@ -1841,8 +1841,6 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     }
     if (bp >= 0) draft_record(n_dsb - 1, bp, l0p, l1p, gmp, tiles_lse<1>(&a4p, invTp));
 
-    // CORRECT sub-blocks: residual mass max(0, p - q) of position s - 1 per chunk with its score,
-    // and the target row's chunk log-masses (the draw falls back to p when no residual is left)
     for (int k = n_dsb; k < ls.n_sb; k++) {
       tid = opaque_tid();
       int b, j;
@@ -1858,7 +1856,6 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       bool c2 = false;
       if (k + 1 < ls.n_sb) row_of(k + 1, b2, j2, c2);
       const uint32_t vo2 = row_off(b2, j2, K);
-      // target logits of the row, each tile loaded a chain ahead of its use
       u32x4 Tt[5][2];
       const uint32_t vot = row_off(b, j, K + 1);
       load_tile(rs_tgt, vot, 0, Tt[0]);
@@ -1952,6 +1949,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+
       const float2 gp = pair32(gm);
       const float g0 = gp.x, g1 = gp.y;
       float m0, t0, m1, t1, mh, th;
@@ -1966,6 +1964,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           corr_step(hs, i, a4, zero, Tt[4][0], Tt[4][1], Tt[4][0], Tt[4][1], c, op, oq);
         corr_end(hs, lp, mh, th);
       }
+
       m0 = has0 ? m0 : 0.0f;
       t0 = has0 ? t0 : -INFINITY;
       m1 = has1 ? m1 : 0.0f;
@@ -2247,10 +2246,9 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
   const bool has0 = AG_CHUNKS * wave < nch, has1 = AG_CHUNKS * wave + 1 < nch, wave_lds = 2 * n_lds > wave;
   auto tile_on = [&](int i) { return i < 2 ? has0 : (i < 4 ? has1 : wave_lds); };
   auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, int i, u32x4 (&T)[2]) {
-    const uint32_t off = i < 4 ? (uint32_t)((i >> 1) * 2 * CH + (i & 1) * 64) : 0u;
-    const uint32_t so = i < 4 ? 0u : dlds;
-    T[0] = ldb16(rs, vo + off, so);
-    T[1] = ldb16(rs, vo + off + 16u, so);
+    const uint32_t off = i < 4 ? (uint32_t)((i >> 1) * 2 * CH + (i & 1) * 64) : dlds;
+    T[0] = ldb16(rs, vo + off, 0u);
+    T[1] = ldb16(rs, vo + off + 16u, 0u);
   };
   auto load_tiles = [&](__amdgpu_buffer_rsrc_t rs, uint32_t vo, u32x4 (&T)[5][2]) {
 #pragma unroll
@@ -2270,8 +2268,8 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
     r.prev = act ? p.prev[r0 + r.lr] : -1;
     const int b = act ? r.rid / K : 0, j = act ? r.rid - b * K : 0;
     r.invT = act ? 1.0f / p.temp[b] : 1.0f;
-    r.vb = act ? (uint32_t)(b * K + j) * Vb + col0 : STATS_PAST;   // inactive: past both tensors
-    r.vt = act ? (uint32_t)(b * (K + 1) + j) * Vb + col0 : STATS_PAST;
+    r.vb = act ? (uint32_t)(b * K + j) * Vb + col0 : PAST_END;   // inactive: past both tensors
+    r.vt = act ? (uint32_t)(b * (K + 1) + j) * Vb + col0 : PAST_END;
     return r;
   };
   auto stage_issue = [&](int prev, u32x4 (&v)[4]) {

@@ -99,13 +99,18 @@ struct Args {
   int G;                   // workgroups
 };
 
+// A byte offset past every logit tensor the resident kernels take (they take tensors of at most
+// this many bytes): buffer loads there read zeros without a memory access, and the largest tile
+// offset added to it stays below 2^32.
+constexpr uint32_t PAST_END = 0xFFF00000u;
+
 // Does the resident cycle take these dimensions on a device with G compute units?
 __host__ __device__ inline bool eligible(int B, int K, int V, int R, int dtype, int noise, int G) {
   if (dtype != SPEC_BF16 || noise != SPEC_NOISE_CHUNKED) return false;
   if (V % CH != 0 || R % 16 != 0 || R > 256 || G < 1 || G > MAX_G) return false;
   if (B < 1 || B > NW * G || B > MAX_B || K < 1 || K > MAX_K) return false;
-  // logit tensors below 4 GiB and A below 2 GiB: their loads use 32-bit byte offsets
-  if ((size_t)B * (K + 1) * V * 2 >= ((size_t)1 << 32) || (size_t)V * R * 2 >= ((size_t)1 << 31)) return false;
+  // logit tensors up to PAST_END bytes and A below 2 GiB: their loads use 32-bit byte offsets
+  if ((size_t)B * (K + 1) * V * 2 > (size_t)PAST_END || (size_t)V * R * 2 >= ((size_t)1 << 31)) return false;
   return (n_chunks(V) + G - 1) / G <= MAX_CHUNKS && (V + TP - 1) / TP <= MAX_G;
 }
 
@@ -113,13 +118,11 @@ __host__ __device__ inline bool eligible(int B, int K, int V, int R, int dtype, 
 // Listed rows go in batches whose base and target logits (4 V bytes a row) fit in this many bytes
 // of the Infinity Cache, so that the second pass over a batch finds them there.
 constexpr size_t STATS_BATCH_BYTES = (size_t)160 << 20;
-// byte offset past both logit tensors: the rows of inactive slots read zeros there
-constexpr uint32_t STATS_PAST = 0xFFFF0000u;
 
 __host__ __device__ inline bool stats_eligible(int B, int K, int V, int R, int dtype, int G) {
   if (dtype != SPEC_BF16 || V % CH != 0 || R % 16 != 0 || R > 256 || G < 1 || G > MAX_G) return false;
   if (B < 1 || K < 1) return false;
-  if ((size_t)B * (K + 1) * V * 2 >= (size_t)STATS_PAST - 4096 || (size_t)V * R * 2 >= ((size_t)1 << 31)) return false;
+  if ((size_t)B * (K + 1) * V * 2 > (size_t)PAST_END || (size_t)V * R * 2 >= ((size_t)1 << 31)) return false;
   return (n_chunks(V) + G - 1) / G <= MAX_CHUNKS;
 }
 

@@ -70,7 +70,7 @@ enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
  *                       instead of kernel boundaries.  Needs bf16 rows, chunked noise, whole
  *                       64-column chunks (V % 64 == 0), 16-byte aligned logits, B <= 4 x compute
  *                       units, at most 640 vocabulary columns per compute unit (V <= 163840 on a
- *                       256-CU gfx950), logit tensors below 4 GiB (B (K + 1) V 2 bytes) and A below
+ *                       256-CU gfx950), logit tensors of at most 4 GiB - 1 MiB (B (K + 1) V 2 bytes) and A below
  *                       2 GiB (V R 2 bytes): its loads use 32-bit byte offsets.  A grid barrier
  *                       that does not complete within about a second (only if the device cannot
  *                       keep the grid resident) marks every request invalid instead of hanging.
@@ -217,7 +217,7 @@ size_t spec_stats_workspace_bytes(const spec_dims* d);
  *   workspace                  device scratch of spec_stats_workspace_bytes(d) bytes, 256-byte
  *                              aligned, no initialisation needed
  * d->path: SPEC_PATH_AUTO or SPEC_PATH_RESIDENT take one cooperative launch with W held on chip
- * (bf16, V a multiple of 64, R <= 256 and a multiple of 16, logit tensors below 4 GiB, 16-byte
+ * (bf16, V a multiple of 64, R <= 256 and a multiple of 16, logit tensors of at most 4 GiB - 1 MiB, 16-byte
  * aligned logits; RESIDENT on other dims returns SPEC_E_DTYPE, AUTO falls back); the rows go in
  * batches whose logits stay in the Infinity Cache between the two passes.  SPEC_PATH_STEPWISE
  * takes the sweep kernels (two passes over the logits, any dtype and V).

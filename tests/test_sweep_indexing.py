@@ -172,9 +172,12 @@ def resident_smem(B):
     return o + NW * 16
 
 
+PAST_END = 0xFFF00000    # byte offset past every logit tensor the resident kernels take (empty slots read there)
+
+
 def resident_eligible(B, K, V, G, R=256):
     return (V % CHUNK == 0 and R % 16 == 0 and R <= 256 and 1 <= B <= NW * G and B <= 1024
-            and 1 <= K <= 32 and B * (K + 1) * V * 2 < 1 << 32 and V * R * 2 < 1 << 31
+            and 1 <= K <= 32 and B * (K + 1) * V * 2 <= PAST_END and V * R * 2 < 1 << 31
             and -(-n_chunks(V) // G) <= MAX_CHUNKS and -(-V // TP) <= MAX_G)
 
 
@@ -187,7 +190,7 @@ def test_resident_tile_offsets_fit(B, K, V):
     staging offsets of a previous token stay below the 2^31 marker that reads zeros."""
     G, R = 256, 256
     if not resident_eligible(B, K, V, G):
-        assert B * (K + 1) * V * 2 >= 1 << 32 or V % CHUNK or B > NW * G
+        assert B * (K + 1) * V * 2 > PAST_END or V % CHUNK or B > NW * G
         pytest.skip("not eligible")
     cb = np.array([chunk_begin(g, G, V) for g in range(G)])
     nc = np.array([chunks_of(g, G, V) for g in range(G)])
@@ -296,13 +299,12 @@ def test_resident_records_in_bounds(B, K):
 # W-resident acceptance statistics (k_stats_res)
 # ---------------------------------------------------------------------------------------------
 STATS_BATCH_BYTES = 160 << 20
-STATS_PAST = 0xFFFF0000
 FLAG_STRIDE = 2
 
 
 def stats_eligible(B, K, V, R, G=256):
     return (V % CHUNK == 0 and R % 16 == 0 and R <= 256 and B >= 1 and K >= 1
-            and B * (K + 1) * V * 2 < STATS_PAST - 4096 and V * R * 2 < 1 << 31
+            and B * (K + 1) * V * 2 <= PAST_END and V * R * 2 < 1 << 31
             and -(-n_chunks(V) // G) <= MAX_CHUNKS)
 
 
@@ -330,7 +332,7 @@ def test_stats_batches_offsets_and_workspace(B, K, V, R):
     wrapping; the library's workspace holds the statistics arrays."""
     from draft_sampling_lossless_spec_amd import binding
     if not stats_eligible(B, K, V, R):
-        assert B * (K + 1) * V * 2 >= STATS_PAST - 4096
+        assert B * (K + 1) * V * 2 > PAST_END
         pytest.skip("not eligible")
     n = B * K
     nbr, off, total = stats_layout(V, n)
@@ -362,7 +364,7 @@ def test_stats_batches_offsets_and_workspace(B, K, V, R):
             dlds = 2 * (CHUNK * (NW * AG_CHUNKS - AG_CHUNKS * w + (w >> 1)) + 32 * (w & 1))
             top = (B * nrow - 1) * 2 * V + 2 * (CHUNK * (cb + AG_CHUNKS * w) + 16) + max(3 * 64 + 64, dlds) + 32
             assert top.max() < 1 << 32
-        assert size <= STATS_PAST and STATS_PAST + 2 * 2 * CHUNK + 64 + 32 + 2 * CHUNK * NW * AG_CHUNKS + 64 < 1 << 32
+        assert size <= PAST_END and PAST_END + 2 * 2 * CHUNK + 64 + 32 + 2 * CHUNK * NW * AG_CHUNKS + 64 < 1 << 32
     # the library's statistics workspace holds these arrays after its sweep arrays
     ws = binding.spec_stats_workspace_bytes(B, K, V, R)
     assert ws >= total
