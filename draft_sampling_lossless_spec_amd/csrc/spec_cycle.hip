@@ -1833,25 +1833,42 @@ struct StatsParams {
   float2* part;            // [slots][nrA] per-range partials
 };
 
-// drafted position j of request b needs a valid temperature and x0, and a drafted token at j - 1
+// drafted position j of request b needs a valid temperature and x0, and a drafted token at j - 1.
+// Thread t takes requests t per .. t per + per - 1 (per <= MAX_B / NT), every load of a request
+// issued before any is used; the listed rows keep the order b K + j.
 __global__ __launch_bounds__(NT) void k_stats_prep(StatsParams sp) {
   const Params& p = sp.c;
   if (threadIdx.x < 2) {
     const uint32_t w = threadIdx.x ? 0xFF80FF80u : 0u;
     ((u32x4*)p.konst)[threadIdx.x] = (u32x4){w, w, w, w};
   }
-  const int n = p.B * p.K, per = (n + NT - 1) / NT, i0 = threadIdx.x * per;
+  const int B = p.B, K = p.K;
+  const int per = (B + NT - 1) / NT, b0 = threadIdx.x * per;
+  constexpr int MAXPER = (MAX_B + NT - 1) / NT;
+  uint32_t okm[MAXPER];
   int cnt = 0;
-  for (int i = i0; i < min(i0 + per, n); i++) {
-    const int b = i / p.K, j = i - b * p.K;
+#pragma unroll
+  for (int r = 0; r < MAXPER; r++) {
+    okm[r] = 0u;
+    const int b = b0 + r;
+    if (r >= per || b >= B) continue;
     const float T = p.temp[b];
     const int x0 = p.x0 ? p.x0[b] : -1;
-    const bool ok = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V && sp.draft[i] >= 0 &&
-                    (j == 0 || (sp.draft[i - 1] >= 0 && sp.draft[i - 1] < p.V));
-    cnt += ok ? 1 : 0;
-    sp.alpha[i] = NAN;
-    if (sp.o_lse_q) sp.o_lse_q[i] = NAN;
-    if (sp.o_lse_p) sp.o_lse_p[i] = NAN;
+    const bool valid = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V;
+    int d[MAX_K];
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) d[j] = j < K ? sp.draft[(size_t)b * K + j] : -1;
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) {
+      if (j >= K) break;
+      const bool ok = valid && d[j] >= 0 && (j == 0 || (d[j - 1] >= 0 && d[j - 1] < p.V));
+      okm[r] |= ok ? (1u << j) : 0u;
+      const size_t i = (size_t)b * K + j;
+      sp.alpha[i] = NAN;
+      if (sp.o_lse_q) sp.o_lse_q[i] = NAN;
+      if (sp.o_lse_p) sp.o_lse_p[i] = NAN;
+    }
+    cnt += __popc(okm[r]);
   }
   // exclusive scan of the per-thread counts (one thread: NT entries)
   __shared__ int cnts[NT];
@@ -1868,15 +1885,16 @@ __global__ __launch_bounds__(NT) void k_stats_prep(StatsParams sp) {
   }
   __syncthreads();
   int k = cnts[threadIdx.x];
-  for (int i = i0; i < min(i0 + per, n); i++) {
-    const int b = i / p.K, j = i - b * p.K;
-    const float T = p.temp[b];
-    const int x0 = p.x0 ? p.x0[b] : -1;
-    const bool ok = (T > 0.0f) && isfinite(T) && x0 >= -1 && x0 < p.V && sp.draft[i] >= 0 &&
-                    (j == 0 || (sp.draft[i - 1] >= 0 && sp.draft[i - 1] < p.V));
-    if (ok) {
+#pragma unroll
+  for (int r = 0; r < MAXPER; r++) {
+    const int b = b0 + r;
+    uint32_t m = okm[r];
+    while (m) {
+      const int j = __ffs((int)m) - 1;
+      m &= m - 1;
+      const int i = b * K + j;
       sp.rows[k] = i;
-      sp.prev[k] = j == 0 ? x0 : sp.draft[i - 1];
+      sp.prev[k] = j == 0 ? (p.x0 ? p.x0[b] : -1) : sp.draft[i - 1];
       k++;
     }
   }
