@@ -1373,21 +1373,27 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
 #pragma unroll
     for (int t = 0; t < KSTEPS; t++) wf[i][t] = w_frag(p, c, i & 1, t);
   }
-  // LDS tile u = 2 (local chunk - 8) + half, processed by wave u
-  for (int e = threadIdx.x; e < 4 * KSTEPS * 64; e += NT) {
-    const int u = e / (KSTEPS * 64), t = (e / 64) % KSTEPS, l = e % 64;
-    const int cl = NW * AG_CHUNKS + (u >> 1);
-    const int c = cl < nch ? cbeg + cl : -1;
-    // the fragment of lane l: same mapping as w_frag, computed for lane l
-    const int mm = l & 31, hh = l >> 5;
-    const int col_in = 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
-    const int v = CH * c + 32 * (u & 1) + col_in;
-    bf16x8 z;
+  // LDS tile u = 2 (local chunk - 8) + half, processed by wave u: all of a thread's loads issued
+  // before any is stored (out of range: read row 0 and store zeros)
+  {
+    constexpr int NE = 4 * KSTEPS * 64 / NT;
+    u32x4 z[NE];
 #pragma unroll
-    for (int i = 0; i < 8; i++) z[i] = (__bf16)0.0f;
-    if (c >= 0 && v < V && t < (p.a.R >> 4))
-      z = *(const bf16x8*)((const uint16_t*)p.a.W + (size_t)v * p.a.R + hh * (p.a.R >> 1) + 8 * t);
-    S.wl[e] = z;
+    for (int q = 0; q < NE; q++) {
+      const int e = (int)threadIdx.x + NT * q;
+      const int u = e / (KSTEPS * 64), t = (e / 64) % KSTEPS, l = e % 64;
+      const int cl = NW * AG_CHUNKS + (u >> 1);
+      const int c = cl < nch ? cbeg + cl : -1;
+      // the fragment of lane l: same mapping as w_frag, computed for lane l
+      const int mm = l & 31, hh = l >> 5;
+      const int col_in = 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
+      const int v = CH * c + 32 * (u & 1) + col_in;
+      const bool in = c >= 0 && v < V && t < (p.a.R >> 4);
+      const u32x4 x = *(const u32x4*)((const uint16_t*)p.a.W + (in ? (size_t)v * p.a.R + hh * (p.a.R >> 1) + 8 * t : 0));
+      z[q] = in ? x : kZero;
+    }
+#pragma unroll
+    for (int q = 0; q < NE; q++) ((u32x4*)S.wl)[threadIdx.x + NT * q] = z[q];
   }
 
   // ---- set-up: verify lengths and validity of every request (every workgroup, redundantly);
@@ -2219,16 +2225,24 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
       wf[i][t] = __builtin_bit_cast(bf16x8, in ? x : kZero);
     }
   }
-  for (int e = tid; e < 4 * KSTEPS * 64; e += NT) {
-    const int u = e / (KSTEPS * 64), t = (e / 64) % KSTEPS, l = e % 64;
-    const int cl = NW * AG_CHUNKS + (u >> 1);
-    const int c = cl < nch ? cbeg + cl : -1;
-    const int mm = l & 31, hh = l >> 5;
-    const int col_in = 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
-    const int v = CH * c + 32 * (u & 1) + col_in;
-    u32x4 z = kZero;
-    if (c >= 0 && v < V && t < nks) z = *(const u32x4*)((const uint16_t*)p.W + (size_t)v * R + hh * (R >> 1) + 8 * t);
-    ((u32x4*)wl)[e] = z;
+  {
+    constexpr int NE = 4 * KSTEPS * 64 / NT;   // every load of the thread before any store
+    u32x4 z[NE];
+#pragma unroll
+    for (int q = 0; q < NE; q++) {
+      const int e = tid + NT * q;
+      const int u = e / (KSTEPS * 64), t = (e / 64) % KSTEPS, l = e % 64;
+      const int cl = NW * AG_CHUNKS + (u >> 1);
+      const int c = cl < nch ? cbeg + cl : -1;
+      const int mm = l & 31, hh = l >> 5;
+      const int col_in = 16 * ((mm >> 2) & 1) + 4 * (mm >> 3) + (mm & 3);
+      const int v = CH * c + 32 * (u & 1) + col_in;
+      const bool in = c >= 0 && v < V && t < nks;
+      const u32x4 x = *(const u32x4*)((const uint16_t*)p.W + (in ? (size_t)v * R + hh * (R >> 1) + 8 * t : 0));
+      z[q] = in ? x : kZero;
+    }
+#pragma unroll
+    for (int q = 0; q < NE; q++) ((u32x4*)wl)[tid + NT * q] = z[q];
   }
   // k-steps past the rank read zeros
   for (int e = tid; e < 2 * KSTEPS * 64; e += NT)
