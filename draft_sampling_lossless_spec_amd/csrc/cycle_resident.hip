@@ -1411,11 +1411,20 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         L = 0;
       }
     } else {
+      // the running fp64 product of the confidences, stopping at the first that falls below the
+      // threshold; every confidence of the request is loaded first (one round trip)
+      float cf[MAX_K];
+#pragma unroll
+      for (int j = 0; j < MAX_K; j++) cf[j] = j < K ? p.a.conf[(size_t)b * K + j] : 0.0f;
       double P = 1.0;
-      for (int j = 0; j < K; j++) {
-        P *= (double)p.a.conf[(size_t)b * K + j];
-        if (!(P >= (double)p.a.threshold)) break;
-        L = j + 1;
+      bool run = true;
+#pragma unroll
+      for (int j = 0; j < MAX_K; j++) {
+        if (j < K && run) {
+          P *= (double)cf[j];
+          run = P >= (double)p.a.threshold;
+          L = run ? j + 1 : L;
+        }
       }
     }
     S.Lq[b] = (uint8_t)L;
