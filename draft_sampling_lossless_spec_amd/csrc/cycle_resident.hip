@@ -917,16 +917,12 @@ struct MergeLds {
 // columns 64 chunk + 16 w .. + 16, four lanes per column, each lane a quarter of the rank (eight
 // 16-byte pieces of the column's W row and the staged A row); the quarters are summed across the
 // lane quad, the winner is found per wave, then across the waves.  Result uniform.
-__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, uint2 arow_v,
-                                          L2Out (&out)[2]) {
+__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int V = p.a.V, R = p.a.R, P16 = R >> 3;
-  // every load of the round is issued before any of them is waited for: the A rows (staged in
-  // LDS below), the W rows, the draft and target logits of the 64 candidate columns
-  const int qa = (tid >> 6) & 1, la = tid & 63;
+  // every load of the round is issued before any of them is waited for: the W rows, the draft and
+  // target logits of the 64 candidate columns (the A rows are in LDS already)
   // (the job is picked by select, not by a run-time index: that would put the jobs in scratch memory)
-  auto needs_a = [&](const Job& j) { return j.kind != L2_NONE && j.kind != L2_TARGET && j.prev >= 0; };
-  const bool lda = tid < 128 && (qa == 0 ? needs_a(jb[0]) : needs_a(jb[1])) && 4 * la < R;
   const int col = 16 * wave + (lane >> 2), kq = lane & 3;
   int v[2];
   bool in[2], need_base[2], need_targ[2], wld[2][8];
@@ -964,8 +960,6 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
     bv[q] = need_base[q] ? bf16_to_f32(bvr[q]) : 0.0f;
     tv[q] = need_targ[q] ? bf16_to_f32(tvr[q]) : 0.0f;
   }
-  if (tid < 128) *(uint2*)&ml->arow[qa][4 * la] = lda ? arow_v : make_uint2(0u, 0u);
-  __syncthreads();   // the A rows are staged
 #pragma unroll
   for (int q = 0; q < 2; q++) {
     float ac[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent chains: the FMAs pipeline
@@ -1192,6 +1186,9 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     auto sel4 = [](bool c, float4 a, float4 b) {
       return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
     };
+    // the A rows of the level-two jobs into LDS (read there after the barriers below; a job without a
+    // previous token, or rank entries past R, hold zeros, and a job without a bias multiplies zero W)
+    if (tid < 128) *(uint2*)&ml->arow[(tid >> 6) & 1][4 * (tid & 63)] = arow_v;
     ml->part[0][tid] = sel4(hasD && tid < G, wg_draft(ad, cb, nl, gld), none);
     ml->part[3][tid] = sel4(hasP && tid < nrP, ap, none);
     if (hasC) {
@@ -1265,7 +1262,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     jb[1].targ = targ_s;
   }
   L2Out r2[2];
-  level_two(p, jb, invT, ml, arow_v, r2);
+  level_two(p, jb, invT, ml, r2);
   const L2Out rd = r2[0], rf = r2[1];
 
   // ---- decision and outputs (uniform over the workgroup; thread 0 writes scalars) ----
