@@ -74,9 +74,7 @@ enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
  *                       2 GiB (V R 2 bytes): its loads use 32-bit byte offsets.  A grid barrier
  *                       that does not complete within about a second (only if the device cannot
  *                       keep the grid resident) marks every request invalid instead of hanging.
- *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies and B <= 2 x compute
- *                       units (it finishes a workgroup's requests one after another), else the
- *                       stepwise one.
+ *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies, else the stepwise one.
  */
 enum { SPEC_PATH_AUTO = 0, SPEC_PATH_STEPWISE = 1, SPEC_PATH_RESIDENT = 2 };
 
