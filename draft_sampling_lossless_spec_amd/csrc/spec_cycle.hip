@@ -1870,32 +1870,43 @@ __global__ __launch_bounds__(NT) void k_stats_prep(StatsParams sp) {
     }
     cnt += __popc(okm[r]);
   }
-  // exclusive scan of the per-thread counts (one thread: NT entries)
-  __shared__ int cnts[NT];
-  cnts[threadIdx.x] = cnt;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int t = 0; t < NT; t++) {
-      const int c = cnts[t];
-      cnts[t] = run;
-      run += c;
-    }
-    sp.n_rows[0] = run;
+  // exclusive scan of the per-thread counts: within each wave by shuffles, then over the waves
+  __shared__ int wsum_s[NT / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    inc += lane >= o ? y : 0;
   }
+  if (lane == 63) wsum_s[wv] = inc;
   __syncthreads();
-  int k = cnts[threadIdx.x];
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; w++) {
+    base += w < wv ? wsum_s[w] : 0;
+    total += wsum_s[w];
+  }
+  if (threadIdx.x == 0) sp.n_rows[0] = total;
+  int k = base + inc - cnt;
+  // the listed rows of the thread's requests in order, previous tokens from the request's drafted
+  // tokens (loaded again, all at once)
 #pragma unroll
   for (int r = 0; r < MAXPER; r++) {
     const int b = b0 + r;
     uint32_t m = okm[r];
-    while (m) {
-      const int j = __ffs((int)m) - 1;
-      m &= m - 1;
-      const int i = b * K + j;
-      sp.rows[k] = i;
-      sp.prev[k] = j == 0 ? (p.x0 ? p.x0[b] : -1) : sp.draft[i - 1];
-      k++;
+    if (m == 0u) continue;
+    int d[MAX_K];
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) d[j] = j < K ? sp.draft[(size_t)b * K + j] : -1;
+    const int x0 = p.x0 ? p.x0[b] : -1;
+#pragma unroll
+    for (int j = 0; j < MAX_K; j++) {
+      if ((m >> j) & 1u) {
+        sp.rows[k] = b * K + j;
+        sp.prev[k] = j == 0 ? x0 : d[j - 1];
+        k++;
+      }
     }
   }
 }
