@@ -947,6 +947,13 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
     bvr[q] = *(need_base[q] ? jb[q].base + v[q] : (const uint16_t*)p.a.base);
     tvr[q] = *(need_targ[q] ? jb[q].targ + v[q] : (const uint16_t*)p.a.target);
   }
+  // this lane's quarter of both A rows, read from LDS while the W rows are in flight (read at the
+  // dot products instead, each read waited for on its own)
+  u32x4 ar[2][8];
+#pragma unroll
+  for (int q = 0; q < 2; q++)
+#pragma unroll
+    for (int i = 0; i < 8; i++) ar[q][i] = *(const u32x4*)&ml->arow[q][64 * kq + 8 * i];
   __builtin_amdgcn_sched_barrier(0);   // every load of the round is in flight before any is used
   // the candidates' Gumbel noise while the loads are in flight
   float gg[2];
@@ -965,11 +972,10 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
     float ac[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent chains: the FMAs pipeline
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const u32x4 ar = *(const u32x4*)&ml->arow[q][64 * kq + 8 * i];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        ac[e] = fmaf(bf_lo(ar[e]), bf_lo(wv[q][i][e]), ac[e]);
-        ac[e] = fmaf(bf_hi(ar[e]), bf_hi(wv[q][i][e]), ac[e]);
+        ac[e] = fmaf(bf_lo(ar[q][i][e]), bf_lo(wv[q][i][e]), ac[e]);
+        ac[e] = fmaf(bf_hi(ar[q][i][e]), bf_hi(wv[q][i][e]), ac[e]);
       }
     }
     float a = (ac[0] + ac[1]) + (ac[2] + ac[3]);
