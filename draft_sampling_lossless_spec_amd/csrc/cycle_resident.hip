@@ -25,8 +25,8 @@
 //   5. merge: request b is finished by workgroup b % G (its requests one after another): it reduces the G
 //      records of each of its rows, draws level two of the chunked sampler inside the winning
 //      chunk (re-reading that chunk's 64 columns and W rows), takes the accept decision, writes
-//      the outputs and the request's roles of step s + 1;
-//   6. grid barrier.
+//      the outputs and publishes the request's roles of step s + 1 in tagged words (see publish),
+//      which the lists of step s + 1 poll: no second grid barrier.
 // The step loop ends when no request has a role left; every workgroup sees the same roles, so
 // they all leave together.
 //
@@ -38,7 +38,8 @@
 // earlier calls never fall in that window (the nonce differs), so nothing is cleared between
 // calls.  A wait that has not finished after about a second sets the workspace's error word and
 // gives up; every later barrier then passes at once and the merges mark every request invalid, so
-// a synchronisation fault ends the kernel with invalid outputs instead of hanging the GPU.
+// a synchronisation fault ends the kernel with invalid outputs instead of hanging the GPU.  The
+// lists' wait for the published words has the same limit and the same error word.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -821,7 +822,29 @@ struct KP {
   float4* rec_p;      // [B][MAX_G]: records of the plain rows' items (ceil(V / TP) <= MAX_G per row)
   uint64_t* flags;    // [G][FLAG_STRIDE]
   uint64_t* err;
+  uint64_t* pub;      // [2][B][PUB_WORDS]: per-request words of the next step (see publish)
 };
+
+// What the merge of request b at step s hands to the lists of step s + 1, as three 64-bit words
+// whose high halves hold the tag s + 1 and whose low halves hold (roles of step s + 1) << 28 |
+// (token drafted at s) + 1, the draft row's log-normaliser at s, and the target row's (the last two
+// matter only to a CORRECT row of step s + 1, which needs both).  Each word is stored and loaded
+// whole (agent-scope 64-bit atomics), so a reader that finds tag s + 1 in a word holds that word's
+// value of step s; the lists poll the words of every request until all carry the step's tag, which
+// also orders the step: a merge publishes only after it has read its records, so no workgroup
+// overwrites records that a merge still reads.  Words of both step parities are cleared (tag 0) at
+// set-up, before the first grid barrier, so words of an earlier call never carry a live tag, and a
+// parity's word of step s - 2 carries tag s - 1.  Tokens fit the 28 bits (V < 2^26: A below 2 GiB).
+__device__ __forceinline__ uint64_t* pub_of(const KP& p, int parity, int b) {
+  return p.pub + ((size_t)parity * p.a.B + b) * PUB_WORDS;
+}
+__device__ __forceinline__ void publish(const KP& p, int s, int b, int roles, int x, float lse_q, float lse_p) {
+  uint64_t* w = pub_of(p, (s + 1) & 1, b);
+  const uint64_t tag = (uint64_t)(uint32_t)(s + 1) << 32;
+  st_u64(&w[0], tag | ((uint32_t)roles << 28) | (uint32_t)(x + 1));
+  st_u64(&w[1], tag | __float_as_uint(lse_q));
+  st_u64(&w[2], tag | __float_as_uint(lse_p));
+}
 
 // W fragment f (tile f of a chunk: 32 columns) at k-step t for lane l: row i = l % 32 of the MFMA
 // A operand is column 64 c + 32 f + perm(i), perm chosen so that accumulator q of lane l holds
@@ -1118,11 +1141,10 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int B = p.a.B, K = p.a.K, V = p.a.V, G = p.a.G;
   MergeLds* ml = (MergeLds*)S.sA;
-  int32_t* roles_next = p.st + (size_t)(ST_ROLES + ((s + 1) & 1)) * B;
   const int roles = S.role[b];
   __syncthreads();   // the scratch of the previous request's merge is no longer read
   if (roles == 0) {
-    if (tid == 0) st_i32(&roles_next[b], 0);
+    if (tid == 0) publish(p, s, b, 0, -1, 0.0f, 0.0f);
     return;
   }
   const ReqMeta rm = S.req[b];
@@ -1274,9 +1296,10 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
   // ---- decision and outputs (uniform over the workgroup; thread 0 writes scalars) ----
   bool invalid = false, rejected_now = false;
   int final_tok = -1, x_s = -1;
-  float logq_s = NAN;
+  float logq_s = NAN, pub_q = 0.0f, pub_p = 0.0f;
   if (hasD) {
     const float lse_q = tot_d.x;
+    pub_q = lse_q;
     if (!isfinite(lse_q) || rd.v < 0) {
       invalid = true;
     } else {
@@ -1284,7 +1307,6 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
       logq_s = rd.sx - lse_q;
       if (tid == 0) {
         st_i32(&p.xs[(size_t)b * K + s], x_s);
-        st_f32(&p.lse_q[(size_t)b * K + s], lse_q);
         if (p.a.d_draft) p.a.d_draft[(size_t)b * K + s] = x_s;
         if (p.a.d_logq) p.a.d_logq[(size_t)b * K + s] = logq_s;
       }
@@ -1292,6 +1314,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
   }
   if (!invalid && (roles & RO_LSEP)) {
     const float lse_p = tot_p.x;
+    pub_p = lse_p;
     if (!isfinite(lse_p) || x_s < 0) {
       invalid = true;
     } else {
@@ -1307,10 +1330,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
         phase = PH_REJECTED;
         rejected_now = true;
       }
-      if (tid == 0) {
-        st_f32(&p.lse_p[(size_t)b * (K + 1) + s], lse_p);
-        if (p.a.d_logp) p.a.d_logp[(size_t)b * K + s] = logp_s;
-      }
+      if (tid == 0 && p.a.d_logp) p.a.d_logp[(size_t)b * K + s] = logp_s;
     }
   }
   if (!invalid && (roles & RO_BONUS)) {
@@ -1334,7 +1354,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
       if (p.a.d_verify_len) p.a.d_verify_len[b] = -1;
       p.st[ST_PHASE * B + b] = PH_INVALID;
       p.st[ST_ACC * B + b] = acc;
-      st_i32(&roles_next[b], 0);
+      publish(p, s, b, 0, -1, 0.0f, 0.0f);
     }
     return;
   }
@@ -1351,7 +1371,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     if (rejected_now) nr |= RO_CORRECT;
     p.st[ST_PHASE * B + b] = phase;
     p.st[ST_ACC * B + b] = acc;
-    st_i32(&roles_next[b], nr);
+    publish(p, s, b, nr, x_s, pub_q, pub_p);
   }
 }
 
@@ -1453,6 +1473,11 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       p.st[ST_PHASE * B + b] = valid ? PH_ALIVE : PH_INVALID;
     }
   }
+  // their published words of both step parities: tag 0 (see publish)
+  for (int i = threadIdx.x; i < NW * 2 * PUB_WORDS; i += NT) {
+    const int b = g + G * (i / (2 * PUB_WORDS)), j = i % (2 * PUB_WORDS);
+    if (b < B) st_u64(&pub_of(p, j / PUB_WORDS, b)[j % PUB_WORDS], 0ull);
+  }
 
   uint64_t token = p.a.nonce;
   for (int s = 0; s <= K; s++) {
@@ -1473,21 +1498,48 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
       const int rounds = (B + NT - 1) / NT;
       for (int i = 0; i < rounds; i++) {
         const int b = i * NT + tid;
-        // the request's role and every input of its table row in one round trip (the inputs are
-        // loaded whatever the role; a request without one does not use them)
+        // the request's role and its table row: at s = 0 the set-up's roles; after that the words
+        // published by the request's merge of step s - 1, polled until all three carry tag s (a
+        // request without a role does not use the rest)
         int r = 0, x0 = -1, xd = -1, xc = -1;
         float T = 1.0f, lpc = 0.0f, lqc = 0.0f;
         const int jc = s > 0 ? s - 1 : 0;
         if (b < B) {
-          r = s > 0 ? ld_i32(&p.st[(ST_ROLES + (s & 1)) * B + b]) : S.role[b];
           x0 = p.a.x0 ? p.a.x0[b] : -1;
-          const int32_t* xr = p.xs + (size_t)b * K;
-          xd = s >= 1 ? ld_i32(&xr[s - 1]) : x0;
-          xc = s >= 2 ? ld_i32(&xr[s - 2]) : x0;
           T = p.a.temp[b];
-          lpc = ld_f32(&p.lse_p[(size_t)b * (K + 1) + jc]);
-          lqc = ld_f32(&p.lse_q[(size_t)b * K + jc]);
-          if (s > 0) S.role[b] = (uint8_t)r;
+          if (s == 0) {
+            r = S.role[b];
+            xd = x0;
+            xc = x0;
+          } else {
+            const uint64_t* w = pub_of(p, s & 1, b);
+            uint64_t w0, w1, w2;
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            while (true) {
+              w0 = ld_u64(&w[0]);
+              w1 = ld_u64(&w[1]);
+              w2 = ld_u64(&w[2]);
+              if ((uint32_t)(w0 >> 32) == (uint32_t)s && (uint32_t)(w1 >> 32) == (uint32_t)s &&
+                  (uint32_t)(w2 >> 32) == (uint32_t)s)
+                break;
+              // a wait that does not end within the barrier's limit fails the call like a barrier
+              // (the request then has no role; the merges mark every request invalid)
+              if (failed(p.err, p.a.nonce) || __builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
+                __hip_atomic_store(p.err, p.a.nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w0 = 0;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+            r = (int)((uint32_t)w0 >> 28);
+            xd = (int)((uint32_t)w0 & 0x0FFFFFFFu) - 1;
+            lqc = __uint_as_float((uint32_t)w1);
+            lpc = __uint_as_float((uint32_t)w2);
+            // the token before position s - 1: the previous step's prev_d, in the table while the
+            // request had a role there (which a CORRECT row at s implies)
+            xc = s >= 2 ? S.req[b].prev_d : x0;
+            S.role[b] = (uint8_t)r;
+          }
         }
         const uint64_t md = __ballot((r & RO_DRAFT) != 0), mc = __ballot((r & RO_CORRECT) != 0),
                        mp = __ballot((r & (RO_LSEP | RO_BONUS)) != 0);
@@ -2140,15 +2192,14 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     // ---- 4. grid barrier: every record of step s is written ----
     grid_barrier(p.flags, p.err, p.a.nonce, G, token++);
 
-    // ---- 5. merges: this workgroup's requests b = g, g + G, ... one after another ----
+    // ---- 5. merges: this workgroup's requests b = g, g + G, ... one after another; each publishes
+    //         its request's roles, drafted token and log-normalisers for step s + 1 ----
     for (int r = 0; r < NW; r++) {
       const int b = g + G * r;
       if (b >= B) break;
       merge_request(p, S, b, s, ls.c0);
     }
-
-    // ---- 6. grid barrier: roles, drafted tokens and log-normalisers of step s are written ----
-    grid_barrier(p.flags, p.err, p.a.nonce, G, token++);
+    __syncthreads();   // the merges' reads of the tables are done before the next lists rewrite them
   }
 #undef lane
 #undef m32
@@ -2616,7 +2667,7 @@ int launch(const Args& a_in, void* stream, void* ev_start, void* ev_stop) {
   Args a = a_in;
   a.nonce = next_nonce();
   const Layout l = layout(a.B, a.K);
-  KP p;
+  KP p{};
   p.a = a;
   char* ws = a.ws;
   p.st = (int32_t*)(ws + l.off_state);
@@ -2632,6 +2683,13 @@ int launch(const Args& a_in, void* stream, void* ev_start, void* ev_stop) {
   p.rec_p = (float4*)(ws + l.off_rec_p);
   p.flags = (uint64_t*)(ws + l.off_flags);
   p.err = p.flags + (size_t)MAX_G * FLAG_STRIDE;
+  p.pub = (uint64_t*)(ws + l.off_pub);
+  // every workspace pointer of the kernel lies inside the workspace (a field left unset is null)
+  {
+    const void* wp[] = {p.st, p.xs, p.lse_q, p.logq, p.lse_p, p.logp, p.rec_d, p.rec_c, p.rec_p, p.flags, p.err, p.pub};
+    for (const void* q : wp)
+      if ((const char*)q < ws || (const char*)q >= ws + l.total) return SPEC_E_WORKSPACE;
+  }
   const size_t lds = smem_bytes(a.B);
   // the dynamic LDS ceiling, once per device
   static std::atomic<int> attr_set[64];

@@ -29,6 +29,7 @@ constexpr int MAX_G = 256;              // workgroups (one per CU of a gfx950)
 constexpr int MAX_B = 1024;
 constexpr int MAX_K = 32;
 constexpr int FLAG_STRIDE = 2;          // uint64 words between two workgroups' barrier flags
+constexpr int PUB_WORDS = 4;            // uint64 words a merge publishes per request and step (3 used)
 
 __host__ __device__ constexpr int n_chunks(int V) { return (V + CH - 1) / CH; }
 __host__ __device__ constexpr int chunks_of(int g, int G, int V) {
@@ -55,6 +56,8 @@ struct Layout {
                        // from the first CORRECT slot
   size_t off_rec_p;    // float4 [B][MAX_G]: plain-row item records (ceil(V / TP) <= MAX_G items)
   size_t off_flags;    // uint64 [G][FLAG_STRIDE]: grid-barrier flags; uint64 [2]: error word
+  size_t off_pub;      // uint64 [2][B][PUB_WORDS]: what each request's merge hands to the next
+                       // step (two step parities)
   size_t total;
 };
 
@@ -70,6 +73,7 @@ __host__ __device__ inline Layout layout(int B, int K) {
   l.off_rec_c = o; o = align256(o + rec_c_bytes(B));
   l.off_rec_p = o; o = align256(o + rec_p_bytes(B));
   l.off_flags = o; o = align256(o + 8 * (size_t)(MAX_G * FLAG_STRIDE + 2));
+  l.off_pub = o; o = align256(o + 8 * (size_t)2 * B * PUB_WORDS);
   l.total = o;
   return l;
 }

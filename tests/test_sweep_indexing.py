@@ -295,6 +295,69 @@ def test_resident_records_in_bounds(B, K):
     assert workspace_bytes(B, K, V, R, 2) >= rec_d + rec_c + rec_p
 
 
+PUB_WORDS = 4   # 64-bit words a merge publishes per request and step (three used)
+
+
+def pub_pack(step, roles, x, lse_q, lse_p):
+    """The three words a merge of step `step` publishes (cycle_resident.hip's publish, restated):
+    tag step + 1 in the high halves; roles << 28 | x + 1, and the two normalisers' bits below."""
+    tag = (step + 1) << 32
+    fq = int(np.float32(lse_q).view(np.uint32))
+    fp = int(np.float32(lse_p).view(np.uint32))
+    return tag | (roles << 28) | (x + 1), tag | fq, tag | fp
+
+
+def pub_unpack(w0, w1, w2):
+    roles = (w0 & 0xFFFFFFFF) >> 28
+    x = (w0 & 0x0FFFFFFF) - 1
+    lq = np.uint32(w1 & 0xFFFFFFFF).view(np.float32)
+    lp = np.uint32(w2 & 0xFFFFFFFF).view(np.float32)
+    return [w >> 32 for w in (w0, w1, w2)], roles, x, lq, lp
+
+
+@pytest.mark.parametrize("B,K", list(itertools.product(BATCHES, POSITIONS)))
+def test_resident_published_words(B, K):
+    """The per-request words a merge hands to the next step's lists: every (parity, request, word)
+    inside the workspace area behind the barrier flags, every one of them cleared at set-up by the
+    workgroup that merges the request, and the tag / roles / token / normaliser packing lossless for
+    every role set and token (the resident path keeps V <= 10 chunks x 64 columns x 256 workgroups)."""
+    G, V, R = 256, 151936, 256
+    if not resident_eligible(B, K, V, G):
+        pytest.skip("not eligible")
+    rec_d = 16 * bias_slots_max(B) * NW * MAX_G
+    rec_c = 16 * (B + SUB) * NW * MAX_G
+    rec_p = 16 * B * MAX_G
+    flags = 8 * (MAX_G * 2 + 2)
+    pub = 8 * 2 * B * PUB_WORDS
+    assert workspace_bytes(B, K, V, R, 2) >= rec_d + rec_c + rec_p + flags + pub
+    # addressing: ((parity B + b) PUB_WORDS + j) over both parities
+    par, b, j = np.meshgrid(np.arange(2), np.arange(B), np.arange(PUB_WORDS), indexing="ij")
+    idx = ((par * B + b) * PUB_WORDS + j).ravel()
+    assert idx.min() == 0 and idx.max() < 2 * B * PUB_WORDS and np.unique(idx).size == idx.size
+    # set-up clear: thread i of workgroup g clears word (i % 2P) of request g + G (i / 2P)
+    cleared = set()
+    for g in range(G):
+        for i in range(NW * 2 * PUB_WORDS):
+            bb, jj = g + G * (i // (2 * PUB_WORDS)), i % (2 * PUB_WORDS)
+            if bb < B:
+                assert bb % G == g   # the workgroup that merges (and later publishes) the request
+                cleared.add(((jj // PUB_WORDS) * B + bb) * PUB_WORDS + jj % PUB_WORDS)
+    assert cleared == set(idx.tolist())
+    # packing: a cleared word (tag 0) never matches a polled step s >= 1, and a parity's word of
+    # step s - 2 carries tag s - 1
+    for step in range(K + 1):
+        for roles in range(16):
+            for x in (-1, 0, 1, V - 1, 163839):
+                lq, lp = np.float32(-11.25 - step), np.float32(np.float32(3.5) * roles)
+                tags, r2, x2, lq2, lp2 = pub_unpack(*pub_pack(step, roles, x, lq, lp))
+                assert tags == [step + 1] * 3 and (r2, x2) == (roles, x)
+                assert lq2 == lq and lp2 == lp
+    tags, r2, x2, _, _ = pub_unpack(0, 0, 0)
+    assert tags == [0, 0, 0] and r2 == 0 and x2 == -1
+    inf_bits = pub_pack(0, 0, -1, -np.inf, np.inf)
+    assert np.isneginf(pub_unpack(*inf_bits)[3]) and np.isposinf(pub_unpack(*inf_bits)[4])
+
+
 # ---------------------------------------------------------------------------------------------
 # W-resident acceptance statistics (k_stats_res)
 # ---------------------------------------------------------------------------------------------
