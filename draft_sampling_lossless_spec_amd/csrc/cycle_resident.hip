@@ -936,124 +936,99 @@ struct MergeLds {
   float4 win[2][NW];       // per-wave level-two winners {score, index, scaled draft logit, target logit}
 };
 
-// Level two of the chunked sampler for two jobs at once by the whole workgroup: wave w takes
-// columns 64 chunk + 16 w .. + 16, four lanes per column, each lane a quarter of the rank (eight
-// 16-byte pieces of the column's W row and the staged A row); the quarters are summed across the
-// lane quad, the winner is found per wave, then across the waves.  Result uniform.
+// Level two of the chunked sampler for two jobs at once by the whole workgroup, the 256-rank dot
+// products on the matrix cores: waves 2q and 2q + 1 take job q, lane l its columns
+// 64 chunk + 32 (w & 1) + l % 32.  Each 16 ranks are one v_mfma_f32_32x32x16_bf16 whose first
+// operand is the job's A row on all 32 rows and whose second is the 32 columns' W rows, so every
+// row of the product is the columns' bias and each lane holds its column's bias in every
+// accumulator (two chains over alternate k-steps).  Lane half h feeds ranks 16 t + 8 h .. + 7 of
+// k-step t.  The lower half's lanes score their columns, the winner is found per wave, then per
+// job.  Result uniform.
 __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int V = p.a.V, R = p.a.R, P16 = R >> 3;
-  // every load of the round is issued before any of them is waited for: the W rows, the draft and
-  // target logits of the 64 candidate columns (the A rows are in LDS already)
-  // (the job is picked by select, not by a run-time index: that would put the jobs in scratch memory)
-  const int col = 16 * wave + (lane >> 2), kq = lane & 3;
-  int v[2];
-  bool in[2], need_base[2], need_targ[2], wld[2][8];
-  float bv[2], tv[2], bias[2];
-  u32x4 wv[2][8];
-  uint16_t bvr[2], tvr[2];
+  const int V = p.a.V, R = p.a.R;
+  const int qj = wave >> 1, hk = lane >> 5;
+  // this wave's job, field by field (a select of whole structs goes through scratch memory)
+  const bool j1 = qj != 0;
+  const int kind = j1 ? jb[1].kind : jb[0].kind;
+  const int chunk = j1 ? jb[1].chunk : jb[0].chunk;
+  const int prev = j1 ? jb[1].prev : jb[0].prev;
+  const uint64_t key = j1 ? jb[1].key : jb[0].key;
+  const uint16_t* base = j1 ? jb[1].base : jb[0].base;
+  const uint16_t* targ = j1 ? jb[1].targ : jb[0].targ;
+  const float lse_p = j1 ? jb[1].lse_p : jb[0].lse_p, lse_q = j1 ? jb[1].lse_q : jb[0].lse_q;
+  const bool want_target = j1 ? jb[1].want_target : jb[0].want_target;
+  const int v = chunk * CH + 32 * (wave & 1) + (lane & 31);
+  const bool in = kind != L2_NONE && chunk >= 0 && v < V;
+  const bool need_base = in && (kind == L2_DRAFT || kind == L2_RESIDUAL);
+  const bool need_targ = in && (kind != L2_DRAFT || want_target);
+  const bool need_bias = in && kind != L2_TARGET && prev >= 0;
+  // every global load is issued before any is waited for: the W rows (buffer loads; k-steps past
+  // the rank and columns without a bias read past the end of W: zeros) and the two logits of the
+  // column; the A row's pieces come from LDS at the products (entries past R are zeros there)
+  const __amdgpu_buffer_rsrc_t rsW = ld_rsrc(p.a.W, (uint32_t)V * (uint32_t)R * 2u);
+  const int KS = R >> 4;
+  u32x4 wv[KSTEPS];
 #pragma unroll
-  for (int q = 0; q < 2; q++) {
-    v[q] = jb[q].chunk * CH + col;
-    in[q] = jb[q].kind != L2_NONE && jb[q].chunk >= 0 && v[q] < V;
-    need_base[q] = in[q] && (jb[q].kind == L2_DRAFT || jb[q].kind == L2_RESIDUAL);
-    need_targ[q] = in[q] && (jb[q].kind != L2_DRAFT || jb[q].want_target);
-    const bool need_bias = in[q] && jb[q].kind != L2_TARGET && jb[q].prev >= 0;
-    // unconditional loads at addresses clamped inside their tensors; values not needed are
-    // replaced after the loads
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int pc = 8 * kq + i;
-      wld[q][i] = need_bias && pc < P16;
-      wv[q][i] = *(const u32x4*)((const uint16_t*)p.a.W + (wld[q][i] ? (size_t)v[q] * R + 8 * pc : 0));
-    }
-    bvr[q] = *(need_base[q] ? jb[q].base + v[q] : (const uint16_t*)p.a.base);
-    tvr[q] = *(need_targ[q] ? jb[q].targ + v[q] : (const uint16_t*)p.a.target);
+  for (int t = 0; t < KSTEPS; t++) {
+    const uint32_t vo = (need_bias && t < KS) ? 2u * (uint32_t)(v * R + 16 * t + 8 * hk) : OOB_OFF;
+    wv[t] = ldb16(rsW, vo, 0u);
   }
-  // this lane's quarter of both A rows, read from LDS while the W rows are in flight (read at the
-  // dot products instead, each read waited for on its own)
-  u32x4 ar[2][8];
-#pragma unroll
-  for (int q = 0; q < 2; q++)
-#pragma unroll
-    for (int i = 0; i < 8; i++) ar[q][i] = *(const u32x4*)&ml->arow[q][64 * kq + 8 * i];
-  __builtin_amdgcn_sched_barrier(0);   // every load of the round is in flight before any is used
-  // the candidates' Gumbel noise while the loads are in flight
-  float gg[2];
-#pragma unroll
-  for (int q = 0; q < 2; q++) gg[q] = gumbel_bf(bits_at(jb[q].key, (uint32_t)v[q]));
+  const uint16_t bvr = *(need_base ? base + v : (const uint16_t*)p.a.base);
+  const uint16_t tvr = *(need_targ ? targ + v : (const uint16_t*)p.a.target);
+  __builtin_amdgcn_sched_barrier(0);   // every load is in flight before any is used
+  const float gg = gumbel_bf(bits_at(key, (uint32_t)v));   // the column's noise meanwhile
   __builtin_amdgcn_sched_barrier(0);
+  f32x16 c0 = {}, c1 = {};
 #pragma unroll
-  for (int q = 0; q < 2; q++) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) wv[q][i] = wld[q][i] ? wv[q][i] : kZero;
-    bv[q] = need_base[q] ? bf16_to_f32(bvr[q]) : 0.0f;
-    tv[q] = need_targ[q] ? bf16_to_f32(tvr[q]) : 0.0f;
+  for (int t = 0; t < KSTEPS; t += 2) {
+    const u32x4 a0 = *(const u32x4*)&ml->arow[qj][16 * t + 8 * hk];
+    const u32x4 a1 = *(const u32x4*)&ml->arow[qj][16 * t + 16 + 8 * hk];
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, wv[t]), c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, wv[t + 1]), c1, 0, 0, 0);
   }
-#pragma unroll
-  for (int q = 0; q < 2; q++) {
-    float ac[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // four independent chains: the FMAs pipeline
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        ac[e] = fmaf(bf_lo(ar[q][i][e]), bf_lo(wv[q][i][e]), ac[e]);
-        ac[e] = fmaf(bf_hi(ar[q][i][e]), bf_hi(wv[q][i][e]), ac[e]);
+  const float bias = c0[0] + c1[0];
+  const float bv = need_base ? bf16_to_f32(bvr) : 0.0f, tv = need_targ ? bf16_to_f32(tvr) : 0.0f;
+  float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
+  int ix = -1;
+  if (in && hk == 0) {
+    if (kind == L2_DRAFT) {
+      const float sv = (bv + bias) * invT;
+      if (want_target) tx = tv;
+      if (sv > -INFINITY) {
+        sc = sv + gg;
+        ix = v;
+        sx = sv;
+      }
+    } else if (kind == L2_TARGET) {
+      const float t = tv * invT;
+      if (t > -INFINITY) {
+        sc = t + gg;
+        ix = v;
+      }
+    } else {
+      const float sv = (bv + bias) * invT, t = tv * invT;
+      const float lp = t - lse_p, lq = sv - lse_q;
+      if (lp > lq) {
+        sc = lp + logf(-expm1f(lq - lp)) + gg;
+        ix = v;
       }
     }
-    float a = (ac[0] + ac[1]) + (ac[2] + ac[3]);
-    a += dpp<0xB1>(a);   // quad sum: xor 1, xor 2
-    a += dpp<0x4E>(a);
-    bias[q] = a;
   }
-#pragma unroll
-  for (int q = 0; q < 2; q++) {
-    float sc = -INFINITY, sx = 0.0f, tx = 0.0f;
-    int ix = -1;
-    if (in[q] && kq == 0) {
-      if (jb[q].kind == L2_DRAFT) {
-        const float sv = (bv[q] + bias[q]) * invT;
-        if (jb[q].want_target) tx = tv[q];
-        if (sv > -INFINITY) {
-          sc = sv + gg[q];
-          ix = v[q];
-          sx = sv;
-        }
-      } else if (jb[q].kind == L2_TARGET) {
-        const float t = tv[q] * invT;
-        if (t > -INFINITY) {
-          sc = t + gg[q];
-          ix = v[q];
-        }
-      } else {
-        const float sv = (bv[q] + bias[q]) * invT, t = tv[q] * invT;
-        const float lp = t - jb[q].lse_p, lq = sv - jb[q].lse_q;
-        if (lp > lq) {
-          sc = lp + logf(-expm1f(lq - lp)) + gg[q];
-          ix = v[q];
-        }
-      }
-    }
-    // the winner's target logit rides along as a second payload: pack (sx, tx) through the argmax
-    // by carrying tx in a separate argmax with the same take decisions is not possible, so the
-    // winning lane is found by ballot after the wave argmax
-    const int ix0 = ix;
-    const float tx0 = tx;
-    wargmax(sc, ix, sx);
-    const unsigned long long wm = __ballot(ix >= 0 && ix0 == ix);
-    const int src = __builtin_amdgcn_readfirstlane(wm ? __ffsll(wm) - 1 : 0);
-    tx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx0), src));
-    if (lane == 0) ml->win[q][wave] = make_float4(sc, __int_as_float(ix), sx, tx);
-  }
+  // the winner's target logit rides along: the winning lane is found by ballot after the argmax
+  const int ix0 = ix;
+  const float tx0 = tx;
+  wargmax(sc, ix, sx);
+  const unsigned long long wm = __ballot(ix >= 0 && ix0 == ix);
+  const int src = __builtin_amdgcn_readfirstlane(wm ? __ffsll(wm) - 1 : 0);
+  tx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tx0), src));
+  if (lane == 0) ml->win[qj][wave & 1] = make_float4(sc, __int_as_float(ix), sx, tx);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 2; q++) {
     float4 bw = ml->win[q][0];
-#pragma unroll
-    for (int w = 1; w < NW; w++) {
-      const float4 c = ml->win[q][w];
-      if (takes(c.x, __float_as_int(c.y), bw.x, __float_as_int(bw.y))) bw = c;
-    }
+    const float4 c = ml->win[q][1];
+    if (takes(c.x, __float_as_int(c.y), bw.x, __float_as_int(bw.y))) bw = c;
     out[q].v = __float_as_int(bw.y);
     out[q].sx = bw.z;
     out[q].tx = bw.w;
