@@ -872,28 +872,29 @@ struct PAcc {
   int ix, nan;
 };
 
-__device__ __forceinline__ void pacc_init(PAcc& a) {
-  a.m = -INFINITY;
+// a lane's running record of N records at once: the largest log-mass first, then N independent
+// exponentials (a NaN log-mass marks the record NaN)
+template <int N>
+__device__ __forceinline__ void pacc_of(PAcc& a, const float4 (&r)[N]) {
+  float m = r[0].x;
+#pragma unroll
+  for (int i = 1; i < N; i++) m = vmax(m, r[i].x);
+  a.nan = m != m;
+  a.m = a.nan ? -INFINITY : m;
   a.s = 0.0f;
+  if (a.m > -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < N; i++) a.s += ex2((r[i].x - a.m) * LOG2E);
+  }
   a.sc = -INFINITY;
   a.ix = -1;
-  a.nan = 0;
-}
-
-__device__ __forceinline__ void pacc_add(PAcc& a, float4 r) {
-  const float m = r.x;
-  if (m != m) {
-    a.nan = 1;
-  } else if (m > a.m) {
-    a.s = 1.0f + a.s * ex2((a.m - m) * LOG2E);   // a.m = -inf: the old sum is 0
-    a.m = m;
-  } else if (m > -INFINITY) {
-    a.s += ex2((m - a.m) * LOG2E);
-  }
-  const int ix = __float_as_int(r.z);
-  if (takes(r.y, ix, a.sc, a.ix)) {
-    a.sc = r.y;
-    a.ix = ix;
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    const int ix = __float_as_int(r[i].z);
+    if (takes(r[i].y, ix, a.sc, a.ix)) {
+      a.sc = r[i].y;
+      a.ix = ix;
+    }
   }
 }
 
@@ -1040,12 +1041,29 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
 // holds the log-mass of the wave's register chunks, their best score and chunk, and the log-mass
 // of the wave's half of an LDS chunk; the halves of LDS chunk i are in waves 2i and 2i + 1, and
 // the chunk's Gumbel score is formed here from the whole chunk.
+// log-sum-exp of N terms with the largest subtracted first: N independent exponentials and one
+// logarithm (a chain of pairwise log-additions costs one exponential and one logarithm per term
+// in sequence).  -inf terms add nothing; a NaN term makes the result NaN (v_maximum propagates it).
+template <int N>
+__device__ __forceinline__ float lse_of(const float (&x)[N]) {
+  float M = x[0];
+#pragma unroll
+  for (int i = 1; i < N; i++) M = vmax(M, x[i]);
+  if (M == -INFINITY) return -INFINITY;
+  float S = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; i++) S += ex2((x[i] - M) * LOG2E);
+  return M + lg2(S) * LN2;
+}
+
 __device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl, const float (&gl)[LDS_CHUNKS]) {
-  float lse = -INFINITY, bs = -INFINITY;
+  float bs = -INFINITY;
   int bc = -1;
+  // the log-mass over the register chunks' wave sums and the LDS chunks' halves
+  float x[NW + 2 * LDS_CHUNKS];
 #pragma unroll
   for (int w = 0; w < NW; w++) {
-    lse = lse_add(lse, a[w].x);
+    x[w] = a[w].x;
     if (takes(a[w].y, __float_as_int(a[w].z), bs, bc)) {
       bs = a[w].y;
       bc = __float_as_int(a[w].z);
@@ -1054,9 +1072,13 @@ __device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl
   // constant indices (the bound is the largest LDS chunk count) keep the records in registers
 #pragma unroll
   for (int i = 0; i < LDS_CHUNKS; i++) {
-    if (i >= nl) break;
-    const float hc = lse_add(a[2 * i].w, a[2 * i + 1].w);
-    lse = lse_add(lse, hc);
+    x[NW + 2 * i] = i < nl ? a[2 * i].w : -INFINITY;
+    x[NW + 2 * i + 1] = i < nl ? a[2 * i + 1].w : -INFINITY;
+  }
+  const float lse = lse_of(x);
+#pragma unroll
+  for (int i = 0; i < LDS_CHUNKS; i++) {
+    const float hc = i < nl ? lse2(a[2 * i].w, a[2 * i + 1].w) : -INFINITY;
     const int cgl = cb + NW * AG_CHUNKS + i;
     const float sc = hc > -INFINITY ? hc + gl[i] : -INFINITY;
     if (hc > -INFINITY && takes(sc, cgl, bs, bc)) {
@@ -1072,8 +1094,9 @@ __device__ __forceinline__ float4 wg_draft(const float4 (&a)[NW], int cb, int nl
 // log-mass, best score, best chunk, target log-mass of the LDS half); both draws use `key`.
 __device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (&t)[NW], int cb, int nl,
                                            const float (&gl)[LDS_CHUNKS], float4& rd, float4& rt) {
-  float ms = 0.0f, lt = -INFINITY, bs = -INFINITY, bt = -INFINITY;
+  float ms = 0.0f, bs = -INFINITY, bt = -INFINITY;
   int bc = -1, btc = -1;
+  float x[NW + 2 * LDS_CHUNKS];
 #pragma unroll
   for (int w = 0; w < NW; w++) {
     ms += a[w].x > -INFINITY ? ex2(a[w].x * LOG2E) : 0.0f;
@@ -1081,7 +1104,7 @@ __device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (
       bs = a[w].y;
       bc = __float_as_int(a[w].z);
     }
-    lt = lse_add(lt, t[w].x);
+    x[w] = t[w].x;
     if (takes(t[w].y, __float_as_int(t[w].z), bt, btc)) {
       bt = t[w].y;
       btc = __float_as_int(t[w].z);
@@ -1089,18 +1112,22 @@ __device__ __forceinline__ void wg_correct(const float4 (&a)[NW], const float4 (
   }
 #pragma unroll
   for (int i = 0; i < LDS_CHUNKS; i++) {
-    if (i >= nl) break;
+    x[NW + 2 * i] = i < nl ? t[2 * i].w : -INFINITY;
+    x[NW + 2 * i + 1] = i < nl ? t[2 * i + 1].w : -INFINITY;
+  }
+  const float lt = lse_of(x);
+#pragma unroll
+  for (int i = 0; i < LDS_CHUNKS; i++) {
     const int cgl = cb + NW * AG_CHUNKS + i;
     const float gg = gl[i];
-    const float mc = a[2 * i].w + a[2 * i + 1].w;
+    const float mc = i < nl ? a[2 * i].w + a[2 * i + 1].w : 0.0f;
     ms += mc;
     const float lmc = mc > 0.0f ? lg2(mc) * LN2 : -INFINITY;
     if (lmc > -INFINITY && takes(lmc + gg, cgl, bs, bc)) {
       bs = lmc + gg;
       bc = cgl;
     }
-    const float tc = lse_add(t[2 * i].w, t[2 * i + 1].w);
-    lt = lse_add(lt, tc);
+    const float tc = i < nl ? lse2(t[2 * i].w, t[2 * i + 1].w) : -INFINITY;
     if (tc > -INFINITY && takes(tc + gg, cgl, bt, btc)) {
       bt = tc + gg;
       btc = cgl;
@@ -1203,10 +1230,11 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     __syncthreads();
     const bool kind_on = wave == 0 ? hasD : (wave == 3 ? hasP : hasC);   // wave-uniform
     if (kind_on) {
-      PAcc a;
-      pacc_init(a);
+      float4 r4[NT / 64];
 #pragma unroll
-      for (int i = 0; i < NT / 64; i++) pacc_add(a, ml->part[wave][64 * i + lane]);
+      for (int i = 0; i < NT / 64; i++) r4[i] = ml->part[wave][64 * i + lane];
+      PAcc a;
+      pacc_of(a, r4);
       const float4 t = pacc_wave(a);
       if (lane == 0) ml->rec[wave][0] = t;
     } else if (lane == 0) {
