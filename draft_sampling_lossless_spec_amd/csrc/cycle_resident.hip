@@ -44,6 +44,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <stdlib.h>
 #include <time.h>
 #include <unistd.h>
 
@@ -82,7 +83,7 @@ __device__ __forceinline__ int ent_req(uint32_t e) { return (int)((e >> 1) & 102
 __device__ __forceinline__ int ent_prev(uint32_t e) { return (int)(e >> 11) - 1; }
 constexpr uint64_t TOKEN_WINDOW = 1ull << 16;
 
-constexpr uint64_t WAIT_TICKS = 100000000ull;   // s_memrealtime runs at 100 MHz: one second
+constexpr uint64_t WAIT_TICKS = 100000000ull;   // default wait limit; s_memrealtime runs at 100 MHz: one second
 
 // per-request inputs of the step's bias rows, rebuilt by every workgroup at every step
 struct ReqMeta {
@@ -732,7 +733,7 @@ __device__ __forceinline__ bool failed(const uint64_t* err, uint64_t nonce) {
   return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nonce;
 }
 
-__device__ void grid_barrier(uint64_t* flags, uint64_t* err, uint64_t nonce, int G, uint64_t token) {
+__device__ void grid_barrier(uint64_t* flags, uint64_t* err, uint64_t nonce, int G, uint64_t token, uint64_t wait_ticks) {
   // every wave's coherent stores of this phase have completed before its workgroup announces
   // arrival (the clobber keeps the compiler from moving memory operations across the wait)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -751,7 +752,7 @@ __device__ void grid_barrier(uint64_t* flags, uint64_t* err, uint64_t nonce, int
       }
       if (__all(ok)) break;
       if (failed(err, nonce)) break;
-      if (__builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) {
         if (lane == 0) __hip_atomic_store(err, nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -960,7 +961,8 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
   const float lse_p = j1 ? jb[1].lse_p : jb[0].lse_p, lse_q = j1 ? jb[1].lse_q : jb[0].lse_q;
   const bool want_target = j1 ? jb[1].want_target : jb[0].want_target;
   const int v = chunk * CH + 32 * (wave & 1) + (lane & 31);
-  const bool in = kind != L2_NONE && chunk >= 0 && v < V;
+  // (a chunk index past the vocabulary comes only from records a timed-out wait left incomplete)
+  const bool in = kind != L2_NONE && chunk >= 0 && chunk < n_chunks(V) && v < V;
   const bool need_base = in && (kind == L2_DRAFT || kind == L2_RESIDUAL);
   const bool need_targ = in && (kind != L2_DRAFT || want_target);
   const bool need_bias = in && kind != L2_TARGET && prev >= 0;
@@ -1527,7 +1529,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
                 break;
               // a wait that does not end within the barrier's limit fails the call like a barrier
               // (the request then has no role; the merges mark every request invalid)
-              if (failed(p.err, p.a.nonce) || __builtin_amdgcn_s_memrealtime() - t0 > WAIT_TICKS) {
+              if (failed(p.err, p.a.nonce) || __builtin_amdgcn_s_memrealtime() - t0 > p.a.wait_ticks) {
                 __hip_atomic_store(p.err, p.a.nonce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 w0 = 0;
                 break;
@@ -2193,7 +2195,7 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     }
 
     // ---- 4. grid barrier: every record of step s is written ----
-    grid_barrier(p.flags, p.err, p.a.nonce, G, token++);
+    grid_barrier(p.flags, p.err, p.a.nonce, G, token++, p.a.wait_ticks);
 
     // ---- 5. merges: this workgroup's requests b = g, g + G, ... one after another; each publishes
     //         its request's roles, drafted token and log-normalisers for step s + 1 ----
@@ -2256,6 +2258,7 @@ struct StatsKP {
   uint64_t* flags;         // [MAX_G][FLAG_STRIDE]
   uint64_t* err;
   uint64_t nonce;
+  uint64_t wait_ticks;     // limit of every bounded wait, s_memrealtime ticks
 };
 
 __host__ __device__ inline size_t stats_smem_bytes() {
@@ -2562,7 +2565,7 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
            return (mp == -INFINITY) ? (sp == 0.0f ? -INFINITY : NAN) : mp * rw.invT + lg2(sp) * LN2;
          },
          true);
-    grid_barrier(p.flags, p.err, p.nonce, G, token++);
+    grid_barrier(p.flags, p.err, p.nonce, G, token++, p.wait_ticks);
     // ---- 2. the rows' log-normalisers: one wave per row (and phase 4 of the previous batch) ----
     if (r0 > 0) merge2(r0 - nbr, nbr);
     for (int lr = g * NW + wave; lr < nb; lr += GW) {
@@ -2596,7 +2599,7 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
         if (p.o_lse_p) p.o_lse_p[rid] = lpv;
       }
     }
-    grid_barrier(p.flags, p.err, p.nonce, G, token++);
+    grid_barrier(p.flags, p.err, p.nonce, G, token++, p.wait_ticks);
     // ---- 3. per-workgroup sums of min(p, q) ----
     pass(r0, nb,
          [&](const RowIn& rw, const f32x16& x, const f32x16& y, int i0, bool two, const u32x4 (&Tt)[5][2], float2 ax) -> float2 {
@@ -2633,7 +2636,7 @@ __global__ __launch_bounds__(NT, 1) void k_stats_res(StatsKP p) {
          [](const RowIn&, const u32x4 (&)[5][2]) { return 0.0f; }, false);
   }
   // ---- 4. alpha of the last batch ----
-  grid_barrier(p.flags, p.err, p.nonce, G, token++);
+  grid_barrier(p.flags, p.err, p.nonce, G, token++, p.wait_ticks);
   if (n > 0) merge2((n - 1) / nbr * nbr, n - (n - 1) / nbr * nbr);
 }
 
@@ -2666,9 +2669,21 @@ static uint64_t next_nonce() {
   return z & ~(TOKEN_WINDOW - 1);
 }
 
+// Limit of the kernels' bounded waits in s_memrealtime ticks: one second, or the decimal value of
+// the environment variable SPEC_RESIDENT_WAIT_TICKS, read at every launch (a test sets 0 to force
+// the timeout path: the call then ends with every request invalid instead of waiting).
+static uint64_t wait_limit() {
+  const char* e = getenv("SPEC_RESIDENT_WAIT_TICKS");
+  if (!e || !*e) return WAIT_TICKS;
+  char* end = nullptr;
+  const unsigned long long v = strtoull(e, &end, 10);
+  return (end && *end == 0) ? (uint64_t)v : WAIT_TICKS;
+}
+
 int launch(const Args& a_in, void* stream, void* ev_start, void* ev_stop) {
   Args a = a_in;
   a.nonce = next_nonce();
+  a.wait_ticks = wait_limit();
   const Layout l = layout(a.B, a.K);
   KP p{};
   p.a = a;
@@ -2715,7 +2730,7 @@ int launch(const Args& a_in, void* stream, void* ev_start, void* ev_stop) {
 
 int launch_stats(const StatsArgs& a, void* stream) {
   const StatsLayout l = stats_layout(a.V, a.B * a.K);
-  StatsKP p;
+  StatsKP p{};
   p.B = a.B;
   p.K = a.K;
   p.V = a.V;
@@ -2740,6 +2755,7 @@ int launch_stats(const StatsArgs& a, void* stream) {
   p.flags = (uint64_t*)(a.ws + l.off_flags);
   p.err = p.flags + (size_t)MAX_G * FLAG_STRIDE;
   p.nonce = next_nonce();
+  p.wait_ticks = wait_limit();
   static std::atomic<int> attr_set[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_HIP;

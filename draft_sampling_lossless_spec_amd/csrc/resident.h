@@ -100,6 +100,7 @@ struct Args {
   float* d_logp;
   char* ws;
   uint64_t nonce;          // per-call value: barrier tokens are nonce + i, unique across calls
+  uint64_t wait_ticks;     // limit of every bounded wait, s_memrealtime ticks (100 MHz)
   int G;                   // workgroups
 };
 
