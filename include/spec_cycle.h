@@ -74,6 +74,9 @@ enum { SPEC_NOISE_FLAT = 0, SPEC_NOISE_CHUNKED = 1 };
  *                       2 GiB (V R 2 bytes): its loads use 32-bit byte offsets.  A grid barrier
  *                       that does not complete within about a second (only if the device cannot
  *                       keep the grid resident) marks every request invalid instead of hanging.
+ *                       The limit is 10^8 ticks of the 100 MHz real-time counter, or the decimal
+ *                       value of the environment variable SPEC_RESIDENT_WAIT_TICKS, read at every
+ *                       launch (0 forces the timeout path; spec_accept_stats then returns NaN).
  *   SPEC_PATH_AUTO      (0) the resident path when the call qualifies, else the stepwise one.
  */
 enum { SPEC_PATH_AUTO = 0, SPEC_PATH_STEPWISE = 1, SPEC_PATH_RESIDENT = 2 };
