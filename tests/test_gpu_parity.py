@@ -181,3 +181,21 @@ def test_side_stream_matches_default_stream():
     for k in g1:
         np.testing.assert_array_equal(g1[k], g2[k])
     assert all(int(j[0].item()) == 7 for j in junk)
+
+
+def test_resident_workspace_reused_across_shapes():
+    """One workspace for consecutive resident calls of different shapes (the same bytes hold one
+    call's records where the next call keeps its published per-request words, and the reverse):
+    every call matches the oracle, so no word left by an earlier call is taken for a live one."""
+    import torch
+    from draft_sampling_lossless_spec_amd import spec_workspace_bytes
+    from gpu_util import PATH_RESIDENT
+    shapes = [dict(B=64, K=6, V=2048, R=32, threshold=0.02), dict(B=32, K=3, V=1024, R=16, threshold=0.05),
+              dict(B=96, K=8, V=2048, R=32, threshold=0.01), dict(B=64, K=6, V=2048, R=32, threshold=0.02)]
+    ws_bytes = max(spec_workspace_bytes(c["B"], c["K"], c["V"], c["R"], path=PATH_RESIDENT) for c in shapes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    for i, cfg in enumerate(shapes):
+        w = wl.generate(wl.small_config(**cfg), gen_seed=i + 1)
+        print(f"shared workspace call {i}: {cfg}", flush=True)
+        g = run_gpu(w, oracle.CHUNKED, workspace=ws, path=PATH_RESIDENT)
+        assert_parity(compare(ref(w, oracle.CHUNKED), g))
