@@ -94,6 +94,7 @@ struct ReqMeta {
   float lse_q_c;
   uint32_t key_d[2]; // DRAFT_C noise key of position s
   uint32_t key_c[2]; // RESIDUAL_C noise key of position s - 1
+  uint32_t key_r[2]; // the request's noise key (set-up)
 };
 
 struct Lists {
@@ -1457,6 +1458,11 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
     }
     S.Lq[b] = (uint8_t)L;
     S.role[b] = valid ? (uint8_t)(L > 0 ? (RO_DRAFT | RO_LSEP) : RO_BONUS) : (uint8_t)0;
+    // the request's table entries that every step keeps: 1/T, the request's noise key, and x0 as
+    // the token before position 0 (used only while the request is valid)
+    S.req[b].invT = 1.0f / T;
+    S.req[b].prev_d = x0;
+    put_key(S.req[b].key_r, req_key(seed, p.a.req_off + b));
   }
   __syncthreads();
   // outputs and state of the requests this workgroup merges (request b: workgroup b % G, wave b / G)
@@ -1506,16 +1512,21 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
         // the request's role and its table row: at s = 0 the set-up's roles; after that the words
         // published by the request's merge of step s - 1, polled until all three carry tag s (a
         // request without a role does not use the rest)
-        int r = 0, x0 = -1, xd = -1, xc = -1;
-        float T = 1.0f, lpc = 0.0f, lqc = 0.0f;
+        int r = 0, xd = -1, xc = -1;
+        float lpc = 0.0f, lqc = 0.0f;
+        uint64_t kd = 0, kc = 0;
         const int jc = s > 0 ? s - 1 : 0;
         if (b < B) {
-          x0 = p.a.x0 ? p.a.x0[b] : -1;
-          T = p.a.temp[b];
+          // the step's noise keys before the wait (the asm keeps them from being moved past it)
+          kd = pos_key(key_of(S.req[b].key_r), s, ST_DRAFT_C);
+          kc = pos_key(key_of(S.req[b].key_r), jc, ST_RESIDUAL_C);
+          asm volatile("" : "+v"(kd), "+v"(kc));
+          // at s = 0 the token before the position is x0, which the set-up left in prev_d; after
+          // that prev_d holds the previous step's token before its position
+          xc = S.req[b].prev_d;
           if (s == 0) {
             r = S.role[b];
-            xd = x0;
-            xc = x0;
+            xd = xc;
           } else {
             const uint64_t* w = pub_of(p, s & 1, b);
             uint64_t w0, w1, w2;
@@ -1540,9 +1551,8 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
             xd = (int)((uint32_t)w0 & 0x0FFFFFFFu) - 1;
             lqc = __uint_as_float((uint32_t)w1);
             lpc = __uint_as_float((uint32_t)w2);
-            // the token before position s - 1: the previous step's prev_d, in the table while the
-            // request had a role there (which a CORRECT row at s implies)
-            xc = s >= 2 ? S.req[b].prev_d : x0;
+            // xc, the token before position s - 1, is the previous step's prev_d: in the table while
+            // the request had a role there (which a CORRECT row at s implies), x0 from the set-up at s = 1
             S.role[b] = (uint8_t)r;
           }
         }
@@ -1578,15 +1588,13 @@ __global__ __launch_bounds__(NT, 1) void k_resident(KP p) {
           S.slot[B + b] = sc;
           S.slot[2 * B + b] = sp;
           if (r) {
-            ReqMeta m;
+            ReqMeta m = S.req[b];   // invT and key_r are kept from the set-up
             m.prev_d = xd;
             m.prev_c = xc;
-            m.invT = 1.0f / T;
             m.lse_p_c = lpc;
             m.lse_q_c = lqc;
-            const uint64_t kr = req_key(seed, p.a.req_off + b);
-            put_key(m.key_d, pos_key(kr, s, ST_DRAFT_C));
-            put_key(m.key_c, pos_key(kr, jc, ST_RESIDUAL_C));
+            put_key(m.key_d, kd);
+            put_key(m.key_c, kc);
             S.req[b] = m;
             if (r & RO_DRAFT) S.blist[sd] = ent_make(b, false, m.prev_d);
           }

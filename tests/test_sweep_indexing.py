@@ -161,10 +161,13 @@ def chunk_begin(g, G, V):
     return g * (n // G) + (g if g < n % G else n % G)
 
 
+RES_REQ_META = 40        # bytes of the resident cycle's per-request table entry (ten 32-bit words)
+
+
 def resident_smem(B):
     o = 4 * 16 * 64 * 16          # W tiles of the LDS chunks
     o += 2 * 16 * 64 * 16         # B operands, double-buffered
-    o += B * REQ_META             # per-request table
+    o += B * RES_REQ_META         # per-request table
     o += 2 * B                    # roles, verify lengths
     o += 3 * B * 2                # slots
     o += bias_slots_max(B) * 4 + B * 2   # 32-bit bias entries, plain list
