@@ -900,18 +900,6 @@ __device__ __forceinline__ void pacc_of(PAcc& a, const float4 (&r)[N]) {
   }
 }
 
-// every lane's running record merged into every lane; returns {log-mass, best score, best chunk}
-__device__ __forceinline__ float4 pacc_wave(PAcc a) {
-  const float M = wmax(a.m);
-  const float sl = (a.m == -INFINITY) ? 0.0f : a.s * ex2((a.m - M) * LOG2E);
-  const float S_ = wsum(sl);
-  const int nan = __ballot(a.nan != 0) != 0ull;
-  float aux = 0.0f;
-  wargmax(a.sc, a.ix, aux);
-  const float lse = nan ? NAN : (M == -INFINITY ? -INFINITY : M + lg2(S_) * LN2);
-  return make_float4(lse, a.sc, __int_as_float(a.ix), 0.0f);
-}
-
 enum { L2_NONE = 0, L2_DRAFT = 1, L2_TARGET = 2, L2_RESIDUAL = 3 };
 
 struct Job {
@@ -947,7 +935,9 @@ struct MergeLds {
 // accumulator (two chains over alternate k-steps).  Lane half h feeds ranks 16 t + 8 h .. + 7 of
 // k-step t.  The lower half's lanes score their columns, the winner is found per wave, then per
 // job.  Result uniform.
-__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2]) {
+template <class Between>
+__device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float invT, MergeLds* ml, L2Out (&out)[2],
+                                          Between&& between) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int V = p.a.V, R = p.a.R;
   const int qj = wave >> 1, hk = lane >> 5;
@@ -982,6 +972,8 @@ __device__ __forceinline__ void level_two(const KP& p, const Job (&jb)[2], float
   const uint16_t tvr = *(need_targ ? targ + v : (const uint16_t*)p.a.target);
   __builtin_amdgcn_sched_barrier(0);   // every load is in flight before any is used
   const float gg = gumbel_bf(bits_at(key, (uint32_t)v));   // the column's noise meanwhile
+  __builtin_amdgcn_sched_barrier(0);
+  between();   // the caller's work that needs none of these loads
   __builtin_amdgcn_sched_barrier(0);
   f32x16 c0 = {}, c1 = {};
 #pragma unroll
@@ -1176,6 +1168,14 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     const uint32_t vo = in ? 2u * (uint32_t)(prev * p.a.R + 4 * la) : OOB_OFF;
     arow_v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsA, (int)vo, 0, 0));
   }
+  // wave r's running record of row kind r (DRAFT, CORRECT residual, CORRECT target, plain)
+  const bool kind_on = wave == 0 ? hasD : (wave == 3 ? hasP : hasC);   // wave-uniform
+  PAcc pa;
+  pa.m = -INFINITY;
+  pa.s = 0.0f;
+  pa.sc = -INFINITY;
+  pa.ix = -1;
+  pa.nan = 0;
   uint64_t key_l2d, key_l2r, key_l2b, key_acc;   // per-index noise keys of the level-two rows and the accept draw
   {
     const uint64_t key_d = key_of(rm.key_d), key_c = key_of(rm.key_c);
@@ -1231,28 +1231,31 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
       ml->part[2][tid] = rt;
     }
     __syncthreads();
-    const bool kind_on = wave == 0 ? hasD : (wave == 3 ? hasP : hasC);   // wave-uniform
+    // wave r reduces row kind r: the winning chunk first (level two's loads need only that), the
+    // log-mass while those loads are in flight (below)
     if (kind_on) {
       float4 r4[NT / 64];
 #pragma unroll
       for (int i = 0; i < NT / 64; i++) r4[i] = ml->part[wave][64 * i + lane];
-      PAcc a;
-      pacc_of(a, r4);
-      const float4 t = pacc_wave(a);
-      if (lane == 0) ml->rec[wave][0] = t;
+      pacc_of(pa, r4);
+      float aux = 0.0f;
+      wargmax(pa.sc, pa.ix, aux);
+      if (lane == 0) ml->rec[wave][1] = make_float4(pa.sc, __int_as_float(pa.ix), 0.0f, 0.0f);
     } else if (lane == 0) {
-      ml->rec[wave][0] = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f);
+      ml->rec[wave][1] = make_float4(-INFINITY, __int_as_float(-1), 0.0f, 0.0f);
     }
   }
   __syncthreads();
-  float4 tot[4];
+  int cz[4];   // each row kind's winning chunk (-1: none)
 #pragma unroll
-  for (int r = 0; r < 4; r++) tot[r] = ml->rec[r][0];
-  const float4 tot_d = tot[0], tot_c = tot[1], tot_c2 = tot[2], tot_p = tot[3];
+  for (int r = 0; r < 4; r++) cz[r] = __float_as_int(ml->rec[r][1].y);
 
   // ---- level two: the DRAFT row and the CORRECT / BONUS row side by side ----
+  // A row kind has a winning chunk exactly when its log-mass is above -inf (a chunk competes only
+  // with a positive mass); where the log-mass is not finite the decision below marks the request
+  // invalid whatever level two drew.
   const int j_c = s - 1;
-  const bool residual = tot_c.x > -INFINITY;
+  const bool residual = cz[1] >= 0;
   const uint16_t* targ_s = (const uint16_t*)p.a.target + ((size_t)b * (K + 1) + s) * V;
   Job jb[2];
 #pragma unroll
@@ -1267,9 +1270,9 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     jb[q].lse_q = 0.0f;
     jb[q].want_target = false;
   }
-  if (hasD && isfinite(tot_d.x)) {
+  if (hasD && cz[0] >= 0) {
     jb[0].kind = L2_DRAFT;
-    jb[0].chunk = __float_as_int(tot_d.z);
+    jb[0].chunk = cz[0];
     jb[0].prev = rm.prev_d;
     jb[0].key = key_l2d;
     jb[0].base = (const uint16_t*)p.a.base + ((size_t)b * K + s) * V;
@@ -1277,7 +1280,7 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     jb[0].want_target = (roles & RO_LSEP) != 0;
   }
   if (hasC) {
-    jb[1].chunk = __float_as_int(residual ? tot_c.z : tot_c2.z);
+    jb[1].chunk = residual ? cz[1] : cz[2];
     jb[1].key = key_l2r;
     jb[1].targ = (const uint16_t*)p.a.target + ((size_t)b * (K + 1) + j_c) * V;
     if (residual) {
@@ -1289,15 +1292,31 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     } else {
       jb[1].kind = L2_TARGET;
     }
-  } else if ((roles & RO_BONUS) && isfinite(tot_p.x)) {
+  } else if ((roles & RO_BONUS) && cz[3] >= 0) {
     jb[1].kind = L2_TARGET;
-    jb[1].chunk = __float_as_int(tot_p.z);
+    jb[1].chunk = cz[3];
     jb[1].key = key_l2b;
     jb[1].targ = targ_s;
   }
   L2Out r2[2];
-  level_two(p, jb, invT, ml, r2);
+  level_two(p, jb, invT, ml, r2, [&]() {
+    // wave r's row-kind log-mass (read after level two's last barrier)
+    if (kind_on) {
+      const float M = wmax(pa.m);
+      const float sl = (pa.m == -INFINITY) ? 0.0f : pa.s * ex2((pa.m - M) * LOG2E);
+      const float S_ = wsum(sl);
+      const int nan = __ballot(pa.nan != 0) != 0ull;
+      const float lse = nan ? NAN : (M == -INFINITY ? -INFINITY : M + lg2(S_) * LN2);
+      if (lane == 0) ml->rec[wave][0] = make_float4(lse, pa.sc, __int_as_float(pa.ix), 0.0f);
+    } else if (lane == 0) {
+      ml->rec[wave][0] = make_float4(-INFINITY, -INFINITY, __int_as_float(-1), 0.0f);
+    }
+  });
   const L2Out rd = r2[0], rf = r2[1];
+  float4 tot[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) tot[r] = ml->rec[r][0];
+  const float4 tot_d = tot[0], tot_c = tot[1], tot_p = tot[3];
 
   // ---- decision and outputs (uniform over the workgroup; thread 0 writes scalars) ----
   bool invalid = false, rejected_now = false;
