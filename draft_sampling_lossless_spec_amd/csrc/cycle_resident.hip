@@ -1189,18 +1189,18 @@ __device__ void merge_request(const KP& p, const Smem& S, int b, int s, int c0) 
     const auto rs_d = rec_rsrc(p.rec_d, rec_d_bytes(B)), rs_p = rec_rsrc(p.rec_p, rec_p_bytes(B)),
                rs_c = rec_rsrc(p.rec_c, rec_c_bytes(B));
     const size_t rd_base = (size_t)(hasD ? sd : 0) * NW * MAX_G + gi;
-    const size_t rc_base = (size_t)(hasC ? sc_ : 0) * NW * MAX_G + gi;
-    const size_t rt_base = (size_t)(hasC ? sc_ - c0 : 0) * NW * MAX_G + gi;
+    // (a request without a CORRECT row reads past the record areas: zeros, no memory access)
+    const size_t REC_PAST = (size_t)1 << 26;
+    const size_t rc_base = hasC ? (size_t)sc_ * NW * MAX_G + gi : REC_PAST;
+    const size_t rt_base = hasC ? (size_t)(sc_ - c0) * NW * MAX_G + gi : REC_PAST;
     float4 ad[NW], ac[NW], at[NW];
 #pragma unroll
     for (int w = 0; w < NW; w++) ad[w] = rec_load(rs_d, rd_base + (size_t)w * MAX_G);
     const float4 ap = rec_load(rs_p, (size_t)(hasP ? sp : 0) * MAX_G + (tid < nrP ? tid : 0));
-    if (hasC) {
 #pragma unroll
-      for (int w = 0; w < NW; w++) {
-        ac[w] = rec_load(rs_d, rc_base + (size_t)w * MAX_G);
-        at[w] = rec_load(rs_c, rt_base + (size_t)w * MAX_G);
-      }
+    for (int w = 0; w < NW; w++) {
+      ac[w] = rec_load(rs_d, rc_base + (size_t)w * MAX_G);
+      at[w] = rec_load(rs_c, rt_base + (size_t)w * MAX_G);
     }
     key_l2d = pos_key(kreq, s, ST_DRAFT);
     key_l2r = pos_key(kreq, s > 0 ? s - 1 : 0, ST_RESIDUAL);
